@@ -1,0 +1,36 @@
+/*
+ * CPU oracle for exhaustive QUBO search.  TEST INFRASTRUCTURE ONLY: only the
+ * tests, the smoke check and the CPU-baseline leg of the benchmark use it.
+ *
+ * E(x) = sum_{i,j} Q_ij x_i x_j over a full row-major n x n int32 Q (Maltsev et
+ * al., "Terastate-per-second QUBO Brute-Force on a Single GPU", sec. I), with the
+ * state index idx(x) = sum_i x_i 2^(n-1-i) (variable 0 most significant,
+ * sec. II.B Fig. 2).  All energies are int64.  Functions return 0 on success,
+ * -1 on a bad argument and -2 when memory runs out.
+ */
+#ifndef QUBO_ORACLE_H
+#define QUBO_ORACLE_H
+#include <stdint.h>
+
+typedef struct {
+    int64_t min_energy;     /* min over the searched states */
+    uint64_t argmin;        /* smallest index attaining it */
+    uint64_t count;         /* number of searched states attaining it (0 = none searched) */
+    int64_t max_abs_energy; /* largest |E| seen (overflow audit for int32 solvers) */
+} oracle_result;
+
+/* E(x) for the state with index idx. */
+int64_t oracle_energy(const int32_t *Q, int n, uint64_t idx);
+void oracle_energy_many(const int32_t *Q, int n, const uint64_t *idx, uint64_t m, int64_t *out);
+
+/* Tier A: direct O(n^2) evaluation of every idx in [lo, hi). */
+int oracle_search_direct(const int32_t *Q, int n, uint64_t lo, uint64_t hi, int threads,
+                         oracle_result *out);
+
+/* Tier B: Gray-code walk over the sub-cube whose variables 0..k-1 equal the k-bit
+ * number `top` (variable 0 most significant); k = 0, top = 0 is the full space. */
+int oracle_search_gray(const int32_t *Q, int n, int k, uint64_t top, int threads,
+                       oracle_result *out);
+
+const char *oracle_version(void);
+#endif

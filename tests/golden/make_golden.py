@@ -1,0 +1,98 @@
+"""Write the stored oracle results under tests/golden/.
+
+Calls only the CPU oracle (``oracle``) on the seeded workloads of
+``qubo_instances``; nothing here comes from the solver.  Usage:
+
+    python tests/golden/make_golden.py C1 C2 C2p        # full searches
+    python tests/golden/make_golden.py C3               # 2^40 states, ~25 min on 8 cores
+    python tests/golden/make_golden.py C4sub C5sub      # seeded sub-cubes of 2^32 states
+
+Full searches store {sha256_Q, n, min_energy, argmin, count, max_abs_energy}.
+Sub-cube files store one record per sub-cube: the first k variables are fixed
+to `top` (variable 0 most significant) and the remaining 32 are searched.
+"""
+from __future__ import annotations
+
+import json
+import os
+import platform
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import qubo_instances as qi  # noqa: E402
+
+SUB_FREE_BITS = 32
+SUB_COUNT = 16
+SUB_SEED = 4242
+
+
+def host_info(threads: int) -> dict:
+    return dict(threads=threads, cpu=platform.processor() or platform.machine(),
+                nproc=os.cpu_count(), oracle=oracle.version())
+
+
+def full(name: str, threads: int) -> dict:
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    t0 = time.time()
+    b = oracle.search_gray(Q, threads=threads)
+    tb = time.time() - t0
+    rec = dict(name=name, desc=cfg["desc"], n=n, seed=cfg["seed"], sha256_Q=qi.sha256_of(Q),
+               min_energy=b.min_energy, argmin=b.argmin, count=b.count,
+               max_abs_energy=b.max_abs_energy, tier="B (Gray walk)", seconds_tier_b=round(tb, 2),
+               host=host_info(threads))
+    if n <= 32:
+        t0 = time.time()
+        a = oracle.search_direct(Q, threads=threads)
+        rec["seconds_tier_a"] = round(time.time() - t0, 2)
+        if a.triple() != b.triple():
+            raise SystemExit("tier A %s != tier B %s on %s" % (a.triple(), b.triple(), name))
+        rec["tier"] = "A (direct) and B (Gray walk), identical"
+    if "C" in cfg:
+        rec["ising_constant_C"] = cfg["C"]
+        rec["ising_min_H"] = b.min_energy + cfg["C"]
+    return rec
+
+
+def subcubes(name: str, threads: int) -> dict:
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    k = n - SUB_FREE_BITS
+    rng = qi.SplitMix64(SUB_SEED + n)
+    tops = []
+    while len(tops) < SUB_COUNT:
+        t = rng.uniform_int(0, (1 << k) - 1)
+        if t not in tops:
+            tops.append(t)
+    cubes = []
+    t_all = time.time()
+    for top in tops:
+        t0 = time.time()
+        r = oracle.search_gray(Q, k=k, top=top, threads=threads)
+        cubes.append(dict(k=k, top=top, min_energy=r.min_energy, argmin=r.argmin, count=r.count,
+                          max_abs_energy=r.max_abs_energy, seconds=round(time.time() - t0, 2)))
+        print("  %s top=%d -> %s" % (name, top, r.triple()), flush=True)
+    return dict(name=name + "sub", desc=cfg["desc"], n=n, seed=cfg["seed"], sha256_Q=qi.sha256_of(Q),
+                free_bits=SUB_FREE_BITS, sub_seed=SUB_SEED + n, cubes=cubes, tier="B (Gray walk)",
+                seconds_total=round(time.time() - t_all, 2), host=host_info(threads))
+
+
+def main(argv):
+    threads = oracle.default_threads()
+    for arg in argv:
+        print("computing", arg, "on", threads, "threads", flush=True)
+        rec = subcubes(arg[:-3], threads) if arg.endswith("sub") else full(arg, threads)
+        path = os.path.join(HERE, arg + ".json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print("wrote", path, {k: rec[k] for k in rec if k in ("min_energy", "argmin", "count")}, flush=True)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:] or ["C1", "C2", "C2p"])

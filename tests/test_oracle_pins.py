@@ -1,0 +1,246 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Every pin is a function of an ``oracle.Oracle`` so that the same checks run on
+the default build and on mutant builds (``-DORACLE_MUTATION=k``) in
+``test_oracle_mutants.py``, which shows that each planted mistake fails a pin.
+
+Sources of truth used here (none of them is the oracle's own code):
+  * hand-worked energies of tiny instances (tests/golden/worked_examples.json);
+  * closed forms E(0) = 0, E(e_i) = Q_ii, E(e_i + e_j) = Q_ii + Q_jj + Q_ij + Q_ji;
+  * a third, numpy implementation: x^T Q x for all 2^n states (n <= 10);
+  * special cases (Q = 0, diagonal Q), the planted-minimiser family, Mattis
+    instances with ground energy -n(n-1)/2 and two ground states;
+  * the Ising <-> QUBO identity H(s) = E_Q(x) + C (Maltsev et al., sec. I);
+  * invariances: relabelling of variables (sec. II.D), change of gauge,
+    antisymmetric additions and positive scaling.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import qubo_instances as qi
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def numpy_all_states(Q) -> tuple[int, int, int]:
+    """(min, argmin, count) from x^T Q x over every state, in numpy (n <= 12)."""
+    Q = np.asarray(Q, dtype=np.int64)
+    n = Q.shape[0]
+    idx = np.arange(1 << n, dtype=np.int64)
+    X = ((idx[:, None] >> (n - 1 - np.arange(n))[None, :]) & 1).astype(np.int64)
+    E = np.einsum("si,ij,sj->s", X, Q, X)
+    m = int(E.min())
+    where = np.nonzero(E == m)[0]
+    return m, int(where[0]), int(where.size)
+
+
+def rand_general(n, seed, lo=-100, hi=100):
+    return qi.general_uniform(n, seed, lo, hi)
+
+
+# --------------------------------------------------------------------------- pins
+
+def pin_worked_examples(o: oracle.Oracle):
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        data = json.load(f)
+    for ex in data["examples"]:
+        Q, n = ex["Q"], len(ex["Q"])
+        got = [o.energy(Q, i) for i in range(1 << n)]
+        assert got == ex["energies"], ex["name"]
+        want = (ex["min"], ex["argmin"], ex["count"])
+        assert o.search_direct(Q).triple() == want, ex["name"]
+        assert o.search_gray(Q, threads=1).triple() == want, ex["name"]
+
+
+def pin_closed_forms(o: oracle.Oracle):
+    for n, seed in [(1, 2001), (2, 2002), (5, 2003), (13, 2004), (40, 2005), (63, 2006)]:
+        Q = rand_general(n, seed, -1000, 1000)
+        assert o.energy(Q, 0) == 0
+        for i in range(n):
+            ei = 1 << (n - 1 - i)
+            assert o.energy(Q, ei) == Q[i][i], (n, i)
+            for j in range(n):
+                if j != i:
+                    ej = 1 << (n - 1 - j)
+                    assert o.energy(Q, ei | ej) == Q[i][i] + Q[j][j] + Q[i][j] + Q[j][i], (n, i, j)
+
+
+def pin_numpy_third_implementation(o: oracle.Oracle):
+    cases = [(n, 2100 + n, -100, 100) for n in range(1, 11)]
+    # small entries make heavy ties, which exercise count and the lowest-index rule
+    cases += [(n, 2200 + n, -1, 1) for n in range(2, 11)]
+    cases += [(n, 2300 + n, -2, 3) for n in (6, 9, 10)]
+    for n, seed, lo, hi in cases:
+        Q = rand_general(n, seed, lo, hi)
+        want = numpy_all_states(Q)
+        assert o.search_direct(Q).triple() == want, (n, seed)
+        for threads in (1, 3):
+            assert o.search_gray(Q, threads=threads).triple() == want, (n, seed, threads)
+
+
+def pin_tiers_agree(o: oracle.Oracle):
+    for n in range(1, 17):
+        Q = rand_general(n, 2400 + n, -50, 50)
+        a = o.search_direct(Q)
+        b = o.search_gray(Q)
+        assert a.triple() == b.triple(), n
+    # sub-cubes: fixing the first k variables is the index range [top<<m, (top+1)<<m)
+    Q = rand_general(14, 2450, -3, 3)
+    for k, top in [(1, 1), (3, 5), (7, 100), (14, 12345)]:
+        m = 14 - k
+        a = o.search_direct(Q, top << m, (top + 1) << m)
+        b = o.search_gray(Q, k, top)
+        assert a.triple() == b.triple(), (k, top)
+
+
+def pin_special_cases(o: oracle.Oracle):
+    for n in (1, 4, 11, 16):
+        zero = qi.zeros(n)
+        assert o.search_gray(zero).triple() == (0, 0, 1 << n)
+        assert o.search_direct(zero).triple() == (0, 0, 1 << n)
+        pos = qi.zeros(n)
+        neg = qi.zeros(n)
+        for i in range(n):
+            pos[i][i] = 1 + i
+            neg[i][i] = -(1 + 2 * i)
+        assert o.search_gray(pos).triple() == (0, 0, 1)
+        assert o.search_direct(neg).triple() == (sum(neg[i][i] for i in range(n)), (1 << n) - 1, 1)
+        assert o.search_gray(neg).triple() == (sum(neg[i][i] for i in range(n)), (1 << n) - 1, 1)
+
+
+def pin_planted(o: oracle.Oracle):
+    for n, seed in [(3, 2501), (8, 2502), (13, 2503), (20, 2504)]:
+        Q, P, a = qi.planted(n, seed)
+        av = np.asarray(a, dtype=np.int64)
+        want_min = -int(av @ np.asarray(P, dtype=np.int64) @ av)
+        want = (want_min, qi.bits_to_index(a), 1)
+        assert o.search_gray(Q).triple() == want, (n, seed)
+        if n <= 13:
+            assert o.search_direct(Q).triple() == want, (n, seed)
+
+
+def pin_mattis(o: oracle.Oracle):
+    for n, seed in [(2, 3001), (5, 3002), (12, 3003), (18, 3004)]:
+        J, h, xi = qi.mattis(n, seed)
+        Q, C = qi.ising_to_qubo(J, h)
+        # s = xi and s = -xi; x = (1 + s) / 2.  The lower index has x_0 = 0.
+        xa = [(1 + s) // 2 for s in xi]
+        xb = [1 - v for v in xa]
+        want_arg = min(qi.bits_to_index(xa), qi.bits_to_index(xb))
+        r = o.search_gray(Q)
+        assert r.min_energy + C == -n * (n - 1) // 2, (n, seed)
+        assert (r.argmin, r.count) == (want_arg, 2), (n, seed)
+
+
+def pin_ising_identity(o: oracle.Oracle):
+    for n, seed in [(3, 3101), (7, 3102), (11, 3103)]:
+        rng = qi.SplitMix64(seed)
+        J = qi.zeros(n)
+        for i in range(n):
+            for j in range(i + 1, n):
+                J[i][j] = rng.uniform_int(-5, 5)
+        h = [rng.uniform_int(-5, 5) for _ in range(n)]
+        Q, C = qi.ising_to_qubo(J, h)
+        idx = np.arange(1 << n, dtype=np.uint64)
+        E = o.energies(Q, idx)
+        S = 2 * ((idx[:, None].astype(np.int64) >> (n - 1 - np.arange(n))[None, :]) & 1) - 1
+        Ju = np.triu(np.asarray(J, dtype=np.int64), 1)
+        H = np.einsum("si,ij,sj->s", S, Ju, S) + S @ np.asarray(h, dtype=np.int64)
+        assert np.array_equal(H, E + C), (n, seed)
+
+
+def pin_invariances(o: oracle.Oracle):
+    n = 9
+    Q = np.asarray(rand_general(n, 3201, -60, 60), dtype=np.int64)
+    base = o.search_gray(Q)
+    assert base.triple() == o.search_direct(Q).triple()
+    # relabelling: x'_i = x_perm[i]
+    perm = [3, 0, 8, 5, 1, 7, 2, 6, 4]
+    Qp = Q[np.ix_(perm, perm)]
+    rp = o.search_gray(Qp)
+    assert (rp.min_energy, rp.count) == (base.min_energy, base.count)
+    if base.count == 1:
+        bits = qi.index_to_bits(base.argmin, n)
+        assert rp.argmin == qi.bits_to_index([bits[p] for p in perm])
+    # gauge: E_Q'(x) = E_Q(x xor a) - E_Q(a)
+    a = [1, 0, 1, 1, 0, 0, 1, 0, 1]
+    Qg = qi.gauge_transform(Q.tolist(), a)
+    av = np.asarray(a, dtype=np.int64)
+    rg = o.search_gray(Qg)
+    assert (rg.min_energy, rg.count) == (base.min_energy - int(av @ Q @ av), base.count)
+    if base.count == 1:
+        assert rg.argmin == base.argmin ^ qi.bits_to_index(a)
+    # antisymmetric additions change no energy
+    K = np.asarray(rand_general(n, 3202, -30, 30), dtype=np.int64)
+    assert o.search_gray(Q + K - K.T).triple() == base.triple()
+    assert o.search_direct(Q + K - K.T).triple() == base.triple()
+    # positive scaling
+    r3 = o.search_gray(3 * Q)
+    assert r3.triple() == (3 * base.min_energy, base.argmin, base.count)
+
+
+ALL_PINS = [pin_worked_examples, pin_closed_forms, pin_numpy_third_implementation, pin_tiers_agree,
+            pin_special_cases, pin_planted, pin_mattis, pin_ising_identity, pin_invariances]
+
+
+# -------------------------------------------------------------------------- tests
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(oracle.default())
+
+
+def test_fig5_gray_sequence():
+    """The binary-reflected Gray code g(i) = i ^ (i >> 1), which orders the
+    prefix walk and the prefix-energy table, is the sequence printed in Fig. 5."""
+    with open(os.path.join(GOLDEN, "gray_fig5.json")) as f:
+        fig = json.load(f)
+    b = fig["bits"]
+    assert [format(i ^ (i >> 1), "0%db" % b) for i in range(1 << b)] == fig["sequence"]
+    # consecutive codes differ in exactly one bit, and the flipped bit is ctz(i+1)
+    for i in range((1 << b) - 1):
+        d = (i ^ (i >> 1)) ^ ((i + 1) ^ ((i + 1) >> 1))
+        assert d == ((i + 1) & -(i + 1))
+
+
+def test_numpy_reference_itself():
+    """The numpy third implementation reproduces the hand-worked energies."""
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        data = json.load(f)
+    for ex in data["examples"]:
+        assert numpy_all_states(ex["Q"]) == (ex["min"], ex["argmin"], ex["count"])
+
+
+def test_generators_are_stable():
+    """The seeded workloads hash to the values recorded with the stored results."""
+    for name in ("C1", "C2", "C2p", "C3", "C4", "C5"):
+        path = os.path.join(GOLDEN, name + ".json")
+        if not os.path.exists(path):
+            pytest.skip("stored result for %s not written yet" % name)
+        with open(path) as f:
+            rec = json.load(f)
+        assert qi.sha256_of(qi.make_config(name)["Q"]) == rec["sha256_Q"], name
+
+
+def test_config_families():
+    """Structural facts of the workloads, read off the matrices."""
+    c3 = qi.make_config("C3")
+    Q = np.asarray(c3["Q"])
+    off = Q[~np.eye(40, dtype=bool)]
+    assert set(np.unique(off)) == {-2, 2}
+    assert np.all(Q % 2 == 0) and np.array_equal(Q, Q.T)
+    c5 = qi.make_config("C5")
+    Q5 = np.asarray(c5["Q"])
+    assert np.array_equal(Q5, Q5.T)
+    # a rank-4 signal stands out of the noise: four eigenvalues well clear of the rest
+    w = np.sort(np.abs(np.linalg.eigvalsh(Q5.astype(float))))[::-1]
+    assert w[3] > 2 * w[4]
+    for name, (lo, hi) in (("C1", (-100, 100)), ("C4", (-100, 100))):
+        Qx = np.asarray(qi.make_config(name)["Q"])
+        assert Qx.min() >= lo and Qx.max() <= hi and np.array_equal(Qx, Qx.T)
