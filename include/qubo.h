@@ -1,0 +1,159 @@
+/*
+ * qubo.h -- C-ABI of the exhaustive dense-QUBO solver for AMD Instinct MI355X (gfx950).
+ *
+ * The solver minimises E(x) = sum_{i,j} Q_ij x_i x_j over all x in {0,1}^n for an
+ * int32 matrix Q (Maltsev, Remnev, Kapranov and Krivtsova, "Terastate-per-second
+ * QUBO Brute-Force on a Single GPU: A Matrix Prefix-Suffix Decomposition",
+ * sec. I), with the prefix-suffix decomposition of sec. II (eq. 4 and eq. 8), the
+ * Gray-code prefix walk of sec. III.B (eq. 9, Algorithm 2) and the parallel
+ * splits of sec. III.C.  Every call is exact: integer arithmetic throughout.
+ *
+ * Conventions shared by every entry point
+ *   - Q is a dense n x n int32 matrix, row-major and contiguous.  It need not be
+ *     symmetric: only Q_ij + Q_ji (i != j) and Q_ii enter E, so it is folded into
+ *     the upper triangle internally (sec. II.A uses an upper-triangular Q).
+ *   - A state is the index idx(x) = sum_i x_i 2^(n-1-i): variable 0 is the most
+ *     significant bit, the lexicographic row order of the state matrix U_N
+ *     (sec. II.B, Fig. 2).  Variable i of the minimiser is (argmin >> (n-1-i)) & 1.
+ *   - Overflow guard: the sum over all entries of |Q_ij| must not exceed
+ *     2^30 - 1.  Every energy, partial energy and table entry the solver forms is
+ *     a signed sub-sum of the folded matrix, and every comparison is between two
+ *     such sums, so int32 is then exact everywhere.  (The paper instead bounds
+ *     the spectrum with simulated annealing, sec. IV.B.5; this guard is exact.)
+ *   - Status codes: 0 on success, a negative QUBO_E* code otherwise.  On error
+ *     the output struct is left untouched.
+ *   - The library keeps no global mutable state except the per-device HIP
+ *     runtime; calls on different streams may run concurrently.
+ */
+#ifndef QUBO_H
+#define QUBO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef QUBO_API
+#define QUBO_API __attribute__((visibility("default")))
+#endif
+
+#define QUBO_OK 0
+#define QUBO_EINVAL (-1)  /* null pointer, n or a split parameter out of range */
+#define QUBO_ERANGE (-2)  /* sum |Q_ij| exceeds 2^30 - 1: int32 would not be exact */
+#define QUBO_EPLAN (-3)   /* the requested split does not fit the kernel's registers/LDS/limits */
+#define QUBO_EDEVICE (-4) /* no usable gfx950 device, or a HIP runtime error */
+#define QUBO_ENOMEM (-5)  /* device or host allocation failed */
+
+#define QUBO_MAX_N 63
+
+/* Result of a search (24 bytes). */
+typedef struct {
+    int32_t min_energy; /* min over the searched states of E(x) */
+    uint32_t reserved;  /* zero */
+    uint64_t argmin;    /* smallest state index attaining min_energy */
+    uint64_t count;     /* exact number of searched states attaining min_energy */
+} qubo_result;
+
+/* The decomposition the solver runs (sec. II.A partition sizes and the
+ * parallel split of sec. III.C), as chosen by the host planner. */
+typedef struct {
+    int32_t n;               /* variables as given */
+    int32_t n_search;        /* variables searched: n, or 5 for n < 5 (see qubo_search) */
+    int32_t prefix_bits;     /* A: prefix variables 0..A-1, walked in Gray order */
+    int32_t suffix_bits;     /* B = n_search - A: suffix variables, one per column bit */
+    int32_t cache_bits;      /* l: Gray bits whose M_int rows are cached on chip
+                                (the lowest reg_bits in VGPRs, the rest in LDS);
+                                rows of higher bits are read from L2/HBM.  The
+                                effective value: at most seg_bits */
+    int32_t reg_bits;        /* Gray bits whose rows live in VGPRs (5) */
+    int32_t cols_per_lane;   /* suffix columns held by one lane (16) */
+    int32_t wave_size;       /* 64 */
+    int32_t waves_per_block; /* waves of a workgroup, sharing one column group */
+    int32_t seg_bits;        /* each wave walks 2^seg_bits consecutive Gray steps per work unit */
+    int32_t blocks;          /* persistent workgroups launched */
+    int32_t lds_bytes;       /* LDS per workgroup for cached rows */
+    uint64_t col_groups;     /* groups of wave_size * cols_per_lane columns */
+    uint64_t work_units;     /* (column group, segment) pairs */
+    uint64_t workspace_bytes;/* device memory the search allocates */
+} qubo_plan;
+
+/* Host only; touches no device.  Plans a search of n variables.
+ *   prefix_bits: A in [5, n], or -1 to let the planner choose;
+ *   cache_bits:  l in [5, A], or -1 to let the planner choose.
+ * Planned for a 256-CU MI355X (qubo_search re-plans for the device it runs on).
+ * Returns QUBO_EINVAL for n outside [1, 63], or a split value outside the ranges
+ * above, and QUBO_EPLAN when the split exceeds the kernel's limits (prefix-energy
+ * table over 2^32 entries, M_int over 2^33 bytes, LDS over 64 KiB). */
+QUBO_API int qubo_make_plan(int n, int prefix_bits, int cache_bits, qubo_plan *out);
+
+/* Host only; touches no device.  Checks the overflow guard on a host copy of Q.
+ * Writes sum |Q_ij| (int64) to *abs_sum if abs_sum is not NULL.
+ * Returns QUBO_OK, QUBO_EINVAL or QUBO_ERANGE. */
+QUBO_API int qubo_check_q(const int32_t *Q_host, int n, int64_t *abs_sum);
+
+/* Exhaustive search over all 2^n states (sec. III.B Algorithm 2 with the
+ * splits of sec. III.C), on the HIP stream `stream` (a hipStream_t; NULL is the
+ * null stream) of the current device.
+ *   Q: device pointer, n x n int32, row-major; read only, owned by the caller.
+ *   n: 1..63.  For n < 5 the solver appends 5 - n dummy variables with
+ *      Q_ii = +1 and no couplings (they are 0 in every minimiser, so min, argmin
+ *      and count are those of the original problem).
+ *   prefix_bits, cache_bits: as for qubo_make_plan (-1 = planner's choice).  The
+ *      result does not depend on them.
+ *   out: host pointer; receives {min_energy, argmin, count}.
+ * The library allocates its workspace with hipMallocAsync on `stream` and frees
+ * it before returning; the call is blocking (it synchronises `stream`).
+ * Ties: argmin is the lowest index among all minimisers, count is exact. */
+QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bits, void *stream,
+                qubo_result *out);
+
+/* Per-stage device times of the last call on this host thread, from HIP events
+ * recorded on the call's stream around each stage.  Zero before any call. */
+typedef struct {
+    float build_ms;   /* cache-builder kernels: E_s, M_int, Gray-ordered E_p */
+    float search_ms;  /* the Gray-walk search kernel */
+    float reduce_ms;  /* the final min/argmin/count reduction */
+    float total_ms;   /* from the first upload to the result download */
+    uint64_t states;  /* states searched */
+    uint32_t slow_bodies; /* 32-step bodies re-walked on the exact path (records and ties) */
+    int32_t blocks;   /* workgroups launched */
+} qubo_timing;
+QUBO_API int qubo_last_timing(qubo_timing *out);
+
+/* Search a slice of the state space: every suffix of every prefix g(j) =
+ * j ^ (j >> 1) (as an A-bit number, variable 0 most significant) for
+ * gray_lo <= j < gray_hi, where A is the prefix size of the plan (prefix_bits
+ * must be given explicitly, 5 <= prefix_bits <= n).  gray_lo and gray_hi must be
+ * multiples of 32 with gray_lo < gray_hi <= 2^A.  The range [m 2^(A-k),
+ * (m+1) 2^(A-k)) is exactly the sub-cube whose first k variables spell g(m)
+ * (the straightforward split of sec. III.C.1).  n must be at least 5.  Same
+ * ownership, blocking and error behaviour as qubo_search; count may be 0 only
+ * if the slice is empty (it never is for valid arguments). */
+QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
+                      uint64_t gray_hi, void *stream, qubo_result *out);
+
+/* Builds the cache tables of a plan into caller-provided device buffers, for
+ * inspection (sec. III.A preprocessing steps 1-3, eq. 8):
+ *   Es:     2^B entries (int32): E_s(c), the energy of the suffix alone, c the
+ *           column index of the suffix (suffix variable A+i is bit B-1-i of c);
+ *   Mint:   A x 2^B entries (int32), row v = prefix variable v:
+ *           M_int[v][c] = sum_j U_{v,A+j} xs_j(c), the prefix-suffix interaction;
+ *   EpGray: 2^A entries (int32): E_p(g(j)), the energy of the prefix alone in
+ *           Gray order (sec. IV.B.3).
+ * U is Q folded to the upper triangle.  Requires n >= 5 and an explicit
+ * prefix_bits.  Blocking; same error codes as qubo_search. */
+QUBO_API int qubo_build_tables(const int32_t *Q, int n, int prefix_bits, int32_t *Es, int32_t *Mint,
+                      int32_t *EpGray, void *stream);
+
+/* Human-readable name of a status code; never NULL. */
+QUBO_API const char *qubo_strerror(int status);
+
+/* Library version and build target. */
+QUBO_API const char *qubo_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUBO_H */

@@ -1,0 +1,210 @@
+"""Exhaustive dense-QUBO search on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of the C-ABI in ``include/qubo.h`` (``lib/libqubo.so``).
+PyTorch supplies device memory and the current HIP stream; every step of the
+search runs in the library's HIP kernels.  The binding fails loudly when the
+library is missing: there is no CPU fallback.
+
+    import torch, ising_ground_state_amd as q
+    Q = torch.tensor(..., dtype=torch.int32, device="cuda")
+    r = q.search(Q)            # r.min_energy, r.argmin, r.count
+
+Method: Maltsev et al., "Terastate-per-second QUBO Brute-Force on a Single GPU:
+A Matrix Prefix-Suffix Decomposition" (prefix-suffix split, sec. II; Gray-code
+prefix walk, sec. III.B; parallel splits, sec. III.C).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libqubo.so")
+
+QUBO_OK = 0
+QUBO_EINVAL = -1
+QUBO_ERANGE = -2
+QUBO_EPLAN = -3
+QUBO_EDEVICE = -4
+QUBO_ENOMEM = -5
+MAX_N = 63
+
+
+class QuboError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        msg = "%s (status %d)" % (strerror(code) if _lib is not None else "qubo error", code)
+        super().__init__(what + ": " + msg if what else msg)
+
+
+class _Result(ctypes.Structure):
+    _fields_ = [("min_energy", ctypes.c_int32), ("reserved", ctypes.c_uint32),
+                ("argmin", ctypes.c_uint64), ("count", ctypes.c_uint64)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in
+                ("n", "n_search", "prefix_bits", "suffix_bits", "cache_bits", "reg_bits",
+                 "cols_per_lane", "wave_size", "waves_per_block", "seg_bits", "blocks", "lds_bytes")] + \
+               [(name, ctypes.c_uint64) for name in ("col_groups", "work_units", "workspace_bytes")]
+
+
+class _Timing(ctypes.Structure):
+    _fields_ = [("build_ms", ctypes.c_float), ("search_ms", ctypes.c_float),
+                ("reduce_ms", ctypes.c_float), ("total_ms", ctypes.c_float),
+                ("states", ctypes.c_uint64), ("slow_bodies", ctypes.c_uint32),
+                ("blocks", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Result:
+    min_energy: int
+    argmin: int
+    count: int
+
+    def triple(self) -> tuple[int, int, int]:
+        return (self.min_energy, self.argmin, self.count)
+
+    def bits(self, n: int) -> list[int]:
+        """The minimiser as a 0/1 list, variable 0 first."""
+        return [(self.argmin >> (n - 1 - i)) & 1 for i in range(n)]
+
+
+_lib = None
+
+EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range",
+           "qubo_build_tables", "qubo_last_timing", "qubo_strerror", "qubo_version")
+
+
+def load(path: str = LIB_PATH):
+    """Loads libqubo.so (built by ``python -m ising_ground_state_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libqubo.so not built: run `python -m ising_ground_state_amd.build` "
+                           "(the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(path)
+    i32p = ctypes.c_void_p
+    lib.qubo_make_plan.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(_Plan)]
+    lib.qubo_check_q.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
+    lib.qubo_search.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.POINTER(_Result)]
+    lib.qubo_search_range.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                      ctypes.c_uint64, ctypes.c_void_p, ctypes.POINTER(_Result)]
+    lib.qubo_build_tables.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    lib.qubo_last_timing.argtypes = [ctypes.POINTER(_Timing)]
+    lib.qubo_strerror.argtypes = [ctypes.c_int]
+    lib.qubo_strerror.restype = ctypes.c_char_p
+    lib.qubo_version.restype = ctypes.c_char_p
+    for name in EXPORTS[:6]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().qubo_strerror(code).decode()
+
+
+def version() -> str:
+    return load().qubo_version().decode()
+
+
+def _opt(v) -> int:
+    return -1 if v is None else int(v)
+
+
+def make_plan(n: int, prefix_bits: int | None = None, cache_bits: int | None = None) -> dict:
+    """Host-only plan of a search of n variables (no device needed)."""
+    p = _Plan()
+    rc = load().qubo_make_plan(int(n), _opt(prefix_bits), _opt(cache_bits), ctypes.byref(p))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_make_plan")
+    return {name: getattr(p, name) for name, _ in _Plan._fields_}
+
+
+def check_q(Q_host) -> int:
+    """Host-only overflow guard on a host int32 matrix; returns sum |Q_ij|."""
+    import numpy as np
+    q = np.ascontiguousarray(np.asarray(Q_host, dtype=np.int32))
+    if q.ndim != 2 or q.shape[0] != q.shape[1]:
+        raise ValueError("Q must be square")
+    s = ctypes.c_int64(0)
+    rc = load().qubo_check_q(q.ctypes.data_as(ctypes.c_void_p), q.shape[0], ctypes.byref(s))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_check_q")
+    return int(s.value)
+
+
+def _device_q(Q):
+    import torch
+    if not isinstance(Q, torch.Tensor) or not Q.is_cuda:
+        raise TypeError("Q must be a torch tensor on a HIP device")
+    if Q.dtype != torch.int32:
+        raise TypeError("Q must be int32")
+    if Q.dim() != 2 or Q.shape[0] != Q.shape[1]:
+        raise ValueError("Q must be square")
+    return Q.contiguous()
+
+
+def _stream(Q, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(Q.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def search(Q, prefix_bits: int | None = None, cache_bits: int | None = None, stream=None) -> Result:
+    """Exhaustive search of min_x x^T Q x over {0,1}^n on Q's device."""
+    import torch
+    Q = _device_q(Q)
+    r = _Result()
+    with torch.cuda.device(Q.device):
+        rc = load().qubo_search(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
+                                _opt(cache_bits), _stream(Q, stream), ctypes.byref(r))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_search")
+    return Result(r.min_energy, r.argmin, r.count)
+
+
+def search_range(Q, prefix_bits: int, gray_lo: int, gray_hi: int, cache_bits: int | None = None,
+                 stream=None) -> Result:
+    """Search the prefixes g(j), gray_lo <= j < gray_hi, with every suffix."""
+    import torch
+    Q = _device_q(Q)
+    r = _Result()
+    with torch.cuda.device(Q.device):
+        rc = load().qubo_search_range(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], int(prefix_bits),
+                                      _opt(cache_bits), int(gray_lo), int(gray_hi), _stream(Q, stream),
+                                      ctypes.byref(r))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_search_range")
+    return Result(r.min_energy, r.argmin, r.count)
+
+
+def build_tables(Q, prefix_bits: int, stream=None):
+    """The cache tables (E_s, M_int, Gray-ordered E_p) as int32 device tensors."""
+    import torch
+    Q = _device_q(Q)
+    n = Q.shape[0]
+    A, B = int(prefix_bits), n - int(prefix_bits)
+    es = torch.empty(1 << B, dtype=torch.int32, device=Q.device)
+    mint = torch.empty((A, 1 << B), dtype=torch.int32, device=Q.device)
+    ep = torch.empty(1 << A, dtype=torch.int32, device=Q.device)
+    with torch.cuda.device(Q.device):
+        rc = load().qubo_build_tables(ctypes.c_void_p(Q.data_ptr()), n, A, ctypes.c_void_p(es.data_ptr()),
+                                      ctypes.c_void_p(mint.data_ptr()), ctypes.c_void_p(ep.data_ptr()),
+                                      _stream(Q, stream))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_build_tables")
+    return es, mint, ep
+
+
+def last_timing() -> dict:
+    """Device times (ms) of the last search on this thread, from HIP events on its stream."""
+    t = _Timing()
+    load().qubo_last_timing(ctypes.byref(t))
+    return {name: getattr(t, name) for name, _ in _Timing._fields_}

@@ -1,0 +1,345 @@
+// C-ABI entry points of the QUBO search (declared in include/qubo.h).
+//
+// Orchestration of one search (Maltsev et al., "Terastate-per-second QUBO
+// Brute-Force on a Single GPU", sec. III, Algorithms 1-2 and sec. III.C):
+//   1. copy Q (n x n int32, at most 16 KiB) to the host, fold it into the upper
+//      triangle and check the overflow guard;
+//   2. plan the split (prefix A, suffix B, cached Gray bits, work units);
+//   3. one stream-ordered allocation for U, E_s, M_int, the Gray-ordered E_p,
+//      the per-wave partial results and a control block;
+//   4. cache builders, search kernel, final reduction, 64-byte result download;
+//   5. free and synchronise the stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+#include "plan.h"
+#include "qubo.h"
+
+namespace {
+
+thread_local qubo_timing g_timing{};
+
+struct DeviceInfo {
+    int num_cus = 0;
+};
+
+int device_info(DeviceInfo *info)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return QUBO_EDEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return QUBO_EDEVICE;
+    info->num_cus = prop.multiProcessorCount;
+    return QUBO_OK;
+}
+
+// Everything one call owns; released in the destructor on every path.
+struct Call {
+    hipStream_t stream = nullptr;
+    void *ws = nullptr;
+    hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    bool events = false;
+
+    ~Call()
+    {
+        if (ws) {
+            (void)hipFreeAsync(ws, stream);
+            (void)hipStreamSynchronize(stream);
+        }
+        if (events)
+            for (auto &e : ev)
+                if (e)
+                    (void)hipEventDestroy(e);
+    }
+};
+
+enum class Mode { Search, Build };
+
+struct Request {
+    const int32_t *Q = nullptr;
+    int n = 0;
+    int prefix_bits = -1;
+    int cache_bits = -1;
+    bool ranged = false;
+    uint64_t gray_lo = 0, gray_hi = 0;
+    hipStream_t stream = nullptr;
+    Mode mode = Mode::Search;
+    int32_t *es_out = nullptr, *mint_out = nullptr, *ep_out = nullptr;
+};
+
+int run(const Request &rq, qubo_result *out)
+{
+    using namespace qubo;
+    if (!rq.Q || rq.n < 1 || rq.n > QUBO_MAX_N)
+        return QUBO_EINVAL;
+    if (rq.mode == Mode::Search && !out)
+        return QUBO_EINVAL;
+    DeviceInfo dev;
+    int rc = device_info(&dev);
+    if (rc != QUBO_OK)
+        return rc;
+
+    Call call;
+    call.stream = rq.stream;
+    const int n = rq.n;
+
+    // 1. Q to the host; fold and guard.
+    std::vector<int32_t> Qh((size_t)n * n);
+    if (hipMemcpyAsync(Qh.data(), rq.Q, Qh.size() * 4, hipMemcpyDeviceToHost, rq.stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    std::vector<int32_t> U;
+    int64_t abs_sum = 0;
+    rc = fold_upper(Qh.data(), n, U, &abs_sum);
+    if (rc != QUBO_OK)
+        return rc;
+
+    // 2. Plan.
+    qubo_plan plan;
+    rc = make_plan(n, rq.prefix_bits, rq.cache_bits, dev.num_cus, &plan);
+    if (rc != QUBO_OK)
+        return rc;
+    const int ns = plan.n_search;
+    if (ns != n)
+        U = pad_upper(U, n, ns);
+    const int A = plan.prefix_bits, B = plan.suffix_bits;
+
+    // Work range in Gray steps and its segments.
+    uint64_t lo = 0, hi = 1ull << A;
+    if (rq.ranged) {
+        lo = rq.gray_lo;
+        hi = rq.gray_hi;
+    }
+    const uint64_t seg_first = lo >> plan.seg_bits;
+    const uint64_t seg_last = (hi - 1) >> plan.seg_bits;
+    const uint64_t segs = seg_last - seg_first + 1;
+    const uint64_t seg_blocks = (segs + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint64_t items = plan.col_groups * seg_blocks;
+
+    int per_cu = 0;
+    if (search_occupancy(&per_cu, plan.lds_bytes) != hipSuccess || per_cu < 1)
+        return QUBO_EDEVICE;
+    const uint64_t want_blocks = (uint64_t)dev.num_cus * (uint64_t)per_cu;
+    plan.blocks = (int)(items < want_blocks ? items : want_blocks);
+    const Layout L = layout_of(plan);
+
+    // 3. Workspace.
+    if (hipMallocAsync(&call.ws, L.total, rq.stream) != hipSuccess) {
+        call.ws = nullptr;
+        return QUBO_ENOMEM;
+    }
+    char *base = static_cast<char *>(call.ws);
+    int32_t *dU = reinterpret_cast<int32_t *>(base + L.off_u);
+    int32_t *des = reinterpret_cast<int32_t *>(base + L.off_es);
+    int32_t *dmint = reinterpret_cast<int32_t *>(base + L.off_mint);
+    int32_t *dep = reinterpret_cast<int32_t *>(base + L.off_ep);
+    Partial *dpart = reinterpret_cast<Partial *>(base + L.off_partials);
+    Ctrl *dctrl = reinterpret_cast<Ctrl *>(base + L.off_ctrl);
+
+    for (auto &e : call.ev)
+        if (hipEventCreate(&e) != hipSuccess)
+            return QUBO_EDEVICE;
+    call.events = true;
+
+    // 4. Upload, build, search, reduce.
+    if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (hipMemcpyAsync(dU, U.data(), U.size() * 4, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (launch_build_tables(dU, ns, A, B, L.cols_padded, des, dmint, dep, rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+
+    if (rq.mode == Mode::Build) {
+        const uint64_t cols = 1ull << B;
+        if (hipMemcpyAsync(rq.es_out, des, cols * 4, hipMemcpyDeviceToDevice, rq.stream) !=
+                hipSuccess ||
+            hipMemcpy2DAsync(rq.mint_out, cols * 4, dmint, L.cols_padded * 4, cols * 4, (size_t)A,
+                             hipMemcpyDeviceToDevice, rq.stream) != hipSuccess ||
+            hipMemcpyAsync(rq.ep_out, dep, (1ull << A) * 4, hipMemcpyDeviceToDevice, rq.stream) !=
+                hipSuccess)
+            return QUBO_EDEVICE;
+        if (hipStreamSynchronize(rq.stream) != hipSuccess)
+            return QUBO_EDEVICE;
+        return QUBO_OK;
+    }
+
+    // The first threshold must be a real energy of the searched set or an upper
+    // bound of all of them: E(0) = 0 when state 0 is searched, else sum |Q_ij|.
+    const int32_t t0 = (lo == 0) ? 0 : (int32_t)abs_sum;
+    if (launch_init_ctrl(dctrl, t0, rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+
+    SearchArgs sa{};
+    sa.es = des;
+    sa.mint = dmint;
+    sa.ep = dep;
+    sa.partials = dpart;
+    sa.ctrl = dctrl;
+    sa.cols_padded = L.cols_padded;
+    sa.gray_lo = lo;
+    sa.gray_hi = hi;
+    sa.seg_first = seg_first;
+    sa.segs = segs;
+    sa.seg_blocks = seg_blocks;
+    sa.items = items;
+    sa.A = A;
+    sa.B = B;
+    sa.l_eff = plan.cache_bits < plan.seg_bits ? plan.cache_bits : plan.seg_bits;
+    sa.seg_bits = plan.seg_bits;
+    if (launch_search(sa, plan.blocks, plan.lds_bytes, rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (hipEventRecord(call.ev[2], rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (launch_reduce(dpart, plan.blocks * plan.waves_per_block, dctrl, rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (hipEventRecord(call.ev[3], rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    Ctrl host_ctrl;
+    if (hipMemcpyAsync(&host_ctrl, dctrl, sizeof(Ctrl), hipMemcpyDeviceToHost, rq.stream) !=
+            hipSuccess ||
+        hipEventRecord(call.ev[4], rq.stream) != hipSuccess ||
+        hipStreamSynchronize(rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+
+    qubo_timing t{};
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, call.ev[0], call.ev[1]) == hipSuccess)
+        t.build_ms = ms;
+    if (hipEventElapsedTime(&ms, call.ev[1], call.ev[2]) == hipSuccess)
+        t.search_ms = ms;
+    if (hipEventElapsedTime(&ms, call.ev[2], call.ev[3]) == hipSuccess)
+        t.reduce_ms = ms;
+    if (hipEventElapsedTime(&ms, call.ev[0], call.ev[4]) == hipSuccess)
+        t.total_ms = ms;
+    t.states = (hi - lo) << B;
+    t.slow_bodies = host_ctrl.slow_total;
+    t.blocks = plan.blocks;
+    g_timing = t;
+
+    const Partial &r = host_ctrl.result;
+    if (r.count == 0)
+        return QUBO_EDEVICE;  // every valid search records at least one state
+    qubo_result res{};
+    res.min_energy = r.e;
+    res.reserved = 0;
+    res.argmin = r.arg >> (ns - n);  // padding variables are the lowest bits and 0 at the min
+    res.count = r.count;
+    *out = res;
+    return QUBO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+QUBO_API int qubo_make_plan(int n, int prefix_bits, int cache_bits, qubo_plan *out)
+{
+    // Host-only planning for a 256-CU MI355X.
+    return qubo::make_plan(n, prefix_bits, cache_bits, 256, out);
+}
+
+QUBO_API int qubo_check_q(const int32_t *Q_host, int n, int64_t *abs_sum)
+{
+    if (!Q_host || n < 1 || n > QUBO_MAX_N)
+        return QUBO_EINVAL;
+    std::vector<int32_t> U;
+    return qubo::fold_upper(Q_host, n, U, abs_sum);
+}
+
+QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bits, void *stream,
+                qubo_result *out)
+{
+    Request rq;
+    rq.Q = Q;
+    rq.n = n;
+    rq.prefix_bits = prefix_bits;
+    rq.cache_bits = cache_bits;
+    rq.stream = static_cast<hipStream_t>(stream);
+    return run(rq, out);
+}
+
+QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
+                      uint64_t gray_hi, void *stream, qubo_result *out)
+{
+    if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||
+        prefix_bits > qubo::kMaxPrefixBits)
+        return QUBO_EINVAL;
+    if ((gray_lo & 31u) || (gray_hi & 31u) || gray_lo >= gray_hi || gray_hi > (1ull << prefix_bits))
+        return QUBO_EINVAL;
+    Request rq;
+    rq.Q = Q;
+    rq.n = n;
+    rq.prefix_bits = prefix_bits;
+    rq.cache_bits = cache_bits;
+    rq.ranged = true;
+    rq.gray_lo = gray_lo;
+    rq.gray_hi = gray_hi;
+    rq.stream = static_cast<hipStream_t>(stream);
+    return run(rq, out);
+}
+
+QUBO_API int qubo_build_tables(const int32_t *Q, int n, int prefix_bits, int32_t *Es, int32_t *Mint,
+                      int32_t *EpGray, void *stream)
+{
+    if (!Es || !Mint || !EpGray)
+        return QUBO_EINVAL;
+    if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n)
+        return QUBO_EINVAL;
+    Request rq;
+    rq.Q = Q;
+    rq.n = n;
+    rq.prefix_bits = prefix_bits;
+    rq.stream = static_cast<hipStream_t>(stream);
+    rq.mode = Mode::Build;
+    rq.es_out = Es;
+    rq.mint_out = Mint;
+    rq.ep_out = EpGray;
+    return run(rq, nullptr);
+}
+
+QUBO_API int qubo_last_timing(qubo_timing *out)
+{
+    if (!out)
+        return QUBO_EINVAL;
+    *out = g_timing;
+    return QUBO_OK;
+}
+
+QUBO_API const char *qubo_strerror(int status)
+{
+    switch (status) {
+    case QUBO_OK:
+        return "ok";
+    case QUBO_EINVAL:
+        return "invalid argument";
+    case QUBO_ERANGE:
+        return "sum of |Q_ij| exceeds 2^30-1 (int32 search would not be exact)";
+    case QUBO_EPLAN:
+        return "split does not fit the kernel (prefix/cache bits out of the supported range)";
+    case QUBO_EDEVICE:
+        return "no usable gfx950 device or HIP runtime error";
+    case QUBO_ENOMEM:
+        return "out of device memory";
+    default:
+        return "unknown status";
+    }
+}
+
+QUBO_API const char *qubo_version(void)
+{
+    return "qubo-mi355x 0.1 (gfx950; 16 columns/lane, 5 register Gray bits, int32)";
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Device-side pieces of the QUBO search and their launchers (HIP, gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace qubo {
+
+// One wave's running result: 24 bytes, the partial-result record of the search.
+struct Partial {
+    int32_t e;        // min energy seen (INT32_MAX when count == 0)
+    uint32_t slow;    // bodies that took the exact (slow) path
+    uint64_t count;   // states attaining e
+    uint64_t arg;     // smallest index attaining e
+};
+
+struct Ctrl {
+    unsigned long long counter;  // next work item
+    int32_t gbest;               // best energy found by any wave so far (a real state's energy)
+    int32_t pad0;
+    uint64_t pad1[6];
+    Partial result;              // final reduction (offset 64)
+    uint32_t slow_total;
+    uint32_t pad2;
+};
+
+struct SearchArgs {
+    const int32_t *es;      // [cols_padded]       suffix energies E_s(c)
+    const int32_t *mint;    // [A][cols_padded]    M_int rows by prefix variable
+    const int32_t *ep;      // [2^A]               prefix energies in Gray order
+    Partial *partials;      // [gridDim.x * waves per block]
+    Ctrl *ctrl;
+    uint64_t cols_padded;
+    uint64_t gray_lo, gray_hi;  // Gray steps searched: [gray_lo, gray_hi)
+    uint64_t seg_first;         // first segment (2^seg_bits steps each) touching the range
+    uint64_t segs;              // segments touching the range
+    uint64_t seg_blocks;        // ceil(segs / waves per block)
+    uint64_t items;             // col_groups * seg_blocks
+    int32_t A, B;
+    int32_t l_eff;              // Gray bits with rows on chip (registers + LDS)
+    int32_t seg_bits;
+};
+
+// Cache builder (Maltsev et al., sec. III.A preprocessing, eq. 8): E_s, M_int
+// and the Gray-ordered prefix energies, from the folded upper-triangular U.
+hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
+                               int32_t *es, int32_t *mint, int32_t *ep, hipStream_t stream);
+
+// Resets the work counter and seeds the shared best with t0 (a real energy or an upper bound).
+hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, hipStream_t stream);
+
+hipError_t launch_search(const SearchArgs &args, int blocks, int lds_bytes, hipStream_t stream);
+
+// Resident workgroups of the search kernel per CU for a given dynamic LDS size.
+hipError_t search_occupancy(int *blocks_per_cu, int lds_bytes);
+
+hipError_t launch_reduce(const Partial *partials, int count, Ctrl *ctrl, hipStream_t stream);
+
+}  // namespace qubo

@@ -1,0 +1,531 @@
+// HIP kernels of the exhaustive QUBO search, written for CDNA4 (gfx950).
+//
+// Method: Maltsev, Remnev, Kapranov and Krivtsova, "Terastate-per-second QUBO
+// Brute-Force on a Single GPU: A Matrix Prefix-Suffix Decomposition".
+//   * sec. II, eq. 8: the energies of all states sharing a prefix x_p are
+//     E_p(x_p) + x_p M_int + E_s(U_B), with M_int = Q_ps U_B^T;
+//   * sec. III.B, eq. 9 and Algorithm 2: walking the prefixes in Gray order,
+//     one prefix bit k flips per step and the suffix-dependent vector moves by
+//     +-M_int[k,:], one integer add per state;
+//   * sec. III.C: suffix columns are split across lanes (column-wise split) and
+//     the prefix walk into segments (ranges of the Gray walk), with a final
+//     min-reduction over the units;
+//   * sec. IV.B.1-3: the rows of M_int and the suffix-dependent vector stay in
+//     registers, the prefix energies are read in Gray order.
+//
+// CDNA4 mapping of the search kernel:
+//   * a lane owns R = 16 suffix columns: c = g*1024 + r*64 + lane, so the lanes
+//     of a wave read consecutive dwords for each r (coalesced loads, conflict-free
+//     LDS reads);
+//   * the M_int rows of the 5 lowest Gray bits live in VGPRs (80 registers), the
+//     rows of the next Gray bits in LDS, shared by the 4 waves of a workgroup that
+//     work on the same column group, and the rest in L2/HBM;
+//   * the walk is unrolled over 32 Gray steps: every flip inside the body has a
+//     compile-time row and sign except the flip of bit 4, whose sign alternates
+//     between bodies (a uniform branch); the flip that leaves the body reads its
+//     row from LDS or global memory;
+//   * per step: 16 v_add/v_sub (one per state), a v_min3_i32 tree (8 VALU) and one
+//     v_cmp against the scalar threshold T - E_p(g(j)) (the prefix energy comes
+//     from a Gray-ordered table through scalar loads).  The comparison results are
+//     OR-ed over the body; a body with any hit is re-walked on an exact slow path
+//     that records every state with E <= T (lowest index and exact counts),
+//     then lowers T.
+//   * the threshold T is shared between waves through a global best-so-far, which
+//     is always a real state's energy, so no minimiser is ever skipped.
+#include "kernels.h"
+
+#include <climits>
+
+namespace qubo {
+
+constexpr int kR = 16;       // columns per lane
+constexpr int kU = 5;        // Gray bits with rows in VGPRs
+constexpr int kBody = 1 << kU;
+constexpr int kWaves = 4;    // waves per workgroup
+constexpr int kGroup = 64 * kR;
+
+__device__ __forceinline__ uint64_t gray(uint64_t i) { return i ^ (i >> 1); }
+
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+
+// Marks a value that is equal in every lane as wave-uniform (kept in SGPRs).
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int R>
+__device__ __forceinline__ int row_min(const int (&E)[R]);
+
+// Min of 16 values as a tree of 3-input mins (7 x v_min3_i32 + 1 x v_min_i32).
+template <>
+__device__ __forceinline__ int row_min<16>(const int (&E)[16])
+{
+    const int a = imin(imin(E[0], E[1]), E[2]);
+    const int b = imin(imin(E[3], E[4]), E[5]);
+    const int c = imin(imin(E[6], E[7]), E[8]);
+    const int d = imin(imin(E[9], E[10]), E[11]);
+    const int e = imin(imin(E[12], E[13]), E[14]);
+    const int f = imin(imin(a, b), c);
+    const int h = imin(imin(d, e), E[15]);
+    return imin(f, h);
+}
+
+template <int R>
+__device__ __forceinline__ void add_row(int (&E)[R], const int (&M)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        E[r] += M[r];
+}
+
+template <int R>
+__device__ __forceinline__ void sub_row(int (&E)[R], const int (&M)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        E[r] -= M[r];
+}
+
+// Combine rule for partial results over disjoint state sets.
+__device__ __forceinline__ void combine(int &e, uint64_t &cnt, uint64_t &arg, int e2, uint64_t c2,
+                                        uint64_t a2)
+{
+    if (c2 == 0)
+        return;
+    if (cnt == 0 || e2 < e) {
+        e = e2;
+        cnt = c2;
+        arg = a2;
+    } else if (e2 == e) {
+        cnt += c2;
+        arg = a2 < arg ? a2 : arg;
+    }
+}
+
+__device__ __forceinline__ int wave_min(int v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const int o = __shfl_xor(v, off, 64);
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ void wave_combine(int &e, uint64_t &cnt, uint64_t &arg)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const int e2 = __shfl_xor(e, off, 64);
+        const uint64_t c2 = __shfl_xor(cnt, off, 64);
+        const uint64_t a2 = __shfl_xor(arg, off, 64);
+        combine(e, cnt, arg, e2, c2, a2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Cache builders.
+// ---------------------------------------------------------------------------
+
+// One thread per suffix column c (suffix variable A+i is bit B-1-i of c):
+//   E_s[c]      = sum_{i <= j} U[A+i][A+j] xs_i xs_j            (eq. 8, E_s(U_B))
+//   M_int[v][c] = sum_j U[v][A+j] xs_j, v < A                   (M_int = Q_ps U_B^T)
+// Padding columns (c >= 2^B) get E_s = INT_MAX and zero rows, so they never
+// reach any threshold and stay constant under row updates.
+__global__ __launch_bounds__(256) void build_suffix_kernel(const int32_t *__restrict__ U, int ns,
+                                                           int A, int B, uint64_t cols_padded,
+                                                           int32_t *__restrict__ es,
+                                                           int32_t *__restrict__ mint)
+{
+    const uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= cols_padded)
+        return;
+    if (c >= (1ull << B)) {
+        es[c] = INT_MAX;
+        for (int v = 0; v < A; ++v)
+            mint[(uint64_t)v * cols_padded + c] = 0;
+        return;
+    }
+    int e = 0;
+    for (int i = 0; i < B; ++i) {
+        const int xi = (int)((c >> (B - 1 - i)) & 1u);
+        int rowsum = 0;
+        for (int j = i; j < B; ++j) {
+            const int xj = (int)((c >> (B - 1 - j)) & 1u);
+            rowsum += xj ? U[(A + i) * ns + (A + j)] : 0;
+        }
+        e += xi ? rowsum : 0;
+    }
+    es[c] = e;
+    for (int v = 0; v < A; ++v) {
+        int m = 0;
+        for (int j = 0; j < B; ++j) {
+            const int xj = (int)((c >> (B - 1 - j)) & 1u);
+            m += xj ? U[v * ns + (A + j)] : 0;
+        }
+        mint[(uint64_t)v * cols_padded + c] = m;
+    }
+}
+
+// Prefix energies in Gray order, ep[j] = E_p(g(j)) over the A prefix variables
+// (prefix variable v is bit A-1-v of the A-bit number).  A block covers 2^L
+// consecutive j (L = min(A, 8)); all of them share the high A-L bits of g(j),
+// which equal g(blockIdx.x).  Splitting x_p into high and low parts,
+//   E_p = E_hi + E_lo + sum_{v in lo, x_v = 1} K[v],   K[v] = sum_{w in hi, x_w = 1} U[w][v],
+// so each block evaluates E_hi and K once and each thread only its low part.
+__global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *__restrict__ U,
+                                                                int ns, int A, int L,
+                                                                int32_t *__restrict__ ep)
+{
+    __shared__ int K[8];
+    __shared__ int ehi_sh;
+    const int H = A - L;
+    const uint64_t hi = gray((uint64_t)blockIdx.x);  // high part of g(j), H bits
+    const int tid = threadIdx.x;
+    if (tid < L) {
+        const int v = H + tid;  // a low variable
+        int k = 0;
+        for (int w = 0; w < H; ++w)
+            k += ((hi >> (H - 1 - w)) & 1u) ? U[w * ns + v] : 0;
+        K[tid] = k;
+    } else if (tid == L) {
+        int e = 0;
+        for (int w = 0; w < H; ++w) {
+            if (!((hi >> (H - 1 - w)) & 1u))
+                continue;
+            for (int w2 = w; w2 < H; ++w2)
+                e += ((hi >> (H - 1 - w2)) & 1u) ? U[w * ns + w2] : 0;
+        }
+        ehi_sh = e;
+    }
+    __syncthreads();
+    const uint64_t j = ((uint64_t)blockIdx.x << L) | (uint64_t)tid;
+    const uint32_t lo = (uint32_t)(gray(j) & ((1u << L) - 1));
+    int e = ehi_sh;
+    for (int a = 0; a < L; ++a) {
+        if (!((lo >> (L - 1 - a)) & 1u))
+            continue;
+        e += K[a];
+        for (int b = a; b < L; ++b)
+            e += ((lo >> (L - 1 - b)) & 1u) ? U[(H + a) * ns + (H + b)] : 0;
+    }
+    ep[j] = e;
+}
+
+hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
+                               int32_t *es, int32_t *mint, int32_t *ep, hipStream_t stream)
+{
+    const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
+    hipLaunchKernelGGL(build_suffix_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
+                       cols_padded, es, mint);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int L = A < 8 ? A : 8;
+    const uint64_t blocks = 1ull << (A - L);
+    if (blocks > 0x7fffffffull)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(build_prefix_gray_kernel, dim3((unsigned)blocks), dim3(1u << L), 0, stream,
+                       U, ns, A, L, ep);
+    return hipGetLastError();
+}
+
+__global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0)
+{
+    ctrl->counter = 0;
+    ctrl->gbest = t0;
+    ctrl->slow_total = 0;
+}
+
+hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, hipStream_t stream)
+{
+    hipLaunchKernelGGL(init_ctrl_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The search.
+// ---------------------------------------------------------------------------
+
+struct LaneBest {
+    int e = INT_MAX;
+    uint64_t cnt = 0;
+    uint64_t arg = ~0ull;
+
+    __device__ __forceinline__ void record(int v, uint64_t idx)
+    {
+        if (v < e) {
+            e = v;
+            cnt = 1;
+            arg = idx;
+        } else if (v == e) {
+            cnt += 1;
+            arg = idx < arg ? idx : arg;
+        }
+    }
+};
+
+__device__ __forceinline__ int read_gbest(const Ctrl *ctrl)
+{
+    const int v = __hip_atomic_load(&ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Exact re-walk of one body of 32 Gray steps starting at `base`.  E holds the
+// state of the body's last step on entry and on exit.  Every state with
+// E_sd + E_p <= T is recorded per lane (E_sd <= T - E_p needs no overflow
+// headroom: both sides are sub-sums of the folded matrix).
+__device__ __forceinline__ void slow_body(int (&E)[kR], const int (&Mr)[kU][kR],
+                                                    uint64_t base, bool top_plus, int T,
+                                                    const int32_t *__restrict__ ep, int B,
+                                                    uint64_t col0, LaneBest &lb)
+{
+    if (top_plus)
+        sub_row(E, Mr[kU - 1]);
+    else
+        add_row(E, Mr[kU - 1]);
+#pragma unroll 1
+    for (int m = 0; m < kBody; ++m) {
+        const uint64_t j = base + (uint64_t)m;
+        const int epm = ep[j];
+        const int th = T - epm;
+        const uint64_t hi = gray(j) << B;
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+            if (E[r] <= th)
+                lb.record(E[r] + epm, hi | (col0 + (uint64_t)r * 64));
+        if (m + 1 < kBody) {
+            const int t = __builtin_ctz((unsigned)(m + 1));
+            const bool plus = (t < kU - 1) ? ((((m + 1) >> (t + 1)) & 1) == 0) : top_plus;
+#pragma unroll
+            for (int tt = 0; tt < kU; ++tt) {
+                if (tt == t) {
+                    if (plus)
+                        add_row(E, Mr[tt]);
+                    else
+                        sub_row(E, Mr[tt]);
+                }
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restrict__ es,
+                                                          const int32_t *__restrict__ mint,
+                                                          const int32_t *__restrict__ ep,
+                                                          Partial *__restrict__ partials,
+                                                          Ctrl *__restrict__ ctrl,
+                                                          const SearchArgs a)
+{
+    extern __shared__ int32_t lds_rows[];  // [l_eff - kU][kGroup]
+    __shared__ unsigned long long item_sh;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int A = a.A;
+    const uint64_t cp = a.cols_padded;
+
+    LaneBest lb;
+    uint32_t slow_bodies = 0;
+    int T = read_gbest(ctrl);
+    long long cur_g = -1;
+
+    for (;;) {
+        if (threadIdx.x == 0)
+            item_sh = atomicAdd(&ctrl->counter, 1ull);
+        __syncthreads();
+        const uint64_t item = uniform64(item_sh);
+        __syncthreads();
+        if (item >= a.items)
+            break;
+        const uint64_t g = item / a.seg_blocks;
+        const uint64_t sb = item - g * a.seg_blocks;
+        if ((long long)g != cur_g) {
+            const int rows = a.l_eff - kU;
+            for (int k = threadIdx.x; k < rows * kGroup; k += blockDim.x) {
+                const int t = kU + k / kGroup;
+                const int col = k % kGroup;
+                lds_rows[k] = mint[(uint64_t)(A - 1 - t) * cp + g * kGroup + col];
+            }
+            __syncthreads();
+            cur_g = (long long)g;
+        }
+        const uint64_t seg = a.seg_first + sb * kWaves + (uint64_t)wave;
+        if (seg >= a.seg_first + a.segs)
+            continue;
+        uint64_t j_begin = seg << a.seg_bits;
+        uint64_t j_end = (seg + 1) << a.seg_bits;
+        j_begin = j_begin > a.gray_lo ? j_begin : a.gray_lo;
+        j_end = j_end < a.gray_hi ? j_end : a.gray_hi;
+        if (j_begin >= j_end)
+            continue;
+
+        const uint64_t col0 = g * kGroup + (uint64_t)lane;  // column of register r is col0 + 64 r
+
+        // E_sd at the first prefix of the segment: E_s + sum of the rows of its set bits (eq. 8).
+        int E[kR];
+        {
+            const int32_t *src = es + col0;
+#pragma unroll
+            for (int r = 0; r < kR; ++r)
+                E[r] = src[r * 64];
+            uint64_t bits = gray(j_begin);
+            while (bits) {
+                const int t = __builtin_ctzll(bits);
+                bits &= bits - 1;
+                const int32_t *row = mint + (uint64_t)(A - 1 - t) * cp + col0;
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    E[r] += row[r * 64];
+            }
+        }
+        int Mr[kU][kR];
+#pragma unroll
+        for (int t = 0; t < kU; ++t) {
+            const int32_t *row = mint + (uint64_t)(A - 1 - t) * cp + col0;
+#pragma unroll
+            for (int r = 0; r < kR; ++r)
+                Mr[t][r] = row[r * 64];
+        }
+        {
+            const int gb = read_gbest(ctrl);
+            T = gb < T ? gb : T;
+        }
+
+        for (uint64_t base = j_begin; base < j_end; base += kBody) {
+            const int32_t *__restrict__ epb = ep + base;
+            const bool top_plus = ((base >> kU) & 1u) == 0;
+            uint64_t acc = 0;
+#pragma unroll
+            for (int m = 0; m < kBody; ++m) {
+                const int th = T - epb[m];
+                const int cm = row_min<kR>(E);
+                acc |= __builtin_amdgcn_ballot_w64(cm <= th);
+                if (m + 1 < kBody) {
+                    const int t = __builtin_ctz((unsigned)(m + 1));
+                    if (t < kU - 1) {
+                        if ((((m + 1) >> (t + 1)) & 1) == 0)
+                            add_row(E, Mr[t]);
+                        else
+                            sub_row(E, Mr[t]);
+                    } else {
+                        if (top_plus)
+                            add_row(E, Mr[kU - 1]);
+                        else
+                            sub_row(E, Mr[kU - 1]);
+                    }
+                }
+            }
+            if (acc) {
+                slow_body(E, Mr, base, top_plus, T, ep, a.B, col0, lb);
+                ++slow_bodies;
+                const int wm = __builtin_amdgcn_readfirstlane(wave_min(lb.e));
+                T = wm < T ? wm : T;
+                if (lane == 0)
+                    atomicMin(&ctrl->gbest, T);
+                const int gb = read_gbest(ctrl);
+                T = gb < T ? gb : T;
+            }
+            const uint64_t next = base + kBody;
+            if (next < j_end) {
+                // Flip of Gray bit t >= 5: its row comes from LDS or global memory.
+                const int t = __builtin_ctzll(next);
+                const bool plus = ((next >> (t + 1)) & 1u) == 0;
+                int row[kR];
+                if (t < a.l_eff) {
+                    const int32_t *src = lds_rows + (t - kU) * kGroup + lane;
+#pragma unroll
+                    for (int r = 0; r < kR; ++r)
+                        row[r] = src[r * 64];
+                } else {
+                    const int32_t *src = mint + (uint64_t)(A - 1 - t) * cp + col0;
+#pragma unroll
+                    for (int r = 0; r < kR; ++r)
+                        row[r] = src[r * 64];
+                }
+                if (plus)
+                    add_row(E, row);
+                else
+                    sub_row(E, row);
+            }
+        }
+    }
+
+    int e = lb.e;
+    uint64_t cnt = lb.cnt, arg = lb.arg;
+    wave_combine(e, cnt, arg);
+    if (lane == 0) {
+        Partial p;
+        p.e = e;
+        p.slow = slow_bodies;
+        p.count = cnt;
+        p.arg = arg;
+        partials[(uint64_t)blockIdx.x * kWaves + wave] = p;
+    }
+}
+
+hipError_t launch_search(const SearchArgs &args, int blocks, int lds_bytes, hipStream_t stream)
+{
+    hipLaunchKernelGGL(gray_search_kernel, dim3(blocks), dim3(64 * kWaves), lds_bytes, stream,
+                       args.es, args.mint, args.ep, args.partials, args.ctrl, args);
+    return hipGetLastError();
+}
+
+hipError_t search_occupancy(int *blocks_per_cu, int lds_bytes)
+{
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks_per_cu, reinterpret_cast<const void *>(gray_search_kernel), 64 * kWaves,
+        (size_t)lds_bytes);
+}
+
+// Final map-reduce step (sec. III.C): min energy, summed counts at the min,
+// lowest index at the min, over every wave's partial.
+__global__ __launch_bounds__(256) void reduce_kernel(const Partial *__restrict__ partials,
+                                                     int count, Ctrl *ctrl)
+{
+    __shared__ int se[4];
+    __shared__ uint64_t sc[4], sa[4];
+    __shared__ uint32_t ss[4];
+    int e = INT_MAX;
+    uint64_t cnt = 0, arg = ~0ull;
+    uint32_t slow = 0;
+    for (int k = threadIdx.x; k < count; k += blockDim.x) {
+        const Partial p = partials[k];
+        combine(e, cnt, arg, p.e, p.count, p.arg);
+        slow += p.slow;
+    }
+    wave_combine(e, cnt, arg);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        slow += __shfl_xor(slow, off, 64);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        se[w] = e;
+        sc[w] = cnt;
+        sa[w] = arg;
+        ss[w] = slow;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < (int)(blockDim.x >> 6); ++k) {
+            combine(e, cnt, arg, se[k], sc[k], sa[k]);
+            slow += ss[k];
+        }
+        ctrl->result.e = e;
+        ctrl->result.slow = 0;
+        ctrl->result.count = cnt;
+        ctrl->result.arg = arg;
+        ctrl->slow_total = slow;
+    }
+}
+
+hipError_t launch_reduce(const Partial *partials, int count, Ctrl *ctrl, hipStream_t stream)
+{
+    hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(256), 0, stream, partials, count, ctrl);
+    return hipGetLastError();
+}
+
+}  // namespace qubo

@@ -1,0 +1,163 @@
+// Host-side planning: fold, overflow guard, prefix/suffix split and cache size.
+//
+// The split follows Maltsev et al., "Terastate-per-second QUBO Brute-Force on a
+// Single GPU", sec. II.A (x = [x_p, x_s], A + B = N) and sec. III.C: suffix
+// columns are spread over lanes and workgroups (column-wise split, III.C.2) and
+// the Gray walk over the prefix is cut into segments handed to waves (a split
+// over ranges of the prefix walk, in the spirit of III.C.1).  The paper tunes
+// A and B empirically for the register file of its GPU (sec. IV.B.1); here the
+// register budget is fixed by the kernel's compile-time shape (16 columns and 5
+// cached rows per lane) and the planner only sizes tables and work units.
+#include "plan.h"
+
+#include <algorithm>
+#include <cstdlib>
+
+namespace qubo {
+
+int fold_upper(const int32_t *Q, int n, std::vector<int32_t> &U, int64_t *abs_sum)
+{
+    int64_t s = 0;
+    for (int64_t k = 0; k < (int64_t)n * n; ++k)
+        s += std::llabs((int64_t)Q[k]);
+    if (abs_sum)
+        *abs_sum = s;
+    if (s > kAbsSumLimit)
+        return QUBO_ERANGE;
+    U.assign((size_t)n * n, 0);
+    for (int i = 0; i < n; ++i) {
+        U[(size_t)i * n + i] = Q[(size_t)i * n + i];
+        for (int j = i + 1; j < n; ++j)
+            U[(size_t)i * n + j] = Q[(size_t)i * n + j] + Q[(size_t)j * n + i];
+    }
+    return QUBO_OK;
+}
+
+std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_search)
+{
+    std::vector<int32_t> P((size_t)n_search * n_search, 0);
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < n; ++j)
+            P[(size_t)i * n_search + j] = U[(size_t)i * n + j];
+    for (int i = n; i < n_search; ++i)
+        P[(size_t)i * n_search + i] = 1;
+    return P;
+}
+
+static int ceil_log2(uint64_t v)
+{
+    int k = 0;
+    while ((1ull << k) < v)
+        ++k;
+    return k;
+}
+
+static uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, qubo_plan *out)
+{
+    if (!out || n < 1 || n > QUBO_MAX_N || num_cus < 1)
+        return QUBO_EINVAL;
+    if (prefix_bits < -1 || prefix_bits > n)
+        return QUBO_EINVAL;
+    if (cache_bits < -1 || cache_bits > (prefix_bits >= 0 ? prefix_bits : n))
+        return QUBO_EINVAL;
+
+    qubo_plan p{};
+    p.n = n;
+    p.n_search = std::max(n, kMinSearchVars);
+    const int ns = p.n_search;
+
+    int A;
+    if (n < kMinSearchVars) {
+        A = ns;  // tiny problems: one fixed split over the padded variables
+    } else if (prefix_bits >= 0) {
+        A = prefix_bits;
+        if (A < kRegBits)
+            return QUBO_EPLAN;
+    } else {
+        // Aim for a 2^28-entry (1 GiB) prefix table and at least one full column group.
+        int B = std::max(std::min(ns - kRegBits, 10), ns - 28);
+        A = ns - B;
+        while (A < kMaxPrefixBits && (uint64_t)A * 4ull * (1ull << (ns - A)) > kMaxMintBytes)
+            ++A;
+    }
+    const int B = ns - A;
+    if (A > kMaxPrefixBits)
+        return QUBO_EPLAN;
+    const uint64_t cols = 1ull << B;
+    const uint64_t cols_padded = (cols + kColsPerGroup - 1) / kColsPerGroup * kColsPerGroup;
+    if ((uint64_t)A * 4ull * cols_padded > kMaxMintBytes)
+        return QUBO_EPLAN;
+
+    int l;
+    if (n < kMinSearchVars || cache_bits < 0)
+        l = std::min(A, 13);
+    else
+        l = cache_bits;
+    if (l < kRegBits)
+        return QUBO_EPLAN;
+
+    p.prefix_bits = A;
+    p.suffix_bits = B;
+    p.reg_bits = kRegBits;
+    p.cols_per_lane = kColsPerLane;
+    p.wave_size = kWave;
+    p.waves_per_block = kWavesPerBlock;
+    p.col_groups = cols_padded / kColsPerGroup;
+
+    // Segments: enough work units for ~8 per resident wave, each at least one
+    // unrolled body (2^5 steps) and at most 2^20 steps.
+    const uint64_t resident_waves = (uint64_t)num_cus * 4 * kWavesPerBlock;
+    const uint64_t target_units = 8 * resident_waves;
+    int split = 0;
+    if (target_units > p.col_groups)
+        split = ceil_log2((target_units + p.col_groups - 1) / p.col_groups);
+    int c = A - split;
+    c = std::max(c, kRegBits);
+    c = std::min(c, 20);
+    c = std::min(c, A);
+    p.seg_bits = c;
+
+    const int l_eff = std::min(l, c);
+    const int lds_rows = std::max(0, l_eff - kRegBits);
+    if (lds_rows > kMaxLdsRows)
+        return QUBO_EPLAN;
+    p.cache_bits = l_eff;  // bits above the segment length never flip inside a unit
+    p.lds_bytes = lds_rows * kColsPerGroup * 4;
+
+    const uint64_t segs = 1ull << (A - c);
+    p.work_units = p.col_groups * segs;
+    const uint64_t block_items = p.col_groups * ((segs + kWavesPerBlock - 1) / kWavesPerBlock);
+    // Two resident workgroups per CU (236 VGPRs per lane -> 2 waves per SIMD);
+    // the search re-sizes the grid from the runtime's occupancy query.
+    p.blocks = (int)std::min<uint64_t>((uint64_t)num_cus * 2, block_items);
+
+    p.workspace_bytes = layout_of(p).total;
+    *out = p;
+    return QUBO_OK;
+}
+
+Layout layout_of(const qubo_plan &p)
+{
+    Layout L{};
+    const uint64_t cols = 1ull << p.suffix_bits;
+    L.cols_padded = (cols + kColsPerGroup - 1) / kColsPerGroup * kColsPerGroup;
+    uint64_t off = 0;
+    L.off_u = off;
+    off = align256(off + (uint64_t)p.n_search * p.n_search * 4);
+    L.off_es = off;
+    off = align256(off + L.cols_padded * 4);
+    L.off_mint = off;
+    off = align256(off + (uint64_t)p.prefix_bits * L.cols_padded * 4);
+    L.off_ep = off;
+    off = align256(off + (1ull << p.prefix_bits) * 4);
+    L.off_partials = off;
+    off = align256(off + (uint64_t)p.blocks * p.waves_per_block * 24);
+    L.off_ctrl = off;
+    off = align256(off + 256);
+    L.total = off;
+    return L;
+}
+
+}  // namespace qubo

@@ -1,0 +1,45 @@
+// Host-side planning for the QUBO search: folding Q, the overflow guard and the
+// choice of the prefix/suffix split and cache size.  Pure C++, no HIP.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "qubo.h"
+
+namespace qubo {
+
+// Compile-time shape of the search kernel.
+constexpr int kRegBits = 5;        // Gray bits whose M_int rows live in VGPRs
+constexpr int kColsPerLane = 16;   // suffix columns per lane (R)
+constexpr int kWave = 64;          // CDNA wavefront
+constexpr int kWavesPerBlock = 4;  // one wave per SIMD of a CU
+constexpr int kColsPerGroup = kWave * kColsPerLane;  // 1024 columns per wave / workgroup
+constexpr int kMinSearchVars = kRegBits;             // n below this is padded
+constexpr int kMaxPrefixBits = 32;                   // prefix-energy table <= 2^32 entries
+constexpr int kMaxLdsRows = 16;                      // 64 KiB of cached rows per workgroup
+constexpr uint64_t kMaxMintBytes = 1ull << 33;       // 8 GiB
+
+constexpr int64_t kAbsSumLimit = (1ll << 30) - 1;
+
+// Folds a full n x n matrix into the upper triangle U (U_ii = Q_ii,
+// U_ij = Q_ij + Q_ji for i < j, 0 below), so x^T Q x = x^T U x, after checking
+// sum |Q_ij| <= 2^30 - 1.  Returns QUBO_OK or QUBO_ERANGE; writes the sum.
+int fold_upper(const int32_t *Q, int n, std::vector<int32_t> &U, int64_t *abs_sum);
+
+// Pads a folded n x n matrix to n_search >= n variables: the extra variables get
+// U_ii = +1 and no couplings, so they are 0 in every minimiser.
+std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_search);
+
+// Fills `out` for n variables on a device with `num_cus` compute units.
+int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, qubo_plan *out);
+
+// Device workspace layout of a plan (byte offsets, all 256-aligned).
+struct Layout {
+    uint64_t cols_padded;  // 2^B rounded up to a multiple of kColsPerGroup
+    uint64_t off_u, off_es, off_mint, off_ep, off_partials, off_ctrl;
+    uint64_t total;
+};
+Layout layout_of(const qubo_plan &p);
+
+}  // namespace qubo

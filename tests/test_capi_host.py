@@ -1,0 +1,114 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load on a machine without a GPU and export every symbol
+include/qubo.h declares; planning, the overflow guard and argument validation
+run on the host only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import ising_ground_state_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "qubo.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"QUBO_API\s+[\w\s\*]*?\b(qubo_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = q.load()
+    names = declared_symbols()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(q.EXPORTS)
+
+
+def test_version_and_strerror():
+    assert "gfx950" in q.version()
+    for code in (0, -1, -2, -3, -4, -5, -99):
+        assert q.strerror(code)
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 5, 6, 12, 24, 32, 40, 48, 50, 56, 58])
+def test_plan_invariants(n):
+    p = q.make_plan(n)
+    assert p["n"] == n and p["n_search"] == max(n, 5)
+    A, B = p["prefix_bits"], p["suffix_bits"]
+    assert A + B == p["n_search"] and A >= 5 and A <= 32
+    assert 5 <= p["cache_bits"] <= A
+    assert 5 <= p["seg_bits"] <= min(A, 20)
+    assert p["lds_bytes"] == max(0, min(p["cache_bits"], p["seg_bits"]) - 5) * 4096 <= 65536
+    assert p["col_groups"] == max(1, (1 << B) // 1024)
+    assert p["work_units"] == p["col_groups"] << (A - p["seg_bits"])
+    # the whole space is covered: units x steps x columns per group >= 2^n
+    assert p["work_units"] * (1 << p["seg_bits"]) * 1024 >= 1 << p["n_search"]
+    assert p["workspace_bytes"] >= 4 * ((1 << A) + A * max(1 << B, 1024))
+
+
+def test_plan_explicit_splits():
+    p = q.make_plan(48, prefix_bits=28, cache_bits=16)
+    assert (p["prefix_bits"], p["suffix_bits"], p["cache_bits"]) == (28, 20, 16)
+    assert p["lds_bytes"] == 11 * 4096
+    p = q.make_plan(48, prefix_bits=28, cache_bits=5)
+    assert p["lds_bytes"] == 0
+    # cached bits beyond one work unit's segment never flip there: the plan reports the effective value
+    p = q.make_plan(40, prefix_bits=30, cache_bits=22)
+    assert p["cache_bits"] == p["seg_bits"] <= 20
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, -1, -1), q.QUBO_EINVAL), ((64, -1, -1), q.QUBO_EINVAL),
+    ((10, 11, -1), q.QUBO_EINVAL), ((10, 8, 9), q.QUBO_EINVAL), ((10, -2, -1), q.QUBO_EINVAL),
+    ((10, 4, -1), q.QUBO_EPLAN), ((10, 8, 4), q.QUBO_EPLAN),
+    ((63, -1, -1), q.QUBO_EPLAN), ((40, 33, -1), q.QUBO_EPLAN),
+])
+def test_plan_rejects(args, code):
+    with pytest.raises(q.QuboError) as e:
+        q.make_plan(*args)
+    assert e.value.code == code
+
+
+def test_check_q_guard():
+    Q = np.zeros((3, 3), dtype=np.int32)
+    Q[0, 1] = 2 ** 29
+    Q[2, 0] = -(2 ** 29 - 1)
+    assert q.check_q(Q) == 2 ** 30 - 1
+    Q[1, 1] = 1
+    with pytest.raises(q.QuboError) as e:
+        q.check_q(Q)
+    assert e.value.code == q.QUBO_ERANGE
+    R = np.asarray([[3, -5], [1, 2]], dtype=np.int32)
+    assert q.check_q(R) == 11
+
+
+def test_null_and_range_arguments_rejected_before_the_device():
+    lib = q.load()
+    r = q._Result()
+    assert lib.qubo_search(None, 10, -1, -1, None, ctypes.byref(r)) == q.QUBO_EINVAL
+    assert lib.qubo_search(ctypes.c_void_p(16), 0, -1, -1, None, ctypes.byref(r)) == q.QUBO_EINVAL
+    assert lib.qubo_search(ctypes.c_void_p(16), 64, -1, -1, None, ctypes.byref(r)) == q.QUBO_EINVAL
+    assert lib.qubo_search(ctypes.c_void_p(16), 10, -1, -1, None, None) == q.QUBO_EINVAL
+    # slices must be 32-aligned, non-empty and inside the prefix walk
+    for lo, hi in [(0, 33), (1, 64), (64, 64), (0, 1 << 9), (32, 0)]:
+        assert lib.qubo_search_range(ctypes.c_void_p(16), 12, 8, -1, lo, hi, None,
+                                     ctypes.byref(r)) == q.QUBO_EINVAL
+    assert lib.qubo_search_range(ctypes.c_void_p(16), 4, 4, -1, 0, 32, None,
+                                 ctypes.byref(r)) == q.QUBO_EINVAL
+    assert lib.qubo_build_tables(ctypes.c_void_p(16), 12, 6, None, None, None, None) == q.QUBO_EINVAL
+    assert lib.qubo_check_q(None, 3, None) == q.QUBO_EINVAL
+    assert r.count == 0  # untouched
+
+
+def test_timing_struct_before_any_search():
+    t = q.last_timing()
+    assert set(t) >= {"build_ms", "search_ms", "reduce_ms", "total_ms", "states", "slow_bodies"}

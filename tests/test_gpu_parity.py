@@ -1,0 +1,222 @@
+"""Parity of the HIP search (through the C-ABI) with the CPU oracle.
+
+Integer work, so the bar is bit-exact: the same (min_energy, argmin, count) as
+the oracle on the same seeded inputs, for every split the library accepts.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import qubo_instances as qi
+from gpu_helpers import announce, dev_q, gray, inv_gray
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ising_ground_state_amd as lib
+    lib.load()
+    return lib
+
+
+def golden(name):
+    path = os.path.join(GOLDEN, name + ".json")
+    if not os.path.exists(path):
+        pytest.skip("stored oracle result %s.json not written yet" % name)
+    with open(path) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- cache builder
+
+@pytest.mark.parametrize("n,A", [(5, 5), (9, 5), (12, 7), (17, 9), (24, 14), (26, 20)])
+def test_tables_match_definition(q, n, A):
+    """E_s, M_int and the Gray-ordered E_p equal energies of states built from
+    the definition: E_s[c] = E(c), M_int[v][c] = E(e_v | c) - E(e_v) - E(c),
+    EpGray[j] = E(g(j) << B) (eq. 8 of the paper, evaluated by the oracle)."""
+    Q = qi.general_uniform(n, 5000 + n, -100, 100)
+    B = n - A
+    announce("tables", n, A)
+    es, mint, ep = q.build_tables(dev_q(Q), A)
+    es, mint, ep = es.cpu().numpy(), mint.cpu().numpy(), ep.cpu().numpy()
+    cols = np.arange(1 << B, dtype=np.uint64)
+    if cols.size > 4096:
+        cols = np.unique(np.concatenate([cols[:1024], cols[-1024:],
+                                         np.random.default_rng(n).choice(cols, 2048)]))
+    Ec = oracle.energies(Q, cols)
+    assert np.array_equal(es[cols.astype(np.int64)], Ec)
+    for v in range(A):
+        ev = np.uint64(1 << (n - 1 - v))
+        want = oracle.energies(Q, cols | ev) - Ec - oracle.energy(Q, int(ev))
+        assert np.array_equal(mint[v, cols.astype(np.int64)], want), v
+    js = np.arange(1 << A, dtype=np.uint64)
+    if js.size > 8192:
+        js = np.unique(np.concatenate([js[:2048], js[-2048:],
+                                       np.random.default_rng(A).choice(js, 4096)]))
+    states = (js ^ (js >> np.uint64(1))) << np.uint64(B)
+    assert np.array_equal(ep[js.astype(np.int64)], oracle.energies(Q, states))
+
+
+# ---------------------------------------------------------------- small instances
+
+SMALL = [(n, 6000 + n, -100, 100) for n in range(1, 21)] + \
+        [(n, 6100 + n, -2, 2) for n in (5, 9, 14, 18)] + \
+        [(n, 6200 + n, -1, 1) for n in (6, 11, 16)]
+
+
+@pytest.mark.parametrize("n,seed,lo,hi", SMALL)
+def test_small_random(q, n, seed, lo, hi):
+    """Non-symmetric Q, with and without heavy ties, against oracle tier B."""
+    Q = qi.general_uniform(n, seed, lo, hi)
+    want = oracle.search_gray(Q).triple()
+    announce("small", n, seed, lo, hi)
+    assert q.search(dev_q(Q)).triple() == want
+
+
+@pytest.mark.parametrize("n", [5, 11, 18, 22])
+def test_every_split(q, n):
+    """The result does not depend on the prefix/suffix split or the cache size
+    (permutation invariance, sec. II.D): every accepted split is exact."""
+    Q = qi.general_uniform(n, 6300 + n, -50, 50)
+    want = oracle.search_gray(Q).triple()
+    for A in range(5, n + 1):
+        for l in sorted({5, min(A, 7), min(A, 13), A} & set(range(5, min(A, 21) + 1))):
+            announce("split", n, A, l)
+            assert q.search(dev_q(Q), prefix_bits=A, cache_bits=l).triple() == want, (A, l)
+
+
+def test_special_cases(q):
+    for n in (3, 7, 16, 21):
+        zero = qi.zeros(n)
+        announce("zero", n)
+        assert q.search(dev_q(zero)).triple() == (0, 0, 1 << n)
+        diag = qi.zeros(n)
+        for i in range(n):
+            diag[i][i] = -(i + 1)
+        announce("negative diagonal", n)
+        assert q.search(dev_q(diag)).triple() == (-n * (n + 1) // 2, (1 << n) - 1, 1)
+        for i in range(n):
+            diag[i][i] = i + 1
+        announce("positive diagonal", n)
+        assert q.search(dev_q(diag)).triple() == (0, 0, 1)
+
+
+def test_planted_and_mattis(q):
+    for n, seed in [(9, 7001), (23, 7002), (30, 7003)]:
+        Q, P, a = qi.planted(n, seed)
+        av = np.asarray(a, dtype=np.int64)
+        want = (-int(av @ np.asarray(P, dtype=np.int64) @ av), qi.bits_to_index(a), 1)
+        announce("planted", n, seed)
+        assert q.search(dev_q(Q)).triple() == want
+    for n, seed in [(6, 7101), (25, 7102), (33, 7103)]:
+        J, h, xi = qi.mattis(n, seed)
+        Q, C = qi.ising_to_qubo(J, h)
+        xa = [(1 + s) // 2 for s in xi]
+        want_arg = min(qi.bits_to_index(xa), qi.bits_to_index([1 - v for v in xa]))
+        announce("mattis", n, seed)
+        r = q.search(dev_q(Q))
+        assert (r.min_energy + C, r.argmin, r.count) == (-n * (n - 1) // 2, want_arg, 2)
+
+
+def test_extreme_entries(q):
+    """Entries near the overflow guard: sum |Q_ij| just under 2^30."""
+    n = 12
+    big = (2 ** 30 - 1) // (n * n)
+    Q = qi.general_uniform(n, 7201, -big, big)
+    want = oracle.search_gray(Q).triple()
+    announce("extreme", n, big)
+    assert q.search(dev_q(Q)).triple() == want
+    assert q.search(dev_q(Q), prefix_bits=6, cache_bits=6).triple() == want
+
+
+# ---------------------------------------------------------------- configs
+
+@pytest.mark.parametrize("name,splits", [
+    ("C1", [(None, None), (14, 5), (19, 13), (10, 10), (24, 20)]),
+    ("C2", [(None, None), (22, 13), (16, 9), (26, 18)]),
+    ("C2p", [(None, None), (20, 12)]),
+    ("C3", [(None, None), (28, 13), (30, 16), (26, 8)]),
+])
+def test_config_vs_stored_oracle(q, name, splits):
+    g = golden(name)
+    cfg = qi.make_config(name)
+    assert qi.sha256_of(cfg["Q"]) == g["sha256_Q"]
+    want = (g["min_energy"], g["argmin"], g["count"])
+    Qd = dev_q(cfg["Q"])
+    for A, l in splits:
+        announce("config", name, A, l)
+        assert q.search(Qd, prefix_bits=A, cache_bits=l).triple() == want, (A, l)
+
+
+# ---------------------------------------------------------------- slices
+
+@pytest.mark.parametrize("n,A,k", [(20, 12, 3), (24, 14, 6), (28, 20, 4)])
+def test_range_is_subcube(q, n, A, k):
+    """The Gray range [m 2^(A-k), (m+1) 2^(A-k)) is the sub-cube whose first k
+    variables spell g(m) (sec. III.C.1); compare with oracle tier B on it."""
+    Q = qi.general_uniform(n, 7300 + n, -100, 100)
+    for m in (0, 1, (1 << k) - 1, (1 << k) // 3):
+        lo, hi = m << (A - k), (m + 1) << (A - k)
+        want = oracle.search_gray(Q, k=k, top=gray(m)).triple()
+        announce("range", n, A, k, m)
+        assert q.search_range(dev_q(Q), A, lo, hi).triple() == want
+
+
+def test_subcubes_at_full_size(q):
+    """n = 48 and n = 50 at the benchmark's split: seeded sub-cubes of 2^32
+    states against the stored oracle results (tests/golden/C4sub, C5sub)."""
+    for name in ("C4sub", "C5sub"):
+        g = golden(name)
+        cfg = qi.make_config(name[:-3])
+        assert qi.sha256_of(cfg["Q"]) == g["sha256_Q"]
+        n = cfg["n"]
+        plan = q.make_plan(n)
+        A = plan["prefix_bits"]
+        Qd = dev_q(cfg["Q"])
+        for cube in g["cubes"][:6]:
+            k, top = cube["k"], cube["top"]
+            m = inv_gray(top)
+            lo, hi = m << (A - k), (m + 1) << (A - k)
+            announce("subcube", name, k, top)
+            r = q.search_range(Qd, A, lo, hi)
+            assert r.triple() == (cube["min_energy"], cube["argmin"], cube["count"])
+
+
+def test_deterministic(q):
+    Q = qi.make_config("C2")["Q"]
+    Qd = dev_q(Q)
+    announce("determinism C2")
+    first = q.search(Qd).triple()
+    for _ in range(3):
+        assert q.search(Qd).triple() == first
+
+
+def test_errors(q):
+    Qd = dev_q(qi.general_uniform(10, 7400, -5, 5))
+    with pytest.raises(q.QuboError) as e:
+        q.search(Qd, prefix_bits=3)
+    assert e.value.code == q.QUBO_EPLAN
+    with pytest.raises(q.QuboError) as e:
+        q.search(Qd, prefix_bits=11)
+    assert e.value.code == q.QUBO_EINVAL
+    with pytest.raises(q.QuboError) as e:
+        q.search(Qd, prefix_bits=8, cache_bits=9)
+    assert e.value.code == q.QUBO_EINVAL
+    with pytest.raises(q.QuboError) as e:
+        q.search_range(Qd, 8, 0, 33)
+    assert e.value.code == q.QUBO_EINVAL
+    big = dev_q([[2 ** 30, 0], [0, 0]])
+    with pytest.raises(q.QuboError) as e:
+        q.search(big)
+    assert e.value.code == q.QUBO_ERANGE
