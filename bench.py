@@ -1,0 +1,187 @@
+"""Benchmark: exhaustive search of the dense n=48 int32 QUBO on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C4] [--no-cpu]
+
+One step is one full qubo_search call on the 2^48-state workload (fold, plan,
+cache builders, Gray-walk search, reduction, result download) with Q already
+resident in HBM.  Prints one JSON line with states/s, the search kernel's
+roofline position (int32 VALU) and the CPU oracle timed on a bounded slice of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "states/sec (×10^12) on dense n=48 int32 QUBO, 1 MI355X; % of int32 VALU peak"
+
+# MI355X int32 vector peak: 256 CUs x 64 lanes per clock (4 SIMD x 16 lanes) x 2.4 GHz.
+CUS, LANES_PER_CU, CLOCK_HZ = 256, 64, 2.4e9
+INT32_VALU_PEAK = CUS * LANES_PER_CU * CLOCK_HZ  # 3.93e13 lane-ops/s
+
+# Algorithmic work per state: one int32 add (eq. 9 of the paper; "one arithmetic
+# operation per state").  The kernel's instruction count per state is larger
+# (16 adds + 8 min + 1 compare per 16 states); both are reported.
+OPS_PER_STATE = 1
+OPS_PER_STATE_ADD_CMP = 2
+VALU_INSTR_PER_STATE = 25 / 16
+
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gray_search_strict_n48_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "ising_ground_state_amd", "csrc", "kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per search launch from committed rocprofv3 counter runs, or None
+    when they are missing or the kernel source changed since they were taken."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, seconds_budget=20.0):
+    """The CPU oracle (tier B, Gray walk) as it stands, on a seeded sub-cube of the
+    same workload: the first k variables fixed (seed 4242), 2^(n-k) states."""
+    import oracle
+    import qubo_instances as qi
+
+    n = cfg["n"]
+    threads = min(16, oracle.default_threads())
+    free = 35 if threads >= 12 else 33
+    k = n - free
+    rng = qi.SplitMix64(4242 + n)
+    top = rng.uniform_int(0, (1 << k) - 1)
+    t0 = time.perf_counter()
+    r = oracle.search_gray(cfg["Q"], k=k, top=top, threads=threads)
+    dt = time.perf_counter() - t0
+    states = 1 << free
+    return {"value": states / dt / 1e12, "unit": "1e12 states/s", "cores": threads, "kind": "oracle",
+            "sample": "tier-B Gray walk over the sub-cube of 2^%d states with the first %d variables "
+                      "fixed to %d (seed %d); %.2f s wall" % (free, k, top, 4242 + n, dt),
+            "states": states, "seconds": dt, "subcube_result": list(r.triple())}
+
+
+def copy_calibration(mib: int):
+    """A plain copy kernel of known size: reads and writes mib MiB once each."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": mib << 20, "copy_calibration_bytes_written": mib << 20}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="C4")
+    ap.add_argument("--prefix-bits", type=int, default=None)
+    ap.add_argument("--cache-bits", type=int, default=None)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (for scaling HBM counters)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the search shards by work unit; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ising_ground_state_amd as q
+    import qubo_instances as qi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    q.load()
+    cfg = qi.make_config(args.config)
+    n = cfg["n"]
+    Qd = torch.tensor(cfg["Q"], dtype=torch.int32, device="cuda:0")
+    plan = q.make_plan(n, args.prefix_bits, args.cache_bits)
+    states = 1 << n
+
+    for _ in range(args.warmup):
+        q.search(Qd, args.prefix_bits, args.cache_bits)
+        print("[bench] warmup", q.last_timing(), file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    kernel_ms, timings, result = [], [], None
+    for k in range(args.steps):
+        result = q.search(Qd, args.prefix_bits, args.cache_bits)
+        t = q.last_timing()
+        timings.append(t)
+        kernel_ms.append(t["search_ms"])
+        print("[bench] step", k, t, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = states * args.steps / elapsed / 1e12
+    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    achieved = OPS_PER_STATE * states / avg_kernel_s
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "1e12 states/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": cfg["desc"] + ", seed %d, 2^%d states per step" % (cfg["seed"], n),
+                   "name": args.config, "n": n, "states_per_step": states,
+                   "prefix_bits": plan["prefix_bits"], "suffix_bits": plan["suffix_bits"],
+                   "cache_bits": plan["cache_bits"], "seg_bits": plan["seg_bits"],
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "alu",
+            "kernel": "gray_search_kernel",
+            "achieved": achieved / 1e12,
+            "peak": INT32_VALU_PEAK / 1e12,
+            "unit": "int32 Tops/s",
+            "frac": achieved / INT32_VALU_PEAK,
+            "traffic": measured_traffic(),
+            "ops_per_state": OPS_PER_STATE,
+            "frac_add_and_compare": OPS_PER_STATE_ADD_CMP * states / avg_kernel_s / INT32_VALU_PEAK,
+            "valu_issue_frac_at_2p4ghz": VALU_INSTR_PER_STATE * states / avg_kernel_s / INT32_VALU_PEAK,
+            "kernel_ms_avg": avg_kernel_s * 1e3,
+            "kernel_timing": "HIP events recorded on the search stream around the kernel launch",
+        },
+        "pct_int32_valu_peak": 100.0 * value * 1e12 / INT32_VALU_PEAK,
+        "result": {"min_energy": result.min_energy, "argmin": result.argmin, "count": result.count},
+        "build_ms_avg": sum(t["build_ms"] for t in timings) / len(timings),
+        "slow_bodies": timings[-1]["slow_bodies"],
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
