@@ -108,16 +108,22 @@ QUBO_API int qubo_check_q(const int32_t *Q_host, int n, int64_t *abs_sum);
 QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bits, void *stream,
                 qubo_result *out);
 
-/* Per-stage device times of the last call on this host thread, from HIP events
- * recorded on the call's stream around each stage.  Zero before any call. */
+/* Per-stage device times and coverage counters of the last search on this host
+ * thread; times come from HIP events recorded on the call's stream around each
+ * stage.  Zero before any call. */
 typedef struct {
     float build_ms;   /* cache-builder kernels: E_s, M_int, Gray-ordered E_p */
     float search_ms;  /* the Gray-walk search kernel */
     float reduce_ms;  /* the final min/argmin/count reduction */
     float total_ms;   /* from the first upload to the result download */
     uint64_t states;  /* states searched */
-    uint32_t slow_bodies; /* 32-step bodies re-walked on the exact path (records and ties) */
     int32_t blocks;   /* workgroups launched */
+    uint32_t reserved;
+    uint64_t bodies;  /* 32-step bodies walked, each over 1024 suffix columns (coverage:
+                         bodies x 32 x 1024 = states, padding columns included, when
+                         2^B >= 1024) */
+    uint64_t checked_bodies; /* bodies that ran the per-step minimum (all of them in strict mode) */
+    uint64_t slow_bodies;    /* bodies re-walked on the exact path (records and ties) */
 } qubo_timing;
 QUBO_API int qubo_last_timing(qubo_timing *out);
 
@@ -132,6 +138,21 @@ QUBO_API int qubo_last_timing(qubo_timing *out);
  * if the slice is empty (it never is for valid arguments). */
 QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
                       uint64_t gray_hi, void *stream, qubo_result *out);
+
+/* Search with options.  gray_lo = gray_hi = 0 searches the whole space (as
+ * qubo_search); any other pair selects a slice exactly as qubo_search_range.
+ * flags: 0, or QUBO_FLAG_STRICT_MIN to take the minimum over every prefix's
+ * suffix vector after every Gray step, as Algorithm 2 does.  By default the
+ * kernel first bounds, for each block of 32 consecutive Gray steps, the lowest
+ * energy any of its states can have (its suffix-dependent energies can fall by
+ * at most the sum of the negative parts of the 5 row updates it applies, and its
+ * prefix energies are at least their minimum over the block); blocks whose bound
+ * exceeds the best energy found so far apply only the row updates (one add per
+ * state).  Both modes return identical results; other flag bits are rejected
+ * with QUBO_EINVAL. */
+#define QUBO_FLAG_STRICT_MIN 1u
+QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
+                            uint64_t gray_hi, uint32_t flags, void *stream, qubo_result *out);
 
 /* Builds the cache tables of a plan into caller-provided device buffers, for
  * inspection (sec. III.A preprocessing steps 1-3, eq. 8):

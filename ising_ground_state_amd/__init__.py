@@ -53,8 +53,9 @@ class _Plan(ctypes.Structure):
 class _Timing(ctypes.Structure):
     _fields_ = [("build_ms", ctypes.c_float), ("search_ms", ctypes.c_float),
                 ("reduce_ms", ctypes.c_float), ("total_ms", ctypes.c_float),
-                ("states", ctypes.c_uint64), ("slow_bodies", ctypes.c_uint32),
-                ("blocks", ctypes.c_int32)]
+                ("states", ctypes.c_uint64), ("blocks", ctypes.c_int32), ("reserved", ctypes.c_uint32),
+                ("bodies", ctypes.c_uint64), ("checked_bodies", ctypes.c_uint64),
+                ("slow_bodies", ctypes.c_uint64)]
 
 
 @dataclass(frozen=True)
@@ -73,8 +74,9 @@ class Result:
 
 _lib = None
 
-EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range",
+EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range", "qubo_search_ex",
            "qubo_build_tables", "qubo_last_timing", "qubo_strerror", "qubo_version")
+FLAG_STRICT_MIN = 1
 
 
 def load(path: str = LIB_PATH):
@@ -93,13 +95,15 @@ def load(path: str = LIB_PATH):
                                 ctypes.POINTER(_Result)]
     lib.qubo_search_range.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
                                       ctypes.c_uint64, ctypes.c_void_p, ctypes.POINTER(_Result)]
+    lib.qubo_search_ex.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                   ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.POINTER(_Result)]
     lib.qubo_build_tables.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p]
     lib.qubo_last_timing.argtypes = [ctypes.POINTER(_Timing)]
     lib.qubo_strerror.argtypes = [ctypes.c_int]
     lib.qubo_strerror.restype = ctypes.c_char_p
     lib.qubo_version.restype = ctypes.c_char_p
-    for name in EXPORTS[:6]:
+    for name in EXPORTS[:7]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -157,29 +161,38 @@ def _stream(Q, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def search(Q, prefix_bits: int | None = None, cache_bits: int | None = None, stream=None) -> Result:
-    """Exhaustive search of min_x x^T Q x over {0,1}^n on Q's device."""
+def search(Q, prefix_bits: int | None = None, cache_bits: int | None = None, stream=None,
+           strict: bool = False) -> Result:
+    """Exhaustive search of min_x x^T Q x over {0,1}^n on Q's device.
+
+    strict=True takes the minimum after every prefix (Algorithm 2 as printed)
+    instead of gating it by the per-block lower bound; the result is the same."""
     import torch
     Q = _device_q(Q)
     r = _Result()
     with torch.cuda.device(Q.device):
-        rc = load().qubo_search(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
-                                _opt(cache_bits), _stream(Q, stream), ctypes.byref(r))
+        if strict:
+            rc = load().qubo_search_ex(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
+                                       _opt(cache_bits), 0, 0, FLAG_STRICT_MIN, _stream(Q, stream),
+                                       ctypes.byref(r))
+        else:
+            rc = load().qubo_search(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
+                                    _opt(cache_bits), _stream(Q, stream), ctypes.byref(r))
     if rc != QUBO_OK:
         raise QuboError(rc, "qubo_search")
     return Result(r.min_energy, r.argmin, r.count)
 
 
 def search_range(Q, prefix_bits: int, gray_lo: int, gray_hi: int, cache_bits: int | None = None,
-                 stream=None) -> Result:
+                 stream=None, strict: bool = False) -> Result:
     """Search the prefixes g(j), gray_lo <= j < gray_hi, with every suffix."""
     import torch
     Q = _device_q(Q)
     r = _Result()
     with torch.cuda.device(Q.device):
-        rc = load().qubo_search_range(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], int(prefix_bits),
-                                      _opt(cache_bits), int(gray_lo), int(gray_hi), _stream(Q, stream),
-                                      ctypes.byref(r))
+        rc = load().qubo_search_ex(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], int(prefix_bits),
+                                   _opt(cache_bits), int(gray_lo), int(gray_hi),
+                                   FLAG_STRICT_MIN if strict else 0, _stream(Q, stream), ctypes.byref(r))
     if rc != QUBO_OK:
         raise QuboError(rc, "qubo_search_range")
     return Result(r.min_energy, r.argmin, r.count)

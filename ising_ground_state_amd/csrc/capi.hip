@@ -73,6 +73,7 @@ struct Request {
     uint64_t gray_lo = 0, gray_hi = 0;
     hipStream_t stream = nullptr;
     Mode mode = Mode::Search;
+    bool gated = true;
     int32_t *es_out = nullptr, *mint_out = nullptr, *ep_out = nullptr;
 };
 
@@ -127,7 +128,7 @@ int run(const Request &rq, qubo_result *out)
     const uint64_t items = plan.col_groups * seg_blocks;
 
     int per_cu = 0;
-    if (search_occupancy(&per_cu, plan.lds_bytes) != hipSuccess || per_cu < 1)
+    if (search_occupancy(rq.gated, &per_cu, plan.lds_bytes) != hipSuccess || per_cu < 1)
         return QUBO_EDEVICE;
     const uint64_t want_blocks = (uint64_t)dev.num_cus * (uint64_t)per_cu;
     plan.blocks = (int)(items < want_blocks ? items : want_blocks);
@@ -143,6 +144,7 @@ int run(const Request &rq, qubo_result *out)
     int32_t *des = reinterpret_cast<int32_t *>(base + L.off_es);
     int32_t *dmint = reinterpret_cast<int32_t *>(base + L.off_mint);
     int32_t *dep = reinterpret_cast<int32_t *>(base + L.off_ep);
+    int32_t *depmin = reinterpret_cast<int32_t *>(base + L.off_epmin);
     Partial *dpart = reinterpret_cast<Partial *>(base + L.off_partials);
     Ctrl *dctrl = reinterpret_cast<Ctrl *>(base + L.off_ctrl);
 
@@ -156,7 +158,8 @@ int run(const Request &rq, qubo_result *out)
         return QUBO_EDEVICE;
     if (hipMemcpyAsync(dU, U.data(), U.size() * 4, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
-    if (launch_build_tables(dU, ns, A, B, L.cols_padded, des, dmint, dep, rq.stream) != hipSuccess)
+    if (launch_build_tables(dU, ns, A, B, L.cols_padded, des, dmint, dep, depmin, rq.stream) !=
+        hipSuccess)
         return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
@@ -185,6 +188,7 @@ int run(const Request &rq, qubo_result *out)
     sa.es = des;
     sa.mint = dmint;
     sa.ep = dep;
+    sa.epmin = depmin;
     sa.partials = dpart;
     sa.ctrl = dctrl;
     sa.cols_padded = L.cols_padded;
@@ -198,7 +202,7 @@ int run(const Request &rq, qubo_result *out)
     sa.B = B;
     sa.l_eff = plan.cache_bits < plan.seg_bits ? plan.cache_bits : plan.seg_bits;
     sa.seg_bits = plan.seg_bits;
-    if (launch_search(sa, plan.blocks, plan.lds_bytes, rq.stream) != hipSuccess)
+    if (launch_search(sa, rq.gated, plan.blocks, plan.lds_bytes, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[2], rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
@@ -225,6 +229,8 @@ int run(const Request &rq, qubo_result *out)
         t.total_ms = ms;
     t.states = (hi - lo) << B;
     t.slow_bodies = host_ctrl.slow_total;
+    t.bodies = host_ctrl.bodies_total;
+    t.checked_bodies = host_ctrl.checked_total;
     t.blocks = plan.blocks;
     g_timing = t;
 
@@ -270,24 +276,38 @@ QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bit
     return run(rq, out);
 }
 
-QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
-                      uint64_t gray_hi, void *stream, qubo_result *out)
+QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
+                           uint64_t gray_hi, uint32_t flags, void *stream, qubo_result *out)
 {
-    if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||
-        prefix_bits > qubo::kMaxPrefixBits)
-        return QUBO_EINVAL;
-    if ((gray_lo & 31u) || (gray_hi & 31u) || gray_lo >= gray_hi || gray_hi > (1ull << prefix_bits))
+    if (flags & ~(uint32_t)QUBO_FLAG_STRICT_MIN)
         return QUBO_EINVAL;
     Request rq;
     rq.Q = Q;
     rq.n = n;
     rq.prefix_bits = prefix_bits;
     rq.cache_bits = cache_bits;
-    rq.ranged = true;
-    rq.gray_lo = gray_lo;
-    rq.gray_hi = gray_hi;
+    rq.gated = !(flags & QUBO_FLAG_STRICT_MIN);
     rq.stream = static_cast<hipStream_t>(stream);
+    if (gray_lo != 0 || gray_hi != 0) {
+        if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||
+            prefix_bits > qubo::kMaxPrefixBits)
+            return QUBO_EINVAL;
+        if ((gray_lo & 31u) || (gray_hi & 31u) || gray_lo >= gray_hi ||
+            gray_hi > (1ull << prefix_bits))
+            return QUBO_EINVAL;
+        rq.ranged = true;
+        rq.gray_lo = gray_lo;
+        rq.gray_hi = gray_hi;
+    }
     return run(rq, out);
+}
+
+QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
+                      uint64_t gray_hi, void *stream, qubo_result *out)
+{
+    if (gray_lo == 0 && gray_hi == 0)
+        return QUBO_EINVAL;
+    return qubo_search_ex(Q, n, prefix_bits, cache_bits, gray_lo, gray_hi, 0u, stream, out);
 }
 
 QUBO_API int qubo_build_tables(const int32_t *Q, int n, int prefix_bits, int32_t *Es, int32_t *Mint,

@@ -7,12 +7,14 @@
 
 namespace qubo {
 
-// One wave's running result: 24 bytes, the partial-result record of the search.
+// One wave's partial result (32 bytes) with its coverage counters.
 struct Partial {
-    int32_t e;        // min energy seen (INT32_MAX when count == 0)
-    uint32_t slow;    // bodies that took the exact (slow) path
-    uint64_t count;   // states attaining e
-    uint64_t arg;     // smallest index attaining e
+    int32_t e;         // min energy seen (INT32_MAX when count == 0)
+    uint32_t slow;     // bodies re-walked on the exact path (records and ties)
+    uint64_t count;    // states attaining e
+    uint64_t arg;      // smallest index attaining e
+    uint32_t bodies;   // 32-step bodies walked (each covers 32 x 1024 states)
+    uint32_t checked;  // bodies that ran the per-step minimum
 };
 
 struct Ctrl {
@@ -21,14 +23,16 @@ struct Ctrl {
     int32_t pad0;
     uint64_t pad1[6];
     Partial result;              // final reduction (offset 64)
-    uint32_t slow_total;
-    uint32_t pad2;
+    uint64_t slow_total;
+    uint64_t bodies_total;
+    uint64_t checked_total;
 };
 
 struct SearchArgs {
     const int32_t *es;      // [cols_padded]       suffix energies E_s(c)
     const int32_t *mint;    // [A][cols_padded]    M_int rows by prefix variable
     const int32_t *ep;      // [2^A]               prefix energies in Gray order
+    const int32_t *epmin;   // [2^A / 32]          min of ep over each 32-step body
     Partial *partials;      // [gridDim.x * waves per block]
     Ctrl *ctrl;
     uint64_t cols_padded;
@@ -45,15 +49,19 @@ struct SearchArgs {
 // Cache builder (Maltsev et al., sec. III.A preprocessing, eq. 8): E_s, M_int
 // and the Gray-ordered prefix energies, from the folded upper-triangular U.
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
-                               int32_t *es, int32_t *mint, int32_t *ep, hipStream_t stream);
+                               int32_t *es, int32_t *mint, int32_t *ep, int32_t *epmin,
+                               hipStream_t stream);
 
 // Resets the work counter and seeds the shared best with t0 (a real energy or an upper bound).
 hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, hipStream_t stream);
 
-hipError_t launch_search(const SearchArgs &args, int blocks, int lds_bytes, hipStream_t stream);
+// gated = true skips the per-step minimum of bodies whose lower bound cannot
+// reach the threshold; gated = false takes it after every prefix (strict).
+hipError_t launch_search(const SearchArgs &args, bool gated, int blocks, int lds_bytes,
+                         hipStream_t stream);
 
 // Resident workgroups of the search kernel per CU for a given dynamic LDS size.
-hipError_t search_occupancy(int *blocks_per_cu, int lds_bytes);
+hipError_t search_occupancy(bool gated, int *blocks_per_cu, int lds_bytes);
 
 hipError_t launch_reduce(const Partial *partials, int count, Ctrl *ctrl, hipStream_t stream);
 

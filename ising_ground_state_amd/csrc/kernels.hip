@@ -176,9 +176,12 @@ __global__ __launch_bounds__(256) void build_suffix_kernel(const int32_t *__rest
 // which equal g(blockIdx.x).  Splitting x_p into high and low parts,
 //   E_p = E_hi + E_lo + sum_{v in lo, x_v = 1} K[v],   K[v] = sum_{w in hi, x_w = 1} U[w][v],
 // so each block evaluates E_hi and K once and each thread only its low part.
+// The same kernel writes epmin[k] = min of ep over the 32-step body k (Gray steps
+// 32k .. 32k+31), which bounds the prefix energy of every state of that body.
 __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *__restrict__ U,
                                                                 int ns, int A, int L,
-                                                                int32_t *__restrict__ ep)
+                                                                int32_t *__restrict__ ep,
+                                                                int32_t *__restrict__ epmin)
 {
     __shared__ int K[8];
     __shared__ int ehi_sh;
@@ -213,10 +216,20 @@ __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *_
             e += ((lo >> (L - 1 - b)) & 1u) ? U[(H + a) * ns + (H + b)] : 0;
     }
     ep[j] = e;
+    // 32 consecutive j are 32 consecutive lanes of one wave (blocks have 2^L >= 32 threads).
+    int m = e;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) {
+        const int o = __shfl_xor(m, off, 64);
+        m = o < m ? o : m;
+    }
+    if ((tid & 31) == 0)
+        epmin[j >> 5] = m;
 }
 
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
-                               int32_t *es, int32_t *mint, int32_t *ep, hipStream_t stream)
+                               int32_t *es, int32_t *mint, int32_t *ep, int32_t *epmin,
+                               hipStream_t stream)
 {
     const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
     hipLaunchKernelGGL(build_suffix_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
@@ -229,7 +242,7 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
     if (blocks > 0x7fffffffull)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(build_prefix_gray_kernel, dim3((unsigned)blocks), dim3(1u << L), 0, stream,
-                       U, ns, A, L, ep);
+                       U, ns, A, L, ep, epmin);
     return hipGetLastError();
 }
 
@@ -238,6 +251,8 @@ __global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0)
     ctrl->counter = 0;
     ctrl->gbest = t0;
     ctrl->slow_total = 0;
+    ctrl->bodies_total = 0;
+    ctrl->checked_total = 0;
 }
 
 hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, hipStream_t stream)
@@ -313,9 +328,85 @@ __device__ __forceinline__ void slow_body(int (&E)[kR], const int (&Mr)[kU][kR],
     }
 }
 
+// Keeps each column's energy of the current state in a VGPR: the compiler may
+// not fold a run of row updates into its net effect, so every state of the walk
+// is materialised by its own add (the O(1)-per-state evaluation of eq. 9).
+__device__ __forceinline__ void materialise(int (&E)[kR])
+{
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+        asm volatile("" : "+v"(E[r]));
+}
+
+// One unrolled body of 32 Gray steps with only the row updates (eq. 9): every
+// flip has a compile-time row and sign except the flip of bit 4, whose sign
+// alternates between bodies.
+__device__ __forceinline__ void adds_body(int (&E)[kR], const int (&Mr)[kU][kR], bool top_plus)
+{
+#pragma unroll
+    for (int m = 0; m + 1 < kBody; ++m) {
+        const int t = __builtin_ctz((unsigned)(m + 1));
+        if (t < kU - 1) {
+            if ((((m + 1) >> (t + 1)) & 1) == 0)
+                add_row(E, Mr[t]);
+            else
+                sub_row(E, Mr[t]);
+        } else {
+            if (top_plus)
+                add_row(E, Mr[kU - 1]);
+            else
+                sub_row(E, Mr[kU - 1]);
+        }
+        materialise(E);
+    }
+}
+
+// The same body with the per-step test of Algorithm 2: after each state, the
+// lane's minimum over its 16 columns (a v_min3 tree) is compared with the
+// threshold T - E_p(g(j)).  Returns the OR over the body of the wave's hit masks.
+__device__ __forceinline__ uint64_t checked_body(int (&E)[kR], const int (&Mr)[kU][kR],
+                                                 bool top_plus, int T,
+                                                 const int32_t *__restrict__ epb)
+{
+    uint64_t acc = 0;
+#pragma unroll
+    for (int m = 0; m < kBody; ++m) {
+        const int th = T - epb[m];
+        const int cm = row_min<kR>(E);
+        acc |= __builtin_amdgcn_ballot_w64(cm <= th);
+        if (m + 1 < kBody) {
+            const int t = __builtin_ctz((unsigned)(m + 1));
+            if (t < kU - 1) {
+                if ((((m + 1) >> (t + 1)) & 1) == 0)
+                    add_row(E, Mr[t]);
+                else
+                    sub_row(E, Mr[t]);
+            } else {
+                if (top_plus)
+                    add_row(E, Mr[kU - 1]);
+                else
+                    sub_row(E, Mr[kU - 1]);
+            }
+        }
+    }
+    return acc;
+}
+
+// Gated = true: before a body, a lower bound on every energy the body will
+// produce decides whether the per-step minimum is needed at all.  The body
+// visits all 32 patterns y of the 5 low Gray bits with the higher prefix bits
+// fixed; from the body's first state (low pattern s<<4, s = bit 5 of the step
+// index) a column's suffix-dependent energy can fall by at most
+//   beta0(c) - s M_4(c),   beta0(c) = sum_{t<5} min(0, M_t(c)),
+// and the prefix energy of any step is at least epmin[body].  If no lane has a
+// column with E(c) + beta0(c) - s M_4(c) <= T - epmin, no state of the body can
+// reach the threshold T, and the body runs the row updates only; otherwise it
+// runs the checked body.  Every state still costs its one add.
+template <bool Gated>
 __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restrict__ es,
                                                           const int32_t *__restrict__ mint,
                                                           const int32_t *__restrict__ ep,
+                                                          const int32_t *__restrict__ epmin,
                                                           Partial *__restrict__ partials,
                                                           Ctrl *__restrict__ ctrl,
                                                           const SearchArgs a)
@@ -329,7 +420,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
     const uint64_t cp = a.cols_padded;
 
     LaneBest lb;
-    uint32_t slow_bodies = 0;
+    uint32_t slow_bodies = 0, bodies = 0, checked = 0;
     int T = read_gbest(ctrl);
     long long cur_g = -1;
 
@@ -390,44 +481,61 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
             for (int r = 0; r < kR; ++r)
                 Mr[t][r] = row[r * 64];
         }
+        int beta0[kR];
+        if (Gated) {
+#pragma unroll
+            for (int r = 0; r < kR; ++r) {
+                int b = 0;
+#pragma unroll
+                for (int t = 0; t < kU; ++t)
+                    b += Mr[t][r] < 0 ? Mr[t][r] : 0;
+                beta0[r] = b;
+            }
+        }
         {
             const int gb = read_gbest(ctrl);
             T = gb < T ? gb : T;
         }
 
+        // Body minima of the prefix energies are read one body ahead (scalar loads).
+        int epm_cur = Gated ? epmin[j_begin >> kU] : 0;
         for (uint64_t base = j_begin; base < j_end; base += kBody) {
-            const int32_t *__restrict__ epb = ep + base;
             const bool top_plus = ((base >> kU) & 1u) == 0;
-            uint64_t acc = 0;
-#pragma unroll
-            for (int m = 0; m < kBody; ++m) {
-                const int th = T - epb[m];
-                const int cm = row_min<kR>(E);
-                acc |= __builtin_amdgcn_ballot_w64(cm <= th);
-                if (m + 1 < kBody) {
-                    const int t = __builtin_ctz((unsigned)(m + 1));
-                    if (t < kU - 1) {
-                        if ((((m + 1) >> (t + 1)) & 1) == 0)
-                            add_row(E, Mr[t]);
-                        else
-                            sub_row(E, Mr[t]);
-                    } else {
-                        if (top_plus)
-                            add_row(E, Mr[kU - 1]);
-                        else
-                            sub_row(E, Mr[kU - 1]);
-                    }
-                }
+            int epm_next = 0;
+            if (Gated) {
+                const uint64_t nb = (base + kBody < j_end) ? (base >> kU) + 1 : (base >> kU);
+                epm_next = epmin[nb];
             }
-            if (acc) {
-                slow_body(E, Mr, base, top_plus, T, ep, a.B, col0, lb);
-                ++slow_bodies;
-                const int wm = __builtin_amdgcn_readfirstlane(wave_min(lb.e));
-                T = wm < T ? wm : T;
-                if (lane == 0)
-                    atomicMin(&ctrl->gbest, T);
-                const int gb = read_gbest(ctrl);
-                T = gb < T ? gb : T;
+            bool check = true;
+            if (Gated) {
+                const int thb = T - epm_cur;
+                int bound[kR];
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    bound[r] = E[r] + beta0[r];
+                if (!top_plus) {
+#pragma unroll
+                    for (int r = 0; r < kR; ++r)
+                        bound[r] -= Mr[kU - 1][r];
+                }
+                check = __builtin_amdgcn_ballot_w64(row_min<kR>(bound) <= thb) != 0;
+            }
+            ++bodies;
+            if (!check) {
+                adds_body(E, Mr, top_plus);
+            } else {
+                ++checked;
+                const uint64_t acc = checked_body(E, Mr, top_plus, T, ep + base);
+                if (acc) {
+                    slow_body(E, Mr, base, top_plus, T, ep, a.B, col0, lb);
+                    ++slow_bodies;
+                    const int wm = __builtin_amdgcn_readfirstlane(wave_min(lb.e));
+                    T = wm < T ? wm : T;
+                    if (lane == 0)
+                        atomicMin(&ctrl->gbest, T);
+                    const int gb = read_gbest(ctrl);
+                    T = gb < T ? gb : T;
+                }
             }
             const uint64_t next = base + kBody;
             if (next < j_end) {
@@ -451,6 +559,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 else
                     sub_row(E, row);
             }
+            epm_cur = epm_next;
         }
     }
 
@@ -463,22 +572,32 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
         p.slow = slow_bodies;
         p.count = cnt;
         p.arg = arg;
+        p.bodies = bodies;
+        p.checked = checked;
         partials[(uint64_t)blockIdx.x * kWaves + wave] = p;
     }
 }
 
-hipError_t launch_search(const SearchArgs &args, int blocks, int lds_bytes, hipStream_t stream)
+hipError_t launch_search(const SearchArgs &args, bool gated, int blocks, int lds_bytes,
+                         hipStream_t stream)
 {
-    hipLaunchKernelGGL(gray_search_kernel, dim3(blocks), dim3(64 * kWaves), lds_bytes, stream,
-                       args.es, args.mint, args.ep, args.partials, args.ctrl, args);
+    if (gated)
+        hipLaunchKernelGGL(gray_search_kernel<true>, dim3(blocks), dim3(64 * kWaves), lds_bytes,
+                           stream, args.es, args.mint, args.ep, args.epmin, args.partials,
+                           args.ctrl, args);
+    else
+        hipLaunchKernelGGL(gray_search_kernel<false>, dim3(blocks), dim3(64 * kWaves), lds_bytes,
+                           stream, args.es, args.mint, args.ep, args.epmin, args.partials,
+                           args.ctrl, args);
     return hipGetLastError();
 }
 
-hipError_t search_occupancy(int *blocks_per_cu, int lds_bytes)
+hipError_t search_occupancy(bool gated, int *blocks_per_cu, int lds_bytes)
 {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, reinterpret_cast<const void *>(gray_search_kernel), 64 * kWaves,
-        (size_t)lds_bytes);
+    const void *fn = gated ? reinterpret_cast<const void *>(gray_search_kernel<true>)
+                           : reinterpret_cast<const void *>(gray_search_kernel<false>);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, 64 * kWaves,
+                                                        (size_t)lds_bytes);
 }
 
 // Final map-reduce step (sec. III.C): min energy, summed counts at the min,
@@ -487,38 +606,47 @@ __global__ __launch_bounds__(256) void reduce_kernel(const Partial *__restrict__
                                                      int count, Ctrl *ctrl)
 {
     __shared__ int se[4];
-    __shared__ uint64_t sc[4], sa[4];
-    __shared__ uint32_t ss[4];
+    __shared__ uint64_t sc[4], sa[4], ss[4], sb[4], sk[4];
     int e = INT_MAX;
-    uint64_t cnt = 0, arg = ~0ull;
-    uint32_t slow = 0;
+    uint64_t cnt = 0, arg = ~0ull, slow = 0, bodies = 0, checked = 0;
     for (int k = threadIdx.x; k < count; k += blockDim.x) {
         const Partial p = partials[k];
         combine(e, cnt, arg, p.e, p.count, p.arg);
         slow += p.slow;
+        bodies += p.bodies;
+        checked += p.checked;
     }
     wave_combine(e, cnt, arg);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
+    for (int off = 32; off >= 1; off >>= 1) {
         slow += __shfl_xor(slow, off, 64);
+        bodies += __shfl_xor(bodies, off, 64);
+        checked += __shfl_xor(checked, off, 64);
+    }
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
         se[w] = e;
         sc[w] = cnt;
         sa[w] = arg;
         ss[w] = slow;
+        sb[w] = bodies;
+        sk[w] = checked;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         for (int k = 1; k < (int)(blockDim.x >> 6); ++k) {
             combine(e, cnt, arg, se[k], sc[k], sa[k]);
             slow += ss[k];
+            bodies += sb[k];
+            checked += sk[k];
         }
         ctrl->result.e = e;
         ctrl->result.slow = 0;
         ctrl->result.count = cnt;
         ctrl->result.arg = arg;
         ctrl->slow_total = slow;
+        ctrl->bodies_total = bodies;
+        ctrl->checked_total = checked;
     }
 }
 

@@ -152,8 +152,10 @@ Layout layout_of(const qubo_plan &p)
     off = align256(off + (uint64_t)p.prefix_bits * L.cols_padded * 4);
     L.off_ep = off;
     off = align256(off + (1ull << p.prefix_bits) * 4);
+    L.off_epmin = off;
+    off = align256(off + (1ull << (p.prefix_bits - kRegBits)) * 4);
     L.off_partials = off;
-    off = align256(off + (uint64_t)p.blocks * p.waves_per_block * 24);
+    off = align256(off + (uint64_t)p.blocks * p.waves_per_block * 32);  // one 32-byte partial per wave
     L.off_ctrl = off;
     off = align256(off + 256);
     L.total = off;

@@ -37,7 +37,7 @@ int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, qubo_plan *ou
 // Device workspace layout of a plan (byte offsets, all 256-aligned).
 struct Layout {
     uint64_t cols_padded;  // 2^B rounded up to a multiple of kColsPerGroup
-    uint64_t off_u, off_es, off_mint, off_ep, off_partials, off_ctrl;
+    uint64_t off_u, off_es, off_mint, off_ep, off_epmin, off_partials, off_ctrl;
     uint64_t total;
 };
 Layout layout_of(const qubo_plan &p);

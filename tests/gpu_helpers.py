@@ -27,3 +27,17 @@ def inv_gray(g: int) -> int:
         j ^= g
         g >>= 1
     return j
+
+
+def check_coverage(q, n, prefix_bits=None, cache_bits=None, lo=None, hi=None, strict=False):
+    """The last search walked every 32-step body of its range exactly once per
+    column group: bodies * 32 == (hi - lo) * col_groups (coverage invariant)."""
+    plan = q.make_plan(n, prefix_bits, cache_bits)
+    A = plan["prefix_bits"]
+    lo = 0 if lo is None else lo
+    hi = (1 << A) if hi is None else hi
+    t = q.last_timing()
+    assert t["bodies"] * 32 == (hi - lo) * plan["col_groups"], (t, plan)
+    if strict:
+        assert t["checked_bodies"] == t["bodies"], t
+    assert t["slow_bodies"] <= t["checked_bodies"] <= t["bodies"], t

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import qubo_instances as qi
-from gpu_helpers import announce, dev_q, gray, inv_gray
+from gpu_helpers import announce, check_coverage, dev_q, gray, inv_gray
 
 pytestmark = pytest.mark.gpu
 
@@ -77,11 +77,15 @@ SMALL = [(n, 6000 + n, -100, 100) for n in range(1, 21)] + \
 
 @pytest.mark.parametrize("n,seed,lo,hi", SMALL)
 def test_small_random(q, n, seed, lo, hi):
-    """Non-symmetric Q, with and without heavy ties, against oracle tier B."""
+    """Non-symmetric Q, with and without heavy ties, against oracle tier B, in
+    both kernel modes (bound-gated default and strict per-step minimum)."""
     Q = qi.general_uniform(n, seed, lo, hi)
     want = oracle.search_gray(Q).triple()
-    announce("small", n, seed, lo, hi)
-    assert q.search(dev_q(Q)).triple() == want
+    Qd = dev_q(Q)
+    for strict in (False, True):
+        announce("small", n, seed, lo, hi, "strict" if strict else "gated")
+        assert q.search(Qd, strict=strict).triple() == want, strict
+        check_coverage(q, n, strict=strict)
 
 
 @pytest.mark.parametrize("n", [5, 11, 18, 22])
@@ -90,26 +94,31 @@ def test_every_split(q, n):
     (permutation invariance, sec. II.D): every accepted split is exact."""
     Q = qi.general_uniform(n, 6300 + n, -50, 50)
     want = oracle.search_gray(Q).triple()
+    Qd = dev_q(Q)
     for A in range(5, n + 1):
         for l in sorted({5, min(A, 7), min(A, 13), A} & set(range(5, min(A, 21) + 1))):
-            announce("split", n, A, l)
-            assert q.search(dev_q(Q), prefix_bits=A, cache_bits=l).triple() == want, (A, l)
+            for strict in (False, True):
+                announce("split", n, A, l, strict)
+                assert q.search(Qd, prefix_bits=A, cache_bits=l, strict=strict).triple() == want, \
+                    (A, l, strict)
+                check_coverage(q, n, A, l, strict=strict)
 
 
-def test_special_cases(q):
+@pytest.mark.parametrize("strict", [False, True])
+def test_special_cases(q, strict):
     for n in (3, 7, 16, 21):
         zero = qi.zeros(n)
         announce("zero", n)
-        assert q.search(dev_q(zero)).triple() == (0, 0, 1 << n)
+        assert q.search(dev_q(zero), strict=strict).triple() == (0, 0, 1 << n)
         diag = qi.zeros(n)
         for i in range(n):
             diag[i][i] = -(i + 1)
         announce("negative diagonal", n)
-        assert q.search(dev_q(diag)).triple() == (-n * (n + 1) // 2, (1 << n) - 1, 1)
+        assert q.search(dev_q(diag), strict=strict).triple() == (-n * (n + 1) // 2, (1 << n) - 1, 1)
         for i in range(n):
             diag[i][i] = i + 1
         announce("positive diagonal", n)
-        assert q.search(dev_q(diag)).triple() == (0, 0, 1)
+        assert q.search(dev_q(diag), strict=strict).triple() == (0, 0, 1)
 
 
 def test_planted_and_mattis(q):
@@ -155,8 +164,11 @@ def test_config_vs_stored_oracle(q, name, splits):
     want = (g["min_energy"], g["argmin"], g["count"])
     Qd = dev_q(cfg["Q"])
     for A, l in splits:
-        announce("config", name, A, l)
-        assert q.search(Qd, prefix_bits=A, cache_bits=l).triple() == want, (A, l)
+        for strict in (False, True):
+            announce("config", name, A, l, strict)
+            assert q.search(Qd, prefix_bits=A, cache_bits=l, strict=strict).triple() == want, \
+                (A, l, strict)
+            check_coverage(q, cfg["n"], A, l, strict=strict)
 
 
 # ---------------------------------------------------------------- slices
@@ -169,8 +181,10 @@ def test_range_is_subcube(q, n, A, k):
     for m in (0, 1, (1 << k) - 1, (1 << k) // 3):
         lo, hi = m << (A - k), (m + 1) << (A - k)
         want = oracle.search_gray(Q, k=k, top=gray(m)).triple()
-        announce("range", n, A, k, m)
-        assert q.search_range(dev_q(Q), A, lo, hi).triple() == want
+        for strict in (False, True):
+            announce("range", n, A, k, m, strict)
+            assert q.search_range(dev_q(Q), A, lo, hi, strict=strict).triple() == want
+            check_coverage(q, n, A, None, lo, hi, strict=strict)
 
 
 def test_subcubes_at_full_size(q):
@@ -184,12 +198,13 @@ def test_subcubes_at_full_size(q):
         plan = q.make_plan(n)
         A = plan["prefix_bits"]
         Qd = dev_q(cfg["Q"])
-        for cube in g["cubes"][:6]:
+        for i, cube in enumerate(g["cubes"][:6]):
             k, top = cube["k"], cube["top"]
             m = inv_gray(top)
             lo, hi = m << (A - k), (m + 1) << (A - k)
-            announce("subcube", name, k, top)
-            r = q.search_range(Qd, A, lo, hi)
+            strict = bool(i % 2)
+            announce("subcube", name, k, top, strict)
+            r = q.search_range(Qd, A, lo, hi, strict=strict)
             assert r.triple() == (cube["min_energy"], cube["argmin"], cube["count"])
 
 
