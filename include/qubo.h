@@ -67,7 +67,7 @@ typedef struct {
                                 rows of higher bits are read from L2/HBM.  The
                                 effective value: at most seg_bits */
     int32_t reg_bits;        /* Gray bits whose rows live in VGPRs (5) */
-    int32_t cols_per_lane;   /* suffix columns held by one lane (16) */
+    int32_t cols_per_lane;   /* suffix columns held by one lane (8 or 16) */
     int32_t wave_size;       /* 64 */
     int32_t waves_per_block; /* waves of a workgroup, sharing one column group */
     int32_t seg_bits;        /* each wave walks 2^seg_bits consecutive Gray steps per work unit */
@@ -148,9 +148,13 @@ QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cac
  * at most the sum of the negative parts of the 5 row updates it applies, and its
  * prefix energies are at least their minimum over the block); blocks whose bound
  * exceeds the best energy found so far apply only the row updates (one add per
- * state).  Both modes return identical results; other flag bits are rejected
- * with QUBO_EINVAL. */
+ * state).  Both modes return identical results; unknown flag bits are
+ * rejected with QUBO_EINVAL. */
 #define QUBO_FLAG_STRICT_MIN 1u
+/* Kernel build: 8 or 16 suffix columns per lane (default: the planner's choice).
+ * Both give identical results; at most one may be set. */
+#define QUBO_FLAG_COLS8 2u
+#define QUBO_FLAG_COLS16 4u
 QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
                             uint64_t gray_hi, uint32_t flags, void *stream, qubo_result *out);
 

@@ -77,6 +77,8 @@ _lib = None
 EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range", "qubo_search_ex",
            "qubo_build_tables", "qubo_last_timing", "qubo_strerror", "qubo_version")
 FLAG_STRICT_MIN = 1
+FLAG_COLS8 = 2
+FLAG_COLS16 = 4
 
 
 def load(path: str = LIB_PATH):
@@ -122,7 +124,8 @@ def _opt(v) -> int:
 
 
 def make_plan(n: int, prefix_bits: int | None = None, cache_bits: int | None = None) -> dict:
-    """Host-only plan of a search of n variables (no device needed)."""
+    """Host-only plan of a search of n variables (no device needed), for the
+    default kernel build."""
     p = _Plan()
     rc = load().qubo_make_plan(int(n), _opt(prefix_bits), _opt(cache_bits), ctypes.byref(p))
     if rc != QUBO_OK:
@@ -161,19 +164,28 @@ def _stream(Q, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _flags(strict: bool, cols_per_lane: int | None) -> int:
+    f = FLAG_STRICT_MIN if strict else 0
+    if cols_per_lane is not None:
+        f |= {8: FLAG_COLS8, 16: FLAG_COLS16}[int(cols_per_lane)]
+    return f
+
+
 def search(Q, prefix_bits: int | None = None, cache_bits: int | None = None, stream=None,
-           strict: bool = False) -> Result:
+           strict: bool = False, cols_per_lane: int | None = None) -> Result:
     """Exhaustive search of min_x x^T Q x over {0,1}^n on Q's device.
 
     strict=True takes the minimum after every prefix (Algorithm 2 as printed)
-    instead of gating it by the per-block lower bound; the result is the same."""
+    instead of gating it by the per-block lower bound; cols_per_lane (8 or 16)
+    picks the kernel build.  The result never depends on these options."""
     import torch
     Q = _device_q(Q)
     r = _Result()
+    flags = _flags(strict, cols_per_lane)
     with torch.cuda.device(Q.device):
-        if strict:
+        if flags:
             rc = load().qubo_search_ex(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
-                                       _opt(cache_bits), 0, 0, FLAG_STRICT_MIN, _stream(Q, stream),
+                                       _opt(cache_bits), 0, 0, flags, _stream(Q, stream),
                                        ctypes.byref(r))
         else:
             rc = load().qubo_search(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
@@ -184,7 +196,7 @@ def search(Q, prefix_bits: int | None = None, cache_bits: int | None = None, str
 
 
 def search_range(Q, prefix_bits: int, gray_lo: int, gray_hi: int, cache_bits: int | None = None,
-                 stream=None, strict: bool = False) -> Result:
+                 stream=None, strict: bool = False, cols_per_lane: int | None = None) -> Result:
     """Search the prefixes g(j), gray_lo <= j < gray_hi, with every suffix."""
     import torch
     Q = _device_q(Q)
@@ -192,7 +204,7 @@ def search_range(Q, prefix_bits: int, gray_lo: int, gray_hi: int, cache_bits: in
     with torch.cuda.device(Q.device):
         rc = load().qubo_search_ex(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], int(prefix_bits),
                                    _opt(cache_bits), int(gray_lo), int(gray_hi),
-                                   FLAG_STRICT_MIN if strict else 0, _stream(Q, stream), ctypes.byref(r))
+                                   _flags(strict, cols_per_lane), _stream(Q, stream), ctypes.byref(r))
     if rc != QUBO_OK:
         raise QuboError(rc, "qubo_search_range")
     return Result(r.min_energy, r.argmin, r.count)

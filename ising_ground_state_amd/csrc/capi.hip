@@ -74,6 +74,7 @@ struct Request {
     hipStream_t stream = nullptr;
     Mode mode = Mode::Search;
     bool gated = true;
+    int cols_per_lane = 0;  // 0: planner's default
     int32_t *es_out = nullptr, *mint_out = nullptr, *ep_out = nullptr;
 };
 
@@ -107,7 +108,7 @@ int run(const Request &rq, qubo_result *out)
 
     // 2. Plan.
     qubo_plan plan;
-    rc = make_plan(n, rq.prefix_bits, rq.cache_bits, dev.num_cus, &plan);
+    rc = make_plan(n, rq.prefix_bits, rq.cache_bits, dev.num_cus, rq.cols_per_lane, &plan);
     if (rc != QUBO_OK)
         return rc;
     const int ns = plan.n_search;
@@ -128,7 +129,8 @@ int run(const Request &rq, qubo_result *out)
     const uint64_t items = plan.col_groups * seg_blocks;
 
     int per_cu = 0;
-    if (search_occupancy(rq.gated, &per_cu, plan.lds_bytes) != hipSuccess || per_cu < 1)
+    if (search_occupancy(plan.cols_per_lane, rq.gated, &per_cu, plan.lds_bytes) != hipSuccess ||
+        per_cu < 1)
         return QUBO_EDEVICE;
     const uint64_t want_blocks = (uint64_t)dev.num_cus * (uint64_t)per_cu;
     plan.blocks = (int)(items < want_blocks ? items : want_blocks);
@@ -202,7 +204,8 @@ int run(const Request &rq, qubo_result *out)
     sa.B = B;
     sa.l_eff = plan.cache_bits < plan.seg_bits ? plan.cache_bits : plan.seg_bits;
     sa.seg_bits = plan.seg_bits;
-    if (launch_search(sa, rq.gated, plan.blocks, plan.lds_bytes, rq.stream) != hipSuccess)
+    if (launch_search(sa, plan.cols_per_lane, rq.gated, plan.blocks, plan.lds_bytes, rq.stream) !=
+        hipSuccess)
         return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[2], rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
@@ -253,7 +256,7 @@ extern "C" {
 QUBO_API int qubo_make_plan(int n, int prefix_bits, int cache_bits, qubo_plan *out)
 {
     // Host-only planning for a 256-CU MI355X.
-    return qubo::make_plan(n, prefix_bits, cache_bits, 256, out);
+    return qubo::make_plan(n, prefix_bits, cache_bits, 256, 0, out);
 }
 
 QUBO_API int qubo_check_q(const int32_t *Q_host, int n, int64_t *abs_sum)
@@ -279,7 +282,8 @@ QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bit
 QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
                            uint64_t gray_hi, uint32_t flags, void *stream, qubo_result *out)
 {
-    if (flags & ~(uint32_t)QUBO_FLAG_STRICT_MIN)
+    const uint32_t known = QUBO_FLAG_STRICT_MIN | QUBO_FLAG_COLS8 | QUBO_FLAG_COLS16;
+    if ((flags & ~known) || ((flags & QUBO_FLAG_COLS8) && (flags & QUBO_FLAG_COLS16)))
         return QUBO_EINVAL;
     Request rq;
     rq.Q = Q;
@@ -287,6 +291,7 @@ QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_
     rq.prefix_bits = prefix_bits;
     rq.cache_bits = cache_bits;
     rq.gated = !(flags & QUBO_FLAG_STRICT_MIN);
+    rq.cols_per_lane = (flags & QUBO_FLAG_COLS8) ? 8 : (flags & QUBO_FLAG_COLS16) ? 16 : 0;
     rq.stream = static_cast<hipStream_t>(stream);
     if (gray_lo != 0 || gray_hi != 0) {
         if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||

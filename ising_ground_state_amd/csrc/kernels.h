@@ -57,11 +57,12 @@ hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, hipStream_t stream);
 
 // gated = true skips the per-step minimum of bodies whose lower bound cannot
 // reach the threshold; gated = false takes it after every prefix (strict).
-hipError_t launch_search(const SearchArgs &args, bool gated, int blocks, int lds_bytes,
-                         hipStream_t stream);
+// cols_per_lane selects the instantiation (8 or 16 suffix columns per lane).
+hipError_t launch_search(const SearchArgs &args, int cols_per_lane, bool gated, int blocks,
+                         int lds_bytes, hipStream_t stream);
 
 // Resident workgroups of the search kernel per CU for a given dynamic LDS size.
-hipError_t search_occupancy(bool gated, int *blocks_per_cu, int lds_bytes);
+hipError_t search_occupancy(int cols_per_lane, bool gated, int *blocks_per_cu, int lds_bytes);
 
 hipError_t launch_reduce(const Partial *partials, int count, Ctrl *ctrl, hipStream_t stream);
 

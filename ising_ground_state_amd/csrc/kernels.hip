@@ -14,17 +14,17 @@
 //     registers, the prefix energies are read in Gray order.
 //
 // CDNA4 mapping of the search kernel:
-//   * a lane owns R = 16 suffix columns: c = g*1024 + r*64 + lane, so the lanes
-//     of a wave read consecutive dwords for each r (coalesced loads, conflict-free
-//     LDS reads);
-//   * the M_int rows of the 5 lowest Gray bits live in VGPRs (80 registers), the
+//   * a lane owns R = 8 or 16 suffix columns: c = g*64R + r*64 + lane, so the
+//     lanes of a wave read consecutive dwords for each r (coalesced loads,
+//     conflict-free LDS reads);
+//   * the M_int rows of the 5 lowest Gray bits live in VGPRs (5R registers), the
 //     rows of the next Gray bits in LDS, shared by the 4 waves of a workgroup that
 //     work on the same column group, and the rest in L2/HBM;
 //   * the walk is unrolled over 32 Gray steps: every flip inside the body has a
 //     compile-time row and sign except the flip of bit 4, whose sign alternates
 //     between bodies (a uniform branch); the flip that leaves the body reads its
 //     row from LDS or global memory;
-//   * per step: 16 v_add/v_sub (one per state), a v_min3_i32 tree (8 VALU) and one
+//   * per step: R v_add/v_sub (one per state), a v_min3_i32 tree (R/2 VALU) and one
 //     v_cmp against the scalar threshold T - E_p(g(j)) (the prefix energy comes
 //     from a Gray-ordered table through scalar loads).  The comparison results are
 //     OR-ed over the body; a body with any hit is re-walked on an exact slow path
@@ -38,11 +38,9 @@
 
 namespace qubo {
 
-constexpr int kR = 16;       // columns per lane
 constexpr int kU = 5;        // Gray bits with rows in VGPRs
 constexpr int kBody = 1 << kU;
 constexpr int kWaves = 4;    // waves per workgroup
-constexpr int kGroup = 64 * kR;
 
 __device__ __forceinline__ uint64_t gray(uint64_t i) { return i ^ (i >> 1); }
 
@@ -58,6 +56,16 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v)
 
 template <int R>
 __device__ __forceinline__ int row_min(const int (&E)[R]);
+
+// Min of 8 values: 3 x v_min3_i32 + 1 x v_min_i32.
+template <>
+__device__ __forceinline__ int row_min<8>(const int (&E)[8])
+{
+    const int a = imin(imin(E[0], E[1]), E[2]);
+    const int b = imin(imin(E[3], E[4]), E[5]);
+    const int c = imin(E[6], E[7]);
+    return imin(imin(a, b), c);
+}
 
 // Min of 16 values as a tree of 3-input mins (7 x v_min3_i32 + 1 x v_min_i32).
 template <>
@@ -293,7 +301,8 @@ __device__ __forceinline__ int read_gbest(const Ctrl *ctrl)
 // state of the body's last step on entry and on exit.  Every state with
 // E_sd + E_p <= T is recorded per lane (E_sd <= T - E_p needs no overflow
 // headroom: both sides are sub-sums of the folded matrix).
-__device__ __forceinline__ void slow_body(int (&E)[kR], const int (&Mr)[kU][kR],
+template <int R>
+__device__ __forceinline__ void slow_body(int (&E)[R], const int (&Mr)[kU][R],
                                                     uint64_t base, bool top_plus, int T,
                                                     const int32_t *__restrict__ ep, int B,
                                                     uint64_t col0, LaneBest &lb)
@@ -309,7 +318,7 @@ __device__ __forceinline__ void slow_body(int (&E)[kR], const int (&Mr)[kU][kR],
         const int th = T - epm;
         const uint64_t hi = gray(j) << B;
 #pragma unroll
-        for (int r = 0; r < kR; ++r)
+        for (int r = 0; r < R; ++r)
             if (E[r] <= th)
                 lb.record(E[r] + epm, hi | (col0 + (uint64_t)r * 64));
         if (m + 1 < kBody) {
@@ -331,17 +340,19 @@ __device__ __forceinline__ void slow_body(int (&E)[kR], const int (&Mr)[kU][kR],
 // Keeps each column's energy of the current state in a VGPR: the compiler may
 // not fold a run of row updates into its net effect, so every state of the walk
 // is materialised by its own add (the O(1)-per-state evaluation of eq. 9).
-__device__ __forceinline__ void materialise(int (&E)[kR])
+template <int R>
+__device__ __forceinline__ void materialise(int (&E)[R])
 {
 #pragma unroll
-    for (int r = 0; r < kR; ++r)
+    for (int r = 0; r < R; ++r)
         asm volatile("" : "+v"(E[r]));
 }
 
 // One unrolled body of 32 Gray steps with only the row updates (eq. 9): every
 // flip has a compile-time row and sign except the flip of bit 4, whose sign
 // alternates between bodies.
-__device__ __forceinline__ void adds_body(int (&E)[kR], const int (&Mr)[kU][kR], bool top_plus)
+template <int R>
+__device__ __forceinline__ void adds_body(int (&E)[R], const int (&Mr)[kU][R], bool top_plus)
 {
 #pragma unroll
     for (int m = 0; m + 1 < kBody; ++m) {
@@ -364,7 +375,8 @@ __device__ __forceinline__ void adds_body(int (&E)[kR], const int (&Mr)[kU][kR],
 // The same body with the per-step test of Algorithm 2: after each state, the
 // lane's minimum over its 16 columns (a v_min3 tree) is compared with the
 // threshold T - E_p(g(j)).  Returns the OR over the body of the wave's hit masks.
-__device__ __forceinline__ uint64_t checked_body(int (&E)[kR], const int (&Mr)[kU][kR],
+template <int R>
+__device__ __forceinline__ uint64_t checked_body(int (&E)[R], const int (&Mr)[kU][R],
                                                  bool top_plus, int T,
                                                  const int32_t *__restrict__ epb)
 {
@@ -372,7 +384,7 @@ __device__ __forceinline__ uint64_t checked_body(int (&E)[kR], const int (&Mr)[k
 #pragma unroll
     for (int m = 0; m < kBody; ++m) {
         const int th = T - epb[m];
-        const int cm = row_min<kR>(E);
+        const int cm = row_min<R>(E);
         acc |= __builtin_amdgcn_ballot_w64(cm <= th);
         if (m + 1 < kBody) {
             const int t = __builtin_ctz((unsigned)(m + 1));
@@ -402,7 +414,7 @@ __device__ __forceinline__ uint64_t checked_body(int (&E)[kR], const int (&Mr)[k
 // column with E(c) + beta0(c) - s M_4(c) <= T - epmin, no state of the body can
 // reach the threshold T, and the body runs the row updates only; otherwise it
 // runs the checked body.  Every state still costs its one add.
-template <bool Gated>
+template <int R, bool Gated>
 __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restrict__ es,
                                                           const int32_t *__restrict__ mint,
                                                           const int32_t *__restrict__ ep,
@@ -411,6 +423,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                                                           Ctrl *__restrict__ ctrl,
                                                           const SearchArgs a)
 {
+    constexpr int kGroup = 64 * R;         // columns of a wave (and of a workgroup)
     extern __shared__ int32_t lds_rows[];  // [l_eff - kU][kGroup]
     __shared__ unsigned long long item_sh;
 
@@ -457,11 +470,11 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
         const uint64_t col0 = g * kGroup + (uint64_t)lane;  // column of register r is col0 + 64 r
 
         // E_sd at the first prefix of the segment: E_s + sum of the rows of its set bits (eq. 8).
-        int E[kR];
+        int E[R];
         {
             const int32_t *src = es + col0;
 #pragma unroll
-            for (int r = 0; r < kR; ++r)
+            for (int r = 0; r < R; ++r)
                 E[r] = src[r * 64];
             uint64_t bits = gray(j_begin);
             while (bits) {
@@ -469,22 +482,22 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 bits &= bits - 1;
                 const int32_t *row = mint + (uint64_t)(A - 1 - t) * cp + col0;
 #pragma unroll
-                for (int r = 0; r < kR; ++r)
+                for (int r = 0; r < R; ++r)
                     E[r] += row[r * 64];
             }
         }
-        int Mr[kU][kR];
+        int Mr[kU][R];
 #pragma unroll
         for (int t = 0; t < kU; ++t) {
             const int32_t *row = mint + (uint64_t)(A - 1 - t) * cp + col0;
 #pragma unroll
-            for (int r = 0; r < kR; ++r)
+            for (int r = 0; r < R; ++r)
                 Mr[t][r] = row[r * 64];
         }
-        int beta0[kR];
+        int beta0[R];
         if (Gated) {
 #pragma unroll
-            for (int r = 0; r < kR; ++r) {
+            for (int r = 0; r < R; ++r) {
                 int b = 0;
 #pragma unroll
                 for (int t = 0; t < kU; ++t)
@@ -509,16 +522,16 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
             bool check = true;
             if (Gated) {
                 const int thb = T - epm_cur;
-                int bound[kR];
+                int bound[R];
 #pragma unroll
-                for (int r = 0; r < kR; ++r)
+                for (int r = 0; r < R; ++r)
                     bound[r] = E[r] + beta0[r];
                 if (!top_plus) {
 #pragma unroll
-                    for (int r = 0; r < kR; ++r)
+                    for (int r = 0; r < R; ++r)
                         bound[r] -= Mr[kU - 1][r];
                 }
-                check = __builtin_amdgcn_ballot_w64(row_min<kR>(bound) <= thb) != 0;
+                check = __builtin_amdgcn_ballot_w64(row_min<R>(bound) <= thb) != 0;
             }
             ++bodies;
             if (!check) {
@@ -542,16 +555,16 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 // Flip of Gray bit t >= 5: its row comes from LDS or global memory.
                 const int t = __builtin_ctzll(next);
                 const bool plus = ((next >> (t + 1)) & 1u) == 0;
-                int row[kR];
+                int row[R];
                 if (t < a.l_eff) {
                     const int32_t *src = lds_rows + (t - kU) * kGroup + lane;
 #pragma unroll
-                    for (int r = 0; r < kR; ++r)
+                    for (int r = 0; r < R; ++r)
                         row[r] = src[r * 64];
                 } else {
                     const int32_t *src = mint + (uint64_t)(A - 1 - t) * cp + col0;
 #pragma unroll
-                    for (int r = 0; r < kR; ++r)
+                    for (int r = 0; r < R; ++r)
                         row[r] = src[r * 64];
                 }
                 if (plus)
@@ -578,24 +591,44 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
     }
 }
 
-hipError_t launch_search(const SearchArgs &args, bool gated, int blocks, int lds_bytes,
-                         hipStream_t stream)
+template <int R, bool Gated>
+static void launch_one(const SearchArgs &args, int blocks, int lds_bytes, hipStream_t stream)
 {
-    if (gated)
-        hipLaunchKernelGGL(gray_search_kernel<true>, dim3(blocks), dim3(64 * kWaves), lds_bytes,
-                           stream, args.es, args.mint, args.ep, args.epmin, args.partials,
-                           args.ctrl, args);
-    else
-        hipLaunchKernelGGL(gray_search_kernel<false>, dim3(blocks), dim3(64 * kWaves), lds_bytes,
-                           stream, args.es, args.mint, args.ep, args.epmin, args.partials,
-                           args.ctrl, args);
+    hipLaunchKernelGGL((gray_search_kernel<R, Gated>), dim3(blocks), dim3(64 * kWaves), lds_bytes,
+                       stream, args.es, args.mint, args.ep, args.epmin, args.partials, args.ctrl,
+                       args);
+}
+
+hipError_t launch_search(const SearchArgs &args, int cols_per_lane, bool gated, int blocks,
+                         int lds_bytes, hipStream_t stream)
+{
+    if (cols_per_lane == 8) {
+        if (gated)
+            launch_one<8, true>(args, blocks, lds_bytes, stream);
+        else
+            launch_one<8, false>(args, blocks, lds_bytes, stream);
+    } else if (cols_per_lane == 16) {
+        if (gated)
+            launch_one<16, true>(args, blocks, lds_bytes, stream);
+        else
+            launch_one<16, false>(args, blocks, lds_bytes, stream);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
-hipError_t search_occupancy(bool gated, int *blocks_per_cu, int lds_bytes)
+hipError_t search_occupancy(int cols_per_lane, bool gated, int *blocks_per_cu, int lds_bytes)
 {
-    const void *fn = gated ? reinterpret_cast<const void *>(gray_search_kernel<true>)
-                           : reinterpret_cast<const void *>(gray_search_kernel<false>);
+    const void *fn = nullptr;
+    if (cols_per_lane == 8)
+        fn = gated ? reinterpret_cast<const void *>(gray_search_kernel<8, true>)
+                   : reinterpret_cast<const void *>(gray_search_kernel<8, false>);
+    else if (cols_per_lane == 16)
+        fn = gated ? reinterpret_cast<const void *>(gray_search_kernel<16, true>)
+                   : reinterpret_cast<const void *>(gray_search_kernel<16, false>);
+    else
+        return hipErrorInvalidValue;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, 64 * kWaves,
                                                         (size_t)lds_bytes);
 }

@@ -54,10 +54,16 @@ static int ceil_log2(uint64_t v)
 
 static uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 
-int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, qubo_plan *out)
+int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, int cols_per_lane,
+              qubo_plan *out)
 {
     if (!out || n < 1 || n > QUBO_MAX_N || num_cus < 1)
         return QUBO_EINVAL;
+    if (cols_per_lane == 0)
+        cols_per_lane = kDefaultColsPerLane;
+    if (cols_per_lane != 8 && cols_per_lane != 16)
+        return QUBO_EINVAL;
+    const int group = kWave * cols_per_lane;  // columns of a wave and of a workgroup
     if (prefix_bits < -1 || prefix_bits > n)
         return QUBO_EINVAL;
     if (cache_bits < -1 || cache_bits > (prefix_bits >= 0 ? prefix_bits : n))
@@ -86,7 +92,7 @@ int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, qubo_plan *ou
     if (A > kMaxPrefixBits)
         return QUBO_EPLAN;
     const uint64_t cols = 1ull << B;
-    const uint64_t cols_padded = (cols + kColsPerGroup - 1) / kColsPerGroup * kColsPerGroup;
+    const uint64_t cols_padded = (cols + group - 1) / group * group;
     if ((uint64_t)A * 4ull * cols_padded > kMaxMintBytes)
         return QUBO_EPLAN;
 
@@ -101,10 +107,10 @@ int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, qubo_plan *ou
     p.prefix_bits = A;
     p.suffix_bits = B;
     p.reg_bits = kRegBits;
-    p.cols_per_lane = kColsPerLane;
+    p.cols_per_lane = cols_per_lane;
     p.wave_size = kWave;
     p.waves_per_block = kWavesPerBlock;
-    p.col_groups = cols_padded / kColsPerGroup;
+    p.col_groups = cols_padded / group;
 
     // Segments: enough work units for ~8 per resident wave, each at least one
     // unrolled body (2^5 steps) and at most 2^20 steps.
@@ -121,16 +127,16 @@ int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, qubo_plan *ou
 
     const int l_eff = std::min(l, c);
     const int lds_rows = std::max(0, l_eff - kRegBits);
-    if (lds_rows > kMaxLdsRows)
+    if (lds_rows * group * 4 > kMaxLdsBytes)
         return QUBO_EPLAN;
     p.cache_bits = l_eff;  // bits above the segment length never flip inside a unit
-    p.lds_bytes = lds_rows * kColsPerGroup * 4;
+    p.lds_bytes = lds_rows * group * 4;
 
     const uint64_t segs = 1ull << (A - c);
     p.work_units = p.col_groups * segs;
     const uint64_t block_items = p.col_groups * ((segs + kWavesPerBlock - 1) / kWavesPerBlock);
-    // Two resident workgroups per CU (236 VGPRs per lane -> 2 waves per SIMD);
-    // the search re-sizes the grid from the runtime's occupancy query.
+    // Two resident workgroups per CU for the host-only plan; the search re-sizes
+    // the grid from the runtime's occupancy query of the chosen kernel.
     p.blocks = (int)std::min<uint64_t>((uint64_t)num_cus * 2, block_items);
 
     p.workspace_bytes = layout_of(p).total;
@@ -142,7 +148,8 @@ Layout layout_of(const qubo_plan &p)
 {
     Layout L{};
     const uint64_t cols = 1ull << p.suffix_bits;
-    L.cols_padded = (cols + kColsPerGroup - 1) / kColsPerGroup * kColsPerGroup;
+    const uint64_t group = (uint64_t)kWave * p.cols_per_lane;
+    L.cols_padded = (cols + group - 1) / group * group;
     uint64_t off = 0;
     L.off_u = off;
     off = align256(off + (uint64_t)p.n_search * p.n_search * 4);

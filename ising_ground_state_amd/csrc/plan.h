@@ -11,14 +11,13 @@ namespace qubo {
 
 // Compile-time shape of the search kernel.
 constexpr int kRegBits = 5;        // Gray bits whose M_int rows live in VGPRs
-constexpr int kColsPerLane = 16;   // suffix columns per lane (R)
-constexpr int kWave = 64;          // CDNA wavefront
-constexpr int kWavesPerBlock = 4;  // one wave per SIMD of a CU
-constexpr int kColsPerGroup = kWave * kColsPerLane;  // 1024 columns per wave / workgroup
-constexpr int kMinSearchVars = kRegBits;             // n below this is padded
-constexpr int kMaxPrefixBits = 32;                   // prefix-energy table <= 2^32 entries
-constexpr int kMaxLdsRows = 16;                      // 64 KiB of cached rows per workgroup
-constexpr uint64_t kMaxMintBytes = 1ull << 33;       // 8 GiB
+constexpr int kDefaultColsPerLane = 8;  // suffix columns per lane (R); 16 is the other build
+constexpr int kWave = 64;                // CDNA wavefront
+constexpr int kWavesPerBlock = 4;        // one wave per SIMD of a CU
+constexpr int kMinSearchVars = kRegBits; // n below this is padded
+constexpr int kMaxPrefixBits = 32;       // prefix-energy table <= 2^32 entries
+constexpr int kMaxLdsBytes = 65536;      // cached rows per workgroup
+constexpr uint64_t kMaxMintBytes = 1ull << 33;  // 8 GiB
 
 constexpr int64_t kAbsSumLimit = (1ll << 30) - 1;
 
@@ -31,12 +30,14 @@ int fold_upper(const int32_t *Q, int n, std::vector<int32_t> &U, int64_t *abs_su
 // U_ii = +1 and no couplings, so they are 0 in every minimiser.
 std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_search);
 
-// Fills `out` for n variables on a device with `num_cus` compute units.
-int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, qubo_plan *out);
+// Fills `out` for n variables on a device with `num_cus` compute units;
+// cols_per_lane is 8 or 16, or 0 for the default.
+int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, int cols_per_lane,
+              qubo_plan *out);
 
 // Device workspace layout of a plan (byte offsets, all 256-aligned).
 struct Layout {
-    uint64_t cols_padded;  // 2^B rounded up to a multiple of kColsPerGroup
+    uint64_t cols_padded;  // 2^B rounded up to a multiple of the column-group size
     uint64_t off_u, off_es, off_mint, off_ep, off_epmin, off_partials, off_ctrl;
     uint64_t total;
 };

@@ -29,15 +29,19 @@ def inv_gray(g: int) -> int:
     return j
 
 
-def check_coverage(q, n, prefix_bits=None, cache_bits=None, lo=None, hi=None, strict=False):
+def check_coverage(q, n, prefix_bits=None, cache_bits=None, lo=None, hi=None, strict=False,
+                   cols_per_lane=None):
     """The last search walked every 32-step body of its range exactly once per
-    column group: bodies * 32 == (hi - lo) * col_groups (coverage invariant)."""
+    column group: bodies * 32 * 64R == (hi - lo) * (2^B padded to 64R columns)."""
     plan = q.make_plan(n, prefix_bits, cache_bits)
-    A = plan["prefix_bits"]
+    A, B = plan["prefix_bits"], plan["suffix_bits"]
+    R = cols_per_lane or plan["cols_per_lane"]
+    group = 64 * R
+    cols_padded = -(-(1 << B) // group) * group
     lo = 0 if lo is None else lo
     hi = (1 << A) if hi is None else hi
     t = q.last_timing()
-    assert t["bodies"] * 32 == (hi - lo) * plan["col_groups"], (t, plan)
+    assert t["bodies"] * 32 * group == (hi - lo) * cols_padded, (t, plan, R)
     if strict:
         assert t["checked_bodies"] == t["bodies"], t
     assert t["slow_bodies"] <= t["checked_bodies"] <= t["bodies"], t

@@ -47,18 +47,20 @@ def test_plan_invariants(n):
     assert A + B == p["n_search"] and A >= 5 and A <= 32
     assert 5 <= p["cache_bits"] <= A
     assert 5 <= p["seg_bits"] <= min(A, 20)
-    assert p["lds_bytes"] == max(0, min(p["cache_bits"], p["seg_bits"]) - 5) * 4096 <= 65536
-    assert p["col_groups"] == max(1, (1 << B) // 1024)
+    group = 64 * p["cols_per_lane"]
+    assert p["cols_per_lane"] in (8, 16)
+    assert p["lds_bytes"] == max(0, min(p["cache_bits"], p["seg_bits"]) - 5) * group * 4 <= 65536
+    assert p["col_groups"] == max(1, (1 << B) // group)
     assert p["work_units"] == p["col_groups"] << (A - p["seg_bits"])
     # the whole space is covered: units x steps x columns per group >= 2^n
-    assert p["work_units"] * (1 << p["seg_bits"]) * 1024 >= 1 << p["n_search"]
-    assert p["workspace_bytes"] >= 4 * ((1 << A) + A * max(1 << B, 1024))
+    assert p["work_units"] * (1 << p["seg_bits"]) * group >= 1 << p["n_search"]
+    assert p["workspace_bytes"] >= 4 * ((1 << A) + A * max(1 << B, group))
 
 
 def test_plan_explicit_splits():
     p = q.make_plan(48, prefix_bits=28, cache_bits=16)
     assert (p["prefix_bits"], p["suffix_bits"], p["cache_bits"]) == (28, 20, 16)
-    assert p["lds_bytes"] == 11 * 4096
+    assert p["lds_bytes"] == 11 * 64 * p["cols_per_lane"] * 4
     p = q.make_plan(48, prefix_bits=28, cache_bits=5)
     assert p["lds_bytes"] == 0
     # cached bits beyond one work unit's segment never flip there: the plan reports the effective value

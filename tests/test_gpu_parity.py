@@ -82,10 +82,11 @@ def test_small_random(q, n, seed, lo, hi):
     Q = qi.general_uniform(n, seed, lo, hi)
     want = oracle.search_gray(Q).triple()
     Qd = dev_q(Q)
-    for strict in (False, True):
-        announce("small", n, seed, lo, hi, "strict" if strict else "gated")
-        assert q.search(Qd, strict=strict).triple() == want, strict
-        check_coverage(q, n, strict=strict)
+    for R in (8, 16):
+        for strict in (False, True):
+            announce("small", n, seed, lo, hi, R, "strict" if strict else "gated")
+            assert q.search(Qd, strict=strict, cols_per_lane=R).triple() == want, (R, strict)
+            check_coverage(q, n, strict=strict, cols_per_lane=R)
 
 
 @pytest.mark.parametrize("n", [5, 11, 18, 22])
@@ -97,11 +98,11 @@ def test_every_split(q, n):
     Qd = dev_q(Q)
     for A in range(5, n + 1):
         for l in sorted({5, min(A, 7), min(A, 13), A} & set(range(5, min(A, 21) + 1))):
-            for strict in (False, True):
-                announce("split", n, A, l, strict)
-                assert q.search(Qd, prefix_bits=A, cache_bits=l, strict=strict).triple() == want, \
-                    (A, l, strict)
-                check_coverage(q, n, A, l, strict=strict)
+            for strict, R in ((False, 8), (True, 8), (False, 16), (True, 16)):
+                announce("split", n, A, l, strict, R)
+                got = q.search(Qd, prefix_bits=A, cache_bits=l, strict=strict, cols_per_lane=R)
+                assert got.triple() == want, (A, l, strict, R)
+                check_coverage(q, n, A, l, strict=strict, cols_per_lane=R)
 
 
 @pytest.mark.parametrize("strict", [False, True])
@@ -164,11 +165,11 @@ def test_config_vs_stored_oracle(q, name, splits):
     want = (g["min_energy"], g["argmin"], g["count"])
     Qd = dev_q(cfg["Q"])
     for A, l in splits:
-        for strict in (False, True):
-            announce("config", name, A, l, strict)
-            assert q.search(Qd, prefix_bits=A, cache_bits=l, strict=strict).triple() == want, \
-                (A, l, strict)
-            check_coverage(q, cfg["n"], A, l, strict=strict)
+        for strict, R in ((False, 8), (True, 8), (False, 16), (True, 16)):
+            announce("config", name, A, l, strict, R)
+            got = q.search(Qd, prefix_bits=A, cache_bits=l, strict=strict, cols_per_lane=R)
+            assert got.triple() == want, (A, l, strict, R)
+            check_coverage(q, cfg["n"], A, l, strict=strict, cols_per_lane=R)
 
 
 # ---------------------------------------------------------------- slices
@@ -181,10 +182,10 @@ def test_range_is_subcube(q, n, A, k):
     for m in (0, 1, (1 << k) - 1, (1 << k) // 3):
         lo, hi = m << (A - k), (m + 1) << (A - k)
         want = oracle.search_gray(Q, k=k, top=gray(m)).triple()
-        for strict in (False, True):
-            announce("range", n, A, k, m, strict)
-            assert q.search_range(dev_q(Q), A, lo, hi, strict=strict).triple() == want
-            check_coverage(q, n, A, None, lo, hi, strict=strict)
+        for strict, R in ((False, 8), (True, 8), (False, 16), (True, 16)):
+            announce("range", n, A, k, m, strict, R)
+            assert q.search_range(dev_q(Q), A, lo, hi, strict=strict, cols_per_lane=R).triple() == want
+            check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
 
 
 def test_subcubes_at_full_size(q):
