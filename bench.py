@@ -170,7 +170,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {
             "bound": "alu",
-            "kernel": "gray_search_kernel<%s>" % ("false" if args.strict else "true"),
+            "kernel": "gray_search_kernel<%d, %s>" % (plan["cols_per_lane"], "false" if args.strict else "true"),
             "achieved": achieved / 1e12,
             "peak": INT32_VALU_PEAK / 1e12,
             "unit": "int32 Tops/s",

@@ -129,9 +129,10 @@ int run(const Request &rq, qubo_result *out)
     const uint64_t items = plan.col_groups * seg_blocks;
 
     int per_cu = 0;
-    if (search_occupancy(plan.cols_per_lane, rq.gated, &per_cu, plan.lds_bytes) != hipSuccess ||
-        per_cu < 1)
+    if (search_occupancy(plan.cols_per_lane, rq.gated, &per_cu, plan.lds_bytes) != hipSuccess)
         return QUBO_EDEVICE;
+    if (per_cu < 1)
+        per_cu = 1;
     const uint64_t want_blocks = (uint64_t)dev.num_cus * (uint64_t)per_cu;
     plan.blocks = (int)(items < want_blocks ? items : want_blocks);
     const Layout L = layout_of(plan);
@@ -183,7 +184,7 @@ int run(const Request &rq, qubo_result *out)
     // The first threshold must be a real energy of the searched set or an upper
     // bound of all of them: E(0) = 0 when state 0 is searched, else sum |Q_ij|.
     const int32_t t0 = (lo == 0) ? 0 : (int32_t)abs_sum;
-    if (launch_init_ctrl(dctrl, t0, rq.stream) != hipSuccess)
+    if (launch_init_ctrl(dctrl, t0, depmin + (1ull << (A - kRegBits)), rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
 
     SearchArgs sa{};

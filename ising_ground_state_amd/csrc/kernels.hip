@@ -254,8 +254,9 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
     return hipGetLastError();
 }
 
-__global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0)
+__global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad)
 {
+    *epmin_pad = INT_MAX;  // read ahead by the last body of the walk, never used
     ctrl->counter = 0;
     ctrl->gbest = t0;
     ctrl->slow_total = 0;
@@ -263,9 +264,9 @@ __global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0)
     ctrl->checked_total = 0;
 }
 
-hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, hipStream_t stream)
+hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, hipStream_t stream)
 {
-    hipLaunchKernelGGL(init_ctrl_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0);
+    hipLaunchKernelGGL(init_ctrl_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0, epmin_pad);
     return hipGetLastError();
 }
 
@@ -297,20 +298,24 @@ __device__ __forceinline__ int read_gbest(const Ctrl *ctrl)
     return __builtin_amdgcn_readfirstlane(v);
 }
 
-// Exact re-walk of one body of 32 Gray steps starting at `base`.  E holds the
-// state of the body's last step on entry and on exit.  Every state with
+// Exact walk of one body of 32 Gray steps starting at `base`: every state with
 // E_sd + E_p <= T is recorded per lane (E_sd <= T - E_p needs no overflow
-// headroom: both sides are sub-sums of the folded matrix).
+// headroom: both sides are sub-sums of the folded matrix).  With from_end, E
+// holds the body's last state on entry (a re-walk after the checked body) and
+// is first taken back to the body's first state (over a body the low four Gray
+// bits return to 0 and only bit 4 flips); otherwise E holds the first state.
+// E holds the body's last state on exit.  A compact loop: it runs rarely.
 template <int R>
-__device__ __forceinline__ void slow_body(int (&E)[R], const int (&Mr)[kU][R],
-                                                    uint64_t base, bool top_plus, int T,
-                                                    const int32_t *__restrict__ ep, int B,
-                                                    uint64_t col0, LaneBest &lb)
+__device__ __forceinline__ void exact_body(int (&E)[R], const int (&Mr)[kU][R], uint64_t base,
+                                           bool top_plus, int T, const int32_t *__restrict__ ep,
+                                           int B, uint64_t col0, LaneBest &lb, bool from_end)
 {
-    if (top_plus)
-        sub_row(E, Mr[kU - 1]);
-    else
-        add_row(E, Mr[kU - 1]);
+    if (from_end) {
+        if (top_plus)
+            sub_row(E, Mr[kU - 1]);
+        else
+            add_row(E, Mr[kU - 1]);
+    }
 #pragma unroll 1
     for (int m = 0; m < kBody; ++m) {
         const uint64_t j = base + (uint64_t)m;
@@ -511,14 +516,17 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
         }
 
         // Body minima of the prefix energies are read one body ahead (scalar loads).
+        // The body loop counts with 32-bit scalars (the SALU has no 64-bit
+        // less-than): a segment holds at most 2^15 bodies.
+        const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
         int epm_cur = Gated ? epmin[j_begin >> kU] : 0;
-        for (uint64_t base = j_begin; base < j_end; base += kBody) {
+        for (uint32_t bi = 0; bi < nbodies; ++bi) {
+            const uint64_t base = j_begin + ((uint64_t)bi << kU);
+            const bool last = bi + 1 == nbodies;
             const bool top_plus = ((base >> kU) & 1u) == 0;
             int epm_next = 0;
-            if (Gated) {
-                const uint64_t nb = (base + kBody < j_end) ? (base >> kU) + 1 : (base >> kU);
-                epm_next = epmin[nb];
-            }
+            if (Gated)  // the table has one padding entry past the last body
+                epm_next = epmin[(base >> kU) + 1];
             bool check = true;
             if (Gated) {
                 const int thb = T - epm_cur;
@@ -538,9 +546,19 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 adds_body(E, Mr, top_plus);
             } else {
                 ++checked;
-                const uint64_t acc = checked_body(E, Mr, top_plus, T, ep + base);
-                if (acc) {
-                    slow_body(E, Mr, base, top_plus, T, ep, a.B, col0, lb);
+                bool walked = false;
+                if (Gated) {
+                    // The bound was reached: walk the body exactly (rare).
+                    exact_body(E, Mr, base, top_plus, T, ep, a.B, col0, lb, false);
+                    walked = true;
+                } else {
+                    const uint64_t acc = checked_body(E, Mr, top_plus, T, ep + base);
+                    if (acc) {
+                        exact_body(E, Mr, base, top_plus, T, ep, a.B, col0, lb, true);
+                        walked = true;
+                    }
+                }
+                if (walked) {
                     ++slow_bodies;
                     const int wm = __builtin_amdgcn_readfirstlane(wave_min(lb.e));
                     T = wm < T ? wm : T;
@@ -551,7 +569,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 }
             }
             const uint64_t next = base + kBody;
-            if (next < j_end) {
+            if (!last) {
                 // Flip of Gray bit t >= 5: its row comes from LDS or global memory.
                 const int t = __builtin_ctzll(next);
                 const bool plus = ((next >> (t + 1)) & 1u) == 0;

@@ -160,7 +160,7 @@ Layout layout_of(const qubo_plan &p)
     L.off_ep = off;
     off = align256(off + (1ull << p.prefix_bits) * 4);
     L.off_epmin = off;
-    off = align256(off + (1ull << (p.prefix_bits - kRegBits)) * 4);
+    off = align256(off + ((1ull << (p.prefix_bits - kRegBits)) + 1) * 4);  // + 1 padding entry
     L.off_partials = off;
     off = align256(off + (uint64_t)p.blocks * p.waves_per_block * 32);  // one 32-byte partial per wave
     L.off_ctrl = off;
