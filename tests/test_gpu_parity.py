@@ -199,14 +199,15 @@ def test_subcubes_at_full_size(q):
         plan = q.make_plan(n)
         A = plan["prefix_bits"]
         Qd = dev_q(cfg["Q"])
-        for i, cube in enumerate(g["cubes"][:6]):
+        for i, cube in enumerate(g["cubes"]):
             k, top = cube["k"], cube["top"]
             m = inv_gray(top)
             lo, hi = m << (A - k), (m + 1) << (A - k)
-            strict = bool(i % 2)
-            announce("subcube", name, k, top, strict)
-            r = q.search_range(Qd, A, lo, hi, strict=strict)
+            strict, R = bool(i % 2), (8 if i % 4 < 2 else 16)
+            announce("subcube", name, k, top, strict, R)
+            r = q.search_range(Qd, A, lo, hi, strict=strict, cols_per_lane=R)
             assert r.triple() == (cube["min_energy"], cube["argmin"], cube["count"])
+            check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
 
 
 def test_deterministic(q):
