@@ -59,7 +59,7 @@ typedef struct {
  * parallel split of sec. III.C), as chosen by the host planner. */
 typedef struct {
     int32_t n;               /* variables as given */
-    int32_t n_search;        /* variables searched: n, or 5 for n < 5 (see qubo_search) */
+    int32_t n_search;        /* variables searched per launch: n - split_bits, at least 5 */
     int32_t prefix_bits;     /* A: prefix variables 0..A-1, walked in Gray order */
     int32_t suffix_bits;     /* B = n_search - A: suffix variables, one per column bit */
     int32_t cache_bits;      /* l: Gray bits whose M_int rows are cached on chip
@@ -73,6 +73,10 @@ typedef struct {
     int32_t seg_bits;        /* each wave walks 2^seg_bits consecutive Gray steps per work unit */
     int32_t blocks;          /* persistent workgroups launched */
     int32_t lds_bytes;       /* LDS per workgroup for cached rows */
+    int32_t split_bits;      /* k > 0: the search runs 2^k sub-problems of n - k variables,
+                                one per assignment of variables 0..k-1 (sec. III.C.1);
+                                the other fields describe one sub-problem */
+    int32_t reserved;
     uint64_t col_groups;     /* groups of wave_size * cols_per_lane columns */
     uint64_t work_units;     /* (column group, segment) pairs */
     uint64_t workspace_bytes;/* device memory the search allocates */
@@ -82,6 +86,9 @@ typedef struct {
  *   prefix_bits: A in [5, n], or -1 to let the planner choose;
  *   cache_bits:  l in [5, A], or -1 to let the planner choose.
  * Planned for a 256-CU MI355X (qubo_search re-plans for the device it runs on).
+ * Above 58 variables the search fixes the first n - 58 variables and runs one
+ * launch per assignment (split_bits > 0); prefix_bits and cache_bits then
+ * refer to the 58-variable sub-problems.
  * Returns QUBO_EINVAL for n outside [1, 63], or a split value outside the ranges
  * above, and QUBO_EPLAN when the split exceeds the kernel's limits (prefix-energy
  * table over 2^32 entries, M_int over 2^33 bytes, LDS over 64 KiB). */
@@ -98,7 +105,9 @@ QUBO_API int qubo_check_q(const int32_t *Q_host, int n, int64_t *abs_sum);
  *   Q: device pointer, n x n int32, row-major; read only, owned by the caller.
  *   n: 1..63.  For n < 5 the solver appends 5 - n dummy variables with
  *      Q_ii = +1 and no couplings (they are 0 in every minimiser, so min, argmin
- *      and count are those of the original problem).
+ *      and count are those of the original problem).  For n > 58 it fixes the
+ *      first n - 58 variables and runs one launch per assignment (hours to days
+ *      of GPU time at these sizes).
  *   prefix_bits, cache_bits: as for qubo_make_plan (-1 = planner's choice).  The
  *      result does not depend on them.
  *   out: host pointer; receives {min_energy, argmin, count}.
@@ -155,6 +164,13 @@ QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cac
  * Both give identical results; at most one may be set. */
 #define QUBO_FLAG_COLS8 2u
 #define QUBO_FLAG_COLS16 4u
+/* Outer split (sec. III.C.1): QUBO_FLAG_SPLIT(k) fixes the first k variables
+ * (1 <= k <= n - 5) and searches the 2^k sub-problems one launch after another,
+ * each capped by the best energy found so far; 0 = automatic (only above 58
+ * variables).  Not combinable with a slice (gray_lo/gray_hi). */
+#define QUBO_FLAG_SPLIT_SHIFT 8
+#define QUBO_FLAG_SPLIT_MASK (0x3fu << QUBO_FLAG_SPLIT_SHIFT)
+#define QUBO_FLAG_SPLIT(k) (((uint32_t)(k) << QUBO_FLAG_SPLIT_SHIFT) & QUBO_FLAG_SPLIT_MASK)
 QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
                             uint64_t gray_hi, uint32_t flags, void *stream, qubo_result *out);
 

@@ -46,7 +46,8 @@ class _Result(ctypes.Structure):
 class _Plan(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("n", "n_search", "prefix_bits", "suffix_bits", "cache_bits", "reg_bits",
-                 "cols_per_lane", "wave_size", "waves_per_block", "seg_bits", "blocks", "lds_bytes")] + \
+                 "cols_per_lane", "wave_size", "waves_per_block", "seg_bits", "blocks", "lds_bytes",
+                 "split_bits", "reserved")] + \
                [(name, ctypes.c_uint64) for name in ("col_groups", "work_units", "workspace_bytes")]
 
 
@@ -79,6 +80,7 @@ EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range",
 FLAG_STRICT_MIN = 1
 FLAG_COLS8 = 2
 FLAG_COLS16 = 4
+FLAG_SPLIT_SHIFT = 8
 
 
 def load(path: str = LIB_PATH):
@@ -164,24 +166,30 @@ def _stream(Q, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _flags(strict: bool, cols_per_lane: int | None) -> int:
+def _flags(strict: bool, cols_per_lane: int | None, split_bits: int | None = None) -> int:
     f = FLAG_STRICT_MIN if strict else 0
     if cols_per_lane is not None:
         f |= {8: FLAG_COLS8, 16: FLAG_COLS16}[int(cols_per_lane)]
+    if split_bits:
+        if not 0 < int(split_bits) < 64:
+            raise ValueError("split_bits must be in 1..63")
+        f |= int(split_bits) << FLAG_SPLIT_SHIFT
     return f
 
 
 def search(Q, prefix_bits: int | None = None, cache_bits: int | None = None, stream=None,
-           strict: bool = False, cols_per_lane: int | None = None) -> Result:
+           strict: bool = False, cols_per_lane: int | None = None, split_bits: int | None = None) -> Result:
     """Exhaustive search of min_x x^T Q x over {0,1}^n on Q's device.
 
     strict=True takes the minimum after every prefix (Algorithm 2 as printed)
     instead of gating it by the per-block lower bound; cols_per_lane (8 or 16)
-    picks the kernel build.  The result never depends on these options."""
+    picks the kernel build; split_bits=k searches the 2^k sub-problems with the
+    first k variables fixed, one launch each (automatic above 58 variables).
+    The result never depends on these options."""
     import torch
     Q = _device_q(Q)
     r = _Result()
-    flags = _flags(strict, cols_per_lane)
+    flags = _flags(strict, cols_per_lane, split_bits)
     with torch.cuda.device(Q.device):
         if flags:
             rc = load().qubo_search_ex(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),

@@ -75,40 +75,37 @@ struct Request {
     Mode mode = Mode::Search;
     bool gated = true;
     int cols_per_lane = 0;  // 0: planner's default
+    int split_bits = 0;     // 0: automatic (only above the single-launch limit)
     int32_t *es_out = nullptr, *mint_out = nullptr, *ep_out = nullptr;
 };
 
-int run(const Request &rq, qubo_result *out)
+void add_timing(qubo_timing &acc, const qubo_timing &t)
+{
+    acc.build_ms += t.build_ms;
+    acc.search_ms += t.search_ms;
+    acc.reduce_ms += t.reduce_ms;
+    acc.total_ms += t.total_ms;
+    acc.states += t.states;
+    acc.blocks = t.blocks;
+    acc.bodies += t.bodies;
+    acc.checked_bodies += t.checked_bodies;
+    acc.slow_bodies += t.slow_bodies;
+}
+
+// One search of the folded upper-triangular matrix U (n x n, host memory) on the
+// device.  have_t0: the search only has to find states with E <= t0_cap (the
+// caller knows a real energy that low elsewhere); then an empty result is valid
+// and *found reports whether any state was recorded.
+int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, int n, int64_t abs_sum,
+            bool have_t0, int32_t t0_cap, qubo_result *out, bool *found, qubo_timing *timing)
 {
     using namespace qubo;
-    if (!rq.Q || rq.n < 1 || rq.n > QUBO_MAX_N)
-        return QUBO_EINVAL;
-    if (rq.mode == Mode::Search && !out)
-        return QUBO_EINVAL;
-    DeviceInfo dev;
-    int rc = device_info(&dev);
-    if (rc != QUBO_OK)
-        return rc;
-
     Call call;
     call.stream = rq.stream;
-    const int n = rq.n;
 
-    // 1. Q to the host; fold and guard.
-    std::vector<int32_t> Qh((size_t)n * n);
-    if (hipMemcpyAsync(Qh.data(), rq.Q, Qh.size() * 4, hipMemcpyDeviceToHost, rq.stream) !=
-            hipSuccess ||
-        hipStreamSynchronize(rq.stream) != hipSuccess)
-        return QUBO_EDEVICE;
-    std::vector<int32_t> U;
-    int64_t abs_sum = 0;
-    rc = fold_upper(Qh.data(), n, U, &abs_sum);
-    if (rc != QUBO_OK)
-        return rc;
-
-    // 2. Plan.
+    // Plan.
     qubo_plan plan;
-    rc = make_plan(n, rq.prefix_bits, rq.cache_bits, dev.num_cus, rq.cols_per_lane, &plan);
+    int rc = make_plan(n, rq.prefix_bits, rq.cache_bits, dev.num_cus, rq.cols_per_lane, 0, &plan);
     if (rc != QUBO_OK)
         return rc;
     const int ns = plan.n_search;
@@ -121,6 +118,8 @@ int run(const Request &rq, qubo_result *out)
     if (rq.ranged) {
         lo = rq.gray_lo;
         hi = rq.gray_hi;
+        if (hi > (1ull << A))
+            return QUBO_EINVAL;
     }
     const uint64_t seg_first = lo >> plan.seg_bits;
     const uint64_t seg_last = (hi - 1) >> plan.seg_bits;
@@ -137,7 +136,7 @@ int run(const Request &rq, qubo_result *out)
     plan.blocks = (int)(items < want_blocks ? items : want_blocks);
     const Layout L = layout_of(plan);
 
-    // 3. Workspace.
+    // Workspace.
     if (hipMallocAsync(&call.ws, L.total, rq.stream) != hipSuccess) {
         call.ws = nullptr;
         return QUBO_ENOMEM;
@@ -156,7 +155,7 @@ int run(const Request &rq, qubo_result *out)
             return QUBO_EDEVICE;
     call.events = true;
 
-    // 4. Upload, build, search, reduce.
+    // Upload, build, search, reduce.
     if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     if (hipMemcpyAsync(dU, U.data(), U.size() * 4, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
@@ -183,7 +182,11 @@ int run(const Request &rq, qubo_result *out)
 
     // The first threshold must be a real energy of the searched set or an upper
     // bound of all of them: E(0) = 0 when state 0 is searched, else sum |Q_ij|.
-    const int32_t t0 = (lo == 0) ? 0 : (int32_t)abs_sum;
+    // A caller's cap (an energy found elsewhere) may only lower it; it is never
+    // below -sum |U_ij| here, so every threshold stays within +-2 sum |U_ij|.
+    int32_t t0 = (lo == 0) ? 0 : (int32_t)abs_sum;
+    if (have_t0 && t0_cap < t0)
+        t0 = t0_cap;
     if (launch_init_ctrl(dctrl, t0, depmin + (1ull << (A - kRegBits)), rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
 
@@ -236,17 +239,117 @@ int run(const Request &rq, qubo_result *out)
     t.bodies = host_ctrl.bodies_total;
     t.checked_bodies = host_ctrl.checked_total;
     t.blocks = plan.blocks;
-    g_timing = t;
+    *timing = t;
 
     const Partial &r = host_ctrl.result;
-    if (r.count == 0)
-        return QUBO_EDEVICE;  // every valid search records at least one state
+    *found = r.count != 0;
+    if (!*found) {
+        // Without a cap the threshold was a searched state's energy or an upper
+        // bound, so some state must have been recorded.
+        return have_t0 ? QUBO_OK : QUBO_EDEVICE;
+    }
     qubo_result res{};
     res.min_energy = r.e;
     res.reserved = 0;
     res.argmin = r.arg >> (ns - n);  // padding variables are the lowest bits and 0 at the min
     res.count = r.count;
     *out = res;
+    return QUBO_OK;
+}
+
+int run(const Request &rq, qubo_result *out)
+{
+    using namespace qubo;
+    if (!rq.Q || rq.n < 1 || rq.n > QUBO_MAX_N)
+        return QUBO_EINVAL;
+    if (rq.mode == Mode::Search && !out)
+        return QUBO_EINVAL;
+    const int n = rq.n;
+    // Outer split: fixed first k variables (the straightforward split of sec. III.C.1).
+    int k = rq.split_bits;
+    if (k == 0 && n > kMaxSingleVars)
+        k = n - kMaxSingleVars;
+    if (k < 0 || (k > 0 && (n - k < kMinSearchVars || rq.mode == Mode::Build || rq.ranged)))
+        return QUBO_EINVAL;
+    if (k > kMaxSplitBits)
+        return QUBO_EPLAN;
+    {
+        // Reject an unplannable split before touching the device.
+        qubo_plan probe;
+        const int rc0 = make_plan(n, rq.prefix_bits, rq.cache_bits, 256, rq.cols_per_lane, k, &probe);
+        if (rc0 != QUBO_OK)
+            return rc0;
+    }
+    DeviceInfo dev;
+    int rc = device_info(&dev);
+    if (rc != QUBO_OK)
+        return rc;
+
+    // Q to the host; fold and guard.
+    std::vector<int32_t> Qh((size_t)n * n);
+    if (hipMemcpyAsync(Qh.data(), rq.Q, Qh.size() * 4, hipMemcpyDeviceToHost, rq.stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    std::vector<int32_t> U;
+    int64_t abs_sum = 0;
+    rc = fold_upper(Qh.data(), n, U, &abs_sum);
+    if (rc != QUBO_OK)
+        return rc;
+
+    if (k == 0) {
+        bool found = false;
+        qubo_timing t{};
+        rc = run_one(rq, dev, std::move(U), n, abs_sum, false, 0, out, &found, &t);
+        if (rc == QUBO_OK && rq.mode == Mode::Search)
+            g_timing = t;
+        return rc;
+    }
+
+    // 2^k sub-problems of n - k variables, each with the reduced matrix and the
+    // constant c(x_f); the best energy found so far caps the later ones.
+    const int m = n - k;
+    qubo_timing acc{};
+    qubo_result best{};
+    bool have_best = false;
+    std::vector<int32_t> Usub;
+    for (uint64_t f = 0; f < (1ull << k); ++f) {
+        int64_t c = 0, sub_abs = 0;
+        reduce_fixed(U, n, k, f, Usub, &c, &sub_abs);
+        bool have_cap = false;
+        int32_t cap = 0;
+        if (have_best) {
+            const int64_t cap64 = (int64_t)best.min_energy - c;
+            if (cap64 < -sub_abs)
+                continue;  // every state of this sub-cube is above the best energy found
+            have_cap = true;
+            cap = (int32_t)(cap64 < 0 ? cap64 : 0);
+        }
+        qubo_result sub{};
+        bool found = false;
+        qubo_timing t{};
+        rc = run_one(rq, dev, Usub, m, sub_abs, have_cap, cap, &sub, &found, &t);
+        if (rc != QUBO_OK)
+            return rc;
+        add_timing(acc, t);
+        if (!found)
+            continue;
+        const int64_t e = (int64_t)sub.min_energy + c;
+        const uint64_t idx = (f << m) | sub.argmin;
+        if (!have_best || e < best.min_energy) {
+            best.min_energy = (int32_t)e;
+            best.argmin = idx;
+            best.count = sub.count;
+            have_best = true;
+        } else if (e == best.min_energy) {
+            best.count += sub.count;
+            best.argmin = idx < best.argmin ? idx : best.argmin;
+        }
+    }
+    if (!have_best)
+        return QUBO_EDEVICE;  // the first sub-problem is searched without a cap
+    g_timing = acc;
+    *out = best;
     return QUBO_OK;
 }
 
@@ -257,7 +360,7 @@ extern "C" {
 QUBO_API int qubo_make_plan(int n, int prefix_bits, int cache_bits, qubo_plan *out)
 {
     // Host-only planning for a 256-CU MI355X.
-    return qubo::make_plan(n, prefix_bits, cache_bits, 256, 0, out);
+    return qubo::make_plan(n, prefix_bits, cache_bits, 256, 0, -1, out);
 }
 
 QUBO_API int qubo_check_q(const int32_t *Q_host, int n, int64_t *abs_sum)
@@ -283,7 +386,8 @@ QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bit
 QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
                            uint64_t gray_hi, uint32_t flags, void *stream, qubo_result *out)
 {
-    const uint32_t known = QUBO_FLAG_STRICT_MIN | QUBO_FLAG_COLS8 | QUBO_FLAG_COLS16;
+    const uint32_t known =
+        QUBO_FLAG_STRICT_MIN | QUBO_FLAG_COLS8 | QUBO_FLAG_COLS16 | QUBO_FLAG_SPLIT_MASK;
     if ((flags & ~known) || ((flags & QUBO_FLAG_COLS8) && (flags & QUBO_FLAG_COLS16)))
         return QUBO_EINVAL;
     Request rq;
@@ -293,6 +397,7 @@ QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_
     rq.cache_bits = cache_bits;
     rq.gated = !(flags & QUBO_FLAG_STRICT_MIN);
     rq.cols_per_lane = (flags & QUBO_FLAG_COLS8) ? 8 : (flags & QUBO_FLAG_COLS16) ? 16 : 0;
+    rq.split_bits = (int)((flags & QUBO_FLAG_SPLIT_MASK) >> QUBO_FLAG_SPLIT_SHIFT);
     rq.stream = static_cast<hipStream_t>(stream);
     if (gray_lo != 0 || gray_hi != 0) {
         if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||

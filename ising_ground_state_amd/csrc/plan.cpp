@@ -54,11 +54,50 @@ static int ceil_log2(uint64_t v)
 
 static uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 
-int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, int cols_per_lane,
-              qubo_plan *out)
+void reduce_fixed(const std::vector<int32_t> &U, int n, int k, uint64_t f,
+                  std::vector<int32_t> &Usub, int64_t *c, int64_t *sub_abs)
 {
-    if (!out || n < 1 || n > QUBO_MAX_N || num_cus < 1)
+    const int m = n - k;
+    int64_t cc = 0;
+    for (int v = 0; v < k; ++v) {
+        if (!((f >> (k - 1 - v)) & 1u))
+            continue;
+        for (int w = v; w < k; ++w)
+            if ((f >> (k - 1 - w)) & 1u)
+                cc += U[(size_t)v * n + w];
+    }
+    Usub.assign((size_t)m * m, 0);
+    int64_t s = 0;
+    for (int i = 0; i < m; ++i) {
+        int64_t d = U[(size_t)(k + i) * n + (k + i)];
+        for (int v = 0; v < k; ++v)
+            if ((f >> (k - 1 - v)) & 1u)
+                d += U[(size_t)v * n + (k + i)];
+        Usub[(size_t)i * m + i] = (int32_t)d;
+        s += d < 0 ? -d : d;
+        for (int j = i + 1; j < m; ++j) {
+            const int32_t u = U[(size_t)(k + i) * n + (k + j)];
+            Usub[(size_t)i * m + j] = u;
+            s += u < 0 ? -(int64_t)u : u;
+        }
+    }
+    *c = cc;
+    *sub_abs = s;
+}
+
+int make_plan(int n_total, int prefix_bits, int cache_bits, int num_cus, int cols_per_lane,
+              int split_bits, qubo_plan *out)
+{
+    if (!out || n_total < 1 || n_total > QUBO_MAX_N || num_cus < 1)
         return QUBO_EINVAL;
+    int k = split_bits;
+    if (k < 0)
+        k = n_total > kMaxSingleVars ? n_total - kMaxSingleVars : 0;
+    if (k > 0 && n_total - k < kMinSearchVars)
+        return QUBO_EINVAL;
+    if (k > kMaxSplitBits)
+        return QUBO_EPLAN;
+    const int n = n_total - k;  // variables of each (sub-)problem
     if (cols_per_lane == 0)
         cols_per_lane = kDefaultColsPerLane;
     if (cols_per_lane != 8 && cols_per_lane != 16)
@@ -70,7 +109,8 @@ int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, int cols_per_
         return QUBO_EINVAL;
 
     qubo_plan p{};
-    p.n = n;
+    p.n = n_total;
+    p.split_bits = k;
     p.n_search = std::max(n, kMinSearchVars);
     const int ns = p.n_search;
 

@@ -18,6 +18,8 @@ constexpr int kMinSearchVars = kRegBits; // n below this is padded
 constexpr int kMaxPrefixBits = 32;       // prefix-energy table <= 2^32 entries
 constexpr int kMaxLdsBytes = 65536;      // cached rows per workgroup
 constexpr uint64_t kMaxMintBytes = 1ull << 33;  // 8 GiB
+constexpr int kMaxSingleVars = 58;       // largest n searched by a single launch
+constexpr int kMaxSplitBits = 32;        // at most 2^32 sub-problems
 
 constexpr int64_t kAbsSumLimit = (1ll << 30) - 1;
 
@@ -31,9 +33,20 @@ int fold_upper(const int32_t *Q, int n, std::vector<int32_t> &U, int64_t *abs_su
 std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_search);
 
 // Fills `out` for n variables on a device with `num_cus` compute units;
-// cols_per_lane is 8 or 16, or 0 for the default.
+// cols_per_lane is 8 or 16, or 0 for the default.  split_bits: -1 splits only
+// above kMaxSingleVars (by n - kMaxSingleVars fixed variables), 0 never, k > 0
+// fixes the first k variables; the plan then describes each sub-problem of
+// n - k variables (prefix_bits and cache_bits apply to it).
 int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, int cols_per_lane,
-              qubo_plan *out);
+              int split_bits, qubo_plan *out);
+
+// The straightforward split of sec. III.C.1 for the k-bit assignment f of the
+// first k variables (variable 0 is the most significant bit of f): the folded
+// (n-k) x (n-k) matrix of the remaining variables, with U_ii increased by the
+// couplings to the fixed ones that are set, and the constant c(x_f) = energy of
+// the fixed variables alone.  Writes sum |Usub_ij| to *sub_abs.
+void reduce_fixed(const std::vector<int32_t> &U, int n, int k, uint64_t f,
+                  std::vector<int32_t> &Usub, int64_t *c, int64_t *sub_abs);
 
 // Device workspace layout of a plan (byte offsets, all 256-aligned).
 struct Layout {

@@ -39,10 +39,12 @@ def test_version_and_strerror():
         assert q.strerror(code)
 
 
-@pytest.mark.parametrize("n", [1, 2, 4, 5, 6, 12, 24, 32, 40, 48, 50, 56, 58])
+@pytest.mark.parametrize("n", [1, 2, 4, 5, 6, 12, 24, 32, 40, 48, 50, 56, 58, 59, 63])
 def test_plan_invariants(n):
     p = q.make_plan(n)
-    assert p["n"] == n and p["n_search"] == max(n, 5)
+    k = p["split_bits"]
+    assert k == max(0, n - 58)
+    assert p["n"] == n and p["n_search"] == max(n - k, 5)
     A, B = p["prefix_bits"], p["suffix_bits"]
     assert A + B == p["n_search"] and A >= 5 and A <= 32
     assert 5 <= p["cache_bits"] <= A
@@ -52,7 +54,7 @@ def test_plan_invariants(n):
     assert p["lds_bytes"] == max(0, min(p["cache_bits"], p["seg_bits"]) - 5) * group * 4 <= 65536
     assert p["col_groups"] == max(1, (1 << B) // group)
     assert p["work_units"] == p["col_groups"] << (A - p["seg_bits"])
-    # the whole space is covered: units x steps x columns per group >= 2^n
+    # the whole space is covered: units x steps x columns per group >= 2^n per sub-problem
     assert p["work_units"] * (1 << p["seg_bits"]) * group >= 1 << p["n_search"]
     assert p["workspace_bytes"] >= 4 * ((1 << A) + A * max(1 << B, group))
 
@@ -72,7 +74,7 @@ def test_plan_explicit_splits():
     ((0, -1, -1), q.QUBO_EINVAL), ((64, -1, -1), q.QUBO_EINVAL),
     ((10, 11, -1), q.QUBO_EINVAL), ((10, 8, 9), q.QUBO_EINVAL), ((10, -2, -1), q.QUBO_EINVAL),
     ((10, 4, -1), q.QUBO_EPLAN), ((10, 8, 4), q.QUBO_EPLAN),
-    ((63, -1, -1), q.QUBO_EPLAN), ((40, 33, -1), q.QUBO_EPLAN),
+    ((40, 33, -1), q.QUBO_EPLAN),
 ])
 def test_plan_rejects(args, code):
     with pytest.raises(q.QuboError) as e:

@@ -210,6 +210,24 @@ def test_subcubes_at_full_size(q):
             check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
 
 
+@pytest.mark.parametrize("n,k,seed,lo,hi", [(9, 4, 7501, -50, 50), (14, 3, 7502, -2, 2),
+                                            (20, 6, 7503, -100, 100), (26, 2, 7504, -1, 1)])
+def test_outer_split(q, n, k, seed, lo, hi):
+    """Fixing the first k variables and searching the 2^k reduced sub-problems
+    (sec. III.C.1, used automatically above 58 variables) gives the oracle's
+    answer, ties included; later sub-problems are capped by the best so far."""
+    Q = qi.general_uniform(n, seed, lo, hi)
+    want = oracle.search_gray(Q).triple()
+    Qd = dev_q(Q)
+    for strict in (False, True):
+        announce("split", n, k, seed, strict)
+        assert q.search(Qd, split_bits=k, strict=strict).triple() == want, (k, strict)
+    t = q.last_timing()
+    assert t["states"] <= 1 << n
+    with pytest.raises(q.QuboError):
+        q.search(Qd, split_bits=n - 4)
+
+
 def test_deterministic(q):
     Q = qi.make_config("C2")["Q"]
     Qd = dev_q(Q)
