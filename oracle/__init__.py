@@ -91,6 +91,10 @@ class Oracle:
         lib.oracle_search_gray.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
                                            ctypes.c_int, ctypes.POINTER(_Result)]
         lib.oracle_search_gray.restype = ctypes.c_int
+        lib.oracle_lowest.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_uint64),
+                                      ctypes.POINTER(ctypes.c_int)]
+        lib.oracle_lowest.restype = ctypes.c_int
         lib.oracle_version.restype = ctypes.c_char_p
         self.lib = lib
         self.path = path
@@ -131,6 +135,19 @@ class Oracle:
             raise ValueError("oracle_search_gray failed (%d)" % rc)
         return Result(r.min_energy, r.argmin, r.count, r.max_abs_energy)
 
+    def lowest(self, Q, k: int, gray_walk: bool = True, threads: int | None = None) -> list[tuple[int, int]]:
+        """The k lowest states as (E, index) pairs, ordered by E then index."""
+        q = _qarray(Q)
+        e = np.zeros(k, dtype=np.int64)
+        ix = np.zeros(k, dtype=np.uint64)
+        found = ctypes.c_int(0)
+        rc = self.lib.oracle_lowest(_ptr(q), q.shape[0], k, 1 if gray_walk else 0, threads or default_threads(),
+                                    e.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                    ix.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), ctypes.byref(found))
+        if rc != 0:
+            raise ValueError("oracle_lowest failed (%d)" % rc)
+        return [(int(e[i]), int(ix[i])) for i in range(found.value)]
+
     def version(self) -> str:
         return self.lib.oracle_version().decode()
 
@@ -161,6 +178,10 @@ def search_direct(Q, lo: int = 0, hi: int | None = None, threads: int | None = N
 
 def search_gray(Q, k: int = 0, top: int = 0, threads: int | None = None) -> Result:
     return default().search_gray(Q, k, top, threads)
+
+
+def lowest(Q, k: int, gray_walk: bool = True, threads: int | None = None) -> list[tuple[int, int]]:
+    return default().lowest(Q, k, gray_walk, threads)
 
 
 def version() -> str:

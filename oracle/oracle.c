@@ -28,6 +28,13 @@
  *          explicit index comparison, because Gray order is not index order.
  * Work is split into contiguous ranges over POSIX threads and merged with the
  * rule (min energy; sum of counts at the min; min index at the min).
+ *
+ * The low-energy spectrum (same paper, sec. VI.B, "Future Work": keep a list of
+ * the k lowest energies instead of one minimum): the first k states in the
+ * order (E ascending, index ascending), each walker keeping its own sorted list
+ * and the lists of disjoint ranges merged by the same order.  Which of several
+ * equal energies at the k-th place to keep is not said; the lower index is this
+ * library's reading, as for the single minimiser.
  */
 #include <pthread.h>
 #include <stdint.h>
@@ -38,6 +45,7 @@
 
 #define ORACLE_MAX_N 63
 #define ORACLE_MAX_THREADS 512
+#define ORACLE_MAX_LOWEST 1024
 
 /* Mutation testing of the pins: building with -DORACLE_MUTATION=k (k > 0)
  * plants one deliberate, plausible mistake so that the test suite can show
@@ -176,6 +184,40 @@ int oracle_search_direct(const int32_t *Q, int n, uint64_t lo, uint64_t hi, int 
 }
 
 /* ------------------------------------------------------------------ */
+/* The k lowest states: the first k states in the order (E ascending,  */
+/* index ascending).  A walker keeps a sorted list of at most k        */
+/* (E, idx) pairs; lists of disjoint ranges merge by the same order.   */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    int64_t e;
+    uint64_t idx;
+} oracle_state;
+
+static int state_less(const oracle_state *a, int64_t e, uint64_t idx)
+{
+    /* MUTANT(5) here: equal energies stay in the order they were met */
+    return a->e < e || (a->e == e && (MUTANT(5) || a->idx < idx));
+}
+
+/* Inserts (e, idx) into the sorted list l of *len <= k entries. */
+static void keep_lowest(oracle_state *l, int *len, int k, int64_t e, uint64_t idx)
+{
+    int pos = *len;
+    while (pos > 0 && !state_less(&l[pos - 1], e, idx))
+        --pos;
+    if (pos >= (MUTANT(10) ? k - 1 : k))
+        return;
+    int last = *len < k ? *len : k - 1;
+    for (int i = last; i > pos; --i)
+        l[i] = l[i - 1];
+    l[pos].e = e;
+    l[pos].idx = idx;
+    if (*len < k)
+        ++*len;
+}
+
+/* ------------------------------------------------------------------ */
 /* Tier B: incremental Gray-code walk over a sub-cube.                */
 /*                                                                    */
 /* The sub-cube fixes variables 0..k-1 to the k-bit number `top`       */
@@ -189,6 +231,9 @@ typedef struct {
     uint64_t top;
     uint64_t i_lo, i_hi; /* Gray counter range over the free variables */
     oracle_result res;
+    int keep;             /* > 0: also keep the `keep` lowest states in list */
+    int len;
+    oracle_state list[ORACLE_MAX_LOWEST];
 } gray_job;
 
 static uint64_t gray(uint64_t i) { return i ^ (i >> 1); }
@@ -208,6 +253,7 @@ static void gray_range(gray_job *job)
     const int32_t *Q = job->Q;
     const int n = job->n, m = n - job->k;
     memset(&job->res, 0, sizeof(job->res));
+    job->len = 0;
     if (job->i_lo >= job->i_hi)
         return;
 
@@ -234,6 +280,8 @@ static void gray_range(gray_job *job)
         field[v] = f;
     }
     record(&job->res, e, idx);
+    if (job->keep)
+        keep_lowest(job->list, &job->len, job->keep, e, idx);
 
     for (uint64_t i = job->i_lo; i + 1 < job->i_hi; ++i) {
         int t = ctz64(i + 1);   /* Gray counter bit that flips ... */
@@ -252,6 +300,8 @@ static void gray_range(gray_job *job)
         }
         idx ^= 1ull << t;
         record(&job->res, e, idx);
+        if (job->keep)
+            keep_lowest(job->list, &job->len, job->keep, e, idx);
     }
 }
 
@@ -268,14 +318,11 @@ static void *gray_worker(void *arg)
     return NULL;
 }
 
-int oracle_search_gray(const int32_t *Q, int n, int k, uint64_t top, int threads,
-                       oracle_result *out)
+/* Runs the Gray walk of the sub-cube (k, top) in pieces over the threads;
+ * returns the pieces (caller frees) or NULL when out of memory. */
+static gray_job *run_gray(const int32_t *Q, int n, int k, uint64_t top, int threads, int keep,
+                          uint64_t *npieces)
 {
-    if (!Q || !out || n < 1 || n > ORACLE_MAX_N || k < 0 || k > n)
-        return -1;
-    if (top >= (1ull << k))
-        return -1;
-    memset(out, 0, sizeof(*out));
     const int m = n - k;
     const uint64_t total = 1ull << m;
     threads = clamp_threads(threads);
@@ -292,13 +339,14 @@ int oracle_search_gray(const int32_t *Q, int n, int k, uint64_t top, int threads
         free(jobs);
         free(args);
         free(tids);
-        return -2;
+        return NULL;
     }
     for (uint64_t p = 0; p < pieces; ++p) {
         jobs[p].Q = Q;
         jobs[p].n = n;
         jobs[p].k = k;
         jobs[p].top = top;
+        jobs[p].keep = keep;
         jobs[p].i_lo = total * p / pieces;      /* total <= 2^63, pieces <= 4096 */
         jobs[p].i_hi = total * (p + 1) / pieces;
     }
@@ -313,11 +361,57 @@ int oracle_search_gray(const int32_t *Q, int n, int k, uint64_t top, int threads
     gray_worker(&args[0]);
     for (int t = 1; t < threads; ++t)
         pthread_join(tids[t], NULL);
+    free(args);
+    free(tids);
+    *npieces = pieces;
+    return jobs;
+}
+
+int oracle_search_gray(const int32_t *Q, int n, int k, uint64_t top, int threads,
+                       oracle_result *out)
+{
+    if (!Q || !out || n < 1 || n > ORACLE_MAX_N || k < 0 || k > n)
+        return -1;
+    if (top >= (1ull << k))
+        return -1;
+    memset(out, 0, sizeof(*out));
+    uint64_t pieces = 0;
+    gray_job *jobs = run_gray(Q, n, k, top, threads, 0, &pieces);
+    if (!jobs)
+        return -2;
     for (uint64_t p = 0; p < pieces; ++p)
         merge(out, &jobs[p].res);
     free(jobs);
-    free(args);
-    free(tids);
+    return 0;
+}
+
+int oracle_lowest(const int32_t *Q, int n, int k, int gray_walk, int threads, int64_t *energies,
+                  uint64_t *indices, int *found)
+{
+    if (!Q || !energies || !indices || !found || n < 1 || n > ORACLE_MAX_N || k < 1 ||
+        k > ORACLE_MAX_LOWEST)
+        return -1;
+    oracle_state merged[ORACLE_MAX_LOWEST];
+    int len = 0;
+    if (gray_walk) {
+        uint64_t pieces = 0;
+        gray_job *jobs = run_gray(Q, n, 0, 0, threads, k, &pieces);
+        if (!jobs)
+            return -2;
+        for (uint64_t p = 0; p < pieces; ++p)
+            for (int i = 0; i < jobs[p].len; ++i)
+                keep_lowest(merged, &len, k, jobs[p].list[i].e, jobs[p].list[i].idx);
+        free(jobs);
+    } else {
+        /* tier A: every state from the definition, in index order, one thread */
+        for (uint64_t idx = 0; idx < (1ull << n); ++idx)
+            keep_lowest(merged, &len, k, oracle_energy(Q, n, idx), idx);
+    }
+    for (int i = 0; i < len; ++i) {
+        energies[i] = merged[i].e;
+        indices[i] = merged[i].idx;
+    }
+    *found = len;
     return 0;
 }
 

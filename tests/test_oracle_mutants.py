@@ -3,8 +3,9 @@
 Each build with -DORACLE_MUTATION=k plants one plausible mistake in the CPU
 oracle (on the CPU only): a dropped diagonal, a reversed bit order, a wrong sign
 in the Gray update, a missing field update, a traversal-order tie-break, a
-count that ignores ties, a field without its diagonal, a dropped x_j factor and
-a flip applied to the wrong variable.  The pin suite must reject every one.
+count that ignores ties, a field without its diagonal, a dropped x_j factor,
+a flip applied to the wrong variable and an off-by-one in the k-lowest list.
+The pin suite must reject every one.
 """
 import pytest
 
@@ -21,6 +22,7 @@ MUTANTS = {
     7: "initial fields miss the diagonal",
     8: "energy drops the x_j factor",
     9: "Gray walk flips variable t instead of n-1-t",
+    10: "the k-lowest list never fills its last slot after it is full",
 }
 
 

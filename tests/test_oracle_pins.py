@@ -185,8 +185,52 @@ def pin_invariances(o: oracle.Oracle):
     assert r3.triple() == (3 * base.min_energy, base.argmin, base.count)
 
 
+def numpy_lowest(Q, k):
+    """The k lowest (E, index) pairs of x^T Q x over every state, ordered by E
+    then index, from a numpy sort (n <= 12)."""
+    Q = np.asarray(Q, dtype=np.int64)
+    n = Q.shape[0]
+    idx = np.arange(1 << n, dtype=np.int64)
+    X = ((idx[:, None] >> (n - 1 - np.arange(n))[None, :]) & 1).astype(np.int64)
+    E = np.einsum("si,ij,sj->s", X, Q, X)
+    order = np.lexsort((idx, E))[:k]
+    return [(int(E[i]), int(i)) for i in order]
+
+
+def pin_lowest(o: oracle.Oracle):
+    """The k lowest states (the low-energy spectrum)."""
+    for n, seed, lo, hi in [(1, 2601, -5, 5), (4, 2602, -2, 2), (7, 2603, -1, 1), (9, 2604, -50, 50),
+                            (10, 2605, -1, 1), (11, 2606, -3, 3)]:
+        Q = rand_general(n, seed, lo, hi)
+        for k in (1, 5, 64, (1 << n) + 3):
+            k = min(k, 1024)
+            want = numpy_lowest(Q, k)
+            assert o.lowest(Q, k, gray_walk=True, threads=3) == want, (n, seed, k)
+            if n <= 10:
+                assert o.lowest(Q, k, gray_walk=False) == want, (n, seed, k)
+        # the list begins with every minimiser, in index order
+        m = o.search_gray(Q)
+        low = o.lowest(Q, min(1 << n, 1024))
+        assert low[0] == (m.min_energy, m.argmin), (n, seed)
+        assert sum(1 for e, _ in low if e == m.min_energy) == m.count, (n, seed)
+    # Q = 0: every state has E = 0, so the list is the first k indices
+    for n in (3, 12):
+        assert o.lowest(qi.zeros(n), 8) == [(0, i) for i in range(8)]
+    # positive diagonal, no couplings: E is a sum of distinct weights 2^i,
+    # so the spectrum is the states ordered by E, each E met once
+    n = 6
+    pos = qi.zeros(n)
+    for i in range(n):
+        pos[i][i] = 1 << i          # variable i has weight 2^i -> E = reverse-bit value
+    low = o.lowest(pos, 1 << n)
+    assert [e for e, _ in low] == list(range(1 << n))
+    for e, idx in low:
+        assert sum(1 << i for i in range(n) if (idx >> (n - 1 - i)) & 1) == e
+
+
 ALL_PINS = [pin_worked_examples, pin_closed_forms, pin_numpy_third_implementation, pin_tiers_agree,
-            pin_special_cases, pin_planted, pin_mattis, pin_ising_identity, pin_invariances]
+            pin_special_cases, pin_planted, pin_mattis, pin_ising_identity, pin_invariances,
+            pin_lowest]
 
 
 # -------------------------------------------------------------------------- tests
