@@ -128,9 +128,9 @@ typedef struct {
     uint64_t states;  /* states searched */
     int32_t blocks;   /* workgroups launched */
     uint32_t reserved;
-    uint64_t bodies;  /* 32-step bodies walked, each over 1024 suffix columns (coverage:
-                         bodies x 32 x 1024 = states, padding columns included, when
-                         2^B >= 1024) */
+    uint64_t bodies;  /* 32-step bodies walked, each over the 64 x cols_per_lane suffix
+                         columns of one wave (coverage: bodies x 32 x 64 x cols_per_lane
+                         = Gray steps x 2^B rounded up to whole column groups) */
     uint64_t checked_bodies; /* bodies that ran the per-step minimum (all of them in strict mode) */
     uint64_t slow_bodies;    /* bodies re-walked on the exact path (records and ties) */
 } qubo_timing;
@@ -173,6 +173,35 @@ QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cac
 #define QUBO_FLAG_SPLIT(k) (((uint32_t)(k) << QUBO_FLAG_SPLIT_SHIFT) & QUBO_FLAG_SPLIT_MASK)
 QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
                             uint64_t gray_hi, uint32_t flags, void *stream, qubo_result *out);
+
+/* The low-energy spectrum: the k lowest states (sec. VI.B, "Future Work",
+ * proposes keeping a list of the k lowest energies in the kernel instead of one
+ * minimum; sec. I.D notes that brute force gives the low-energy spectrum).
+ * The order is energy ascending, then index ascending: the result is the first
+ * k states of that order, which is unique.  One entry (16 bytes): */
+typedef struct {
+    int32_t energy;   /* E(x) */
+    uint32_t reserved;/* zero */
+    uint64_t index;   /* idx(x), variable 0 most significant */
+} qubo_state;
+#define QUBO_MAX_LOWEST 64
+/* Q, n, prefix_bits, cache_bits, gray_lo, gray_hi, stream: as for
+ * qubo_search_ex (a slice restricts the spectrum to the slice's states).
+ *   k: 1..QUBO_MAX_LOWEST.
+ *   flags: QUBO_FLAG_COLS8 / QUBO_FLAG_COLS16 / QUBO_FLAG_SPLIT(k) as for
+ *      qubo_search_ex; QUBO_FLAG_STRICT_MIN is rejected (the spectrum search is
+ *      always bound-gated).  Above 58 variables the sub-problems run in order,
+ *      each capped by the k-th energy found so far.
+ *   out: host pointer to k entries; entries 0..*found-1 receive the states in
+ *      order, the rest are left untouched.
+ *   found: host pointer; min(k, number of states searched).
+ * Each wave of the search keeps its own k lowest states, one per lane; the
+ * threshold of the bound gate is the lowest k-th energy of any wave so far.  A
+ * final one-workgroup kernel merges the per-wave lists.  Blocking; same
+ * ownership and error behaviour as qubo_search_ex. */
+QUBO_API int qubo_search_lowest(const int32_t *Q, int n, int k, int prefix_bits, int cache_bits,
+                                uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
+                                qubo_state *out, int *found);
 
 /* Builds the cache tables of a plan into caller-provided device buffers, for
  * inspection (sec. III.A preprocessing steps 1-3, eq. 8):

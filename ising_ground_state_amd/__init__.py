@@ -8,6 +8,7 @@ library is missing: there is no CPU fallback.
     import torch, ising_ground_state_amd as q
     Q = torch.tensor(..., dtype=torch.int32, device="cuda")
     r = q.search(Q)            # r.min_energy, r.argmin, r.count
+    low = q.lowest(Q, 10)      # the 10 lowest (energy, index) pairs
 
 Method: Maltsev et al., "Terastate-per-second QUBO Brute-Force on a Single GPU:
 A Matrix Prefix-Suffix Decomposition" (prefix-suffix split, sec. II; Gray-code
@@ -43,6 +44,10 @@ class _Result(ctypes.Structure):
                 ("argmin", ctypes.c_uint64), ("count", ctypes.c_uint64)]
 
 
+class _State(ctypes.Structure):
+    _fields_ = [("energy", ctypes.c_int32), ("reserved", ctypes.c_uint32), ("index", ctypes.c_uint64)]
+
+
 class _Plan(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("n", "n_search", "prefix_bits", "suffix_bits", "cache_bits", "reg_bits",
@@ -76,7 +81,8 @@ class Result:
 _lib = None
 
 EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range", "qubo_search_ex",
-           "qubo_build_tables", "qubo_last_timing", "qubo_strerror", "qubo_version")
+           "qubo_build_tables", "qubo_last_timing", "qubo_search_lowest", "qubo_strerror", "qubo_version")
+MAX_LOWEST = 64
 FLAG_STRICT_MIN = 1
 FLAG_COLS8 = 2
 FLAG_COLS16 = 4
@@ -104,10 +110,13 @@ def load(path: str = LIB_PATH):
     lib.qubo_build_tables.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p]
     lib.qubo_last_timing.argtypes = [ctypes.POINTER(_Timing)]
+    lib.qubo_search_lowest.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p,
+                                       ctypes.POINTER(_State), ctypes.POINTER(ctypes.c_int)]
     lib.qubo_strerror.argtypes = [ctypes.c_int]
     lib.qubo_strerror.restype = ctypes.c_char_p
     lib.qubo_version.restype = ctypes.c_char_p
-    for name in EXPORTS[:7]:
+    for name in EXPORTS[:8]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -216,6 +225,27 @@ def search_range(Q, prefix_bits: int, gray_lo: int, gray_hi: int, cache_bits: in
     if rc != QUBO_OK:
         raise QuboError(rc, "qubo_search_range")
     return Result(r.min_energy, r.argmin, r.count)
+
+
+def lowest(Q, k: int, prefix_bits: int | None = None, cache_bits: int | None = None, stream=None,
+           cols_per_lane: int | None = None, split_bits: int | None = None, gray_lo: int = 0,
+           gray_hi: int = 0) -> list[tuple[int, int]]:
+    """The k lowest states (k <= 64) as (energy, index) pairs, energy ascending
+    then index ascending: the low-energy spectrum.  gray_lo/gray_hi select a
+    slice as in search_range (prefix_bits must then be given)."""
+    import torch
+    Q = _device_q(Q)
+    k = int(k)
+    out = (_State * max(k, 1))()
+    found = ctypes.c_int(0)
+    with torch.cuda.device(Q.device):
+        rc = load().qubo_search_lowest(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], k, _opt(prefix_bits),
+                                       _opt(cache_bits), int(gray_lo), int(gray_hi),
+                                       _flags(False, cols_per_lane, split_bits), _stream(Q, stream),
+                                       out, ctypes.byref(found))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_search_lowest")
+    return [(out[i].energy, out[i].index) for i in range(found.value)]
 
 
 def build_tables(Q, prefix_bits: int, stream=None):

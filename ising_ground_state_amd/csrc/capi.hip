@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstring>
+#include <iterator>
 #include <vector>
 
 #include "kernels.h"
@@ -76,8 +77,25 @@ struct Request {
     bool gated = true;
     int cols_per_lane = 0;  // 0: planner's default
     int split_bits = 0;     // 0: automatic (only above the single-launch limit)
+    int lowest_k = 0;       // > 0: the spectrum search (the lowest_k lowest states)
     int32_t *es_out = nullptr, *mint_out = nullptr, *ep_out = nullptr;
 };
+
+static_assert(sizeof(qubo::LowEntry) == sizeof(qubo_state), "list entry layout");
+
+// Keeps the k first states of `acc` merged with `add`, in (energy, index) order.
+void merge_lowest(std::vector<qubo_state> &acc, const std::vector<qubo_state> &add, int k)
+{
+    std::vector<qubo_state> m;
+    m.reserve(acc.size() + add.size());
+    std::merge(acc.begin(), acc.end(), add.begin(), add.end(), std::back_inserter(m),
+               [](const qubo_state &a, const qubo_state &b) {
+                   return a.energy < b.energy || (a.energy == b.energy && a.index < b.index);
+               });
+    if ((int)m.size() > k)
+        m.resize((size_t)k);
+    acc.swap(m);
+}
 
 void add_timing(qubo_timing &acc, const qubo_timing &t)
 {
@@ -94,10 +112,13 @@ void add_timing(qubo_timing &acc, const qubo_timing &t)
 
 // One search of the folded upper-triangular matrix U (n x n, host memory) on the
 // device.  have_t0: the search only has to find states with E <= t0_cap (the
-// caller knows a real energy that low elsewhere); then an empty result is valid
-// and *found reports whether any state was recorded.
+// caller knows a real energy that low elsewhere, or k of them for the
+// spectrum); then an empty result is valid and *found reports whether any
+// state was recorded.  The spectrum search (rq.lowest_k > 0) writes its states
+// to *low, in order, and leaves *out alone.
 int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, int n, int64_t abs_sum,
-            bool have_t0, int32_t t0_cap, qubo_result *out, bool *found, qubo_timing *timing)
+            bool have_t0, int32_t t0_cap, qubo_result *out, bool *found, qubo_timing *timing,
+            std::vector<qubo_state> *low = nullptr)
 {
     using namespace qubo;
     Call call;
@@ -112,6 +133,12 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     if (ns != n)
         U = pad_upper(U, n, ns);
     const int A = plan.prefix_bits, B = plan.suffix_bits;
+    const bool lowest = rq.lowest_k > 0;
+    // With padding variables (n < 5, so 2^ns = 32 states) the list keeps every
+    // state; the padded ones are dropped afterwards.
+    const int k_low = !lowest ? 0 : (ns != n ? (1 << ns) : rq.lowest_k);
+    if (lowest && (k_low < 1 || k_low > kMaxLowest))
+        return QUBO_EINVAL;
 
     // Work range in Gray steps and its segments.
     uint64_t lo = 0, hi = 1ull << A;
@@ -128,16 +155,23 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     const uint64_t items = plan.col_groups * seg_blocks;
 
     int per_cu = 0;
-    if (search_occupancy(plan.cols_per_lane, rq.gated, &per_cu, plan.lds_bytes) != hipSuccess)
+    if (search_occupancy(plan.cols_per_lane, rq.gated, lowest, &per_cu, plan.lds_bytes) !=
+        hipSuccess)
         return QUBO_EDEVICE;
     if (per_cu < 1)
         per_cu = 1;
     const uint64_t want_blocks = (uint64_t)dev.num_cus * (uint64_t)per_cu;
     plan.blocks = (int)(items < want_blocks ? items : want_blocks);
     const Layout L = layout_of(plan);
+    // The spectrum search appends the per-wave lists, the merged list and its size.
+    const uint64_t list_entries = lowest ? (uint64_t)plan.blocks * plan.waves_per_block * k_low : 0;
+    const uint64_t off_lists = (L.total + 255) & ~uint64_t(255);
+    const uint64_t off_low_out = off_lists + ((list_entries * sizeof(LowEntry) + 255) & ~uint64_t(255));
+    const uint64_t off_low_found = off_low_out + kMaxLowest * sizeof(LowEntry);
+    const uint64_t ws_total = lowest ? off_low_found + 256 : L.total;
 
     // Workspace.
-    if (hipMallocAsync(&call.ws, L.total, rq.stream) != hipSuccess) {
+    if (hipMallocAsync(&call.ws, ws_total, rq.stream) != hipSuccess) {
         call.ws = nullptr;
         return QUBO_ENOMEM;
     }
@@ -181,10 +215,12 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     }
 
     // The first threshold must be a real energy of the searched set or an upper
-    // bound of all of them: E(0) = 0 when state 0 is searched, else sum |Q_ij|.
-    // A caller's cap (an energy found elsewhere) may only lower it; it is never
-    // below -sum |U_ij| here, so every threshold stays within +-2 sum |U_ij|.
-    int32_t t0 = (lo == 0) ? 0 : (int32_t)abs_sum;
+    // bound of all of them: E(0) = 0 when state 0 is searched, else sum |Q_ij|
+    // (always sum |Q_ij| for the spectrum, whose threshold bounds the k-th
+    // energy).  A caller's cap (an energy found elsewhere) may only lower it; it
+    // is never below -sum |U_ij| here, so every threshold stays within
+    // +-2 sum |U_ij|.
+    int32_t t0 = (lo == 0 && !lowest) ? 0 : (int32_t)abs_sum;
     if (have_t0 && t0_cap < t0)
         t0 = t0_cap;
     if (launch_init_ctrl(dctrl, t0, depmin + (1ull << (A - kRegBits)), rq.stream) != hipSuccess)
@@ -208,19 +244,38 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     sa.B = B;
     sa.l_eff = plan.cache_bits < plan.seg_bits ? plan.cache_bits : plan.seg_bits;
     sa.seg_bits = plan.seg_bits;
-    if (launch_search(sa, plan.cols_per_lane, rq.gated, plan.blocks, plan.lds_bytes, rq.stream) !=
-        hipSuccess)
+    LowEntry *dlists = reinterpret_cast<LowEntry *>(base + off_lists);
+    LowEntry *dlow = reinterpret_cast<LowEntry *>(base + off_low_out);
+    int32_t *dlow_found = reinterpret_cast<int32_t *>(base + off_low_found);
+    if (lowest) {
+        sa.lists = dlists;
+        sa.k_low = k_low;
+    }
+    if (launch_search(sa, plan.cols_per_lane, rq.gated, lowest, plan.blocks, plan.lds_bytes,
+                      rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[2], rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     if (launch_reduce(dpart, plan.blocks * plan.waves_per_block, dctrl, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
+    if (lowest && launch_lowest_merge(dlists, list_entries, k_low, dlow, dlow_found, rq.stream) !=
+                      hipSuccess)
+        return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[3], rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     Ctrl host_ctrl;
+    LowEntry host_low[kMaxLowest];
+    int32_t host_low_found = 0;
     if (hipMemcpyAsync(&host_ctrl, dctrl, sizeof(Ctrl), hipMemcpyDeviceToHost, rq.stream) !=
-            hipSuccess ||
-        hipEventRecord(call.ev[4], rq.stream) != hipSuccess ||
+        hipSuccess)
+        return QUBO_EDEVICE;
+    if (lowest &&
+        (hipMemcpyAsync(host_low, dlow, sizeof(host_low), hipMemcpyDeviceToHost, rq.stream) !=
+             hipSuccess ||
+         hipMemcpyAsync(&host_low_found, dlow_found, sizeof(int32_t), hipMemcpyDeviceToHost,
+                        rq.stream) != hipSuccess))
+        return QUBO_EDEVICE;
+    if (hipEventRecord(call.ev[4], rq.stream) != hipSuccess ||
         hipStreamSynchronize(rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
 
@@ -241,6 +296,34 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     t.blocks = plan.blocks;
     *timing = t;
 
+    if (lowest) {
+        if (host_low_found < 0 || host_low_found > k_low)
+            return QUBO_EDEVICE;
+        low->clear();
+        const int pad = ns - n;
+        for (int i = 0; i < host_low_found; ++i) {
+            const LowEntry &le = host_low[i];
+            if (le.x & ((1ull << pad) - 1))
+                continue;  // a padding variable is set: not a state of the problem
+            qubo_state st;
+            st.energy = le.e;
+            st.reserved = 0;
+            st.index = le.x >> pad;
+            low->push_back(st);
+            if ((int)low->size() == rq.lowest_k)
+                break;
+        }
+        // Without a cap the first threshold bounds every energy of the problem
+        // (padded states may exceed it; they are dropped anyway), so every state
+        // was offered and min(k, states searched) of them must be listed.
+        const uint64_t states = t.states >> pad;
+        const uint64_t expect = states < (uint64_t)rq.lowest_k ? states : (uint64_t)rq.lowest_k;
+        if (!have_t0 && low->size() != expect)
+            return QUBO_EDEVICE;
+        *found = !low->empty();
+        return QUBO_OK;
+    }
+
     const Partial &r = host_ctrl.result;
     *found = r.count != 0;
     if (!*found) {
@@ -257,12 +340,16 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     return QUBO_OK;
 }
 
-int run(const Request &rq, qubo_result *out)
+int run(const Request &rq, qubo_result *out, qubo_state *low_out = nullptr,
+        int *low_found = nullptr)
 {
     using namespace qubo;
+    const bool lowest = rq.lowest_k > 0;
     if (!rq.Q || rq.n < 1 || rq.n > QUBO_MAX_N)
         return QUBO_EINVAL;
-    if (rq.mode == Mode::Search && !out)
+    if (rq.mode == Mode::Search && !lowest && !out)
+        return QUBO_EINVAL;
+    if (lowest && (!low_out || !low_found || rq.lowest_k > kMaxLowest || !rq.gated))
         return QUBO_EINVAL;
     const int n = rq.n;
     // Outer split: fixed first k variables (the straightforward split of sec. III.C.1).
@@ -300,10 +387,53 @@ int run(const Request &rq, qubo_result *out)
     if (k == 0) {
         bool found = false;
         qubo_timing t{};
-        rc = run_one(rq, dev, std::move(U), n, abs_sum, false, 0, out, &found, &t);
+        std::vector<qubo_state> low;
+        rc = run_one(rq, dev, std::move(U), n, abs_sum, false, 0, out, &found, &t, &low);
         if (rc == QUBO_OK && rq.mode == Mode::Search)
             g_timing = t;
+        if (rc == QUBO_OK && lowest) {
+            std::copy(low.begin(), low.end(), low_out);
+            *low_found = (int)low.size();
+        }
         return rc;
+    }
+
+    if (lowest) {
+        // 2^k sub-problems; once k states are known, their k-th energy caps the
+        // later sub-problems, and a sub-cube whose every state lies above it is
+        // skipped.
+        const int m = n - k;
+        qubo_timing acc{};
+        std::vector<qubo_state> best, sub;
+        std::vector<int32_t> Usub;
+        for (uint64_t f = 0; f < (1ull << k); ++f) {
+            int64_t c = 0, sub_abs = 0;
+            reduce_fixed(U, n, k, f, Usub, &c, &sub_abs);
+            bool have_cap = false;
+            int32_t cap = 0;
+            if ((int)best.size() == rq.lowest_k) {
+                const int64_t cap64 = (int64_t)best.back().energy - c;
+                if (cap64 < -sub_abs)
+                    continue;
+                have_cap = true;
+                cap = (int32_t)(cap64 < sub_abs ? cap64 : sub_abs);
+            }
+            bool found = false;
+            qubo_timing t{};
+            rc = run_one(rq, dev, Usub, m, sub_abs, have_cap, cap, nullptr, &found, &t, &sub);
+            if (rc != QUBO_OK)
+                return rc;
+            add_timing(acc, t);
+            for (auto &st : sub) {
+                st.energy = (int32_t)((int64_t)st.energy + c);
+                st.index |= f << m;
+            }
+            merge_lowest(best, sub, rq.lowest_k);
+        }
+        g_timing = acc;
+        std::copy(best.begin(), best.end(), low_out);
+        *low_found = (int)best.size();
+        return QUBO_OK;
     }
 
     // 2^k sub-problems of n - k variables, each with the reduced matrix and the
@@ -413,6 +543,38 @@ QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_
     return run(rq, out);
 }
 
+QUBO_API int qubo_search_lowest(const int32_t *Q, int n, int k, int prefix_bits, int cache_bits,
+                                uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
+                                qubo_state *out, int *found)
+{
+    const uint32_t known = QUBO_FLAG_COLS8 | QUBO_FLAG_COLS16 | QUBO_FLAG_SPLIT_MASK;
+    if ((flags & ~known) || ((flags & QUBO_FLAG_COLS8) && (flags & QUBO_FLAG_COLS16)))
+        return QUBO_EINVAL;
+    if (!out || !found || k < 1 || k > QUBO_MAX_LOWEST)
+        return QUBO_EINVAL;
+    Request rq;
+    rq.Q = Q;
+    rq.n = n;
+    rq.prefix_bits = prefix_bits;
+    rq.cache_bits = cache_bits;
+    rq.cols_per_lane = (flags & QUBO_FLAG_COLS8) ? 8 : (flags & QUBO_FLAG_COLS16) ? 16 : 0;
+    rq.split_bits = (int)((flags & QUBO_FLAG_SPLIT_MASK) >> QUBO_FLAG_SPLIT_SHIFT);
+    rq.lowest_k = k;
+    rq.stream = static_cast<hipStream_t>(stream);
+    if (gray_lo != 0 || gray_hi != 0) {
+        if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||
+            prefix_bits > qubo::kMaxPrefixBits)
+            return QUBO_EINVAL;
+        if ((gray_lo & 31u) || (gray_hi & 31u) || gray_lo >= gray_hi ||
+            gray_hi > (1ull << prefix_bits))
+            return QUBO_EINVAL;
+        rq.ranged = true;
+        rq.gray_lo = gray_lo;
+        rq.gray_hi = gray_hi;
+    }
+    return run(rq, nullptr, out, found);
+}
+
 QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cache_bits, uint64_t gray_lo,
                       uint64_t gray_hi, void *stream, qubo_result *out)
 {
@@ -470,7 +632,7 @@ QUBO_API const char *qubo_strerror(int status)
 
 QUBO_API const char *qubo_version(void)
 {
-    return "qubo-mi355x 0.1 (gfx950; 16 columns/lane, 5 register Gray bits, int32)";
+    return "qubo-mi355x 0.2 (gfx950; 8 or 16 columns/lane, 5 register Gray bits, int32; k-lowest)";
 }
 
 }  // extern "C"

@@ -17,6 +17,16 @@ struct Partial {
     uint32_t checked;  // bodies that ran the per-step minimum
 };
 
+// One entry of a low-energy list: a state's energy and index (16 bytes).
+// e == INT32_MAX marks an empty slot (no energy reaches it: |E| <= 2^30 - 1).
+struct LowEntry {
+    int32_t e;
+    uint32_t pad;
+    uint64_t x;
+};
+
+constexpr int kMaxLowest = 64;  // one list entry per lane of a wave
+
 struct Ctrl {
     unsigned long long counter;  // next work item
     int32_t gbest;               // best energy found by any wave so far (a real state's energy)
@@ -35,6 +45,7 @@ struct SearchArgs {
     const int32_t *epmin;   // [2^A / 32 + 1]      min of ep over each 32-step body, + 1 padding
     Partial *partials;      // [gridDim.x * waves per block]
     Ctrl *ctrl;
+    LowEntry *lists;        // [gridDim.x * waves per block][k_low] (spectrum search only)
     uint64_t cols_padded;
     uint64_t gray_lo, gray_hi;  // Gray steps searched: [gray_lo, gray_hi)
     uint64_t seg_first;         // first segment (2^seg_bits steps each) touching the range
@@ -44,6 +55,8 @@ struct SearchArgs {
     int32_t A, B;
     int32_t l_eff;              // Gray bits with rows on chip (registers + LDS)
     int32_t seg_bits;
+    int32_t k_low;              // spectrum search: states kept per wave (1..64); else 0
+    int32_t pad;
 };
 
 // Cache builder (Maltsev et al., sec. III.A preprocessing, eq. 8): E_s, M_int
@@ -59,12 +72,21 @@ hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, hipStrea
 // gated = true skips the per-step minimum of bodies whose lower bound cannot
 // reach the threshold; gated = false takes it after every prefix (strict).
 // cols_per_lane selects the instantiation (8 or 16 suffix columns per lane).
-hipError_t launch_search(const SearchArgs &args, int cols_per_lane, bool gated, int blocks,
-                         int lds_bytes, hipStream_t stream);
+// lowest = true (gated only) keeps each wave's k_low lowest states in
+// args.lists instead of the minimum, count and lowest minimiser.
+hipError_t launch_search(const SearchArgs &args, int cols_per_lane, bool gated, bool lowest,
+                         int blocks, int lds_bytes, hipStream_t stream);
 
 // Resident workgroups of the search kernel per CU for a given dynamic LDS size.
-hipError_t search_occupancy(int cols_per_lane, bool gated, int *blocks_per_cu, int lds_bytes);
+hipError_t search_occupancy(int cols_per_lane, bool gated, bool lowest, int *blocks_per_cu,
+                            int lds_bytes);
 
 hipError_t launch_reduce(const Partial *partials, int count, Ctrl *ctrl, hipStream_t stream);
+
+// Merges `lists` (count entries: the per-wave lists of k states each, empty
+// slots allowed) into the k lowest states overall, ordered by energy then
+// index, in out[0..k); *found = number of non-empty entries written.
+hipError_t launch_lowest_merge(const LowEntry *lists, uint64_t count, int k, LowEntry *out,
+                               int32_t *found, hipStream_t stream);
 
 }  // namespace qubo

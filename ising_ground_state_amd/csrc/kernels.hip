@@ -35,6 +35,7 @@
 #include "kernels.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace qubo {
 
@@ -274,6 +275,15 @@ hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, hipStrea
 // The search.
 // ---------------------------------------------------------------------------
 
+// Per-thread record slots of a workgroup in LDS (energy and two 64-bit words).
+struct RecordSlots {
+    int *e;
+    uint64_t *a;
+    uint64_t *b;
+};
+
+// What the exact walk does with the states it visits.  LaneBest keeps, per
+// lane, the minimum over the lane's columns with its count and lowest index.
 struct LaneBest {
     int e = INT_MAX;
     uint64_t cnt = 0;
@@ -290,6 +300,120 @@ struct LaneBest {
             arg = idx < arg ? idx : arg;
         }
     }
+
+    // Records every state of one Gray step with E_sd + E_p <= T (E_sd <= T - E_p
+    // needs no overflow headroom: both sides are sub-sums of the folded matrix).
+    template <int R>
+    __device__ __forceinline__ void step(const int (&E)[R], int epm, uint64_t hi, uint64_t col0,
+                                         int &T)
+    {
+        const int th = T - epm;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (E[r] <= th)
+                record(E[r] + epm, hi | (col0 + (uint64_t)r * 64));
+    }
+
+    // A real energy of the wave's states (or INT_MAX): an upper bound of the minimum.
+    __device__ __forceinline__ int bound() const
+    {
+        return __builtin_amdgcn_readfirstlane(wave_min(e));
+    }
+
+    // Between exact walks the record lives in LDS (slot = thread), so the hot
+    // loop carries no record registers.
+    __device__ __forceinline__ void load(const RecordSlots &s, int slot)
+    {
+        e = s.e[slot];
+        cnt = s.a[slot];
+        arg = s.b[slot];
+    }
+    __device__ __forceinline__ void store(RecordSlots &s, int slot) const
+    {
+        s.e[slot] = e;
+        s.a[slot] = cnt;
+        s.b[slot] = arg;
+    }
+};
+
+// The low-energy spectrum (sec. VI.B, future work: a list of the k lowest
+// energies instead of one minimum).  A wave keeps the k lowest states it has
+// recorded, in the order (E ascending, index ascending), one per lane: lane i
+// holds the i-th (empty slots hold INT_MAX).  A state is inserted by counting
+// the entries before it (a ballot) and shifting the later ones up one lane.
+// Any wave's k-th energy bounds the k-th lowest energy overall from above (k
+// real states reach it), so it is a valid shared threshold; a state among the
+// k lowest overall is never displaced from its wave's list, because k states
+// before it there would also precede it overall.
+struct WaveList {
+    int e = INT_MAX;
+    uint64_t x = ~0ull;
+    int k = 1;     // entries kept (1..64), wave-uniform
+    int lane = 0;
+
+    __device__ __forceinline__ void insert(int ce, uint64_t cx)
+    {
+        const bool before = lane < k && (e < ce || (e == ce && x < cx));
+        const int pos = __builtin_popcountll(__builtin_amdgcn_ballot_w64(before));
+        if (pos >= k)
+            return;
+        const int eu = __shfl_up(e, 1, 64);
+        const uint64_t xu = __shfl_up(x, 1, 64);
+        if (lane > pos) {
+            e = eu;
+            x = xu;
+        }
+        if (lane == pos) {
+            e = ce;
+            x = cx;
+        }
+    }
+
+    // Inserts the lanes of `mask`, whose entries are (ce, cx) in their own lane.
+    __device__ __forceinline__ void insert_lanes(uint64_t mask, int ce, uint64_t cx)
+    {
+        while (mask) {
+            const int l = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const int e1 = __builtin_amdgcn_readlane(ce, l);
+            const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)cx, l);
+            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(cx >> 32), l);
+            insert(e1, ((uint64_t)hi << 32) | lo);
+        }
+    }
+
+    // k-th energy of the list (INT_MAX until k states are in it).
+    __device__ __forceinline__ int kth() const { return __builtin_amdgcn_readlane(e, k - 1); }
+
+    // Offers every state of one Gray step with E_sd + E_p <= T, then lowers T
+    // to the list's k-th energy.
+    template <int R>
+    __device__ __forceinline__ void step(const int (&E)[R], int epm, uint64_t hi, uint64_t col0,
+                                         int &T)
+    {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint64_t mask = __builtin_amdgcn_ballot_w64(E[r] <= T - epm);
+            if (mask) {
+                insert_lanes(mask, E[r] + epm, hi | (col0 + (uint64_t)r * 64));
+                const int kt = kth();
+                T = kt < T ? kt : T;
+            }
+        }
+    }
+
+    __device__ __forceinline__ int bound() const { return kth(); }
+
+    __device__ __forceinline__ void load(const RecordSlots &s, int slot)
+    {
+        e = s.e[slot];
+        x = s.b[slot];
+    }
+    __device__ __forceinline__ void store(RecordSlots &s, int slot) const
+    {
+        s.e[slot] = e;
+        s.b[slot] = x;
+    }
 };
 
 __device__ __forceinline__ int read_gbest(const Ctrl *ctrl)
@@ -299,16 +423,15 @@ __device__ __forceinline__ int read_gbest(const Ctrl *ctrl)
 }
 
 // Exact walk of one body of 32 Gray steps starting at `base`: every state with
-// E_sd + E_p <= T is recorded per lane (E_sd <= T - E_p needs no overflow
-// headroom: both sides are sub-sums of the folded matrix).  With from_end, E
+// E_sd + E_p <= T is offered to the sink (which may lower T).  With from_end, E
 // holds the body's last state on entry (a re-walk after the checked body) and
 // is first taken back to the body's first state (over a body the low four Gray
 // bits return to 0 and only bit 4 flips); otherwise E holds the first state.
 // E holds the body's last state on exit.  A compact loop: it runs rarely.
-template <int R>
+template <int R, class Sink>
 __device__ __forceinline__ void exact_body(int (&E)[R], const int (&Mr)[kU][R], uint64_t base,
-                                           bool top_plus, int T, const int32_t *__restrict__ ep,
-                                           int B, uint64_t col0, LaneBest &lb, bool from_end)
+                                           bool top_plus, int &T, const int32_t *__restrict__ ep,
+                                           int B, uint64_t col0, Sink &sink, bool from_end)
 {
     if (from_end) {
         if (top_plus)
@@ -320,12 +443,7 @@ __device__ __forceinline__ void exact_body(int (&E)[R], const int (&Mr)[kU][R], 
     for (int m = 0; m < kBody; ++m) {
         const uint64_t j = base + (uint64_t)m;
         const int epm = ep[j];
-        const int th = T - epm;
-        const uint64_t hi = gray(j) << B;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (E[r] <= th)
-                lb.record(E[r] + epm, hi | (col0 + (uint64_t)r * 64));
+        sink.step(E, epm, gray(j) << B, col0, T);
         if (m + 1 < kBody) {
             const int t = __builtin_ctz((unsigned)(m + 1));
             const bool plus = (t < kU - 1) ? ((((m + 1) >> (t + 1)) & 1) == 0) : top_plus;
@@ -419,7 +537,7 @@ __device__ __forceinline__ uint64_t checked_body(int (&E)[R], const int (&Mr)[kU
 // column with E(c) + beta0(c) - s M_4(c) <= T - epmin, no state of the body can
 // reach the threshold T, and the body runs the row updates only; otherwise it
 // runs the checked body.  Every state still costs its one add.
-template <int R, bool Gated>
+template <int R, bool Gated, bool Lowest>
 __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restrict__ es,
                                                           const int32_t *__restrict__ mint,
                                                           const int32_t *__restrict__ ep,
@@ -437,7 +555,14 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
     const int A = a.A;
     const uint64_t cp = a.cols_padded;
 
-    LaneBest lb;
+    using Sink = typename std::conditional<Lowest, WaveList, LaneBest>::type;
+    __shared__ int rec_e[64 * kWaves];
+    __shared__ uint64_t rec_a[64 * kWaves], rec_b[64 * kWaves];
+    RecordSlots rec{rec_e, rec_a, rec_b};
+    {
+        Sink fresh;
+        fresh.store(rec, threadIdx.x);  // each thread only ever touches its own slot
+    }
     uint32_t slow_bodies = 0, bodies = 0, checked = 0;
     int T = read_gbest(ctrl);
     long long cur_g = -1;
@@ -546,21 +671,22 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 adds_body(E, Mr, top_plus);
             } else {
                 ++checked;
-                bool walked = false;
-                if (Gated) {
-                    // The bound was reached: walk the body exactly (rare).
-                    exact_body(E, Mr, base, top_plus, T, ep, a.B, col0, lb, false);
-                    walked = true;
-                } else {
-                    const uint64_t acc = checked_body(E, Mr, top_plus, T, ep + base);
-                    if (acc) {
-                        exact_body(E, Mr, base, top_plus, T, ep, a.B, col0, lb, true);
-                        walked = true;
-                    }
-                }
-                if (walked) {
+                // Strict mode walks exactly only after the per-step test hit; the
+                // gated kernel has already decided that the bound was reached.
+                bool walk = Gated;
+                if (!Gated)
+                    walk = checked_body(E, Mr, top_plus, T, ep + base) != 0;
+                if (walk) {
                     ++slow_bodies;
-                    const int wm = __builtin_amdgcn_readfirstlane(wave_min(lb.e));
+                    Sink sink;
+                    sink.load(rec, threadIdx.x);
+                    if constexpr (Lowest) {
+                        sink.k = a.k_low;
+                        sink.lane = lane;
+                    }
+                    exact_body(E, Mr, base, top_plus, T, ep, a.B, col0, sink, !Gated);
+                    sink.store(rec, threadIdx.x);
+                    const int wm = sink.bound();
                     T = wm < T ? wm : T;
                     if (lane == 0)
                         atomicMin(&ctrl->gbest, T);
@@ -594,9 +720,24 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
         }
     }
 
-    int e = lb.e;
-    uint64_t cnt = lb.cnt, arg = lb.arg;
-    wave_combine(e, cnt, arg);
+    Sink sink;
+    sink.load(rec, threadIdx.x);
+    int e = INT_MAX;
+    uint64_t cnt = 0, arg = ~0ull;
+    if constexpr (Lowest) {
+        if (lane < a.k_low) {
+            LowEntry le;
+            le.e = sink.e;
+            le.pad = 0;
+            le.x = sink.x;
+            a.lists[((uint64_t)blockIdx.x * kWaves + wave) * (uint64_t)a.k_low + lane] = le;
+        }
+    } else {
+        e = sink.e;
+        cnt = sink.cnt;
+        arg = sink.arg;
+        wave_combine(e, cnt, arg);
+    }
     if (lane == 0) {
         Partial p;
         p.e = e;
@@ -609,43 +750,65 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
     }
 }
 
-template <int R, bool Gated>
+template <int R, bool Gated, bool Lowest>
 static void launch_one(const SearchArgs &args, int blocks, int lds_bytes, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gray_search_kernel<R, Gated>), dim3(blocks), dim3(64 * kWaves), lds_bytes,
-                       stream, args.es, args.mint, args.ep, args.epmin, args.partials, args.ctrl,
-                       args);
+    hipLaunchKernelGGL((gray_search_kernel<R, Gated, Lowest>), dim3(blocks), dim3(64 * kWaves),
+                       lds_bytes, stream, args.es, args.mint, args.ep, args.epmin, args.partials,
+                       args.ctrl, args);
 }
 
-hipError_t launch_search(const SearchArgs &args, int cols_per_lane, bool gated, int blocks,
-                         int lds_bytes, hipStream_t stream)
+// The instantiations: {8, 16} columns per lane x {gated, strict} for the
+// minimum, and gated only for the spectrum.
+static const void *search_fn(int cols_per_lane, bool gated, bool lowest)
 {
     if (cols_per_lane == 8) {
-        if (gated)
-            launch_one<8, true>(args, blocks, lds_bytes, stream);
-        else
-            launch_one<8, false>(args, blocks, lds_bytes, stream);
-    } else if (cols_per_lane == 16) {
-        if (gated)
-            launch_one<16, true>(args, blocks, lds_bytes, stream);
-        else
-            launch_one<16, false>(args, blocks, lds_bytes, stream);
-    } else {
+        if (lowest)
+            return gated ? reinterpret_cast<const void *>(gray_search_kernel<8, true, true>)
+                         : nullptr;
+        return gated ? reinterpret_cast<const void *>(gray_search_kernel<8, true, false>)
+                     : reinterpret_cast<const void *>(gray_search_kernel<8, false, false>);
+    }
+    if (cols_per_lane == 16) {
+        if (lowest)
+            return gated ? reinterpret_cast<const void *>(gray_search_kernel<16, true, true>)
+                         : nullptr;
+        return gated ? reinterpret_cast<const void *>(gray_search_kernel<16, true, false>)
+                     : reinterpret_cast<const void *>(gray_search_kernel<16, false, false>);
+    }
+    return nullptr;
+}
+
+hipError_t launch_search(const SearchArgs &args, int cols_per_lane, bool gated, bool lowest,
+                         int blocks, int lds_bytes, hipStream_t stream)
+{
+    if (!search_fn(cols_per_lane, gated, lowest))
         return hipErrorInvalidValue;
+    if (lowest && (args.k_low < 1 || args.k_low > kMaxLowest || !args.lists))
+        return hipErrorInvalidValue;
+    if (cols_per_lane == 8) {
+        if (lowest)
+            launch_one<8, true, true>(args, blocks, lds_bytes, stream);
+        else if (gated)
+            launch_one<8, true, false>(args, blocks, lds_bytes, stream);
+        else
+            launch_one<8, false, false>(args, blocks, lds_bytes, stream);
+    } else {
+        if (lowest)
+            launch_one<16, true, true>(args, blocks, lds_bytes, stream);
+        else if (gated)
+            launch_one<16, true, false>(args, blocks, lds_bytes, stream);
+        else
+            launch_one<16, false, false>(args, blocks, lds_bytes, stream);
     }
     return hipGetLastError();
 }
 
-hipError_t search_occupancy(int cols_per_lane, bool gated, int *blocks_per_cu, int lds_bytes)
+hipError_t search_occupancy(int cols_per_lane, bool gated, bool lowest, int *blocks_per_cu,
+                            int lds_bytes)
 {
-    const void *fn = nullptr;
-    if (cols_per_lane == 8)
-        fn = gated ? reinterpret_cast<const void *>(gray_search_kernel<8, true>)
-                   : reinterpret_cast<const void *>(gray_search_kernel<8, false>);
-    else if (cols_per_lane == 16)
-        fn = gated ? reinterpret_cast<const void *>(gray_search_kernel<16, true>)
-                   : reinterpret_cast<const void *>(gray_search_kernel<16, false>);
-    else
+    const void *fn = search_fn(cols_per_lane, gated, lowest);
+    if (!fn)
         return hipErrorInvalidValue;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, 64 * kWaves,
                                                         (size_t)lds_bytes);
@@ -704,6 +867,71 @@ __global__ __launch_bounds__(256) void reduce_kernel(const Partial *__restrict__
 hipError_t launch_reduce(const Partial *partials, int count, Ctrl *ctrl, hipStream_t stream)
 {
     hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(256), 0, stream, partials, count, ctrl);
+    return hipGetLastError();
+}
+
+// The k lowest states overall from the per-wave lists (the final map-reduce
+// step of sec. III.C with the list merge in place of the min).  One workgroup:
+// each wave merges a strided quarter of the entries into its own WaveList,
+// admitting only entries at or below its current k-th energy, then wave 0
+// merges the other three lists.
+__global__ __launch_bounds__(256) void lowest_merge_kernel(const LowEntry *__restrict__ lists,
+                                                           uint64_t count, int k,
+                                                           LowEntry *__restrict__ out,
+                                                           int32_t *__restrict__ found)
+{
+    __shared__ LowEntry staged[kWaves - 1][kMaxLowest];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    WaveList wl;
+    wl.k = k;
+    wl.lane = lane;
+    for (uint64_t b = (uint64_t)wave * 64; b < count; b += 64 * kWaves) {
+        const uint64_t i = b + (uint64_t)lane;
+        LowEntry le{INT_MAX, 0, ~0ull};
+        if (i < count)
+            le = lists[i];
+        const int kt = wl.kth();
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(le.e != INT_MAX && le.e <= kt);
+        wl.insert_lanes(mask, le.e, le.x);
+    }
+    if (wave > 0 && lane < k) {
+        LowEntry le;
+        le.e = wl.e;
+        le.pad = 0;
+        le.x = wl.x;
+        staged[wave - 1][lane] = le;
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+    for (int w = 0; w < kWaves - 1; ++w) {
+        LowEntry le{INT_MAX, 0, ~0ull};
+        if (lane < k)
+            le = staged[w][lane];
+        const int kt = wl.kth();
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(le.e != INT_MAX && le.e <= kt);
+        wl.insert_lanes(mask, le.e, le.x);
+    }
+    const uint64_t filled = __builtin_amdgcn_ballot_w64(lane < k && wl.e != INT_MAX);
+    if (lane < k) {
+        LowEntry le;
+        le.e = wl.e;
+        le.pad = 0;
+        le.x = wl.x;
+        out[lane] = le;
+    }
+    if (lane == 0)
+        *found = (int32_t)__builtin_popcountll(filled);
+}
+
+hipError_t launch_lowest_merge(const LowEntry *lists, uint64_t count, int k, LowEntry *out,
+                               int32_t *found, hipStream_t stream)
+{
+    if (k < 1 || k > kMaxLowest)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lowest_merge_kernel, dim3(1), dim3(64 * kWaves), 0, stream, lists, count, k,
+                       out, found);
     return hipGetLastError();
 }
 

@@ -92,8 +92,8 @@ class Oracle:
                                            ctypes.c_int, ctypes.POINTER(_Result)]
         lib.oracle_search_gray.restype = ctypes.c_int
         lib.oracle_lowest.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                      ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_uint64),
-                                      ctypes.POINTER(ctypes.c_int)]
+                                      ctypes.c_uint64, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                      ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)]
         lib.oracle_lowest.restype = ctypes.c_int
         lib.oracle_version.restype = ctypes.c_char_p
         self.lib = lib
@@ -135,13 +135,16 @@ class Oracle:
             raise ValueError("oracle_search_gray failed (%d)" % rc)
         return Result(r.min_energy, r.argmin, r.count, r.max_abs_energy)
 
-    def lowest(self, Q, k: int, gray_walk: bool = True, threads: int | None = None) -> list[tuple[int, int]]:
-        """The k lowest states as (E, index) pairs, ordered by E then index."""
+    def lowest(self, Q, k: int, gray_walk: bool = True, threads: int | None = None, fixed: int = 0,
+               top: int = 0) -> list[tuple[int, int]]:
+        """The k lowest states as (E, index) pairs, ordered by E then index, of
+        the sub-cube whose first `fixed` variables spell `top` (default: all)."""
         q = _qarray(Q)
         e = np.zeros(k, dtype=np.int64)
         ix = np.zeros(k, dtype=np.uint64)
         found = ctypes.c_int(0)
-        rc = self.lib.oracle_lowest(_ptr(q), q.shape[0], k, 1 if gray_walk else 0, threads or default_threads(),
+        rc = self.lib.oracle_lowest(_ptr(q), q.shape[0], k, 1 if gray_walk else 0, fixed, top,
+                                    threads or default_threads(),
                                     e.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                     ix.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), ctypes.byref(found))
         if rc != 0:
@@ -180,8 +183,9 @@ def search_gray(Q, k: int = 0, top: int = 0, threads: int | None = None) -> Resu
     return default().search_gray(Q, k, top, threads)
 
 
-def lowest(Q, k: int, gray_walk: bool = True, threads: int | None = None) -> list[tuple[int, int]]:
-    return default().lowest(Q, k, gray_walk, threads)
+def lowest(Q, k: int, gray_walk: bool = True, threads: int | None = None, fixed: int = 0,
+           top: int = 0) -> list[tuple[int, int]]:
+    return default().lowest(Q, k, gray_walk, threads, fixed, top)
 
 
 def version() -> str:

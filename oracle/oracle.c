@@ -385,17 +385,19 @@ int oracle_search_gray(const int32_t *Q, int n, int k, uint64_t top, int threads
     return 0;
 }
 
-int oracle_lowest(const int32_t *Q, int n, int k, int gray_walk, int threads, int64_t *energies,
-                  uint64_t *indices, int *found)
+int oracle_lowest(const int32_t *Q, int n, int k, int gray_walk, int fixed, uint64_t top,
+                  int threads, int64_t *energies, uint64_t *indices, int *found)
 {
     if (!Q || !energies || !indices || !found || n < 1 || n > ORACLE_MAX_N || k < 1 ||
-        k > ORACLE_MAX_LOWEST)
+        k > ORACLE_MAX_LOWEST || fixed < 0 || fixed > n)
+        return -1;
+    if (top >= (1ull << fixed))
         return -1;
     oracle_state merged[ORACLE_MAX_LOWEST];
     int len = 0;
     if (gray_walk) {
         uint64_t pieces = 0;
-        gray_job *jobs = run_gray(Q, n, 0, 0, threads, k, &pieces);
+        gray_job *jobs = run_gray(Q, n, fixed, top, threads, k, &pieces);
         if (!jobs)
             return -2;
         for (uint64_t p = 0; p < pieces; ++p)
@@ -403,8 +405,9 @@ int oracle_lowest(const int32_t *Q, int n, int k, int gray_walk, int threads, in
                 keep_lowest(merged, &len, k, jobs[p].list[i].e, jobs[p].list[i].idx);
         free(jobs);
     } else {
-        /* tier A: every state from the definition, in index order, one thread */
-        for (uint64_t idx = 0; idx < (1ull << n); ++idx)
+        /* tier A: every state of the sub-cube from the definition, in index order */
+        const int m = n - fixed;
+        for (uint64_t idx = top << m; idx < ((top + 1) << m); ++idx)
             keep_lowest(merged, &len, k, oracle_energy(Q, n, idx), idx);
     }
     for (int i = 0; i < len; ++i) {

@@ -33,11 +33,12 @@ int oracle_search_gray(const int32_t *Q, int n, int k, uint64_t top, int threads
                        oracle_result *out);
 
 /* The k lowest states (1 <= k <= 1024): the first k states in the order
- * (E ascending, index ascending), over the whole space; gray_walk = 0 evaluates
- * every state directly (tier A), 1 walks in Gray order (tier B).  Writes
- * min(k, 2^n) pairs and their number to *found. */
-int oracle_lowest(const int32_t *Q, int n, int k, int gray_walk, int threads, int64_t *energies,
-                  uint64_t *indices, int *found);
+ * (E ascending, index ascending) of the sub-cube whose first `fixed` variables
+ * spell `top` (fixed = 0: the whole space); gray_walk = 0 evaluates every state
+ * directly (tier A, one thread), 1 walks in Gray order (tier B).  Writes
+ * min(k, 2^(n - fixed)) pairs and their number to *found. */
+int oracle_lowest(const int32_t *Q, int n, int k, int gray_walk, int fixed, uint64_t top,
+                  int threads, int64_t *energies, uint64_t *indices, int *found);
 
 const char *oracle_version(void);
 #endif

@@ -6,10 +6,14 @@ Calls only the CPU oracle (``oracle``) on the seeded workloads of
     python tests/golden/make_golden.py C1 C2 C2p        # full searches
     python tests/golden/make_golden.py C3               # 2^40 states, ~25 min on 8 cores
     python tests/golden/make_golden.py C4sub C5sub      # seeded sub-cubes of 2^32 states
+    python tests/golden/make_golden.py C1low C2low C2plow C4sublow C5sublow
+                                                        # the 64 lowest states (spectrum)
 
 Full searches store {sha256_Q, n, min_energy, argmin, count, max_abs_energy}.
 Sub-cube files store one record per sub-cube: the first k variables are fixed
 to `top` (variable 0 most significant) and the remaining 32 are searched.
+Spectrum files (names ending in "low") store the first 64 states in the order
+(E ascending, index ascending) of the whole space or of each sub-cube.
 """
 from __future__ import annotations
 
@@ -63,15 +67,9 @@ def subcubes(name: str, threads: int) -> dict:
     cfg = qi.make_config(name)
     Q, n = cfg["Q"], cfg["n"]
     k = n - SUB_FREE_BITS
-    rng = qi.SplitMix64(SUB_SEED + n)
-    tops = []
-    while len(tops) < SUB_COUNT:
-        t = rng.uniform_int(0, (1 << k) - 1)
-        if t not in tops:
-            tops.append(t)
     cubes = []
     t_all = time.time()
-    for top in tops:
+    for top in sub_tops(n):
         t0 = time.time()
         r = oracle.search_gray(Q, k=k, top=top, threads=threads)
         cubes.append(dict(k=k, top=top, min_energy=r.min_energy, argmin=r.argmin, count=r.count,
@@ -82,16 +80,63 @@ def subcubes(name: str, threads: int) -> dict:
                 seconds_total=round(time.time() - t_all, 2), host=host_info(threads))
 
 
+LOW_K = 64
+
+
+def sub_tops(n: int) -> list[int]:
+    k = n - SUB_FREE_BITS
+    rng = qi.SplitMix64(SUB_SEED + n)
+    tops = []
+    while len(tops) < SUB_COUNT:
+        t = rng.uniform_int(0, (1 << k) - 1)
+        if t not in tops:
+            tops.append(t)
+    return tops
+
+
+def lowest_full(name: str, threads: int) -> dict:
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    t0 = time.time()
+    low = oracle.lowest(Q, LOW_K, gray_walk=True, threads=threads)
+    return dict(name=name + "low", desc=cfg["desc"], n=n, seed=cfg["seed"], sha256_Q=qi.sha256_of(Q),
+                k=LOW_K, states=[list(p) for p in low], tier="B (Gray walk)",
+                seconds=round(time.time() - t0, 2), host=host_info(threads))
+
+
+def lowest_subcubes(name: str, threads: int) -> dict:
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    k = n - SUB_FREE_BITS
+    cubes = []
+    t_all = time.time()
+    for top in sub_tops(n):
+        low = oracle.lowest(Q, LOW_K, gray_walk=True, threads=threads, fixed=k, top=top)
+        cubes.append(dict(k=k, top=top, states=[list(p) for p in low]))
+        print("  %s top=%d -> %s" % (name, top, low[0]), flush=True)
+    return dict(name=name + "sublow", desc=cfg["desc"], n=n, seed=cfg["seed"], sha256_Q=qi.sha256_of(Q),
+                free_bits=SUB_FREE_BITS, sub_seed=SUB_SEED + n, k_lowest=LOW_K, cubes=cubes,
+                tier="B (Gray walk)", seconds_total=round(time.time() - t_all, 2), host=host_info(threads))
+
+
 def main(argv):
     threads = oracle.default_threads()
     for arg in argv:
         print("computing", arg, "on", threads, "threads", flush=True)
-        rec = subcubes(arg[:-3], threads) if arg.endswith("sub") else full(arg, threads)
+        if arg.endswith("sublow"):
+            rec = lowest_subcubes(arg[:-6], threads)
+        elif arg.endswith("low"):
+            rec = lowest_full(arg[:-3], threads)
+        elif arg.endswith("sub"):
+            rec = subcubes(arg[:-3], threads)
+        else:
+            rec = full(arg, threads)
         path = os.path.join(HERE, arg + ".json")
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
-        print("wrote", path, {k: rec[k] for k in rec if k in ("min_energy", "argmin", "count")}, flush=True)
+        print("wrote", path, {k: rec[k] for k in rec if k in ("min_energy", "argmin", "count", "seconds")},
+              flush=True)
 
 
 if __name__ == "__main__":

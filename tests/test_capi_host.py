@@ -111,6 +111,19 @@ def test_null_and_range_arguments_rejected_before_the_device():
     assert lib.qubo_build_tables(ctypes.c_void_p(16), 12, 6, None, None, None, None) == q.QUBO_EINVAL
     assert lib.qubo_check_q(None, 3, None) == q.QUBO_EINVAL
     assert r.count == 0  # untouched
+    # spectrum: k in 1..64, outputs present, no strict mode, no unknown flags, valid slices
+    out = (q._State * 64)()
+    found = ctypes.c_int(-3)
+    P = ctypes.c_void_p(16)
+    for k, flags, lo, hi, o, fo in [(0, 0, 0, 0, out, found), (65, 0, 0, 0, out, found),
+                                    (4, q.FLAG_STRICT_MIN, 0, 0, out, found), (4, 1 << 20, 0, 0, out, found),
+                                    (4, q.FLAG_COLS8 | q.FLAG_COLS16, 0, 0, out, found),
+                                    (4, 0, 0, 33, out, found), (4, 0, 0, 0, None, found),
+                                    (4, 0, 0, 0, out, None)]:
+        fp = ctypes.byref(fo) if fo is not None else None
+        assert lib.qubo_search_lowest(P, 12, k, 8, -1, lo, hi, flags, None, o, fp) == q.QUBO_EINVAL, (k, flags)
+    assert lib.qubo_search_lowest(None, 12, 4, -1, -1, 0, 0, 0, None, out, ctypes.byref(found)) == q.QUBO_EINVAL
+    assert found.value == -3  # untouched
 
 
 def test_timing_struct_before_any_search():

@@ -76,3 +76,36 @@ def test_benchmark_workloads(q, name):
         r2 = q.search(Qd, strict=True, cols_per_lane=16)
         check_coverage(q, n, strict=True, cols_per_lane=16)
         assert r2.triple() == r.triple()
+
+
+def test_spectrum_n48(q):
+    """The 64 lowest states of the benchmark workload (n = 48), checked by what
+    holds at any size: the oracle's energy of every listed state, the order,
+    the minimum search's answer at the head, the merge of the two halves of the
+    space (two slices, the other kernel build), and closure under single flips:
+    a neighbour that precedes a listed state in the (E, index) order must be
+    listed too."""
+    cfg = qi.make_config("C4")
+    Q, n = cfg["Q"], cfg["n"]
+    Qd = dev_q(Q)
+    announce("full spectrum C4 k=64 R=8")
+    low = q.lowest(Qd, 64)
+    check_coverage(q, n)
+    assert len(low) == 64 and low == sorted(low)
+    idx = np.asarray([i for _, i in low], dtype=np.uint64)
+    assert oracle.energies(Q, idx).tolist() == [e for e, _ in low]
+    r = q.search(Qd)
+    assert low[0] == (r.min_energy, r.argmin)
+    assert sum(1 for e, _ in low if e == r.min_energy) == min(r.count, 64)
+    listed = set(low)
+    for e, i in low:
+        nb = np.asarray([i ^ (1 << b) for b in range(n)], dtype=np.uint64)
+        for e2, i2 in zip(oracle.energies(Q, nb).tolist(), nb.tolist()):
+            if (e2, i2) < (e, i):
+                assert (e2, i2) in listed, ((e, i), (e2, i2))
+    A = q.make_plan(n)["prefix_bits"]
+    half = 1 << (A - 1)
+    announce("full spectrum C4 halves R=16")
+    h0 = q.lowest(Qd, 64, prefix_bits=A, gray_lo=0, gray_hi=half, cols_per_lane=16)
+    h1 = q.lowest(Qd, 64, prefix_bits=A, gray_lo=half, gray_hi=2 * half, cols_per_lane=16)
+    assert sorted(h0 + h1)[:64] == low

@@ -213,6 +213,14 @@ def pin_lowest(o: oracle.Oracle):
         low = o.lowest(Q, min(1 << n, 1024))
         assert low[0] == (m.min_energy, m.argmin), (n, seed)
         assert sum(1 for e, _ in low if e == m.min_energy) == m.count, (n, seed)
+    # a sub-cube (first `fixed` variables spell `top`) is the index range [top << m, (top + 1) << m)
+    Q = rand_general(12, 2607, -2, 2)
+    full = numpy_lowest(Q, 1 << 12)
+    for fixed, top in [(1, 1), (3, 5), (6, 40)]:
+        m = 12 - fixed
+        want = [p for p in full if (p[1] >> m) == top][:40]
+        assert o.lowest(Q, 40, gray_walk=True, threads=2, fixed=fixed, top=top) == want, (fixed, top)
+        assert o.lowest(Q, 40, gray_walk=False, fixed=fixed, top=top) == want, (fixed, top)
     # Q = 0: every state has E = 0, so the list is the first k indices
     for n in (3, 12):
         assert o.lowest(qi.zeros(n), 8) == [(0, i) for i in range(8)]
