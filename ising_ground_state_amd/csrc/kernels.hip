@@ -303,15 +303,24 @@ struct LaneBest {
 
     // Records every state of one Gray step with E_sd + E_p <= T (E_sd <= T - E_p
     // needs no overflow headroom: both sides are sub-sums of the folded matrix).
+    // key = (g(j) << B) | (first column of the group), wave-uniform; column r of
+    // a lane is key | r*64 | lane.  The record keeps the index without the
+    // lane's 6 bits (equal for all of a lane's states, so comparisons between
+    // them are unchanged); they are added once at the end (with_lane), which
+    // keeps per-lane column indices out of the registers of the walk.
     template <int R>
-    __device__ __forceinline__ void step(const int (&E)[R], int epm, uint64_t hi, uint64_t col0,
-                                         int &T)
+    __device__ __forceinline__ void step(const int (&E)[R], int epm, uint64_t key, int &T)
     {
         const int th = T - epm;
 #pragma unroll
         for (int r = 0; r < R; ++r)
             if (E[r] <= th)
-                record(E[r] + epm, hi | (col0 + (uint64_t)r * 64));
+                record(E[r] + epm, key | ((uint64_t)r << 6));
+    }
+
+    __device__ __forceinline__ uint64_t with_lane(int lane) const
+    {
+        return cnt ? (arg | (uint64_t)lane) : ~0ull;
     }
 
     // A real energy of the wave's states (or INT_MAX): an upper bound of the minimum.
@@ -382,20 +391,29 @@ struct WaveList {
         }
     }
 
+    // The same for entries whose index is key | lane (key wave-uniform).
+    __device__ __forceinline__ void insert_lanes_key(uint64_t mask, int ce, uint64_t key)
+    {
+        while (mask) {
+            const int l = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            insert(__builtin_amdgcn_readlane(ce, l), key | (uint64_t)l);
+        }
+    }
+
     // k-th energy of the list (INT_MAX until k states are in it).
     __device__ __forceinline__ int kth() const { return __builtin_amdgcn_readlane(e, k - 1); }
 
     // Offers every state of one Gray step with E_sd + E_p <= T, then lowers T
     // to the list's k-th energy.
     template <int R>
-    __device__ __forceinline__ void step(const int (&E)[R], int epm, uint64_t hi, uint64_t col0,
-                                         int &T)
+    __device__ __forceinline__ void step(const int (&E)[R], int epm, uint64_t key, int &T)
     {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint64_t mask = __builtin_amdgcn_ballot_w64(E[r] <= T - epm);
             if (mask) {
-                insert_lanes(mask, E[r] + epm, hi | (col0 + (uint64_t)r * 64));
+                insert_lanes_key(mask, E[r] + epm, key | ((uint64_t)r << 6));
                 const int kt = kth();
                 T = kt < T ? kt : T;
             }
@@ -431,7 +449,7 @@ __device__ __forceinline__ int read_gbest(const Ctrl *ctrl)
 template <int R, class Sink>
 __device__ __forceinline__ void exact_body(int (&E)[R], const int (&Mr)[kU][R], uint64_t base,
                                            bool top_plus, int &T, const int32_t *__restrict__ ep,
-                                           int B, uint64_t col0, Sink &sink, bool from_end)
+                                           int B, uint64_t colbase, Sink &sink, bool from_end)
 {
     if (from_end) {
         if (top_plus)
@@ -439,23 +457,26 @@ __device__ __forceinline__ void exact_body(int (&E)[R], const int (&Mr)[kU][R], 
         else
             add_row(E, Mr[kU - 1]);
     }
+    const int neg_top = top_plus ? 0 : -1;
 #pragma unroll 1
     for (int m = 0; m < kBody; ++m) {
         const uint64_t j = base + (uint64_t)m;
         const int epm = ep[j];
-        sink.step(E, epm, gray(j) << B, col0, T);
-        if (m + 1 < kBody) {
-            const int t = __builtin_ctz((unsigned)(m + 1));
-            const bool plus = (t < kU - 1) ? ((((m + 1) >> (t + 1)) & 1) == 0) : top_plus;
+        sink.step(E, epm, (gray(j) << B) | colbase, T);
+        // The row of the flipped bit t is chosen with selects, not branches:
+        // branches over t made the compiler keep copies of E at every merge.
+        // After the last step t = 5 and no row is chosen (d = 0).  The sign is
+        // an integer mask (0: add, -1: subtract, (d ^ neg) - neg), which stays
+        // in scalar registers; a boolean select here pulled T into VGPRs.
+        const int t = __builtin_ctz((unsigned)(m + 1));
+        const int neg = (t < kU - 1) ? -(((m + 1) >> (t + 1)) & 1) : neg_top;
 #pragma unroll
-            for (int tt = 0; tt < kU; ++tt) {
-                if (tt == t) {
-                    if (plus)
-                        add_row(E, Mr[tt]);
-                    else
-                        sub_row(E, Mr[tt]);
-                }
-            }
+        for (int r = 0; r < R; ++r) {
+            int d = 0;
+#pragma unroll
+            for (int tt = 0; tt < kU; ++tt)
+                d = (tt == t) ? Mr[tt][r] : d;
+            E[r] += (d ^ neg) - neg;
         }
     }
 }
@@ -533,10 +554,12 @@ __device__ __forceinline__ uint64_t checked_body(int (&E)[R], const int (&Mr)[kU
 // fixed; from the body's first state (low pattern s<<4, s = bit 5 of the step
 // index) a column's suffix-dependent energy can fall by at most
 //   beta0(c) - s M_4(c),   beta0(c) = sum_{t<5} min(0, M_t(c)),
-// and the prefix energy of any step is at least epmin[body].  If no lane has a
-// column with E(c) + beta0(c) - s M_4(c) <= T - epmin, no state of the body can
-// reach the threshold T, and the body runs the row updates only; otherwise it
-// runs the checked body.  Every state still costs its one add.
+// and the prefix energy of any step is at least epmin[body].  A lane bounds all
+// its columns at once: min_c E(c) + min_c (beta0(c) - s M_4(c)), the second term
+// fixed per work unit for s = 0 and s = 1.  If no lane's bound reaches
+// T - epmin, no state of the body can reach the threshold T, and the body runs
+// the row updates only; otherwise it is walked exactly.  Every state still
+// costs its one add.
 template <int R, bool Gated, bool Lowest>
 __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restrict__ es,
                                                           const int32_t *__restrict__ mint,
@@ -624,15 +647,19 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
             for (int r = 0; r < R; ++r)
                 Mr[t][r] = row[r * 64];
         }
-        int beta0[R];
+        // Lane bounds of the fall within a body, for s = 0 and s = 1.
+        int beta_s0 = 0, beta_s1 = 0;
         if (Gated) {
+            beta_s0 = INT_MAX;
+            beta_s1 = INT_MAX;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 int b = 0;
 #pragma unroll
                 for (int t = 0; t < kU; ++t)
                     b += Mr[t][r] < 0 ? Mr[t][r] : 0;
-                beta0[r] = b;
+                beta_s0 = imin(beta_s0, b);
+                beta_s1 = imin(beta_s1, b - Mr[kU - 1][r]);
             }
         }
         {
@@ -654,17 +681,11 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 epm_next = epmin[(base >> kU) + 1];
             bool check = true;
             if (Gated) {
+                // Padding columns hold INT_MAX with zero rows (beta 0), so a lane
+                // of padding columns only has the bound INT_MAX.
                 const int thb = T - epm_cur;
-                int bound[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    bound[r] = E[r] + beta0[r];
-                if (!top_plus) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        bound[r] -= Mr[kU - 1][r];
-                }
-                check = __builtin_amdgcn_ballot_w64(row_min<R>(bound) <= thb) != 0;
+                const int bound = row_min<R>(E) + (top_plus ? beta_s0 : beta_s1);
+                check = __builtin_amdgcn_ballot_w64(bound <= thb) != 0;
             }
             ++bodies;
             if (!check) {
@@ -684,12 +705,14 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                         sink.k = a.k_low;
                         sink.lane = lane;
                     }
-                    exact_body(E, Mr, base, top_plus, T, ep, a.B, col0, sink, !Gated);
+                    exact_body(E, Mr, base, top_plus, T, ep, a.B, g * kGroup, sink, !Gated);
                     sink.store(rec, threadIdx.x);
+                    // Every lane offers the same T to the shared best: a lane-0
+                    // branch here (a divergent region inside the body loop) made
+                    // the compiler keep T and the counters in VGPRs.
                     const int wm = sink.bound();
                     T = wm < T ? wm : T;
-                    if (lane == 0)
-                        atomicMin(&ctrl->gbest, T);
+                    atomicMin(&ctrl->gbest, T);
                     const int gb = read_gbest(ctrl);
                     T = gb < T ? gb : T;
                 }
@@ -735,7 +758,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
     } else {
         e = sink.e;
         cnt = sink.cnt;
-        arg = sink.arg;
+        arg = sink.with_lane(lane);
         wave_combine(e, cnt, arg);
     }
     if (lane == 0) {
