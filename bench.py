@@ -38,12 +38,17 @@ OPS_PER_STATE = 1
 OPS_PER_STATE_ADD_CMP = 2
 
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gray_search_gated_n48_counters.json")
-KERNEL_SRC = os.path.join(ROOT, "ising_ground_state_amd", "csrc", "kernels.hip")
+# What the search kernel's machine code is built from: its source, its header and the build flags.
+KERNEL_INPUTS = [os.path.join(ROOT, "ising_ground_state_amd", *parts) for parts in
+                 (("csrc", "kernels.hip"), ("csrc", "kernels.h"), ("build.py",))]
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_INPUTS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

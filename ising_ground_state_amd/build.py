@@ -29,6 +29,11 @@ FLAGS = [
     "-fvisibility=hidden",
     # never let the compiler form packed FP32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Leave wave-uniform branches unstructured (they run as scalar branches).
+    # Structurizing the search kernel's uniform body-loop branches added flow
+    # blocks whose undefined incoming values are VGPRs; the scalar threshold
+    # and counters then moved to VGPRs with copies in every 32-step body.
+    "-mllvm", "-structurizecfg-skip-uniform-regions",
     "-Wall",
 ]
 
