@@ -575,6 +575,9 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // This lane's column in the LDS rows, biased so that bit t's row is
+    // lds_lane + t * kGroup (one add per outer flip).
+    const int32_t *lds_lane = lds_rows - kU * kGroup + lane;
     const int A = a.A;
     const uint64_t cp = a.cols_padded;
 
@@ -724,7 +727,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 const bool plus = ((next >> (t + 1)) & 1u) == 0;
                 int row[R];
                 if (t < a.l_eff) {
-                    const int32_t *src = lds_rows + (t - kU) * kGroup + lane;
+                    const int32_t *src = lds_lane + t * kGroup;  // row of bit t, this lane
 #pragma unroll
                     for (int r = 0; r < R; ++r)
                         row[r] = src[r * 64];

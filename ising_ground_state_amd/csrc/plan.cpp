@@ -153,7 +153,8 @@ int make_plan(int n_total, int prefix_bits, int cache_bits, int num_cus, int col
     p.col_groups = cols_padded / group;
 
     // Segments: enough work units for ~8 per resident wave, each at least one
-    // unrolled body (2^5 steps) and at most 2^20 steps.
+    // unrolled body (2^5 steps) and at most 2^18 steps, so that the last round
+    // of the persistent grid is short (n=48: ~340 items per workgroup).
     const uint64_t resident_waves = (uint64_t)num_cus * 4 * kWavesPerBlock;
     const uint64_t target_units = 8 * resident_waves;
     int split = 0;
@@ -161,7 +162,7 @@ int make_plan(int n_total, int prefix_bits, int cache_bits, int num_cus, int col
         split = ceil_log2((target_units + p.col_groups - 1) / p.col_groups);
     int c = A - split;
     c = std::max(c, kRegBits);
-    c = std::min(c, 20);
+    c = std::min(c, kMaxSegBits);
     c = std::min(c, A);
     p.seg_bits = c;
 

@@ -20,6 +20,7 @@ constexpr int kMaxLdsBytes = 65536;      // cached rows per workgroup
 constexpr uint64_t kMaxMintBytes = 1ull << 33;  // 8 GiB
 constexpr int kMaxSingleVars = 58;       // largest n searched by a single launch
 constexpr int kMaxSplitBits = 32;        // at most 2^32 sub-problems
+constexpr int kMaxSegBits = 18;          // Gray steps per work unit at most 2^18 (a fine tail)
 
 constexpr int64_t kAbsSumLimit = (1ll << 30) - 1;
 

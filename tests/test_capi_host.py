@@ -48,7 +48,7 @@ def test_plan_invariants(n):
     A, B = p["prefix_bits"], p["suffix_bits"]
     assert A + B == p["n_search"] and A >= 5 and A <= 32
     assert 5 <= p["cache_bits"] <= A
-    assert 5 <= p["seg_bits"] <= min(A, 20)
+    assert 5 <= p["seg_bits"] <= min(A, 18)
     group = 64 * p["cols_per_lane"]
     assert p["cols_per_lane"] in (8, 16)
     assert p["lds_bytes"] == max(0, min(p["cache_bits"], p["seg_bits"]) - 5) * group * 4 <= 65536
@@ -67,7 +67,7 @@ def test_plan_explicit_splits():
     assert p["lds_bytes"] == 0
     # cached bits beyond one work unit's segment never flip there: the plan reports the effective value
     p = q.make_plan(40, prefix_bits=30, cache_bits=22)
-    assert p["cache_bits"] == p["seg_bits"] <= 20
+    assert p["cache_bits"] == p["seg_bits"] <= 18
 
 
 @pytest.mark.parametrize("args,code", [
