@@ -42,7 +42,7 @@ struct SearchArgs {
     const int32_t *es;      // [cols_padded]       suffix energies E_s(c)
     const int32_t *mint;    // [A][cols_padded]    M_int rows by prefix variable
     const int32_t *ep;      // [2^A]               prefix energies in Gray order
-    const int32_t *epmin;   // [2^A / 32 + 1]      min of ep over each 32-step body, + 1 padding
+    const int32_t *epmin;   // [2^A / 32 + 2]      min of ep over each 32-step body, + 2 padding
     Partial *partials;      // [gridDim.x * waves per block]
     Ctrl *ctrl;
     LowEntry *lists;        // [gridDim.x * waves per block][k_low] (spectrum search only)
@@ -66,7 +66,7 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
                                hipStream_t stream);
 
 // Resets the work counter, seeds the shared best with t0 (a real energy or an
-// upper bound) and fills the body-minimum table's padding entry.
+// upper bound) and fills the body-minimum table's two padding entries.
 hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, hipStream_t stream);
 
 // gated = true skips the per-step minimum of bodies whose lower bound cannot

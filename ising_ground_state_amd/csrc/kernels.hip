@@ -257,7 +257,8 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
 
 __global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad)
 {
-    *epmin_pad = INT_MAX;  // read ahead by the last body of the walk, never used
+    epmin_pad[0] = INT_MAX;  // read ahead by the last two bodies of the walk, never used
+    epmin_pad[1] = INT_MAX;
     ctrl->counter = 0;
     ctrl->gbest = t0;
     ctrl->slow_total = 0;
@@ -650,11 +651,17 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
             for (int r = 0; r < R; ++r)
                 Mr[t][r] = row[r * 64];
         }
-        // Lane bounds of the fall within a body, for s = 0 and s = 1.
-        int beta_s0 = 0, beta_s1 = 0;
+        // Lane bounds of the fall within a body, for s = 0 and s = 1, and within
+        // an aligned pair of bodies (64 steps, Gray bits 0..5), for bit 5 = 0
+        // and 1 at the pair's start.  Bit 5's row is read here only.
+        int beta_s0 = 0, beta_s1 = 0, beta_p0 = 0, beta_p1 = 0;
         if (Gated) {
             beta_s0 = INT_MAX;
             beta_s1 = INT_MAX;
+            beta_p0 = INT_MAX;
+            beta_p1 = INT_MAX;
+            // (with A = 5 there is no bit 5: row 0 is read, in bounds, and ignored)
+            const int32_t *row5 = mint + (uint64_t)(A > kU ? A - 1 - kU : 0) * cp + col0;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 int b = 0;
@@ -663,6 +670,9 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                     b += Mr[t][r] < 0 ? Mr[t][r] : 0;
                 beta_s0 = imin(beta_s0, b);
                 beta_s1 = imin(beta_s1, b - Mr[kU - 1][r]);
+                const int m5 = A > kU ? row5[r * 64] : 0;
+                beta_p0 = imin(beta_p0, b + (m5 < 0 ? m5 : 0));
+                beta_p1 = imin(beta_p1, b - (m5 > 0 ? m5 : 0));
             }
         }
         {
@@ -670,25 +680,45 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
             T = gb < T ? gb : T;
         }
 
-        // Body minima of the prefix energies are read one body ahead (scalar loads).
-        // The body loop counts with 32-bit scalars (the SALU has no 64-bit
-        // less-than): a segment holds at most 2^15 bodies.
+        // Body minima of the prefix energies are read two bodies ahead (scalar
+        // loads).  The body loop counts with 32-bit scalars (the SALU has no
+        // 64-bit less-than): a segment holds at most 2^13 bodies.
         const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
         int epm_cur = Gated ? epmin[j_begin >> kU] : 0;
+        int epm_next = Gated ? epmin[(j_begin >> kU) + 1] : 0;
+        bool pair_clear = false;  // the previous body's pair bound covered this body
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
             const uint64_t base = j_begin + ((uint64_t)bi << kU);
             const bool last = bi + 1 == nbodies;
             const bool top_plus = ((base >> kU) & 1u) == 0;
-            int epm_next = 0;
-            if (Gated)  // the table has one padding entry past the last body
-                epm_next = epmin[(base >> kU) + 1];
+            int epm_after = 0;
+            if (Gated)  // the table has two padding entries past the last body
+                epm_after = epmin[(base >> kU) + 2];
             bool check = true;
             if (Gated) {
                 // Padding columns hold INT_MAX with zero rows (beta 0), so a lane
                 // of padding columns only has the bound INT_MAX.
-                const int thb = T - epm_cur;
-                const int bound = row_min<R>(E) + (top_plus ? beta_s0 : beta_s1);
-                check = __builtin_amdgcn_ballot_w64(bound <= thb) != 0;
+                if (pair_clear) {
+                    // T has not risen since the pair's bound was checked.
+                    check = false;
+                    pair_clear = false;
+                } else {
+                    const int emin = row_min<R>(E);
+                    if (top_plus && !last && A > kU) {
+                        // An even body and its partner: the 64 states of Gray bits
+                        // 0..5 fall by at most beta_p(bit 5 at the pair's start).
+                        const int thp = T - imin(epm_cur, epm_next);
+                        const int bp = emin + (((base >> (kU + 1)) & 1u) ? beta_p1 : beta_p0);
+                        pair_clear = __builtin_amdgcn_ballot_w64(bp <= thp) == 0;
+                    }
+                    if (pair_clear) {
+                        check = false;
+                    } else {
+                        const int thb = T - epm_cur;
+                        const int bound = emin + (top_plus ? beta_s0 : beta_s1);
+                        check = __builtin_amdgcn_ballot_w64(bound <= thb) != 0;
+                    }
+                }
             }
             ++bodies;
             if (!check) {
@@ -743,6 +773,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                     sub_row(E, row);
             }
             epm_cur = epm_next;
+            epm_next = epm_after;
         }
     }
 

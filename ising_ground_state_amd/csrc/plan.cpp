@@ -201,7 +201,7 @@ Layout layout_of(const qubo_plan &p)
     L.off_ep = off;
     off = align256(off + (1ull << p.prefix_bits) * 4);
     L.off_epmin = off;
-    off = align256(off + ((1ull << (p.prefix_bits - kRegBits)) + 1) * 4);  // + 1 padding entry
+    off = align256(off + ((1ull << (p.prefix_bits - kRegBits)) + 2) * 4);  // + 2 padding entries
     L.off_partials = off;
     off = align256(off + (uint64_t)p.blocks * p.waves_per_block * 32);  // one 32-byte partial per wave
     L.off_ctrl = off;

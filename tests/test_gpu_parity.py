@@ -188,6 +188,39 @@ def test_range_is_subcube(q, n, A, k):
             check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
 
 
+RAGGED = [(32, 96), (96, 160), (0, 32), (32, 64), (64, 128 + 32), (1024 + 32, 2048 - 32), (0, 2048)]
+
+
+def _slice_states(n, A, lo, hi):
+    """Indices of the states the slice [lo, hi) of the Gray walk covers."""
+    B = n - A
+    js = np.arange(lo, hi, dtype=np.uint64)
+    pre = (js ^ (js >> np.uint64(1))) << np.uint64(B)
+    return (pre[:, None] | np.arange(1 << B, dtype=np.uint64)[None, :]).ravel()
+
+
+@pytest.mark.parametrize("lo,hi", RAGGED)
+def test_ragged_slices(q, lo, hi):
+    """Slices that start or end on an odd 32-step body (or hold one body), so
+    that the 64-step pair bound and the single-body bound both decide; the
+    oracle evaluates every state of the slice from the definition."""
+    n, A = 16, 11
+    Q = qi.general_uniform(n, 7350, -4, 4)
+    idx = _slice_states(n, A, lo, hi)
+    E = oracle.energies(Q, idx)
+    m = int(E.min())
+    want = (m, int(idx[E == m].min()), int((E == m).sum()))
+    Qd = dev_q(Q)
+    for strict, R in ((False, 8), (True, 8), (False, 16)):
+        announce("ragged", lo, hi, strict, R)
+        assert q.search_range(Qd, A, lo, hi, strict=strict, cols_per_lane=R).triple() == want
+        check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
+    order = np.lexsort((idx, E))[:64]
+    announce("ragged lowest", lo, hi)
+    assert q.lowest(Qd, 64, prefix_bits=A, gray_lo=lo, gray_hi=hi) == \
+        [(int(E[i]), int(idx[i])) for i in order]
+
+
 def test_subcubes_at_full_size(q):
     """n = 48 and n = 50 at the benchmark's split: seeded sub-cubes of 2^32
     states against the stored oracle results (tests/golden/C4sub, C5sub)."""
