@@ -80,10 +80,17 @@ def cpu_baseline(cfg, seconds_budget=20.0):
     r = oracle.search_gray(cfg["Q"], k=k, top=top, threads=threads)
     dt = time.perf_counter() - t0
     states = 1 << free
+    # Tier A (every state from the definition) on the 2^24-state workload, for context.
+    c1 = qi.make_config("C1")
+    t1 = time.perf_counter()
+    oracle.search_direct(c1["Q"], threads=threads)
+    dt_a = time.perf_counter() - t1
     return {"value": states / dt / 1e12, "unit": "1e12 states/s", "cores": threads, "kind": "oracle",
             "sample": "tier-B Gray walk over the sub-cube of 2^%d states with the first %d variables "
                       "fixed to %d (seed %d); %.2f s wall" % (free, k, top, 4242 + n, dt),
-            "states": states, "seconds": dt, "subcube_result": list(r.triple())}
+            "states": states, "seconds": dt, "subcube_result": list(r.triple()),
+            "tier_a_c1": {"value": (1 << c1["n"]) / dt_a / 1e12, "unit": "1e12 states/s",
+                          "sample": "tier A (direct O(n^2) per state), all 2^%d states of C1" % c1["n"]}}
 
 
 def copy_calibration(mib: int):

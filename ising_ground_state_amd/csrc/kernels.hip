@@ -180,60 +180,67 @@ __global__ __launch_bounds__(256) void build_suffix_kernel(const int32_t *__rest
 }
 
 // Prefix energies in Gray order, ep[j] = E_p(g(j)) over the A prefix variables
-// (prefix variable v is bit A-1-v of the A-bit number).  A block covers 2^L
-// consecutive j (L = min(A, 8)); all of them share the high A-L bits of g(j),
-// which equal g(blockIdx.x).  Splitting x_p into high and low parts,
+// (prefix variable v is bit A-1-v of the A-bit number).  Block index b covers
+// the 2^L consecutive j = b 2^L .. b 2^L + 2^L - 1 (L = min(A, 8)); all of them
+// share the high A-L bits of g(j), which equal g(b).  Splitting x_p into high
+// and low parts,
 //   E_p = E_hi + E_lo + sum_{v in lo, x_v = 1} K[v],   K[v] = sum_{w in hi, x_w = 1} U[w][v],
 // so each block evaluates E_hi and K once and each thread only its low part.
 // The same kernel writes epmin[k] = min of ep over the 32-step body k (Gray steps
 // 32k .. 32k+31), which bounds the prefix energy of every state of that body.
 __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *__restrict__ U,
                                                                 int ns, int A, int L,
+                                                                uint64_t nblocks,
                                                                 int32_t *__restrict__ ep,
                                                                 int32_t *__restrict__ epmin)
 {
     __shared__ int K[8];
     __shared__ int ehi_sh;
     const int H = A - L;
-    const uint64_t hi = gray((uint64_t)blockIdx.x);  // high part of g(j), H bits
     const int tid = threadIdx.x;
-    if (tid < L) {
-        const int v = H + tid;  // a low variable
-        int k = 0;
-        for (int w = 0; w < H; ++w)
-            k += ((hi >> (H - 1 - w)) & 1u) ? U[w * ns + v] : 0;
-        K[tid] = k;
-    } else if (tid == L) {
-        int e = 0;
-        for (int w = 0; w < H; ++w) {
-            if (!((hi >> (H - 1 - w)) & 1u))
-                continue;
-            for (int w2 = w; w2 < H; ++w2)
-                e += ((hi >> (H - 1 - w2)) & 1u) ? U[w * ns + w2] : 0;
+    // Block-stride loop: a dispatch holds fewer than 2^32 work-items, and A = 32
+    // needs 2^32 prefixes.  The trip count is the same for every thread of a block.
+    for (uint64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+        const uint64_t hi = gray(blk);  // high part of g(j), H bits
+        if (tid < L) {
+            const int v = H + tid;  // a low variable
+            int k = 0;
+            for (int w = 0; w < H; ++w)
+                k += ((hi >> (H - 1 - w)) & 1u) ? U[w * ns + v] : 0;
+            K[tid] = k;
+        } else if (tid == L) {
+            int e = 0;
+            for (int w = 0; w < H; ++w) {
+                if (!((hi >> (H - 1 - w)) & 1u))
+                    continue;
+                for (int w2 = w; w2 < H; ++w2)
+                    e += ((hi >> (H - 1 - w2)) & 1u) ? U[w * ns + w2] : 0;
+            }
+            ehi_sh = e;
         }
-        ehi_sh = e;
-    }
-    __syncthreads();
-    const uint64_t j = ((uint64_t)blockIdx.x << L) | (uint64_t)tid;
-    const uint32_t lo = (uint32_t)(gray(j) & ((1u << L) - 1));
-    int e = ehi_sh;
-    for (int a = 0; a < L; ++a) {
-        if (!((lo >> (L - 1 - a)) & 1u))
-            continue;
-        e += K[a];
-        for (int b = a; b < L; ++b)
-            e += ((lo >> (L - 1 - b)) & 1u) ? U[(H + a) * ns + (H + b)] : 0;
-    }
-    ep[j] = e;
-    // 32 consecutive j are 32 consecutive lanes of one wave (blocks have 2^L >= 32 threads).
-    int m = e;
+        __syncthreads();
+        const uint64_t j = (blk << L) | (uint64_t)tid;
+        const uint32_t lo = (uint32_t)(gray(j) & ((1u << L) - 1));
+        int e = ehi_sh;
+        for (int a = 0; a < L; ++a) {
+            if (!((lo >> (L - 1 - a)) & 1u))
+                continue;
+            e += K[a];
+            for (int b = a; b < L; ++b)
+                e += ((lo >> (L - 1 - b)) & 1u) ? U[(H + a) * ns + (H + b)] : 0;
+        }
+        ep[j] = e;
+        // 32 consecutive j are 32 consecutive lanes of one wave (blocks have 2^L >= 32 threads).
+        int m = e;
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) {
-        const int o = __shfl_xor(m, off, 64);
-        m = o < m ? o : m;
+        for (int off = 16; off >= 1; off >>= 1) {
+            const int o = __shfl_xor(m, off, 64);
+            m = o < m ? o : m;
+        }
+        if ((tid & 31) == 0)
+            epmin[j >> 5] = m;
+        __syncthreads();  // K and ehi_sh are rewritten by the next iteration
     }
-    if ((tid & 31) == 0)
-        epmin[j >> 5] = m;
 }
 
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
@@ -247,11 +254,10 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
     if (err != hipSuccess)
         return err;
     const int L = A < 8 ? A : 8;
-    const uint64_t blocks = 1ull << (A - L);
-    if (blocks > 0x7fffffffull)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL(build_prefix_gray_kernel, dim3((unsigned)blocks), dim3(1u << L), 0, stream,
-                       U, ns, A, L, ep, epmin);
+    const uint64_t nblocks = 1ull << (A - L);
+    const uint64_t grid = nblocks < (1ull << 20) ? nblocks : (1ull << 20);
+    hipLaunchKernelGGL(build_prefix_gray_kernel, dim3((unsigned)grid), dim3(1u << L), 0, stream,
+                       U, ns, A, L, nblocks, ep, epmin);
     return hipGetLastError();
 }
 

@@ -109,3 +109,21 @@ def test_spectrum_n48(q):
     h0 = q.lowest(Qd, 64, prefix_bits=A, gray_lo=0, gray_hi=half, cols_per_lane=16)
     h1 = q.lowest(Qd, 64, prefix_bits=A, gray_lo=half, gray_hi=2 * half, cols_per_lane=16)
     assert sorted(h0 + h1)[:64] == low
+
+
+def test_split_invariance_n48(q):
+    """The benchmark workload (n = 48) at other prefix/suffix splits and cache
+    sizes gives the same triple and the same 64 lowest states: the result
+    depends on Q only."""
+    cfg = qi.make_config("C4")
+    Qd = dev_q(cfg["Q"])
+    announce("C4 default split")
+    want = q.search(Qd).triple()
+    for A, l in [(26, 8), (30, 10), (32, 14)]:
+        announce("C4 split", A, l)
+        assert q.search(Qd, prefix_bits=A, cache_bits=l).triple() == want, (A, l)
+        check_coverage(q, 48, A, l)
+    announce("C4 spectrum default split")
+    low = q.lowest(Qd, 64)
+    announce("C4 spectrum split 31 12")
+    assert q.lowest(Qd, 64, prefix_bits=31, cache_bits=12) == low

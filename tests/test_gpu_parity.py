@@ -40,7 +40,7 @@ def golden(name):
 
 # ---------------------------------------------------------------- cache builder
 
-@pytest.mark.parametrize("n,A", [(5, 5), (9, 5), (12, 7), (17, 9), (24, 14), (26, 20)])
+@pytest.mark.parametrize("n,A", [(5, 5), (9, 5), (12, 7), (17, 9), (24, 14), (26, 20), (30, 29)])
 def test_tables_match_definition(q, n, A):
     """E_s, M_int and the Gray-ordered E_p equal energies of states built from
     the definition: E_s[c] = E(c), M_int[v][c] = E(e_v | c) - E(e_v) - E(c),
