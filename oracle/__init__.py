@@ -5,7 +5,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 imports nothing from the solver: it shares no code, header, table or helper with
 the HIP path.  Its inputs come from ``qubo_instances`` (random draws only).
 
-The arithmetic lives in ``oracle.c`` (plain C, int64): the definition
+The arithmetic lives in ``oracle.c`` (plain C, int64; binary64 for a
+floating-point Q, summed in a fixed row-major order): the definition
 E(x) = sum_ij Q_ij x_i x_j of Maltsev et al., "Terastate-per-second QUBO
 Brute-Force on a Single GPU", sec. I, evaluated directly (tier A) and by an
 incremental Gray-code walk (tier B, sec. I.D).  This module only marshals
@@ -57,6 +58,33 @@ class Result:
         return (self.min_energy, self.argmin, self.count)
 
 
+class _ResultF64(ctypes.Structure):
+    _fields_ = [("min_energy", ctypes.c_double), ("argmin", ctypes.c_uint64),
+                ("count", ctypes.c_uint64), ("max_abs_energy", ctypes.c_double)]
+
+
+@dataclass(frozen=True)
+class ResultF64:
+    min_energy: float
+    argmin: int
+    count: int
+    max_abs_energy: float
+
+    def triple(self) -> tuple[float, int, int]:
+        return (self.min_energy, self.argmin, self.count)
+
+
+def _farray(Q) -> np.ndarray:
+    q = np.ascontiguousarray(np.asarray(Q, dtype=np.float64))
+    if q.ndim != 2 or q.shape[0] != q.shape[1]:
+        raise ValueError("Q must be square")
+    return q
+
+
+def _fptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
 def _qarray(Q) -> np.ndarray:
     q = np.asarray(Q, dtype=np.int64)
     if q.ndim != 2 or q.shape[0] != q.shape[1]:
@@ -95,6 +123,15 @@ class Oracle:
                                       ctypes.c_uint64, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)]
         lib.oracle_lowest.restype = ctypes.c_int
+        f64p = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_energy_f64.argtypes = [f64p, ctypes.c_int, ctypes.c_uint64]
+        lib.oracle_energy_f64.restype = ctypes.c_double
+        lib.oracle_energy_many_f64.argtypes = [f64p, ctypes.c_int, ctypes.POINTER(ctypes.c_uint64),
+                                               ctypes.c_uint64, f64p]
+        lib.oracle_energy_many_f64.restype = None
+        lib.oracle_search_direct_f64.argtypes = [f64p, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                                                 ctypes.c_int, ctypes.POINTER(_ResultF64)]
+        lib.oracle_search_direct_f64.restype = ctypes.c_int
         lib.oracle_version.restype = ctypes.c_char_p
         self.lib = lib
         self.path = path
@@ -151,6 +188,32 @@ class Oracle:
             raise ValueError("oracle_lowest failed (%d)" % rc)
         return [(int(e[i]), int(ix[i])) for i in range(found.value)]
 
+    def energy_f64(self, Q, idx: int) -> float:
+        """E(x) of a float64 Q, summed in the fixed row-major order."""
+        q = _farray(Q)
+        return float(self.lib.oracle_energy_f64(_fptr(q), q.shape[0], int(idx)))
+
+    def energies_f64(self, Q, idx) -> np.ndarray:
+        q = _farray(Q)
+        ids = np.ascontiguousarray(np.asarray(idx, dtype=np.uint64))
+        out = np.empty(ids.shape, dtype=np.float64)
+        self.lib.oracle_energy_many_f64(_fptr(q), q.shape[0],
+                                        ids.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), ids.size,
+                                        _fptr(out))
+        return out
+
+    def search_direct_f64(self, Q, lo: int = 0, hi: int | None = None, threads: int | None = None) -> ResultF64:
+        """Tier A for a float64 Q over the indices [lo, hi)."""
+        q = _farray(Q)
+        n = q.shape[0]
+        if hi is None:
+            hi = 1 << n
+        r = _ResultF64()
+        rc = self.lib.oracle_search_direct_f64(_fptr(q), n, lo, hi, threads or default_threads(), ctypes.byref(r))
+        if rc != 0:
+            raise ValueError("oracle_search_direct_f64 failed (%d)" % rc)
+        return ResultF64(r.min_energy, r.argmin, r.count, r.max_abs_energy)
+
     def version(self) -> str:
         return self.lib.oracle_version().decode()
 
@@ -186,6 +249,18 @@ def search_gray(Q, k: int = 0, top: int = 0, threads: int | None = None) -> Resu
 def lowest(Q, k: int, gray_walk: bool = True, threads: int | None = None, fixed: int = 0,
            top: int = 0) -> list[tuple[int, int]]:
     return default().lowest(Q, k, gray_walk, threads, fixed, top)
+
+
+def energy_f64(Q, idx: int) -> float:
+    return default().energy_f64(Q, idx)
+
+
+def energies_f64(Q, idx) -> np.ndarray:
+    return default().energies_f64(Q, idx)
+
+
+def search_direct_f64(Q, lo: int = 0, hi: int | None = None, threads: int | None = None) -> ResultF64:
+    return default().search_direct_f64(Q, lo, hi, threads)
 
 
 def version() -> str:

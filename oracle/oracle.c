@@ -418,4 +418,131 @@ int oracle_lowest(const int32_t *Q, int n, int k, int gray_walk, int fixed, uint
     return 0;
 }
 
-const char *oracle_version(void) { return "qubo-oracle 1 (tier A direct, tier B Gray)"; }
+/* ------------------------------------------------------------------ */
+/* Floating-point Q (fp64).  The energy is the definition summed in a   */
+/* fixed order: e = 0; for i ascending with x_i = 1, for j ascending    */
+/* with x_j = 1: e += Q_ij, every add an IEEE binary64 add rounded to   */
+/* nearest.  (Adding the zero products Q_ij x_i x_j of unset variables  */
+/* would leave e unchanged: e starts at +0 and never becomes -0.)       */
+/* The minimum, the lowest minimiser and the count of states with       */
+/* exactly that value follow as for integers.                           */
+/* ------------------------------------------------------------------ */
+
+double oracle_energy_f64(const double *Q, int n, uint64_t idx)
+{
+    double e = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (!((idx >> (n - 1 - i)) & 1u))
+            continue;
+        for (int j = 0; j < n; ++j) {
+            if (!((idx >> (n - 1 - j)) & 1u))
+                continue;
+            /* MUTANT(11): the terms in column-major order */
+            e += MUTANT(11) ? Q[(size_t)j * n + i] : Q[(size_t)i * n + j];
+        }
+    }
+    return e;
+}
+
+void oracle_energy_many_f64(const double *Q, int n, const uint64_t *idx, uint64_t m, double *out)
+{
+    for (uint64_t k = 0; k < m; ++k)
+        out[k] = oracle_energy_f64(Q, n, idx[k]);
+}
+
+typedef struct {
+    const double *Q;
+    int n;
+    uint64_t lo, hi;
+    oracle_result_f64 res;
+} direct_job_f64;
+
+static int near_tie(double a, double b)
+{
+    double d = a - b, m = (a < 0 ? -a : a);
+    return (d < 0 ? -d : d) <= 1e-12 * m;
+}
+
+static void record_f64(oracle_result_f64 *r, double e, uint64_t idx)
+{
+    if (MUTANT(12) && r->count != 0 && near_tie(e, r->min_energy))
+        e = r->min_energy; /* MUTANT(12): a tolerance decides ties */
+    if (r->count == 0 || e < r->min_energy) {
+        r->min_energy = e;
+        r->count = 1;
+        r->argmin = idx;
+    } else if (e == r->min_energy) {
+        r->count += 1;
+        if (idx < r->argmin)
+            r->argmin = idx;
+    }
+    double a = e < 0 ? -e : e;
+    if (a > r->max_abs_energy)
+        r->max_abs_energy = a;
+}
+
+static void merge_f64(oracle_result_f64 *acc, const oracle_result_f64 *part)
+{
+    if (part->count == 0)
+        return;
+    if (acc->count == 0 || part->min_energy < acc->min_energy) {
+        acc->min_energy = part->min_energy;
+        acc->count = part->count;
+        acc->argmin = part->argmin;
+    } else if (part->min_energy == acc->min_energy) {
+        acc->count += part->count;
+        if (part->argmin < acc->argmin)
+            acc->argmin = part->argmin;
+    }
+    if (part->max_abs_energy > acc->max_abs_energy)
+        acc->max_abs_energy = part->max_abs_energy;
+}
+
+static void *direct_worker_f64(void *arg)
+{
+    direct_job_f64 *job = (direct_job_f64 *)arg;
+    memset(&job->res, 0, sizeof(job->res));
+    for (uint64_t idx = job->lo; idx < job->hi; ++idx)
+        record_f64(&job->res, oracle_energy_f64(job->Q, job->n, idx), idx);
+    return NULL;
+}
+
+int oracle_search_direct_f64(const double *Q, int n, uint64_t lo, uint64_t hi, int threads,
+                             oracle_result_f64 *out)
+{
+    if (!Q || !out || n < 1 || n > ORACLE_MAX_N)
+        return -1;
+    uint64_t total = 1ull << n;
+    if (hi > total || lo > hi)
+        return -1;
+    memset(out, 0, sizeof(*out));
+    threads = clamp_threads(threads);
+    uint64_t span = hi - lo;
+    if ((uint64_t)threads > span)
+        threads = span ? (int)span : 1;
+    direct_job_f64 *jobs = (direct_job_f64 *)calloc((size_t)threads, sizeof(direct_job_f64));
+    pthread_t *tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    if (!jobs || !tids) {
+        free(jobs);
+        free(tids);
+        return -2;
+    }
+    for (int t = 0; t < threads; ++t) {
+        jobs[t].Q = Q;
+        jobs[t].n = n;
+        jobs[t].lo = lo + span * (uint64_t)t / (uint64_t)threads;
+        jobs[t].hi = lo + span * (uint64_t)(t + 1) / (uint64_t)threads;
+    }
+    for (int t = 1; t < threads; ++t)
+        pthread_create(&tids[t], NULL, direct_worker_f64, &jobs[t]);
+    direct_worker_f64(&jobs[0]);
+    for (int t = 1; t < threads; ++t)
+        pthread_join(tids[t], NULL);
+    for (int t = 0; t < threads; ++t)
+        merge_f64(out, &jobs[t].res);
+    free(jobs);
+    free(tids);
+    return 0;
+}
+
+const char *oracle_version(void) { return "qubo-oracle 2 (tier A direct, tier B Gray; fp64 tier A)"; }

@@ -40,5 +40,21 @@ int oracle_search_gray(const int32_t *Q, int n, int k, uint64_t top, int threads
 int oracle_lowest(const int32_t *Q, int n, int k, int gray_walk, int fixed, uint64_t top,
                   int threads, int64_t *energies, uint64_t *indices, int *found);
 
+/* Floating-point Q (row-major n x n binary64).  E(x) is the sum, in this
+ * order, of Q_ij over i ascending with x_i = 1 and, inside, j ascending with
+ * x_j = 1, each add rounded to nearest; ties are exact equality. */
+typedef struct {
+    double min_energy;
+    uint64_t argmin;
+    uint64_t count;
+    double max_abs_energy;
+} oracle_result_f64;
+
+double oracle_energy_f64(const double *Q, int n, uint64_t idx);
+void oracle_energy_many_f64(const double *Q, int n, const uint64_t *idx, uint64_t m, double *out);
+/* Tier A over idx in [lo, hi). */
+int oracle_search_direct_f64(const double *Q, int n, uint64_t lo, uint64_t hi, int threads,
+                             oracle_result_f64 *out);
+
 const char *oracle_version(void);
 #endif

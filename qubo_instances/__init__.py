@@ -94,6 +94,29 @@ def general_uniform(n: int, seed: int, lo: int, hi: int) -> list[list[int]]:
     return [[rng.uniform_int(lo, hi) for _ in range(n)] for _ in range(n)]
 
 
+def _real(rng: SplitMix64, lo: float, hi: float) -> float:
+    return lo + (hi - lo) * rng.uniform01()
+
+
+def symmetric_uniform_f64(n: int, seed: int, lo: float, hi: float) -> list[list[float]]:
+    """Real symmetric Q (binary64): upper triangle drawn row-major, uniform in
+    [lo, hi), and mirrored."""
+    rng = SplitMix64(seed)
+    q = [[0.0] * n for _ in range(n)]
+    for i in range(n):
+        for j in range(i, n):
+            v = _real(rng, lo, hi)
+            q[i][j] = v
+            q[j][i] = v
+    return q
+
+
+def general_uniform_f64(n: int, seed: int, lo: float, hi: float) -> list[list[float]]:
+    """Real non-symmetric Q (binary64), every entry uniform in [lo, hi), row-major."""
+    rng = SplitMix64(seed)
+    return [[_real(rng, lo, hi) for _ in range(n)] for _ in range(n)]
+
+
 def ising_to_qubo(J: list[list[int]], h: list[int]) -> tuple[list[list[int]], int]:
     """Map H(s) = sum_{i<j} J_ij s_i s_j + sum_i h_i s_i (s = 2x - 1) to a QUBO.
 
@@ -216,6 +239,10 @@ CONFIGS = {
     "C3": dict(n=40, seed=1003, desc="+-1 Sherrington-Kirkpatrick n=40, h=0, as an int32 QUBO via x=(1+s)/2"),
     "C4": dict(n=48, seed=1004, desc="dense QUBO n=48, symmetric, all entries uniform in [-100,100]"),
     "C5": dict(n=50, seed=1005, desc="dense QUBO n=50, round(10 U U^T) + uniform[-20,20] noise, U 50x4 standard normal"),
+    # real-valued (binary64) counterparts of C1, C2 and C4
+    "C1f": dict(n=24, seed=1011, desc="dense real QUBO n=24, symmetric, binary64 entries uniform in [-100,100)"),
+    "C2f": dict(n=32, seed=1012, desc="dense real QUBO n=32, symmetric, binary64 entries uniform in [-100,100)"),
+    "C4f": dict(n=48, seed=1014, desc="dense real QUBO n=48, symmetric, binary64 entries uniform in [-100,100)"),
 }
 
 
@@ -238,6 +265,8 @@ def make_config(name: str) -> dict:
         out.update(Q=q, J=J, h=h, C=c)
     elif name == "C5":
         out["Q"] = low_rank_noise(n, seed)
+    elif name in ("C1f", "C2f", "C4f"):
+        out["Q"] = symmetric_uniform_f64(n, seed, -100.0, 100.0)
     else:
         raise KeyError(name)
     return out
@@ -263,7 +292,9 @@ def as_array(q):
 
 
 def sha256_of(q) -> str:
-    """SHA-256 of the little-endian int32 row-major bytes of Q."""
+    """SHA-256 of the little-endian row-major bytes of Q: int32 entries, or
+    binary64 when the entries are floats."""
     n = len(q)
-    buf = b"".join(struct.pack("<%di" % n, *row) for row in q)
+    fmt = "<%dd" % n if isinstance(q[0][0], float) else "<%di" % n
+    buf = b"".join(struct.pack(fmt, *row) for row in q)
     return hashlib.sha256(buf).hexdigest()

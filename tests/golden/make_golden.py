@@ -8,6 +8,7 @@ Calls only the CPU oracle (``oracle``) on the seeded workloads of
     python tests/golden/make_golden.py C4sub C5sub      # seeded sub-cubes of 2^32 states
     python tests/golden/make_golden.py C1low C2low C2plow C4sublow C5sublow
                                                         # the 64 lowest states (spectrum)
+    python tests/golden/make_golden.py C1f C2f C4fsub   # real-valued (binary64) workloads, tier A
 
 Full searches store {sha256_Q, n, min_energy, argmin, count, max_abs_energy}.
 Sub-cube files store one record per sub-cube: the first k variables are fixed
@@ -119,11 +120,54 @@ def lowest_subcubes(name: str, threads: int) -> dict:
                 tier="B (Gray walk)", seconds_total=round(time.time() - t_all, 2), host=host_info(threads))
 
 
+F_SUB_FREE_BITS = 28
+F_SUB_COUNT = 8
+
+
+def full_f64(name: str, threads: int) -> dict:
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    t0 = time.time()
+    r = oracle.search_direct_f64(Q, threads=threads)
+    return dict(name=name, desc=cfg["desc"], n=n, seed=cfg["seed"], sha256_Q=qi.sha256_of(Q),
+                min_energy_hex=float.hex(r.min_energy), min_energy=r.min_energy, argmin=r.argmin,
+                count=r.count, tier="A (direct, binary64 in row-major order)",
+                seconds=round(time.time() - t0, 2), host=host_info(threads))
+
+
+def subcubes_f64(name: str, threads: int) -> dict:
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    k = n - F_SUB_FREE_BITS
+    rng = qi.SplitMix64(SUB_SEED + 100 + n)
+    tops = []
+    while len(tops) < F_SUB_COUNT:
+        t = rng.uniform_int(0, (1 << k) - 1)
+        if t not in tops:
+            tops.append(t)
+    cubes = []
+    t_all = time.time()
+    m = F_SUB_FREE_BITS
+    for top in tops:
+        r = oracle.search_direct_f64(Q, top << m, (top + 1) << m, threads=threads)
+        cubes.append(dict(k=k, top=top, min_energy_hex=float.hex(r.min_energy), min_energy=r.min_energy,
+                          argmin=r.argmin, count=r.count))
+        print("  %s top=%d -> %s" % (name, top, r.triple()), flush=True)
+    return dict(name=name + "sub", desc=cfg["desc"], n=n, seed=cfg["seed"], sha256_Q=qi.sha256_of(Q),
+                free_bits=F_SUB_FREE_BITS, sub_seed=SUB_SEED + 100 + n, cubes=cubes,
+                tier="A (direct, binary64 in row-major order)", seconds_total=round(time.time() - t_all, 2),
+                host=host_info(threads))
+
+
 def main(argv):
     threads = oracle.default_threads()
     for arg in argv:
         print("computing", arg, "on", threads, "threads", flush=True)
-        if arg.endswith("sublow"):
+        if arg.endswith("fsub"):
+            rec = subcubes_f64(arg[:-3], threads)
+        elif arg in ("C1f", "C2f"):
+            rec = full_f64(arg, threads)
+        elif arg.endswith("sublow"):
             rec = lowest_subcubes(arg[:-6], threads)
         elif arg.endswith("low"):
             rec = lowest_full(arg[:-3], threads)

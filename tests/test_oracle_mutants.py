@@ -4,13 +4,14 @@ Each build with -DORACLE_MUTATION=k plants one plausible mistake in the CPU
 oracle (on the CPU only): a dropped diagonal, a reversed bit order, a wrong sign
 in the Gray update, a missing field update, a traversal-order tie-break, a
 count that ignores ties, a field without its diagonal, a dropped x_j factor,
-a flip applied to the wrong variable and an off-by-one in the k-lowest list.
+a flip applied to the wrong variable, an off-by-one in the k-lowest list, a
+floating-point sum in the wrong order and floating-point ties within a tolerance.
 The pin suite must reject every one.
 """
 import pytest
 
 import oracle
-from test_oracle_pins import ALL_PINS
+from test_oracle_pins import ALL_PINS, ALL_PINS_F64
 
 MUTANTS = {
     1: "energy drops the diagonal terms",
@@ -23,6 +24,8 @@ MUTANTS = {
     8: "energy drops the x_j factor",
     9: "Gray walk flips variable t instead of n-1-t",
     10: "the k-lowest list never fills its last slot after it is full",
+    11: "floating-point energies summed in column-major order",
+    12: "floating-point energies within a relative 1e-12 count as ties",
 }
 
 
@@ -31,7 +34,7 @@ def test_pins_reject_mutant(k, tmp_path):
     path = oracle.build(str(tmp_path / ("liboracle_m%d.so" % k)), defines=("ORACLE_MUTATION=%d" % k,))
     o = oracle.Oracle(path)
     failed = []
-    for pin in ALL_PINS:
+    for pin in ALL_PINS + ALL_PINS_F64:
         try:
             pin(o)
         except AssertionError:

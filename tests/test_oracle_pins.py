@@ -236,6 +236,66 @@ def pin_lowest(o: oracle.Oracle):
         assert sum(1 << i for i in range(n) if (idx >> (n - 1 - i)) & 1) == e
 
 
+# ------------------------------------------------------------------- fp64 pins
+
+def _f(v) -> float:
+    return float.fromhex(v) if "0x" in v else float(v)
+
+
+def pin_f64_worked_examples(o: oracle.Oracle):
+    with open(os.path.join(GOLDEN, "worked_examples_f64.json")) as f:
+        data = json.load(f)
+    for ex in data["examples"]:
+        vals = [_f(v) for v in ex["Q"]]
+        n = int(round(len(vals) ** 0.5))
+        Q = np.asarray(vals, dtype=np.float64).reshape(n, n)
+        got = [o.energy_f64(Q, i) for i in range(1 << n)]
+        assert got == [_f(v) for v in ex["energies"]], ex["name"]
+        want = (_f(ex["min"]), ex["argmin"], ex["count"])
+        for threads in (1, 2, 4):
+            assert o.search_direct_f64(Q, threads=threads).triple() == want, (ex["name"], threads)
+
+
+def pin_f64_integer_valued(o: oracle.Oracle):
+    """Integer-valued binary64 matrices sum exactly (|partial sums| < 2^53), so
+    the floating-point result equals the integer oracle's."""
+    for n, seed, lo, hi in [(1, 2701, -5, 5), (6, 2702, -1, 1), (9, 2703, -100, 100), (12, 2704, -2, 2),
+                            (14, 2705, -1000, 1000)]:
+        Q = rand_general(n, seed, lo, hi)
+        r = o.search_direct(Q)
+        rf = o.search_direct_f64(np.asarray(Q, dtype=np.float64), threads=3)
+        assert rf.triple() == (float(r.min_energy), r.argmin, r.count), (n, seed)
+        idx = np.arange(1 << n, dtype=np.uint64)
+        assert np.array_equal(o.energies_f64(np.asarray(Q, dtype=np.float64), idx),
+                              o.energies(Q, idx).astype(np.float64)), (n, seed)
+
+
+def pin_f64_fractional(o: oracle.Oracle):
+    """Fractional matrices: exact scaling by powers of two, closed forms of
+    single-variable states, and a planted instance whose minimiser is known."""
+    rng = np.random.default_rng(2711)
+    for n in (5, 10, 13):
+        Q = rng.uniform(-50.0, 50.0, size=(n, n))
+        base = o.search_direct_f64(Q)
+        for k in (-3, 1, 7):  # x 2^k is exact in every partial sum
+            r = o.search_direct_f64(Q * 2.0 ** k)
+            assert r.triple() == (base.min_energy * 2.0 ** k, base.argmin, base.count), (n, k)
+        assert o.energy_f64(Q, 0) == 0.0
+        for i in range(n):
+            assert o.energy_f64(Q, 1 << (n - 1 - i)) == Q[i, i]
+    # planted: Q = gauge transform of a positive-definite-like P (integer part)
+    # plus tiny fractional noise; the minimiser stays x* (gap >= 1 >> noise)
+    Qi, P, a = qi.planted(11, 2712)
+    Qf = np.asarray(Qi, dtype=np.float64) + rng.uniform(-1e-3, 1e-3, size=(11, 11))
+    r = o.search_direct_f64(Qf)
+    av = np.asarray(a, dtype=np.int64)
+    assert (r.argmin, r.count) == (qi.bits_to_index(a), 1)
+    assert abs(r.min_energy + float(av @ np.asarray(P, dtype=np.int64) @ av)) < 11 * 11 * 1e-3
+
+
+ALL_PINS_F64 = [pin_f64_worked_examples, pin_f64_integer_valued, pin_f64_fractional]
+
+
 ALL_PINS = [pin_worked_examples, pin_closed_forms, pin_numpy_third_implementation, pin_tiers_agree,
             pin_special_cases, pin_planted, pin_mattis, pin_ising_identity, pin_invariances,
             pin_lowest]
@@ -243,7 +303,7 @@ ALL_PINS = [pin_worked_examples, pin_closed_forms, pin_numpy_third_implementatio
 
 # -------------------------------------------------------------------------- tests
 
-@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+@pytest.mark.parametrize("pin", ALL_PINS + ALL_PINS_F64, ids=lambda p: p.__name__)
 def test_pin(pin):
     pin(oracle.default())
 
