@@ -38,16 +38,17 @@ OPS_PER_STATE = 1
 OPS_PER_STATE_ADD_CMP = 2
 
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gray_search_gated_n48_counters.json")
-# What the search kernel's machine code is built from: its source, its header and the build flags.
-KERNEL_INPUTS = [os.path.join(ROOT, "ising_ground_state_amd", *parts) for parts in
-                 (("csrc", "kernels.hip"), ("csrc", "kernels.h"), ("build.py",))]
+# What the search kernel's machine code is built from: its source, its header and the compiler flags.
+KERNEL_INPUTS = [os.path.join(ROOT, "ising_ground_state_amd", "csrc", name) for name in ("kernels.hip", "kernels.h")]
 
 
 def kernel_source_hash() -> str:
+    from ising_ground_state_amd import build as libbuild
     h = hashlib.sha256()
     for path in KERNEL_INPUTS:
         with open(path, "rb") as f:
             h.update(f.read())
+    h.update(repr(libbuild.FLAGS).encode())
     return h.hexdigest()[:16]
 
 

@@ -133,6 +133,7 @@ typedef struct {
                          = Gray steps x 2^B rounded up to whole column groups) */
     uint64_t checked_bodies; /* bodies that ran the per-step minimum (all of them in strict mode) */
     uint64_t slow_bodies;    /* bodies re-walked on the exact path (records and ties) */
+    uint64_t candidates;     /* real-valued search: states re-evaluated from the definition */
 } qubo_timing;
 QUBO_API int qubo_last_timing(qubo_timing *out);
 
@@ -202,6 +203,35 @@ typedef struct {
 QUBO_API int qubo_search_lowest(const int32_t *Q, int n, int k, int prefix_bits, int cache_bits,
                                 uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
                                 qubo_state *out, int *found);
+
+/* A real-valued Q (sec. VI.B names floating-point matrices as future work,
+ * with the rounding that long incremental Gray-code updates accumulate as the
+ * difficulty).  Definition used here: E(x) is the binary64 sum of Q_ij over i
+ * ascending with x_i = 1 and, inside, j ascending with x_j = 1, each add
+ * rounded to nearest (the sum of sec. I in one fixed order); min_energy is the
+ * smallest such value, argmin the lowest index attaining it exactly, count the
+ * number of states attaining it exactly.  Result (24 bytes): */
+typedef struct {
+    double min_energy;
+    uint64_t argmin;
+    uint64_t count;
+} qubo_result_f64;
+/* Q: device pointer, n x n binary64, row-major; read only.  n: 1..58 (no
+ * outer split).  prefix_bits, cache_bits, gray_lo, gray_hi, stream: as for
+ * qubo_search_ex (cache_bits defaults to min(A, 11): binary64 rows in LDS).
+ * flags: 0 or QUBO_FLAG_COLS8.  Every entry must be finite and sum |Q_ij| at
+ * most 2^100 (else QUBO_ERANGE).
+ * The walk is the integer kernel's, with a binary64 anchor per column advanced
+ * twice per 32-step body and the 32 states of a body one fp32 add each; a
+ * state whose fp32 energy comes within delta = 2^-14 sum |Q_ij| of the best
+ * exact energy so far is re-evaluated from the definition on the GPU, so the
+ * result is exactly the definition's.  Instances with many states within delta
+ * of the minimum (e.g. Q = 0) are correct but slow: each such state costs an
+ * O(n^2) evaluation.  Blocking; same ownership and error behaviour as
+ * qubo_search_ex; qubo_last_timing reports the re-evaluated states. */
+QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_bits,
+                             uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
+                             qubo_result_f64 *out);
 
 /* Builds the cache tables of a plan into caller-provided device buffers, for
  * inspection (sec. III.A preprocessing steps 1-3, eq. 8):

@@ -44,6 +44,10 @@ class _Result(ctypes.Structure):
                 ("argmin", ctypes.c_uint64), ("count", ctypes.c_uint64)]
 
 
+class _ResultF64(ctypes.Structure):
+    _fields_ = [("min_energy", ctypes.c_double), ("argmin", ctypes.c_uint64), ("count", ctypes.c_uint64)]
+
+
 class _State(ctypes.Structure):
     _fields_ = [("energy", ctypes.c_int32), ("reserved", ctypes.c_uint32), ("index", ctypes.c_uint64)]
 
@@ -61,7 +65,7 @@ class _Timing(ctypes.Structure):
                 ("reduce_ms", ctypes.c_float), ("total_ms", ctypes.c_float),
                 ("states", ctypes.c_uint64), ("blocks", ctypes.c_int32), ("reserved", ctypes.c_uint32),
                 ("bodies", ctypes.c_uint64), ("checked_bodies", ctypes.c_uint64),
-                ("slow_bodies", ctypes.c_uint64)]
+                ("slow_bodies", ctypes.c_uint64), ("candidates", ctypes.c_uint64)]
 
 
 @dataclass(frozen=True)
@@ -81,7 +85,8 @@ class Result:
 _lib = None
 
 EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range", "qubo_search_ex",
-           "qubo_build_tables", "qubo_last_timing", "qubo_search_lowest", "qubo_strerror", "qubo_version")
+           "qubo_build_tables", "qubo_last_timing", "qubo_search_lowest", "qubo_search_f64",
+           "qubo_strerror", "qubo_version")
 MAX_LOWEST = 64
 FLAG_STRICT_MIN = 1
 FLAG_COLS8 = 2
@@ -116,7 +121,9 @@ def load(path: str = LIB_PATH):
     lib.qubo_strerror.argtypes = [ctypes.c_int]
     lib.qubo_strerror.restype = ctypes.c_char_p
     lib.qubo_version.restype = ctypes.c_char_p
-    for name in EXPORTS[:8]:
+    lib.qubo_search_f64.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                    ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.POINTER(_ResultF64)]
+    for name in EXPORTS[:9]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -246,6 +253,28 @@ def lowest(Q, k: int, prefix_bits: int | None = None, cache_bits: int | None = N
     if rc != QUBO_OK:
         raise QuboError(rc, "qubo_search_lowest")
     return [(out[i].energy, out[i].index) for i in range(found.value)]
+
+
+def search_f64(Q, prefix_bits: int | None = None, cache_bits: int | None = None, stream=None,
+               gray_lo: int = 0, gray_hi: int = 0) -> Result:
+    """Exhaustive search of a real-valued (float64) Q: the minimum of the
+    binary64 energy summed in row-major order over the set variables, its
+    lowest minimiser and the exact count.  Returns a Result with a float
+    min_energy."""
+    import torch
+    if not isinstance(Q, torch.Tensor) or not Q.is_cuda or Q.dtype != torch.float64:
+        raise TypeError("Q must be a float64 torch tensor on a HIP device")
+    if Q.dim() != 2 or Q.shape[0] != Q.shape[1]:
+        raise ValueError("Q must be square")
+    Q = Q.contiguous()
+    r = _ResultF64()
+    with torch.cuda.device(Q.device):
+        rc = load().qubo_search_f64(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
+                                    _opt(cache_bits), int(gray_lo), int(gray_hi), 0, _stream(Q, stream),
+                                    ctypes.byref(r))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_search_f64")
+    return Result(r.min_energy, r.argmin, r.count)
 
 
 def build_tables(Q, prefix_bits: int, stream=None):

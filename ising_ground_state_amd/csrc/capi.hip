@@ -17,7 +17,10 @@
 #include <iterator>
 #include <vector>
 
+#include <cmath>
+
 #include "kernels.h"
+#include "kernels_f64.h"
 #include "plan.h"
 #include "qubo.h"
 
@@ -483,6 +486,208 @@ int run(const Request &rq, qubo_result *out, qubo_state *low_out = nullptr,
     return QUBO_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Real-valued (binary64) Q.
+// ---------------------------------------------------------------------------
+
+struct RequestF64 {
+    const double *Q = nullptr;
+    int n = 0;
+    int prefix_bits = -1;
+    int cache_bits = -1;
+    bool ranged = false;
+    uint64_t gray_lo = 0, gray_hi = 0;
+    hipStream_t stream = nullptr;
+};
+
+int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
+{
+    using namespace qubo;
+    if (!rq.Q || !out || rq.n < 1 || rq.n > kMaxSingleVars)
+        return QUBO_EINVAL;
+    const int n = rq.n;
+    // The binary64 rows of Gray bits 4 .. l-1 sit in LDS (4 KiB each per
+    // workgroup): the default keeps 7 of them.
+    int cache_bits = rq.cache_bits;
+    if (cache_bits < 0 && n >= kMinSearchVars) {  // (tiny problems: the planner's fixed split)
+        qubo_plan probe;
+        const int rc0 = make_plan(n, rq.prefix_bits, -1, 256, 8, 0, &probe);
+        if (rc0 != QUBO_OK)
+            return rc0;
+        cache_bits = probe.prefix_bits < 11 ? probe.prefix_bits : 11;
+    }
+    DeviceInfo dev;
+    int rc = device_info(&dev);
+    if (rc != QUBO_OK)
+        return rc;
+    qubo_plan plan;
+    rc = make_plan(n, rq.prefix_bits, cache_bits, dev.num_cus, 8, 0, &plan);
+    if (rc != QUBO_OK)
+        return rc;
+    const int ns = plan.n_search, A = plan.prefix_bits, B = plan.suffix_bits;
+    const int l_eff = plan.cache_bits;
+    const int group = kWave * 8;
+    const int lds_bytes = (l_eff - 4) * group * 8;
+    if (lds_bytes > kMaxLdsBytes)
+        return QUBO_EPLAN;
+
+    // Q to the host; the guard: finite entries and sum |Q_ij| <= 2^100, so that
+    // fp32 energies never overflow.
+    std::vector<double> Qh((size_t)n * n);
+    if (hipMemcpyAsync(Qh.data(), rq.Q, Qh.size() * 8, hipMemcpyDeviceToHost, rq.stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    double S = 0.0;
+    for (double v : Qh) {
+        if (!std::isfinite(v))
+            return QUBO_ERANGE;
+        S += std::fabs(v);
+    }
+    S *= 1.0 + 0x1p-40;  // rounding of the sum itself (at most n^2 ulp)
+    if (!(S <= 0x1p100))
+        return QUBO_ERANGE;
+    // Fold to the upper triangle in binary64 (the walk's tables only; states
+    // are scored against Q itself) and pad small problems.
+    std::vector<double> U((size_t)ns * ns, 0.0);
+    for (int i = 0; i < n; ++i) {
+        U[(size_t)i * ns + i] = Qh[(size_t)i * n + i];
+        for (int j = i + 1; j < n; ++j)
+            U[(size_t)i * ns + j] = Qh[(size_t)i * n + j] + Qh[(size_t)j * n + i];
+    }
+    for (int i = n; i < ns; ++i)
+        U[(size_t)i * ns + i] = 1.0;
+
+    uint64_t lo = 0, hi = 1ull << A;
+    if (rq.ranged) {
+        lo = rq.gray_lo;
+        hi = rq.gray_hi;
+        if (hi > (1ull << A))
+            return QUBO_EINVAL;
+    }
+    const uint64_t seg_first = lo >> plan.seg_bits;
+    const uint64_t seg_last = (hi - 1) >> plan.seg_bits;
+    const uint64_t segs = seg_last - seg_first + 1;
+    const uint64_t seg_blocks = (segs + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint64_t items = plan.col_groups * seg_blocks;
+    int per_cu = 0;
+    if (search_occupancy_f64(&per_cu, lds_bytes) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (per_cu < 1)
+        per_cu = 1;
+    const uint64_t want_blocks = (uint64_t)dev.num_cus * (uint64_t)per_cu;
+    const int blocks = (int)(items < want_blocks ? items : want_blocks);
+
+    // Workspace.
+    const uint64_t cols_padded = (((1ull << B) + group - 1) / group) * group;
+    auto al = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
+    const uint64_t off_u = 0;
+    const uint64_t off_es = al(off_u + (uint64_t)ns * ns * 8);
+    const uint64_t off_mint = al(off_es + cols_padded * 8);
+    const uint64_t off_ep = al(off_mint + (uint64_t)A * cols_padded * 8);
+    const uint64_t off_epmin = al(off_ep + (1ull << A) * 8);
+    const uint64_t off_part = al(off_epmin + ((1ull << (A - kRegBits)) + 2) * 4);
+    const uint64_t off_ctrl = al(off_part + (uint64_t)blocks * kWavesPerBlock * sizeof(PartialF64));
+    const uint64_t total = al(off_ctrl + sizeof(CtrlF64));
+    Call call;
+    call.stream = rq.stream;
+    if (hipMallocAsync(&call.ws, total, rq.stream) != hipSuccess) {
+        call.ws = nullptr;
+        return QUBO_ENOMEM;
+    }
+    char *base = static_cast<char *>(call.ws);
+    double *dU = reinterpret_cast<double *>(base + off_u);
+    double *des = reinterpret_cast<double *>(base + off_es);
+    double *dmint = reinterpret_cast<double *>(base + off_mint);
+    double *dep = reinterpret_cast<double *>(base + off_ep);
+    float *depmin = reinterpret_cast<float *>(base + off_epmin);
+    PartialF64 *dpart = reinterpret_cast<PartialF64 *>(base + off_part);
+    CtrlF64 *dctrl = reinterpret_cast<CtrlF64 *>(base + off_ctrl);
+    for (auto &e : call.ev)
+        if (hipEventCreate(&e) != hipSuccess)
+            return QUBO_EDEVICE;
+    call.events = true;
+
+    // A state passes the filter when its fp32 energy is within delta of the
+    // best binary64 energy so far; delta bounds (several times over) every fp32
+    // rounding of the walk and the gate, about 125 ulp(S) at 2^-24 S each.
+    const double delta = std::ldexp(S, -14);
+    float delta32 = (float)delta;
+    if ((double)delta32 < delta)
+        delta32 = std::nextafter(delta32, INFINITY);
+    // The first threshold: E(0) = 0 when state 0 is searched, else above every energy.
+    const double t0 = (lo == 0) ? 0.0 : 4.0 * S + 1.0;
+
+    if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess ||
+        hipMemcpyAsync(dU, U.data(), U.size() * 8, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, des, dmint, dep, depmin, rq.stream) !=
+        hipSuccess)
+        return QUBO_EDEVICE;
+    if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess ||
+        launch_init_ctrl_f64(dctrl, t0, depmin + (1ull << (A - kRegBits)), rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    SearchArgsF64 sa{};
+    sa.es = des;
+    sa.mint = dmint;
+    sa.ep = dep;
+    sa.epmin = depmin;
+    sa.Q = rq.Q;
+    sa.partials = dpart;
+    sa.ctrl = dctrl;
+    sa.cols_padded = cols_padded;
+    sa.gray_lo = lo;
+    sa.gray_hi = hi;
+    sa.seg_first = seg_first;
+    sa.segs = segs;
+    sa.seg_blocks = seg_blocks;
+    sa.items = items;
+    sa.A = A;
+    sa.B = B;
+    sa.n = n;
+    sa.pad = ns - n;
+    sa.l_eff = l_eff;
+    sa.seg_bits = plan.seg_bits;
+    sa.delta = delta32;
+    if (launch_search_f64(sa, blocks, lds_bytes, rq.stream) != hipSuccess ||
+        hipEventRecord(call.ev[2], rq.stream) != hipSuccess ||
+        launch_reduce_f64(dpart, blocks * kWavesPerBlock, dctrl, rq.stream) != hipSuccess ||
+        hipEventRecord(call.ev[3], rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    CtrlF64 host_ctrl;
+    if (hipMemcpyAsync(&host_ctrl, dctrl, sizeof(CtrlF64), hipMemcpyDeviceToHost, rq.stream) !=
+            hipSuccess ||
+        hipEventRecord(call.ev[4], rq.stream) != hipSuccess ||
+        hipStreamSynchronize(rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+
+    qubo_timing t{};
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, call.ev[0], call.ev[1]) == hipSuccess)
+        t.build_ms = ms;
+    if (hipEventElapsedTime(&ms, call.ev[1], call.ev[2]) == hipSuccess)
+        t.search_ms = ms;
+    if (hipEventElapsedTime(&ms, call.ev[2], call.ev[3]) == hipSuccess)
+        t.reduce_ms = ms;
+    if (hipEventElapsedTime(&ms, call.ev[0], call.ev[4]) == hipSuccess)
+        t.total_ms = ms;
+    t.states = (hi - lo) << B;
+    t.blocks = blocks;
+    t.bodies = host_ctrl.bodies_total;
+    t.checked_bodies = host_ctrl.slow_total;
+    t.slow_bodies = host_ctrl.slow_total;
+    t.candidates = host_ctrl.candidates_total;
+    g_timing = t;
+
+    const PartialF64 &r = host_ctrl.result;
+    if (r.count == 0)
+        return QUBO_EDEVICE;  // every state passes the first threshold: some must be recorded
+    out->min_energy = r.e;
+    out->argmin = r.arg;
+    out->count = r.count;
+    return QUBO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -581,6 +786,32 @@ QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cac
     if (gray_lo == 0 && gray_hi == 0)
         return QUBO_EINVAL;
     return qubo_search_ex(Q, n, prefix_bits, cache_bits, gray_lo, gray_hi, 0u, stream, out);
+}
+
+QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_bits,
+                             uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
+                             qubo_result_f64 *out)
+{
+    if (flags & ~QUBO_FLAG_COLS8)
+        return QUBO_EINVAL;
+    RequestF64 rq;
+    rq.Q = Q;
+    rq.n = n;
+    rq.prefix_bits = prefix_bits;
+    rq.cache_bits = cache_bits;
+    rq.stream = static_cast<hipStream_t>(stream);
+    if (gray_lo != 0 || gray_hi != 0) {
+        if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||
+            prefix_bits > qubo::kMaxPrefixBits)
+            return QUBO_EINVAL;
+        if ((gray_lo & 31u) || (gray_hi & 31u) || gray_lo >= gray_hi ||
+            gray_hi > (1ull << prefix_bits))
+            return QUBO_EINVAL;
+        rq.ranged = true;
+        rq.gray_lo = gray_lo;
+        rq.gray_hi = gray_hi;
+    }
+    return run_f64(rq, out);
 }
 
 QUBO_API int qubo_build_tables(const int32_t *Q, int n, int prefix_bits, int32_t *Es, int32_t *Mint,

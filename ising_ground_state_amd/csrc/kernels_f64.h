@@ -1,0 +1,67 @@
+// Device-side pieces of the search for a real-valued (binary64) Q and their
+// launchers (HIP, gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace qubo {
+
+// One wave's partial result (40 bytes).
+struct PartialF64 {
+    double e;            // min energy seen (+inf when count == 0)
+    uint64_t count;      // states with exactly that energy
+    uint64_t arg;        // smallest index attaining it
+    uint32_t bodies;     // 32-step bodies walked
+    uint32_t slow;       // bodies walked exactly
+    uint64_t candidates; // states re-evaluated from the definition
+};
+
+struct CtrlF64 {
+    unsigned long long counter;  // next work item
+    long long gbest;             // best energy so far, as an order-preserving integer key
+    uint64_t pad[6];
+    PartialF64 result;           // final reduction (offset 64)
+    uint64_t slow_total;
+    uint64_t bodies_total;
+    uint64_t candidates_total;
+};
+
+struct SearchArgsF64 {
+    const double *es;       // [cols_padded]       E_s(c)
+    const double *mint;     // [A][cols_padded]    M_int rows by prefix variable
+    const double *ep;       // [2^A]               E_p(g(j))
+    const float *epmin;     // [2^A / 32 + 2]      min over each body of ep rounded to fp32, + 2 padding
+    const double *Q;        // [n][n]              the caller's matrix (the definition's terms)
+    PartialF64 *partials;   // [gridDim.x * 4]
+    CtrlF64 *ctrl;
+    uint64_t cols_padded;
+    uint64_t gray_lo, gray_hi;
+    uint64_t seg_first, segs, seg_blocks, items;
+    int32_t A, B;
+    int32_t n;              // variables of Q
+    int32_t pad;            // padding variables appended below n (n < 5), the lowest index bits
+    int32_t l_eff;          // Gray bits with rows on chip (registers + LDS)
+    int32_t seg_bits;
+    float delta;            // filter margin: bounds every fp32 rounding of the walk and the gate
+    int32_t reserved;
+};
+
+// E_s, M_int and E_p(g(j)) in binary64 from the folded matrix, and the per-body
+// minima of E_p rounded to fp32.
+hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
+                                   double *es, double *mint, double *ep, float *epmin,
+                                   hipStream_t stream);
+
+hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, hipStream_t stream);
+
+hipError_t launch_search_f64(const SearchArgsF64 &args, int blocks, int lds_bytes,
+                             hipStream_t stream);
+
+hipError_t search_occupancy_f64(int *blocks_per_cu, int lds_bytes);
+
+hipError_t launch_reduce_f64(const PartialF64 *partials, int count, CtrlF64 *ctrl,
+                             hipStream_t stream);
+
+}  // namespace qubo

@@ -1,0 +1,591 @@
+// Exhaustive search of a real-valued (binary64) QUBO matrix on CDNA4 (gfx950).
+//
+// Maltsev, Remnev, Kapranov and Krivtsova, "Terastate-per-second QUBO
+// Brute-Force on a Single GPU: A Matrix Prefix-Suffix Decomposition", name
+// floating-point matrices as future work (sec. VI.B): the long incremental
+// Gray-code updates accumulate rounding, to be handled by mixed precision or a
+// periodic correction.  This kernel does both:
+//   * energies are defined as the binary64 sum of Q_ij over i ascending with
+//     x_i = 1 and, inside, j ascending with x_j = 1 (the definition of sec. I in
+//     one fixed order);
+//   * the walk is the integer kernel's decomposition (eq. 8, eq. 9): per column,
+//     a binary64 anchor E64 follows the walk at body granularity (two row
+//     updates per 32 steps), and inside each 32-step body the states' energies
+//     are one fp32 add each (the same 2-cycle rate as int32), re-anchored from
+//     E64 at every body so rounding never accumulates beyond 32 steps;
+//   * every fp32 rounding of the walk, the tables and the gate is bounded by a
+//     margin delta (2^-14 sum |Q_ij|, several times the worst case); a state is
+//     re-evaluated from the definition, in binary64 and in the same order as
+//     the definition, whenever its fp32 energy is within delta of the best
+//     definition energy so far.  So the minimum, its lowest index and the count
+//     of states with exactly that energy are those of the definition.
+#include "kernels_f64.h"
+
+#include <cfloat>
+#include <climits>
+#include <cmath>
+
+namespace qubo {
+namespace {
+
+constexpr int kU = 5;  // Gray bits with rows in VGPRs (fp32)
+constexpr int kBody = 1 << kU;
+constexpr int kWaves = 4;
+constexpr int kR = 8;  // columns per lane
+
+__device__ __forceinline__ uint64_t gray(uint64_t i) { return i ^ (i >> 1); }
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ double uniform_f64(double v)
+{
+    return __longlong_as_double((long long)uniform64((uint64_t)__double_as_longlong(v)));
+}
+
+// Order-preserving integer key of a binary64 value (for an atomic minimum).
+__device__ __forceinline__ long long order_key(double d)
+{
+    const long long b = __double_as_longlong(d);
+    return b < 0 ? (b ^ 0x7fffffffffffffffLL) : b;
+}
+
+__device__ __forceinline__ double from_key(long long k)
+{
+    return __longlong_as_double(k < 0 ? (k ^ 0x7fffffffffffffffLL) : k);
+}
+
+__device__ __forceinline__ float fmin3(float a, float b, float c) { return fminf(fminf(a, b), c); }
+
+__device__ __forceinline__ float row_min8(const float (&E)[kR])
+{
+    return fminf(fminf(fmin3(E[0], E[1], E[2]), fmin3(E[3], E[4], E[5])), fminf(E[6], E[7]));
+}
+
+// The definition for one state: binary64, i ascending, j ascending, over the
+// set variables of the n-variable index idx (variable 0 most significant).
+__device__ double energy_def(const double *__restrict__ Q, int n, uint64_t idx)
+{
+    double e = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (!((idx >> (n - 1 - i)) & 1u))
+            continue;
+        const double *row = Q + (size_t)i * n;
+        for (int j = 0; j < n; ++j)
+            if ((idx >> (n - 1 - j)) & 1u)
+                e += row[j];
+    }
+    return e;
+}
+
+__device__ __forceinline__ double wave_min_f64(double v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double o = __shfl_xor(v, off, 64);
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ void combine(double &e, uint64_t &cnt, uint64_t &arg, double e2,
+                                        uint64_t c2, uint64_t a2)
+{
+    if (c2 == 0)
+        return;
+    if (cnt == 0 || e2 < e) {
+        e = e2;
+        cnt = c2;
+        arg = a2;
+    } else if (e2 == e) {
+        cnt += c2;
+        arg = a2 < arg ? a2 : arg;
+    }
+}
+
+__device__ __forceinline__ void wave_combine(double &e, uint64_t &cnt, uint64_t &arg)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double e2 = __shfl_xor(e, off, 64);
+        const uint64_t c2 = __shfl_xor(cnt, off, 64);
+        const uint64_t a2 = __shfl_xor(arg, off, 64);
+        combine(e, cnt, arg, e2, c2, a2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Cache builders (binary64), as in the integer build.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void build_suffix_f64_kernel(const double *__restrict__ U, int ns,
+                                                               int A, int B, uint64_t cols_padded,
+                                                               double *__restrict__ es,
+                                                               double *__restrict__ mint)
+{
+    const uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= cols_padded)
+        return;
+    if (c >= (1ull << B)) {
+        // padding column: +inf never passes a finite threshold, and zero rows keep it there
+        es[c] = __longlong_as_double(0x7ff0000000000000LL);
+        for (int v = 0; v < A; ++v)
+            mint[(uint64_t)v * cols_padded + c] = 0.0;
+        return;
+    }
+    double e = 0.0;
+    for (int i = 0; i < B; ++i) {
+        if (!((c >> (B - 1 - i)) & 1u))
+            continue;
+        for (int j = i; j < B; ++j)
+            if ((c >> (B - 1 - j)) & 1u)
+                e += U[(A + i) * ns + (A + j)];
+    }
+    es[c] = e;
+    for (int v = 0; v < A; ++v) {
+        double m = 0.0;
+        for (int j = 0; j < B; ++j)
+            if ((c >> (B - 1 - j)) & 1u)
+                m += U[v * ns + (A + j)];
+        mint[(uint64_t)v * cols_padded + c] = m;
+    }
+}
+
+// ep[j] = E_p(g(j)) over the A prefix variables, summed directly (O(A^2) per
+// prefix; the table is built once), and epmin[k] = min over body k of ep
+// rounded to fp32.  Block-stride loop over 256-prefix blocks.
+__global__ __launch_bounds__(256) void build_prefix_f64_kernel(const double *__restrict__ U, int ns,
+                                                               int A, uint64_t total,
+                                                               double *__restrict__ ep,
+                                                               float *__restrict__ epmin)
+{
+    for (uint64_t j0 = (uint64_t)blockIdx.x * blockDim.x; j0 < total;
+         j0 += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t j = j0 + threadIdx.x;
+        float m = __int_as_float(0x7f800000);
+        if (j < total) {
+            const uint64_t p = gray(j);
+            double e = 0.0;
+            for (int i = 0; i < A; ++i) {
+                if (!((p >> (A - 1 - i)) & 1u))
+                    continue;
+                for (int k = i; k < A; ++k)
+                    if ((p >> (A - 1 - k)) & 1u)
+                        e += U[i * ns + k];
+            }
+            ep[j] = e;
+            m = (float)e;
+        }
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1)
+            m = fminf(m, __shfl_xor(m, off, 64));
+        if (j < total && (j & 31) == 0)
+            epmin[j >> 5] = m;
+    }
+}
+
+__global__ void init_ctrl_f64_kernel(CtrlF64 *ctrl, double t0, float *epmin_pad)
+{
+    epmin_pad[0] = __int_as_float(0x7f800000);
+    epmin_pad[1] = __int_as_float(0x7f800000);
+    ctrl->counter = 0;
+    ctrl->gbest = order_key(t0);
+    ctrl->slow_total = 0;
+    ctrl->bodies_total = 0;
+    ctrl->candidates_total = 0;
+}
+
+// ---------------------------------------------------------------------------
+// The search.
+// ---------------------------------------------------------------------------
+
+// Per-lane record between exact walks, kept in LDS.
+struct RecordF64 {
+    double e;
+    uint64_t cnt;
+    uint64_t arg;
+};
+
+__device__ __forceinline__ void materialise(float (&E)[kR])
+{
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+        asm volatile("" : "+v"(E[r]));
+}
+
+template <bool Plus>
+__device__ __forceinline__ void step_rows(float (&E)[kR], const float (&M)[kR])
+{
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+        E[r] = Plus ? E[r] + M[r] : E[r] - M[r];
+}
+
+// One unrolled body of 32 states: 31 fp32 row updates, every state's energy
+// kept in registers (one add per state).
+__device__ __forceinline__ void adds_body(float (&E)[kR], const float (&Mr)[kU][kR], bool top_plus)
+{
+#pragma unroll
+    for (int m = 0; m + 1 < kBody; ++m) {
+        const int t = __builtin_ctz((unsigned)(m + 1));
+        if (t < kU - 1) {
+            if ((((m + 1) >> (t + 1)) & 1) == 0)
+                step_rows<true>(E, Mr[t]);
+            else
+                step_rows<false>(E, Mr[t]);
+        } else {
+            if (top_plus)
+                step_rows<true>(E, Mr[kU - 1]);
+            else
+                step_rows<false>(E, Mr[kU - 1]);
+        }
+        materialise(E);
+    }
+}
+
+__global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF64 a)
+{
+    constexpr int kGroup = 64 * kR;
+    extern __shared__ double lds_rows64[];  // [l_eff - 4][kGroup]: rows of Gray bits 4 .. l_eff-1
+    __shared__ unsigned long long item_sh;
+    __shared__ double rec_e[64 * kWaves];
+    __shared__ uint64_t rec_c[64 * kWaves], rec_a[64 * kWaves];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int A = a.A, B = a.B;
+    const uint64_t cp = a.cols_padded;
+    const double *__restrict__ mint = a.mint;
+    const double *lds_lane = lds_rows64 - 4 * kGroup + lane;  // row of bit t: lds_lane + t * kGroup
+
+    rec_e[threadIdx.x] = __longlong_as_double(0x7ff0000000000000LL);
+    rec_c[threadIdx.x] = 0;
+    rec_a[threadIdx.x] = ~0ull;
+
+    uint32_t bodies = 0, slow = 0;
+    uint64_t candidates = 0;
+    double T = uniform_f64(from_key(
+        __hip_atomic_load(&a.ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+    long long cur_g = -1;
+
+    for (;;) {
+        if (threadIdx.x == 0)
+            item_sh = atomicAdd(&a.ctrl->counter, 1ull);
+        __syncthreads();
+        const uint64_t item = uniform64(item_sh);
+        __syncthreads();
+        if (item >= a.items)
+            break;
+        const uint64_t g = item / a.seg_blocks;
+        const uint64_t sb = item - g * a.seg_blocks;
+        if ((long long)g != cur_g) {
+            const int rows = a.l_eff - 4;
+            for (int k = threadIdx.x; k < rows * kGroup; k += blockDim.x) {
+                const int t = 4 + k / kGroup;
+                const int col = k % kGroup;
+                lds_rows64[k] = mint[(uint64_t)(A - 1 - t) * cp + g * kGroup + col];
+            }
+            __syncthreads();
+            cur_g = (long long)g;
+        }
+        const uint64_t seg = a.seg_first + sb * kWaves + (uint64_t)wave;
+        if (seg >= a.seg_first + a.segs)
+            continue;
+        uint64_t j_begin = seg << a.seg_bits;
+        uint64_t j_end = (seg + 1) << a.seg_bits;
+        j_begin = j_begin > a.gray_lo ? j_begin : a.gray_lo;
+        j_end = j_end < a.gray_hi ? j_end : a.gray_hi;
+        if (j_begin >= j_end)
+            continue;
+
+        const uint64_t col0 = g * kGroup + (uint64_t)lane;
+        // binary64 anchors at the segment's first prefix (eq. 8)
+        double E64[kR];
+        {
+            const double *src = a.es + col0;
+#pragma unroll
+            for (int r = 0; r < kR; ++r)
+                E64[r] = src[r * 64];
+            uint64_t bits = gray(j_begin);
+            while (bits) {
+                const int t = __builtin_ctzll(bits);
+                bits &= bits - 1;
+                const double *row = mint + (uint64_t)(A - 1 - t) * cp + col0;
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    E64[r] += row[r * 64];
+            }
+        }
+        float Mr[kU][kR];
+#pragma unroll
+        for (int t = 0; t < kU; ++t) {
+            const double *row = mint + (uint64_t)(A - 1 - t) * cp + col0;
+#pragma unroll
+            for (int r = 0; r < kR; ++r)
+                Mr[t][r] = (float)row[r * 64];
+        }
+        // Lane bounds of the fall within a body (s = bit 4 at its start) and a
+        // pair of bodies (bit 5 at its start), in fp32 (their rounding is in delta).
+        float beta_s0 = INFINITY, beta_s1 = INFINITY, beta_p0 = INFINITY, beta_p1 = INFINITY;
+        {
+            const double *row5 = mint + (uint64_t)(A > kU ? A - 1 - kU : 0) * cp + col0;
+#pragma unroll
+            for (int r = 0; r < kR; ++r) {
+                float b = 0.f;
+#pragma unroll
+                for (int t = 0; t < kU; ++t)
+                    b += fminf(Mr[t][r], 0.f);
+                beta_s0 = fminf(beta_s0, b);
+                beta_s1 = fminf(beta_s1, b - Mr[kU - 1][r]);
+                const float m5 = A > kU ? (float)row5[r * 64] : 0.f;
+                beta_p0 = fminf(beta_p0, b + fminf(m5, 0.f));
+                beta_p1 = fminf(beta_p1, b - fmaxf(m5, 0.f));
+            }
+        }
+        {
+            const double gb = uniform_f64(from_key(__hip_atomic_load(
+                &a.ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+            T = gb < T ? gb : T;
+        }
+        float TD = (float)T + a.delta;  // filter threshold: E32 + E_p32 <= TD
+
+        const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
+        float epm_cur = a.epmin[j_begin >> kU];
+        float epm_next = a.epmin[(j_begin >> kU) + 1];
+        bool pair_clear = false;
+        for (uint32_t bi = 0; bi < nbodies; ++bi) {
+            const uint64_t base = j_begin + ((uint64_t)bi << kU);
+            const bool last = bi + 1 == nbodies;
+            const bool top_plus = ((base >> kU) & 1u) == 0;
+            const float epm_after = a.epmin[(base >> kU) + 2];
+            float E[kR];
+#pragma unroll
+            for (int r = 0; r < kR; ++r)
+                E[r] = (float)E64[r];  // re-anchor (round to nearest)
+            bool check;
+            if (pair_clear) {
+                check = false;
+                pair_clear = false;
+            } else {
+                const float emin = row_min8(E);
+                if (top_plus && !last && A > kU) {
+                    const float bp = emin + (((base >> (kU + 1)) & 1u) ? beta_p1 : beta_p0);
+                    pair_clear =
+                        __builtin_amdgcn_ballot_w64(bp + fminf(epm_cur, epm_next) <= TD) == 0;
+                }
+                if (pair_clear) {
+                    check = false;
+                } else {
+                    const float bound = emin + (top_plus ? beta_s0 : beta_s1);
+                    check = __builtin_amdgcn_ballot_w64(bound + epm_cur <= TD) != 0;
+                }
+            }
+            ++bodies;
+            if (!check) {
+                adds_body(E, Mr, top_plus);
+            } else {
+                // Exact walk: every state within delta of T is re-evaluated.
+                ++slow;
+                RecordF64 rec{rec_e[threadIdx.x], rec_c[threadIdx.x], rec_a[threadIdx.x]};
+                const uint32_t neg_top = top_plus ? 0u : 0x80000000u;
+                const uint64_t colbase = g * kGroup;
+#pragma unroll 1
+                for (int m = 0; m < kBody; ++m) {
+                    const uint64_t j = base + (uint64_t)m;
+                    const float ep32 = (float)a.ep[j];
+                    const uint64_t hi = (gray(j) << B) | colbase;
+#pragma unroll
+                    for (int r = 0; r < kR; ++r) {
+                        if (E[r] + ep32 <= TD) {
+                            const uint64_t idx = hi | ((uint64_t)r << 6) | (uint64_t)lane;
+                            if ((idx & ((1ull << a.pad) - 1)) == 0) {
+                                ++candidates;
+                                const double v = energy_def(a.Q, a.n, idx >> a.pad);
+                                const uint64_t real = idx >> a.pad;
+                                if (v < rec.e) {
+                                    rec.e = v;
+                                    rec.cnt = 1;
+                                    rec.arg = real;
+                                } else if (v == rec.e) {
+                                    rec.cnt += 1;
+                                    rec.arg = real < rec.arg ? real : rec.arg;
+                                }
+                            }
+                        }
+                    }
+                    // flip into the next state (after the last one t = 5: no row)
+                    const int t = __builtin_ctz((unsigned)(m + 1));
+                    const uint32_t sign = (t < kU - 1) ? ((((m + 1) >> (t + 1)) & 1) ? 0x80000000u : 0u)
+                                                       : neg_top;
+#pragma unroll
+                    for (int r = 0; r < kR; ++r) {
+                        float d = 0.f;
+#pragma unroll
+                        for (int tt = 0; tt < kU; ++tt)
+                            d = (tt == t) ? Mr[tt][r] : d;
+                        E[r] += __uint_as_float(__float_as_uint(d) ^ sign);
+                    }
+                }
+                rec_e[threadIdx.x] = rec.e;
+                rec_c[threadIdx.x] = rec.cnt;
+                rec_a[threadIdx.x] = rec.arg;
+                const double wm = uniform_f64(wave_min_f64(rec.e));
+                T = wm < T ? wm : T;
+                atomicMin(&a.ctrl->gbest, order_key(T));
+                const double gb = uniform_f64(from_key(__hip_atomic_load(
+                    &a.ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+                T = gb < T ? gb : T;
+                TD = (float)T + a.delta;
+            }
+            // binary64 anchor to the next body: bit 4 flips inside this body,
+            // then the outer flip of Gray bit t >= 5
+            {
+                const double *m4 = lds_lane + 4 * kGroup;
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    E64[r] = top_plus ? E64[r] + m4[r * 64] : E64[r] - m4[r * 64];
+            }
+            if (!last) {
+                const uint64_t next = base + kBody;
+                const int t = __builtin_ctzll(next);
+                const bool plus = ((next >> (t + 1)) & 1u) == 0;
+                double row[kR];
+                if (t < a.l_eff) {
+                    const double *src = lds_lane + t * kGroup;
+#pragma unroll
+                    for (int r = 0; r < kR; ++r)
+                        row[r] = src[r * 64];
+                } else {
+                    const double *src = mint + (uint64_t)(A - 1 - t) * cp + col0;
+#pragma unroll
+                    for (int r = 0; r < kR; ++r)
+                        row[r] = src[r * 64];
+                }
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    E64[r] = plus ? E64[r] + row[r] : E64[r] - row[r];
+            }
+            epm_cur = epm_next;
+            epm_next = epm_after;
+        }
+    }
+
+    double e = rec_e[threadIdx.x];
+    uint64_t cnt = rec_c[threadIdx.x], arg = rec_a[threadIdx.x];
+    wave_combine(e, cnt, arg);
+    uint64_t cand = candidates;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        cand += __shfl_xor(cand, off, 64);
+    if (lane == 0) {
+        PartialF64 p;
+        p.e = e;
+        p.count = cnt;
+        p.arg = arg;
+        p.bodies = bodies;
+        p.slow = slow;
+        p.candidates = cand;
+        a.partials[(uint64_t)blockIdx.x * kWaves + wave] = p;
+    }
+}
+
+__global__ __launch_bounds__(256) void reduce_f64_kernel(const PartialF64 *__restrict__ partials,
+                                                         int count, CtrlF64 *ctrl)
+{
+    __shared__ double se[4];
+    __shared__ uint64_t sc[4], sa[4], ss[4], sb[4], sk[4];
+    double e = __longlong_as_double(0x7ff0000000000000LL);
+    uint64_t cnt = 0, arg = ~0ull, slow = 0, bodies = 0, cand = 0;
+    for (int k = threadIdx.x; k < count; k += blockDim.x) {
+        const PartialF64 p = partials[k];
+        combine(e, cnt, arg, p.e, p.count, p.arg);
+        slow += p.slow;
+        bodies += p.bodies;
+        cand += p.candidates;
+    }
+    wave_combine(e, cnt, arg);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        slow += __shfl_xor(slow, off, 64);
+        bodies += __shfl_xor(bodies, off, 64);
+        cand += __shfl_xor(cand, off, 64);
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        se[w] = e;
+        sc[w] = cnt;
+        sa[w] = arg;
+        ss[w] = slow;
+        sb[w] = bodies;
+        sk[w] = cand;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < (int)(blockDim.x >> 6); ++k) {
+            combine(e, cnt, arg, se[k], sc[k], sa[k]);
+            slow += ss[k];
+            bodies += sb[k];
+            cand += sk[k];
+        }
+        ctrl->result.e = e;
+        ctrl->result.count = cnt;
+        ctrl->result.arg = arg;
+        ctrl->slow_total = slow;
+        ctrl->bodies_total = bodies;
+        ctrl->candidates_total = cand;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
+                                   double *es, double *mint, double *ep, float *epmin,
+                                   hipStream_t stream)
+{
+    const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
+    hipLaunchKernelGGL(build_suffix_f64_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
+                       cols_padded, es, mint);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const uint64_t total = 1ull << A;
+    const uint64_t blocks = (total + 255) / 256;
+    const uint64_t grid = blocks < (1ull << 20) ? blocks : (1ull << 20);
+    hipLaunchKernelGGL(build_prefix_f64_kernel, dim3((unsigned)grid), dim3(256), 0, stream, U, ns,
+                       A, total, ep, epmin);
+    return hipGetLastError();
+}
+
+hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, hipStream_t stream)
+{
+    hipLaunchKernelGGL(init_ctrl_f64_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0, epmin_pad);
+    return hipGetLastError();
+}
+
+hipError_t launch_search_f64(const SearchArgsF64 &args, int blocks, int lds_bytes,
+                             hipStream_t stream)
+{
+    hipLaunchKernelGGL(gray_search_f64_kernel, dim3(blocks), dim3(64 * kWaves), lds_bytes, stream,
+                       args);
+    return hipGetLastError();
+}
+
+hipError_t search_occupancy_f64(int *blocks_per_cu, int lds_bytes)
+{
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks_per_cu, reinterpret_cast<const void *>(gray_search_f64_kernel), 64 * kWaves,
+        (size_t)lds_bytes);
+}
+
+hipError_t launch_reduce_f64(const PartialF64 *partials, int count, CtrlF64 *ctrl,
+                             hipStream_t stream)
+{
+    hipLaunchKernelGGL(reduce_f64_kernel, dim3(1), dim3(256), 0, stream, partials, count, ctrl);
+    return hipGetLastError();
+}
+
+}  // namespace qubo

@@ -124,6 +124,13 @@ def test_null_and_range_arguments_rejected_before_the_device():
         assert lib.qubo_search_lowest(P, 12, k, 8, -1, lo, hi, flags, None, o, fp) == q.QUBO_EINVAL, (k, flags)
     assert lib.qubo_search_lowest(None, 12, 4, -1, -1, 0, 0, 0, None, out, ctypes.byref(found)) == q.QUBO_EINVAL
     assert found.value == -3  # untouched
+    # real-valued search: n in 1..58 (no outer split), only the 8-column flag, valid slices
+    rf = q._ResultF64()
+    for n_, flags, lo, hi in [(0, 0, 0, 0), (59, 0, 0, 0), (12, q.FLAG_STRICT_MIN, 0, 0),
+                              (12, q.FLAG_COLS16, 0, 0), (12, 0, 0, 33)]:
+        assert lib.qubo_search_f64(P, n_, 8, -1, lo, hi, flags, None, ctypes.byref(rf)) == q.QUBO_EINVAL, n_
+    assert lib.qubo_search_f64(None, 12, -1, -1, 0, 0, 0, None, ctypes.byref(rf)) == q.QUBO_EINVAL
+    assert lib.qubo_search_f64(P, 12, -1, -1, 0, 0, 0, None, None) == q.QUBO_EINVAL
 
 
 def test_timing_struct_before_any_search():
