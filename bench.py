@@ -118,6 +118,8 @@ def main():
                     help="time the strict kernel (minimum after every prefix) instead of the default")
     ap.add_argument("--no-strict-leg", action="store_true",
                     help="skip the extra strict-kernel step reported beside the default mode")
+    ap.add_argument("--no-f64-leg", action="store_true",
+                    help="skip the extra step of the real-valued (binary64) search of C4f")
     ap.add_argument("--no-spectrum-leg", action="store_true",
                     help="skip the extra step of the 64-lowest-states search reported beside the minimum")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -233,6 +235,23 @@ def main():
                                 "first": list(low[0]), "last": list(low[-1]),
                                 "head_is_min": tuple(low[0]) == (result.min_energy, result.argmin)}
         print("[bench] spectrum", tl, file=sys.stderr, flush=True)
+    if not args.no_f64_leg:
+        cf = qi.make_config("C4f")
+        Qf = torch.tensor(cf["Q"], dtype=torch.float64, device="cuda:0")
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        rf = q.search_f64(Qf)
+        torch.cuda.synchronize()
+        tf = q.last_timing()
+        line["f64_C4f"] = {"value": states / (time.perf_counter() - t1) / 1e12, "unit": "1e12 states/s",
+                           "workload": cf["desc"] + ", seed %d" % cf["seed"],
+                           "kernel": "gray_search_f64_kernel (fp32 walk, binary64 anchors and re-evaluation)",
+                           "kernel_ms": tf["search_ms"],
+                           "frac_fp32_add_peak": states / (tf["search_ms"] / 1e3) / INT32_VALU_PEAK,
+                           "slow_bodies": tf["slow_bodies"], "candidates": tf["candidates"],
+                           "coverage_ok": tf["bodies"] * 32 == (1 << plan["prefix_bits"]) * plan["col_groups"],
+                           "result": [float.hex(rf.min_energy), rf.argmin, rf.count]}
+        print("[bench] f64", tf, file=sys.stderr, flush=True)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)

@@ -584,7 +584,8 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
     const uint64_t off_u = 0;
     const uint64_t off_es = al(off_u + (uint64_t)ns * ns * 8);
     const uint64_t off_mint = al(off_es + cols_padded * 8);
-    const uint64_t off_ep = al(off_mint + (uint64_t)A * cols_padded * 8);
+    const uint64_t off_mint32 = al(off_mint + (uint64_t)A * cols_padded * 8);
+    const uint64_t off_ep = al(off_mint32 + (uint64_t)A * cols_padded * 4);
     const uint64_t off_epmin = al(off_ep + (1ull << A) * 8);
     const uint64_t off_part = al(off_epmin + ((1ull << (A - kRegBits)) + 2) * 4);
     const uint64_t off_ctrl = al(off_part + (uint64_t)blocks * kWavesPerBlock * sizeof(PartialF64));
@@ -599,6 +600,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
     double *dU = reinterpret_cast<double *>(base + off_u);
     double *des = reinterpret_cast<double *>(base + off_es);
     double *dmint = reinterpret_cast<double *>(base + off_mint);
+    float *dmint32 = reinterpret_cast<float *>(base + off_mint32);
     double *dep = reinterpret_cast<double *>(base + off_ep);
     float *depmin = reinterpret_cast<float *>(base + off_epmin);
     PartialF64 *dpart = reinterpret_cast<PartialF64 *>(base + off_part);
@@ -621,7 +623,8 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
     if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess ||
         hipMemcpyAsync(dU, U.data(), U.size() * 8, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
-    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, des, dmint, dep, depmin, rq.stream) !=
+    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, des, dmint, dmint32, dep, depmin,
+                                rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess ||
@@ -630,6 +633,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
     SearchArgsF64 sa{};
     sa.es = des;
     sa.mint = dmint;
+    sa.mint32 = dmint32;
     sa.ep = dep;
     sa.epmin = depmin;
     sa.Q = rq.Q;

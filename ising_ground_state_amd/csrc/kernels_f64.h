@@ -20,7 +20,7 @@ struct PartialF64 {
 
 struct CtrlF64 {
     unsigned long long counter;  // next work item
-    long long gbest;             // best energy so far, as an order-preserving integer key
+    long long gbest;             // upper bound of the minimum, as an order-preserving integer key
     uint64_t pad[6];
     PartialF64 result;           // final reduction (offset 64)
     uint64_t slow_total;
@@ -31,6 +31,7 @@ struct CtrlF64 {
 struct SearchArgsF64 {
     const double *es;       // [cols_padded]       E_s(c)
     const double *mint;     // [A][cols_padded]    M_int rows by prefix variable
+    const float *mint32;    // [A][cols_padded]    the same rows rounded to fp32 (the walk's rows)
     const double *ep;       // [2^A]               E_p(g(j))
     const float *epmin;     // [2^A / 32 + 2]      min over each body of ep rounded to fp32, + 2 padding
     const double *Q;        // [n][n]              the caller's matrix (the definition's terms)
@@ -48,11 +49,11 @@ struct SearchArgsF64 {
     int32_t reserved;
 };
 
-// E_s, M_int and E_p(g(j)) in binary64 from the folded matrix, and the per-body
-// minima of E_p rounded to fp32.
+// E_s, M_int and E_p(g(j)) in binary64 from the folded matrix, M_int rounded to
+// fp32, and the per-body minima of E_p rounded to fp32.
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
-                                   double *es, double *mint, double *ep, float *epmin,
-                                   hipStream_t stream);
+                                   double *es, double *mint, float *mint32, double *ep,
+                                   float *epmin, hipStream_t stream);
 
 hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, hipStream_t stream);
 

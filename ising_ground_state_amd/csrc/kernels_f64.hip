@@ -16,9 +16,12 @@
 //   * every fp32 rounding of the walk, the tables and the gate is bounded by a
 //     margin delta (2^-14 sum |Q_ij|, several times the worst case); a state is
 //     re-evaluated from the definition, in binary64 and in the same order as
-//     the definition, whenever its fp32 energy is within delta of the best
-//     definition energy so far.  So the minimum, its lowest index and the count
-//     of states with exactly that energy are those of the definition.
+//     the definition, whenever its fp32 energy is within delta of the threshold T;
+//   * T only has to bound the minimum from above: it is lowered to the best
+//     exact energy recorded and, before a body is walked exactly, to the body's
+//     smallest fp32 energy plus delta (which bounds that state's exact energy).
+//     Every minimiser passes every filter, so the minimum, its lowest index and
+//     the count of states with exactly that energy are those of the definition.
 #include "kernels_f64.h"
 
 #include <cfloat>
@@ -125,7 +128,8 @@ __device__ __forceinline__ void wave_combine(double &e, uint64_t &cnt, uint64_t 
 __global__ __launch_bounds__(256) void build_suffix_f64_kernel(const double *__restrict__ U, int ns,
                                                                int A, int B, uint64_t cols_padded,
                                                                double *__restrict__ es,
-                                                               double *__restrict__ mint)
+                                                               double *__restrict__ mint,
+                                                               float *__restrict__ mint32)
 {
     const uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= cols_padded)
@@ -133,8 +137,10 @@ __global__ __launch_bounds__(256) void build_suffix_f64_kernel(const double *__r
     if (c >= (1ull << B)) {
         // padding column: +inf never passes a finite threshold, and zero rows keep it there
         es[c] = __longlong_as_double(0x7ff0000000000000LL);
-        for (int v = 0; v < A; ++v)
+        for (int v = 0; v < A; ++v) {
             mint[(uint64_t)v * cols_padded + c] = 0.0;
+            mint32[(uint64_t)v * cols_padded + c] = 0.f;
+        }
         return;
     }
     double e = 0.0;
@@ -152,6 +158,7 @@ __global__ __launch_bounds__(256) void build_suffix_f64_kernel(const double *__r
             if ((c >> (B - 1 - j)) & 1u)
                 m += U[v * ns + (A + j)];
         mint[(uint64_t)v * cols_padded + c] = m;
+        mint32[(uint64_t)v * cols_padded + c] = (float)m;  // the walk's fp32 rows
     }
 }
 
@@ -247,7 +254,16 @@ __device__ __forceinline__ void adds_body(float (&E)[kR], const float (&Mr)[kU][
     }
 }
 
-__global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF64 a)
+// Four waves per SIMD: the register budget (128 VGPRs) the compiler must meet.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gray_search_f64_kernel(const double *__restrict__ es,
+                                                              const double *__restrict__ mint,
+                                                              const float *__restrict__ mint32,
+                                                              const double *__restrict__ ep,
+                                                              const float *__restrict__ epmin,
+                                                              const double *__restrict__ Q,
+                                                              PartialF64 *__restrict__ partials,
+                                                              CtrlF64 *__restrict__ ctrl,
+                                                              const SearchArgsF64 a)
 {
     constexpr int kGroup = 64 * kR;
     extern __shared__ double lds_rows64[];  // [l_eff - 4][kGroup]: rows of Gray bits 4 .. l_eff-1
@@ -259,22 +275,20 @@ __global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF6
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int A = a.A, B = a.B;
     const uint64_t cp = a.cols_padded;
-    const double *__restrict__ mint = a.mint;
     const double *lds_lane = lds_rows64 - 4 * kGroup + lane;  // row of bit t: lds_lane + t * kGroup
 
     rec_e[threadIdx.x] = __longlong_as_double(0x7ff0000000000000LL);
     rec_c[threadIdx.x] = 0;
     rec_a[threadIdx.x] = ~0ull;
 
-    uint32_t bodies = 0, slow = 0;
-    uint64_t candidates = 0;
+    uint32_t bodies = 0, slow = 0, candidates = 0;
     double T = uniform_f64(from_key(
-        __hip_atomic_load(&a.ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+        __hip_atomic_load(&ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
     long long cur_g = -1;
 
     for (;;) {
         if (threadIdx.x == 0)
-            item_sh = atomicAdd(&a.ctrl->counter, 1ull);
+            item_sh = atomicAdd(&ctrl->counter, 1ull);
         __syncthreads();
         const uint64_t item = uniform64(item_sh);
         __syncthreads();
@@ -306,7 +320,7 @@ __global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF6
         // binary64 anchors at the segment's first prefix (eq. 8)
         double E64[kR];
         {
-            const double *src = a.es + col0;
+            const double *src = es + col0;
 #pragma unroll
             for (int r = 0; r < kR; ++r)
                 E64[r] = src[r * 64];
@@ -323,16 +337,16 @@ __global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF6
         float Mr[kU][kR];
 #pragma unroll
         for (int t = 0; t < kU; ++t) {
-            const double *row = mint + (uint64_t)(A - 1 - t) * cp + col0;
+            const float *row = mint32 + (uint64_t)(A - 1 - t) * cp + col0;
 #pragma unroll
             for (int r = 0; r < kR; ++r)
-                Mr[t][r] = (float)row[r * 64];
+                Mr[t][r] = row[r * 64];
         }
         // Lane bounds of the fall within a body (s = bit 4 at its start) and a
         // pair of bodies (bit 5 at its start), in fp32 (their rounding is in delta).
         float beta_s0 = INFINITY, beta_s1 = INFINITY, beta_p0 = INFINITY, beta_p1 = INFINITY;
         {
-            const double *row5 = mint + (uint64_t)(A > kU ? A - 1 - kU : 0) * cp + col0;
+            const float *row5 = mint32 + (uint64_t)(A > kU ? A - 1 - kU : 0) * cp + col0;
 #pragma unroll
             for (int r = 0; r < kR; ++r) {
                 float b = 0.f;
@@ -341,27 +355,27 @@ __global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF6
                     b += fminf(Mr[t][r], 0.f);
                 beta_s0 = fminf(beta_s0, b);
                 beta_s1 = fminf(beta_s1, b - Mr[kU - 1][r]);
-                const float m5 = A > kU ? (float)row5[r * 64] : 0.f;
+                const float m5 = A > kU ? row5[r * 64] : 0.f;
                 beta_p0 = fminf(beta_p0, b + fminf(m5, 0.f));
                 beta_p1 = fminf(beta_p1, b - fmaxf(m5, 0.f));
             }
         }
         {
             const double gb = uniform_f64(from_key(__hip_atomic_load(
-                &a.ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+                &ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
             T = gb < T ? gb : T;
         }
         float TD = (float)T + a.delta;  // filter threshold: E32 + E_p32 <= TD
 
         const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
-        float epm_cur = a.epmin[j_begin >> kU];
-        float epm_next = a.epmin[(j_begin >> kU) + 1];
+        float epm_cur = epmin[j_begin >> kU];
+        float epm_next = epmin[(j_begin >> kU) + 1];
         bool pair_clear = false;
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
             const uint64_t base = j_begin + ((uint64_t)bi << kU);
             const bool last = bi + 1 == nbodies;
             const bool top_plus = ((base >> kU) & 1u) == 0;
-            const float epm_after = a.epmin[(base >> kU) + 2];
+            const float epm_after = epmin[(base >> kU) + 2];
             float E[kR];
 #pragma unroll
             for (int r = 0; r < kR; ++r)
@@ -390,13 +404,48 @@ __global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF6
             } else {
                 // Exact walk: every state within delta of T is re-evaluated.
                 ++slow;
-                RecordF64 rec{rec_e[threadIdx.x], rec_c[threadIdx.x], rec_a[threadIdx.x]};
                 const uint32_t neg_top = top_plus ? 0u : 0x80000000u;
                 const uint64_t colbase = g * kGroup;
+                // First pass: the body's smallest fp32 energy plus delta bounds
+                // the best exact energy in the body from above, so T (which only
+                // has to bound the minimum from above) falls to it before any
+                // state is re-evaluated.
+                {
+                    float est = INFINITY;
+#pragma unroll 1
+                    for (int m = 0; m < kBody; ++m) {
+                        const float ep32 = (float)ep[base + (uint64_t)m];
+#pragma unroll
+                        for (int r = 0; r < kR; ++r)
+                            est = fminf(est, E[r] + ep32);
+                        const int t = __builtin_ctz((unsigned)(m + 1));
+                        const uint32_t sign = (t < kU - 1) ? ((((m + 1) >> (t + 1)) & 1) ? 0x80000000u : 0u)
+                                                           : neg_top;
+#pragma unroll
+                        for (int r = 0; r < kR; ++r) {
+                            float d = 0.f;
+#pragma unroll
+                            for (int tt = 0; tt < kU; ++tt)
+                                d = (tt == t) ? Mr[tt][r] : d;
+                            E[r] += __uint_as_float(__float_as_uint(d) ^ sign);
+                        }
+                    }
+#pragma unroll
+                    for (int off = 32; off >= 1; off >>= 1)
+                        est = fminf(est, __shfl_xor(est, off, 64));
+                    const double up = (double)__uint_as_float(
+                        __builtin_amdgcn_readfirstlane(__float_as_uint(est + a.delta)));
+                    T = up < T ? up : T;
+                    TD = (float)T + a.delta;
+#pragma unroll
+                    for (int r = 0; r < kR; ++r)
+                        E[r] = (float)E64[r];  // back to the body's first state
+                }
+                RecordF64 rec{rec_e[threadIdx.x], rec_c[threadIdx.x], rec_a[threadIdx.x]};
 #pragma unroll 1
                 for (int m = 0; m < kBody; ++m) {
                     const uint64_t j = base + (uint64_t)m;
-                    const float ep32 = (float)a.ep[j];
+                    const float ep32 = (float)ep[j];
                     const uint64_t hi = (gray(j) << B) | colbase;
 #pragma unroll
                     for (int r = 0; r < kR; ++r) {
@@ -404,7 +453,7 @@ __global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF6
                             const uint64_t idx = hi | ((uint64_t)r << 6) | (uint64_t)lane;
                             if ((idx & ((1ull << a.pad) - 1)) == 0) {
                                 ++candidates;
-                                const double v = energy_def(a.Q, a.n, idx >> a.pad);
+                                const double v = energy_def(Q, a.n, idx >> a.pad);
                                 const uint64_t real = idx >> a.pad;
                                 if (v < rec.e) {
                                     rec.e = v;
@@ -435,9 +484,9 @@ __global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF6
                 rec_a[threadIdx.x] = rec.arg;
                 const double wm = uniform_f64(wave_min_f64(rec.e));
                 T = wm < T ? wm : T;
-                atomicMin(&a.ctrl->gbest, order_key(T));
+                atomicMin(&ctrl->gbest, order_key(T));
                 const double gb = uniform_f64(from_key(__hip_atomic_load(
-                    &a.ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+                    &ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
                 T = gb < T ? gb : T;
                 TD = (float)T + a.delta;
             }
@@ -477,7 +526,7 @@ __global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF6
     double e = rec_e[threadIdx.x];
     uint64_t cnt = rec_c[threadIdx.x], arg = rec_a[threadIdx.x];
     wave_combine(e, cnt, arg);
-    uint64_t cand = candidates;
+    uint64_t cand = candidates;  // a lane evaluates far fewer than 2^32 states
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
         cand += __shfl_xor(cand, off, 64);
@@ -489,7 +538,7 @@ __global__ __launch_bounds__(256) void gray_search_f64_kernel(const SearchArgsF6
         p.bodies = bodies;
         p.slow = slow;
         p.candidates = cand;
-        a.partials[(uint64_t)blockIdx.x * kWaves + wave] = p;
+        partials[(uint64_t)blockIdx.x * kWaves + wave] = p;
     }
 }
 
@@ -543,12 +592,12 @@ __global__ __launch_bounds__(256) void reduce_f64_kernel(const PartialF64 *__res
 }  // namespace
 
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
-                                   double *es, double *mint, double *ep, float *epmin,
-                                   hipStream_t stream)
+                                   double *es, double *mint, float *mint32, double *ep,
+                                   float *epmin, hipStream_t stream)
 {
     const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
     hipLaunchKernelGGL(build_suffix_f64_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
-                       cols_padded, es, mint);
+                       cols_padded, es, mint, mint32);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
@@ -570,7 +619,8 @@ hipError_t launch_search_f64(const SearchArgsF64 &args, int blocks, int lds_byte
                              hipStream_t stream)
 {
     hipLaunchKernelGGL(gray_search_f64_kernel, dim3(blocks), dim3(64 * kWaves), lds_bytes, stream,
-                       args);
+                       args.es, args.mint, args.mint32, args.ep, args.epmin, args.Q, args.partials,
+                       args.ctrl, args);
     return hipGetLastError();
 }
 
