@@ -288,3 +288,35 @@ def test_errors(q):
     with pytest.raises(q.QuboError) as e:
         q.search(big)
     assert e.value.code == q.QUBO_ERANGE
+
+
+def test_concurrent_streams(q):
+    """Calls on different streams from different host threads run concurrently
+    (each call owns its workspace and timing record) and give the same answers
+    as alone."""
+    import threading
+    import torch
+    cases = [qi.general_uniform(n, 7600 + n, -50, 50) for n in (22, 23, 24, 25)]
+    want = [oracle.search_gray(Q).triple() for Q in cases]
+    got = [None] * len(cases)
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                Qd = dev_q(cases[i])
+                for _ in range(3):
+                    got[i] = q.search(Qd, stream=s).triple()
+                    assert q.last_timing()["states"] == 1 << len(cases[i])
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    announce("concurrent streams")
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    assert got == want
