@@ -65,7 +65,7 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, seconds_budget=20.0):
+def cpu_baseline(cfg):
     """The CPU oracle (tier B, Gray walk) as it stands, on a seeded sub-cube of the
     same workload: the first k variables fixed (seed 4242), 2^(n-k) states."""
     import oracle
@@ -130,8 +130,9 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the search shards by work unit; see DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the work units of one search are independent and would be split across GPUs, "
+              "with one 24-byte result per GPU combined at the end)", file=sys.stderr)
         sys.exit(2)
 
     import torch

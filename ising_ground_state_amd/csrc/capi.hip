@@ -867,7 +867,7 @@ QUBO_API const char *qubo_strerror(int status)
 
 QUBO_API const char *qubo_version(void)
 {
-    return "qubo-mi355x 0.2 (gfx950; 8 or 16 columns/lane, 5 register Gray bits, int32; k-lowest)";
+    return "qubo-mi355x 0.3 (gfx950; int32 minimum and k-lowest, 8 or 16 columns/lane; binary64)";
 }
 
 }  // extern "C"
