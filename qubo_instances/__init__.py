@@ -239,6 +239,8 @@ CONFIGS = {
     "C3": dict(n=40, seed=1003, desc="+-1 Sherrington-Kirkpatrick n=40, h=0, as an int32 QUBO via x=(1+s)/2"),
     "C4": dict(n=48, seed=1004, desc="dense QUBO n=48, symmetric, all entries uniform in [-100,100]"),
     "C5": dict(n=50, seed=1005, desc="dense QUBO n=50, round(10 U U^T) + uniform[-20,20] noise, U 50x4 standard normal"),
+    # the largest single-launch size (A = 32, B = 26 at the default split)
+    "C58": dict(n=58, seed=1058, desc="dense QUBO n=58, symmetric, all entries uniform in [-100,100]"),
     # real-valued (binary64) counterparts of C1, C2 and C4
     "C1f": dict(n=24, seed=1011, desc="dense real QUBO n=24, symmetric, binary64 entries uniform in [-100,100)"),
     "C2f": dict(n=32, seed=1012, desc="dense real QUBO n=32, symmetric, binary64 entries uniform in [-100,100)"),
@@ -252,7 +254,7 @@ def make_config(name: str) -> dict:
     spec = CONFIGS[name]
     n, seed = spec["n"], spec["seed"]
     out = dict(name=name, n=n, desc=spec["desc"], seed=seed)
-    if name in ("C1", "C4"):
+    if name in ("C1", "C4", "C58"):
         out["Q"] = symmetric_uniform(n, seed, -100, 100)
     elif name == "C2":
         out["Q"] = symmetric_uniform(n, seed, -100, 100, -200, 200)

@@ -9,6 +9,7 @@ Calls only the CPU oracle (``oracle``) on the seeded workloads of
     python tests/golden/make_golden.py C1low C2low C2plow C4sublow C5sublow
                                                         # the 64 lowest states (spectrum)
     python tests/golden/make_golden.py C1f C2f C4fsub   # real-valued (binary64) workloads, tier A
+    python tests/golden/make_golden.py C58sub           # n = 58 (largest single launch): 2^36-state sub-cubes
 
 Full searches store {sha256_Q, n, min_energy, argmin, count, max_abs_energy}.
 Sub-cube files store one record per sub-cube: the first k variables are fixed
@@ -159,11 +160,44 @@ def subcubes_f64(name: str, threads: int) -> dict:
                 host=host_info(threads))
 
 
+MAX_SUB_FREE_BITS = 36
+MAX_SUB_COUNT = 2
+
+
+def subcubes_max(name: str, threads: int) -> dict:
+    """Sub-cubes of 2^36 states of the n = 58 workload, with the first 22
+    variables fixed, for the minimum, and the 16 lowest states of the first."""
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    k = n - MAX_SUB_FREE_BITS
+    rng = qi.SplitMix64(SUB_SEED + 200 + n)
+    tops = []
+    while len(tops) < MAX_SUB_COUNT:
+        t = rng.uniform_int(0, (1 << k) - 1)
+        if t not in tops:
+            tops.append(t)
+    cubes = []
+    t_all = time.time()
+    for i, top in enumerate(tops):
+        r = oracle.search_gray(Q, k=k, top=top, threads=threads)
+        cube = dict(k=k, top=top, min_energy=r.min_energy, argmin=r.argmin, count=r.count)
+        if i == 0:
+            cube["lowest16"] = [list(p) for p in oracle.lowest(Q, 16, gray_walk=True, threads=threads,
+                                                                 fixed=k, top=top)]
+        cubes.append(cube)
+        print("  %s top=%d -> %s" % (name, top, r.triple()), flush=True)
+    return dict(name=name + "sub", desc=cfg["desc"], n=n, seed=cfg["seed"], sha256_Q=qi.sha256_of(Q),
+                free_bits=MAX_SUB_FREE_BITS, sub_seed=SUB_SEED + 200 + n, cubes=cubes, tier="B (Gray walk)",
+                seconds_total=round(time.time() - t_all, 2), host=host_info(threads))
+
+
 def main(argv):
     threads = oracle.default_threads()
     for arg in argv:
         print("computing", arg, "on", threads, "threads", flush=True)
-        if arg.endswith("fsub"):
+        if arg == "C58sub":
+            rec = subcubes_max("C58", threads)
+        elif arg.endswith("fsub"):
             rec = subcubes_f64(arg[:-3], threads)
         elif arg in ("C1f", "C2f"):
             rec = full_f64(arg, threads)

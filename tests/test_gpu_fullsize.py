@@ -14,12 +14,15 @@ in test_gpu_parity.py::test_subcubes_at_full_size.
 """
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import pytest
 
 import oracle
 import qubo_instances as qi
-from gpu_helpers import announce, check_coverage, dev_q
+from gpu_helpers import announce, check_coverage, dev_q, inv_gray
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +130,33 @@ def test_split_invariance_n48(q):
     low = q.lowest(Qd, 64)
     announce("C4 spectrum split 31 12")
     assert q.lowest(Qd, 64, prefix_bits=31, cache_bits=12) == low
+
+
+def test_largest_single_launch_n58(q):
+    """n = 58, the largest size one launch searches: the planner's split is
+    A = 32, B = 26 (a 16 GiB prefix table and 8 GiB of M_int, at the caps).
+    Seeded slices of 2^36 states against stored oracle results
+    (tests/golden/C58sub.json): minimum, count and index, and the 16 lowest."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "C58sub.json")
+    if not os.path.exists(path):
+        pytest.skip("stored oracle result C58sub.json not written yet")
+    with open(path) as f:
+        g = json.load(f)
+    cfg = qi.make_config("C58")
+    assert qi.sha256_of(cfg["Q"]) == g["sha256_Q"]
+    plan = q.make_plan(58)
+    A = plan["prefix_bits"]
+    assert (A, plan["suffix_bits"]) == (32, 26)
+    Qd = dev_q(cfg["Q"])
+    for cube in g["cubes"]:
+        k, top = cube["k"], cube["top"]
+        m = inv_gray(top)
+        lo, hi = m << (A - k), (m + 1) << (A - k)
+        announce("n=58 slice", k, top)
+        r = q.search_range(Qd, A, lo, hi)
+        assert r.triple() == (cube["min_energy"], cube["argmin"], cube["count"]), top
+        check_coverage(q, 58, A, None, lo, hi)
+        if "lowest16" in cube:
+            announce("n=58 slice lowest", k, top)
+            low = q.lowest(Qd, 16, prefix_bits=A, gray_lo=lo, gray_hi=hi)
+            assert low == [(int(e), int(i)) for e, i in cube["lowest16"]]
