@@ -491,32 +491,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 TD = (float)T + a.delta;
             }
             // binary64 anchor to the next body: bit 4 flips inside this body,
-            // then the outer flip of Gray bit t >= 5
-            {
-                const double *m4 = lds_lane + 4 * kGroup;
-#pragma unroll
-                for (int r = 0; r < kR; ++r)
-                    E64[r] = top_plus ? E64[r] + m4[r * 64] : E64[r] - m4[r * 64];
-            }
+            // then the outer flip of Gray bit t >= 5 (after the unit's last body
+            // the anchor is not used).  fma with a wave-uniform +-1 is the signed
+            // add, rounded once, with no sign select per register.
             if (!last) {
+                const double s4 = top_plus ? 1.0 : -1.0;
                 const uint64_t next = base + kBody;
                 const int t = __builtin_ctzll(next);
-                const bool plus = ((next >> (t + 1)) & 1u) == 0;
-                double row[kR];
+                const double st = ((next >> (t + 1)) & 1u) ? -1.0 : 1.0;
+                const double *m4 = lds_lane + 4 * kGroup;
+                double row4[kR], row[kR];
                 if (t < a.l_eff) {
                     const double *src = lds_lane + t * kGroup;
 #pragma unroll
-                    for (int r = 0; r < kR; ++r)
+                    for (int r = 0; r < kR; ++r) {
+                        row4[r] = m4[r * 64];
                         row[r] = src[r * 64];
+                    }
                 } else {
                     const double *src = mint + (uint64_t)(A - 1 - t) * cp + col0;
 #pragma unroll
-                    for (int r = 0; r < kR; ++r)
+                    for (int r = 0; r < kR; ++r) {
+                        row4[r] = m4[r * 64];
                         row[r] = src[r * 64];
+                    }
                 }
 #pragma unroll
                 for (int r = 0; r < kR; ++r)
-                    E64[r] = plus ? E64[r] + row[r] : E64[r] - row[r];
+                    E64[r] = fma(row[r], st, fma(row4[r], s4, E64[r]));
             }
             epm_cur = epm_next;
             epm_next = epm_after;
