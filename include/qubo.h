@@ -40,7 +40,8 @@ extern "C" {
 
 #define QUBO_OK 0
 #define QUBO_EINVAL (-1)  /* null pointer, n or a split parameter out of range */
-#define QUBO_ERANGE (-2)  /* sum |Q_ij| exceeds 2^30 - 1: int32 would not be exact */
+#define QUBO_ERANGE (-2)  /* int32 Q: sum |Q_ij| exceeds 2^30 - 1 (int32 would not be exact);
+                             binary64 Q: an entry not finite or sum |Q_ij| above 2^100 */
 #define QUBO_EPLAN (-3)   /* the requested split does not fit the kernel's registers/LDS/limits */
 #define QUBO_EDEVICE (-4) /* no usable gfx950 device, or a HIP runtime error */
 #define QUBO_ENOMEM (-5)  /* device or host allocation failed */

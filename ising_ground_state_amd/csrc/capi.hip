@@ -51,7 +51,18 @@ struct Call {
     hipStream_t stream = nullptr;
     void *ws = nullptr;
     hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
-    bool events = false;
+
+    // Every event that was created is destroyed, also after a partial failure.
+    bool create_events()
+    {
+        for (auto &e : ev) {
+            hipEvent_t tmp = nullptr;
+            if (hipEventCreate(&tmp) != hipSuccess)
+                return false;
+            e = tmp;
+        }
+        return true;
+    }
 
     ~Call()
     {
@@ -59,10 +70,9 @@ struct Call {
             (void)hipFreeAsync(ws, stream);
             (void)hipStreamSynchronize(stream);
         }
-        if (events)
-            for (auto &e : ev)
-                if (e)
-                    (void)hipEventDestroy(e);
+        for (auto &e : ev)
+            if (e)
+                (void)hipEventDestroy(e);
     }
 };
 
@@ -187,10 +197,8 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     Partial *dpart = reinterpret_cast<Partial *>(base + L.off_partials);
     Ctrl *dctrl = reinterpret_cast<Ctrl *>(base + L.off_ctrl);
 
-    for (auto &e : call.ev)
-        if (hipEventCreate(&e) != hipSuccess)
-            return QUBO_EDEVICE;
-    call.events = true;
+    if (!call.create_events())
+        return QUBO_EDEVICE;
 
     // Upload, build, search, reduce.
     if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess)
@@ -605,10 +613,8 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
     float *depmin = reinterpret_cast<float *>(base + off_epmin);
     PartialF64 *dpart = reinterpret_cast<PartialF64 *>(base + off_part);
     CtrlF64 *dctrl = reinterpret_cast<CtrlF64 *>(base + off_ctrl);
-    for (auto &e : call.ev)
-        if (hipEventCreate(&e) != hipSuccess)
-            return QUBO_EDEVICE;
-    call.events = true;
+    if (!call.create_events())
+        return QUBO_EDEVICE;
 
     // A state passes the filter when its fp32 energy is within delta of the
     // best binary64 energy so far; delta bounds (several times over) every fp32
@@ -692,6 +698,17 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
     return QUBO_OK;
 }
 
+// A slice [gray_lo, gray_hi) of the Gray walk over an explicit prefix size:
+// whole 32-step bodies, non-empty, inside the 2^prefix_bits steps.
+bool valid_slice(int n, int prefix_bits, uint64_t gray_lo, uint64_t gray_hi)
+{
+    if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||
+        prefix_bits > qubo::kMaxPrefixBits)
+        return false;
+    return !(gray_lo & 31u) && !(gray_hi & 31u) && gray_lo < gray_hi &&
+           gray_hi <= (1ull << prefix_bits);
+}
+
 }  // namespace
 
 extern "C" {
@@ -739,11 +756,7 @@ QUBO_API int qubo_search_ex(const int32_t *Q, int n, int prefix_bits, int cache_
     rq.split_bits = (int)((flags & QUBO_FLAG_SPLIT_MASK) >> QUBO_FLAG_SPLIT_SHIFT);
     rq.stream = static_cast<hipStream_t>(stream);
     if (gray_lo != 0 || gray_hi != 0) {
-        if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||
-            prefix_bits > qubo::kMaxPrefixBits)
-            return QUBO_EINVAL;
-        if ((gray_lo & 31u) || (gray_hi & 31u) || gray_lo >= gray_hi ||
-            gray_hi > (1ull << prefix_bits))
+        if (!valid_slice(n, prefix_bits, gray_lo, gray_hi))
             return QUBO_EINVAL;
         rq.ranged = true;
         rq.gray_lo = gray_lo;
@@ -771,11 +784,7 @@ QUBO_API int qubo_search_lowest(const int32_t *Q, int n, int k, int prefix_bits,
     rq.lowest_k = k;
     rq.stream = static_cast<hipStream_t>(stream);
     if (gray_lo != 0 || gray_hi != 0) {
-        if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||
-            prefix_bits > qubo::kMaxPrefixBits)
-            return QUBO_EINVAL;
-        if ((gray_lo & 31u) || (gray_hi & 31u) || gray_lo >= gray_hi ||
-            gray_hi > (1ull << prefix_bits))
+        if (!valid_slice(n, prefix_bits, gray_lo, gray_hi))
             return QUBO_EINVAL;
         rq.ranged = true;
         rq.gray_lo = gray_lo;
@@ -805,11 +814,7 @@ QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_
     rq.cache_bits = cache_bits;
     rq.stream = static_cast<hipStream_t>(stream);
     if (gray_lo != 0 || gray_hi != 0) {
-        if (n < qubo::kMinSearchVars || prefix_bits < qubo::kRegBits || prefix_bits > n ||
-            prefix_bits > qubo::kMaxPrefixBits)
-            return QUBO_EINVAL;
-        if ((gray_lo & 31u) || (gray_hi & 31u) || gray_lo >= gray_hi ||
-            gray_hi > (1ull << prefix_bits))
+        if (!valid_slice(n, prefix_bits, gray_lo, gray_hi))
             return QUBO_EINVAL;
         rq.ranged = true;
         rq.gray_lo = gray_lo;
@@ -853,7 +858,8 @@ QUBO_API const char *qubo_strerror(int status)
     case QUBO_EINVAL:
         return "invalid argument";
     case QUBO_ERANGE:
-        return "sum of |Q_ij| exceeds 2^30-1 (int32 search would not be exact)";
+        return "Q out of range (int32: sum of |Q_ij| above 2^30-1; binary64: an entry not finite "
+               "or sum of |Q_ij| above 2^100)";
     case QUBO_EPLAN:
         return "split does not fit the kernel (prefix/cache bits out of the supported range)";
     case QUBO_EDEVICE:
