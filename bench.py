@@ -124,6 +124,11 @@ def main():
                     help="skip the extra step of the 64-lowest-states search reported beside the minimum")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling HBM counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time one search per split of the grid below on --config (one JSON line "
+                         "per point, then a summary line); every point must give the same result")
+    ap.add_argument("--sweep-prefix", default="24,26,28,30,32", help="prefix_bits values of the sweep")
+    ap.add_argument("--sweep-cache", default="8,10,12,13,14,16,18", help="cache_bits values of the sweep")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -144,6 +149,10 @@ def main():
     cfg = qi.make_config(args.config)
     n = cfg["n"]
     Qd = torch.tensor(cfg["Q"], dtype=torch.int32, device="cuda:0")
+    if args.sweep:
+        split_sweep(q, Qd, cfg, [int(v) for v in args.sweep_prefix.split(",")],
+                    [int(v) for v in args.sweep_cache.split(",")])
+        return
     plan = q.make_plan(n, args.prefix_bits, args.cache_bits)
     states = 1 << n
 
@@ -256,6 +265,51 @@ def main():
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)
+
+
+def split_sweep(q, Qd, cfg, prefixes, caches):
+    """One search per (prefix_bits, cache_bits) with 8 columns per lane, and per
+    cache_bits with 16 columns per lane at the planner's prefix size.  Splits the
+    planner rejects are listed as such.  The result is the same at every split."""
+    import torch
+    n = cfg["n"]
+    states = 1 << n
+    default = q.make_plan(n)
+    ref = q.search(Qd)  # also the warm-up
+    ref_t = q.last_timing()
+    points = [(A, l, 8) for A in prefixes for l in caches]
+    points += [(default["prefix_bits"], l, 16) for l in caches]
+    rows = []
+    for A, l, cols in points:
+        rec = {"prefix_bits": A, "suffix_bits": n - A, "cache_bits": l, "cols_per_lane": cols}
+        if l > A:
+            continue
+        try:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            r = q.search(Qd, A, l, cols_per_lane=cols)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        except q.QuboError as e:
+            rec["rejected"] = q.strerror(e.code)
+            print(json.dumps({"sweep_point": rec}), flush=True)
+            continue
+        t = q.last_timing()
+        rec.update({"search_ms": t["search_ms"], "total_ms": t["total_ms"], "wall_ms": wall * 1e3,
+                    "kernel_states_per_s": states / (t["search_ms"] / 1e3) / 1e12,
+                    "frac": states / (t["search_ms"] / 1e3) / INT32_VALU_PEAK,
+                    "slow_bodies": t["slow_bodies"], "same_result": r.triple() == ref.triple()})
+        rows.append(rec)
+        print(json.dumps({"sweep_point": rec}), flush=True)
+    best = min(rows, key=lambda r: r["search_ms"])
+    print(json.dumps({"sweep": cfg["name"], "n": n, "states": states,
+                      "planner_default": {"prefix_bits": default["prefix_bits"],
+                                          "cache_bits": default["cache_bits"],
+                                          "cols_per_lane": default["cols_per_lane"],
+                                          "search_ms": ref_t["search_ms"]},
+                      "best": best, "points": len(rows),
+                      "all_same_result": all(r["same_result"] for r in rows),
+                      "result": list(ref.triple())}), flush=True)
 
 
 if __name__ == "__main__":
