@@ -234,6 +234,52 @@ QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_
                              uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
                              qubo_result_f64 *out);
 
+/* A search run in steps, so that a long search (n = 58 takes about an hour,
+ * n = 63 about 35 hours) can be stopped and resumed, or its steps spread over
+ * time.  The work units are independent (sec. III.C), so the state space is
+ * walked as the 2^k sub-problems of the outer split (sec. III.C.1; k = 0 for
+ * n <= 58 unless asked for), each as consecutive slices of 2^chunk_bits Gray
+ * steps of its prefix walk (qubo_search_range), and the slices' results are
+ * combined by the rule of the final reduction (sec. III.C: minimum, count at
+ * the minimum, lowest index).  The whole state of the run is this plain struct
+ * (96 bytes, no pointers): the caller keeps it between calls, in memory or in
+ * a file, and the same Q continues the run from it. */
+typedef struct {
+    uint64_t q_hash;      /* fingerprint of n and Q (FNV-1a over the int32 entries) */
+    int32_t n;            /* variables */
+    int32_t split_bits;   /* k: first k variables fixed per sub-problem (0: one problem) */
+    int32_t prefix_bits;  /* A of each (sub-)problem of n - k variables */
+    int32_t chunk_bits;   /* each step searches 2^chunk_bits Gray steps (all suffixes) */
+    uint64_t sub;         /* current sub-problem: the values of the first k variables */
+    uint64_t next;        /* first Gray step of the next slice of the current sub-problem */
+    uint64_t steps_done;  /* slices searched or skipped so far */
+    uint64_t steps_total; /* 2^k * 2^(A - chunk_bits) */
+    int32_t done;         /* 1 once every state has been searched */
+    int32_t have_best;    /* 1 once best holds a searched state */
+    qubo_result best;     /* the combined result of the slices searched so far */
+    uint64_t reserved;    /* zero */
+} qubo_progress;
+
+/* Starts a run: fills *p for Q (device pointer, n x n int32, as for qubo_search).
+ *   prefix_bits: A of each (sub-)problem, or -1 for the planner's choice.
+ *   chunk_bits:  Gray steps per step as a power of two, 5 <= chunk_bits <= A, or
+ *                -1 for slices of about 2^48 states (a few seconds each).
+ *   flags: 0 or QUBO_FLAG_SPLIT(k) as for qubo_search_ex (above 58 variables
+ *          the split is automatic).  n - k must be at least 5.
+ * Blocking (Q is read to form the fingerprint); error codes as qubo_search. */
+QUBO_API int qubo_progress_init(const int32_t *Q, int n, int prefix_bits, int chunk_bits, uint32_t flags,
+                                void *stream, qubo_progress *p);
+
+/* Searches the next slice of the run in *p and folds its result into p->best.
+ * Q and n must be the ones *p was started with (QUBO_EINVAL otherwise, checked
+ * against the fingerprint).  A sub-problem whose every state lies above the
+ * best energy found so far is skipped whole.  Once p->done is 1 the call does
+ * nothing and returns QUBO_OK; p->best is then exactly qubo_search's result.
+ * On error *p is untouched, so the step can be retried.  Blocking; same
+ * ownership and error behaviour as qubo_search; qubo_last_timing reports the
+ * step. */
+QUBO_API int qubo_search_step(const int32_t *Q, int n, void *stream, qubo_progress *p);
+
 /* Builds the cache tables of a plan into caller-provided device buffers, for
  * inspection (sec. III.A preprocessing steps 1-3, eq. 8):
  *   Es:     2^B entries (int32): E_s(c), the energy of the suffix alone, c the

@@ -60,6 +60,22 @@ class _Plan(ctypes.Structure):
                [(name, ctypes.c_uint64) for name in ("col_groups", "work_units", "workspace_bytes")]
 
 
+class Progress(ctypes.Structure):
+    """The state of a search run in slices (``qubo_progress``, 96 bytes): keep it
+    between steps, e.g. as ``bytes(progress)`` in a file."""
+    _fields_ = [("q_hash", ctypes.c_uint64), ("n", ctypes.c_int32), ("split_bits", ctypes.c_int32),
+                ("prefix_bits", ctypes.c_int32), ("chunk_bits", ctypes.c_int32),
+                ("sub", ctypes.c_uint64), ("next", ctypes.c_uint64),
+                ("steps_done", ctypes.c_uint64), ("steps_total", ctypes.c_uint64),
+                ("done", ctypes.c_int32), ("have_best", ctypes.c_int32), ("best", _Result),
+                ("reserved", ctypes.c_uint64)]
+
+    def result(self) -> "Result":
+        if not self.have_best:
+            raise ValueError("no state searched yet")
+        return Result(self.best.min_energy, self.best.argmin, self.best.count)
+
+
 class _Timing(ctypes.Structure):
     _fields_ = [("build_ms", ctypes.c_float), ("search_ms", ctypes.c_float),
                 ("reduce_ms", ctypes.c_float), ("total_ms", ctypes.c_float),
@@ -86,7 +102,7 @@ _lib = None
 
 EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range", "qubo_search_ex",
            "qubo_build_tables", "qubo_last_timing", "qubo_search_lowest", "qubo_search_f64",
-           "qubo_strerror", "qubo_version")
+           "qubo_progress_init", "qubo_search_step", "qubo_strerror", "qubo_version")
 MAX_LOWEST = 64
 FLAG_STRICT_MIN = 1
 FLAG_COLS8 = 2
@@ -123,8 +139,12 @@ def load(path: str = LIB_PATH):
     lib.qubo_version.restype = ctypes.c_char_p
     lib.qubo_search_f64.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
                                     ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.POINTER(_ResultF64)]
-    for name in EXPORTS[:9]:
-        getattr(lib, name).restype = ctypes.c_int
+    lib.qubo_progress_init.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                                       ctypes.c_void_p, ctypes.POINTER(Progress)]
+    lib.qubo_search_step.argtypes = [i32p, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(Progress)]
+    for name in EXPORTS:
+        if name not in ("qubo_strerror", "qubo_version"):
+            getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -253,6 +273,67 @@ def lowest(Q, k: int, prefix_bits: int | None = None, cache_bits: int | None = N
     if rc != QUBO_OK:
         raise QuboError(rc, "qubo_search_lowest")
     return [(out[i].energy, out[i].index) for i in range(found.value)]
+
+
+def progress_init(Q, prefix_bits: int | None = None, chunk_bits: int | None = None,
+                  split_bits: int | None = None, stream=None) -> Progress:
+    """Starts a search run in slices of 2^chunk_bits Gray steps (default: about
+    2^48 states per step); split_bits as for search."""
+    import torch
+    Q = _device_q(Q)
+    p = Progress()
+    with torch.cuda.device(Q.device):
+        rc = load().qubo_progress_init(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
+                                       _opt(chunk_bits), _flags(False, None, split_bits), _stream(Q, stream),
+                                       ctypes.byref(p))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_progress_init")
+    return p
+
+
+def search_step(Q, progress: Progress, stream=None) -> bool:
+    """Searches the next slice of the run and updates ``progress`` in place;
+    returns progress.done."""
+    import torch
+    Q = _device_q(Q)
+    with torch.cuda.device(Q.device):
+        rc = load().qubo_search_step(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _stream(Q, stream),
+                                     ctypes.byref(progress))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_search_step")
+    return bool(progress.done)
+
+
+def search_resumable(Q, path: str, prefix_bits: int | None = None, chunk_bits: int | None = None,
+                     split_bits: int | None = None, max_steps: int | None = None, stream=None):
+    """A search that survives interruption: the run's state (96 bytes) is kept in
+    the file ``path`` and rewritten atomically after every step, and a later call
+    with the same Q continues from it.  Returns the Result once every state has
+    been searched, or None after max_steps steps of an unfinished run."""
+    if os.path.exists(path):
+        with open(path, "rb") as f:
+            raw = f.read()
+        if len(raw) != ctypes.sizeof(Progress):
+            raise ValueError("%s is not a search state (%d bytes)" % (path, len(raw)))
+        p = Progress.from_buffer_copy(raw)
+    else:
+        p = progress_init(Q, prefix_bits, chunk_bits, split_bits, stream)
+        _save_progress(path, p)
+    steps = 0
+    while not p.done and (max_steps is None or steps < max_steps):
+        search_step(Q, p, stream)
+        _save_progress(path, p)
+        steps += 1
+    return p.result() if p.done else None
+
+
+def _save_progress(path: str, p: Progress) -> None:
+    tmp = path + ".tmp"
+    with open(tmp, "wb") as f:
+        f.write(bytes(p))
+        f.flush()
+        os.fsync(f.fileno())
+    os.replace(tmp, path)
 
 
 def search_f64(Q, prefix_bits: int | None = None, cache_bits: int | None = None, stream=None,

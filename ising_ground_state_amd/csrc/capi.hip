@@ -46,6 +46,32 @@ int device_info(DeviceInfo *info)
     return QUBO_OK;
 }
 
+// Copies Q (n x n int32, device) to the host.
+int read_q(const int32_t *Q, int n, hipStream_t stream, std::vector<int32_t> &Qh)
+{
+    Qh.resize((size_t)n * n);
+    if (hipMemcpyAsync(Qh.data(), Q, Qh.size() * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    return QUBO_OK;
+}
+
+// FNV-1a (64 bit) over n and the entries of Q, each as 4 little-endian bytes.
+uint64_t fingerprint(const std::vector<int32_t> &Qh, int n)
+{
+    uint64_t h = 0xcbf29ce484222325ull;
+    auto mix = [&h](uint32_t v) {
+        for (int b = 0; b < 4; ++b) {
+            h ^= (v >> (8 * b)) & 0xffu;
+            h *= 0x100000001b3ull;
+        }
+    };
+    mix((uint32_t)n);
+    for (int32_t v : Qh)
+        mix((uint32_t)v);
+    return h;
+}
+
 // Everything one call owns; released in the destructor on every path.
 struct Call {
     hipStream_t stream = nullptr;
@@ -95,6 +121,7 @@ struct Request {
 };
 
 static_assert(sizeof(qubo::LowEntry) == sizeof(qubo_state), "list entry layout");
+static_assert(sizeof(qubo_progress) == 96, "the run state is a fixed 96-byte record");
 
 // Keeps the k first states of `acc` merged with `add`, in (energy, index) order.
 void merge_lowest(std::vector<qubo_state> &acc, const std::vector<qubo_state> &add, int k)
@@ -384,11 +411,10 @@ int run(const Request &rq, qubo_result *out, qubo_state *low_out = nullptr,
         return rc;
 
     // Q to the host; fold and guard.
-    std::vector<int32_t> Qh((size_t)n * n);
-    if (hipMemcpyAsync(Qh.data(), rq.Q, Qh.size() * 4, hipMemcpyDeviceToHost, rq.stream) !=
-            hipSuccess ||
-        hipStreamSynchronize(rq.stream) != hipSuccess)
-        return QUBO_EDEVICE;
+    std::vector<int32_t> Qh;
+    rc = read_q(rq.Q, n, rq.stream, Qh);
+    if (rc != QUBO_OK)
+        return rc;
     std::vector<int32_t> U;
     int64_t abs_sum = 0;
     rc = fold_upper(Qh.data(), n, U, &abs_sum);
@@ -491,6 +517,97 @@ int run(const Request &rq, qubo_result *out, qubo_state *low_out = nullptr,
         return QUBO_EDEVICE;  // the first sub-problem is searched without a cap
     g_timing = acc;
     *out = best;
+    return QUBO_OK;
+}
+
+// One step of a run in slices (qubo_search_step): the next slice of the
+// current sub-problem, folded into the run's result by the final reduction's
+// rule; the new state goes to *next (the caller's struct is left alone on error).
+int run_step(const int32_t *Q, int n, hipStream_t stream, const qubo_progress &p, qubo_progress *next)
+{
+    using namespace qubo;
+    const int k = p.split_bits, A = p.prefix_bits, cb = p.chunk_bits, m = n - k;
+    if (k < 0 || k > kMaxSplitBits || m < kMinSearchVars || m > kMaxSingleVars || A < kRegBits ||
+        A > m || A > kMaxPrefixBits || cb < kRegBits || cb > A || p.sub >= (1ull << k) ||
+        p.next >= (1ull << A) || (p.next & ((1ull << cb) - 1)) || p.steps_total == 0)
+        return QUBO_EINVAL;
+    DeviceInfo dev;
+    int rc = device_info(&dev);
+    if (rc != QUBO_OK)
+        return rc;
+    std::vector<int32_t> Qh;
+    rc = read_q(Q, n, stream, Qh);
+    if (rc != QUBO_OK)
+        return rc;
+    if (fingerprint(Qh, n) != p.q_hash)
+        return QUBO_EINVAL;  // not the matrix this run was started with
+    std::vector<int32_t> U;
+    int64_t abs_sum = 0;
+    rc = fold_upper(Qh.data(), n, U, &abs_sum);
+    if (rc != QUBO_OK)
+        return rc;
+    std::vector<int32_t> Usub;
+    int64_t c = 0, sub_abs = abs_sum;
+    if (k > 0)
+        reduce_fixed(U, n, k, p.sub, Usub, &c, &sub_abs);
+    else
+        Usub.swap(U);
+
+    qubo_progress q = p;
+    const uint64_t slices = 1ull << (A - cb);
+    qubo_timing t{};
+    bool have_cap = false;
+    int32_t cap = 0;
+    if (p.have_best) {
+        const int64_t cap64 = (int64_t)p.best.min_energy - c;
+        if (cap64 < -sub_abs) {
+            // every state of this sub-problem lies above the best energy found so far
+            q.steps_done += slices - (p.next >> cb);
+            q.next = 1ull << A;
+        } else {
+            have_cap = true;
+            cap = (int32_t)(cap64 < sub_abs ? cap64 : sub_abs);
+        }
+    }
+    if (q.next < (1ull << A)) {
+        Request rq;
+        rq.Q = Q;
+        rq.n = m;
+        rq.prefix_bits = A;
+        rq.ranged = true;
+        rq.gray_lo = p.next;
+        rq.gray_hi = p.next + (1ull << cb);
+        rq.stream = stream;
+        qubo_result r{};
+        bool found = false;
+        rc = run_one(rq, dev, std::move(Usub), m, sub_abs, have_cap, cap, &r, &found, &t);
+        if (rc != QUBO_OK)
+            return rc;
+        if (found) {
+            const int32_t e = (int32_t)((int64_t)r.min_energy + c);  // a state's energy: |e| <= abs_sum
+            const uint64_t idx = (k > 0 ? (p.sub << m) : 0) | r.argmin;
+            if (!q.have_best || e < q.best.min_energy) {
+                q.best.min_energy = e;
+                q.best.reserved = 0;
+                q.best.argmin = idx;
+                q.best.count = r.count;
+                q.have_best = 1;
+            } else if (e == q.best.min_energy) {
+                q.best.count += r.count;
+                q.best.argmin = idx < q.best.argmin ? idx : q.best.argmin;
+            }
+        }
+        q.steps_done += 1;
+        q.next = p.next + (1ull << cb);
+    }
+    if (q.next == (1ull << A)) {
+        q.next = 0;
+        q.sub = p.sub + 1;
+        if (q.sub == (1ull << k))
+            q.done = 1;
+    }
+    g_timing = t;
+    *next = q;
     return QUBO_OK;
 }
 
@@ -801,6 +918,59 @@ QUBO_API int qubo_search_range(const int32_t *Q, int n, int prefix_bits, int cac
     return qubo_search_ex(Q, n, prefix_bits, cache_bits, gray_lo, gray_hi, 0u, stream, out);
 }
 
+QUBO_API int qubo_progress_init(const int32_t *Q, int n, int prefix_bits, int chunk_bits, uint32_t flags,
+                                void *stream, qubo_progress *p)
+{
+    using namespace qubo;
+    if (!Q || !p || n < 1 || n > QUBO_MAX_N || (flags & ~QUBO_FLAG_SPLIT_MASK))
+        return QUBO_EINVAL;
+    int k = (int)((flags & QUBO_FLAG_SPLIT_MASK) >> QUBO_FLAG_SPLIT_SHIFT);
+    if (k == 0 && n > kMaxSingleVars)
+        k = n - kMaxSingleVars;
+    if (n - k < kMinSearchVars)
+        return QUBO_EINVAL;
+    qubo_plan plan;
+    int rc = make_plan(n, prefix_bits, -1, 256, 0, k, &plan);
+    if (rc != QUBO_OK)
+        return rc;
+    const int A = plan.prefix_bits, B = plan.suffix_bits;
+    if (chunk_bits < 0)
+        chunk_bits = std::max(kRegBits, std::min(A, 48 - B));  // about 2^48 states per step
+    if (chunk_bits < kRegBits || chunk_bits > A)
+        return QUBO_EINVAL;
+    DeviceInfo dev;
+    rc = device_info(&dev);
+    if (rc != QUBO_OK)
+        return rc;
+    std::vector<int32_t> Qh;
+    rc = read_q(Q, n, static_cast<hipStream_t>(stream), Qh);
+    if (rc != QUBO_OK)
+        return rc;
+    std::vector<int32_t> U;
+    int64_t abs_sum = 0;
+    rc = fold_upper(Qh.data(), n, U, &abs_sum);
+    if (rc != QUBO_OK)
+        return rc;
+    qubo_progress q{};
+    q.q_hash = fingerprint(Qh, n);
+    q.n = n;
+    q.split_bits = k;
+    q.prefix_bits = A;
+    q.chunk_bits = chunk_bits;
+    q.steps_total = (1ull << k) << (A - chunk_bits);
+    *p = q;
+    return QUBO_OK;
+}
+
+QUBO_API int qubo_search_step(const int32_t *Q, int n, void *stream, qubo_progress *p)
+{
+    if (!Q || !p || n < 1 || n > QUBO_MAX_N || p->n != n)
+        return QUBO_EINVAL;
+    if (p->done)
+        return QUBO_OK;
+    return run_step(Q, n, static_cast<hipStream_t>(stream), *p, p);
+}
+
 QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_bits,
                              uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
                              qubo_result_f64 *out)
@@ -873,7 +1043,7 @@ QUBO_API const char *qubo_strerror(int status)
 
 QUBO_API const char *qubo_version(void)
 {
-    return "qubo-mi355x 0.3 (gfx950; int32 minimum and k-lowest, 8 or 16 columns/lane; binary64)";
+    return "qubo-mi355x 0.4 (gfx950; int32 minimum and k-lowest, 8 or 16 columns/lane; binary64; runs in steps)";
 }
 
 }  // extern "C"

@@ -133,6 +133,43 @@ def test_null_and_range_arguments_rejected_before_the_device():
     assert lib.qubo_search_f64(P, 12, -1, -1, 0, 0, 0, None, None) == q.QUBO_EINVAL
 
 
+def test_progress_record_and_rejections_before_the_device():
+    """The run state of a search in slices is a fixed 96-byte record; malformed
+    arguments and records are refused before any device call, and a finished
+    run's step does nothing."""
+    lib = q.load()
+    assert ctypes.sizeof(q.Progress) == 96
+    offsets = {name: getattr(q.Progress, name).offset for name, _ in q.Progress._fields_}
+    assert offsets == {"q_hash": 0, "n": 8, "split_bits": 12, "prefix_bits": 16, "chunk_bits": 20,
+                       "sub": 24, "next": 32, "steps_done": 40, "steps_total": 48, "done": 56,
+                       "have_best": 60, "best": 64, "reserved": 88}
+    P = ctypes.c_void_p(16)
+    p = q.Progress()
+    assert lib.qubo_progress_init(None, 12, -1, -1, 0, None, ctypes.byref(p)) == q.QUBO_EINVAL
+    assert lib.qubo_progress_init(P, 12, -1, -1, 0, None, None) == q.QUBO_EINVAL
+    for n_, pb, cb, flags in [(0, -1, -1, 0), (64, -1, -1, 0), (12, -1, -1, q.FLAG_STRICT_MIN),
+                              (12, -1, -1, q.FLAG_COLS8), (12, 8, 4, 0), (12, 8, 9, 0),
+                              (12, -1, -1, 8 << q.FLAG_SPLIT_SHIFT)]:
+        assert lib.qubo_progress_init(P, n_, pb, cb, flags, None, ctypes.byref(p)) == q.QUBO_EINVAL, (n_, pb, cb)
+    assert bytes(p) == bytes(96)  # untouched
+    # a record that does not describe a run of this n, or is out of range
+    good = dict(n=12, split_bits=0, prefix_bits=8, chunk_bits=6, steps_total=4)
+    bad = [dict(n=13), dict(split_bits=-1), dict(split_bits=8), dict(prefix_bits=4), dict(prefix_bits=13),
+           dict(chunk_bits=4), dict(chunk_bits=9), dict(next=32), dict(next=1 << 8), dict(sub=1),
+           dict(steps_total=0)]
+    for change in bad:
+        p = q.Progress(**{**good, **change})
+        before = bytes(p)
+        assert lib.qubo_search_step(P, 12, None, ctypes.byref(p)) == q.QUBO_EINVAL, change
+        assert bytes(p) == before
+    assert lib.qubo_search_step(None, 12, None, ctypes.byref(q.Progress(**good))) == q.QUBO_EINVAL
+    assert lib.qubo_search_step(P, 12, None, None) == q.QUBO_EINVAL
+    done = q.Progress(**good, done=1)
+    before = bytes(done)
+    assert lib.qubo_search_step(P, 12, None, ctypes.byref(done)) == q.QUBO_OK
+    assert bytes(done) == before
+
+
 def test_timing_struct_before_any_search():
     t = q.last_timing()
     assert set(t) >= {"build_ms", "search_ms", "reduce_ms", "total_ms", "states", "slow_bodies"}
