@@ -232,7 +232,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
         return QUBO_EDEVICE;
     if (hipMemcpyAsync(dU, U.data(), U.size() * 4, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
-    if (launch_build_tables(dU, ns, A, B, L.cols_padded, des, dmint, dep, depmin, rq.stream) !=
+    if (launch_build_tables(dU, ns, A, B, L.cols_padded, des, dmint, dep, depmin, lo, hi, rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess)
@@ -746,7 +746,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
     if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess ||
         hipMemcpyAsync(dU, U.data(), U.size() * 8, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
-    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, des, dmint, dmint32, dep, depmin,
+    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, des, dmint, dmint32, dep, depmin, lo, hi,
                                 rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;

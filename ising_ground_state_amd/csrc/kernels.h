@@ -61,9 +61,11 @@ struct SearchArgs {
 
 // Cache builder (Maltsev et al., sec. III.A preprocessing, eq. 8): E_s, M_int
 // and the Gray-ordered prefix energies, from the folded upper-triangular U.
+// Only the prefix energies a search of the Gray steps [j_lo, j_hi) reads are
+// written (j_lo, j_hi multiples of 32; the tables keep their full size).
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
                                int32_t *es, int32_t *mint, int32_t *ep, int32_t *epmin,
-                               hipStream_t stream);
+                               uint64_t j_lo, uint64_t j_hi, hipStream_t stream);
 
 // Resets the work counter, seeds the shared best with t0 (a real energy or an
 // upper bound) and fills the body-minimum table's two padding entries.

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void build_suffix_kernel(const int32_t *__rest
 // 32k .. 32k+31), which bounds the prefix energy of every state of that body.
 __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *__restrict__ U,
                                                                 int ns, int A, int L,
-                                                                uint64_t nblocks,
+                                                                uint64_t blk_first, uint64_t blk_end,
                                                                 int32_t *__restrict__ ep,
                                                                 int32_t *__restrict__ epmin)
 {
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *_
     const int tid = threadIdx.x;
     // Block-stride loop: a dispatch holds fewer than 2^32 work-items, and A = 32
     // needs 2^32 prefixes.  The trip count is the same for every thread of a block.
-    for (uint64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    for (uint64_t blk = blk_first + blockIdx.x; blk < blk_end; blk += gridDim.x) {
         const uint64_t hi = gray(blk);  // high part of g(j), H bits
         if (tid < L) {
             const int v = H + tid;  // a low variable
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *_
 
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
                                int32_t *es, int32_t *mint, int32_t *ep, int32_t *epmin,
-                               hipStream_t stream)
+                               uint64_t j_lo, uint64_t j_hi, hipStream_t stream)
 {
     const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
     hipLaunchKernelGGL(build_suffix_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
@@ -253,11 +253,14 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
+    if (j_lo >= j_hi || j_hi > (1ull << A))
+        return hipErrorInvalidValue;
     const int L = A < 8 ? A : 8;
-    const uint64_t nblocks = 1ull << (A - L);
+    const uint64_t blk_first = j_lo >> L, blk_end = ((j_hi - 1) >> L) + 1;  // blocks holding the range
+    const uint64_t nblocks = blk_end - blk_first;
     const uint64_t grid = nblocks < (1ull << 20) ? nblocks : (1ull << 20);
     hipLaunchKernelGGL(build_prefix_gray_kernel, dim3((unsigned)grid), dim3(1u << L), 0, stream,
-                       U, ns, A, L, nblocks, ep, epmin);
+                       U, ns, A, L, blk_first, blk_end, ep, epmin);
     return hipGetLastError();
 }
 

@@ -51,9 +51,11 @@ struct SearchArgsF64 {
 
 // E_s, M_int and E_p(g(j)) in binary64 from the folded matrix, M_int rounded to
 // fp32, and the per-body minima of E_p rounded to fp32.
+// Only the prefix energies of the Gray steps [j_lo, j_hi) are written (multiples
+// of 32; the tables keep their full size).
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
                                    double *es, double *mint, float *mint32, double *ep,
-                                   float *epmin, hipStream_t stream);
+                                   float *epmin, uint64_t j_lo, uint64_t j_hi, hipStream_t stream);
 
 hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, hipStream_t stream);
 

@@ -165,16 +165,17 @@ __global__ __launch_bounds__(256) void build_suffix_f64_kernel(const double *__r
 // ep[j] = E_p(g(j)) over the A prefix variables, summed directly (O(A^2) per
 // prefix; the table is built once), and epmin[k] = min over body k of ep
 // rounded to fp32.  Block-stride loop over 256-prefix blocks.
+// Gray steps j_first <= j < j_end (j_first a multiple of 256, j_end of 32).
 __global__ __launch_bounds__(256) void build_prefix_f64_kernel(const double *__restrict__ U, int ns,
-                                                               int A, uint64_t total,
+                                                               int A, uint64_t j_first, uint64_t j_end,
                                                                double *__restrict__ ep,
                                                                float *__restrict__ epmin)
 {
-    for (uint64_t j0 = (uint64_t)blockIdx.x * blockDim.x; j0 < total;
+    for (uint64_t j0 = j_first + (uint64_t)blockIdx.x * blockDim.x; j0 < j_end;
          j0 += (uint64_t)gridDim.x * blockDim.x) {
         const uint64_t j = j0 + threadIdx.x;
         float m = __int_as_float(0x7f800000);
-        if (j < total) {
+        if (j < j_end) {
             const uint64_t p = gray(j);
             double e = 0.0;
             for (int i = 0; i < A; ++i) {
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256) void build_prefix_f64_kernel(const double *__r
 #pragma unroll
         for (int off = 16; off >= 1; off >>= 1)
             m = fminf(m, __shfl_xor(m, off, 64));
-        if (j < total && (j & 31) == 0)
+        if (j < j_end && (j & 31) == 0)
             epmin[j >> 5] = m;
     }
 }
@@ -595,7 +596,7 @@ __global__ __launch_bounds__(256) void reduce_f64_kernel(const PartialF64 *__res
 
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
                                    double *es, double *mint, float *mint32, double *ep,
-                                   float *epmin, hipStream_t stream)
+                                   float *epmin, uint64_t j_lo, uint64_t j_hi, hipStream_t stream)
 {
     const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
     hipLaunchKernelGGL(build_suffix_f64_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
@@ -603,11 +604,13 @@ hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    const uint64_t total = 1ull << A;
-    const uint64_t blocks = (total + 255) / 256;
+    if (j_lo >= j_hi || j_hi > (1ull << A) || (j_lo & 31) || (j_hi & 31))
+        return hipErrorInvalidValue;
+    const uint64_t j_first = j_lo & ~uint64_t(255);
+    const uint64_t blocks = (j_hi - j_first + 255) / 256;
     const uint64_t grid = blocks < (1ull << 20) ? blocks : (1ull << 20);
     hipLaunchKernelGGL(build_prefix_f64_kernel, dim3((unsigned)grid), dim3(256), 0, stream, U, ns,
-                       A, total, ep, epmin);
+                       A, j_first, j_hi, ep, epmin);
     return hipGetLastError();
 }
 
