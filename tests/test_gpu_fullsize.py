@@ -132,6 +132,47 @@ def test_split_invariance_n48(q):
     assert q.lowest(Qd, 64, prefix_bits=31, cache_bits=12) == low
 
 
+def test_invariances_full_size(q):
+    """The whole n = 48 space (C4) under four changes of the matrix whose effect
+    on the result is known: a permutation of the variables (min and count kept,
+    the minimiser's bits permuted), an added antisymmetric matrix (nothing
+    changes: E depends on Q_ij + Q_ji only), the gauge flip x -> x xor m
+    (min - E(m), count kept, argmin xor m) and scaling by 3 (min x 3).  The
+    minimiser is unique (count 1), so its index is determined by the map."""
+    cfg = qi.make_config("C4")
+    n = 48
+    Q = np.array(cfg["Q"], dtype=np.int64)
+    announce("C4 reference")
+    r0 = q.search(dev_q(Q))
+    assert r0.count == 1
+    x0 = r0.bits(n)
+    rng = qi.SplitMix64(9201)
+    perm = list(range(n))
+    for i in range(n - 1, 0, -1):  # Fisher-Yates
+        j = rng.uniform_int(0, i)
+        perm[i], perm[j] = perm[j], perm[i]
+    Qp = Q[np.ix_(perm, perm)]  # variable i of Qp is variable perm[i] of Q
+    announce("C4 permuted")
+    rp = q.search(dev_q(Qp))
+    assert (rp.min_energy, rp.count) == (r0.min_energy, 1)
+    assert rp.bits(n) == [x0[perm[i]] for i in range(n)]
+    S = np.zeros((n, n), dtype=np.int64)
+    for i in range(n):
+        for j in range(i + 1, n):
+            S[i, j] = rng.uniform_int(-100, 100)
+            S[j, i] = -S[i, j]
+    announce("C4 plus antisymmetric")
+    assert q.search(dev_q(Q + S)).triple() == r0.triple()
+    mask = [rng.uniform_int(0, 1) for _ in range(n)]
+    m = qi.bits_to_index(mask)
+    Qg = np.array(qi.gauge_transform(Q.tolist(), mask), dtype=np.int64)
+    announce("C4 gauge flip")
+    rg = q.search(dev_q(Qg))
+    assert rg.triple() == (r0.min_energy - oracle.energy(Q.tolist(), m), r0.argmin ^ m, 1)
+    announce("C4 times 3")
+    assert q.search(dev_q(3 * Q)).triple() == (3 * r0.min_energy, r0.argmin, 1)
+
+
 def test_largest_single_launch_n58(q):
     """n = 58, the largest size one launch searches: the planner's split is
     A = 32, B = 26 (a 16 GiB prefix table and 8 GiB of M_int, at the caps).
