@@ -223,7 +223,7 @@ typedef struct {
  * flags: 0 or QUBO_FLAG_COLS8.  Every entry must be finite and sum |Q_ij| at
  * most 2^100 (else QUBO_ERANGE).
  * The walk is the integer kernel's, with a binary64 anchor per column advanced
- * twice per 32-step body and the 32 states of a body one fp32 add each; a
+ * once per four 32-step bodies and every state one fp32 add; a
  * state whose fp32 energy comes within delta = 2^-14 sum |Q_ij| of the best
  * exact energy so far is re-evaluated from the definition on the GPU, so the
  * result is exactly the definition's.  Instances with many states within delta

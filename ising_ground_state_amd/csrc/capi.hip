@@ -734,8 +734,9 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
         return QUBO_EDEVICE;
 
     // A state passes the filter when its fp32 energy is within delta of the
-    // best binary64 energy so far; delta bounds (several times over) every fp32
-    // rounding of the walk and the gate, about 125 ulp(S) at 2^-24 S each.
+    // best binary64 energy so far; delta = 1024 * 2^-24 S bounds every fp32
+    // rounding of the walk, the compare and the gates (at most about
+    // 260 * 2^-24 S) almost four times over.
     const double delta = std::ldexp(S, -14);
     float delta32 = (float)delta;
     if ((double)delta32 < delta)

@@ -9,12 +9,14 @@
 //     x_i = 1 and, inside, j ascending with x_j = 1 (the definition of sec. I in
 //     one fixed order);
 //   * the walk is the integer kernel's decomposition (eq. 8, eq. 9): per column,
-//     a binary64 anchor E64 follows the walk at body granularity (two row
-//     updates per 32 steps), and inside each 32-step body the states' energies
-//     are one fp32 add each (the same 2-cycle rate as int32), re-anchored from
-//     E64 at every body so rounding never accumulates beyond 32 steps;
-//   * every fp32 rounding of the walk, the tables and the gate is bounded by a
-//     margin delta (2^-14 sum |Q_ij|, several times the worst case); a state is
+//     a binary64 anchor E64 follows the walk once per aligned group of four
+//     32-step bodies (two row updates per group), and every state's energy is
+//     one fp32 add (the same 2-cycle rate as int32), re-anchored from E64 at
+//     the start of every group, so rounding never accumulates beyond 127 steps;
+//   * with S = sum |Q_ij|, an fp32 energy is within 255 * 2^-24 S of exact
+//     (the anchor's rounding, then per step the row's and the add's) and the
+//     compare and gates add at most a few 2^-24 S more; the margin delta =
+//     2^-14 S = 1024 * 2^-24 S covers that almost four times over; a state is
 //     re-evaluated from the definition, in binary64 and in the same order as
 //     the definition, whenever its fp32 energy is within delta of the threshold T;
 //   * T only has to bound the minimum from above: it is lowered to the best
@@ -35,6 +37,10 @@ constexpr int kU = 5;  // Gray bits with rows in VGPRs (fp32)
 constexpr int kBody = 1 << kU;
 constexpr int kWaves = 4;
 constexpr int kR = 8;  // columns per lane
+// Bodies share one binary64 anchor in aligned groups of 2^kAnchorBits: inside
+// a group the fp32 walk runs on through the flips of Gray bits 5 .. 4+kAnchorBits.
+constexpr int kAnchorBits = 2;
+constexpr int kAnchorGroup = 1 << kAnchorBits;
 
 __device__ __forceinline__ uint64_t gray(uint64_t i) { return i ^ (i >> 1); }
 
@@ -233,6 +239,36 @@ __device__ __forceinline__ void step_rows(float (&E)[kR], const float (&M)[kR])
         E[r] = Plus ? E[r] + M[r] : E[r] - M[r];
 }
 
+// The flip of Gray bit t (wave-uniform; t >= kU flips no row here) with sign s
+// (+-1): one branch per row, each add an fma by +-1 (rounded once, as the add).
+__device__ __forceinline__ void flip_row(float (&E)[kR], const float (&Mr)[kU][kR], int t, float s)
+{
+    switch (t) {
+#define QUBO_FLIP_CASE(k)                          \
+    case k:                                        \
+        _Pragma("unroll") for (int r = 0; r < kR; ++r) \
+            E[r] = fmaf(Mr[k][r], s, E[r]);        \
+        break;
+        QUBO_FLIP_CASE(0)
+        QUBO_FLIP_CASE(1)
+        QUBO_FLIP_CASE(2)
+        QUBO_FLIP_CASE(3)
+        QUBO_FLIP_CASE(4)
+#undef QUBO_FLIP_CASE
+    default:
+        break;
+    }
+}
+
+// Sign of the flip leaving step m of a body (Gray bit t = ctz(m + 1)): bits
+// below kU - 1 by the step index, bit kU - 1 by the body (top_plus).
+__device__ __forceinline__ float flip_sign(int m, int t, bool top_plus)
+{
+    if (t < kU - 1)
+        return (((m + 1) >> (t + 1)) & 1) ? -1.f : 1.f;
+    return top_plus ? 1.f : -1.f;
+}
+
 // One unrolled body of 32 states: 31 fp32 row updates, every state's energy
 // kept in registers (one add per state).
 __device__ __forceinline__ void adds_body(float (&E)[kR], const float (&Mr)[kU][kR], bool top_plus)
@@ -271,12 +307,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
     __shared__ unsigned long long item_sh;
     __shared__ double rec_e[64 * kWaves];
     __shared__ uint64_t rec_c[64 * kWaves], rec_a[64 * kWaves];
+    __shared__ float carry32[kAnchorBits][kGroup];  // fp32 rows of Gray bits 5 .. 4+kAnchorBits
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int A = a.A, B = a.B;
     const uint64_t cp = a.cols_padded;
     const double *lds_lane = lds_rows64 - 4 * kGroup + lane;  // row of bit t: lds_lane + t * kGroup
+    const float *carry_lane = &carry32[0][0] + lane;  // row of bit 5+i: carry_lane + i * kGroup
 
     rec_e[threadIdx.x] = __longlong_as_double(0x7ff0000000000000LL);
     rec_c[threadIdx.x] = 0;
@@ -303,6 +341,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 const int t = 4 + k / kGroup;
                 const int col = k % kGroup;
                 lds_rows64[k] = mint[(uint64_t)(A - 1 - t) * cp + g * kGroup + col];
+            }
+            for (int k = threadIdx.x; k < kAnchorBits * kGroup; k += blockDim.x) {
+                const int t = kU + k / kGroup;
+                carry32[0][k] = t < A ? mint32[(uint64_t)(A - 1 - t) * cp + g * kGroup + k % kGroup] : 0.f;
             }
             __syncthreads();
             cur_g = (long long)g;
@@ -347,7 +389,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         // pair of bodies (bit 5 at its start), in fp32 (their rounding is in delta).
         float beta_s0 = INFINITY, beta_s1 = INFINITY, beta_p0 = INFINITY, beta_p1 = INFINITY;
         {
-            const float *row5 = mint32 + (uint64_t)(A > kU ? A - 1 - kU : 0) * cp + col0;
 #pragma unroll
             for (int r = 0; r < kR; ++r) {
                 float b = 0.f;
@@ -356,7 +397,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                     b += fminf(Mr[t][r], 0.f);
                 beta_s0 = fminf(beta_s0, b);
                 beta_s1 = fminf(beta_s1, b - Mr[kU - 1][r]);
-                const float m5 = A > kU ? row5[r * 64] : 0.f;
+                const float m5 = carry_lane[r * 64];  // 0 when A = 5
                 beta_p0 = fminf(beta_p0, b + fminf(m5, 0.f));
                 beta_p1 = fminf(beta_p1, b - fmaxf(m5, 0.f));
             }
@@ -372,15 +413,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         float epm_cur = epmin[j_begin >> kU];
         float epm_next = epmin[(j_begin >> kU) + 1];
         bool pair_clear = false;
+        float E[kR];
+        uint64_t anchor_j = j_begin;  // E64 holds the suffix energies at prefix g(anchor_j)
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
             const uint64_t base = j_begin + ((uint64_t)bi << kU);
             const bool last = bi + 1 == nbodies;
             const bool top_plus = ((base >> kU) & 1u) == 0;
             const float epm_after = epmin[(base >> kU) + 2];
-            float E[kR];
+            // The first body of an aligned group, and a unit's first body, start
+            // from the binary64 anchor E64 (rounded to nearest); the others
+            // continue the fp32 walk, so E64 moves once per group.
+            const uint32_t in_group = (uint32_t)(base >> kU) & (kAnchorGroup - 1);
+            const bool carried = in_group != 0 && bi != 0;
+            if (!carried) {
 #pragma unroll
-            for (int r = 0; r < kR; ++r)
-                E[r] = (float)E64[r];  // re-anchor (round to nearest)
+                for (int r = 0; r < kR; ++r)
+                    E[r] = (float)E64[r];
+            }
             bool check;
             if (pair_clear) {
                 check = false;
@@ -405,31 +454,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
             } else {
                 // Exact walk: every state within delta of T is re-evaluated.
                 ++slow;
-                const uint32_t neg_top = top_plus ? 0u : 0x80000000u;
                 const uint64_t colbase = g * kGroup;
                 // First pass: the body's smallest fp32 energy plus delta bounds
                 // the best exact energy in the body from above, so T (which only
                 // has to bound the minimum from above) falls to it before any
                 // state is re-evaluated.
                 {
+                    float W[kR];  // the walk on a copy: E stays at the body's first state
+#pragma unroll
+                    for (int r = 0; r < kR; ++r)
+                        W[r] = E[r];
                     float est = INFINITY;
 #pragma unroll 1
                     for (int m = 0; m < kBody; ++m) {
                         const float ep32 = (float)ep[base + (uint64_t)m];
 #pragma unroll
                         for (int r = 0; r < kR; ++r)
-                            est = fminf(est, E[r] + ep32);
+                            est = fminf(est, W[r] + ep32);
                         const int t = __builtin_ctz((unsigned)(m + 1));
-                        const uint32_t sign = (t < kU - 1) ? ((((m + 1) >> (t + 1)) & 1) ? 0x80000000u : 0u)
-                                                           : neg_top;
-#pragma unroll
-                        for (int r = 0; r < kR; ++r) {
-                            float d = 0.f;
-#pragma unroll
-                            for (int tt = 0; tt < kU; ++tt)
-                                d = (tt == t) ? Mr[tt][r] : d;
-                            E[r] += __uint_as_float(__float_as_uint(d) ^ sign);
-                        }
+                        flip_row(W, Mr, t, flip_sign(m, t, top_plus));
                     }
 #pragma unroll
                     for (int off = 32; off >= 1; off >>= 1)
@@ -438,9 +481,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                         __builtin_amdgcn_readfirstlane(__float_as_uint(est + a.delta)));
                     T = up < T ? up : T;
                     TD = (float)T + a.delta;
-#pragma unroll
-                    for (int r = 0; r < kR; ++r)
-                        E[r] = (float)E64[r];  // back to the body's first state
                 }
                 RecordF64 rec{rec_e[threadIdx.x], rec_c[threadIdx.x], rec_a[threadIdx.x]};
 #pragma unroll 1
@@ -448,37 +488,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                     const uint64_t j = base + (uint64_t)m;
                     const float ep32 = (float)ep[j];
                     const uint64_t hi = (gray(j) << B) | colbase;
+                    uint32_t hits = 0;  // columns r whose state passes the filter
 #pragma unroll
-                    for (int r = 0; r < kR; ++r) {
-                        if (E[r] + ep32 <= TD) {
-                            const uint64_t idx = hi | ((uint64_t)r << 6) | (uint64_t)lane;
-                            if ((idx & ((1ull << a.pad) - 1)) == 0) {
-                                ++candidates;
-                                const double v = energy_def(Q, a.n, idx >> a.pad);
-                                const uint64_t real = idx >> a.pad;
-                                if (v < rec.e) {
-                                    rec.e = v;
-                                    rec.cnt = 1;
-                                    rec.arg = real;
-                                } else if (v == rec.e) {
-                                    rec.cnt += 1;
-                                    rec.arg = real < rec.arg ? real : rec.arg;
-                                }
+                    for (int r = 0; r < kR; ++r)
+                        hits |= (E[r] + ep32 <= TD ? 1u : 0u) << r;
+                    while (hits) {
+                        const int r = __builtin_ctz(hits);
+                        hits &= hits - 1;
+                        const uint64_t idx = hi | ((uint64_t)r << 6) | (uint64_t)lane;
+                        if ((idx & ((1ull << a.pad) - 1)) == 0) {
+                            ++candidates;
+                            const uint64_t real = idx >> a.pad;
+                            const double v = energy_def(Q, a.n, real);
+                            if (v < rec.e) {
+                                rec.e = v;
+                                rec.cnt = 1;
+                                rec.arg = real;
+                            } else if (v == rec.e) {
+                                rec.cnt += 1;
+                                rec.arg = real < rec.arg ? real : rec.arg;
                             }
                         }
                     }
                     // flip into the next state (after the last one t = 5: no row)
                     const int t = __builtin_ctz((unsigned)(m + 1));
-                    const uint32_t sign = (t < kU - 1) ? ((((m + 1) >> (t + 1)) & 1) ? 0x80000000u : 0u)
-                                                       : neg_top;
-#pragma unroll
-                    for (int r = 0; r < kR; ++r) {
-                        float d = 0.f;
-#pragma unroll
-                        for (int tt = 0; tt < kU; ++tt)
-                            d = (tt == t) ? Mr[tt][r] : d;
-                        E[r] += __uint_as_float(__float_as_uint(d) ^ sign);
-                    }
+                    flip_row(E, Mr, t, flip_sign(m, t, top_plus));
                 }
                 rec_e[threadIdx.x] = rec.e;
                 rec_c[threadIdx.x] = rec.cnt;
@@ -491,35 +525,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 T = gb < T ? gb : T;
                 TD = (float)T + a.delta;
             }
-            // binary64 anchor to the next body: bit 4 flips inside this body,
-            // then the outer flip of Gray bit t >= 5 (after the unit's last body
-            // the anchor is not used).  fma with a wave-uniform +-1 is the signed
-            // add, rounded once, with no sign select per register.
+            // To the next body (after the unit's last body nothing is needed).
+            // Signed adds are fma with a wave-uniform +-1: rounded once, with no
+            // sign select per register.
             if (!last) {
-                const double s4 = top_plus ? 1.0 : -1.0;
                 const uint64_t next = base + kBody;
-                const int t = __builtin_ctzll(next);
-                const double st = ((next >> (t + 1)) & 1u) ? -1.0 : 1.0;
-                const double *m4 = lds_lane + 4 * kGroup;
-                double row4[kR], row[kR];
-                if (t < a.l_eff) {
-                    const double *src = lds_lane + t * kGroup;
+                if (in_group != kAnchorGroup - 1) {
+                    // inside a group: the fp32 walk flips Gray bit t (5 <= t < 5 +
+                    // kAnchorBits) into the next body (two-operand adds: a
+                    // three-register fma issues at half rate)
+                    const int t = __builtin_ctzll(next);
+                    const float *src = carry_lane + (t - kU) * kGroup;
+                    float row[kR];
 #pragma unroll
-                    for (int r = 0; r < kR; ++r) {
-                        row4[r] = m4[r * 64];
+                    for (int r = 0; r < kR; ++r)
                         row[r] = src[r * 64];
-                    }
+                    if (((next >> (t + 1)) & 1u) == 0)
+                        step_rows<true>(E, row);
+                    else
+                        step_rows<false>(E, row);
                 } else {
-                    const double *src = mint + (uint64_t)(A - 1 - t) * cp + col0;
+                    // E64 from g(anchor_j) to g(next): one signed row per differing
+                    // bit (an aligned group: Gray bit 4 + kAnchorBits and the bit
+                    // t >= 5 + kAnchorBits of the next group).
+                    const uint64_t gn = gray(next);
+                    uint64_t diff = gray(anchor_j) ^ gn;
+                    while (diff) {
+                        const int t = __builtin_ctzll(diff);
+                        diff &= diff - 1;
+                        const double st = ((gn >> t) & 1u) ? 1.0 : -1.0;
+                        double row[kR];
+                        if (t < a.l_eff) {
+                            const double *src = lds_lane + t * kGroup;
 #pragma unroll
-                    for (int r = 0; r < kR; ++r) {
-                        row4[r] = m4[r * 64];
-                        row[r] = src[r * 64];
+                            for (int r = 0; r < kR; ++r)
+                                row[r] = src[r * 64];
+                        } else {
+                            const double *src = mint + (uint64_t)(A - 1 - t) * cp + col0;
+#pragma unroll
+                            for (int r = 0; r < kR; ++r)
+                                row[r] = src[r * 64];
+                        }
+#pragma unroll
+                        for (int r = 0; r < kR; ++r)
+                            E64[r] = fma(row[r], st, E64[r]);
                     }
+                    anchor_j = next;
                 }
-#pragma unroll
-                for (int r = 0; r < kR; ++r)
-                    E64[r] = fma(row[r], st, fma(row4[r], s4, E64[r]));
             }
             epm_cur = epm_next;
             epm_next = epm_after;

@@ -120,6 +120,34 @@ def test_range_is_subcube_real(q, n, A, k):
         check_coverage(q, n, A, None, lo, hi)
 
 
+RAGGED_F64 = [(32, 96), (64, 320), (96, 160), (32, 64), (96, 96 + 32 * 9), (160, 1024 + 96),
+              (1024 + 32, 2048 - 32), (0, 2048)]
+
+
+@pytest.mark.parametrize("lo,hi", RAGGED_F64)
+def test_ragged_slices_real(q, lo, hi):
+    """Slices that start on the second, third or fourth 32-step body of an
+    aligned group of four (the binary64 anchor then starts mid-group) or end
+    inside one, with the rows of the anchor's moves in LDS or in global memory;
+    the oracle evaluates every state of the slice from the binary64 definition.
+    One real matrix (no ties) and one integer-valued (exact sums, many ties)."""
+    n, A = 16, 11
+    B = n - A
+    js = np.arange(lo, hi, dtype=np.uint64)
+    pre = (js ^ (js >> np.uint64(1))) << np.uint64(B)
+    idx = (pre[:, None] | np.arange(1 << B, dtype=np.uint64)[None, :]).ravel()
+    for Q in (real_matrix(n, 8600), np.array(qi.general_uniform(n, 8601, -3, 3), dtype=np.float64)):
+        E = oracle.energies_f64(Q, idx)
+        m = E.min()
+        want = (float(m), int(idx[E == m].min()), int((E == m).sum()))
+        Qd = dev_f(Q)
+        for cache_bits in (5, 8, 11):
+            announce("f64 ragged", lo, hi, cache_bits)
+            r = q.search_f64(Qd, prefix_bits=A, cache_bits=cache_bits, gray_lo=lo, gray_hi=hi)
+            assert r.triple() == want, (lo, hi, cache_bits)
+            check_coverage(q, n, A, None, lo, hi)
+
+
 @pytest.mark.parametrize("name", ["C1f", "C2f"])
 def test_real_configs_vs_stored_oracle(q, name):
     g = golden(name)
