@@ -256,8 +256,12 @@ typedef struct {
     uint64_t steps_total; /* 2^k * 2^(A - chunk_bits) */
     int32_t done;         /* 1 once every state has been searched */
     int32_t have_best;    /* 1 once best holds a searched state */
-    qubo_result best;     /* the combined result of the slices searched so far */
-    uint64_t reserved;    /* zero */
+    union {                         /* the combined result of the slices searched so far */
+        qubo_result best;           /* kind 0 */
+        qubo_result_f64 best_f64;   /* kind 1 */
+    };
+    uint32_t kind;        /* 0: int32 Q (qubo_progress_init), 1: binary64 Q (qubo_progress_init_f64) */
+    uint32_t reserved;    /* zero */
 } qubo_progress;
 
 /* Starts a run: fills *p for Q (device pointer, n x n int32, as for qubo_search).
@@ -279,6 +283,14 @@ QUBO_API int qubo_progress_init(const int32_t *Q, int n, int prefix_bits, int ch
  * ownership and error behaviour as qubo_search; qubo_last_timing reports the
  * step. */
 QUBO_API int qubo_search_step(const int32_t *Q, int n, void *stream, qubo_progress *p);
+
+/* The same for a binary64 Q (qubo_search_f64's definition and limits: n from
+ * 5 to 58, no outer split, so split_bits is 0).  The record has kind 1 and its
+ * result in best_f64; every later slice starts from the best energy found so
+ * far.  The int32 and binary64 steps refuse each other's records. */
+QUBO_API int qubo_progress_init_f64(const double *Q, int n, int prefix_bits, int chunk_bits, void *stream,
+                                    qubo_progress *p);
+QUBO_API int qubo_search_step_f64(const double *Q, int n, void *stream, qubo_progress *p);
 
 /* Builds the cache tables of a plan into caller-provided device buffers, for
  * inspection (sec. III.A preprocessing steps 1-3, eq. 8):

@@ -60,20 +60,27 @@ class _Plan(ctypes.Structure):
                [(name, ctypes.c_uint64) for name in ("col_groups", "work_units", "workspace_bytes")]
 
 
+class _Best(ctypes.Union):
+    _fields_ = [("best", _Result), ("best_f64", _ResultF64)]
+
+
 class Progress(ctypes.Structure):
     """The state of a search run in slices (``qubo_progress``, 96 bytes): keep it
-    between steps, e.g. as ``bytes(progress)`` in a file."""
+    between steps, e.g. as ``bytes(progress)`` in a file.  kind 0: int32 Q,
+    kind 1: binary64 Q."""
+    _anonymous_ = ("u",)
     _fields_ = [("q_hash", ctypes.c_uint64), ("n", ctypes.c_int32), ("split_bits", ctypes.c_int32),
                 ("prefix_bits", ctypes.c_int32), ("chunk_bits", ctypes.c_int32),
                 ("sub", ctypes.c_uint64), ("next", ctypes.c_uint64),
                 ("steps_done", ctypes.c_uint64), ("steps_total", ctypes.c_uint64),
-                ("done", ctypes.c_int32), ("have_best", ctypes.c_int32), ("best", _Result),
-                ("reserved", ctypes.c_uint64)]
+                ("done", ctypes.c_int32), ("have_best", ctypes.c_int32), ("u", _Best),
+                ("kind", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
     def result(self) -> "Result":
         if not self.have_best:
             raise ValueError("no state searched yet")
-        return Result(self.best.min_energy, self.best.argmin, self.best.count)
+        b = self.best_f64 if self.kind == 1 else self.best
+        return Result(b.min_energy, b.argmin, b.count)
 
 
 class _Timing(ctypes.Structure):
@@ -102,7 +109,8 @@ _lib = None
 
 EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range", "qubo_search_ex",
            "qubo_build_tables", "qubo_last_timing", "qubo_search_lowest", "qubo_search_f64",
-           "qubo_progress_init", "qubo_search_step", "qubo_strerror", "qubo_version")
+           "qubo_progress_init", "qubo_search_step", "qubo_progress_init_f64", "qubo_search_step_f64",
+           "qubo_strerror", "qubo_version")
 MAX_LOWEST = 64
 FLAG_STRICT_MIN = 1
 FLAG_COLS8 = 2
@@ -142,6 +150,9 @@ def load(path: str = LIB_PATH):
     lib.qubo_progress_init.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
                                        ctypes.c_void_p, ctypes.POINTER(Progress)]
     lib.qubo_search_step.argtypes = [i32p, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(Progress)]
+    lib.qubo_progress_init_f64.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.POINTER(Progress)]
+    lib.qubo_search_step_f64.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(Progress)]
     for name in EXPORTS:
         if name not in ("qubo_strerror", "qubo_version"):
             getattr(lib, name).restype = ctypes.c_int
@@ -275,13 +286,38 @@ def lowest(Q, k: int, prefix_bits: int | None = None, cache_bits: int | None = N
     return [(out[i].energy, out[i].index) for i in range(found.value)]
 
 
+def _is_f64(Q) -> bool:
+    import torch
+    return isinstance(Q, torch.Tensor) and Q.dtype == torch.float64
+
+
+def _device_f64(Q):
+    import torch
+    if not isinstance(Q, torch.Tensor) or not Q.is_cuda or Q.dtype != torch.float64:
+        raise TypeError("Q must be a float64 torch tensor on a HIP device")
+    if Q.dim() != 2 or Q.shape[0] != Q.shape[1]:
+        raise ValueError("Q must be square")
+    return Q.contiguous()
+
+
 def progress_init(Q, prefix_bits: int | None = None, chunk_bits: int | None = None,
                   split_bits: int | None = None, stream=None) -> Progress:
     """Starts a search run in slices of 2^chunk_bits Gray steps (default: about
-    2^48 states per step); split_bits as for search."""
+    2^48 states per step); split_bits as for search.  An int32 Q runs
+    qubo_search's definition, a float64 Q qubo_search_f64's (no split)."""
     import torch
-    Q = _device_q(Q)
     p = Progress()
+    if _is_f64(Q):
+        if split_bits:
+            raise ValueError("a binary64 run has no outer split")
+        Q = _device_f64(Q)
+        with torch.cuda.device(Q.device):
+            rc = load().qubo_progress_init_f64(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
+                                               _opt(chunk_bits), _stream(Q, stream), ctypes.byref(p))
+        if rc != QUBO_OK:
+            raise QuboError(rc, "qubo_progress_init_f64")
+        return p
+    Q = _device_q(Q)
     with torch.cuda.device(Q.device):
         rc = load().qubo_progress_init(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
                                        _opt(chunk_bits), _flags(False, None, split_bits), _stream(Q, stream),
@@ -295,12 +331,14 @@ def search_step(Q, progress: Progress, stream=None) -> bool:
     """Searches the next slice of the run and updates ``progress`` in place;
     returns progress.done."""
     import torch
-    Q = _device_q(Q)
+    f64 = _is_f64(Q)
+    Q = _device_f64(Q) if f64 else _device_q(Q)
+    name = "qubo_search_step_f64" if f64 else "qubo_search_step"
     with torch.cuda.device(Q.device):
-        rc = load().qubo_search_step(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _stream(Q, stream),
-                                     ctypes.byref(progress))
+        rc = getattr(load(), name)(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _stream(Q, stream),
+                                   ctypes.byref(progress))
     if rc != QUBO_OK:
-        raise QuboError(rc, "qubo_search_step")
+        raise QuboError(rc, name)
     return bool(progress.done)
 
 
@@ -308,8 +346,9 @@ def search_resumable(Q, path: str, prefix_bits: int | None = None, chunk_bits: i
                      split_bits: int | None = None, max_steps: int | None = None, stream=None):
     """A search that survives interruption: the run's state (96 bytes) is kept in
     the file ``path`` and rewritten atomically after every step, and a later call
-    with the same Q continues from it.  Returns the Result once every state has
-    been searched, or None after max_steps steps of an unfinished run."""
+    with the same Q continues from it.  Q is int32 or float64 (as for search and
+    search_f64).  Returns the Result once every state has been searched, or None
+    after max_steps steps of an unfinished run."""
     if os.path.exists(path):
         with open(path, "rb") as f:
             raw = f.read()

@@ -56,20 +56,36 @@ int read_q(const int32_t *Q, int n, hipStream_t stream, std::vector<int32_t> &Qh
     return QUBO_OK;
 }
 
-// FNV-1a (64 bit) over n and the entries of Q, each as 4 little-endian bytes.
-uint64_t fingerprint(const std::vector<int32_t> &Qh, int n)
+// FNV-1a (64 bit) over n (4 little-endian bytes) and the bytes of Q's entries.
+uint64_t fingerprint(const void *Qh, size_t bytes, int n)
 {
     uint64_t h = 0xcbf29ce484222325ull;
-    auto mix = [&h](uint32_t v) {
-        for (int b = 0; b < 4; ++b) {
-            h ^= (v >> (8 * b)) & 0xffu;
-            h *= 0x100000001b3ull;
-        }
+    auto mix = [&h](uint8_t b) {
+        h ^= b;
+        h *= 0x100000001b3ull;
     };
-    mix((uint32_t)n);
-    for (int32_t v : Qh)
-        mix((uint32_t)v);
+    for (int b = 0; b < 4; ++b)
+        mix((uint8_t)((uint32_t)n >> (8 * b)));
+    const uint8_t *q = static_cast<const uint8_t *>(Qh);
+    for (size_t i = 0; i < bytes; ++i)
+        mix(q[i]);
     return h;
+}
+
+// The binary64 guard: finite entries and S = sum |Q_ij| (rounded up) <= 2^100.
+int guard_f64(const std::vector<double> &Qh, double *S_out)
+{
+    double S = 0.0;
+    for (double v : Qh) {
+        if (!std::isfinite(v))
+            return QUBO_ERANGE;
+        S += std::fabs(v);
+    }
+    S *= 1.0 + 0x1p-40;  // rounding of the sum itself (at most n^2 ulp)
+    if (!(S <= 0x1p100))
+        return QUBO_ERANGE;
+    *S_out = S;
+    return QUBO_OK;
 }
 
 // Everything one call owns; released in the destructor on every path.
@@ -529,7 +545,7 @@ int run_step(const int32_t *Q, int n, hipStream_t stream, const qubo_progress &p
     const int k = p.split_bits, A = p.prefix_bits, cb = p.chunk_bits, m = n - k;
     if (k < 0 || k > kMaxSplitBits || m < kMinSearchVars || m > kMaxSingleVars || A < kRegBits ||
         A > m || A > kMaxPrefixBits || cb < kRegBits || cb > A || p.sub >= (1ull << k) ||
-        p.next >= (1ull << A) || (p.next & ((1ull << cb) - 1)) || p.steps_total == 0)
+        p.next >= (1ull << A) || (p.next & ((1ull << cb) - 1)) || p.steps_total == 0 || p.kind != 0)
         return QUBO_EINVAL;
     DeviceInfo dev;
     int rc = device_info(&dev);
@@ -539,7 +555,7 @@ int run_step(const int32_t *Q, int n, hipStream_t stream, const qubo_progress &p
     rc = read_q(Q, n, stream, Qh);
     if (rc != QUBO_OK)
         return rc;
-    if (fingerprint(Qh, n) != p.q_hash)
+    if (fingerprint(Qh.data(), Qh.size() * 4, n) != p.q_hash)
         return QUBO_EINVAL;  // not the matrix this run was started with
     std::vector<int32_t> U;
     int64_t abs_sum = 0;
@@ -625,7 +641,11 @@ struct RequestF64 {
     hipStream_t stream = nullptr;
 };
 
-int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
+// have_cap: the search only has to find states with E <= cap (a real energy
+// found elsewhere); an empty result is then valid and *found says whether any
+// state was recorded.
+int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap = false, double cap = 0.0,
+            bool *found = nullptr)
 {
     using namespace qubo;
     if (!rq.Q || !out || rq.n < 1 || rq.n > kMaxSingleVars)
@@ -664,14 +684,9 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
         hipStreamSynchronize(rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     double S = 0.0;
-    for (double v : Qh) {
-        if (!std::isfinite(v))
-            return QUBO_ERANGE;
-        S += std::fabs(v);
-    }
-    S *= 1.0 + 0x1p-40;  // rounding of the sum itself (at most n^2 ulp)
-    if (!(S <= 0x1p100))
-        return QUBO_ERANGE;
+    rc = guard_f64(Qh, &S);
+    if (rc != QUBO_OK)
+        return rc;
     // Fold to the upper triangle in binary64 (the walk's tables only; states
     // are scored against Q itself) and pad small problems.
     std::vector<double> U((size_t)ns * ns, 0.0);
@@ -742,7 +757,9 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
     if ((double)delta32 < delta)
         delta32 = std::nextafter(delta32, INFINITY);
     // The first threshold: E(0) = 0 when state 0 is searched, else above every energy.
-    const double t0 = (lo == 0) ? 0.0 : 4.0 * S + 1.0;
+    double t0 = (lo == 0) ? 0.0 : 4.0 * S + 1.0;
+    if (have_cap && cap < t0)
+        t0 = cap;
 
     if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess ||
         hipMemcpyAsync(dU, U.data(), U.size() * 8, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
@@ -808,11 +825,61 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out)
     g_timing = t;
 
     const PartialF64 &r = host_ctrl.result;
-    if (r.count == 0)
-        return QUBO_EDEVICE;  // every state passes the first threshold: some must be recorded
+    if (found)
+        *found = r.count != 0;
+    if (r.count == 0)  // without a cap every state passes the first threshold
+        return have_cap ? QUBO_OK : QUBO_EDEVICE;
     out->min_energy = r.e;
     out->argmin = r.arg;
     out->count = r.count;
+    return QUBO_OK;
+}
+
+// One step of a binary64 run: the next slice, capped by the best energy so far.
+int run_step_f64(const double *Q, int n, hipStream_t stream, const qubo_progress &p, qubo_progress *next)
+{
+    using namespace qubo;
+    const int A = p.prefix_bits, cb = p.chunk_bits;
+    if (p.kind != 1 || p.split_bits != 0 || n < kMinSearchVars || n > kMaxSingleVars || A < kRegBits ||
+        A > n || A > kMaxPrefixBits || cb < kRegBits || cb > A || p.sub != 0 || p.next >= (1ull << A) ||
+        (p.next & ((1ull << cb) - 1)) || p.steps_total == 0)
+        return QUBO_EINVAL;
+    std::vector<double> Qh((size_t)n * n);
+    if (hipMemcpyAsync(Qh.data(), Q, Qh.size() * 8, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (fingerprint(Qh.data(), Qh.size() * 8, n) != p.q_hash)
+        return QUBO_EINVAL;  // not the matrix this run was started with
+    RequestF64 rq;
+    rq.Q = Q;
+    rq.n = n;
+    rq.prefix_bits = A;
+    rq.ranged = true;
+    rq.gray_lo = p.next;
+    rq.gray_hi = p.next + (1ull << cb);
+    rq.stream = stream;
+    qubo_result_f64 r{};
+    bool found = false;
+    const int rc = run_f64(rq, &r, p.have_best != 0, p.best_f64.min_energy, &found);
+    if (rc != QUBO_OK)
+        return rc;
+    qubo_progress q = p;
+    if (found) {
+        if (!q.have_best || r.min_energy < q.best_f64.min_energy) {
+            q.best_f64 = r;
+            q.have_best = 1;
+        } else if (r.min_energy == q.best_f64.min_energy) {
+            q.best_f64.count += r.count;
+            q.best_f64.argmin = r.argmin < q.best_f64.argmin ? r.argmin : q.best_f64.argmin;
+        }
+    }
+    q.steps_done += 1;
+    q.next = p.next + (1ull << cb);
+    if (q.next == (1ull << A)) {
+        q.next = 0;
+        q.done = 1;
+    }
+    *next = q;
     return QUBO_OK;
 }
 
@@ -953,7 +1020,7 @@ QUBO_API int qubo_progress_init(const int32_t *Q, int n, int prefix_bits, int ch
     if (rc != QUBO_OK)
         return rc;
     qubo_progress q{};
-    q.q_hash = fingerprint(Qh, n);
+    q.q_hash = fingerprint(Qh.data(), Qh.size() * 4, n);
     q.n = n;
     q.split_bits = k;
     q.prefix_bits = A;
@@ -965,11 +1032,59 @@ QUBO_API int qubo_progress_init(const int32_t *Q, int n, int prefix_bits, int ch
 
 QUBO_API int qubo_search_step(const int32_t *Q, int n, void *stream, qubo_progress *p)
 {
-    if (!Q || !p || n < 1 || n > QUBO_MAX_N || p->n != n)
+    if (!Q || !p || n < 1 || n > QUBO_MAX_N || p->n != n || p->kind != 0)
         return QUBO_EINVAL;
     if (p->done)
         return QUBO_OK;
     return run_step(Q, n, static_cast<hipStream_t>(stream), *p, p);
+}
+
+QUBO_API int qubo_progress_init_f64(const double *Q, int n, int prefix_bits, int chunk_bits, void *stream,
+                                    qubo_progress *p)
+{
+    using namespace qubo;
+    if (!Q || !p || n < kMinSearchVars || n > kMaxSingleVars)
+        return QUBO_EINVAL;
+    qubo_plan plan;
+    int rc = make_plan(n, prefix_bits, -1, 256, 8, 0, &plan);
+    if (rc != QUBO_OK)
+        return rc;
+    const int A = plan.prefix_bits, B = plan.suffix_bits;
+    if (chunk_bits < 0)
+        chunk_bits = std::max(kRegBits, std::min(A, 48 - B));  // about 2^48 states per step
+    if (chunk_bits < kRegBits || chunk_bits > A)
+        return QUBO_EINVAL;
+    DeviceInfo dev;
+    rc = device_info(&dev);
+    if (rc != QUBO_OK)
+        return rc;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    std::vector<double> Qh((size_t)n * n);
+    if (hipMemcpyAsync(Qh.data(), Q, Qh.size() * 8, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return QUBO_EDEVICE;
+    double S = 0.0;
+    rc = guard_f64(Qh, &S);
+    if (rc != QUBO_OK)
+        return rc;
+    qubo_progress q{};
+    q.q_hash = fingerprint(Qh.data(), Qh.size() * 8, n);
+    q.n = n;
+    q.prefix_bits = A;
+    q.chunk_bits = chunk_bits;
+    q.steps_total = 1ull << (A - chunk_bits);
+    q.kind = 1;
+    *p = q;
+    return QUBO_OK;
+}
+
+QUBO_API int qubo_search_step_f64(const double *Q, int n, void *stream, qubo_progress *p)
+{
+    if (!Q || !p || n < 1 || n > QUBO_MAX_N || p->n != n || p->kind != 1)
+        return QUBO_EINVAL;
+    if (p->done)
+        return QUBO_OK;
+    return run_step_f64(Q, n, static_cast<hipStream_t>(stream), *p, p);
 }
 
 QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_bits,

@@ -142,7 +142,8 @@ def test_progress_record_and_rejections_before_the_device():
     offsets = {name: getattr(q.Progress, name).offset for name, _ in q.Progress._fields_}
     assert offsets == {"q_hash": 0, "n": 8, "split_bits": 12, "prefix_bits": 16, "chunk_bits": 20,
                        "sub": 24, "next": 32, "steps_done": 40, "steps_total": 48, "done": 56,
-                       "have_best": 60, "best": 64, "reserved": 88}
+                       "have_best": 60, "u": 64, "kind": 88, "reserved": 92}
+    assert q.Progress.best.offset == q.Progress.best_f64.offset == 64
     P = ctypes.c_void_p(16)
     p = q.Progress()
     assert lib.qubo_progress_init(None, 12, -1, -1, 0, None, ctypes.byref(p)) == q.QUBO_EINVAL
@@ -167,6 +168,23 @@ def test_progress_record_and_rejections_before_the_device():
     done = q.Progress(**good, done=1)
     before = bytes(done)
     assert lib.qubo_search_step(P, 12, None, ctypes.byref(done)) == q.QUBO_OK
+    assert bytes(done) == before
+    # binary64 runs: n from 5 to 58, no split; each kind's step refuses the other's record
+    for n_, pb, cb in [(4, -1, -1), (59, -1, -1), (12, 8, 4), (12, 8, 9), (12, 13, -1)]:
+        assert lib.qubo_progress_init_f64(P, n_, pb, cb, None, ctypes.byref(p)) == q.QUBO_EINVAL, (n_, pb, cb)
+    assert lib.qubo_progress_init_f64(None, 12, -1, -1, None, ctypes.byref(p)) == q.QUBO_EINVAL
+    assert lib.qubo_progress_init_f64(P, 12, -1, -1, None, None) == q.QUBO_EINVAL
+    f_good = dict(good, kind=1)
+    assert lib.qubo_search_step(P, 12, None, ctypes.byref(q.Progress(**f_good))) == q.QUBO_EINVAL
+    assert lib.qubo_search_step_f64(P, 12, None, ctypes.byref(q.Progress(**good))) == q.QUBO_EINVAL
+    for change in bad + [dict(split_bits=1)]:
+        rec = q.Progress(**{**f_good, **change})
+        before = bytes(rec)
+        assert lib.qubo_search_step_f64(P, 12, None, ctypes.byref(rec)) == q.QUBO_EINVAL, change
+        assert bytes(rec) == before
+    done = q.Progress(**f_good, done=1)
+    before = bytes(done)
+    assert lib.qubo_search_step_f64(P, 12, None, ctypes.byref(done)) == q.QUBO_OK
     assert bytes(done) == before
 
 

@@ -1,7 +1,7 @@
-"""A search run in slices (qubo_progress_init / qubo_search_step): resumed from
-its 96-byte state it gives exactly the one-call search's result, with and
-without the outer split (the straightforward split of sec. III.C.1), and
-whole sub-problems above the best energy are skipped."""
+"""A search run in slices (qubo_progress_init / qubo_search_step and their
+binary64 forms): resumed from its 96-byte state it gives exactly the one-call
+search's result, with and without the outer split (the straightforward split of
+sec. III.C.1), and whole sub-problems above the best energy are skipped."""
 from __future__ import annotations
 
 import ctypes
@@ -158,3 +158,42 @@ def test_first_step_of_n60(q):
     assert p.result().triple() == r.triple()
     del sub
     torch.cuda.synchronize()
+
+
+def test_resume_f64_from_bytes_n32(q):
+    """The real-valued n = 32 workload (C2f) in 8 slices, stopped
+    after 3 and continued from the record's bytes: the stored oracle result."""
+    import torch
+    with open(os.path.join(GOLDEN, "C2f.json")) as f:
+        g = json.load(f)
+    cfg = qi.make_config("C2f")
+    assert qi.sha256_of(cfg["Q"]) == g["sha256_Q"]
+    Qd = torch.as_tensor(np.asarray(cfg["Q"], dtype=np.float64)).to("cuda:0").contiguous()
+    announce("resumable C2f init")
+    p = q.progress_init(Qd, chunk_bits=q.make_plan(32)["prefix_bits"] - 3)
+    assert (p.kind, p.split_bits, p.steps_total) == (1, 0, 8)
+    for i in range(3):
+        announce("resumable C2f step", i)
+        q.search_step(Qd, p)
+    p2 = q.Progress.from_buffer_copy(bytes(p))
+    announce("resumable C2f rest")
+    while not q.search_step(Qd, p2):
+        pass
+    r = p2.result()
+    assert (float.hex(r.min_energy), r.argmin, r.count) == (g["min_energy_hex"], g["argmin"], g["count"])
+    with pytest.raises(q.QuboError) as e:  # an int32 step refuses a binary64 record
+        q.search_step(dev_q(np.zeros((32, 32))), p2)
+    assert e.value.code == q.QUBO_EINVAL
+
+
+def test_search_resumable_file_f64(q, tmp_path):
+    import torch
+    n = 20
+    rng = np.random.default_rng(9301)
+    Q = rng.uniform(-10.0, 10.0, size=(n, n))
+    want = oracle.search_direct_f64(Q).triple()
+    Qd = torch.as_tensor(Q).to("cuda:0").contiguous()
+    path = str(tmp_path / "run_f64.qubo")
+    announce("resumable file f64")
+    assert q.search_resumable(Qd, path, chunk_bits=6, max_steps=3) is None
+    assert q.search_resumable(Qd, path).triple() == want
