@@ -122,8 +122,14 @@ int make_plan(int n_total, int prefix_bits, int cache_bits, int num_cus, int col
         if (A < kRegBits)
             return QUBO_EPLAN;
     } else {
-        // Aim for a 2^28-entry (1 GiB) prefix table and at least one full column group.
-        int B = std::max(std::min(ns - kRegBits, 10), ns - 28);
+        // 2^16 suffix columns (128 column groups), fewer for small n, more
+        // where the prefix table would pass 2^28 entries (1 GiB): n = 48 and 50
+        // take A = 28, n = 40 A = 24, n = 32 A = 16, n = 24 A = 8.  Measured
+        // splits (whole searches on the MI355X): A = 24 is the fastest at
+        // n = 40 (17.5 ms against 25.1 ms at A = 28, which spends 7 ms building
+        // its prefix table), A = 8 at n = 24; at n = 32, A = 16 is within 20 %
+        // of the fastest (A = 18).
+        int B = std::max(std::min(ns - kRegBits, 16), ns - 28);
         A = ns - B;
         while (A < kMaxPrefixBits && (uint64_t)A * 4ull * (1ull << (ns - A)) > kMaxMintBytes)
             ++A;
@@ -161,6 +167,10 @@ int make_plan(int n_total, int prefix_bits, int cache_bits, int num_cus, int col
     if (target_units > p.col_groups)
         split = ceil_log2((target_units + p.col_groups - 1) / p.col_groups);
     int c = A - split;
+    // but at least 2^10 steps (32 bodies) per unit where the walk is that long:
+    // a unit's start (its anchor rows and register rows from memory) must stay
+    // small against its walk, even when fewer units than resident waves result
+    c = std::max(c, std::min(A, kMinSegBits));
     c = std::max(c, kRegBits);
     c = std::min(c, kMaxSegBits);
     c = std::min(c, A);

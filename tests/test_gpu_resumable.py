@@ -74,10 +74,9 @@ def test_outer_split_in_slices(q, n, k, seed):
     want = oracle.search_gray(Q).triple()
     Qd = dev_q(Q)
     announce("resumable split", n, k)
-    p = q.progress_init(Qd, chunk_bits=8, split_bits=k)
-    m = n - k
-    A = q.make_plan(m)["prefix_bits"]
-    assert (p.split_bits, p.prefix_bits, p.steps_total) == (k, A, (1 << k) << (A - 8))
+    A = 12  # 8 slices of 2^9 Gray steps per sub-problem
+    p = q.progress_init(Qd, prefix_bits=A, chunk_bits=9, split_bits=k)
+    assert (p.split_bits, p.prefix_bits, p.steps_total) == (k, A, (1 << k) << (A - 9))
     run_all(q, Qd, p)
     assert p.steps_done == p.steps_total
     assert p.result().triple() == want
@@ -108,7 +107,7 @@ def test_other_matrix_refused(q):
     Q2[3][7] += 1
     Qd1, Qd2 = dev_q(Q1), dev_q(Q2)
     announce("resumable fingerprint")
-    p = q.progress_init(Qd1, chunk_bits=6)
+    p = q.progress_init(Qd1, prefix_bits=10, chunk_bits=6)
     before = bytes(p)
     with pytest.raises(q.QuboError) as e:
         q.search_step(Qd2, p)
@@ -127,7 +126,7 @@ def test_search_resumable_file(q, tmp_path):
     Qd = dev_q(Q)
     path = str(tmp_path / "run.qubo")
     announce("resumable file")
-    assert q.search_resumable(Qd, path, chunk_bits=10, max_steps=2) is None
+    assert q.search_resumable(Qd, path, prefix_bits=16, chunk_bits=10, max_steps=2) is None
     assert os.path.getsize(path) == 96
     p = q.Progress.from_buffer_copy(open(path, "rb").read())
     assert p.steps_done == 2 and not p.done
@@ -195,5 +194,5 @@ def test_search_resumable_file_f64(q, tmp_path):
     Qd = torch.as_tensor(Q).to("cuda:0").contiguous()
     path = str(tmp_path / "run_f64.qubo")
     announce("resumable file f64")
-    assert q.search_resumable(Qd, path, chunk_bits=6, max_steps=3) is None
+    assert q.search_resumable(Qd, path, prefix_bits=10, chunk_bits=6, max_steps=3) is None
     assert q.search_resumable(Qd, path).triple() == want
