@@ -70,9 +70,20 @@ __device__ __forceinline__ double from_key(long long k)
 
 __device__ __forceinline__ float fmin3(float a, float b, float c) { return fminf(fminf(a, b), c); }
 
+// Minimum of two wave-uniform floats (never NaN) on the scalar unit: the
+// integer keys b ^ ((b >> 31) & 0x7fffffff) order floats as their values.
+__device__ __forceinline__ float uniform_fmin(float a, float b)
+{
+    const int ia = __float_as_int(a), ib = __float_as_int(b);
+    const int ka = ia ^ ((ia >> 31) & 0x7fffffff), kb = ib ^ ((ib >> 31) & 0x7fffffff);
+    return __int_as_float(ka < kb ? ia : ib);  // an integer select stays scalar
+}
+
 __device__ __forceinline__ float row_min8(const float (&E)[kR])
 {
-    return fminf(fminf(fmin3(E[0], E[1], E[2]), fmin3(E[3], E[4], E[5])), fminf(E[6], E[7]));
+    // four three-input minima (E[5] twice): a two-input fminf would first
+    // canonicalise its operands (two more instructions)
+    return fmin3(fmin3(E[0], E[1], E[2]), fmin3(E[3], E[4], E[5]), fmin3(E[5], E[6], E[7]));
 }
 
 // The definition for one state: binary64, i ascending, j ascending, over the
@@ -439,7 +450,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 if (top_plus && !last && A > kU) {
                     const float bp = emin + (((base >> (kU + 1)) & 1u) ? beta_p1 : beta_p0);
                     pair_clear =
-                        __builtin_amdgcn_ballot_w64(bp + fminf(epm_cur, epm_next) <= TD) == 0;
+                        __builtin_amdgcn_ballot_w64(bp + uniform_fmin(epm_cur, epm_next) <= TD) == 0;
                 }
                 if (pair_clear) {
                     check = false;
