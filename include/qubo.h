@@ -284,6 +284,24 @@ QUBO_API int qubo_progress_init(const int32_t *Q, int n, int prefix_bits, int ch
  * step. */
 QUBO_API int qubo_search_step(const int32_t *Q, int n, void *stream, qubo_progress *p);
 
+/* A spectrum run in steps (the k lowest states, as qubo_search_lowest): the
+ * run's header (kind 2; its best is unused) and the k lowest states found so
+ * far (1128 bytes, no pointers).  Once k states are known, their k-th energy
+ * caps every later slice and a sub-problem wholly above it is skipped. */
+typedef struct {
+    qubo_progress head;
+    int32_t k;                               /* 1 .. QUBO_MAX_LOWEST */
+    int32_t found;                           /* entries of states[] in use (<= k) */
+    qubo_state states[QUBO_MAX_LOWEST];      /* (energy, index) ascending */
+} qubo_progress_lowest;
+
+/* Starts a spectrum run: arguments as for qubo_progress_init, plus k. */
+QUBO_API int qubo_progress_init_lowest(const int32_t *Q, int n, int k, int prefix_bits, int chunk_bits,
+                                       uint32_t flags, void *stream, qubo_progress_lowest *p);
+/* Searches the next slice and merges its k lowest states into p->states; once
+ * p->head.done is 1, states[0 .. found) is exactly qubo_search_lowest's list. */
+QUBO_API int qubo_search_step_lowest(const int32_t *Q, int n, void *stream, qubo_progress_lowest *p);
+
 /* The same for a binary64 Q (qubo_search_f64's definition and limits: n from
  * 5 to 58, no outer split, so split_bits is 0).  The record has kind 1 and its
  * result in best_f64; every later slice starts from the best energy found so

@@ -83,6 +83,20 @@ class Progress(ctypes.Structure):
         return Result(b.min_energy, b.argmin, b.count)
 
 
+class ProgressLowest(ctypes.Structure):
+    """The state of a spectrum run in slices (``qubo_progress_lowest``, 1128
+    bytes): the run's header (kind 2) and the k lowest states found so far."""
+    _fields_ = [("head", Progress), ("k", ctypes.c_int32), ("found", ctypes.c_int32),
+                ("states", _State * 64)]
+
+    @property
+    def done(self) -> bool:
+        return bool(self.head.done)
+
+    def result(self) -> list[tuple[int, int]]:
+        return [(self.states[i].energy, self.states[i].index) for i in range(self.found)]
+
+
 class _Timing(ctypes.Structure):
     _fields_ = [("build_ms", ctypes.c_float), ("search_ms", ctypes.c_float),
                 ("reduce_ms", ctypes.c_float), ("total_ms", ctypes.c_float),
@@ -109,8 +123,8 @@ _lib = None
 
 EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range", "qubo_search_ex",
            "qubo_build_tables", "qubo_last_timing", "qubo_search_lowest", "qubo_search_f64",
-           "qubo_progress_init", "qubo_search_step", "qubo_progress_init_f64", "qubo_search_step_f64",
-           "qubo_strerror", "qubo_version")
+           "qubo_progress_init", "qubo_search_step", "qubo_progress_init_lowest", "qubo_search_step_lowest",
+           "qubo_progress_init_f64", "qubo_search_step_f64", "qubo_strerror", "qubo_version")
 MAX_LOWEST = 64
 FLAG_STRICT_MIN = 1
 FLAG_COLS8 = 2
@@ -150,6 +164,9 @@ def load(path: str = LIB_PATH):
     lib.qubo_progress_init.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
                                        ctypes.c_void_p, ctypes.POINTER(Progress)]
     lib.qubo_search_step.argtypes = [i32p, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(Progress)]
+    lib.qubo_progress_init_lowest.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_uint32, ctypes.c_void_p, ctypes.POINTER(ProgressLowest)]
+    lib.qubo_search_step_lowest.argtypes = [i32p, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ProgressLowest)]
     lib.qubo_progress_init_f64.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_void_p, ctypes.POINTER(Progress)]
     lib.qubo_search_step_f64.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(Progress)]
@@ -301,11 +318,23 @@ def _device_f64(Q):
 
 
 def progress_init(Q, prefix_bits: int | None = None, chunk_bits: int | None = None,
-                  split_bits: int | None = None, stream=None) -> Progress:
+                  split_bits: int | None = None, stream=None, k: int | None = None):
     """Starts a search run in slices of 2^chunk_bits Gray steps (default: about
     2^48 states per step); split_bits as for search.  An int32 Q runs
-    qubo_search's definition, a float64 Q qubo_search_f64's (no split)."""
+    qubo_search's definition (with k: qubo_search_lowest's k lowest states,
+    returning a ProgressLowest), a float64 Q qubo_search_f64's (no split)."""
     import torch
+    if k is not None:
+        Q = _device_q(Q)
+        pl = ProgressLowest()
+        with torch.cuda.device(Q.device):
+            rc = load().qubo_progress_init_lowest(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], int(k),
+                                                  _opt(prefix_bits), _opt(chunk_bits),
+                                                  _flags(False, None, split_bits), _stream(Q, stream),
+                                                  ctypes.byref(pl))
+        if rc != QUBO_OK:
+            raise QuboError(rc, "qubo_progress_init_lowest")
+        return pl
     p = Progress()
     if _is_f64(Q):
         if split_bits:
@@ -327,13 +356,16 @@ def progress_init(Q, prefix_bits: int | None = None, chunk_bits: int | None = No
     return p
 
 
-def search_step(Q, progress: Progress, stream=None) -> bool:
-    """Searches the next slice of the run and updates ``progress`` in place;
-    returns progress.done."""
+def search_step(Q, progress, stream=None) -> bool:
+    """Searches the next slice of the run and updates ``progress`` (a Progress
+    or a ProgressLowest) in place; returns whether the run is done."""
     import torch
     f64 = _is_f64(Q)
     Q = _device_f64(Q) if f64 else _device_q(Q)
-    name = "qubo_search_step_f64" if f64 else "qubo_search_step"
+    if isinstance(progress, ProgressLowest):
+        name = "qubo_search_step_lowest"
+    else:
+        name = "qubo_search_step_f64" if f64 else "qubo_search_step"
     with torch.cuda.device(Q.device):
         rc = getattr(load(), name)(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _stream(Q, stream),
                                    ctypes.byref(progress))
@@ -343,20 +375,23 @@ def search_step(Q, progress: Progress, stream=None) -> bool:
 
 
 def search_resumable(Q, path: str, prefix_bits: int | None = None, chunk_bits: int | None = None,
-                     split_bits: int | None = None, max_steps: int | None = None, stream=None):
-    """A search that survives interruption: the run's state (96 bytes) is kept in
-    the file ``path`` and rewritten atomically after every step, and a later call
-    with the same Q continues from it.  Q is int32 or float64 (as for search and
-    search_f64).  Returns the Result once every state has been searched, or None
-    after max_steps steps of an unfinished run."""
+                     split_bits: int | None = None, max_steps: int | None = None, stream=None,
+                     k: int | None = None):
+    """A search that survives interruption: the run's state (96 bytes; 1128 for
+    a spectrum run, k given) is kept in the file ``path`` and rewritten
+    atomically after every step, and a later call with the same Q continues
+    from it.  Q is int32 or float64 (as for search and search_f64).  Returns the
+    Result (the k lowest states for a spectrum run) once every state has been
+    searched, or None after max_steps steps of an unfinished run."""
+    kind = ProgressLowest if k is not None else Progress
     if os.path.exists(path):
         with open(path, "rb") as f:
             raw = f.read()
-        if len(raw) != ctypes.sizeof(Progress):
-            raise ValueError("%s is not a search state (%d bytes)" % (path, len(raw)))
-        p = Progress.from_buffer_copy(raw)
+        if len(raw) != ctypes.sizeof(kind):
+            raise ValueError("%s is not a search state of this kind (%d bytes)" % (path, len(raw)))
+        p = kind.from_buffer_copy(raw)
     else:
-        p = progress_init(Q, prefix_bits, chunk_bits, split_bits, stream)
+        p = progress_init(Q, prefix_bits, chunk_bits, split_bits, stream, k=k)
         _save_progress(path, p)
     steps = 0
     while not p.done and (max_steps is None or steps < max_steps):
@@ -366,7 +401,7 @@ def search_resumable(Q, path: str, prefix_bits: int | None = None, chunk_bits: i
     return p.result() if p.done else None
 
 
-def _save_progress(path: str, p: Progress) -> None:
+def _save_progress(path: str, p) -> None:
     tmp = path + ".tmp"
     with open(tmp, "wb") as f:
         f.write(bytes(p))

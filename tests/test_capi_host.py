@@ -188,6 +188,36 @@ def test_progress_record_and_rejections_before_the_device():
     assert bytes(done) == before
 
 
+def test_spectrum_progress_record_and_rejections():
+    """The spectrum run's record: the 96-byte header, k, found and 64 states;
+    malformed arguments and records are refused before any device call."""
+    lib = q.load()
+    assert ctypes.sizeof(q.ProgressLowest) == 1128
+    assert (q.ProgressLowest.head.offset, q.ProgressLowest.k.offset, q.ProgressLowest.found.offset,
+            q.ProgressLowest.states.offset) == (0, 96, 100, 104)
+    P = ctypes.c_void_p(16)
+    pl = q.ProgressLowest()
+    for k in (0, 65):
+        assert lib.qubo_progress_init_lowest(P, 12, k, -1, -1, 0, None, ctypes.byref(pl)) == q.QUBO_EINVAL
+    assert lib.qubo_progress_init_lowest(P, 12, 4, -1, -1, 0, None, None) == q.QUBO_EINVAL
+    assert lib.qubo_progress_init_lowest(None, 12, 4, -1, -1, 0, None, ctypes.byref(pl)) == q.QUBO_EINVAL
+    assert lib.qubo_progress_init_lowest(P, 12, 4, 8, 4, 0, None, ctypes.byref(pl)) == q.QUBO_EINVAL
+    assert bytes(pl) == bytes(1128)
+    head = dict(n=12, split_bits=0, prefix_bits=8, chunk_bits=6, steps_total=4, kind=2)
+    for h, k, found in [(dict(head, kind=0), 4, 0), (head, 0, 0), (head, 65, 0), (head, 4, 5), (head, 4, -1),
+                        (dict(head, chunk_bits=9), 4, 0), (dict(head, n=13), 4, 0)]:
+        rec = q.ProgressLowest(head=q.Progress(**h), k=k, found=found)
+        before = bytes(rec)
+        assert lib.qubo_search_step_lowest(P, 12, None, ctypes.byref(rec)) == q.QUBO_EINVAL, (h, k, found)
+        assert bytes(rec) == before
+    # a spectrum record is not a minimum record, and a finished run's step does nothing
+    assert lib.qubo_search_step(P, 12, None, ctypes.byref(q.Progress(**head))) == q.QUBO_EINVAL
+    done = q.ProgressLowest(head=q.Progress(**dict(head, done=1)), k=4)
+    before = bytes(done)
+    assert lib.qubo_search_step_lowest(P, 12, None, ctypes.byref(done)) == q.QUBO_OK
+    assert bytes(done) == before
+
+
 def test_timing_struct_before_any_search():
     t = q.last_timing()
     assert set(t) >= {"build_ms", "search_ms", "reduce_ms", "total_ms", "states", "slow_bodies"}

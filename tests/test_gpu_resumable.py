@@ -196,3 +196,60 @@ def test_search_resumable_file_f64(q, tmp_path):
     announce("resumable file f64")
     assert q.search_resumable(Qd, path, prefix_bits=10, chunk_bits=6, max_steps=3) is None
     assert q.search_resumable(Qd, path).triple() == want
+
+
+def test_spectrum_run_resumed_n32(q):
+    """The 64 lowest states of C2 (n=32) in 8 slices, stopped after 3 and
+    continued from the record's bytes: the stored oracle list."""
+    with open(os.path.join(GOLDEN, "C2low.json")) as f:
+        g = json.load(f)
+    cfg = qi.make_config("C2")
+    assert qi.sha256_of(cfg["Q"]) == g["sha256_Q"]
+    Qd = dev_q(cfg["Q"])
+    A = q.make_plan(32)["prefix_bits"]
+    announce("spectrum run C2 init")
+    p = q.progress_init(Qd, chunk_bits=A - 3, k=64)
+    assert (p.head.kind, p.k, p.found, p.head.steps_total) == (2, 64, 0, 8)
+    for i in range(3):
+        announce("spectrum run C2 step", i)
+        assert not q.search_step(Qd, p)
+    p2 = q.ProgressLowest.from_buffer_copy(bytes(p))
+    announce("spectrum run C2 rest")
+    while not q.search_step(Qd, p2):
+        pass
+    assert p2.result() == [(int(e), int(i)) for e, i in g["states"]]
+    assert p2.result() == q.lowest(Qd, 64)
+
+
+@pytest.mark.parametrize("n,k,seed", [(24, 2, 9401), (22, 3, 9402)])
+def test_spectrum_run_split(q, n, k, seed):
+    Q = qi.general_uniform(n, seed, -3, 3)  # heavy ties: the list's order decides
+    want = [tuple(map(int, s)) for s in oracle.lowest(Q, 40)]
+    Qd = dev_q(Q)
+    announce("spectrum run split", n, k)
+    p = q.progress_init(Qd, prefix_bits=12, chunk_bits=9, split_bits=k, k=40)
+    while not q.search_step(Qd, p):
+        pass
+    assert p.head.steps_done == p.head.steps_total == (1 << k) << 3
+    assert p.result() == want
+
+
+def test_spectrum_run_skips_sub_problems(q, tmp_path):
+    """With +100000 on variable 0, once the x_0 = 0 half has filled the list,
+    the x_0 = 1 sub-problem lies above its 8th energy and is skipped; the file
+    loop gives the same list."""
+    n = 22
+    Q = np.array(qi.symmetric_uniform(n, 9403, -100, 100), dtype=np.int64)
+    Q[0, 0] = 100000
+    want = [tuple(map(int, s)) for s in oracle.lowest(Q.tolist(), 8)]
+    Qd = dev_q(Q)
+    announce("spectrum run skip")
+    p = q.progress_init(Qd, chunk_bits=q.make_plan(n - 1)["prefix_bits"], split_bits=1, k=8)
+    assert not q.search_step(Qd, p)
+    assert q.search_step(Qd, p)
+    assert q.last_timing()["states"] == 0  # skipped: nothing launched
+    assert p.result() == want
+    path = str(tmp_path / "spectrum.qubo")
+    assert q.search_resumable(Qd, path, split_bits=1, k=8, max_steps=1) is None
+    assert os.path.getsize(path) == 1128
+    assert q.search_resumable(Qd, path, split_bits=1, k=8) == want
