@@ -219,11 +219,11 @@ typedef struct {
 } qubo_result_f64;
 /* Q: device pointer, n x n binary64, row-major; read only.  n: 1..58 (no
  * outer split).  prefix_bits, cache_bits, gray_lo, gray_hi, stream: as for
- * qubo_search_ex (cache_bits defaults to min(A, 11): binary64 rows in LDS).
+ * qubo_search_ex (cache_bits defaults to min(A, 10): binary64 rows in LDS).
  * flags: 0 or QUBO_FLAG_COLS8.  Every entry must be finite and sum |Q_ij| at
  * most 2^100 (else QUBO_ERANGE).
  * The walk is the integer kernel's, with a binary64 anchor per column advanced
- * once per four 32-step bodies and every state one fp32 add; a
+ * once per eight 32-step bodies and every state one fp32 add; a
  * state whose fp32 energy comes within delta = 2^-14 sum |Q_ij| of the best
  * exact energy so far is re-evaluated from the definition on the GPU, so the
  * result is exactly the definition's.  Instances with many states within delta

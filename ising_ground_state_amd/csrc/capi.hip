@@ -741,14 +741,15 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap = false, d
         return QUBO_EINVAL;
     const int n = rq.n;
     // The binary64 rows of Gray bits 4 .. l-1 sit in LDS (4 KiB each per
-    // workgroup): the default keeps 7 of them.
+    // workgroup): the default keeps 6 of them, so that with the fp32 rows of
+    // the walk's carries four workgroups fit a CU.
     int cache_bits = rq.cache_bits;
     if (cache_bits < 0 && n >= kMinSearchVars) {  // (tiny problems: the planner's fixed split)
         qubo_plan probe;
         const int rc0 = make_plan(n, rq.prefix_bits, -1, 256, 8, 0, &probe);
         if (rc0 != QUBO_OK)
             return rc0;
-        cache_bits = probe.prefix_bits < 11 ? probe.prefix_bits : 11;
+        cache_bits = probe.prefix_bits < 10 ? probe.prefix_bits : 10;
     }
     DeviceInfo dev;
     int rc = device_info(&dev);
@@ -840,7 +841,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap = false, d
     // A state passes the filter when its fp32 energy is within delta of the
     // best binary64 energy so far; delta = 1024 * 2^-24 S bounds every fp32
     // rounding of the walk, the compare and the gates (at most about
-    // 260 * 2^-24 S) almost four times over.
+    // 290 * 2^-24 S) more than three times over.
     const double delta = std::ldexp(S, -14);
     float delta32 = (float)delta;
     if ((double)delta32 < delta)

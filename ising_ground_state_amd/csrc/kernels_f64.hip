@@ -9,13 +9,16 @@
 //     x_i = 1 and, inside, j ascending with x_j = 1 (the definition of sec. I in
 //     one fixed order);
 //   * the walk is the integer kernel's decomposition (eq. 8, eq. 9): per column,
-//     a binary64 anchor E64 follows the walk once per aligned group of four
+//     a binary64 anchor E64 follows the walk once per aligned group of eight
 //     32-step bodies (two row updates per group), and every state's energy is
 //     one fp32 add (the same 2-cycle rate as int32), re-anchored from E64 at
-//     the start of every group, so rounding never accumulates beyond 127 steps;
-//   * with S = sum |Q_ij|, an fp32 energy is within 255 * 2^-24 S of exact
-//     (the anchor's rounding, then per step the row's and the add's) and the
-//     compare and gates add at most a few 2^-24 S more; the margin delta =
+//     the start of every group, so at most 255 fp32 adds separate a state
+//     from its anchor;
+//   * with S = sum |Q_ij|, an fp32 energy is within 257 * 2^-24 S of exact:
+//     the anchor's rounding, each add's (the sums stay below S), and the rows'
+//     rounding to fp32 once (a state differs from its anchor by each row at
+//     most once, and the rows of one column sum to at most S in magnitude);
+//     the compare and gates add a few 2^-24 S more, and the margin delta =
 //     2^-14 S = 1024 * 2^-24 S covers that almost four times over; a state is
 //     re-evaluated from the definition, in binary64 and in the same order as
 //     the definition, whenever its fp32 energy is within delta of the threshold T;
@@ -38,8 +41,9 @@ constexpr int kBody = 1 << kU;
 constexpr int kWaves = 4;
 constexpr int kR = 8;  // columns per lane
 // Bodies share one binary64 anchor in aligned groups of 2^kAnchorBits: inside
-// a group the fp32 walk runs on through the flips of Gray bits 5 .. 4+kAnchorBits.
-constexpr int kAnchorBits = 2;
+// a group the fp32 walk runs on through the flips of Gray bits 5 .. 4+kAnchorBits
+// (fp32 rows in LDS).
+constexpr int kAnchorBits = 3;
 constexpr int kAnchorGroup = 1 << kAnchorBits;
 
 __device__ __forceinline__ uint64_t gray(uint64_t i) { return i ^ (i >> 1); }
