@@ -176,6 +176,22 @@ def test_real_subcubes_at_full_size(q):
                                                                  cube["count"]), top
 
 
+def test_real_full_size_whole_space(q):
+    """The whole n = 48 real-valued workload (C4f), checked by what holds at
+    any size: the oracle's binary64 energy of the reported minimiser is the
+    reported minimum, no single flip of it is lower, and every 32-step body was
+    walked once per column group."""
+    cfg = qi.make_config("C4f")
+    Q = np.asarray(cfg["Q"], dtype=np.float64)
+    announce("f64 C4f whole space")
+    r = q.search_f64(dev_f(Q))
+    check_coverage(q, 48)
+    assert r.count >= 1
+    assert oracle.energy_f64(Q, r.argmin) == r.min_energy
+    flips = np.asarray([r.argmin ^ (1 << k) for k in range(48)], dtype=np.uint64)
+    assert (oracle.energies_f64(Q, flips) >= r.min_energy).all()
+
+
 def test_integer_valued_full_size(q):
     """The n = 48 integer workload as binary64 gives the integer kernel's triple."""
     import torch
