@@ -132,6 +132,10 @@ class Oracle:
         lib.oracle_search_direct_f64.argtypes = [f64p, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
                                                  ctypes.c_int, ctypes.POINTER(_ResultF64)]
         lib.oracle_search_direct_f64.restype = ctypes.c_int
+        lib.oracle_lowest_f64.argtypes = [f64p, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                                          ctypes.c_int, f64p, ctypes.POINTER(ctypes.c_uint64),
+                                          ctypes.POINTER(ctypes.c_int)]
+        lib.oracle_lowest_f64.restype = ctypes.c_int
         lib.oracle_version.restype = ctypes.c_char_p
         self.lib = lib
         self.path = path
@@ -214,6 +218,23 @@ class Oracle:
             raise ValueError("oracle_search_direct_f64 failed (%d)" % rc)
         return ResultF64(r.min_energy, r.argmin, r.count, r.max_abs_energy)
 
+    def lowest_f64(self, Q, k: int, lo: int = 0, hi: int | None = None,
+                   threads: int | None = None) -> list[tuple[float, int]]:
+        """Tier A for a float64 Q: the k lowest states of the indices [lo, hi)
+        as (E, index) pairs, ordered by E then index."""
+        q = _farray(Q)
+        n = q.shape[0]
+        if hi is None:
+            hi = 1 << n
+        e = np.zeros(k, dtype=np.float64)
+        ix = np.zeros(k, dtype=np.uint64)
+        found = ctypes.c_int(0)
+        rc = self.lib.oracle_lowest_f64(_fptr(q), n, k, lo, hi, threads or default_threads(), _fptr(e),
+                                        ix.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), ctypes.byref(found))
+        if rc != 0:
+            raise ValueError("oracle_lowest_f64 failed (%d)" % rc)
+        return [(float(e[i]), int(ix[i])) for i in range(found.value)]
+
     def version(self) -> str:
         return self.lib.oracle_version().decode()
 
@@ -261,6 +282,11 @@ def energies_f64(Q, idx) -> np.ndarray:
 
 def search_direct_f64(Q, lo: int = 0, hi: int | None = None, threads: int | None = None) -> ResultF64:
     return default().search_direct_f64(Q, lo, hi, threads)
+
+
+def lowest_f64(Q, k: int, lo: int = 0, hi: int | None = None,
+               threads: int | None = None) -> list[tuple[float, int]]:
+    return default().lowest_f64(Q, k, lo, hi, threads)
 
 
 def version() -> str:

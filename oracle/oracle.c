@@ -545,4 +545,100 @@ int oracle_search_direct_f64(const double *Q, int n, uint64_t lo, uint64_t hi, i
     return 0;
 }
 
-const char *oracle_version(void) { return "qubo-oracle 2 (tier A direct, tier B Gray; fp64 tier A)"; }
+/* The k lowest states of a floating-point Q: the first k states in the order
+ * (E ascending, index ascending) with E the fixed-order binary64 sum above,
+ * each thread keeping its own sorted list over a contiguous index range and
+ * the lists merged by the same order. */
+typedef struct {
+    double e;
+    uint64_t idx;
+} oracle_state_f64;
+
+static int state_less_f64(const oracle_state_f64 *a, double e, uint64_t idx)
+{
+    /* MUTANT(13), with the merge below: equal energies stay in the order met */
+    return a->e < e || (a->e == e && (MUTANT(13) || a->idx < idx));
+}
+
+static void keep_lowest_f64(oracle_state_f64 *l, int *len, int k, double e, uint64_t idx)
+{
+    int pos = *len;
+    while (pos > 0 && !state_less_f64(&l[pos - 1], e, idx))
+        --pos;
+    if (pos >= k)
+        return;
+    int last = *len < k ? *len : k - 1;
+    for (int i = last; i > pos; --i)
+        l[i] = l[i - 1];
+    l[pos].e = e;
+    l[pos].idx = idx;
+    if (*len < k)
+        ++*len;
+}
+
+typedef struct {
+    const double *Q;
+    int n, k;
+    uint64_t lo, hi;
+    int len;
+    oracle_state_f64 list[ORACLE_MAX_LOWEST];
+} lowest_job_f64;
+
+static void *lowest_worker_f64(void *arg)
+{
+    lowest_job_f64 *job = (lowest_job_f64 *)arg;
+    job->len = 0;
+    for (uint64_t idx = job->lo; idx < job->hi; ++idx)
+        keep_lowest_f64(job->list, &job->len, job->k, oracle_energy_f64(job->Q, job->n, idx), idx);
+    return NULL;
+}
+
+int oracle_lowest_f64(const double *Q, int n, int k, uint64_t lo, uint64_t hi, int threads,
+                      double *energies, uint64_t *indices, int *found)
+{
+    if (!Q || !energies || !indices || !found || n < 1 || n > ORACLE_MAX_N || k < 1 ||
+        k > ORACLE_MAX_LOWEST)
+        return -1;
+    if (hi > (1ull << n) || lo > hi)
+        return -1;
+    threads = clamp_threads(threads);
+    const uint64_t span = hi - lo;
+    if ((uint64_t)threads > span)
+        threads = span ? (int)span : 1;
+    lowest_job_f64 *jobs = (lowest_job_f64 *)calloc((size_t)threads, sizeof(lowest_job_f64));
+    pthread_t *tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    if (!jobs || !tids) {
+        free(jobs);
+        free(tids);
+        return -2;
+    }
+    for (int t = 0; t < threads; ++t) {
+        jobs[t].Q = Q;
+        jobs[t].n = n;
+        jobs[t].k = k;
+        jobs[t].lo = lo + span * (uint64_t)t / (uint64_t)threads;
+        jobs[t].hi = lo + span * (uint64_t)(t + 1) / (uint64_t)threads;
+    }
+    for (int t = 1; t < threads; ++t)
+        pthread_create(&tids[t], NULL, lowest_worker_f64, &jobs[t]);
+    lowest_worker_f64(&jobs[0]);
+    for (int t = 1; t < threads; ++t)
+        pthread_join(tids[t], NULL);
+    oracle_state_f64 merged[ORACLE_MAX_LOWEST];
+    int len = 0;
+    for (int s = 0; s < threads; ++s) {
+        const int t = MUTANT(13) ? threads - 1 - s : s; /* MUTANT(13): last thread's list first */
+        for (int i = 0; i < jobs[t].len; ++i)
+            keep_lowest_f64(merged, &len, k, jobs[t].list[i].e, jobs[t].list[i].idx);
+    }
+    for (int i = 0; i < len; ++i) {
+        energies[i] = merged[i].e;
+        indices[i] = merged[i].idx;
+    }
+    *found = len;
+    free(jobs);
+    free(tids);
+    return 0;
+}
+
+const char *oracle_version(void) { return "qubo-oracle 3 (tier A direct, tier B Gray; fp64 tier A and k lowest)"; }

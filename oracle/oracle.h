@@ -55,6 +55,10 @@ void oracle_energy_many_f64(const double *Q, int n, const uint64_t *idx, uint64_
 /* Tier A over idx in [lo, hi). */
 int oracle_search_direct_f64(const double *Q, int n, uint64_t lo, uint64_t hi, int threads,
                              oracle_result_f64 *out);
+/* Tier A over idx in [lo, hi): the k lowest states (k <= 1024) in the order
+ * (E ascending, index ascending); *found = min(k, hi - lo). */
+int oracle_lowest_f64(const double *Q, int n, int k, uint64_t lo, uint64_t hi, int threads,
+                      double *energies, uint64_t *indices, int *found);
 
 const char *oracle_version(void);
 #endif

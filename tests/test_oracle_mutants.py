@@ -5,7 +5,8 @@ oracle (on the CPU only): a dropped diagonal, a reversed bit order, a wrong sign
 in the Gray update, a missing field update, a traversal-order tie-break, a
 count that ignores ties, a field without its diagonal, a dropped x_j factor,
 a flip applied to the wrong variable, an off-by-one in the k-lowest list, a
-floating-point sum in the wrong order and floating-point ties within a tolerance.
+floating-point sum in the wrong order, floating-point ties within a tolerance
+and floating-point k-lowest lists merged without the index order of ties.
 The pin suite must reject every one.
 """
 import pytest
@@ -26,6 +27,7 @@ MUTANTS = {
     10: "the k-lowest list never fills its last slot after it is full",
     11: "floating-point energies summed in column-major order",
     12: "floating-point energies within a relative 1e-12 count as ties",
+    13: "the floating-point k-lowest lists merge last thread first, equal energies in the order met",
 }
 
 

@@ -293,7 +293,39 @@ def pin_f64_fractional(o: oracle.Oracle):
     assert abs(r.min_energy + float(av @ np.asarray(P, dtype=np.int64) @ av)) < 11 * 11 * 1e-3
 
 
-ALL_PINS_F64 = [pin_f64_worked_examples, pin_f64_integer_valued, pin_f64_fractional]
+def pin_f64_lowest(o: oracle.Oracle):
+    """The k lowest states of a float64 Q: the sort of all 2^n definition
+    energies by (E, index) (numpy's lexsort; the energies are pinned above),
+    the integer oracle's list on integer-valued matrices (exact sums, heavy
+    ties), the minimum search's head, and index ranges."""
+    rng = np.random.default_rng(2721)
+    for n in (1, 5, 9, 11):
+        for Q in (rng.uniform(-20.0, 20.0, size=(n, n)),
+                  np.asarray(rand_general(n, 2722 + n, -2, 2), dtype=np.float64)):
+            idx = np.arange(1 << n, dtype=np.uint64)
+            E = o.energies_f64(Q, idx)
+            order = np.lexsort((idx, E))
+            for k in (1, 7, 64, (1 << n) + 3):
+                k = min(k, 1024)
+                want = [(float(E[i]), int(idx[i])) for i in order[:k]]
+                for threads in (1, 3):
+                    assert o.lowest_f64(Q, k, threads=threads) == want, (n, k, threads)
+            m = o.search_direct_f64(Q)
+            low = o.lowest_f64(Q, min(1 << n, 1024))
+            assert low[0] == (m.min_energy, m.argmin)
+            assert sum(1 for e, _ in low if e == m.min_energy) == m.count
+    Qi = rand_general(10, 2723, -1, 1)
+    assert o.lowest_f64(np.asarray(Qi, dtype=np.float64), 50) == \
+        [(float(e), i) for e, i in o.lowest(Qi, 50)]
+    Q = rng.uniform(-5.0, 5.0, size=(12, 12))
+    full = o.lowest_f64(Q, 1024)
+    for lo, hi in [(0, 64), (100, 1000), (4000, 4096)]:
+        assert o.lowest_f64(Q, 20, lo, hi, threads=2) == sorted(
+            (o.energy_f64(Q, i), i) for i in range(lo, hi))[:20], (lo, hi)
+    assert o.lowest_f64(Q, 20)[:20] == full[:20]
+
+
+ALL_PINS_F64 = [pin_f64_worked_examples, pin_f64_integer_valued, pin_f64_fractional, pin_f64_lowest]
 
 
 ALL_PINS = [pin_worked_examples, pin_closed_forms, pin_numpy_third_implementation, pin_tiers_agree,
