@@ -10,6 +10,7 @@ Calls only the CPU oracle (``oracle``) on the seeded workloads of
                                                         # the 64 lowest states (spectrum)
     python tests/golden/make_golden.py C1f C2f C4fsub   # real-valued (binary64) workloads, tier A
     python tests/golden/make_golden.py C58sub           # n = 58 (largest single launch): 2^36-state sub-cubes
+    python tests/golden/make_golden.py C1flow C4fsublow # binary64 spectrum: whole C1f, two C4f sub-cubes
 
 Full searches store {sha256_Q, n, min_energy, argmin, count, max_abs_energy}.
 Sub-cube files store one record per sub-cube: the first k variables are fixed
@@ -160,6 +161,50 @@ def subcubes_f64(name: str, threads: int) -> dict:
                 host=host_info(threads))
 
 
+F_LOW_CUBES = 2
+
+
+def lowest_full_f64(name: str, threads: int) -> dict:
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    t0 = time.time()
+    low = oracle.lowest_f64(Q, 64, threads=threads)
+    return dict(name=name + "low", desc=cfg["desc"], n=n, seed=cfg["seed"], sha256_Q=qi.sha256_of(Q), k=64,
+                states=[[float.hex(e), i] for e, i in low], tier="A (direct, binary64 in row-major order)",
+                seconds=round(time.time() - t0, 2), host=host_info(threads))
+
+
+def lowest_subcubes_f64(name: str, threads: int) -> dict:
+    """The 64 lowest states of the first sub-cubes of the binary64 sub-cube set."""
+    sub = subcubes_f64_tops(name)
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    m = F_SUB_FREE_BITS
+    cubes = []
+    t_all = time.time()
+    for top in sub[:F_LOW_CUBES]:
+        low = oracle.lowest_f64(Q, 64, top << m, (top + 1) << m, threads=threads)
+        cubes.append(dict(k=n - m, top=top, states=[[float.hex(e), i] for e, i in low]))
+        print("  %s top=%d -> %s" % (name, top, low[0]), flush=True)
+    return dict(name=name + "sublow", desc=cfg["desc"], n=n, seed=cfg["seed"], sha256_Q=qi.sha256_of(Q),
+                free_bits=m, sub_seed=SUB_SEED + 100 + n, k_lowest=64, cubes=cubes,
+                tier="A (direct, binary64 in row-major order)", seconds_total=round(time.time() - t_all, 2),
+                host=host_info(threads))
+
+
+def subcubes_f64_tops(name: str) -> list[int]:
+    """The seeded sub-cube tops of the binary64 sub-cube set (as in subcubes_f64)."""
+    n = qi.make_config(name)["n"]
+    k = n - F_SUB_FREE_BITS
+    rng = qi.SplitMix64(SUB_SEED + 100 + n)
+    tops = []
+    while len(tops) < F_SUB_COUNT:
+        t = rng.uniform_int(0, (1 << k) - 1)
+        if t not in tops:
+            tops.append(t)
+    return tops
+
+
 MAX_SUB_FREE_BITS = 36
 MAX_SUB_COUNT = 2
 
@@ -197,6 +242,10 @@ def main(argv):
         print("computing", arg, "on", threads, "threads", flush=True)
         if arg == "C58sub":
             rec = subcubes_max("C58", threads)
+        elif arg == "C1flow":
+            rec = lowest_full_f64("C1f", threads)
+        elif arg == "C4fsublow":
+            rec = lowest_subcubes_f64("C4f", threads)
         elif arg.endswith("fsub"):
             rec = subcubes_f64(arg[:-3], threads)
         elif arg in ("C1f", "C2f"):
