@@ -262,6 +262,19 @@ def main():
                            "coverage_ok": tf["bodies"] * 32 == (1 << plan["prefix_bits"]) * plan["col_groups"],
                            "result": [float.hex(rf.min_energy), rf.argmin, rf.count]}
         print("[bench] f64", tf, file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        lowf = q.lowest(Qf, 64)
+        torch.cuda.synchronize()
+        tl = q.last_timing()
+        line["f64_spectrum_k64"] = {"value": states / (time.perf_counter() - t1) / 1e12, "unit": "1e12 states/s",
+                                    "kernel": "gray_search_f64_kernel<lowest> (the 64 lowest binary64 states)",
+                                    "kernel_ms": tl["search_ms"], "slow_bodies": tl["slow_bodies"],
+                                    "candidates": tl["candidates"],
+                                    "first": [float.hex(lowf[0][0]), lowf[0][1]],
+                                    "last": [float.hex(lowf[-1][0]), lowf[-1][1]],
+                                    "head_is_min": (lowf[0][0], lowf[0][1]) == (rf.min_energy, rf.argmin)}
+        print("[bench] f64 spectrum", tl, file=sys.stderr, flush=True)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)

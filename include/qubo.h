@@ -234,6 +234,22 @@ QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_
                              uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
                              qubo_result_f64 *out);
 
+/* The k lowest states of a binary64 Q (the definition of qubo_search_f64): the
+ * first k states in the order (energy ascending, index ascending), as
+ * qubo_search_lowest does for int32.  k: 1..QUBO_MAX_LOWEST.  Arguments, limits
+ * and errors as for qubo_search_f64; out: host pointer to k entries, entries
+ * 0..*found-1 receive the states in order; found: min(k, states searched).
+ * Every state whose fp32 energy comes within delta of the lowest k-th exact
+ * energy of any wave is re-evaluated from the definition, so the list is
+ * exactly the definition's. */
+typedef struct {
+    double energy;
+    uint64_t index;
+} qubo_state_f64;
+QUBO_API int qubo_search_lowest_f64(const double *Q, int n, int k, int prefix_bits, int cache_bits,
+                                    uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
+                                    qubo_state_f64 *out, int *found);
+
 /* A search run in steps, so that a long search (n = 58 takes about an hour,
  * n = 63 about 35 hours) can be stopped and resumed, or its steps spread over
  * time.  The work units are independent (sec. III.C), so the state space is

@@ -52,6 +52,10 @@ class _State(ctypes.Structure):
     _fields_ = [("energy", ctypes.c_int32), ("reserved", ctypes.c_uint32), ("index", ctypes.c_uint64)]
 
 
+class _StateF64(ctypes.Structure):
+    _fields_ = [("energy", ctypes.c_double), ("index", ctypes.c_uint64)]
+
+
 class _Plan(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("n", "n_search", "prefix_bits", "suffix_bits", "cache_bits", "reg_bits",
@@ -123,6 +127,7 @@ _lib = None
 
 EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range", "qubo_search_ex",
            "qubo_build_tables", "qubo_last_timing", "qubo_search_lowest", "qubo_search_f64",
+           "qubo_search_lowest_f64",
            "qubo_progress_init", "qubo_search_step", "qubo_progress_init_lowest", "qubo_search_step_lowest",
            "qubo_progress_init_f64", "qubo_search_step_f64", "qubo_strerror", "qubo_version")
 MAX_LOWEST = 64
@@ -164,6 +169,10 @@ def load(path: str = LIB_PATH):
     lib.qubo_progress_init.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
                                        ctypes.c_void_p, ctypes.POINTER(Progress)]
     lib.qubo_search_step.argtypes = [i32p, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(Progress)]
+    lib.qubo_search_lowest_f64.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32,
+                                           ctypes.c_void_p, ctypes.POINTER(_StateF64),
+                                           ctypes.POINTER(ctypes.c_int)]
     lib.qubo_progress_init_lowest.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_uint32, ctypes.c_void_p, ctypes.POINTER(ProgressLowest)]
     lib.qubo_search_step_lowest.argtypes = [i32p, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ProgressLowest)]
@@ -287,8 +296,23 @@ def lowest(Q, k: int, prefix_bits: int | None = None, cache_bits: int | None = N
            gray_hi: int = 0) -> list[tuple[int, int]]:
     """The k lowest states (k <= 64) as (energy, index) pairs, energy ascending
     then index ascending: the low-energy spectrum.  gray_lo/gray_hi select a
-    slice as in search_range (prefix_bits must then be given)."""
+    slice as in search_range (prefix_bits must then be given).  A float64 Q
+    gives binary64 energies (search_f64's definition; no outer split)."""
     import torch
+    if _is_f64(Q):
+        if split_bits or (cols_per_lane not in (None, 8)):
+            raise ValueError("the binary64 spectrum has no outer split and 8 columns per lane")
+        Q = _device_f64(Q)
+        k = int(k)
+        outf = (_StateF64 * max(k, 1))()
+        found = ctypes.c_int(0)
+        with torch.cuda.device(Q.device):
+            rc = load().qubo_search_lowest_f64(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], k, _opt(prefix_bits),
+                                               _opt(cache_bits), int(gray_lo), int(gray_hi), 0,
+                                               _stream(Q, stream), outf, ctypes.byref(found))
+        if rc != QUBO_OK:
+            raise QuboError(rc, "qubo_search_lowest_f64")
+        return [(outf[i].energy, outf[i].index) for i in range(found.value)]
     Q = _device_q(Q)
     k = int(k)
     out = (_State * max(k, 1))()

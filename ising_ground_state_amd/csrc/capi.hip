@@ -728,16 +728,20 @@ struct RequestF64 {
     bool ranged = false;
     uint64_t gray_lo = 0, gray_hi = 0;
     hipStream_t stream = nullptr;
+    int lowest_k = 0;  // > 0: the k-lowest search (its states go to *low)
 };
+
+static_assert(sizeof(qubo::LowEntryF64) == sizeof(qubo_state_f64), "list entry layout");
 
 // have_cap: the search only has to find states with E <= cap (a real energy
 // found elsewhere); an empty result is then valid and *found says whether any
 // state was recorded.
 int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap = false, double cap = 0.0,
-            bool *found = nullptr)
+            bool *found = nullptr, std::vector<qubo_state_f64> *low = nullptr)
 {
     using namespace qubo;
-    if (!rq.Q || !out || rq.n < 1 || rq.n > kMaxSingleVars)
+    const bool lowest = rq.lowest_k > 0;
+    if (!rq.Q || rq.n < 1 || rq.n > kMaxSingleVars || (lowest ? (!low || rq.lowest_k > kMaxLowest) : !out))
         return QUBO_EINVAL;
     const int n = rq.n;
     // The binary64 rows of Gray bits 4 .. l-1 sit in LDS (4 KiB each per
@@ -801,7 +805,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap = false, d
     const uint64_t seg_blocks = (segs + kWavesPerBlock - 1) / kWavesPerBlock;
     const uint64_t items = plan.col_groups * seg_blocks;
     int per_cu = 0;
-    if (search_occupancy_f64(&per_cu, lds_bytes) != hipSuccess)
+    if (search_occupancy_f64(lowest, &per_cu, lds_bytes) != hipSuccess)
         return QUBO_EDEVICE;
     if (per_cu < 1)
         per_cu = 1;
@@ -819,7 +823,12 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap = false, d
     const uint64_t off_epmin = al(off_ep + (1ull << A) * 8);
     const uint64_t off_part = al(off_epmin + ((1ull << (A - kRegBits)) + 2) * 4);
     const uint64_t off_ctrl = al(off_part + (uint64_t)blocks * kWavesPerBlock * sizeof(PartialF64));
-    const uint64_t total = al(off_ctrl + sizeof(CtrlF64));
+    // the k-lowest search: the per-wave lists, the merged list and its length
+    const uint64_t list_entries = lowest ? (uint64_t)blocks * kWavesPerBlock * rq.lowest_k : 0;
+    const uint64_t off_lists = al(off_ctrl + sizeof(CtrlF64));
+    const uint64_t off_low = al(off_lists + list_entries * sizeof(LowEntryF64));
+    const uint64_t off_low_found = al(off_low + kMaxLowest * sizeof(LowEntryF64));
+    const uint64_t total = lowest ? al(off_low_found + 4) : off_lists;
     Call call;
     call.stream = rq.stream;
     if (hipMallocAsync(&call.ws, total, rq.stream) != hipSuccess) {
@@ -847,7 +856,8 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap = false, d
     if ((double)delta32 < delta)
         delta32 = std::nextafter(delta32, INFINITY);
     // The first threshold: E(0) = 0 when state 0 is searched, else above every energy.
-    double t0 = (lo == 0) ? 0.0 : 4.0 * S + 1.0;
+    // (for the k-lowest search: always the bound, E(0) bounds only the minimum)
+    double t0 = (lo == 0 && !lowest) ? 0.0 : 4.0 * S + 1.0;
     if (have_cap && cap < t0)
         t0 = cap;
 
@@ -884,14 +894,29 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap = false, d
     sa.l_eff = l_eff;
     sa.seg_bits = plan.seg_bits;
     sa.delta = delta32;
-    if (launch_search_f64(sa, blocks, lds_bytes, rq.stream) != hipSuccess ||
+    LowEntryF64 *dlists = reinterpret_cast<LowEntryF64 *>(base + off_lists);
+    LowEntryF64 *dlow = reinterpret_cast<LowEntryF64 *>(base + off_low);
+    int32_t *dlow_found = reinterpret_cast<int32_t *>(base + off_low_found);
+    if (lowest) {
+        sa.lists = dlists;
+        sa.k_low = rq.lowest_k;
+    }
+    if (launch_search_f64(sa, lowest, blocks, lds_bytes, rq.stream) != hipSuccess ||
         hipEventRecord(call.ev[2], rq.stream) != hipSuccess ||
         launch_reduce_f64(dpart, blocks * kWavesPerBlock, dctrl, rq.stream) != hipSuccess ||
+        (lowest && launch_lowest_merge_f64(dlists, list_entries, rq.lowest_k, dlow, dlow_found,
+                                           rq.stream) != hipSuccess) ||
         hipEventRecord(call.ev[3], rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     CtrlF64 host_ctrl;
+    LowEntryF64 host_low[kMaxLowest];
+    int32_t host_low_found = 0;
     if (hipMemcpyAsync(&host_ctrl, dctrl, sizeof(CtrlF64), hipMemcpyDeviceToHost, rq.stream) !=
             hipSuccess ||
+        (lowest &&
+         (hipMemcpyAsync(host_low, dlow, sizeof(host_low), hipMemcpyDeviceToHost, rq.stream) != hipSuccess ||
+          hipMemcpyAsync(&host_low_found, dlow_found, 4, hipMemcpyDeviceToHost, rq.stream) !=
+              hipSuccess)) ||
         hipEventRecord(call.ev[4], rq.stream) != hipSuccess ||
         hipStreamSynchronize(rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
@@ -914,6 +939,22 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap = false, d
     t.candidates = host_ctrl.candidates_total;
     g_timing = t;
 
+    if (lowest) {
+        // Only states of the problem are offered (padding variables unset), and
+        // without a cap the first threshold bounds every energy, so every state
+        // was offered and min(k, states searched) of them must be listed.
+        const uint64_t states = t.states >> (ns - n);
+        const uint64_t expect = states < (uint64_t)rq.lowest_k ? states : (uint64_t)rq.lowest_k;
+        if (host_low_found < 0 || host_low_found > rq.lowest_k ||
+            (!have_cap && (uint64_t)host_low_found != expect))
+            return QUBO_EDEVICE;
+        low->clear();
+        for (int i = 0; i < host_low_found; ++i)
+            low->push_back(qubo_state_f64{host_low[i].e, host_low[i].x});
+        if (found)
+            *found = host_low_found > 0;
+        return QUBO_OK;
+    }
     const PartialF64 &r = host_ctrl.result;
     if (found)
         *found = r.count != 0;
@@ -1209,6 +1250,35 @@ QUBO_API int qubo_search_step_f64(const double *Q, int n, void *stream, qubo_pro
     if (p->done)
         return QUBO_OK;
     return run_step_f64(Q, n, static_cast<hipStream_t>(stream), *p, p);
+}
+
+QUBO_API int qubo_search_lowest_f64(const double *Q, int n, int k, int prefix_bits, int cache_bits,
+                                    uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
+                                    qubo_state_f64 *out, int *found)
+{
+    if ((flags & ~QUBO_FLAG_COLS8) || !out || !found || k < 1 || k > QUBO_MAX_LOWEST)
+        return QUBO_EINVAL;
+    RequestF64 rq;
+    rq.Q = Q;
+    rq.n = n;
+    rq.prefix_bits = prefix_bits;
+    rq.cache_bits = cache_bits;
+    rq.stream = static_cast<hipStream_t>(stream);
+    rq.lowest_k = k;
+    if (gray_lo != 0 || gray_hi != 0) {
+        if (!valid_slice(n, prefix_bits, gray_lo, gray_hi))
+            return QUBO_EINVAL;
+        rq.ranged = true;
+        rq.gray_lo = gray_lo;
+        rq.gray_hi = gray_hi;
+    }
+    std::vector<qubo_state_f64> low;
+    const int rc = run_f64(rq, nullptr, false, 0.0, nullptr, &low);
+    if (rc != QUBO_OK)
+        return rc;
+    std::copy(low.begin(), low.end(), out);
+    *found = (int)low.size();
+    return QUBO_OK;
 }
 
 QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_bits,

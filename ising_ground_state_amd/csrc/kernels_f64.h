@@ -18,6 +18,12 @@ struct PartialF64 {
     uint64_t candidates; // states re-evaluated from the definition
 };
 
+// One entry of a k-lowest list: a state's binary64 energy and index (16 bytes).
+struct LowEntryF64 {
+    double e;    // +inf for an empty slot
+    uint64_t x;
+};
+
 struct CtrlF64 {
     unsigned long long counter;  // next work item
     long long gbest;             // upper bound of the minimum, as an order-preserving integer key
@@ -37,6 +43,7 @@ struct SearchArgsF64 {
     const double *Q;        // [n][n]              the caller's matrix (the definition's terms)
     PartialF64 *partials;   // [gridDim.x * 4]
     CtrlF64 *ctrl;
+    LowEntryF64 *lists;     // k-lowest search: [gridDim.x * 4][k_low], else unused
     uint64_t cols_padded;
     uint64_t gray_lo, gray_hi;
     uint64_t seg_first, segs, seg_blocks, items;
@@ -46,7 +53,7 @@ struct SearchArgsF64 {
     int32_t l_eff;          // Gray bits with rows on chip (registers + LDS)
     int32_t seg_bits;
     float delta;            // filter margin: bounds every fp32 rounding of the walk and the gate
-    int32_t reserved;
+    int32_t k_low;          // k-lowest search: states kept per wave (1..64), else 0
 };
 
 // E_s, M_int and E_p(g(j)) in binary64 from the folded matrix, M_int rounded to
@@ -59,10 +66,17 @@ hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64
 
 hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, hipStream_t stream);
 
-hipError_t launch_search_f64(const SearchArgsF64 &args, int blocks, int lds_bytes,
+// lowest: the k-lowest search (each wave keeps its k lowest states in
+// args.lists) instead of the minimum, count and lowest minimiser.
+hipError_t launch_search_f64(const SearchArgsF64 &args, bool lowest, int blocks, int lds_bytes,
                              hipStream_t stream);
 
-hipError_t search_occupancy_f64(int *blocks_per_cu, int lds_bytes);
+hipError_t search_occupancy_f64(bool lowest, int *blocks_per_cu, int lds_bytes);
+
+// Merges `count` entries (the per-wave lists, each sorted) into the k lowest
+// by (energy, index); writes k entries to out and their number to *found.
+hipError_t launch_lowest_merge_f64(const LowEntryF64 *lists, uint64_t count, int k, LowEntryF64 *out,
+                                   int32_t *found, hipStream_t stream);
 
 hipError_t launch_reduce_f64(const PartialF64 *partials, int count, CtrlF64 *ctrl,
                              hipStream_t stream);

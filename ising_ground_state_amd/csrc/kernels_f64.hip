@@ -284,6 +284,63 @@ __device__ __forceinline__ float flip_sign(int m, int t, bool top_plus)
     return top_plus ? 1.f : -1.f;
 }
 
+// The low-energy spectrum for a real-valued Q: a wave keeps the k lowest
+// states it has evaluated from the definition, in the order (E ascending,
+// index ascending), one per lane (lane i holds the i-th; empty slots hold
+// +inf).  A state goes in by counting the entries before it (a ballot) and
+// shifting the later ones up one lane.  As for integers, any wave's k-th
+// energy bounds the k-th lowest energy overall from above, and a state among
+// the k lowest overall is never displaced from its wave's list.
+struct WaveListF64 {
+    double e = __longlong_as_double(0x7ff0000000000000LL);
+    uint64_t x = ~0ull;
+    int k = 1;     // entries kept (1..64), wave-uniform
+    int lane = 0;
+
+    __device__ __forceinline__ void insert(double ce, uint64_t cx)
+    {
+        const bool before = lane < k && (e < ce || (e == ce && x < cx));
+        const int pos = __builtin_popcountll(__builtin_amdgcn_ballot_w64(before));
+        if (pos >= k)
+            return;
+        const double eu = __shfl_up(e, 1, 64);
+        const uint64_t xu = __shfl_up(x, 1, 64);
+        if (lane > pos) {
+            e = eu;
+            x = xu;
+        }
+        if (lane == pos) {
+            e = ce;
+            x = cx;
+        }
+    }
+
+    // Inserts the lanes of `mask`, whose entries are (ce, cx) in their own lane.
+    __device__ __forceinline__ void insert_lanes(uint64_t mask, double ce, uint64_t cx)
+    {
+        while (mask) {
+            const int l = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const uint64_t eb = (uint64_t)__double_as_longlong(ce);
+            const uint32_t elo = __builtin_amdgcn_readlane((uint32_t)eb, l);
+            const uint32_t ehi = __builtin_amdgcn_readlane((uint32_t)(eb >> 32), l);
+            const uint32_t xlo = __builtin_amdgcn_readlane((uint32_t)cx, l);
+            const uint32_t xhi = __builtin_amdgcn_readlane((uint32_t)(cx >> 32), l);
+            insert(__longlong_as_double((long long)(((uint64_t)ehi << 32) | elo)),
+                   ((uint64_t)xhi << 32) | xlo);
+        }
+    }
+
+    // k-th energy of the list (+inf until k states are in it), wave-uniform.
+    __device__ __forceinline__ double kth() const
+    {
+        const uint64_t eb = (uint64_t)__double_as_longlong(e);
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)eb, k - 1);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(eb >> 32), k - 1);
+        return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    }
+};
+
 // One unrolled body of 32 states: 31 fp32 row updates, every state's energy
 // kept in registers (one add per state).
 __device__ __forceinline__ void adds_body(float (&E)[kR], const float (&Mr)[kU][kR], bool top_plus)
@@ -307,6 +364,11 @@ __device__ __forceinline__ void adds_body(float (&E)[kR], const float (&Mr)[kU][
 }
 
 // Four waves per SIMD: the register budget (128 VGPRs) the compiler must meet.
+// Lowest: keep each wave's k lowest states (args.lists) instead of the
+// minimum, its count and lowest minimiser; the threshold is then the k-th
+// energy, and the first pass of an exact walk (which bounds only the minimum)
+// is skipped.
+template <bool Lowest>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gray_search_f64_kernel(const double *__restrict__ es,
                                                               const double *__restrict__ mint,
                                                               const float *__restrict__ mint32,
@@ -474,7 +536,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 // the best exact energy in the body from above, so T (which only
                 // has to bound the minimum from above) falls to it before any
                 // state is re-evaluated.
-                {
+                if (!Lowest) {
                     float W[kR];  // the walk on a copy: E stays at the body's first state
 #pragma unroll
                     for (int r = 0; r < kR; ++r)
@@ -497,6 +559,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                     T = up < T ? up : T;
                     TD = (float)T + a.delta;
                 }
+                if (Lowest) {
+                    WaveListF64 wl;
+                    wl.k = a.k_low;
+                    wl.lane = lane;
+                    wl.e = rec_e[threadIdx.x];
+                    wl.x = rec_a[threadIdx.x];
+#pragma unroll 1
+                    for (int m = 0; m < kBody; ++m) {
+                        const uint64_t j = base + (uint64_t)m;
+                        const float ep32 = (float)ep[j];
+                        const uint64_t hi = (gray(j) << B) | colbase;
+                        uint32_t hits = 0;
+#pragma unroll
+                        for (int r = 0; r < kR; ++r)
+                            hits |= (E[r] + ep32 <= TD ? 1u : 0u) << r;
+                        // one candidate per lane per round, evaluated side by side,
+                        // then offered to the list lane by lane
+                        while (__builtin_amdgcn_ballot_w64(hits != 0)) {
+                            double v = 0.0;
+                            uint64_t real = 0;
+                            bool ok = false;
+                            if (hits) {
+                                const int r = __builtin_ctz(hits);
+                                hits &= hits - 1;
+                                const uint64_t idx = hi | ((uint64_t)r << 6) | (uint64_t)lane;
+                                if ((idx & ((1ull << a.pad) - 1)) == 0) {
+                                    ++candidates;
+                                    real = idx >> a.pad;
+                                    v = energy_def(Q, a.n, real);
+                                    ok = true;
+                                }
+                            }
+                            wl.insert_lanes(__builtin_amdgcn_ballot_w64(ok), v, real);
+                        }
+                        const int t = __builtin_ctz((unsigned)(m + 1));
+                        flip_row(E, Mr, t, flip_sign(m, t, top_plus));
+                    }
+                    rec_e[threadIdx.x] = wl.e;
+                    rec_a[threadIdx.x] = wl.x;
+                    const double kt = wl.kth();
+                    T = kt < T ? kt : T;
+                } else {
                 RecordF64 rec{rec_e[threadIdx.x], rec_c[threadIdx.x], rec_a[threadIdx.x]};
 #pragma unroll 1
                 for (int m = 0; m < kBody; ++m) {
@@ -534,6 +638,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 rec_a[threadIdx.x] = rec.arg;
                 const double wm = uniform_f64(wave_min_f64(rec.e));
                 T = wm < T ? wm : T;
+                }
                 atomicMin(&ctrl->gbest, order_key(T));
                 const double gb = uniform_f64(from_key(__hip_atomic_load(
                     &ctrl->gbest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
@@ -595,6 +700,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
 
     double e = rec_e[threadIdx.x];
     uint64_t cnt = rec_c[threadIdx.x], arg = rec_a[threadIdx.x];
+    if (Lowest) {
+        if (lane < a.k_low) {
+            LowEntryF64 le;
+            le.e = e;
+            le.x = arg;
+            a.lists[((uint64_t)blockIdx.x * kWaves + wave) * (uint64_t)a.k_low + (uint64_t)lane] = le;
+        }
+        cnt = 0;  // the partials carry the statistics only
+    }
     wave_combine(e, cnt, arg);
     uint64_t cand = candidates;  // a lane evaluates far fewer than 2^32 states
 #pragma unroll
@@ -659,6 +773,49 @@ __global__ __launch_bounds__(256) void reduce_f64_kernel(const PartialF64 *__res
     }
 }
 
+// Merges the per-wave lists into the k lowest: each of the 4 waves of one
+// workgroup folds a strided quarter of the entries into its own list (offering
+// only entries at or below its current k-th energy), then wave 0 merges the
+// other three lists.
+__global__ __launch_bounds__(256) void lowest_merge_f64_kernel(const LowEntryF64 *__restrict__ lists,
+                                                               uint64_t count, int k,
+                                                               LowEntryF64 *__restrict__ out,
+                                                               int32_t *__restrict__ found)
+{
+    __shared__ LowEntryF64 staged[kWaves - 1][64];
+    const double inf = __longlong_as_double(0x7ff0000000000000LL);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    WaveListF64 wl;
+    wl.k = k;
+    wl.lane = lane;
+    for (uint64_t b = (uint64_t)wave * 64; b < count; b += 64 * kWaves) {
+        const uint64_t i = b + (uint64_t)lane;
+        LowEntryF64 le{inf, ~0ull};
+        if (i < count)
+            le = lists[i];
+        const double kt = wl.kth();
+        wl.insert_lanes(__builtin_amdgcn_ballot_w64(le.e != inf && le.e <= kt), le.e, le.x);
+    }
+    if (wave > 0 && lane < k)
+        staged[wave - 1][lane] = LowEntryF64{wl.e, wl.x};
+    __syncthreads();
+    if (wave != 0)
+        return;
+    for (int w = 0; w < kWaves - 1; ++w) {
+        LowEntryF64 le{inf, ~0ull};
+        if (lane < k)
+            le = staged[w][lane];
+        const double kt = wl.kth();
+        wl.insert_lanes(__builtin_amdgcn_ballot_w64(le.e != inf && le.e <= kt), le.e, le.x);
+    }
+    const uint64_t filled = __builtin_amdgcn_ballot_w64(lane < k && wl.e != inf);
+    if (lane < k)
+        out[lane] = LowEntryF64{wl.e, wl.x};
+    if (lane == 0)
+        *found = (int32_t)__builtin_popcountll(filled);
+}
+
 }  // namespace
 
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
@@ -687,20 +844,37 @@ hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_search_f64(const SearchArgsF64 &args, int blocks, int lds_bytes,
+hipError_t launch_search_f64(const SearchArgsF64 &args, bool lowest, int blocks, int lds_bytes,
                              hipStream_t stream)
 {
-    hipLaunchKernelGGL(gray_search_f64_kernel, dim3(blocks), dim3(64 * kWaves), lds_bytes, stream,
-                       args.es, args.mint, args.mint32, args.ep, args.epmin, args.Q, args.partials,
-                       args.ctrl, args);
+    if (lowest && (args.k_low < 1 || args.k_low > 64 || !args.lists))
+        return hipErrorInvalidValue;
+    if (lowest)
+        hipLaunchKernelGGL(gray_search_f64_kernel<true>, dim3(blocks), dim3(64 * kWaves), lds_bytes,
+                           stream, args.es, args.mint, args.mint32, args.ep, args.epmin, args.Q,
+                           args.partials, args.ctrl, args);
+    else
+        hipLaunchKernelGGL(gray_search_f64_kernel<false>, dim3(blocks), dim3(64 * kWaves), lds_bytes,
+                           stream, args.es, args.mint, args.mint32, args.ep, args.epmin, args.Q,
+                           args.partials, args.ctrl, args);
     return hipGetLastError();
 }
 
-hipError_t search_occupancy_f64(int *blocks_per_cu, int lds_bytes)
+hipError_t search_occupancy_f64(bool lowest, int *blocks_per_cu, int lds_bytes)
 {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, reinterpret_cast<const void *>(gray_search_f64_kernel), 64 * kWaves,
-        (size_t)lds_bytes);
+    const void *fn = lowest ? reinterpret_cast<const void *>(gray_search_f64_kernel<true>)
+                            : reinterpret_cast<const void *>(gray_search_f64_kernel<false>);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, 64 * kWaves, (size_t)lds_bytes);
+}
+
+hipError_t launch_lowest_merge_f64(const LowEntryF64 *lists, uint64_t count, int k, LowEntryF64 *out,
+                                   int32_t *found, hipStream_t stream)
+{
+    if (k < 1 || k > 64)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lowest_merge_f64_kernel, dim3(1), dim3(64 * kWaves), 0, stream, lists, count, k,
+                       out, found);
+    return hipGetLastError();
 }
 
 hipError_t launch_reduce_f64(const PartialF64 *partials, int count, CtrlF64 *ctrl,

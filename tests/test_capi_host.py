@@ -131,6 +131,21 @@ def test_null_and_range_arguments_rejected_before_the_device():
         assert lib.qubo_search_f64(P, n_, 8, -1, lo, hi, flags, None, ctypes.byref(rf)) == q.QUBO_EINVAL, n_
     assert lib.qubo_search_f64(None, 12, -1, -1, 0, 0, 0, None, ctypes.byref(rf)) == q.QUBO_EINVAL
     assert lib.qubo_search_f64(P, 12, -1, -1, 0, 0, 0, None, None) == q.QUBO_EINVAL
+    # real-valued spectrum: k in 1..64, outputs present, n in 1..58, the 8-column flag only, valid slices
+    outf = (q._StateF64 * 64)()
+    foundf = ctypes.c_int(-7)
+    for n_, k, flags, lo, hi, o, fo in [(12, 0, 0, 0, 0, outf, foundf), (12, 65, 0, 0, 0, outf, foundf),
+                                        (59, 4, 0, 0, 0, outf, foundf), (0, 4, 0, 0, 0, outf, foundf),
+                                        (12, 4, q.FLAG_COLS16, 0, 0, outf, foundf),
+                                        (12, 4, q.FLAG_STRICT_MIN, 0, 0, outf, foundf),
+                                        (12, 4, 0, 0, 33, outf, foundf), (12, 4, 0, 0, 0, None, foundf),
+                                        (12, 4, 0, 0, 0, outf, None)]:
+        fp = ctypes.byref(fo) if fo is not None else None
+        assert lib.qubo_search_lowest_f64(P, n_, k, 8, -1, lo, hi, flags, None, o, fp) == q.QUBO_EINVAL, \
+            (n_, k, flags, lo, hi)
+    assert lib.qubo_search_lowest_f64(None, 12, 4, -1, -1, 0, 0, 0, None, outf, ctypes.byref(foundf)) == \
+        q.QUBO_EINVAL
+    assert foundf.value == -7  # untouched
 
 
 def test_progress_record_and_rejections_before_the_device():
