@@ -601,43 +601,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                     const double kt = wl.kth();
                     T = kt < T ? kt : T;
                 } else {
-                RecordF64 rec{rec_e[threadIdx.x], rec_c[threadIdx.x], rec_a[threadIdx.x]};
+                    RecordF64 rec{rec_e[threadIdx.x], rec_c[threadIdx.x], rec_a[threadIdx.x]};
 #pragma unroll 1
-                for (int m = 0; m < kBody; ++m) {
-                    const uint64_t j = base + (uint64_t)m;
-                    const float ep32 = (float)ep[j];
-                    const uint64_t hi = (gray(j) << B) | colbase;
-                    uint32_t hits = 0;  // columns r whose state passes the filter
+                    for (int m = 0; m < kBody; ++m) {
+                        const uint64_t j = base + (uint64_t)m;
+                        const float ep32 = (float)ep[j];
+                        const uint64_t hi = (gray(j) << B) | colbase;
+                        uint32_t hits = 0;  // columns r whose state passes the filter
 #pragma unroll
-                    for (int r = 0; r < kR; ++r)
-                        hits |= (E[r] + ep32 <= TD ? 1u : 0u) << r;
-                    while (hits) {
-                        const int r = __builtin_ctz(hits);
-                        hits &= hits - 1;
-                        const uint64_t idx = hi | ((uint64_t)r << 6) | (uint64_t)lane;
-                        if ((idx & ((1ull << a.pad) - 1)) == 0) {
-                            ++candidates;
-                            const uint64_t real = idx >> a.pad;
-                            const double v = energy_def(Q, a.n, real);
-                            if (v < rec.e) {
-                                rec.e = v;
-                                rec.cnt = 1;
-                                rec.arg = real;
-                            } else if (v == rec.e) {
-                                rec.cnt += 1;
-                                rec.arg = real < rec.arg ? real : rec.arg;
+                        for (int r = 0; r < kR; ++r)
+                            hits |= (E[r] + ep32 <= TD ? 1u : 0u) << r;
+                        while (hits) {
+                            const int r = __builtin_ctz(hits);
+                            hits &= hits - 1;
+                            const uint64_t idx = hi | ((uint64_t)r << 6) | (uint64_t)lane;
+                            if ((idx & ((1ull << a.pad) - 1)) == 0) {
+                                ++candidates;
+                                const uint64_t real = idx >> a.pad;
+                                const double v = energy_def(Q, a.n, real);
+                                if (v < rec.e) {
+                                    rec.e = v;
+                                    rec.cnt = 1;
+                                    rec.arg = real;
+                                } else if (v == rec.e) {
+                                    rec.cnt += 1;
+                                    rec.arg = real < rec.arg ? real : rec.arg;
+                                }
                             }
                         }
+                        // flip into the next state (after the last one t = 5: no row)
+                        const int t = __builtin_ctz((unsigned)(m + 1));
+                        flip_row(E, Mr, t, flip_sign(m, t, top_plus));
                     }
-                    // flip into the next state (after the last one t = 5: no row)
-                    const int t = __builtin_ctz((unsigned)(m + 1));
-                    flip_row(E, Mr, t, flip_sign(m, t, top_plus));
-                }
-                rec_e[threadIdx.x] = rec.e;
-                rec_c[threadIdx.x] = rec.cnt;
-                rec_a[threadIdx.x] = rec.arg;
-                const double wm = uniform_f64(wave_min_f64(rec.e));
-                T = wm < T ? wm : T;
+                    rec_e[threadIdx.x] = rec.e;
+                    rec_c[threadIdx.x] = rec.cnt;
+                    rec_a[threadIdx.x] = rec.arg;
+                    const double wm = uniform_f64(wave_min_f64(rec.e));
+                    T = wm < T ? wm : T;
                 }
                 atomicMin(&ctrl->gbest, order_key(T));
                 const double gb = uniform_f64(from_key(__hip_atomic_load(
