@@ -3,7 +3,8 @@
     python -m ising_ground_state_amd.build
 
 The library is the C-ABI of include/qubo.h: host planning (plan.cpp), the HIP
-kernels (kernels.hip) and the entry points (capi.hip).
+kernels (kernels.hip, kernels_f64.hip), the host side of the searches (host.hip,
+run_int.hip, run_f64.hip, run_steps.hip) and the entry points (capi.hip).
 """
 from __future__ import annotations
 
@@ -17,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libqubo.so")
-SOURCES = ["plan.cpp", "kernels.hip", "kernels_f64.hip", "capi.hip"]
+SOURCES = ["plan.cpp", "kernels.hip", "kernels_f64.hip", "host.hip", "run_int.hip", "run_f64.hip", "run_steps.hip",
+           "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

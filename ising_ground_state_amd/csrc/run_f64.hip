@@ -1,0 +1,293 @@
+// One search of a real-valued (binary64) Q on the device, and one step of a
+// binary64 run in slices.
+#include "host.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace qubo_host {
+
+static_assert(sizeof(qubo::LowEntryF64) == sizeof(qubo_state_f64), "list entry layout");
+
+// have_cap: the search only has to find states with E <= cap (a real energy
+// found elsewhere); an empty result is then valid and *found says whether any
+// state was recorded.
+int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double cap, bool *found,
+            std::vector<qubo_state_f64> *low)
+{
+    using namespace qubo;
+    const bool lowest = rq.lowest_k > 0;
+    if (!rq.Q || rq.n < 1 || rq.n > kMaxSingleVars || (lowest ? (!low || rq.lowest_k > kMaxLowest) : !out))
+        return QUBO_EINVAL;
+    const int n = rq.n;
+    // The binary64 rows of Gray bits 4 .. l-1 sit in LDS (4 KiB each per
+    // workgroup): the default keeps 6 of them, so that with the fp32 rows of
+    // the walk's carries four workgroups fit a CU.
+    int cache_bits = rq.cache_bits;
+    if (cache_bits < 0 && n >= kMinSearchVars) {  // (tiny problems: the planner's fixed split)
+        qubo_plan probe;
+        const int rc0 = make_plan(n, rq.prefix_bits, -1, 256, 8, 0, &probe);
+        if (rc0 != QUBO_OK)
+            return rc0;
+        cache_bits = probe.prefix_bits < 10 ? probe.prefix_bits : 10;
+    }
+    DeviceInfo dev;
+    int rc = device_info(&dev);
+    if (rc != QUBO_OK)
+        return rc;
+    qubo_plan plan;
+    rc = make_plan(n, rq.prefix_bits, cache_bits, dev.num_cus, 8, 0, &plan);
+    if (rc != QUBO_OK)
+        return rc;
+    const int ns = plan.n_search, A = plan.prefix_bits, B = plan.suffix_bits;
+    const int l_eff = plan.cache_bits;
+    const int group = kWave * 8;
+    const int lds_bytes = (l_eff - 4) * group * 8;
+    if (lds_bytes > kMaxLdsBytes)
+        return QUBO_EPLAN;
+
+    // Q to the host; the guard: finite entries and sum |Q_ij| <= 2^100, so that
+    // fp32 energies never overflow.
+    std::vector<double> Qh((size_t)n * n);
+    if (hipMemcpyAsync(Qh.data(), rq.Q, Qh.size() * 8, hipMemcpyDeviceToHost, rq.stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    double S = 0.0;
+    rc = guard_f64(Qh, &S);
+    if (rc != QUBO_OK)
+        return rc;
+    // Fold to the upper triangle in binary64 (the walk's tables only; states
+    // are scored against Q itself) and pad small problems.
+    std::vector<double> U((size_t)ns * ns, 0.0);
+    for (int i = 0; i < n; ++i) {
+        U[(size_t)i * ns + i] = Qh[(size_t)i * n + i];
+        for (int j = i + 1; j < n; ++j)
+            U[(size_t)i * ns + j] = Qh[(size_t)i * n + j] + Qh[(size_t)j * n + i];
+    }
+    for (int i = n; i < ns; ++i)
+        U[(size_t)i * ns + i] = 1.0;
+
+    uint64_t lo = 0, hi = 1ull << A;
+    if (rq.ranged) {
+        lo = rq.gray_lo;
+        hi = rq.gray_hi;
+        if (hi > (1ull << A))
+            return QUBO_EINVAL;
+    }
+    const uint64_t seg_first = lo >> plan.seg_bits;
+    const uint64_t seg_last = (hi - 1) >> plan.seg_bits;
+    const uint64_t segs = seg_last - seg_first + 1;
+    const uint64_t seg_blocks = (segs + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint64_t items = plan.col_groups * seg_blocks;
+    int per_cu = 0;
+    if (search_occupancy_f64(lowest, &per_cu, lds_bytes) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (per_cu < 1)
+        per_cu = 1;
+    const uint64_t want_blocks = (uint64_t)dev.num_cus * (uint64_t)per_cu;
+    const int blocks = (int)(items < want_blocks ? items : want_blocks);
+
+    // Workspace.
+    const uint64_t cols_padded = (((1ull << B) + group - 1) / group) * group;
+    auto al = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
+    const uint64_t off_u = 0;
+    const uint64_t off_es = al(off_u + (uint64_t)ns * ns * 8);
+    const uint64_t off_mint = al(off_es + cols_padded * 8);
+    const uint64_t off_mint32 = al(off_mint + (uint64_t)A * cols_padded * 8);
+    const uint64_t off_ep = al(off_mint32 + (uint64_t)A * cols_padded * 4);
+    const uint64_t off_epmin = al(off_ep + (1ull << A) * 8);
+    const uint64_t off_part = al(off_epmin + ((1ull << (A - kRegBits)) + 2) * 4);
+    const uint64_t off_ctrl = al(off_part + (uint64_t)blocks * kWavesPerBlock * sizeof(PartialF64));
+    // the k-lowest search: the per-wave lists, the merged list and its length
+    const uint64_t list_entries = lowest ? (uint64_t)blocks * kWavesPerBlock * rq.lowest_k : 0;
+    const uint64_t off_lists = al(off_ctrl + sizeof(CtrlF64));
+    const uint64_t off_low = al(off_lists + list_entries * sizeof(LowEntryF64));
+    const uint64_t off_low_found = al(off_low + kMaxLowest * sizeof(LowEntryF64));
+    const uint64_t total = lowest ? al(off_low_found + 4) : off_lists;
+    Call call;
+    call.stream = rq.stream;
+    if (hipMallocAsync(&call.ws, total, rq.stream) != hipSuccess) {
+        call.ws = nullptr;
+        return QUBO_ENOMEM;
+    }
+    char *base = static_cast<char *>(call.ws);
+    double *dU = reinterpret_cast<double *>(base + off_u);
+    double *des = reinterpret_cast<double *>(base + off_es);
+    double *dmint = reinterpret_cast<double *>(base + off_mint);
+    float *dmint32 = reinterpret_cast<float *>(base + off_mint32);
+    double *dep = reinterpret_cast<double *>(base + off_ep);
+    float *depmin = reinterpret_cast<float *>(base + off_epmin);
+    PartialF64 *dpart = reinterpret_cast<PartialF64 *>(base + off_part);
+    CtrlF64 *dctrl = reinterpret_cast<CtrlF64 *>(base + off_ctrl);
+    if (!call.create_events())
+        return QUBO_EDEVICE;
+
+    // A state passes the filter when its fp32 energy is within delta of the
+    // best binary64 energy so far; delta = 1024 * 2^-24 S bounds every fp32
+    // rounding of the walk, the compare and the gates (at most about
+    // 290 * 2^-24 S) more than three times over.
+    const double delta = std::ldexp(S, -14);
+    float delta32 = (float)delta;
+    if ((double)delta32 < delta)
+        delta32 = std::nextafter(delta32, INFINITY);
+    // The first threshold: E(0) = 0 when state 0 is searched, else above every energy.
+    // (for the k-lowest search: always the bound, E(0) bounds only the minimum)
+    double t0 = (lo == 0 && !lowest) ? 0.0 : 4.0 * S + 1.0;
+    if (have_cap && cap < t0)
+        t0 = cap;
+
+    if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess ||
+        hipMemcpyAsync(dU, U.data(), U.size() * 8, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, des, dmint, dmint32, dep, depmin, lo, hi,
+                                rq.stream) !=
+        hipSuccess)
+        return QUBO_EDEVICE;
+    if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess ||
+        launch_init_ctrl_f64(dctrl, t0, depmin + (1ull << (A - kRegBits)), rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    SearchArgsF64 sa{};
+    sa.es = des;
+    sa.mint = dmint;
+    sa.mint32 = dmint32;
+    sa.ep = dep;
+    sa.epmin = depmin;
+    sa.Q = rq.Q;
+    sa.partials = dpart;
+    sa.ctrl = dctrl;
+    sa.cols_padded = cols_padded;
+    sa.gray_lo = lo;
+    sa.gray_hi = hi;
+    sa.seg_first = seg_first;
+    sa.segs = segs;
+    sa.seg_blocks = seg_blocks;
+    sa.items = items;
+    sa.A = A;
+    sa.B = B;
+    sa.n = n;
+    sa.pad = ns - n;
+    sa.l_eff = l_eff;
+    sa.seg_bits = plan.seg_bits;
+    sa.delta = delta32;
+    LowEntryF64 *dlists = reinterpret_cast<LowEntryF64 *>(base + off_lists);
+    LowEntryF64 *dlow = reinterpret_cast<LowEntryF64 *>(base + off_low);
+    int32_t *dlow_found = reinterpret_cast<int32_t *>(base + off_low_found);
+    if (lowest) {
+        sa.lists = dlists;
+        sa.k_low = rq.lowest_k;
+    }
+    if (launch_search_f64(sa, lowest, blocks, lds_bytes, rq.stream) != hipSuccess ||
+        hipEventRecord(call.ev[2], rq.stream) != hipSuccess ||
+        launch_reduce_f64(dpart, blocks * kWavesPerBlock, dctrl, rq.stream) != hipSuccess ||
+        (lowest && launch_lowest_merge_f64(dlists, list_entries, rq.lowest_k, dlow, dlow_found,
+                                           rq.stream) != hipSuccess) ||
+        hipEventRecord(call.ev[3], rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    CtrlF64 host_ctrl;
+    LowEntryF64 host_low[kMaxLowest];
+    int32_t host_low_found = 0;
+    if (hipMemcpyAsync(&host_ctrl, dctrl, sizeof(CtrlF64), hipMemcpyDeviceToHost, rq.stream) !=
+            hipSuccess ||
+        (lowest &&
+         (hipMemcpyAsync(host_low, dlow, sizeof(host_low), hipMemcpyDeviceToHost, rq.stream) != hipSuccess ||
+          hipMemcpyAsync(&host_low_found, dlow_found, 4, hipMemcpyDeviceToHost, rq.stream) !=
+              hipSuccess)) ||
+        hipEventRecord(call.ev[4], rq.stream) != hipSuccess ||
+        hipStreamSynchronize(rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+
+    qubo_timing t{};
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, call.ev[0], call.ev[1]) == hipSuccess)
+        t.build_ms = ms;
+    if (hipEventElapsedTime(&ms, call.ev[1], call.ev[2]) == hipSuccess)
+        t.search_ms = ms;
+    if (hipEventElapsedTime(&ms, call.ev[2], call.ev[3]) == hipSuccess)
+        t.reduce_ms = ms;
+    if (hipEventElapsedTime(&ms, call.ev[0], call.ev[4]) == hipSuccess)
+        t.total_ms = ms;
+    t.states = (hi - lo) << B;
+    t.blocks = blocks;
+    t.bodies = host_ctrl.bodies_total;
+    t.checked_bodies = host_ctrl.slow_total;
+    t.slow_bodies = host_ctrl.slow_total;
+    t.candidates = host_ctrl.candidates_total;
+    last_timing() = t;
+
+    if (lowest) {
+        // Only states of the problem are offered (padding variables unset), and
+        // without a cap the first threshold bounds every energy, so every state
+        // was offered and min(k, states searched) of them must be listed.
+        const uint64_t states = t.states >> (ns - n);
+        const uint64_t expect = states < (uint64_t)rq.lowest_k ? states : (uint64_t)rq.lowest_k;
+        if (host_low_found < 0 || host_low_found > rq.lowest_k ||
+            (!have_cap && (uint64_t)host_low_found != expect))
+            return QUBO_EDEVICE;
+        low->clear();
+        for (int i = 0; i < host_low_found; ++i)
+            low->push_back(qubo_state_f64{host_low[i].e, host_low[i].x});
+        if (found)
+            *found = host_low_found > 0;
+        return QUBO_OK;
+    }
+    const PartialF64 &r = host_ctrl.result;
+    if (found)
+        *found = r.count != 0;
+    if (r.count == 0)  // without a cap every state passes the first threshold
+        return have_cap ? QUBO_OK : QUBO_EDEVICE;
+    out->min_energy = r.e;
+    out->argmin = r.arg;
+    out->count = r.count;
+    return QUBO_OK;
+}
+
+// One step of a binary64 run: the next slice, capped by the best energy so far.
+int run_step_f64(const double *Q, int n, hipStream_t stream, const qubo_progress &p, qubo_progress *next)
+{
+    using namespace qubo;
+    const int A = p.prefix_bits, cb = p.chunk_bits;
+    if (p.kind != 1 || p.split_bits != 0 || n < kMinSearchVars || n > kMaxSingleVars || A < kRegBits ||
+        A > n || A > kMaxPrefixBits || cb < kRegBits || cb > A || p.sub != 0 || p.next >= (1ull << A) ||
+        (p.next & ((1ull << cb) - 1)) || p.steps_total == 0)
+        return QUBO_EINVAL;
+    std::vector<double> Qh((size_t)n * n);
+    if (hipMemcpyAsync(Qh.data(), Q, Qh.size() * 8, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (fingerprint(Qh.data(), Qh.size() * 8, n) != p.q_hash)
+        return QUBO_EINVAL;  // not the matrix this run was started with
+    RequestF64 rq;
+    rq.Q = Q;
+    rq.n = n;
+    rq.prefix_bits = A;
+    rq.ranged = true;
+    rq.gray_lo = p.next;
+    rq.gray_hi = p.next + (1ull << cb);
+    rq.stream = stream;
+    qubo_result_f64 r{};
+    bool found = false;
+    const int rc = run_f64(rq, &r, p.have_best != 0, p.best_f64.min_energy, &found);
+    if (rc != QUBO_OK)
+        return rc;
+    qubo_progress q = p;
+    if (found) {
+        if (!q.have_best || r.min_energy < q.best_f64.min_energy) {
+            q.best_f64 = r;
+            q.have_best = 1;
+        } else if (r.min_energy == q.best_f64.min_energy) {
+            q.best_f64.count += r.count;
+            q.best_f64.argmin = r.argmin < q.best_f64.argmin ? r.argmin : q.best_f64.argmin;
+        }
+    }
+    q.steps_done += 1;
+    q.next = p.next + (1ull << cb);
+    if (q.next == (1ull << A)) {
+        q.next = 0;
+        q.done = 1;
+    }
+    *next = q;
+    return QUBO_OK;
+}
+
+}  // namespace qubo_host
