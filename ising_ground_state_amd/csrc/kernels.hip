@@ -660,17 +660,24 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
             for (int r = 0; r < R; ++r)
                 Mr[t][r] = row[r * 64];
         }
-        // Lane bounds of the fall within a body, for s = 0 and s = 1, and within
-        // an aligned pair of bodies (64 steps, Gray bits 0..5), for bit 5 = 0
-        // and 1 at the pair's start.  Bit 5's row is read here only.
-        int beta_s0 = 0, beta_s1 = 0, beta_p0 = 0, beta_p1 = 0;
+        // Lane bounds of the fall within a body, for s = 0 and s = 1; within an
+        // aligned pair of bodies (64 steps, Gray bits 0..5), for bit 5 = 0 and 1
+        // at the pair's start; and within an aligned group of four bodies (128
+        // steps, Gray bits 0..6: bits 0..5 start at 0), for bit 6 = 0 and 1 at
+        // the group's start.  The rows of bits 5 and 6 are read here only.
+        int beta_s0 = 0, beta_s1 = 0, beta_p0 = 0, beta_p1 = 0, beta_q0 = 0, beta_q1 = 0;
         if (Gated) {
             beta_s0 = INT_MAX;
             beta_s1 = INT_MAX;
             beta_p0 = INT_MAX;
             beta_p1 = INT_MAX;
-            // (with A = 5 there is no bit 5: row 0 is read, in bounds, and ignored)
+            beta_q0 = INT_MAX;
+            beta_q1 = INT_MAX;
+            // (a bit that A does not have reads row 0, in bounds, and is ignored)
             const int32_t *row5 = mint + (uint64_t)(A > kU ? A - 1 - kU : 0) * cp + col0;
+            const int32_t *row6 = mint + (uint64_t)(A > kU + 1 ? A - 2 - kU : 0) * cp + col0;
+            // Loaded either way (in bounds) and masked: no branch around the loads.
+            const int has5 = -(int)(A > kU), has6 = -(int)(A > kU + 1);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 int b = 0;
@@ -679,9 +686,21 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                     b += Mr[t][r] < 0 ? Mr[t][r] : 0;
                 beta_s0 = imin(beta_s0, b);
                 beta_s1 = imin(beta_s1, b - Mr[kU - 1][r]);
-                const int m5 = A > kU ? row5[r * 64] : 0;
+                const int m5 = row5[r * 64] & has5;
                 beta_p0 = imin(beta_p0, b + (m5 < 0 ? m5 : 0));
                 beta_p1 = imin(beta_p1, b - (m5 > 0 ? m5 : 0));
+                const int m6 = row6[r * 64] & has6;
+                const int b5 = b + (m5 < 0 ? m5 : 0);
+                beta_q0 = imin(beta_q0, b5 + (m6 < 0 ? m6 : 0));
+                beta_q1 = imin(beta_q1, b5 - (m6 > 0 ? m6 : 0));
+                // One column at a time: with the sixteen row values loaded up
+                // front and the eight columns summed side by side, this set-up
+                // set the kernel's register count (a wave per SIMD less).
+                asm volatile(""
+                             : "+v"(beta_s0), "+v"(beta_s1), "+v"(beta_p0), "+v"(beta_p1), "+v"(beta_q0),
+                               "+v"(beta_q1)
+                             :
+                             : "memory");
             }
         }
         {
@@ -695,7 +714,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
         const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
         int epm_cur = Gated ? epmin[j_begin >> kU] : 0;
         int epm_next = Gated ? epmin[(j_begin >> kU) + 1] : 0;
-        bool pair_clear = false;  // the previous body's pair bound covered this body
+        uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
             const uint64_t base = j_begin + ((uint64_t)bi << kU);
             const bool last = bi + 1 == nbodies;
@@ -707,20 +726,30 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
             if (Gated) {
                 // Padding columns hold INT_MAX with zero rows (beta 0), so a lane
                 // of padding columns only has the bound INT_MAX.
-                if (pair_clear) {
-                    // T has not risen since the pair's bound was checked.
+                if (covered != 0) {
+                    // T has not risen since the bound that cleared this body was checked.
                     check = false;
-                    pair_clear = false;
+                    --covered;
                 } else {
                     const int emin = row_min<R>(E);
-                    if (top_plus && !last && A > kU) {
+                    if (((base >> kU) & 3u) == 0 && bi + 3 < nbodies && A > kU + 1) {
+                        // The first of four aligned bodies: their 128 states of Gray
+                        // bits 0..6 fall by at most beta_q(bit 6 at the group's start).
+                        const int epm_4 = epmin[(base >> kU) + 3];
+                        const int thq = T - imin(imin(epm_cur, epm_next), imin(epm_after, epm_4));
+                        const int bq = emin + (((base >> (kU + 2)) & 1u) ? beta_q1 : beta_q0);
+                        if (__builtin_amdgcn_ballot_w64(bq <= thq) == 0)
+                            covered = 3;
+                    }
+                    if (covered == 0 && top_plus && !last && A > kU) {
                         // An even body and its partner: the 64 states of Gray bits
                         // 0..5 fall by at most beta_p(bit 5 at the pair's start).
                         const int thp = T - imin(epm_cur, epm_next);
                         const int bp = emin + (((base >> (kU + 1)) & 1u) ? beta_p1 : beta_p0);
-                        pair_clear = __builtin_amdgcn_ballot_w64(bp <= thp) == 0;
+                        if (__builtin_amdgcn_ballot_w64(bp <= thp) == 0)
+                            covered = 1;
                     }
-                    if (pair_clear) {
+                    if (covered != 0) {
                         check = false;
                     } else {
                         const int thb = T - epm_cur;
