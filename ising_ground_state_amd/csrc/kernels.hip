@@ -795,10 +795,20 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 const bool plus = ((next >> (t + 1)) & 1u) == 0;
                 int row[R];
                 if (t < a.l_eff) {
-                    const int32_t *src = lds_lane + t * kGroup;  // row of bit t, this lane
+                    // Bit 5 (every other body) reads at constant offsets: the general
+                    // address costs a VALU instruction per body.  The asm marker keeps
+                    // the compiler from merging the branches into that address again.
+                    if (t == kU) {
+                        asm volatile("; exit flip of bit 5");
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        row[r] = src[r * 64];
+                        for (int r = 0; r < R; ++r)
+                            row[r] = lds_lane[kU * kGroup + r * 64];
+                    } else {
+                        const int32_t *src = lds_lane + t * kGroup;  // row of bit t, this lane
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            row[r] = src[r * 64];
+                    }
                 } else {
                     const int32_t *src = mint + (uint64_t)(A - 1 - t) * cp + col0;
 #pragma unroll
