@@ -391,7 +391,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
     const int A = a.A, B = a.B;
     const uint64_t cp = a.cols_padded;
     const double *lds_lane = lds_rows64 - 4 * kGroup + lane;  // row of bit t: lds_lane + t * kGroup
-    const float *carry_lane = &carry32[0][0] + lane;  // row of bit 5+i: carry_lane + i * kGroup
+    // The lane's offset passes through an empty asm: knowing its range, the
+    // compiler turned "+ r * 64" into bitwise ors that it does not fold into the
+    // LDS reads' immediate offsets, and spent a VALU instruction per register.
+    int lane_off = lane;
+    asm volatile("" : "+v"(lane_off));
+    const float *carry_lane = &carry32[0][0] + lane_off;  // row of bit 5+i: carry_lane + i * kGroup
 
     rec_e[threadIdx.x] = __longlong_as_double(0x7ff0000000000000LL);
     rec_c[threadIdx.x] = 0;
@@ -462,9 +467,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
             for (int r = 0; r < kR; ++r)
                 Mr[t][r] = row[r * 64];
         }
-        // Lane bounds of the fall within a body (s = bit 4 at its start) and a
-        // pair of bodies (bit 5 at its start), in fp32 (their rounding is in delta).
+        // Lane bounds of the fall within a body (s = bit 4 at its start), a pair
+        // of bodies (bit 5 at its start) and an aligned group of four (bits 0..5
+        // start at 0; bit 6 at its start), in fp32 (their rounding is in delta).
         float beta_s0 = INFINITY, beta_s1 = INFINITY, beta_p0 = INFINITY, beta_p1 = INFINITY;
+        float beta_q0 = INFINITY, beta_q1 = INFINITY;
         {
 #pragma unroll
             for (int r = 0; r < kR; ++r) {
@@ -474,9 +481,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                     b += fminf(Mr[t][r], 0.f);
                 beta_s0 = fminf(beta_s0, b);
                 beta_s1 = fminf(beta_s1, b - Mr[kU - 1][r]);
-                const float m5 = carry_lane[r * 64];  // 0 when A = 5
+                const float m5 = carry_lane[r * 64];           // 0 when A = 5
+                const float m6 = carry_lane[kGroup + r * 64];  // 0 when A <= 6
                 beta_p0 = fminf(beta_p0, b + fminf(m5, 0.f));
                 beta_p1 = fminf(beta_p1, b - fmaxf(m5, 0.f));
+                const float b5 = b + fminf(m5, 0.f);
+                beta_q0 = fminf(beta_q0, b5 + fminf(m6, 0.f));
+                beta_q1 = fminf(beta_q1, b5 - fmaxf(m6, 0.f));
             }
         }
         {
@@ -489,7 +500,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
         float epm_cur = epmin[j_begin >> kU];
         float epm_next = epmin[(j_begin >> kU) + 1];
-        bool pair_clear = false;
+        uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
         float E[kR];
         uint64_t anchor_j = j_begin;  // E64 holds the suffix energies at prefix g(anchor_j)
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
@@ -508,17 +519,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                     E[r] = (float)E64[r];
             }
             bool check;
-            if (pair_clear) {
+            if (covered != 0) {
                 check = false;
-                pair_clear = false;
+                --covered;
             } else {
                 const float emin = row_min8(E);
-                if (top_plus && !last && A > kU) {
-                    const float bp = emin + (((base >> (kU + 1)) & 1u) ? beta_p1 : beta_p0);
-                    pair_clear =
-                        __builtin_amdgcn_ballot_w64(bp + uniform_fmin(epm_cur, epm_next) <= TD) == 0;
+                // (the k-lowest search, whose threshold is its list's k-th energy,
+                // measured slower with this gate than without it)
+                if (!Lowest && (in_group & 3u) == 0 && bi + 3 < nbodies && A > kU + 1) {
+                    // four aligned bodies (never across an anchor group of eight)
+                    const float epm_4 = epmin[(base >> kU) + 3];
+                    const float bq = emin + (((base >> (kU + 2)) & 1u) ? beta_q1 : beta_q0);
+                    const float ep4 = uniform_fmin(uniform_fmin(epm_cur, epm_next), uniform_fmin(epm_after, epm_4));
+                    if (__builtin_amdgcn_ballot_w64(bq + ep4 <= TD) == 0)
+                        covered = 3;
                 }
-                if (pair_clear) {
+                if (covered == 0 && top_plus && !last && A > kU) {
+                    const float bp = emin + (((base >> (kU + 1)) & 1u) ? beta_p1 : beta_p0);
+                    if (__builtin_amdgcn_ballot_w64(bp + uniform_fmin(epm_cur, epm_next) <= TD) == 0)
+                        covered = 1;
+                }
+                if (covered != 0) {
                     check = false;
                 } else {
                     const float bound = emin + (top_plus ? beta_s0 : beta_s1);
@@ -654,12 +675,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                     // inside a group: the fp32 walk flips Gray bit t (5 <= t < 5 +
                     // kAnchorBits) into the next body (two-operand adds: a
                     // three-register fma issues at half rate)
-                    const int t = __builtin_ctzll(next);
-                    const float *src = carry_lane + (t - kU) * kGroup;
+                    // the carried bit from the body's place in its group: a 32-bit
+                    // value, so the branches below compare on the scalar unit
+                    const int t = kU + __builtin_ctz(in_group + 1);
+                    // Each of the three rows is read at constant offsets: from
+                    // (t - 5) * kGroup the compiler made negative offsets, which LDS
+                    // reads cannot take, and spent an address add per register.
+                    // The asm after the reads keeps the compiler from merging the
+                    // three branches into one read through a computed address.
+                    static_assert(kAnchorBits == 3 && kR == 8, "one branch per carried bit");
                     float row[kR];
+#define QUBO_PIN_ROW(tag)                                                                              \
+    asm volatile(tag : "+v"(row[0]), "+v"(row[1]), "+v"(row[2]), "+v"(row[3]), "+v"(row[4]), "+v"(row[5]), \
+                 "+v"(row[6]), "+v"(row[7]))
+                    if (t == kU) {
 #pragma unroll
-                    for (int r = 0; r < kR; ++r)
-                        row[r] = src[r * 64];
+                        for (int r = 0; r < kR; ++r)
+                            row[r] = carry_lane[r * 64];
+                        QUBO_PIN_ROW("; carry row of bit 5");
+                    } else if (t == kU + 1) {
+#pragma unroll
+                        for (int r = 0; r < kR; ++r)
+                            row[r] = carry_lane[kGroup + r * 64];
+                        QUBO_PIN_ROW("; carry row of bit 6");
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < kR; ++r)
+                            row[r] = carry_lane[2 * kGroup + r * 64];
+                        QUBO_PIN_ROW("; carry row of bit 7");
+                    }
+#undef QUBO_PIN_ROW
                     if (((next >> (t + 1)) & 1u) == 0)
                         step_rows<true>(E, row);
                     else

@@ -188,7 +188,10 @@ def test_range_is_subcube(q, n, A, k):
             check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
 
 
-RAGGED = [(32, 96), (96, 160), (0, 32), (32, 64), (64, 128 + 32), (1024 + 32, 2048 - 32), (0, 2048)]
+# (96, 288): bodies 3..8, one whole aligned group of four (4..7) between ragged
+# ends; (128, 224): bodies 4..6, a group start without its fourth body.
+RAGGED = [(32, 96), (96, 160), (0, 32), (32, 64), (64, 128 + 32), (1024 + 32, 2048 - 32), (0, 2048),
+          (96, 288), (128, 224)]
 
 
 def _slice_states(n, A, lo, hi):
@@ -202,8 +205,9 @@ def _slice_states(n, A, lo, hi):
 @pytest.mark.parametrize("lo,hi", RAGGED)
 def test_ragged_slices(q, lo, hi):
     """Slices that start or end on an odd 32-step body (or hold one body), so
-    that the 64-step pair bound and the single-body bound both decide; the
-    oracle evaluates every state of the slice from the definition."""
+    that the 128-step group bound, the 64-step pair bound and the single-body
+    bound all decide; the oracle evaluates every state of the slice from the
+    definition."""
     n, A = 16, 11
     Q = qi.general_uniform(n, 7350, -4, 4)
     idx = _slice_states(n, A, lo, hi)
