@@ -14,7 +14,9 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -87,11 +89,100 @@ def cpu_baseline(cfg):
     oracle.search_direct(c1["Q"], threads=threads)
     dt_a = time.perf_counter() - t1
     return {"value": states / dt / 1e12, "unit": "1e12 states/s", "cores": threads, "kind": "oracle",
+            "host": host_cpu(),
             "sample": "tier-B Gray walk over the sub-cube of 2^%d states with the first %d variables "
                       "fixed to %d (seed %d); %.2f s wall" % (free, k, top, 4242 + n, dt),
             "states": states, "seconds": dt, "subcube_result": list(r.triple()),
             "tier_a_c1": {"value": (1 << c1["n"]) / dt_a / 1e12, "unit": "1e12 states/s",
                           "sample": "tier A (direct O(n^2) per state), all 2^%d states of C1" % c1["n"]}}
+
+
+def host_cpu():
+    """The host's CPU model, the threads this process may run on, and SMT."""
+    model, siblings, cores = None, None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model is None:
+                    model = val
+                elif key == "siblings" and siblings is None:
+                    siblings = int(val)
+                elif key == "cpu cores" and cores is None:
+                    cores = int(val)
+    except OSError:
+        pass
+    smt = None if siblings is None or cores is None else siblings > cores
+    return {"model": model, "threads_available": len(os.sched_getaffinity(0)), "smt": smt}
+
+
+class GpuTelemetry:
+    """Samples the engine clock of every XCD and the hotspot temperature with
+    amd-smi, in a thread of its own, while the timed steps run.  A missing or
+    failing amd-smi only leaves the record empty."""
+
+    def __init__(self, interval_s: float = 2.0):
+        self.interval_s = interval_s
+        self.clocks, self.temps, self.errors = [], [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def parse(data):
+        """(mean gfx clock over the XCDs in MHz, hotspot temperature in C or None)
+        of the busiest device in the JSON of `amd-smi metric --clock --temperature`."""
+        gpus = data["gpu_data"] if isinstance(data, dict) else data
+        best = None
+        for g in gpus:
+            clk = [v["clk"]["value"] for k, v in g.get("clock", {}).items()
+                   if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
+                   and isinstance(v["clk"].get("value"), (int, float))]
+            if clk and (best is None or sum(clk) / len(clk) > best[0]):
+                hot = g.get("temperature", {}).get("hotspot")
+                temp = hot.get("value") if isinstance(hot, dict) else None
+                best = (sum(clk) / len(clk), temp if isinstance(temp, (int, float)) else None)
+        if best is None:
+            raise ValueError("no gfx clock in amd-smi output")
+        return best
+
+    def _sample(self):
+        out = subprocess.run(["amd-smi", "metric", "--clock", "--temperature", "--json"],
+                             capture_output=True, text=True, timeout=30)
+        clk, temp = self.parse(json.loads(out.stdout))
+        self.clocks.append(clk)
+        if temp is not None:
+            self.temps.append(temp)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self._sample()
+            except Exception as e:  # telemetry is context: never fail the benchmark for it
+                self.errors.append("%s: %s" % (type(e).__name__, e))
+                if len(self.errors) >= 3:
+                    return
+            self._stop.wait(self.interval_s)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=60)
+
+    def summary(self):
+        rec = {"source": "amd-smi metric --clock --temperature, every %g s during the timed steps"
+                         % self.interval_s, "samples": len(self.clocks)}
+        if self.clocks:
+            rec["gfx_clock_mhz"] = {"min": min(self.clocks), "mean": round(sum(self.clocks) / len(self.clocks), 1),
+                                    "max": max(self.clocks), "note": "mean over the XCDs of one sample"}
+        if self.temps:
+            rec["hotspot_c_max"] = max(self.temps)
+        if self.errors:
+            rec["errors"] = self.errors[:3]
+        return rec
 
 
 def copy_calibration(mib: int):
@@ -161,16 +252,17 @@ def main():
         print("[bench] warmup", q.last_timing(), file=sys.stderr, flush=True)
 
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    kernel_ms, timings, result = [], [], None
-    for k in range(args.steps):
-        result = q.search(Qd, args.prefix_bits, args.cache_bits, strict=args.strict)
-        t = q.last_timing()
-        timings.append(t)
-        kernel_ms.append(t["search_ms"])
-        print("[bench] step", k, t, file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with GpuTelemetry() as telemetry:
+        t0 = time.perf_counter()
+        kernel_ms, timings, result = [], [], None
+        for k in range(args.steps):
+            result = q.search(Qd, args.prefix_bits, args.cache_bits, strict=args.strict)
+            t = q.last_timing()
+            timings.append(t)
+            kernel_ms.append(t["search_ms"])
+            print("[bench] step", k, t, file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     coverage_ok = all(t["bodies"] * 32 == (1 << plan["prefix_bits"]) * plan["col_groups"] for t in timings)
 
     ms_per_step = elapsed * 1e3 / args.steps
@@ -211,6 +303,7 @@ def main():
         },
         "pct_int32_valu_peak": 100.0 * value * 1e12 / INT32_VALU_PEAK,
         "result": {"min_energy": result.min_energy, "argmin": result.argmin, "count": result.count},
+        "gpu_telemetry": telemetry.summary(),
         "mode": "strict (minimum after every prefix)" if args.strict else
                 "bound-gated minimum (one add per state; per-step minimum only where a 32-step bound can reach the best)",
         "coverage_ok": coverage_ok,
