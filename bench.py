@@ -122,8 +122,9 @@ class GpuTelemetry:
     amd-smi, in a thread of its own, while the timed steps run.  A missing or
     failing amd-smi only leaves the record empty."""
 
-    def __init__(self, interval_s: float = 2.0):
+    def __init__(self, interval_s: float = 2.0, enabled: bool = True):
         self.interval_s = interval_s
+        self.enabled = enabled
         self.clocks, self.temps, self.errors = [], [], []
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
@@ -165,14 +166,18 @@ class GpuTelemetry:
             self._stop.wait(self.interval_s)
 
     def __enter__(self):
-        self._thread.start()
+        if self.enabled:
+            self._thread.start()
         return self
 
     def __exit__(self, *exc):
         self._stop.set()
-        self._thread.join(timeout=60)
+        if self.enabled:
+            self._thread.join(timeout=60)
 
     def summary(self):
+        if not self.enabled:
+            return {"samples": 0, "skipped": "--no-telemetry"}
         rec = {"source": "amd-smi metric --clock --temperature, every %g s during the timed steps"
                          % self.interval_s, "samples": len(self.clocks)}
         if self.clocks:
@@ -205,6 +210,10 @@ def main():
     ap.add_argument("--prefix-bits", type=int, default=None)
     ap.add_argument("--cache-bits", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="no amd-smi sampling (for runs under a profiler, whose preloaded library has "
+                         "initialised the GPU before this program starts: a child process would be an exec "
+                         "after GPU initialisation)")
     ap.add_argument("--strict", action="store_true",
                     help="time the strict kernel (minimum after every prefix) instead of the default")
     ap.add_argument("--no-strict-leg", action="store_true",
@@ -252,7 +261,7 @@ def main():
         print("[bench] warmup", q.last_timing(), file=sys.stderr, flush=True)
 
     torch.cuda.synchronize()
-    with GpuTelemetry() as telemetry:
+    with GpuTelemetry(enabled=not args.no_telemetry) as telemetry:
         t0 = time.perf_counter()
         kernel_ms, timings, result = [], [], None
         for k in range(args.steps):

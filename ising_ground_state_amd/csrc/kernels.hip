@@ -188,6 +188,10 @@ __global__ __launch_bounds__(256) void build_suffix_kernel(const int32_t *__rest
 // so each block evaluates E_hi and K once and each thread only its low part.
 // The same kernel writes epmin[k] = min of ep over the 32-step body k (Gray steps
 // 32k .. 32k+31), which bounds the prefix energy of every state of that body.
+// E_hi is summed in parallel, one high variable per thread, into one of two
+// LDS accumulators that alternate between blocks (each is cleared one block
+// ahead, so a block needs two barriers).  The A x A prefix part of U sits in
+// LDS for the whole launch (A <= 32).
 __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *__restrict__ U,
                                                                 int ns, int A, int L,
                                                                 uint64_t blk_first, uint64_t blk_end,
@@ -195,39 +199,48 @@ __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *_
                                                                 int32_t *__restrict__ epmin)
 {
     __shared__ int K[8];
-    __shared__ int ehi_sh;
+    __shared__ int Upp[32][32];
+    __shared__ int ehi_acc[2];
     const int H = A - L;
     const int tid = threadIdx.x;
+    for (int k = tid; k < A * A; k += blockDim.x)
+        Upp[k / A][k % A] = k % A >= k / A ? U[(k / A) * ns + (k % A)] : 0;
+    if (tid < 2)
+        ehi_acc[tid] = 0;
+    __syncthreads();
     // Block-stride loop: a dispatch holds fewer than 2^32 work-items, and A = 32
     // needs 2^32 prefixes.  The trip count is the same for every thread of a block.
-    for (uint64_t blk = blk_first + blockIdx.x; blk < blk_end; blk += gridDim.x) {
+    // Blocks have 2^L > L + H threads: L = 8 whenever H > 0, and H = A - 8 <= 24.
+    int it = 0;
+    for (uint64_t blk = blk_first + blockIdx.x; blk < blk_end; blk += gridDim.x, it ^= 1) {
         const uint64_t hi = gray(blk);  // high part of g(j), H bits
         if (tid < L) {
             const int v = H + tid;  // a low variable
             int k = 0;
             for (int w = 0; w < H; ++w)
-                k += ((hi >> (H - 1 - w)) & 1u) ? U[w * ns + v] : 0;
+                k += (int)((hi >> (H - 1 - w)) & 1u) * Upp[w][v];
             K[tid] = k;
-        } else if (tid == L) {
-            int e = 0;
-            for (int w = 0; w < H; ++w) {
-                if (!((hi >> (H - 1 - w)) & 1u))
-                    continue;
+        } else if (tid < L + H) {
+            const int w = tid - L;  // a high variable: its row of E_hi
+            if ((hi >> (H - 1 - w)) & 1u) {
+                int e = 0;
                 for (int w2 = w; w2 < H; ++w2)
-                    e += ((hi >> (H - 1 - w2)) & 1u) ? U[w * ns + w2] : 0;
+                    e += (int)((hi >> (H - 1 - w2)) & 1u) * Upp[w][w2];
+                atomicAdd(&ehi_acc[it], e);
             }
-            ehi_sh = e;
+        } else if (tid == L + H) {
+            ehi_acc[it ^ 1] = 0;  // the next block's accumulator (last read before this block began)
         }
         __syncthreads();
         const uint64_t j = (blk << L) | (uint64_t)tid;
         const uint32_t lo = (uint32_t)(gray(j) & ((1u << L) - 1));
-        int e = ehi_sh;
+        int e = ehi_acc[it];
         for (int a = 0; a < L; ++a) {
-            if (!((lo >> (L - 1 - a)) & 1u))
-                continue;
-            e += K[a];
+            const int xa = (int)((lo >> (L - 1 - a)) & 1u);
+            int row = K[a];
             for (int b = a; b < L; ++b)
-                e += ((lo >> (L - 1 - b)) & 1u) ? U[(H + a) * ns + (H + b)] : 0;
+                row += (int)((lo >> (L - 1 - b)) & 1u) * Upp[H + a][H + b];
+            e += xa * row;
         }
         ep[j] = e;
         // 32 consecutive j are 32 consecutive lanes of one wave (blocks have 2^L >= 32 threads).
@@ -239,7 +252,7 @@ __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *_
         }
         if ((tid & 31) == 0)
             epmin[j >> 5] = m;
-        __syncthreads();  // K and ehi_sh are rewritten by the next iteration
+        __syncthreads();  // K and this block's accumulator are rewritten two blocks on
     }
 }
 
@@ -258,7 +271,11 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
     const int L = A < 8 ? A : 8;
     const uint64_t blk_first = j_lo >> L, blk_end = ((j_hi - 1) >> L) + 1;  // blocks holding the range
     const uint64_t nblocks = blk_end - blk_first;
-    const uint64_t grid = nblocks < (1ull << 20) ? nblocks : (1ull << 20);
+    // Enough blocks to fill the chip several times over; each then walks many
+    // prefix blocks with the prefix part of U staged once.
+    const uint64_t grid = nblocks < (1ull << 14) ? nblocks : (1ull << 14);
+    if (A > 32)
+        return hipErrorInvalidValue;  // (the builder stages at most 32 x 32 entries of U)
     hipLaunchKernelGGL(build_prefix_gray_kernel, dim3((unsigned)grid), dim3(1u << L), 0, stream,
                        U, ns, A, L, blk_first, blk_end, ep, epmin);
     return hipGetLastError();

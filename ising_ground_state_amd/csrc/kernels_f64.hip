@@ -183,28 +183,65 @@ __global__ __launch_bounds__(256) void build_suffix_f64_kernel(const double *__r
     }
 }
 
-// ep[j] = E_p(g(j)) over the A prefix variables, summed directly (O(A^2) per
-// prefix; the table is built once), and epmin[k] = min over body k of ep
-// rounded to fp32.  Block-stride loop over 256-prefix blocks.
-// Gray steps j_first <= j < j_end (j_first a multiple of 256, j_end of 32).
+// ep[j] = E_p(g(j)) over the A prefix variables, and epmin[k] = min over body
+// k of ep rounded to fp32.  Block-stride loop over 256-prefix blocks, Gray
+// steps j_first <= j < j_end (j_first a multiple of 256, j_end of 32).  The
+// 256 prefixes of a block share the high H = A - L bits of g(j) (L = min(A, 8)),
+// so with x_p split into high and low parts
+//   E_p = E_hi + sum_{a in lo, x_a = 1} (K[a] + sum_{b in lo, b >= a, x_b = 1} U[a][b]),
+//   K[a] = sum_{w in hi, x_w = 1} U[w][a];
+// a block computes K and one row of E_hi per high variable in parallel, and
+// every thread adds the rows in the same order (no floating-point atomics, so
+// the table does not depend on timing).  The order differs from the
+// definition's; the walk only uses these values in its filters, whose margin
+// covers any order.
 __global__ __launch_bounds__(256) void build_prefix_f64_kernel(const double *__restrict__ U, int ns,
                                                                int A, uint64_t j_first, uint64_t j_end,
                                                                double *__restrict__ ep,
                                                                float *__restrict__ epmin)
 {
+    __shared__ double K[8];
+    __shared__ double Upp[32][32];  // the A x A prefix part of U (A <= 32)
+    __shared__ double ehi_row[32];  // H = A - 8 <= 24
+    const int L = A < 8 ? A : 8, H = A - L;
+    const int tid = threadIdx.x;
+    for (int k = tid; k < A * A; k += blockDim.x)
+        Upp[k / A][k % A] = k % A >= k / A ? U[(k / A) * ns + (k % A)] : 0.0;
+    __syncthreads();
     for (uint64_t j0 = j_first + (uint64_t)blockIdx.x * blockDim.x; j0 < j_end;
          j0 += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t hi = gray(j0 >> L);  // high part of g(j), H bits (j0 is a multiple of 256)
+        if (tid < L) {
+            double k = 0.0;
+            for (int w = 0; w < H; ++w)
+                if ((hi >> (H - 1 - w)) & 1u)
+                    k += Upp[w][H + tid];
+            K[tid] = k;
+        } else if (tid < L + H) {
+            const int w = tid - L;
+            double e = 0.0;
+            if ((hi >> (H - 1 - w)) & 1u)
+                for (int w2 = w; w2 < H; ++w2)
+                    if ((hi >> (H - 1 - w2)) & 1u)
+                        e += Upp[w][w2];
+            ehi_row[w] = e;
+        }
+        __syncthreads();
         const uint64_t j = j0 + threadIdx.x;
         float m = __int_as_float(0x7f800000);
         if (j < j_end) {
-            const uint64_t p = gray(j);
             double e = 0.0;
-            for (int i = 0; i < A; ++i) {
-                if (!((p >> (A - 1 - i)) & 1u))
+            for (int w = 0; w < H; ++w)
+                e += ehi_row[w];
+            const uint32_t lo = (uint32_t)(gray(j) & ((1u << L) - 1));
+            for (int a = 0; a < L; ++a) {
+                if (!((lo >> (L - 1 - a)) & 1u))
                     continue;
-                for (int k = i; k < A; ++k)
-                    if ((p >> (A - 1 - k)) & 1u)
-                        e += U[i * ns + k];
+                double row = K[a];
+                for (int b = a; b < L; ++b)
+                    if ((lo >> (L - 1 - b)) & 1u)
+                        row += Upp[H + a][H + b];
+                e += row;
             }
             ep[j] = e;
             m = (float)e;
@@ -214,6 +251,7 @@ __global__ __launch_bounds__(256) void build_prefix_f64_kernel(const double *__r
             m = fminf(m, __shfl_xor(m, off, 64));
         if (j < j_end && (j & 31) == 0)
             epmin[j >> 5] = m;
+        __syncthreads();  // K and ehi_row are rewritten by the next block
     }
 }
 
@@ -873,11 +911,11 @@ hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    if (j_lo >= j_hi || j_hi > (1ull << A) || (j_lo & 31) || (j_hi & 31))
-        return hipErrorInvalidValue;
+    if (A < 5 || A > 32 || j_lo >= j_hi || j_hi > (1ull << A) || (j_lo & 31) || (j_hi & 31))
+        return hipErrorInvalidValue;  // (the builder stages at most 32 x 32 entries of U)
     const uint64_t j_first = j_lo & ~uint64_t(255);
     const uint64_t blocks = (j_hi - j_first + 255) / 256;
-    const uint64_t grid = blocks < (1ull << 20) ? blocks : (1ull << 20);
+    const uint64_t grid = blocks < (1ull << 14) ? blocks : (1ull << 14);
     hipLaunchKernelGGL(build_prefix_f64_kernel, dim3((unsigned)grid), dim3(256), 0, stream, U, ns,
                        A, j_first, j_hi, ep, epmin);
     return hipGetLastError();

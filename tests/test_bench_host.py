@@ -55,3 +55,10 @@ def test_host_cpu_record():
     h = bench.host_cpu()
     assert h["threads_available"] >= 1
     assert h["smt"] in (True, False, None)
+
+
+def test_disabled_telemetry_starts_nothing():
+    t = bench.GpuTelemetry(enabled=False)
+    with t:
+        pass
+    assert not t._thread.is_alive() and t.summary() == {"samples": 0, "skipped": "--no-telemetry"}
