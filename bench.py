@@ -67,6 +67,14 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+def covers(t, A, B):
+    """A search's timing shows every 32-step body of 2^A Gray steps walked once
+    per column group of 64 x (its columns per lane) columns."""
+    group = 64 * t["cols_per_lane"]
+    cols_padded = -(-(1 << B) // group) * group
+    return group > 0 and t["bodies"] * 32 * group == (1 << A) * cols_padded
+
+
 def cpu_baseline(cfg):
     """The CPU oracle (tier B, Gray walk) as it stands, on a seeded sub-cube of the
     same workload: the first k variables fixed (seed 4242), 2^(n-k) states."""
@@ -272,7 +280,7 @@ def main():
             print("[bench] step", k, t, file=sys.stderr, flush=True)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-    coverage_ok = all(t["bodies"] * 32 == (1 << plan["prefix_bits"]) * plan["col_groups"] for t in timings)
+    coverage_ok = all(covers(t, plan["prefix_bits"], plan["suffix_bits"]) for t in timings)
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = states * args.steps / elapsed / 1e12
@@ -343,7 +351,7 @@ def main():
                                 "kernel_ms": tl["search_ms"],
                                 "frac": OPS_PER_STATE * states / (tl["search_ms"] / 1e3) / INT32_VALU_PEAK,
                                 "slow_bodies": tl["slow_bodies"],
-                                "coverage_ok": tl["bodies"] * 32 == (1 << plan["prefix_bits"]) * plan["col_groups"],
+                                "coverage_ok": covers(tl, plan["prefix_bits"], plan["suffix_bits"]),
                                 "first": list(low[0]), "last": list(low[-1]),
                                 "head_is_min": tuple(low[0]) == (result.min_energy, result.argmin)}
         print("[bench] spectrum", tl, file=sys.stderr, flush=True)
@@ -361,7 +369,7 @@ def main():
                            "kernel_ms": tf["search_ms"],
                            "frac_fp32_add_peak": states / (tf["search_ms"] / 1e3) / INT32_VALU_PEAK,
                            "slow_bodies": tf["slow_bodies"], "candidates": tf["candidates"],
-                           "coverage_ok": tf["bodies"] * 32 == (1 << plan["prefix_bits"]) * plan["col_groups"],
+                           "coverage_ok": covers(tf, plan["prefix_bits"], plan["suffix_bits"]),
                            "result": [float.hex(rf.min_energy), rf.argmin, rf.count]}
         print("[bench] f64", tf, file=sys.stderr, flush=True)
         torch.cuda.synchronize()

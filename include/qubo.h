@@ -128,7 +128,8 @@ typedef struct {
     float total_ms;   /* from the first upload to the result download */
     uint64_t states;  /* states searched */
     int32_t blocks;   /* workgroups launched */
-    uint32_t reserved;
+    uint32_t cols_per_lane; /* suffix columns per lane of the search kernel (8 or 16; 8 for a
+                               binary64 Q) */
     uint64_t bodies;  /* 32-step bodies walked, each over the 64 x cols_per_lane suffix
                          columns of one wave (coverage: bodies x 32 x 64 x cols_per_lane
                          = Gray steps x 2^B rounded up to whole column groups) */

@@ -104,7 +104,7 @@ class ProgressLowest(ctypes.Structure):
 class _Timing(ctypes.Structure):
     _fields_ = [("build_ms", ctypes.c_float), ("search_ms", ctypes.c_float),
                 ("reduce_ms", ctypes.c_float), ("total_ms", ctypes.c_float),
-                ("states", ctypes.c_uint64), ("blocks", ctypes.c_int32), ("reserved", ctypes.c_uint32),
+                ("states", ctypes.c_uint64), ("blocks", ctypes.c_int32), ("cols_per_lane", ctypes.c_uint32),
                 ("bodies", ctypes.c_uint64), ("checked_bodies", ctypes.c_uint64),
                 ("slow_bodies", ctypes.c_uint64), ("candidates", ctypes.c_uint64)]
 

@@ -93,6 +93,8 @@ void add_timing(qubo_timing &acc, const qubo_timing &t)
     acc.total_ms += t.total_ms;
     acc.states += t.states;
     acc.blocks = t.blocks;
+    if (t.cols_per_lane != 0)  // (a skipped sub-problem launched nothing)
+        acc.cols_per_lane = t.cols_per_lane;
     acc.bodies += t.bodies;
     acc.checked_bodies += t.checked_bodies;
     acc.slow_bodies += t.slow_bodies;

@@ -8,6 +8,11 @@
 
 namespace qubo {
 
+// Suffix columns per lane of the binary64 search (120 VGPRs, four waves per
+// SIMD).  Four columns fit six waves but ran 10 % slower: a body's fixed work
+// then covers half as many states.
+constexpr int kColsPerLaneF64 = 8;
+
 // One wave's partial result (40 bytes).
 struct PartialF64 {
     double e;            // min energy seen (+inf when count == 0)

@@ -39,7 +39,7 @@ namespace {
 constexpr int kU = 5;  // Gray bits with rows in VGPRs (fp32)
 constexpr int kBody = 1 << kU;
 constexpr int kWaves = 4;
-constexpr int kR = 8;  // columns per lane
+constexpr int kR = kColsPerLaneF64;  // columns per lane
 // Bodies share one binary64 anchor in aligned groups of 2^kAnchorBits: inside
 // a group the fp32 walk runs on through the flips of Gray bits 5 .. 4+kAnchorBits
 // (fp32 rows in LDS).

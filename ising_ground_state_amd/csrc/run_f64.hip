@@ -26,7 +26,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     int cache_bits = rq.cache_bits;
     if (cache_bits < 0 && n >= kMinSearchVars) {  // (tiny problems: the planner's fixed split)
         qubo_plan probe;
-        const int rc0 = make_plan(n, rq.prefix_bits, -1, 256, 8, 0, &probe);
+        const int rc0 = make_plan(n, rq.prefix_bits, -1, 256, kColsPerLaneF64, 0, &probe);
         if (rc0 != QUBO_OK)
             return rc0;
         cache_bits = probe.prefix_bits < 10 ? probe.prefix_bits : 10;
@@ -36,12 +36,12 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     if (rc != QUBO_OK)
         return rc;
     qubo_plan plan;
-    rc = make_plan(n, rq.prefix_bits, cache_bits, dev.num_cus, 8, 0, &plan);
+    rc = make_plan(n, rq.prefix_bits, cache_bits, dev.num_cus, kColsPerLaneF64, 0, &plan);
     if (rc != QUBO_OK)
         return rc;
     const int ns = plan.n_search, A = plan.prefix_bits, B = plan.suffix_bits;
     const int l_eff = plan.cache_bits;
-    const int group = kWave * 8;
+    const int group = kWave * kColsPerLaneF64;
     const int lds_bytes = (l_eff - 4) * group * 8;
     if (lds_bytes > kMaxLdsBytes)
         return QUBO_EPLAN;
@@ -209,6 +209,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
         t.total_ms = ms;
     t.states = (hi - lo) << B;
     t.blocks = blocks;
+    t.cols_per_lane = kColsPerLaneF64;
     t.bodies = host_ctrl.bodies_total;
     t.checked_bodies = host_ctrl.slow_total;
     t.slow_bodies = host_ctrl.slow_total;

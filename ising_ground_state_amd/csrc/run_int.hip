@@ -198,6 +198,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     t.bodies = host_ctrl.bodies_total;
     t.checked_bodies = host_ctrl.checked_total;
     t.blocks = plan.blocks;
+    t.cols_per_lane = (uint32_t)plan.cols_per_lane;
     *timing = t;
 
     if (lowest) {

@@ -32,15 +32,17 @@ def inv_gray(g: int) -> int:
 def check_coverage(q, n, prefix_bits=None, cache_bits=None, lo=None, hi=None, strict=False,
                    cols_per_lane=None):
     """The last search walked every 32-step body of its range exactly once per
-    column group: bodies * 32 * 64R == (hi - lo) * (2^B padded to 64R columns)."""
+    column group: bodies * 32 * 64R == (hi - lo) * (2^B padded to 64R columns),
+    R the columns per lane that the search reports (and, when given, asked for)."""
     plan = q.make_plan(n, prefix_bits, cache_bits)
     A, B = plan["prefix_bits"], plan["suffix_bits"]
-    R = cols_per_lane or plan["cols_per_lane"]
+    t = q.last_timing()
+    R = t["cols_per_lane"]
+    assert cols_per_lane in (None, R), (cols_per_lane, t)
     group = 64 * R
     cols_padded = -(-(1 << B) // group) * group
     lo = 0 if lo is None else lo
     hi = (1 << A) if hi is None else hi
-    t = q.last_timing()
     assert t["bodies"] * 32 * group == (hi - lo) * cols_padded, (t, plan, R)
     if strict:
         assert t["checked_bodies"] == t["bodies"], t
