@@ -40,16 +40,20 @@ def golden(name):
 
 # ---------------------------------------------------------------- cache builder
 
-@pytest.mark.parametrize("n,A", [(5, 5), (9, 5), (12, 7), (17, 9), (24, 14), (26, 20), (30, 29)])
+@pytest.mark.parametrize("n,A", [(5, 5), (9, 5), (12, 7), (17, 9), (24, 14), (26, 20), (30, 29), (34, 30),
+                                 (32, 32)])
 def test_tables_match_definition(q, n, A):
     """E_s, M_int and the Gray-ordered E_p equal energies of states built from
     the definition: E_s[c] = E(c), M_int[v][c] = E(e_v | c) - E(e_v) - E(c),
-    EpGray[j] = E(g(j) << B) (eq. 8 of the paper, evaluated by the oracle)."""
+    EpGray[j] = E(g(j) << B) (eq. 8 of the paper, evaluated by the oracle).
+    A = 32 is the largest prefix (24 high bits above the builder's 8 low ones;
+    a 16 GiB table, sampled on the device)."""
+    import torch
     Q = qi.general_uniform(n, 5000 + n, -100, 100)
     B = n - A
     announce("tables", n, A)
-    es, mint, ep = q.build_tables(dev_q(Q), A)
-    es, mint, ep = es.cpu().numpy(), mint.cpu().numpy(), ep.cpu().numpy()
+    es, mint, ep_dev = q.build_tables(dev_q(Q), A)
+    es, mint = es.cpu().numpy(), mint.cpu().numpy()
     cols = np.arange(1 << B, dtype=np.uint64)
     if cols.size > 4096:
         cols = np.unique(np.concatenate([cols[:1024], cols[-1024:],
@@ -60,12 +64,17 @@ def test_tables_match_definition(q, n, A):
         ev = np.uint64(1 << (n - 1 - v))
         want = oracle.energies(Q, cols | ev) - Ec - oracle.energy(Q, int(ev))
         assert np.array_equal(mint[v, cols.astype(np.int64)], want), v
-    js = np.arange(1 << A, dtype=np.uint64)
-    if js.size > 8192:
-        js = np.unique(np.concatenate([js[:2048], js[-2048:],
-                                       np.random.default_rng(A).choice(js, 4096)]))
+    if A <= 13:
+        js = np.arange(1 << A, dtype=np.uint64)
+    else:  # both ends and a seeded sample, drawn without listing all 2^A steps
+        js = np.unique(np.concatenate([np.arange(2048, dtype=np.uint64),
+                                       np.arange((1 << A) - 2048, 1 << A, dtype=np.uint64),
+                                       np.random.default_rng(A).integers(0, 1 << A, 4096, dtype=np.uint64)]))
     states = (js ^ (js >> np.uint64(1))) << np.uint64(B)
-    assert np.array_equal(ep[js.astype(np.int64)], oracle.energies(Q, states))
+    ep = ep_dev[torch.as_tensor(js.astype(np.int64), device=ep_dev.device)].cpu().numpy()
+    del ep_dev
+    torch.cuda.synchronize()
+    assert np.array_equal(ep, oracle.energies(Q, states))
 
 
 # ---------------------------------------------------------------- small instances
