@@ -14,6 +14,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import subprocess
 import sys
 import threading
@@ -44,12 +45,24 @@ PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gray_search_gated_n48_counter
 KERNEL_INPUTS = [os.path.join(ROOT, "ising_ground_state_amd", "csrc", name) for name in ("kernels.hip", "kernels.h")]
 
 
+_C_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"', re.S)
+
+
+def strip_c_comments(text: str) -> str:
+    """C/C++ source without its comments (string literals kept as they are),
+    every run of white space collapsed to one blank."""
+    code = _C_TOKENS.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return re.sub(r"\s+", " ", code).strip()
+
+
 def kernel_source_hash() -> str:
+    """Identifies the compiled search kernel: its sources without comments, and
+    the compiler flags (counters taken before a comment edit stay valid)."""
     from ising_ground_state_amd import build as libbuild
     h = hashlib.sha256()
     for path in KERNEL_INPUTS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(strip_c_comments(f.read()).encode())
     h.update(repr(libbuild.FLAGS).encode())
     return h.hexdigest()[:16]
 

@@ -29,7 +29,14 @@
 //     from a Gray-ordered table through scalar loads).  The comparison results are
 //     OR-ed over the body; a body with any hit is re-walked on an exact slow path
 //     that records every state with E <= T (lowest index and exact counts),
-//     then lowers T.
+//     then lowers T.  This is the strict mode;
+//   * the default (gated) mode drops the per-step minimum: before an aligned
+//     group of four bodies, then before an aligned pair, then before a single
+//     body, one bound per lane (the smallest column energy at the start plus the
+//     largest possible fall over the free Gray bits, plus the smallest prefix
+//     energy of those bodies) is compared with T; only bodies some lane's bound
+//     reaches are walked on the exact path, and every other state costs its add
+//     alone;
 //   * the threshold T is shared between waves through a global best-so-far, which
 //     is always a real state's energy, so no minimiser is ever skipped.
 #include "kernels.h"

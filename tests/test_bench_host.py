@@ -62,3 +62,14 @@ def test_disabled_telemetry_starts_nothing():
     with t:
         pass
     assert not t._thread.is_alive() and t.summary() == {"samples": 0, "skipped": "--no-telemetry"}
+
+
+def test_kernel_hash_ignores_comments_not_code():
+    src = 'int f(int a) { // add one\n    return a + 1; /* the\n answer */ }\nconst char *s = "x // y";\n'
+    commented = '// header\n' + src.replace('// add one', '// adds one to a')
+    changed = src.replace('a + 1', 'a + 2')
+    literal = src.replace('"x // y"', '"x // z"')
+    assert bench.strip_c_comments(src) == bench.strip_c_comments(commented)
+    assert bench.strip_c_comments(src) != bench.strip_c_comments(changed)
+    assert bench.strip_c_comments(src) != bench.strip_c_comments(literal)  # strings are code
+
