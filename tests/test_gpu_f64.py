@@ -205,6 +205,45 @@ def test_integer_valued_full_size(q):
     check_coverage(q, 48)
 
 
+def test_concurrent_streams_real(q):
+    """Binary64 minimum and spectrum searches and an int32 search, each on a
+    stream of its own from its own host thread at the same time, give the
+    oracle's answers (each call owns its workspace and timing record)."""
+    import threading
+    import torch
+    Qa, Qb = real_matrix(21, 8601), real_matrix(22, 8602)
+    Qi = qi.general_uniform(23, 8603, -50, 50)
+    want = [oracle.search_direct_f64(Qa).triple(), oracle.lowest_f64(Qb, 16), oracle.search_gray(Qi).triple()]
+    got = [None] * 3
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    if i == 0:
+                        got[0] = q.search_f64(dev_f(Qa), stream=s).triple()
+                        assert q.last_timing()["states"] == 1 << 21
+                    elif i == 1:
+                        got[1] = q.lowest(dev_f(Qb), 16, stream=s)
+                    else:
+                        got[2] = q.search(torch.as_tensor(np.asarray(Qi, dtype=np.int32)).to("cuda:0"),
+                                          stream=s).triple()
+                        assert q.last_timing()["states"] == 1 << 23
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    announce("concurrent streams real")
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(3)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    assert got == want
+
+
 def test_f64_errors(q):
     Q = real_matrix(6, 8500)
     for bad in (np.nan, np.inf):
