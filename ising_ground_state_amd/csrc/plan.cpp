@@ -158,11 +158,14 @@ int make_plan(int n_total, int prefix_bits, int cache_bits, int num_cus, int col
     p.waves_per_block = kWavesPerBlock;
     p.col_groups = cols_padded / group;
 
-    // Segments: enough work units for ~8 per resident wave, each at least one
-    // unrolled body (2^5 steps) and at most 2^18 steps, so that the last round
-    // of the persistent grid is short (n=48: ~340 items per workgroup).
-    const uint64_t resident_waves = (uint64_t)num_cus * 4 * kWavesPerBlock;
-    const uint64_t target_units = 8 * resident_waves;
+    // Segments: enough work units for ~32 per resident wave (the gated kernel
+    // keeps six workgroups of four waves per CU), each at least one unrolled
+    // body (2^5 steps) and at most 2^18 steps, so that the last round of the
+    // persistent grid is short.  n = 48 and 50 reach the 2^18 cap either way;
+    // at n = 40 (2^13-step units) this measured 4 % faster than ~5 units per
+    // wave, while 2^11-step units ran 20 % slower (their start-up dominates).
+    const uint64_t resident_waves = (uint64_t)num_cus * 6 * kWavesPerBlock;
+    const uint64_t target_units = 32 * resident_waves;
     int split = 0;
     if (target_units > p.col_groups)
         split = ceil_log2((target_units + p.col_groups - 1) / p.col_groups);
