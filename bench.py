@@ -36,13 +36,17 @@ INT32_VALU_PEAK = CUS * LANES_PER_CU_CLOCK * CLOCK_HZ  # 7.86e13 lane-ops/s
 
 # Algorithmic work per state: one int32 add (eq. 9 of the paper: the suffix
 # vector moves by one row per Gray step, a single integer operation per state).
-# The reading that also counts a comparison per state (two ops) is reported too.
+# The strict kernel (Algorithm 2 as printed) also compares every state with the
+# threshold: two ops per state, reported for that kernel.
 OPS_PER_STATE = 1
-OPS_PER_STATE_ADD_CMP = 2
+OPS_PER_STATE_STRICT = 2
 
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gray_search_gated_n48_counters.json")
-# What the search kernel's machine code is built from: its source, its header and the compiler flags.
-KERNEL_INPUTS = [os.path.join(ROOT, "ising_ground_state_amd", "csrc", name) for name in ("kernels.hip", "kernels.h")]
+# What the counted launch is built from: the kernel source and header, the planner
+# (split, segments, LDS rows) and the host run that sizes the grid, and the
+# compiler flags.
+KERNEL_INPUTS = [os.path.join(ROOT, "ising_ground_state_amd", "csrc", name)
+                 for name in ("kernels.hip", "kernels.h", "plan.cpp", "plan.h", "run_int.hip")]
 
 
 _C_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"', re.S)
@@ -56,8 +60,9 @@ def strip_c_comments(text: str) -> str:
 
 
 def kernel_source_hash() -> str:
-    """Identifies the compiled search kernel: its sources without comments, and
-    the compiler flags (counters taken before a comment edit stay valid)."""
+    """Identifies the counted search launch: the kernel, planner and host-run
+    sources without comments, and the compiler flags (counters taken before a
+    comment edit stay valid)."""
     from ising_ground_state_amd import build as libbuild
     h = hashlib.sha256()
     for path in KERNEL_INPUTS:
@@ -88,23 +93,28 @@ def covers(t, A, B):
     return group > 0 and t["bodies"] * 32 * group == (1 << A) * cols_padded
 
 
+CPU_SAMPLE_FREE_BITS = 36
+CPU_SAMPLE_SEED = 4242
+
+
 def cpu_baseline(cfg):
-    """The CPU oracle (tier B, Gray walk) as it stands, on a seeded sub-cube of the
-    same workload: the first k variables fixed (seed 4242), 2^(n-k) states."""
+    """The CPU oracle (tier B, Gray walk) as it stands, on every hardware thread
+    this process may run on, over a seeded sub-cube of the same workload: the
+    first n - 36 variables fixed to a value drawn with seed 4242, 2^36 states.
+    Tier A (every state from the definition) on the whole n = 24 workload."""
     import oracle
     import qubo_instances as qi
 
     n = cfg["n"]
-    threads = min(16, oracle.default_threads())
-    free = 35 if threads >= 12 else 33
+    threads = len(os.sched_getaffinity(0))
+    free = CPU_SAMPLE_FREE_BITS
     k = n - free
-    rng = qi.SplitMix64(4242 + n)
+    rng = qi.SplitMix64(CPU_SAMPLE_SEED)
     top = rng.uniform_int(0, (1 << k) - 1)
     t0 = time.perf_counter()
     r = oracle.search_gray(cfg["Q"], k=k, top=top, threads=threads)
     dt = time.perf_counter() - t0
     states = 1 << free
-    # Tier A (every state from the definition) on the 2^24-state workload, for context.
     c1 = qi.make_config("C1")
     t1 = time.perf_counter()
     oracle.search_direct(c1["Q"], threads=threads)
@@ -112,14 +122,16 @@ def cpu_baseline(cfg):
     return {"value": states / dt / 1e12, "unit": "1e12 states/s", "cores": threads, "kind": "oracle",
             "host": host_cpu(),
             "sample": "tier-B Gray walk over the sub-cube of 2^%d states with the first %d variables "
-                      "fixed to %d (seed %d); %.2f s wall" % (free, k, top, 4242 + n, dt),
+                      "fixed to %d (seed %d); %.2f s wall on %d threads" % (free, k, top, CPU_SAMPLE_SEED, dt,
+                                                                            threads),
             "states": states, "seconds": dt, "subcube_result": list(r.triple()),
-            "tier_a_c1": {"value": (1 << c1["n"]) / dt_a / 1e12, "unit": "1e12 states/s",
+            "tier_a_c1": {"value": (1 << c1["n"]) / dt_a / 1e12, "unit": "1e12 states/s", "seconds": dt_a,
                           "sample": "tier A (direct O(n^2) per state), all 2^%d states of C1" % c1["n"]}}
 
 
 def host_cpu():
-    """The host's CPU model, the threads this process may run on, and SMT."""
+    """The host's CPU model, its logical CPUs, the threads this process may run
+    on, and SMT."""
     model, siblings, cores = None, None, None
     try:
         with open("/proc/cpuinfo") as f:
@@ -135,7 +147,8 @@ def host_cpu():
     except OSError:
         pass
     smt = None if siblings is None or cores is None else siblings > cores
-    return {"model": model, "threads_available": len(os.sched_getaffinity(0)), "smt": smt}
+    return {"model": model, "nproc": os.cpu_count(), "threads_available": len(os.sched_getaffinity(0)),
+            "smt": smt}
 
 
 class GpuTelemetry:
@@ -243,6 +256,8 @@ def main():
                     help="skip the extra step of the real-valued (binary64) search of C4f")
     ap.add_argument("--no-spectrum-leg", action="store_true",
                     help="skip the extra step of the 64-lowest-states search reported beside the minimum")
+    ap.add_argument("--no-config-legs", action="store_true",
+                    help="skip the one-search legs of the other workloads (C1, C2, C2p, C3, C5)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling HBM counters)")
     ap.add_argument("--sweep", action="store_true",
@@ -326,7 +341,6 @@ def main():
             "frac": achieved / INT32_VALU_PEAK,
             "traffic": measured_traffic(),
             "ops_per_state": OPS_PER_STATE,
-            "frac_add_and_compare": OPS_PER_STATE_ADD_CMP * states / avg_kernel_s / INT32_VALU_PEAK,
             "peak_derivation": "256 CU x 4 SIMD x 32 lanes/clock x 2.4 GHz (two-operand int32 add)",
             "kernel_ms_avg": avg_kernel_s * 1e3,
             "kernel_timing": "HIP events recorded on the search stream around the kernel launch",
@@ -349,8 +363,12 @@ def main():
         torch.cuda.synchronize()
         ts = q.last_timing()
         line["strict_mode"] = {"value": states / (time.perf_counter() - t1) / 1e12, "unit": "1e12 states/s",
+                               "kernel": "gray_search_kernel<%d, false>" % plan["cols_per_lane"],
                                "kernel_ms": ts["search_ms"],
                                "frac": OPS_PER_STATE * states / (ts["search_ms"] / 1e3) / INT32_VALU_PEAK,
+                               "ops_per_state_strict": OPS_PER_STATE_STRICT,
+                               "frac_add_and_compare": OPS_PER_STATE_STRICT * states / (ts["search_ms"] / 1e3)
+                               / INT32_VALU_PEAK,
                                "same_result": rs.triple() == result.triple()}
         print("[bench] strict", ts, file=sys.stderr, flush=True)
     if not args.no_spectrum_leg:
@@ -398,9 +416,57 @@ def main():
                                     "last": [float.hex(lowf[-1][0]), lowf[-1][1]],
                                     "head_is_min": (lowf[0][0], lowf[0][1]) == (rf.min_energy, rf.argmin)}
         print("[bench] f64 spectrum", tl, file=sys.stderr, flush=True)
+    if not args.no_config_legs:
+        line["other_configs"] = config_legs(q, args.config)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)
+
+
+LEG_CONFIGS = ("C1", "C2", "C2p", "C3", "C5")
+
+
+def config_legs(q, skip):
+    """One whole-space search of each other workload (after one warm-up search
+    for the small ones), with its kernel time, rate, the bodies walked exactly
+    and the roofline fraction: the gated kernel's time depends on the instance
+    (how often a body's bound reaches the best energy).  Results with a stored
+    oracle answer (tests/golden/<name>.json) are compared with it."""
+    import torch
+    import qubo_instances as qi
+    legs = {}
+    for name in LEG_CONFIGS:
+        if name == skip:
+            continue
+        cfg = qi.make_config(name)
+        n = cfg["n"]
+        Qd = torch.tensor(cfg["Q"], dtype=torch.int32, device="cuda:0")
+        plan = q.make_plan(n)
+        if n <= 40:
+            q.search(Qd)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        r = q.search(Qd)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        t = q.last_timing()
+        states = 1 << n
+        leg = {"n": n, "seed": cfg["seed"], "value": states / wall / 1e12, "unit": "1e12 states/s",
+               "kernel_ms": t["search_ms"], "total_ms": t["total_ms"],
+               "kernel_states_per_s": states / (t["search_ms"] / 1e3) / 1e12,
+               "frac": OPS_PER_STATE * states / (t["search_ms"] / 1e3) / INT32_VALU_PEAK,
+               "bodies": t["bodies"], "slow_bodies": t["slow_bodies"],
+               "coverage_ok": covers(t, plan["prefix_bits"], plan["suffix_bits"]),
+               "result": list(r.triple())}
+        stored = os.path.join(ROOT, "tests", "golden", name + ".json")
+        if os.path.exists(stored):
+            with open(stored) as f:
+                g = json.load(f)
+            leg["oracle_result"] = [g["min_energy"], g["argmin"], g["count"]]
+            leg["same_as_oracle"] = leg["oracle_result"] == leg["result"] and g["sha256_Q"] == qi.sha256_of(cfg["Q"])
+        legs[name] = leg
+        print("[bench] config", name, t, file=sys.stderr, flush=True)
+    return legs
 
 
 def split_sweep(q, Qd, cfg, prefixes, caches):

@@ -41,7 +41,8 @@ extern "C" {
 #define QUBO_OK 0
 #define QUBO_EINVAL (-1)  /* null pointer, n or a split parameter out of range */
 #define QUBO_ERANGE (-2)  /* int32 Q: sum |Q_ij| exceeds 2^30 - 1 (int32 would not be exact);
-                             binary64 Q: an entry not finite or sum |Q_ij| above 2^100 */
+                             binary64 Q: an entry not finite, or sum |Q_ij| above 2^100 or
+                             in (0, 2^-100) */
 #define QUBO_EPLAN (-3)   /* the requested split does not fit the kernel's registers/LDS/limits */
 #define QUBO_EDEVICE (-4) /* no usable gfx950 device, or a HIP runtime error */
 #define QUBO_ENOMEM (-5)  /* device or host allocation failed */
@@ -95,10 +96,24 @@ typedef struct {
  * table over 2^32 entries, M_int over 2^33 bytes, LDS over 64 KiB). */
 QUBO_API int qubo_make_plan(int n, int prefix_bits, int cache_bits, qubo_plan *out);
 
-/* Host only; touches no device.  Checks the overflow guard on a host copy of Q.
- * Writes sum |Q_ij| (int64) to *abs_sum if abs_sum is not NULL.
- * Returns QUBO_OK, QUBO_EINVAL or QUBO_ERANGE. */
-QUBO_API int qubo_check_q(const int32_t *Q_host, int n, int64_t *abs_sum);
+/* Host only; touches no device.  Checks the overflow guard on a host copy of Q
+ * (n x n int32, row-major): sum |Q_ij| <= 2^30 - 1.
+ * Returns QUBO_OK, QUBO_EINVAL (null Q, n outside [1, 63]) or QUBO_ERANGE. */
+QUBO_API int qubo_check_q(const int32_t *Q_host, int n);
+
+/* Host only; touches no device.  Writes sum |Q_ij| of a host int32 matrix
+ * (n x n, row-major), in int64, to *abs_sum; no range check.
+ * Returns QUBO_OK or QUBO_EINVAL (null pointer, n outside [1, 63]). */
+QUBO_API int qubo_abs_sum(const int32_t *Q_host, int n, int64_t *abs_sum);
+
+/* Host only; touches no device.  The guard of the binary64 searches
+ * (qubo_search_f64 and its relatives) on a host copy of Q (n x n binary64,
+ * row-major): every entry finite and S = sum |Q_ij| either 0 or in
+ * [2^-100, 2^100].  Above, fp32 values of the walk could overflow; below, the
+ * absolute error of fp32 arithmetic near its underflow threshold could exceed
+ * the re-evaluation margin 2^-14 S.
+ * Returns QUBO_OK, QUBO_EINVAL (null Q, n outside [1, 63]) or QUBO_ERANGE. */
+QUBO_API int qubo_check_q_f64(const double *Q_host, int n);
 
 /* Exhaustive search over all 2^n states (sec. III.B Algorithm 2 with the
  * splits of sec. III.C), on the HIP stream `stream` (a hipStream_t; NULL is the
@@ -221,8 +236,8 @@ typedef struct {
 /* Q: device pointer, n x n binary64, row-major; read only.  n: 1..58 (no
  * outer split).  prefix_bits, cache_bits, gray_lo, gray_hi, stream: as for
  * qubo_search_ex (cache_bits defaults to min(A, 10): binary64 rows in LDS).
- * flags: 0 or QUBO_FLAG_COLS8.  Every entry must be finite and sum |Q_ij| at
- * most 2^100 (else QUBO_ERANGE).
+ * flags: 0 or QUBO_FLAG_COLS8.  Every entry must be finite and sum |Q_ij|
+ * either 0 or in [2^-100, 2^100] (else QUBO_ERANGE; qubo_check_q_f64).
  * The walk is the integer kernel's, with a binary64 anchor per column advanced
  * once per eight 32-step bodies and every state one fp32 add; a
  * state whose fp32 energy comes within delta = 2^-14 sum |Q_ij| of the best

@@ -125,7 +125,7 @@ class Result:
 
 _lib = None
 
-EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_search", "qubo_search_range", "qubo_search_ex",
+EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_abs_sum", "qubo_check_q_f64", "qubo_search", "qubo_search_range", "qubo_search_ex",
            "qubo_build_tables", "qubo_last_timing", "qubo_search_lowest", "qubo_search_f64",
            "qubo_search_lowest_f64",
            "qubo_progress_init", "qubo_search_step", "qubo_progress_init_lowest", "qubo_search_step_lowest",
@@ -148,7 +148,9 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     i32p = ctypes.c_void_p
     lib.qubo_make_plan.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(_Plan)]
-    lib.qubo_check_q.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
+    lib.qubo_check_q.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.qubo_abs_sum.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
+    lib.qubo_check_q_f64.argtypes = [ctypes.c_void_p, ctypes.c_int]
     lib.qubo_search.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                 ctypes.POINTER(_Result)]
     lib.qubo_search_range.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
@@ -214,11 +216,28 @@ def check_q(Q_host) -> int:
     q = np.ascontiguousarray(np.asarray(Q_host, dtype=np.int32))
     if q.ndim != 2 or q.shape[0] != q.shape[1]:
         raise ValueError("Q must be square")
-    s = ctypes.c_int64(0)
-    rc = load().qubo_check_q(q.ctypes.data_as(ctypes.c_void_p), q.shape[0], ctypes.byref(s))
+    lib = load()
+    rc = lib.qubo_check_q(q.ctypes.data_as(ctypes.c_void_p), q.shape[0])
     if rc != QUBO_OK:
         raise QuboError(rc, "qubo_check_q")
+    s = ctypes.c_int64(0)
+    rc = lib.qubo_abs_sum(q.ctypes.data_as(ctypes.c_void_p), q.shape[0], ctypes.byref(s))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_abs_sum")
     return int(s.value)
+
+
+def check_q_f64(Q_host) -> None:
+    """Host-only guard of the binary64 searches on a host matrix (raises
+    QuboError(QUBO_ERANGE) for a non-finite entry or sum |Q_ij| outside
+    {0} and [2^-100, 2^100])."""
+    import numpy as np
+    q = np.ascontiguousarray(np.asarray(Q_host, dtype=np.float64))
+    if q.ndim != 2 or q.shape[0] != q.shape[1]:
+        raise ValueError("Q must be square")
+    rc = load().qubo_check_q_f64(q.ctypes.data_as(ctypes.c_void_p), q.shape[0])
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_check_q_f64")
 
 
 def _device_q(Q):

@@ -5,6 +5,10 @@
 The library is the C-ABI of include/qubo.h: host planning (plan.cpp), the HIP
 kernels (kernels.hip, kernels_f64.hip), the host side of the searches (host.hip,
 run_int.hip, run_f64.hip, run_steps.hip) and the entry points (capi.hip).
+
+The same call builds lib/qubo_valu_rate from csrc/valu_rate.hip: a stand-alone
+program that measures the vector ALU's issue rate per instruction form, the
+peak the search kernels are priced against.
 """
 from __future__ import annotations
 
@@ -21,6 +25,8 @@ LIB_PATH = os.path.join(LIB_DIR, "libqubo.so")
 SOURCES = ["plan.cpp", "kernels.hip", "kernels_f64.hip", "host.hip", "run_int.hip", "run_f64.hip", "run_steps.hip",
            "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+VALU_RATE_SOURCE = "valu_rate.hip"
+VALU_RATE_PATH = os.path.join(LIB_DIR, "qubo_valu_rate")
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -58,7 +64,23 @@ def build(verbose: bool = False) -> str:
         if lines:
             sys.stderr.write("\n".join(lines) + "\n")
     os.replace(tmp, LIB_PATH)
+    build_valu_rate(verbose)
     return LIB_PATH
+
+
+def build_valu_rate(verbose: bool = False) -> str:
+    """Compile the issue-rate program into lib/qubo_valu_rate (always recompiles)."""
+    tmp = VALU_RATE_PATH + ".tmp%d" % os.getpid()
+    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC", "-fvisibility=hidden")]
+    cmd = [HIPCC, *flags, os.path.join(CSRC, VALU_RATE_SOURCE), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building qubo_valu_rate")
+    os.replace(tmp, VALU_RATE_PATH)
+    return VALU_RATE_PATH
 
 
 if __name__ == "__main__":

@@ -19,12 +19,32 @@ QUBO_API int qubo_make_plan(int n, int prefix_bits, int cache_bits, qubo_plan *o
     return qubo::make_plan(n, prefix_bits, cache_bits, 256, 0, -1, out);
 }
 
-QUBO_API int qubo_check_q(const int32_t *Q_host, int n, int64_t *abs_sum)
+QUBO_API int qubo_check_q(const int32_t *Q_host, int n)
 {
     if (!Q_host || n < 1 || n > QUBO_MAX_N)
         return QUBO_EINVAL;
     std::vector<int32_t> U;
-    return qubo::fold_upper(Q_host, n, U, abs_sum);
+    return qubo::fold_upper(Q_host, n, U, nullptr);
+}
+
+QUBO_API int qubo_abs_sum(const int32_t *Q_host, int n, int64_t *abs_sum)
+{
+    if (!Q_host || !abs_sum || n < 1 || n > QUBO_MAX_N)
+        return QUBO_EINVAL;
+    int64_t s = 0;
+    for (size_t i = 0; i < (size_t)n * n; ++i)
+        s += Q_host[i] < 0 ? -(int64_t)Q_host[i] : (int64_t)Q_host[i];
+    *abs_sum = s;
+    return QUBO_OK;
+}
+
+QUBO_API int qubo_check_q_f64(const double *Q_host, int n)
+{
+    if (!Q_host || n < 1 || n > QUBO_MAX_N)
+        return QUBO_EINVAL;
+    const std::vector<double> Qh(Q_host, Q_host + (size_t)n * n);
+    double S = 0.0;
+    return guard_f64(Qh, &S);
 }
 
 QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bits, void *stream,

@@ -31,7 +31,8 @@ int read_q(const int32_t *Q, int n, hipStream_t stream, std::vector<int32_t> &Qh
 // FNV-1a (64 bit) over n (4 little-endian bytes) and the bytes of Q's entries.
 uint64_t fingerprint(const void *Qh, size_t bytes, int n);
 
-// The binary64 guard: finite entries and S = sum |Q_ij| (rounded up) <= 2^100.
+// The binary64 guard: finite entries and S = sum |Q_ij| (rounded up) either 0
+// or in [2^-100, 2^100] (QUBO_ERANGE otherwise).
 int guard_f64(const std::vector<double> &Qh, double *S_out);
 
 // Everything one call owns; released in the destructor on every path.

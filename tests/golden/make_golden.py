@@ -11,6 +11,8 @@ Calls only the CPU oracle (``oracle``) on the seeded workloads of
     python tests/golden/make_golden.py C1f C2f C4fsub   # real-valued (binary64) workloads, tier A
     python tests/golden/make_golden.py C58sub           # n = 58 (largest single launch): 2^36-state sub-cubes
     python tests/golden/make_golden.py C1flow C4fsublow # binary64 spectrum: whole C1f, two C4f sub-cubes
+    python tests/golden/make_golden.py C4sub36 C5sub37  # deeper sub-cubes: 2^36 (n=48) and 2^37 (n=50) states
+    python tests/golden/make_golden.py C4slice          # 8 consecutive 2^37-state sub-cubes of n=48 (2^40 states)
 
 Full searches store {sha256_Q, n, min_energy, argmin, count, max_abs_energy}.
 Sub-cube files store one record per sub-cube: the first k variables are fixed
@@ -236,11 +238,80 @@ def subcubes_max(name: str, threads: int) -> dict:
                 seconds_total=round(time.time() - t_all, 2), host=host_info(threads))
 
 
+DEEP_COUNT = {"C4": 4, "C5": 3}
+
+
+def subcubes_deep(name: str, free: int, threads: int) -> dict:
+    """Sub-cubes of 2^free states (the first n - free variables fixed): with the
+    prefix walked over 28 variables they span 2^(28 - n + free) Gray steps, so
+    the walk flips prefix variables far above the low ones."""
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    k = n - free
+    rng = qi.SplitMix64(SUB_SEED + 300 + free + n)
+    tops = []
+    while len(tops) < DEEP_COUNT[name]:
+        t = rng.uniform_int(0, (1 << k) - 1)
+        if t not in tops:
+            tops.append(t)
+    cubes = []
+    t_all = time.time()
+    for top in tops:
+        t0 = time.time()
+        r = oracle.search_gray(Q, k=k, top=top, threads=threads)
+        cubes.append(dict(k=k, top=top, min_energy=r.min_energy, argmin=r.argmin, count=r.count,
+                          max_abs_energy=r.max_abs_energy, seconds=round(time.time() - t0, 2)))
+        print("  %s top=%d -> %s" % (name, top, r.triple()), flush=True)
+    return dict(name="%ssub%d" % (name, free), desc=cfg["desc"], n=n, seed=cfg["seed"],
+                sha256_Q=qi.sha256_of(Q), free_bits=free, sub_seed=SUB_SEED + 300 + free + n, cubes=cubes,
+                tier="B (Gray walk)", seconds_total=round(time.time() - t_all, 2), host=host_info(threads))
+
+
+SLICE_K = 11
+SLICE_CUBES = 8
+
+
+def long_slice(name: str, threads: int) -> dict:
+    """SLICE_CUBES sub-cubes with the first SLICE_K variables fixed whose values
+    are g(j) for SLICE_CUBES consecutive j, starting at an odd j (seeded): the
+    union of the ranges [j 2^(A-k), (j+1) 2^(A-k)) of any A-variable prefix walk,
+    so one contiguous Gray range.  Each cube's result, and the combination of
+    all of them by the rule of the final reduction (minimum, count at the
+    minimum, lowest index)."""
+    cfg = qi.make_config(name)
+    Q, n = cfg["Q"], cfg["n"]
+    k = SLICE_K
+    rng = qi.SplitMix64(SUB_SEED + 400 + n)
+    j0 = 2 * rng.uniform_int(0, ((1 << k) - SLICE_CUBES - 1) // 2) + 1
+    cubes = []
+    best = None
+    t_all = time.time()
+    for j in range(j0, j0 + SLICE_CUBES):
+        top = j ^ (j >> 1)
+        t0 = time.time()
+        r = oracle.search_gray(Q, k=k, top=top, threads=threads)
+        cubes.append(dict(k=k, j=j, top=top, min_energy=r.min_energy, argmin=r.argmin, count=r.count,
+                          seconds=round(time.time() - t0, 2)))
+        print("  %s j=%d top=%d -> %s" % (name, j, top, r.triple()), flush=True)
+        if best is None or r.min_energy < best[0]:
+            best = [r.min_energy, r.argmin, r.count]
+        elif r.min_energy == best[0]:
+            best = [best[0], min(best[1], r.argmin), best[2] + r.count]
+    return dict(name=name + "slice", desc=cfg["desc"], n=n, seed=cfg["seed"], sha256_Q=qi.sha256_of(Q),
+                k=k, j_first=j0, cubes_in_slice=SLICE_CUBES, slice_seed=SUB_SEED + 400 + n, cubes=cubes,
+                min_energy=best[0], argmin=best[1], count=best[2], tier="B (Gray walk)",
+                seconds_total=round(time.time() - t_all, 2), host=host_info(threads))
+
+
 def main(argv):
     threads = oracle.default_threads()
     for arg in argv:
         print("computing", arg, "on", threads, "threads", flush=True)
-        if arg == "C58sub":
+        if arg in ("C4sub36", "C5sub37"):
+            rec = subcubes_deep(arg[:2], int(arg[5:]), threads)
+        elif arg == "C4slice":
+            rec = long_slice("C4", threads)
+        elif arg == "C58sub":
             rec = subcubes_max("C58", threads)
         elif arg == "C1flow":
             rec = lowest_full_f64("C1f", threads)

@@ -95,6 +95,45 @@ def test_check_q_guard():
     assert q.check_q(R) == 11
 
 
+def test_check_q_f64_guard():
+    """The binary64 guard: finite entries and S = sum |Q_ij| either 0 or in
+    [2^-100, 2^100].  The floor keeps the re-evaluation margin 2^-14 S above
+    the absolute error of fp32 arithmetic near its underflow threshold."""
+    q.check_q_f64(np.zeros((4, 4)))
+    q.check_q_f64(-np.zeros((4, 4)))  # negative zeros: S = 0
+    for bad in (np.nan, np.inf, -np.inf):
+        Q = np.ones((3, 3))
+        Q[1, 2] = bad
+        with pytest.raises(q.QuboError) as e:
+            q.check_q_f64(Q)
+        assert e.value.code == q.QUBO_ERANGE
+    # S just above the floor passes, just below it fails; the sum is rounded up
+    # by the guard (a factor 1 + 2^-40), so test a little way from 2^-100
+    Q = np.zeros((2, 2))
+    Q[0, 0] = 2.0 ** -100 * (1 + 2.0 ** -30)
+    q.check_q_f64(Q)
+    Q[0, 0] = 2.0 ** -100 * (1 - 2.0 ** -30)
+    with pytest.raises(q.QuboError) as e:
+        q.check_q_f64(Q)
+    assert e.value.code == q.QUBO_ERANGE
+    # one entry deep in fp32's subnormal range next to one that lifts S above the floor
+    Q = np.full((3, 3), 2.0 ** -140)
+    Q[2, 2] = 2.0 ** -99
+    q.check_q_f64(Q)
+    Q[2, 2] = 2.0 ** -102
+    with pytest.raises(q.QuboError) as e:
+        q.check_q_f64(Q)
+    assert e.value.code == q.QUBO_ERANGE
+    # the upper end
+    Q = np.zeros((2, 2))
+    Q[0, 1] = 2.0 ** 99
+    q.check_q_f64(Q)
+    Q[1, 0] = 2.0 ** 99 * 1.01
+    with pytest.raises(q.QuboError) as e:
+        q.check_q_f64(Q)
+    assert e.value.code == q.QUBO_ERANGE
+
+
 def test_null_and_range_arguments_rejected_before_the_device():
     lib = q.load()
     r = q._Result()
@@ -109,7 +148,14 @@ def test_null_and_range_arguments_rejected_before_the_device():
     assert lib.qubo_search_range(ctypes.c_void_p(16), 4, 4, -1, 0, 32, None,
                                  ctypes.byref(r)) == q.QUBO_EINVAL
     assert lib.qubo_build_tables(ctypes.c_void_p(16), 12, 6, None, None, None, None) == q.QUBO_EINVAL
-    assert lib.qubo_check_q(None, 3, None) == q.QUBO_EINVAL
+    assert lib.qubo_check_q(None, 3) == q.QUBO_EINVAL
+    assert lib.qubo_check_q_f64(None, 3) == q.QUBO_EINVAL
+    s = ctypes.c_int64(-7)
+    assert lib.qubo_abs_sum(None, 3, ctypes.byref(s)) == q.QUBO_EINVAL
+    z = np.zeros((3, 3), dtype=np.int32)
+    assert lib.qubo_abs_sum(z.ctypes.data_as(ctypes.c_void_p), 3, None) == q.QUBO_EINVAL
+    assert lib.qubo_abs_sum(z.ctypes.data_as(ctypes.c_void_p), 64, ctypes.byref(s)) == q.QUBO_EINVAL
+    assert s.value == -7
     assert r.count == 0  # untouched
     # spectrum: k in 1..64, outputs present, no strict mode, no unknown flags, valid slices
     out = (q._State * 64)()

@@ -98,6 +98,31 @@ def test_every_split_real(q, n):
             check_coverage(q, n, A, l)
 
 
+@pytest.mark.parametrize("case", ["normal", "subnormal"])
+def test_near_the_floor(q, case):
+    """S = sum |Q_ij| just above the guard's floor 2^-100.  'normal': every entry
+    in fp32's normal range (about 2^-107), so the re-evaluation margin 2^-14 S
+    is tight around the minimum.  'subnormal': every entry but one in fp32's
+    subnormal range (below 2^-126), where fp32 keeps only a few bits and errs by
+    an absolute amount; one diagonal entry lifts S above the floor.  The
+    minimum, its lowest index, the count and the 16 lowest states equal the
+    oracle's binary64 definition."""
+    n = 14
+    rng = np.random.default_rng(8701 if case == "normal" else 8702)
+    Q = rng.uniform(-1.0, 1.0, size=(n, n))
+    if case == "normal":
+        Q *= 1.5 * 2.0 ** -100 / np.abs(Q).sum()
+    else:
+        Q *= 2.0 ** -136
+        Q[3, 3] = -(2.0 ** -100)
+    q.check_q_f64(Q)
+    Qd = dev_f(Q)
+    announce("f64 near the floor", case)
+    assert q.search_f64(Qd).triple() == oracle.search_direct_f64(Q).triple()
+    announce("f64 near the floor lowest", case)
+    assert q.lowest(Qd, 16) == oracle.lowest_f64(Q, 16)
+
+
 def test_zero_and_diagonal(q):
     announce("f64 zero")
     assert q.search_f64(dev_f(np.zeros((8, 8)))).triple() == (0.0, 0, 256)
@@ -252,6 +277,10 @@ def test_f64_errors(q):
         with pytest.raises(q.QuboError) as e:
             q.search_f64(dev_f(Qb))
         assert e.value.code == q.QUBO_ERANGE
+    # S below the floor 2^-100 (rejected on the host, before any kernel)
+    with pytest.raises(q.QuboError) as e:
+        q.search_f64(dev_f(Q * (2.0 ** -100 / np.abs(Q).sum() / 2)))
+    assert e.value.code == q.QUBO_ERANGE
     lib = q.load()
     r = q._ResultF64()
     Qd = dev_f(real_matrix(59, 8501))

@@ -234,26 +234,62 @@ def test_ragged_slices(q, lo, hi):
         [(int(E[i]), int(idx[i])) for i in order]
 
 
-def test_subcubes_at_full_size(q):
-    """n = 48 and n = 50 at the benchmark's split: seeded sub-cubes of 2^32
-    states against the stored oracle results (tests/golden/C4sub, C5sub)."""
-    for name in ("C4sub", "C5sub"):
-        g = golden(name)
-        cfg = qi.make_config(name[:-3])
-        assert qi.sha256_of(cfg["Q"]) == g["sha256_Q"]
-        n = cfg["n"]
-        plan = q.make_plan(n)
-        A = plan["prefix_bits"]
-        Qd = dev_q(cfg["Q"])
-        for i, cube in enumerate(g["cubes"]):
-            k, top = cube["k"], cube["top"]
-            m = inv_gray(top)
-            lo, hi = m << (A - k), (m + 1) << (A - k)
-            strict, R = bool(i % 2), (8 if i % 4 < 2 else 16)
-            announce("subcube", name, k, top, strict, R)
-            r = q.search_range(Qd, A, lo, hi, strict=strict, cols_per_lane=R)
-            assert r.triple() == (cube["min_energy"], cube["argmin"], cube["count"])
-            check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
+@pytest.mark.parametrize("name", ["C4sub", "C5sub", "C4sub36", "C5sub37"])
+def test_subcubes_at_full_size(q, name):
+    """n = 48 and n = 50 at the benchmark's split (A = 28): seeded sub-cubes
+    against the stored oracle results, each in one of the four kernel builds
+    (bound-gated or strict, 8 or 16 columns per lane).  C4sub and C5sub hold
+    2^32 states (2^12 and 2^10 Gray steps); C4sub36 and C5sub37 hold 2^36 and
+    2^37 states (2^16 and 2^15 Gray steps), so the walk flips prefix bits at
+    and above cache_bits, whose rows come from global memory."""
+    g = golden(name)
+    cfg = qi.make_config(name[:2])
+    assert qi.sha256_of(cfg["Q"]) == g["sha256_Q"]
+    n = cfg["n"]
+    plan = q.make_plan(n)
+    A = plan["prefix_bits"]
+    Qd = dev_q(cfg["Q"])
+    for i, cube in enumerate(g["cubes"]):
+        k, top = cube["k"], cube["top"]
+        m = inv_gray(top)
+        lo, hi = m << (A - k), (m + 1) << (A - k)
+        if name.endswith(("36", "37")):
+            assert (hi - lo) >> plan["cache_bits"] >= 2  # bits above the cached ones flip
+        strict, R = bool(i % 2), (8 if i % 4 < 2 else 16)
+        announce("subcube", name, k, top, strict, R)
+        r = q.search_range(Qd, A, lo, hi, strict=strict, cols_per_lane=R)
+        assert r.triple() == (cube["min_energy"], cube["argmin"], cube["count"])
+        check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
+
+
+def test_long_slice_at_full_size(q):
+    """n = 48 at the benchmark's split: a slice of 2^20 Gray steps (2^40 states)
+    that starts in the middle of a 2^18-step work-unit segment, so it spans five
+    segments (a part of the first, three whole, a part of the last) and every
+    wave of a workgroup walks one; against the stored oracle result
+    (tests/golden/C4slice.json: eight consecutive sub-cubes, combined by the
+    final reduction's rule), in all four kernel builds, and per sub-cube."""
+    g = golden("C4slice")
+    cfg = qi.make_config("C4")
+    assert qi.sha256_of(cfg["Q"]) == g["sha256_Q"]
+    n = cfg["n"]
+    plan = q.make_plan(n)
+    A, seg = plan["prefix_bits"], plan["seg_bits"]
+    k, j0, c = g["k"], g["j_first"], g["cubes_in_slice"]
+    assert [cube["top"] for cube in g["cubes"]] == [gray(j) for j in range(j0, j0 + c)]
+    lo, hi = j0 << (A - k), (j0 + c) << (A - k)
+    assert lo % (1 << seg) != 0 and (hi - 1 >> seg) - (lo >> seg) + 1 >= 5
+    Qd = dev_q(cfg["Q"])
+    for strict, R in ((False, 8), (True, 8), (False, 16), (True, 16)):
+        announce("long slice", lo, hi, strict, R)
+        r = q.search_range(Qd, A, lo, hi, strict=strict, cols_per_lane=R)
+        assert r.triple() == (g["min_energy"], g["argmin"], g["count"]), (strict, R)
+        check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
+    for cube in g["cubes"]:
+        j = cube["j"]
+        announce("long slice cube", j)
+        r = q.search_range(Qd, A, j << (A - k), (j + 1) << (A - k))
+        assert r.triple() == (cube["min_energy"], cube["argmin"], cube["count"]), j
 
 
 @pytest.mark.parametrize("n,k,seed,lo,hi", [(9, 4, 7501, -50, 50), (14, 3, 7502, -2, 2),

@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import json
 import os
+import re
 
 import numpy as np
 import pytest
@@ -362,14 +363,27 @@ def test_numpy_reference_itself():
 
 
 def test_generators_are_stable():
-    """The seeded workloads hash to the values recorded with the stored results."""
-    for name in ("C1", "C2", "C2p", "C3", "C4", "C5"):
-        path = os.path.join(GOLDEN, name + ".json")
-        if not os.path.exists(path):
-            pytest.skip("stored result for %s not written yet" % name)
-        with open(path) as f:
+    """The seeded workloads hash to the values recorded with every stored result
+    (whole spaces, sub-cubes, slices and spectra): each stored file names its
+    workload by the leading part of its name (C4sub36 -> C4, C2plow -> C2p)."""
+    hashes = {}
+    checked = set()
+    for fname in sorted(os.listdir(GOLDEN)):
+        if not fname.endswith(".json"):
+            continue
+        with open(os.path.join(GOLDEN, fname)) as f:
             rec = json.load(f)
-        assert qi.sha256_of(qi.make_config(name)["Q"]) == rec["sha256_Q"], name
+        if "sha256_Q" not in rec:
+            continue
+        m = re.match(r"C\d+[pf]?", fname)
+        assert m, fname
+        name = m.group(0)
+        if name not in hashes:
+            hashes[name] = qi.sha256_of(qi.make_config(name)["Q"])
+        assert hashes[name] == rec["sha256_Q"], fname
+        checked.add(name)
+    # every benchmark workload has stored results to check against
+    assert {"C1", "C2", "C2p", "C3", "C4", "C5", "C1f", "C2f", "C4f", "C58"} <= checked, checked
 
 
 def test_config_families():
