@@ -295,8 +295,8 @@ QUBO_API const char *qubo_strerror(int status)
     case QUBO_EINVAL:
         return "invalid argument";
     case QUBO_ERANGE:
-        return "Q out of range (int32: sum of |Q_ij| above 2^30-1; binary64: an entry not finite "
-               "or sum of |Q_ij| above 2^100)";
+        return "Q out of range (int32: sum of |Q_ij| above 2^30-1; binary64: an entry not finite, "
+               "or sum of |Q_ij| above 2^100 or in (0, 2^-100))";
     case QUBO_EPLAN:
         return "split does not fit the kernel (prefix/cache bits out of the supported range)";
     case QUBO_EDEVICE:
