@@ -7,10 +7,10 @@
 // update is issued (the compiler may not fold or vectorise across it).  Per
 // form it prints:
 //   * lane-ops/s = threads x trips x 128 updates / kernel time (HIP events);
-//   * cycles per wave-instruction on one SIMD: the shader-clock ticks (s_memtime)
-//     a wave spends in the loop, divided by the instructions all waves sharing its
-//     SIMD issue meanwhile (waves per SIMD x updates per wave);
-//   * the shader clock itself: s_memtime ticks over s_memrealtime ticks (100 MHz).
+//   * the shader clock during the loop: s_memtime ticks (shader clock) over
+//     s_memrealtime ticks (a constant 100 MHz), summed over one wave per workgroup;
+//   * cycles per wave-instruction on one SIMD: kernel time x that clock, over the
+//     instructions each SIMD issues (waves per SIMD x updates per wave).
 // Forms: v_add_u32 with two VGPR operands, with an inline constant and with an
 // SGPR; v_min3_i32 over three VGPRs; v_pk_add_u16 (two 16-bit adds per lane);
 // v_add_f32 with two VGPRs.
@@ -151,7 +151,7 @@ int main()
         const int blocks = cus * wps;
         for (int form = 0; form < kForms; ++form) {
             float best = 1e30f;
-            double cyc = 0.0, mhz = 0.0;
+            double mhz = 0.0;
             for (int rep = 0; rep < 2; ++rep) {
                 if (!ok(hipEventRecord(e0), "hipEventRecord"))
                     return 1;
@@ -171,11 +171,11 @@ int main()
                         c += (double)h[2 * b];
                         w += (double)h[2 * b + 1];
                     }
-                    const double instr_per_wave = (double)trips * kRounds * kRegs;
-                    cyc = c / blocks / (instr_per_wave * wps);
                     mhz = w > 0 ? c / w * 100.0 : 0.0;  // s_memrealtime runs at 100 MHz
                 }
             }
+            const double instr_per_wave = (double)trips * kRounds * kRegs;
+            const double cyc = best * 1e-3 * mhz * 1e6 / (instr_per_wave * wps);
             const double ops = (double)blocks * kThreads * trips * kRounds * kRegs * kElems[form];
             std::printf("%-18s %10d %9.2f %14.4e %16.3f %12.0f\n", kNames[form], wps, best, ops / (best * 1e-3),
                         cyc, mhz);
