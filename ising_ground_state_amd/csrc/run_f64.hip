@@ -46,8 +46,9 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     if (lds_bytes > kMaxLdsBytes)
         return QUBO_EPLAN;
 
-    // Q to the host; the guard: finite entries and sum |Q_ij| <= 2^100, so that
-    // fp32 energies never overflow.
+    // Q to the host; the guard: finite entries and sum |Q_ij| either 0 or in
+    // [2^-100, 2^100], so that fp32 energies never overflow and the absolute
+    // error of fp32 near underflow stays inside the re-evaluation margin.
     std::vector<double> Qh((size_t)n * n);
     if (hipMemcpyAsync(Qh.data(), rq.Q, Qh.size() * 8, hipMemcpyDeviceToHost, rq.stream) !=
             hipSuccess ||
