@@ -46,6 +46,8 @@ extern "C" {
 #define QUBO_EPLAN (-3)   /* the requested split does not fit the kernel's registers/LDS/limits */
 #define QUBO_EDEVICE (-4) /* no usable gfx950 device, or a HIP runtime error */
 #define QUBO_ENOMEM (-5)  /* device or host allocation failed */
+#define QUBO_ESCRATCH (-6) /* qubo_search_noalloc: the search needs more device memory than
+                              its static buffer holds (QUBO_NOALLOC_BYTES) */
 
 #define QUBO_MAX_N 63
 
@@ -132,6 +134,29 @@ QUBO_API int qubo_check_q_f64(const double *Q_host, int n);
  * Ties: argmin is the lowest index among all minimisers, count is exact. */
 QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bits, void *stream,
                 qubo_result *out);
+
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): qubo_search without
+ * any allocation.  Same arguments, result, blocking and error behaviour as
+ * qubo_search; in place of the stream-ordered workspace, every call on a GPU
+ * uses one static device buffer of QUBO_NOALLOC_BYTES (128 MiB) that the
+ * library holds on each GPU it runs on until the process ends.
+ *   - Sizes: the plan's workspace (U, E_s, M_int, 4 x 2^prefix_bits bytes of
+ *     prefix energies and their per-body minima, 32 bytes per wave, 256 bytes)
+ *     must fit the buffer, else QUBO_ESCRATCH before any device work.  The
+ *     planner's default split fits up to n = 40 (72.5 MiB at n = 40); larger n
+ *     fit with a smaller prefix_bits while M_int stays small (n = 42 at
+ *     prefix_bits 24: 90 MiB); n = 48 does not fit.
+ *   - The buffer keeps the last call's contents; every call writes what it
+ *     reads before reading it (its tables, partials and counters come from its
+ *     own kernels, with no memset), so nothing carries over between calls.
+ *   - Calls that overlap on one GPU race on the buffer: serialise them (one
+ *     stream, or one call at a time per GPU).
+ *   - No HIP events are created: qubo_last_timing then reports the coverage
+ *     counters and the zero stage times. */
+#define QUBO_NOALLOC_BYTES (128u << 20)
+QUBO_API int qubo_search_noalloc(const int32_t *Q, int n, int prefix_bits, int cache_bits, void *stream,
+                                 qubo_result *out);
 
 /* Per-stage device times and coverage counters of the last search on this host
  * thread; times come from HIP events recorded on the call's stream around each

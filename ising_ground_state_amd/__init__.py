@@ -29,6 +29,7 @@ QUBO_ERANGE = -2
 QUBO_EPLAN = -3
 QUBO_EDEVICE = -4
 QUBO_ENOMEM = -5
+QUBO_ESCRATCH = -6
 MAX_N = 63
 
 
@@ -125,7 +126,7 @@ class Result:
 
 _lib = None
 
-EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_abs_sum", "qubo_check_q_f64", "qubo_search", "qubo_search_range", "qubo_search_ex",
+EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_abs_sum", "qubo_check_q_f64", "qubo_search", "qubo_search_noalloc", "qubo_search_range", "qubo_search_ex",
            "qubo_build_tables", "qubo_last_timing", "qubo_search_lowest", "qubo_search_f64",
            "qubo_search_lowest_f64",
            "qubo_progress_init", "qubo_search_step", "qubo_progress_init_lowest", "qubo_search_step_lowest",
@@ -153,6 +154,8 @@ def load(path: str = LIB_PATH):
     lib.qubo_check_q_f64.argtypes = [ctypes.c_void_p, ctypes.c_int]
     lib.qubo_search.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                 ctypes.POINTER(_Result)]
+    lib.qubo_search_noalloc.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.POINTER(_Result)]
     lib.qubo_search_range.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
                                       ctypes.c_uint64, ctypes.c_void_p, ctypes.POINTER(_Result)]
     lib.qubo_search_ex.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
@@ -292,6 +295,22 @@ def search(Q, prefix_bits: int | None = None, cache_bits: int | None = None, str
                                     _opt(cache_bits), _stream(Q, stream), ctypes.byref(r))
     if rc != QUBO_OK:
         raise QuboError(rc, "qubo_search")
+    return Result(r.min_energy, r.argmin, r.count)
+
+
+def search_noalloc(Q, prefix_bits: int | None = None, cache_bits: int | None = None, stream=None) -> Result:
+    """search() through qubo_search_noalloc: no device allocation; the library's
+    static 128 MiB buffer per GPU holds the workspace (QuboError(QUBO_ESCRATCH)
+    when the plan needs more).  Calls that overlap on one GPU must be
+    serialised."""
+    import torch
+    Q = _device_q(Q)
+    r = _Result()
+    with torch.cuda.device(Q.device):
+        rc = load().qubo_search_noalloc(ctypes.c_void_p(Q.data_ptr()), Q.shape[0], _opt(prefix_bits),
+                                        _opt(cache_bits), _stream(Q, stream), ctypes.byref(r))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_search_noalloc")
     return Result(r.min_energy, r.argmin, r.count)
 
 

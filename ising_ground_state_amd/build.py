@@ -4,7 +4,8 @@
 
 The library is the C-ABI of include/qubo.h: host planning (plan.cpp), the HIP
 kernels (kernels.hip, kernels_f64.hip), the host side of the searches (host.hip,
-run_int.hip, run_f64.hip, run_steps.hip) and the entry points (capi.hip).
+run_int.hip, run_f64.hip, run_steps.hip) and the entry points (capi.hip, and
+noalloc.hip for the search that allocates nothing).
 
 The same call builds lib/qubo_valu_rate from csrc/valu_rate.hip: a stand-alone
 program that measures the vector ALU's issue rate per instruction form, the
@@ -23,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libqubo.so")
 SOURCES = ["plan.cpp", "kernels.hip", "kernels_f64.hip", "host.hip", "run_int.hip", "run_f64.hip", "run_steps.hip",
-           "capi.hip"]
+           "capi.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 VALU_RATE_SOURCE = "valu_rate.hip"
 VALU_RATE_PATH = os.path.join(LIB_DIR, "qubo_valu_rate")

@@ -303,6 +303,8 @@ QUBO_API const char *qubo_strerror(int status)
         return "no usable gfx950 device or HIP runtime error";
     case QUBO_ENOMEM:
         return "out of device memory";
+    case QUBO_ESCRATCH:
+        return "the search's workspace exceeds the static buffer of qubo_search_noalloc (128 MiB)";
     default:
         return "unknown status";
     }

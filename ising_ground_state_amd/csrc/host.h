@@ -39,6 +39,9 @@ int guard_f64(const std::vector<double> &Qh, double *S_out);
 struct Call {
     hipStream_t stream = nullptr;
     void *ws = nullptr;
+    // Work enqueued on a caller-provided workspace: the destructor waits for it,
+    // so that no call returns while its kernels still use that buffer.
+    bool enqueued = false;
     hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
 
     // Every event that was created is destroyed, also after a partial failure.
@@ -57,6 +60,8 @@ struct Call {
     {
         if (ws) {
             (void)hipFreeAsync(ws, stream);
+            (void)hipStreamSynchronize(stream);
+        } else if (enqueued) {
             (void)hipStreamSynchronize(stream);
         }
         for (auto &e : ev)
@@ -81,6 +86,10 @@ struct Request {
     int split_bits = 0;     // 0: automatic (only above the single-launch limit)
     int lowest_k = 0;       // > 0: the spectrum search (the lowest_k lowest states)
     int32_t *es_out = nullptr, *mint_out = nullptr, *ep_out = nullptr;
+    // Caller-provided device workspace (qubo_search_noalloc): used instead of a
+    // stream-ordered allocation, and no HIP events are created (no stage times).
+    void *scratch = nullptr;
+    uint64_t scratch_bytes = 0;
 };
 
 struct RequestF64 {

@@ -4,7 +4,8 @@
 //      triangle and check the overflow guard;
 //   2. plan the split (prefix A, suffix B, cached Gray bits, work units);
 //   3. one stream-ordered allocation for U, E_s, M_int, the Gray-ordered E_p,
-//      the per-wave partial results and a control block;
+//      the per-wave partial results and a control block (or the caller's
+//      device buffer, for the entry point that allocates nothing);
 //   4. cache builders, search kernel, final reduction, 64-byte result download;
 //   5. free and synchronise the stream.
 // Above 58 variables (or when asked for) the 2^k sub-problems of the
@@ -76,12 +77,20 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     const uint64_t off_low_found = off_low_out + kMaxLowest * sizeof(LowEntry);
     const uint64_t ws_total = lowest ? off_low_found + 256 : L.total;
 
-    // Workspace.
-    if (hipMallocAsync(&call.ws, ws_total, rq.stream) != hipSuccess) {
-        call.ws = nullptr;
-        return QUBO_ENOMEM;
+    // Workspace: one stream-ordered allocation, or the caller's buffer.
+    char *base = nullptr;
+    if (rq.scratch) {
+        if (ws_total > rq.scratch_bytes)
+            return QUBO_ESCRATCH;
+        base = static_cast<char *>(rq.scratch);
+        call.enqueued = true;
+    } else {
+        if (hipMallocAsync(&call.ws, ws_total, rq.stream) != hipSuccess) {
+            call.ws = nullptr;
+            return QUBO_ENOMEM;
+        }
+        base = static_cast<char *>(call.ws);
     }
-    char *base = static_cast<char *>(call.ws);
     int32_t *dU = reinterpret_cast<int32_t *>(base + L.off_u);
     int32_t *des = reinterpret_cast<int32_t *>(base + L.off_es);
     int32_t *dmint = reinterpret_cast<int32_t *>(base + L.off_mint);
@@ -90,18 +99,21 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     Partial *dpart = reinterpret_cast<Partial *>(base + L.off_partials);
     Ctrl *dctrl = reinterpret_cast<Ctrl *>(base + L.off_ctrl);
 
-    if (!call.create_events())
+    // Stage times come from events, which a call that must not allocate skips.
+    const bool timed = !rq.scratch;
+    if (timed && !call.create_events())
         return QUBO_EDEVICE;
+    auto mark = [&](int i) { return !timed || hipEventRecord(call.ev[i], rq.stream) == hipSuccess; };
 
     // Upload, build, search, reduce.
-    if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess)
+    if (!mark(0))
         return QUBO_EDEVICE;
     if (hipMemcpyAsync(dU, U.data(), U.size() * 4, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     if (launch_build_tables(dU, ns, A, B, L.cols_padded, des, dmint, dep, depmin, lo, hi, rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;
-    if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess)
+    if (!mark(1))
         return QUBO_EDEVICE;
 
     if (rq.mode == Mode::Build) {
@@ -158,14 +170,14 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     if (launch_search(sa, plan.cols_per_lane, rq.gated, lowest, plan.blocks, plan.lds_bytes,
                       rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
-    if (hipEventRecord(call.ev[2], rq.stream) != hipSuccess)
+    if (!mark(2))
         return QUBO_EDEVICE;
     if (launch_reduce(dpart, plan.blocks * plan.waves_per_block, dctrl, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     if (lowest && launch_lowest_merge(dlists, list_entries, k_low, dlow, dlow_found, rq.stream) !=
                       hipSuccess)
         return QUBO_EDEVICE;
-    if (hipEventRecord(call.ev[3], rq.stream) != hipSuccess)
+    if (!mark(3))
         return QUBO_EDEVICE;
     Ctrl host_ctrl;
     LowEntry host_low[kMaxLowest];
@@ -179,20 +191,21 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
          hipMemcpyAsync(&host_low_found, dlow_found, sizeof(int32_t), hipMemcpyDeviceToHost,
                         rq.stream) != hipSuccess))
         return QUBO_EDEVICE;
-    if (hipEventRecord(call.ev[4], rq.stream) != hipSuccess ||
-        hipStreamSynchronize(rq.stream) != hipSuccess)
+    if (!mark(4) || hipStreamSynchronize(rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
 
     qubo_timing t{};
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, call.ev[0], call.ev[1]) == hipSuccess)
-        t.build_ms = ms;
-    if (hipEventElapsedTime(&ms, call.ev[1], call.ev[2]) == hipSuccess)
-        t.search_ms = ms;
-    if (hipEventElapsedTime(&ms, call.ev[2], call.ev[3]) == hipSuccess)
-        t.reduce_ms = ms;
-    if (hipEventElapsedTime(&ms, call.ev[0], call.ev[4]) == hipSuccess)
-        t.total_ms = ms;
+    if (timed) {
+        if (hipEventElapsedTime(&ms, call.ev[0], call.ev[1]) == hipSuccess)
+            t.build_ms = ms;
+        if (hipEventElapsedTime(&ms, call.ev[1], call.ev[2]) == hipSuccess)
+            t.search_ms = ms;
+        if (hipEventElapsedTime(&ms, call.ev[2], call.ev[3]) == hipSuccess)
+            t.reduce_ms = ms;
+        if (hipEventElapsedTime(&ms, call.ev[0], call.ev[4]) == hipSuccess)
+            t.total_ms = ms;
+    }
     t.states = (hi - lo) << B;
     t.slow_bodies = host_ctrl.slow_total;
     t.bodies = host_ctrl.bodies_total;
