@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert "gfx950" in q.version()
-    for code in (0, -1, -2, -3, -4, -5, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
         assert q.strerror(code)
 
 
