@@ -7,15 +7,18 @@
 
 namespace qubo {
 
-// One wave's partial result (32 bytes) with its coverage counters.
+// One workgroup's partial result (40 bytes) with its coverage counters.
 struct Partial {
     int32_t e;         // min energy seen (INT32_MAX when count == 0)
     uint32_t slow;     // bodies re-walked on the exact path (records and ties)
     uint64_t count;    // states attaining e
     uint64_t arg;      // smallest index attaining e
-    uint32_t bodies;   // 32-step bodies walked (each covers 32 x 1024 states)
+    uint64_t bodies;   // 32-step bodies walked (each over 64 x cols_per_lane columns)
     uint32_t checked;  // bodies that ran the per-step minimum
+    uint32_t pad;
 };
+constexpr int kPartialBytes = 64;  // workspace bytes reserved per workgroup's partial
+static_assert(sizeof(Partial) <= kPartialBytes, "partial slot");
 
 // One entry of a low-energy list: a state's energy and index (16 bytes).
 // e == INT32_MAX marks an empty slot (no energy reaches it: |E| <= 2^30 - 1).
@@ -43,7 +46,7 @@ struct SearchArgs {
     const int32_t *mint;    // [A][cols_padded]    M_int rows by prefix variable
     const int32_t *ep;      // [2^A]               prefix energies in Gray order
     const int32_t *epmin;   // [2^A / 32 + 2]      min of ep over each 32-step body, + 2 padding
-    Partial *partials;      // [gridDim.x * waves per block]
+    Partial *partials;      // [gridDim.x]: one per workgroup
     Ctrl *ctrl;
     LowEntry *lists;        // [gridDim.x * waves per block][k_low] (spectrum search only)
     uint64_t cols_padded;

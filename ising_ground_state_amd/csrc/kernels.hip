@@ -121,25 +121,102 @@ __device__ __forceinline__ void combine(int &e, uint64_t &cnt, uint64_t &arg, in
     }
 }
 
+// Cross-lane moves through DPP (data-parallel primitives: the source lane is
+// picked by the VALU instruction itself, no LDS round trip).  gfx9 controls:
+// quad_perm within 4 lanes, mirrors within 8 and 16 lanes, and the broadcasts of
+// lane 15 of each row into the next row and of lane 31 into rows 2 and 3.  Lanes
+// of rows outside row_mask keep `old`.
+constexpr int kDppSwap1 = 0xB1;      // quad_perm [1, 0, 3, 2]: lane ^ 1
+constexpr int kDppSwap2 = 0x4E;      // quad_perm [2, 3, 0, 1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within 8 lanes
+constexpr int kDppMirror = 0x140;    // lane i <- 15 - i within 16 lanes
+constexpr int kDppBcast15 = 0x142;   // rows 1, 3 <- lane 15 of rows 0, 2
+constexpr int kDppBcast31 = 0x143;   // rows 2, 3 <- lane 31
+
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ int dpp_i32(int old, int v)
+{
+    return __builtin_amdgcn_update_dpp(old, v, Ctrl, RowMask, 0xf, false);
+}
+
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t old, uint64_t v)
+{
+    const uint32_t lo = (uint32_t)dpp_i32<Ctrl, RowMask>((int)(uint32_t)old, (int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)dpp_i32<Ctrl, RowMask>((int)(uint32_t)(old >> 32), (int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One reduction step of `op` over lanes paired by a DPP control; lanes outside
+// row_mask combine with the identity `id`.
+template <int Ctrl, int RowMask, class T, class Op>
+__device__ __forceinline__ void dpp_step(T &v, T id, Op op)
+{
+    if constexpr (sizeof(T) == 8)
+        v = op(v, (T)dpp_u64<Ctrl, RowMask>((uint64_t)id, (uint64_t)v));
+    else
+        v = op(v, (T)dpp_i32<Ctrl, RowMask>((int)id, (int)v));
+}
+
+// Reduction of a commutative, associative `op` over the 64 lanes: pairs, quads,
+// half-rows and rows by swaps and mirrors, then rows 0+1 and 2+3 by the lane-15
+// broadcast and all four by the lane-31 broadcast.  Lane 63 ends with the
+// result, which is returned to every lane (wave-uniform).
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T v, T id, Op op)
+{
+    dpp_step<kDppSwap1, 0xf>(v, id, op);
+    dpp_step<kDppSwap2, 0xf>(v, id, op);
+    dpp_step<kDppHalfMirror, 0xf>(v, id, op);
+    dpp_step<kDppMirror, 0xf>(v, id, op);
+    dpp_step<kDppBcast15, 0xa>(v, id, op);
+    dpp_step<kDppBcast31, 0xc>(v, id, op);
+    if constexpr (sizeof(T) == 8)
+        return (T)readlane_u64((uint64_t)v, 63);
+    else
+        return (T)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ __forceinline__ int wave_min(int v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const int o = __shfl_xor(v, off, 64);
-        v = o < v ? o : v;
-    }
-    return v;
+    return wave_reduce(v, INT_MAX, [](int a, int b) { return a < b ? a : b; });
+}
+
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v)
+{
+    return wave_reduce(v, (uint64_t)0, [](uint64_t a, uint64_t b) { return a + b; });
+}
+
+// The partial result {min energy, count at the min, lowest index at the min} of
+// the 64 lanes, by the same DPP steps with `combine` as the operation; the
+// result is wave-uniform.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ void dpp_combine_step(int &e, uint64_t &cnt, uint64_t &arg)
+{
+    const int e2 = dpp_i32<Ctrl, RowMask>(INT_MAX, e);
+    const uint64_t c2 = dpp_u64<Ctrl, RowMask>(0, cnt);
+    const uint64_t a2 = dpp_u64<Ctrl, RowMask>(~0ull, arg);
+    combine(e, cnt, arg, e2, c2, a2);
 }
 
 __device__ __forceinline__ void wave_combine(int &e, uint64_t &cnt, uint64_t &arg)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const int e2 = __shfl_xor(e, off, 64);
-        const uint64_t c2 = __shfl_xor(cnt, off, 64);
-        const uint64_t a2 = __shfl_xor(arg, off, 64);
-        combine(e, cnt, arg, e2, c2, a2);
-    }
+    dpp_combine_step<kDppSwap1, 0xf>(e, cnt, arg);
+    dpp_combine_step<kDppSwap2, 0xf>(e, cnt, arg);
+    dpp_combine_step<kDppHalfMirror, 0xf>(e, cnt, arg);
+    dpp_combine_step<kDppMirror, 0xf>(e, cnt, arg);
+    dpp_combine_step<kDppBcast15, 0xa>(e, cnt, arg);
+    dpp_combine_step<kDppBcast31, 0xc>(e, cnt, arg);
+    e = __builtin_amdgcn_readlane(e, 63);
+    cnt = readlane_u64(cnt, 63);
+    arg = readlane_u64(arg, 63);
 }
 
 // ---------------------------------------------------------------------------
@@ -358,10 +435,7 @@ struct LaneBest {
     }
 
     // A real energy of the wave's states (or INT_MAX): an upper bound of the minimum.
-    __device__ __forceinline__ int bound() const
-    {
-        return __builtin_amdgcn_readfirstlane(wave_min(e));
-    }
+    __device__ __forceinline__ int bound() const { return wave_min(e); }
 
     // Between exact walks the record lives in LDS (slot = thread), so the hot
     // loop carries no record registers.
@@ -867,6 +941,11 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
         arg = sink.with_lane(lane);
         wave_combine(e, cnt, arg);
     }
+    // Workgroup stage through LDS: one slot per wave, combined in wave order by
+    // one thread into the workgroup's partial (the grid reduction then reads one
+    // partial per workgroup).  Every wave of the workgroup leaves the item loop
+    // together, so all of them reach the barrier.
+    __shared__ Partial wg_part[kWaves];
     if (lane == 0) {
         Partial p;
         p.e = e;
@@ -875,7 +954,20 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
         p.arg = arg;
         p.bodies = bodies;
         p.checked = checked;
-        partials[(uint64_t)blockIdx.x * kWaves + wave] = p;
+        p.pad = 0;
+        wg_part[wave] = p;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Partial p = wg_part[0];
+        for (int w = 1; w < kWaves; ++w) {
+            const Partial &o = wg_part[w];
+            combine(p.e, p.count, p.arg, o.e, o.count, o.arg);
+            p.slow += o.slow;
+            p.bodies += o.bodies;
+            p.checked += o.checked;
+        }
+        partials[blockIdx.x] = p;
     }
 }
 
@@ -944,7 +1036,9 @@ hipError_t search_occupancy(int cols_per_lane, bool gated, bool lowest, int *blo
 }
 
 // Final map-reduce step (sec. III.C): min energy, summed counts at the min,
-// lowest index at the min, over every wave's partial.
+// lowest index at the min, over every workgroup's partial.  Each thread folds a
+// strided share, each wave reduces its lanes with DPP, and thread 0 combines the
+// waves' results from LDS.
 __global__ __launch_bounds__(256) void reduce_kernel(const Partial *__restrict__ partials,
                                                      int count, Ctrl *ctrl)
 {
@@ -960,12 +1054,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(const Partial *__restrict__
         checked += p.checked;
     }
     wave_combine(e, cnt, arg);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        slow += __shfl_xor(slow, off, 64);
-        bodies += __shfl_xor(bodies, off, 64);
-        checked += __shfl_xor(checked, off, 64);
-    }
+    slow = wave_sum(slow);
+    bodies = wave_sum(bodies);
+    checked = wave_sum(checked);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
         se[w] = e;

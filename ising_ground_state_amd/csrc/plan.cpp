@@ -216,7 +216,7 @@ Layout layout_of(const qubo_plan &p)
     L.off_epmin = off;
     off = align256(off + ((1ull << (p.prefix_bits - kRegBits)) + 2) * 4);  // + 2 padding entries
     L.off_partials = off;
-    off = align256(off + (uint64_t)p.blocks * p.waves_per_block * 32);  // one 32-byte partial per wave
+    off = align256(off + (uint64_t)p.blocks * 64);  // one partial (at most 64 bytes) per workgroup
     L.off_ctrl = off;
     off = align256(off + 256);
     L.total = off;

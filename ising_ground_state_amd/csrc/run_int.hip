@@ -17,6 +17,8 @@
 
 namespace qubo_host {
 
+static_assert(qubo::kPartialBytes == 64, "layout_of reserves 64 bytes per workgroup's partial");
+
 // One search of the folded upper-triangular matrix U (n x n, host memory) on the
 // device.  have_t0: the search only has to find states with E <= t0_cap (the
 // caller knows a real energy that low elsewhere, or k of them for the
@@ -172,7 +174,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
         return QUBO_EDEVICE;
     if (!mark(2))
         return QUBO_EDEVICE;
-    if (launch_reduce(dpart, plan.blocks * plan.waves_per_block, dctrl, rq.stream) != hipSuccess)
+    if (launch_reduce(dpart, plan.blocks, dctrl, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     if (lowest && launch_lowest_merge(dlists, list_entries, k_low, dlow, dlow_found, rq.stream) !=
                       hipSuccess)
