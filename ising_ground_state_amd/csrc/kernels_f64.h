@@ -13,6 +13,11 @@ namespace qubo {
 // then covers half as many states.
 constexpr int kColsPerLaneF64 = 8;
 
+// The lowest Gray bit whose binary64 row the search keeps in LDS: the anchor of
+// a column moves once per aligned group of eight 32-step bodies, by the rows of
+// Gray bit 7 and of one bit above it.
+constexpr int kLdsFirstBitF64 = 7;
+
 // One wave's partial result (40 bytes).
 struct PartialF64 {
     double e;            // min energy seen (+inf when count == 0)

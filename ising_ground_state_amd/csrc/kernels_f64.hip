@@ -45,6 +45,11 @@ constexpr int kR = kColsPerLaneF64;  // columns per lane
 // (fp32 rows in LDS).
 constexpr int kAnchorBits = 3;
 constexpr int kAnchorGroup = 1 << kAnchorBits;
+// The binary64 rows the anchor moves by at the end of an aligned group: Gray bit
+// 4 + kAnchorBits and a bit above it.  Rows of lower bits are needed only when a
+// unit starts inside a group, and are read from global memory then.
+constexpr int kLdsFirstBit = kU - 1 + kAnchorBits;
+static_assert(kLdsFirstBit == kLdsFirstBitF64, "LDS row layout shared with the host");
 
 __device__ __forceinline__ uint64_t gray(uint64_t i) { return i ^ (i >> 1); }
 
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                                                               const SearchArgsF64 a)
 {
     constexpr int kGroup = 64 * kR;
-    extern __shared__ double lds_rows64[];  // [l_eff - 4][kGroup]: rows of Gray bits 4 .. l_eff-1
+    extern __shared__ double lds_rows64[];  // [l_eff - 7][kGroup]: rows of Gray bits 7 .. l_eff-1
     __shared__ unsigned long long item_sh;
     __shared__ double rec_e[64 * kWaves];
     __shared__ uint64_t rec_c[64 * kWaves], rec_a[64 * kWaves];
@@ -428,7 +433,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int A = a.A, B = a.B;
     const uint64_t cp = a.cols_padded;
-    const double *lds_lane = lds_rows64 - 4 * kGroup + lane;  // row of bit t: lds_lane + t * kGroup
+    const double *lds_lane = lds_rows64 - kLdsFirstBit * kGroup + lane;  // row of bit t: lds_lane + t * kGroup
     // The lane's offset passes through an empty asm: knowing its range, the
     // compiler turned "+ r * 64" into bitwise ors that it does not fold into the
     // LDS reads' immediate offsets, and spent a VALU instruction per register.
@@ -456,9 +461,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         const uint64_t g = item / a.seg_blocks;
         const uint64_t sb = item - g * a.seg_blocks;
         if ((long long)g != cur_g) {
-            const int rows = a.l_eff - 4;
+            const int rows = a.l_eff > kLdsFirstBit ? a.l_eff - kLdsFirstBit : 0;
             for (int k = threadIdx.x; k < rows * kGroup; k += blockDim.x) {
-                const int t = 4 + k / kGroup;
+                const int t = kLdsFirstBit + k / kGroup;
                 const int col = k % kGroup;
                 lds_rows64[k] = mint[(uint64_t)(A - 1 - t) * cp + g * kGroup + col];
             }
@@ -758,7 +763,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                         diff &= diff - 1;
                         const double st = ((gn >> t) & 1u) ? 1.0 : -1.0;
                         double row[kR];
-                        if (t < a.l_eff) {
+                        if (t >= kLdsFirstBit && t < a.l_eff) {
                             const double *src = lds_lane + t * kGroup;
 #pragma unroll
                             for (int r = 0; r < kR; ++r)

@@ -20,9 +20,8 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     if (!rq.Q || rq.n < 1 || rq.n > kMaxSingleVars || (lowest ? (!low || rq.lowest_k > kMaxLowest) : !out))
         return QUBO_EINVAL;
     const int n = rq.n;
-    // The binary64 rows of Gray bits 4 .. l-1 sit in LDS (4 KiB each per
-    // workgroup): the default keeps 6 of them, so that with the fp32 rows of
-    // the walk's carries four workgroups fit a CU.
+    // The binary64 rows of Gray bits 7 .. l-1 (the anchor's moves) sit in LDS
+    // (4 KiB each per workgroup): the default keeps 3 of them.
     int cache_bits = rq.cache_bits;
     if (cache_bits < 0 && n >= kMinSearchVars) {  // (tiny problems: the planner's fixed split)
         qubo_plan probe;
@@ -42,7 +41,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     const int ns = plan.n_search, A = plan.prefix_bits, B = plan.suffix_bits;
     const int l_eff = plan.cache_bits;
     const int group = kWave * kColsPerLaneF64;
-    const int lds_bytes = (l_eff - 4) * group * 8;
+    const int lds_bytes = (l_eff > kLdsFirstBitF64 ? l_eff - kLdsFirstBitF64 : 0) * group * 8;
     if (lds_bytes > kMaxLdsBytes)
         return QUBO_EPLAN;
 
