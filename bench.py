@@ -46,7 +46,7 @@ PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gray_search_gated_n48_counter
 # (split, segments, LDS rows) and the host run that sizes the grid, and the
 # compiler flags.
 KERNEL_INPUTS = [os.path.join(ROOT, "ising_ground_state_amd", "csrc", name)
-                 for name in ("kernels.hip", "kernels.h", "plan.cpp", "plan.h", "run_int.hip")]
+                 for name in ("kernels.hip", "kernels.h", "dpp.h", "plan.cpp", "plan.h", "run_int.hip")]
 
 
 _C_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"', re.S)

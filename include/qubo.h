@@ -113,7 +113,7 @@ QUBO_API int qubo_abs_sum(const int32_t *Q_host, int n, int64_t *abs_sum);
  * row-major): every entry finite and S = sum |Q_ij| either 0 or in
  * [2^-100, 2^100].  Above, fp32 values of the walk could overflow; below, the
  * absolute error of fp32 arithmetic near its underflow threshold could exceed
- * the re-evaluation margin 2^-14 S.
+ * the re-evaluation margin 2^-13 S.
  * Returns QUBO_OK, QUBO_EINVAL (null Q, n outside [1, 63]) or QUBO_ERANGE. */
 QUBO_API int qubo_check_q_f64(const double *Q_host, int n);
 
@@ -264,8 +264,8 @@ typedef struct {
  * flags: 0 or QUBO_FLAG_COLS8.  Every entry must be finite and sum |Q_ij|
  * either 0 or in [2^-100, 2^100] (else QUBO_ERANGE; qubo_check_q_f64).
  * The walk is the integer kernel's, with a binary64 anchor per column advanced
- * once per eight 32-step bodies and every state one fp32 add; a
- * state whose fp32 energy comes within delta = 2^-14 sum |Q_ij| of the best
+ * once per 32 32-step bodies and every state one fp32 add; a
+ * state whose fp32 energy comes within delta = 2^-13 sum |Q_ij| of the best
  * exact energy so far is re-evaluated from the definition on the GPU, so the
  * result is exactly the definition's.  Instances with many states within delta
  * of the minimum (e.g. Q = 0) are correct but slow: each such state costs an

@@ -57,12 +57,12 @@ uint64_t fingerprint(const void *Qh, size_t bytes, int n)
 
 // The binary64 guard: finite entries and S = sum |Q_ij| (rounded up) either 0
 // or in [2^-100, 2^100].  The upper end keeps every fp32 value of the walk in
-// range.  The lower end keeps the filter margin 2^-14 S above the absolute
+// range.  The lower end keeps the filter margin 2^-13 S above the absolute
 // error of fp32 arithmetic near underflow: each fp32 rounding errs by at most
 // 2^-24 of its result plus 2^-126 (the largest error of a value flushed to zero;
 // this build keeps subnormals, which err by at most 2^-150), and the fewer than
-// 300 roundings between a binary64 anchor and a compare add at most 2^-117,
-// below the 732 * 2^-24 S >= 2^-114 of the margin left over by the relative
+// 1100 roundings between a binary64 anchor and a compare add at most 2^-115.8,
+// below the 988 * 2^-24 S >= 2^-114.1 of the margin left over by the relative
 // terms.  S = 0 means every entry is zero: every fp32 value is then exactly 0.
 int guard_f64(const std::vector<double> &Qh, double *S_out)
 {

@@ -40,6 +40,7 @@
 //   * the threshold T is shared between waves through a global best-so-far, which
 //     is always a real state's energy, so no minimiser is ever skipped.
 #include "kernels.h"
+#include "dpp.h"
 
 #include <climits>
 #include <type_traits>
@@ -119,69 +120,6 @@ __device__ __forceinline__ void combine(int &e, uint64_t &cnt, uint64_t &arg, in
         cnt += c2;
         arg = a2 < arg ? a2 : arg;
     }
-}
-
-// Cross-lane moves through DPP (data-parallel primitives: the source lane is
-// picked by the VALU instruction itself, no LDS round trip).  gfx9 controls:
-// quad_perm within 4 lanes, mirrors within 8 and 16 lanes, and the broadcasts of
-// lane 15 of each row into the next row and of lane 31 into rows 2 and 3.  Lanes
-// of rows outside row_mask keep `old`.
-constexpr int kDppSwap1 = 0xB1;      // quad_perm [1, 0, 3, 2]: lane ^ 1
-constexpr int kDppSwap2 = 0x4E;      // quad_perm [2, 3, 0, 1]: lane ^ 2
-constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within 8 lanes
-constexpr int kDppMirror = 0x140;    // lane i <- 15 - i within 16 lanes
-constexpr int kDppBcast15 = 0x142;   // rows 1, 3 <- lane 15 of rows 0, 2
-constexpr int kDppBcast31 = 0x143;   // rows 2, 3 <- lane 31
-
-template <int Ctrl, int RowMask>
-__device__ __forceinline__ int dpp_i32(int old, int v)
-{
-    return __builtin_amdgcn_update_dpp(old, v, Ctrl, RowMask, 0xf, false);
-}
-
-template <int Ctrl, int RowMask>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t old, uint64_t v)
-{
-    const uint32_t lo = (uint32_t)dpp_i32<Ctrl, RowMask>((int)(uint32_t)old, (int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)dpp_i32<Ctrl, RowMask>((int)(uint32_t)(old >> 32), (int)(uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane)
-{
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// One reduction step of `op` over lanes paired by a DPP control; lanes outside
-// row_mask combine with the identity `id`.
-template <int Ctrl, int RowMask, class T, class Op>
-__device__ __forceinline__ void dpp_step(T &v, T id, Op op)
-{
-    if constexpr (sizeof(T) == 8)
-        v = op(v, (T)dpp_u64<Ctrl, RowMask>((uint64_t)id, (uint64_t)v));
-    else
-        v = op(v, (T)dpp_i32<Ctrl, RowMask>((int)id, (int)v));
-}
-
-// Reduction of a commutative, associative `op` over the 64 lanes: pairs, quads,
-// half-rows and rows by swaps and mirrors, then rows 0+1 and 2+3 by the lane-15
-// broadcast and all four by the lane-31 broadcast.  Lane 63 ends with the
-// result, which is returned to every lane (wave-uniform).
-template <class T, class Op>
-__device__ __forceinline__ T wave_reduce(T v, T id, Op op)
-{
-    dpp_step<kDppSwap1, 0xf>(v, id, op);
-    dpp_step<kDppSwap2, 0xf>(v, id, op);
-    dpp_step<kDppHalfMirror, 0xf>(v, id, op);
-    dpp_step<kDppMirror, 0xf>(v, id, op);
-    dpp_step<kDppBcast15, 0xa>(v, id, op);
-    dpp_step<kDppBcast31, 0xc>(v, id, op);
-    if constexpr (sizeof(T) == 8)
-        return (T)readlane_u64((uint64_t)v, 63);
-    else
-        return (T)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ int wave_min(int v)
@@ -809,17 +747,21 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
         // Body minima of the prefix energies are read two bodies ahead (scalar
         // loads).  The body loop counts with 32-bit scalars (the SALU has no
         // 64-bit less-than): a segment holds at most 2^13 bodies.
+        // Bodies are counted by their index b = j >> 5, a 32-bit value (A <= 32),
+        // so that the per-body bookkeeping is 32-bit scalar arithmetic; the
+        // 64-bit Gray step is formed only where a walk needs it.
         const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
-        int epm_cur = Gated ? epmin[j_begin >> kU] : 0;
-        int epm_next = Gated ? epmin[(j_begin >> kU) + 1] : 0;
+        const uint32_t b0 = (uint32_t)(j_begin >> kU);
+        int epm_cur = Gated ? epmin[b0] : 0;
+        int epm_next = Gated ? epmin[b0 + 1] : 0;
         uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
-            const uint64_t base = j_begin + ((uint64_t)bi << kU);
+            const uint32_t b = b0 + bi;
             const bool last = bi + 1 == nbodies;
-            const bool top_plus = ((base >> kU) & 1u) == 0;
+            const bool top_plus = (b & 1u) == 0;
             int epm_after = 0;
             if (Gated)  // the table has two padding entries past the last body
-                epm_after = epmin[(base >> kU) + 2];
+                epm_after = epmin[b + 2];
             bool check = true;
             if (Gated) {
                 // Padding columns hold INT_MAX with zero rows (beta 0), so a lane
@@ -830,12 +772,12 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                     --covered;
                 } else {
                     const int emin = row_min<R>(E);
-                    if (((base >> kU) & 3u) == 0 && bi + 3 < nbodies && A > kU + 1) {
+                    if ((b & 3u) == 0 && bi + 3 < nbodies && A > kU + 1) {
                         // The first of four aligned bodies: their 128 states of Gray
                         // bits 0..6 fall by at most beta_q(bit 6 at the group's start).
-                        const int epm_4 = epmin[(base >> kU) + 3];
+                        const int epm_4 = epmin[b + 3];
                         const int thq = T - imin(imin(epm_cur, epm_next), imin(epm_after, epm_4));
-                        const int bq = emin + (((base >> (kU + 2)) & 1u) ? beta_q1 : beta_q0);
+                        const int bq = emin + (((b >> 2) & 1u) ? beta_q1 : beta_q0);
                         if (__builtin_amdgcn_ballot_w64(bq <= thq) == 0)
                             covered = 3;
                     }
@@ -843,7 +785,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                         // An even body and its partner: the 64 states of Gray bits
                         // 0..5 fall by at most beta_p(bit 5 at the pair's start).
                         const int thp = T - imin(epm_cur, epm_next);
-                        const int bp = emin + (((base >> (kU + 1)) & 1u) ? beta_p1 : beta_p0);
+                        const int bp = emin + (((b >> 1) & 1u) ? beta_p1 : beta_p0);
                         if (__builtin_amdgcn_ballot_w64(bp <= thp) == 0)
                             covered = 1;
                     }
@@ -863,6 +805,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 ++checked;
                 // Strict mode walks exactly only after the per-step test hit; the
                 // gated kernel has already decided that the bound was reached.
+                const uint64_t base = (uint64_t)b << kU;
                 bool walk = Gated;
                 if (!Gated)
                     walk = checked_body(E, Mr, top_plus, T, ep + base) != 0;
@@ -886,11 +829,12 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                     T = gb < T ? gb : T;
                 }
             }
-            const uint64_t next = base + kBody;
             if (!last) {
-                // Flip of Gray bit t >= 5: its row comes from LDS or global memory.
-                const int t = __builtin_ctzll(next);
-                const bool plus = ((next >> (t + 1)) & 1u) == 0;
+                // Flip of Gray bit t = 5 + ctz(b + 1) into the next body (its sign is
+                // bit t + 1 of the next body's first step): its row comes from LDS or
+                // global memory.
+                const int t = kU + __builtin_ctz(b + 1);
+                const bool plus = (((b + 1) >> (t - kU + 1)) & 1u) == 0;
                 int row[R];
                 if (t < a.l_eff) {
                     // Bit 5 (every other body) reads at constant offsets: the general

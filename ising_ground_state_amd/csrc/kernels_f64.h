@@ -8,23 +8,23 @@
 
 namespace qubo {
 
-// Suffix columns per lane of the binary64 search (120 VGPRs, four waves per
-// SIMD).  Four columns fit six waves but ran 10 % slower: a body's fixed work
+// Suffix columns per lane of the binary64 search (four waves per SIMD).  Four columns fit six waves but ran 10 % slower: a body's fixed work
 // then covers half as many states.
 constexpr int kColsPerLaneF64 = 8;
 
 // The lowest Gray bit whose binary64 row the search keeps in LDS: the anchor of
-// a column moves once per aligned group of eight 32-step bodies, by the rows of
-// Gray bit 7 and of one bit above it.
-constexpr int kLdsFirstBitF64 = 7;
+// a column moves once per aligned group of 32 32-step bodies, by the rows of
+// Gray bit 9 and of one bit above it.
+constexpr int kLdsFirstBitF64 = 9;
 
-// One wave's partial result (40 bytes).
+// One workgroup's partial result (48 bytes).
 struct PartialF64 {
     double e;            // min energy seen (+inf when count == 0)
     uint64_t count;      // states with exactly that energy
     uint64_t arg;        // smallest index attaining it
-    uint32_t bodies;     // 32-step bodies walked
+    uint64_t bodies;     // 32-step bodies walked
     uint32_t slow;       // bodies walked exactly
+    uint32_t pad;
     uint64_t candidates; // states re-evaluated from the definition
 };
 
@@ -51,7 +51,7 @@ struct SearchArgsF64 {
     const double *ep;       // [2^A]               E_p(g(j))
     const float *epmin;     // [2^A / 32 + 2]      min over each body of ep rounded to fp32, + 2 padding
     const double *Q;        // [n][n]              the caller's matrix (the definition's terms)
-    PartialF64 *partials;   // [gridDim.x * 4]
+    PartialF64 *partials;   // [gridDim.x]: one per workgroup
     CtrlF64 *ctrl;
     LowEntryF64 *lists;     // k-lowest search: [gridDim.x * 4][k_low], else unused
     uint64_t cols_padded;

@@ -9,17 +9,18 @@
 //     x_i = 1 and, inside, j ascending with x_j = 1 (the definition of sec. I in
 //     one fixed order);
 //   * the walk is the integer kernel's decomposition (eq. 8, eq. 9): per column,
-//     a binary64 anchor E64 follows the walk once per aligned group of eight
+//     a binary64 anchor E64 follows the walk once per aligned group of 32
 //     32-step bodies (two row updates per group), and every state's energy is
 //     one fp32 add (the same 2-cycle rate as int32), re-anchored from E64 at
-//     the start of every group, so at most 255 fp32 adds separate a state
+//     the start of every group, so at most 1023 fp32 adds separate a state
 //     from its anchor;
-//   * with S = sum |Q_ij|, an fp32 energy is within 257 * 2^-24 S of exact:
+//   * with S = sum |Q_ij|, an fp32 energy is within 1025 * 2^-24 S of exact:
 //     the anchor's rounding, each add's (the sums stay below S), and the rows'
 //     rounding to fp32 once (a state differs from its anchor by each row at
 //     most once, and the rows of one column sum to at most S in magnitude);
-//     the compare and gates add a few 2^-24 S more, and the margin delta =
-//     2^-14 S = 1024 * 2^-24 S covers that almost four times over; a state is
+//     the compare and gates add a few dozen 2^-24 S more (at most 1060 in
+//     all), and the margin delta = 2^-13 S = 2048 * 2^-24 S covers that 1.93
+//     times over; a state is
 //     re-evaluated from the definition, in binary64 and in the same order as
 //     the definition, whenever its fp32 energy is within delta of the threshold T;
 //   * T only has to bound the minimum from above: it is lowered to the best
@@ -28,6 +29,7 @@
 //     Every minimiser passes every filter, so the minimum, its lowest index and
 //     the count of states with exactly that energy are those of the definition.
 #include "kernels_f64.h"
+#include "dpp.h"
 
 #include <cfloat>
 #include <climits>
@@ -43,7 +45,7 @@ constexpr int kR = kColsPerLaneF64;  // columns per lane
 // Bodies share one binary64 anchor in aligned groups of 2^kAnchorBits: inside
 // a group the fp32 walk runs on through the flips of Gray bits 5 .. 4+kAnchorBits
 // (fp32 rows in LDS).
-constexpr int kAnchorBits = 3;
+constexpr int kAnchorBits = 5;
 constexpr int kAnchorGroup = 1 << kAnchorBits;
 // The binary64 rows the anchor moves by at the end of an aligned group: Gray bit
 // 4 + kAnchorBits and a bit above it.  Rows of lower bits are needed only when a
@@ -111,14 +113,16 @@ __device__ double energy_def(const double *__restrict__ Q, int n, uint64_t idx)
     return e;
 }
 
+__device__ __forceinline__ double bits_f64(uint64_t b) { return __longlong_as_double((long long)b); }
+__device__ __forceinline__ uint64_t f64_bits(double d) { return (uint64_t)__double_as_longlong(d); }
+
+// Minimum over the wave's lanes (none NaN) by the DPP steps of dpp.h, on the
+// order-preserving integer keys; wave-uniform.
 __device__ __forceinline__ double wave_min_f64(double v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const double o = __shfl_xor(v, off, 64);
-        v = o < v ? o : v;
-    }
-    return v;
+    const long long k = wave_reduce(order_key(v), (long long)0x7fffffffffffffffLL,
+                                    [](long long a, long long b) { return a < b ? a : b; });
+    return from_key(k);
 }
 
 __device__ __forceinline__ void combine(double &e, uint64_t &cnt, uint64_t &arg, double e2,
@@ -136,15 +140,34 @@ __device__ __forceinline__ void combine(double &e, uint64_t &cnt, uint64_t &arg,
     }
 }
 
+// {min energy, count at the min, lowest index at the min} over the wave's
+// lanes: the DPP steps of dpp.h with `combine` as the operation (lanes outside
+// a broadcast's rows meet the empty triple); the result is wave-uniform.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ void dpp_combine_step(double &e, uint64_t &cnt, uint64_t &arg)
+{
+    const double e2 = bits_f64(dpp_u64<Ctrl, RowMask>(0x7ff0000000000000ull, f64_bits(e)));
+    const uint64_t c2 = dpp_u64<Ctrl, RowMask>(0, cnt);
+    const uint64_t a2 = dpp_u64<Ctrl, RowMask>(~0ull, arg);
+    combine(e, cnt, arg, e2, c2, a2);
+}
+
 __device__ __forceinline__ void wave_combine(double &e, uint64_t &cnt, uint64_t &arg)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const double e2 = __shfl_xor(e, off, 64);
-        const uint64_t c2 = __shfl_xor(cnt, off, 64);
-        const uint64_t a2 = __shfl_xor(arg, off, 64);
-        combine(e, cnt, arg, e2, c2, a2);
-    }
+    dpp_combine_step<kDppSwap1, 0xf>(e, cnt, arg);
+    dpp_combine_step<kDppSwap2, 0xf>(e, cnt, arg);
+    dpp_combine_step<kDppHalfMirror, 0xf>(e, cnt, arg);
+    dpp_combine_step<kDppMirror, 0xf>(e, cnt, arg);
+    dpp_combine_step<kDppBcast15, 0xa>(e, cnt, arg);
+    dpp_combine_step<kDppBcast31, 0xc>(e, cnt, arg);
+    e = bits_f64(readlane_u64(f64_bits(e), 63));
+    cnt = readlane_u64(cnt, 63);
+    arg = readlane_u64(arg, 63);
+}
+
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v)
+{
+    return wave_reduce(v, (uint64_t)0, [](uint64_t a, uint64_t b) { return a + b; });
 }
 
 // ---------------------------------------------------------------------------
@@ -540,21 +563,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         }
         float TD = (float)T + a.delta;  // filter threshold: E32 + E_p32 <= TD
 
+        // Bodies are counted by their index b = j >> 5, a 32-bit value (A <= 32),
+        // so that the per-body bookkeeping is 32-bit scalar arithmetic; the
+        // 64-bit Gray step is formed only on the rare paths that need it.
         const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
-        float epm_cur = epmin[j_begin >> kU];
-        float epm_next = epmin[(j_begin >> kU) + 1];
+        const uint32_t b0 = (uint32_t)(j_begin >> kU);
+        float epm_cur = epmin[b0];
+        float epm_next = epmin[b0 + 1];
         uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
         float E[kR];
         uint64_t anchor_j = j_begin;  // E64 holds the suffix energies at prefix g(anchor_j)
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
-            const uint64_t base = j_begin + ((uint64_t)bi << kU);
+            const uint32_t b = b0 + bi;
             const bool last = bi + 1 == nbodies;
-            const bool top_plus = ((base >> kU) & 1u) == 0;
-            const float epm_after = epmin[(base >> kU) + 2];
+            const bool top_plus = (b & 1u) == 0;
+            const float epm_after = epmin[b + 2];
             // The first body of an aligned group, and a unit's first body, start
             // from the binary64 anchor E64 (rounded to nearest); the others
             // continue the fp32 walk, so E64 moves once per group.
-            const uint32_t in_group = (uint32_t)(base >> kU) & (kAnchorGroup - 1);
+            const uint32_t in_group = b & (kAnchorGroup - 1);
             const bool carried = in_group != 0 && bi != 0;
             if (!carried) {
 #pragma unroll
@@ -570,15 +597,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 // (the k-lowest search, whose threshold is its list's k-th energy,
                 // measured slower with this gate than without it)
                 if (!Lowest && (in_group & 3u) == 0 && bi + 3 < nbodies && A > kU + 1) {
-                    // four aligned bodies (never across an anchor group of eight)
-                    const float epm_4 = epmin[(base >> kU) + 3];
-                    const float bq = emin + (((base >> (kU + 2)) & 1u) ? beta_q1 : beta_q0);
+                    // four aligned bodies (never across an anchor group)
+                    const float epm_4 = epmin[b + 3];
+                    const float bq = emin + (((b >> 2) & 1u) ? beta_q1 : beta_q0);
                     const float ep4 = uniform_fmin(uniform_fmin(epm_cur, epm_next), uniform_fmin(epm_after, epm_4));
                     if (__builtin_amdgcn_ballot_w64(bq + ep4 <= TD) == 0)
                         covered = 3;
                 }
                 if (covered == 0 && top_plus && !last && A > kU) {
-                    const float bp = emin + (((base >> (kU + 1)) & 1u) ? beta_p1 : beta_p0);
+                    const float bp = emin + (((b >> 1) & 1u) ? beta_p1 : beta_p0);
                     if (__builtin_amdgcn_ballot_w64(bp + uniform_fmin(epm_cur, epm_next) <= TD) == 0)
                         covered = 1;
                 }
@@ -595,6 +622,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
             } else {
                 // Exact walk: every state within delta of T is re-evaluated.
                 ++slow;
+                const uint64_t base = (uint64_t)b << kU;
                 const uint64_t colbase = g * kGroup;
                 // First pass: the body's smallest fp32 energy plus delta bounds
                 // the best exact energy in the body from above, so T (which only
@@ -713,42 +741,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
             // Signed adds are fma with a wave-uniform +-1: rounded once, with no
             // sign select per register.
             if (!last) {
-                const uint64_t next = base + kBody;
                 if (in_group != kAnchorGroup - 1) {
-                    // inside a group: the fp32 walk flips Gray bit t (5 <= t < 5 +
-                    // kAnchorBits) into the next body (two-operand adds: a
-                    // three-register fma issues at half rate)
-                    // the carried bit from the body's place in its group: a 32-bit
-                    // value, so the branches below compare on the scalar unit
-                    const int t = kU + __builtin_ctz(in_group + 1);
-                    // Each of the three rows is read at constant offsets: from
-                    // (t - 5) * kGroup the compiler made negative offsets, which LDS
-                    // reads cannot take, and spent an address add per register.
-                    // The asm after the reads keeps the compiler from merging the
-                    // three branches into one read through a computed address.
-                    static_assert(kAnchorBits == 3 && kR == 8, "one branch per carried bit");
+                    // inside a group: the fp32 walk flips Gray bit 5 + c into the next
+                    // body, c = ctz(in_group + 1) < kAnchorBits (two-operand adds: a
+                    // three-register fma issues at half rate); its sign is bit c + 1
+                    // of the next body's index
+                    const uint32_t c = __builtin_ctz(in_group + 1);
+                    // Each of the rows is read at constant offsets: from c * kGroup
+                    // the compiler made negative offsets, which LDS reads cannot take,
+                    // and spent an address add per register.  The asm after the reads
+                    // keeps the compiler from merging the branches into one read
+                    // through a computed address.
+                    static_assert(kAnchorBits == 5 && kR == 8, "one branch per carried bit");
                     float row[kR];
-#define QUBO_PIN_ROW(tag)                                                                              \
+#define QUBO_CARRY_ROW(k, tag)                                                                             \
+    _Pragma("unroll") for (int r = 0; r < kR; ++r) row[r] = carry_lane[(k) * kGroup + r * 64];              \
     asm volatile(tag : "+v"(row[0]), "+v"(row[1]), "+v"(row[2]), "+v"(row[3]), "+v"(row[4]), "+v"(row[5]), \
                  "+v"(row[6]), "+v"(row[7]))
-                    if (t == kU) {
-#pragma unroll
-                        for (int r = 0; r < kR; ++r)
-                            row[r] = carry_lane[r * 64];
-                        QUBO_PIN_ROW("; carry row of bit 5");
-                    } else if (t == kU + 1) {
-#pragma unroll
-                        for (int r = 0; r < kR; ++r)
-                            row[r] = carry_lane[kGroup + r * 64];
-                        QUBO_PIN_ROW("; carry row of bit 6");
+                    if (c == 0) {
+                        QUBO_CARRY_ROW(0, "; carry row of bit 5");
+                    } else if (c == 1) {
+                        QUBO_CARRY_ROW(1, "; carry row of bit 6");
+                    } else if (c == 2) {
+                        QUBO_CARRY_ROW(2, "; carry row of bit 7");
+                    } else if (c == 3) {
+                        QUBO_CARRY_ROW(3, "; carry row of bit 8");
                     } else {
-#pragma unroll
-                        for (int r = 0; r < kR; ++r)
-                            row[r] = carry_lane[2 * kGroup + r * 64];
-                        QUBO_PIN_ROW("; carry row of bit 7");
+                        QUBO_CARRY_ROW(4, "; carry row of bit 9");
                     }
-#undef QUBO_PIN_ROW
-                    if (((next >> (t + 1)) & 1u) == 0)
+#undef QUBO_CARRY_ROW
+                    if ((((b + 1) >> (c + 1)) & 1u) == 0)
                         step_rows<true>(E, row);
                     else
                         step_rows<false>(E, row);
@@ -756,6 +778,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                     // E64 from g(anchor_j) to g(next): one signed row per differing
                     // bit (an aligned group: Gray bit 4 + kAnchorBits and the bit
                     // t >= 5 + kAnchorBits of the next group).
+                    const uint64_t next = (uint64_t)(b + 1) << kU;
                     const uint64_t gn = gray(next);
                     uint64_t diff = gray(anchor_j) ^ gn;
                     while (diff) {
@@ -798,10 +821,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         cnt = 0;  // the partials carry the statistics only
     }
     wave_combine(e, cnt, arg);
-    uint64_t cand = candidates;  // a lane evaluates far fewer than 2^32 states
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        cand += __shfl_xor(cand, off, 64);
+    const uint64_t cand = wave_sum(candidates);
+    // Workgroup stage through LDS: one slot per wave, combined in wave order by
+    // one thread into the workgroup's partial.  The waves of a workgroup leave
+    // the item loop together, so all of them reach the barrier.
+    __shared__ PartialF64 wg_part[kWaves];
     if (lane == 0) {
         PartialF64 p;
         p.e = e;
@@ -809,8 +833,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         p.arg = arg;
         p.bodies = bodies;
         p.slow = slow;
+        p.pad = 0;
         p.candidates = cand;
-        partials[(uint64_t)blockIdx.x * kWaves + wave] = p;
+        wg_part[wave] = p;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        PartialF64 p = wg_part[0];
+        for (int w = 1; w < kWaves; ++w) {
+            const PartialF64 &o = wg_part[w];
+            combine(p.e, p.count, p.arg, o.e, o.count, o.arg);
+            p.bodies += o.bodies;
+            p.slow += o.slow;
+            p.candidates += o.candidates;
+        }
+        partials[blockIdx.x] = p;
     }
 }
 
@@ -829,12 +866,9 @@ __global__ __launch_bounds__(256) void reduce_f64_kernel(const PartialF64 *__res
         cand += p.candidates;
     }
     wave_combine(e, cnt, arg);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        slow += __shfl_xor(slow, off, 64);
-        bodies += __shfl_xor(bodies, off, 64);
-        cand += __shfl_xor(cand, off, 64);
-    }
+    slow = wave_sum(slow);
+    bodies = wave_sum(bodies);
+    cand = wave_sum(cand);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
         se[w] = e;

@@ -20,15 +20,15 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     if (!rq.Q || rq.n < 1 || rq.n > kMaxSingleVars || (lowest ? (!low || rq.lowest_k > kMaxLowest) : !out))
         return QUBO_EINVAL;
     const int n = rq.n;
-    // The binary64 rows of Gray bits 7 .. l-1 (the anchor's moves) sit in LDS
-    // (4 KiB each per workgroup): the default keeps 3 of them.
+    // The binary64 rows of Gray bits 9 .. l-1 (the anchor's moves) sit in LDS
+    // (4 KiB each per workgroup): the default keeps 2 of them.
     int cache_bits = rq.cache_bits;
     if (cache_bits < 0 && n >= kMinSearchVars) {  // (tiny problems: the planner's fixed split)
         qubo_plan probe;
         const int rc0 = make_plan(n, rq.prefix_bits, -1, 256, kColsPerLaneF64, 0, &probe);
         if (rc0 != QUBO_OK)
             return rc0;
-        cache_bits = probe.prefix_bits < 10 ? probe.prefix_bits : 10;
+        cache_bits = probe.prefix_bits < 11 ? probe.prefix_bits : 11;
     }
     DeviceInfo dev;
     int rc = device_info(&dev);
@@ -98,7 +98,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     const uint64_t off_ep = al(off_mint32 + (uint64_t)A * cols_padded * 4);
     const uint64_t off_epmin = al(off_ep + (1ull << A) * 8);
     const uint64_t off_part = al(off_epmin + ((1ull << (A - kRegBits)) + 2) * 4);
-    const uint64_t off_ctrl = al(off_part + (uint64_t)blocks * kWavesPerBlock * sizeof(PartialF64));
+    const uint64_t off_ctrl = al(off_part + (uint64_t)blocks * sizeof(PartialF64));  // one per workgroup
     // the k-lowest search: the per-wave lists, the merged list and its length
     const uint64_t list_entries = lowest ? (uint64_t)blocks * kWavesPerBlock * rq.lowest_k : 0;
     const uint64_t off_lists = al(off_ctrl + sizeof(CtrlF64));
@@ -124,10 +124,10 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
         return QUBO_EDEVICE;
 
     // A state passes the filter when its fp32 energy is within delta of the
-    // best binary64 energy so far; delta = 1024 * 2^-24 S bounds every fp32
-    // rounding of the walk, the compare and the gates (at most about
-    // 290 * 2^-24 S) more than three times over.
-    const double delta = std::ldexp(S, -14);
+    // best binary64 energy so far; delta = 2048 * 2^-24 S bounds every fp32
+    // rounding of the walk, the compare and the gates (at most 1060 * 2^-24 S)
+    // 1.93 times over.
+    const double delta = std::ldexp(S, -13);
     float delta32 = (float)delta;
     if ((double)delta32 < delta)
         delta32 = std::nextafter(delta32, INFINITY);
@@ -179,7 +179,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     }
     if (launch_search_f64(sa, lowest, blocks, lds_bytes, rq.stream) != hipSuccess ||
         hipEventRecord(call.ev[2], rq.stream) != hipSuccess ||
-        launch_reduce_f64(dpart, blocks * kWavesPerBlock, dctrl, rq.stream) != hipSuccess ||
+        launch_reduce_f64(dpart, blocks, dctrl, rq.stream) != hipSuccess ||
         (lowest && launch_lowest_merge_f64(dlists, list_entries, rq.lowest_k, dlow, dlow_found,
                                            rq.stream) != hipSuccess) ||
         hipEventRecord(call.ev[3], rq.stream) != hipSuccess)

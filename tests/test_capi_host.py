@@ -97,7 +97,7 @@ def test_check_q_guard():
 
 def test_check_q_f64_guard():
     """The binary64 guard: finite entries and S = sum |Q_ij| either 0 or in
-    [2^-100, 2^100].  The floor keeps the re-evaluation margin 2^-14 S above
+    [2^-100, 2^100].  The floor keeps the re-evaluation margin 2^-13 S above
     the absolute error of fp32 arithmetic near its underflow threshold."""
     q.check_q_f64(np.zeros((4, 4)))
     q.check_q_f64(-np.zeros((4, 4)))  # negative zeros: S = 0

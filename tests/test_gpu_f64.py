@@ -101,7 +101,7 @@ def test_every_split_real(q, n):
 @pytest.mark.parametrize("case", ["normal", "subnormal"])
 def test_near_the_floor(q, case):
     """S = sum |Q_ij| just above the guard's floor 2^-100.  'normal': every entry
-    in fp32's normal range (about 2^-107), so the re-evaluation margin 2^-14 S
+    in fp32's normal range (about 2^-107), so the re-evaluation margin 2^-13 S
     is tight around the minimum.  'subnormal': every entry but one in fp32's
     subnormal range (below 2^-126), where fp32 keeps only a few bits and errs by
     an absolute amount; one diagonal entry lifts S above the floor.  The
