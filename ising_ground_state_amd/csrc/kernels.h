@@ -46,6 +46,7 @@ struct SearchArgs {
     const int32_t *mint;    // [A][cols_padded]    M_int rows by prefix variable
     const int32_t *ep;      // [2^A]               prefix energies in Gray order
     const int32_t *epmin;   // [2^A / 32 + 2]      min of ep over each 32-step body, + 2 padding
+    const int32_t *epmin4;  // [2^A / 128 + 1]     min of epmin over each aligned group of 4 bodies, + 1 padding
     Partial *partials;      // [gridDim.x]: one per workgroup
     Ctrl *ctrl;
     LowEntry *lists;        // [gridDim.x * waves per block][k_low] (spectrum search only)
@@ -66,13 +67,17 @@ struct SearchArgs {
 // and the Gray-ordered prefix energies, from the folded upper-triangular U.
 // Only the prefix energies a search of the Gray steps [j_lo, j_hi) reads are
 // written (j_lo, j_hi multiples of 32; the tables keep their full size).
+// The same launch writes epmin4[k] = min(epmin[4k .. 4k+3]) for the aligned
+// groups of four bodies that hold the slice's bodies (A >= 7).
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
                                int32_t *es, int32_t *mint, int32_t *ep, int32_t *epmin,
-                               uint64_t j_lo, uint64_t j_hi, hipStream_t stream);
+                               int32_t *epmin4, uint64_t j_lo, uint64_t j_hi, hipStream_t stream);
 
 // Resets the work counter, seeds the shared best with t0 (a real energy or an
-// upper bound) and fills the body-minimum table's two padding entries.
-hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, hipStream_t stream);
+// upper bound) and fills the body-minimum table's two padding entries and the
+// group-minimum table's one.
+hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int32_t *epmin4_pad,
+                            hipStream_t stream);
 
 // gated = true skips the per-step minimum of bodies whose lower bound cannot
 // reach the threshold; gated = false takes it after every prefix (strict).

@@ -278,9 +278,23 @@ __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *_
     }
 }
 
+// Minimum of the body minima over each aligned group of four bodies (128 Gray
+// steps): the prefix-energy bound of the search's group gate, one scalar load per
+// group.  Groups that straddle the slice's ends get values that are never read.
+__global__ __launch_bounds__(256) void build_group_min_kernel(const int32_t *__restrict__ epmin,
+                                                              int32_t *__restrict__ epmin4,
+                                                              uint64_t k_first, uint64_t k_end)
+{
+    const uint64_t k = k_first + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= k_end)
+        return;
+    const int32_t *e = epmin + 4 * k;
+    epmin4[k] = imin(imin(e[0], e[1]), imin(e[2], e[3]));
+}
+
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
                                int32_t *es, int32_t *mint, int32_t *ep, int32_t *epmin,
-                               uint64_t j_lo, uint64_t j_hi, hipStream_t stream)
+                               int32_t *epmin4, uint64_t j_lo, uint64_t j_hi, hipStream_t stream)
 {
     const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
     hipLaunchKernelGGL(build_suffix_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
@@ -300,13 +314,25 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
         return hipErrorInvalidValue;  // (the builder stages at most 32 x 32 entries of U)
     hipLaunchKernelGGL(build_prefix_gray_kernel, dim3((unsigned)grid), dim3(1u << L), 0, stream,
                        U, ns, A, L, blk_first, blk_end, ep, epmin);
+    err = hipGetLastError();
+    if (err != hipSuccess || A < kU + 2)
+        return err;
+    // groups of four bodies holding the slice's bodies (their epmin entries lie
+    // inside the prefix blocks just written: blocks span 2^L >= 128 steps)
+    const uint64_t k_first = j_lo >> (kU + 2), k_end = ((j_hi - 1) >> (kU + 2)) + 1;
+    const uint64_t g3 = (k_end - k_first + 255) / 256;
+    if (g3 > 0xffffffffull)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(build_group_min_kernel, dim3((unsigned)g3), dim3(256), 0, stream, epmin, epmin4,
+                       k_first, k_end);
     return hipGetLastError();
 }
 
-__global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad)
+__global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int32_t *epmin4_pad)
 {
     epmin_pad[0] = INT_MAX;  // read ahead by the last two bodies of the walk, never used
     epmin_pad[1] = INT_MAX;
+    epmin4_pad[0] = INT_MAX;  // read ahead by the walk's last group, never used
     ctrl->counter = 0;
     ctrl->gbest = t0;
     ctrl->slow_total = 0;
@@ -314,9 +340,10 @@ __global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad)
     ctrl->checked_total = 0;
 }
 
-hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, hipStream_t stream)
+hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int32_t *epmin4_pad,
+                            hipStream_t stream)
 {
-    hipLaunchKernelGGL(init_ctrl_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0, epmin_pad);
+    hipLaunchKernelGGL(init_ctrl_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0, epmin_pad, epmin4_pad);
     return hipGetLastError();
 }
 
@@ -752,16 +779,15 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
         // 64-bit Gray step is formed only where a walk needs it.
         const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
         const uint32_t b0 = (uint32_t)(j_begin >> kU);
-        int epm_cur = Gated ? epmin[b0] : 0;
-        int epm_next = Gated ? epmin[b0 + 1] : 0;
+        // The group gate's prefix bound comes from the per-group table, read one
+        // group ahead (the table has one padding entry past the last group); the
+        // body minima are read only where a pair or body gate needs them.
+        int q_next = Gated && A > kU + 1 ? a.epmin4[(b0 + 3) >> 2] : 0;
         uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
             const uint32_t b = b0 + bi;
             const bool last = bi + 1 == nbodies;
             const bool top_plus = (b & 1u) == 0;
-            int epm_after = 0;
-            if (Gated)  // the table has two padding entries past the last body
-                epm_after = epmin[b + 2];
             bool check = true;
             if (Gated) {
                 // Padding columns hold INT_MAX with zero rows (beta 0), so a lane
@@ -775,26 +801,32 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                     if ((b & 3u) == 0 && bi + 3 < nbodies && A > kU + 1) {
                         // The first of four aligned bodies: their 128 states of Gray
                         // bits 0..6 fall by at most beta_q(bit 6 at the group's start).
-                        const int epm_4 = epmin[b + 3];
-                        const int thq = T - imin(imin(epm_cur, epm_next), imin(epm_after, epm_4));
+                        const int q = q_next;
+                        q_next = a.epmin4[(b >> 2) + 1];
+                        const int thq = T - q;
                         const int bq = emin + (((b >> 2) & 1u) ? beta_q1 : beta_q0);
                         if (__builtin_amdgcn_ballot_w64(bq <= thq) == 0)
                             covered = 3;
                     }
-                    if (covered == 0 && top_plus && !last && A > kU) {
-                        // An even body and its partner: the 64 states of Gray bits
-                        // 0..5 fall by at most beta_p(bit 5 at the pair's start).
-                        const int thp = T - imin(epm_cur, epm_next);
-                        const int bp = emin + (((b >> 1) & 1u) ? beta_p1 : beta_p0);
-                        if (__builtin_amdgcn_ballot_w64(bp <= thp) == 0)
-                            covered = 1;
-                    }
                     if (covered != 0) {
                         check = false;
                     } else {
-                        const int thb = T - epm_cur;
-                        const int bound = emin + (top_plus ? beta_s0 : beta_s1);
-                        check = __builtin_amdgcn_ballot_w64(bound <= thb) != 0;
+                        const int epm_cur = epmin[b];
+                        if (top_plus && !last && A > kU) {
+                            // An even body and its partner: the 64 states of Gray bits
+                            // 0..5 fall by at most beta_p(bit 5 at the pair's start).
+                            const int thp = T - imin(epm_cur, epmin[b + 1]);
+                            const int bp = emin + (((b >> 1) & 1u) ? beta_p1 : beta_p0);
+                            if (__builtin_amdgcn_ballot_w64(bp <= thp) == 0)
+                                covered = 1;
+                        }
+                        if (covered != 0) {
+                            check = false;
+                        } else {
+                            const int thb = T - epm_cur;
+                            const int bound = emin + (top_plus ? beta_s0 : beta_s1);
+                            check = __builtin_amdgcn_ballot_w64(bound <= thb) != 0;
+                        }
                     }
                 }
             }
@@ -862,8 +894,6 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                 else
                     sub_row(E, row);
             }
-            epm_cur = epm_next;
-            epm_next = epm_after;
         }
     }
 

@@ -215,6 +215,8 @@ Layout layout_of(const qubo_plan &p)
     off = align256(off + (1ull << p.prefix_bits) * 4);
     L.off_epmin = off;
     off = align256(off + ((1ull << (p.prefix_bits - kRegBits)) + 2) * 4);  // + 2 padding entries
+    L.off_epmin4 = off;  // per aligned group of four bodies, + 1 padding entry
+    off = align256(off + ((p.prefix_bits > kRegBits + 2 ? 1ull << (p.prefix_bits - kRegBits - 2) : 1ull) + 1) * 4);
     L.off_partials = off;
     off = align256(off + (uint64_t)p.blocks * 64);  // one partial (at most 64 bytes) per workgroup
     L.off_ctrl = off;

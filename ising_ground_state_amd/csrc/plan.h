@@ -53,7 +53,7 @@ void reduce_fixed(const std::vector<int32_t> &U, int n, int k, uint64_t f,
 // Device workspace layout of a plan (byte offsets, all 256-aligned).
 struct Layout {
     uint64_t cols_padded;  // 2^B rounded up to a multiple of the column-group size
-    uint64_t off_u, off_es, off_mint, off_ep, off_epmin, off_partials, off_ctrl;
+    uint64_t off_u, off_es, off_mint, off_ep, off_epmin, off_epmin4, off_partials, off_ctrl;
     uint64_t total;
 };
 Layout layout_of(const qubo_plan &p);

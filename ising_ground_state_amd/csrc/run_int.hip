@@ -98,6 +98,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     int32_t *dmint = reinterpret_cast<int32_t *>(base + L.off_mint);
     int32_t *dep = reinterpret_cast<int32_t *>(base + L.off_ep);
     int32_t *depmin = reinterpret_cast<int32_t *>(base + L.off_epmin);
+    int32_t *depmin4 = reinterpret_cast<int32_t *>(base + L.off_epmin4);
     Partial *dpart = reinterpret_cast<Partial *>(base + L.off_partials);
     Ctrl *dctrl = reinterpret_cast<Ctrl *>(base + L.off_ctrl);
 
@@ -112,7 +113,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
         return QUBO_EDEVICE;
     if (hipMemcpyAsync(dU, U.data(), U.size() * 4, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
-    if (launch_build_tables(dU, ns, A, B, L.cols_padded, des, dmint, dep, depmin, lo, hi, rq.stream) !=
+    if (launch_build_tables(dU, ns, A, B, L.cols_padded, des, dmint, dep, depmin, depmin4, lo, hi, rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;
     if (!mark(1))
@@ -141,7 +142,9 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     int32_t t0 = (lo == 0 && !lowest) ? 0 : (int32_t)abs_sum;
     if (have_t0 && t0_cap < t0)
         t0 = t0_cap;
-    if (launch_init_ctrl(dctrl, t0, depmin + (1ull << (A - kRegBits)), rq.stream) != hipSuccess)
+    const uint64_t groups = A > kRegBits + 2 ? 1ull << (A - kRegBits - 2) : 1ull;
+    if (launch_init_ctrl(dctrl, t0, depmin + (1ull << (A - kRegBits)), depmin4 + groups, rq.stream) !=
+        hipSuccess)
         return QUBO_EDEVICE;
 
     SearchArgs sa{};
@@ -149,6 +152,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     sa.mint = dmint;
     sa.ep = dep;
     sa.epmin = depmin;
+    sa.epmin4 = depmin4;
     sa.partials = dpart;
     sa.ctrl = dctrl;
     sa.cols_padded = L.cols_padded;
