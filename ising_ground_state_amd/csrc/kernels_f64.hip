@@ -574,14 +574,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         float E[kR];
         uint64_t anchor_j = j_begin;  // E64 holds the suffix energies at prefix g(anchor_j)
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
-            const uint32_t b = b0 + bi;
-            const bool last = bi + 1 == nbodies;
+            uint32_t b = b0 + bi;
+            bool last = bi + 1 == nbodies;
             const bool top_plus = (b & 1u) == 0;
-            const float epm_after = epmin[b + 2];
+            float epm_after = epmin[b + 2];
             // The first body of an aligned group, and a unit's first body, start
             // from the binary64 anchor E64 (rounded to nearest); the others
             // continue the fp32 walk, so E64 moves once per group.
-            const uint32_t in_group = b & (kAnchorGroup - 1);
+            uint32_t in_group = b & (kAnchorGroup - 1);
             const bool carried = in_group != 0 && bi != 0;
             if (!carried) {
 #pragma unroll
@@ -617,7 +617,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 }
             }
             ++bodies;
-            if (!check) {
+            if (!check && (b & 3u) == 0 && covered >= 3) {
+                // An aligned group of four bodies cleared by the group bound: all
+                // four run here with their row signs fixed, joined by the flips of
+                // Gray bits 5, 6 and 5 (inside the anchor group).
+                float row[kR];
+                adds_body(E, Mr, true);
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    row[r] = carry_lane[r * 64];
+                if ((((b + 1) >> 1) & 1u) == 0)
+                    step_rows<true>(E, row);
+                else
+                    step_rows<false>(E, row);
+                adds_body(E, Mr, false);
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    row[r] = carry_lane[kGroup + r * 64];
+                if ((((b + 2) >> 2) & 1u) == 0)
+                    step_rows<true>(E, row);
+                else
+                    step_rows<false>(E, row);
+                adds_body(E, Mr, true);
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    row[r] = carry_lane[r * 64];
+                if ((((b + 3) >> 1) & 1u) == 0)
+                    step_rows<true>(E, row);
+                else
+                    step_rows<false>(E, row);
+                covered -= 3;
+                bodies += 3;
+                bi += 3;
+                b += 3;
+                last = bi + 1 == nbodies;
+                in_group = b & (kAnchorGroup - 1);
+                epm_cur = epmin[b];
+                epm_next = epmin[b + 1];
+                epm_after = epmin[b + 2];
+                adds_body(E, Mr, false);
+            } else if (!check && top_plus && covered != 0) {
+                // An even body whose odd partner a bound has cleared too: both run
+                // here with their row signs fixed, joined by the flip of Gray bit 5
+                // (inside the anchor group: an even body is never its last).
+                adds_body(E, Mr, true);
+                const uint32_t b1 = b + 1;
+                float row5[kR];
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    row5[r] = carry_lane[r * 64];
+                if (((b1 >> 1) & 1u) == 0)
+                    step_rows<true>(E, row5);
+                else
+                    step_rows<false>(E, row5);
+                --covered;
+                ++bodies;
+                ++bi;
+                b = b1;
+                last = bi + 1 == nbodies;
+                in_group = b & (kAnchorGroup - 1);
+                epm_cur = epm_next;
+                epm_next = epm_after;
+                epm_after = epmin[b + 2];
+                adds_body(E, Mr, false);
+            } else if (!check) {
                 adds_body(E, Mr, top_plus);
             } else {
                 // Exact walk: every state within delta of T is re-evaluated.
