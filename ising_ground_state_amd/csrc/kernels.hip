@@ -38,7 +38,10 @@
 //     reaches are walked on the exact path, and every other state costs its add
 //     alone;
 //   * the threshold T is shared between waves through a global best-so-far, which
-//     is always a real state's energy, so no minimiser is ever skipped.
+//     is always a real state's energy, so no minimiser is ever skipped;
+//   * at the end, each wave combines its lanes' records with DPP lane moves,
+//     the workgroup's four waves through LDS, and one small kernel the
+//     workgroups' partials (the reduction tree of sec. IV.B.6).
 #include "kernels.h"
 #include "dpp.h"
 
@@ -771,9 +774,8 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
             T = gb < T ? gb : T;
         }
 
-        // Body minima of the prefix energies are read two bodies ahead (scalar
-        // loads).  The body loop counts with 32-bit scalars (the SALU has no
-        // 64-bit less-than): a segment holds at most 2^13 bodies.
+        // The body loop counts with 32-bit scalars (the SALU has no 64-bit
+        // less-than): a segment holds at most 2^13 bodies.
         // Bodies are counted by their index b = j >> 5, a 32-bit value (A <= 32),
         // so that the per-body bookkeeping is 32-bit scalar arithmetic; the
         // 64-bit Gray step is formed only where a walk needs it.

@@ -1,8 +1,8 @@
 // qubo_search_noalloc: the int32 whole-space search of qubo_search without any
 // device allocation, for callers that cannot allocate (code under graph capture,
 // tight serving loops, harnesses that forbid it).  The workspace (U, E_s, M_int,
-// the Gray-ordered prefix energies, their per-body minima, the per-wave partials
-// and the control block) lives in one static device array per GPU.
+// the Gray-ordered prefix energies, their per-body and per-group minima, the
+// per-workgroup partials and the control block) lives in one static device array per GPU.
 #include "host.h"
 
 #include <mutex>

@@ -4,7 +4,7 @@
 //      triangle and check the overflow guard;
 //   2. plan the split (prefix A, suffix B, cached Gray bits, work units);
 //   3. one stream-ordered allocation for U, E_s, M_int, the Gray-ordered E_p,
-//      the per-wave partial results and a control block (or the caller's
+//      the per-workgroup partial results and a control block (or the caller's
 //      device buffer, for the entry point that allocates nothing);
 //   4. cache builders, search kernel, final reduction, 64-byte result download;
 //   5. free and synchronise the stream.
