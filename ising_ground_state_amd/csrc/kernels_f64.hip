@@ -594,9 +594,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 --covered;
             } else {
                 const float emin = row_min8(E);
-                // (the k-lowest search, whose threshold is its list's k-th energy,
-                // measured slower with this gate than without it)
-                if (!Lowest && (in_group & 3u) == 0 && bi + 3 < nbodies && A > kU + 1) {
+                if ((in_group & 3u) == 0 && bi + 3 < nbodies && A > kU + 1) {
                     // four aligned bodies (never across an anchor group)
                     const float epm_4 = epmin[b + 3];
                     const float bq = emin + (((b >> 2) & 1u) ? beta_q1 : beta_q0);
