@@ -44,6 +44,41 @@ std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_searc
     return P;
 }
 
+int64_t descent_energy(const std::vector<int32_t> &U, int n)
+{
+    // F[v]: the change of E when variable v goes from 0 to 1 given the others
+    // (U_vv plus the couplings to the set variables); flipping v moves E by F[v]
+    // if x_v = 0 and by -F[v] if x_v = 1.
+    std::vector<int64_t> F((size_t)n);
+    std::vector<int> x((size_t)n, 0);
+    for (int v = 0; v < n; ++v)
+        F[(size_t)v] = U[(size_t)v * n + v];
+    int64_t e = 0;
+    for (int step = 0; step < 4 * n + 4; ++step) {
+        int best = -1;
+        int64_t best_d = 0;
+        for (int v = 0; v < n; ++v) {
+            const int64_t d = x[(size_t)v] ? -F[(size_t)v] : F[(size_t)v];
+            if (d < best_d) {
+                best_d = d;
+                best = v;
+            }
+        }
+        if (best < 0)
+            break;  // a local minimum under single flips
+        const int64_t s = x[(size_t)best] ? -1 : 1;
+        x[(size_t)best] ^= 1;
+        e += best_d;
+        for (int j = 0; j < n; ++j) {
+            if (j == best)
+                continue;
+            const int32_t u = j < best ? U[(size_t)j * n + best] : U[(size_t)best * n + j];
+            F[(size_t)j] += s * u;
+        }
+    }
+    return e;
+}
+
 static int ceil_log2(uint64_t v)
 {
     int k = 0;

@@ -34,6 +34,12 @@ int fold_upper(const int32_t *Q, int n, std::vector<int32_t> &U, int64_t *abs_su
 // U_ii = +1 and no couplings, so they are 0 in every minimiser.
 std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_search);
 
+// Energy of the state that a steepest single-flip descent from state 0 reaches on
+// the folded matrix U (n x n upper triangle): a real state's energy, at most
+// E(0) = 0, used as the first threshold of a whole-space minimum search so that
+// the bound gates clear bodies from the start.  Exact in int64.
+int64_t descent_energy(const std::vector<int32_t> &U, int n);
+
 // Fills `out` for n variables on a device with `num_cus` compute units;
 // cols_per_lane is 8 or 16, or 0 for the default.  split_bits: -1 splits only
 // above kMaxSingleVars (by n - kMaxSingleVars fixed variables), 0 never, k > 0
