@@ -50,6 +50,7 @@ struct SearchArgsF64 {
     const float *mint32;    // [A][cols_padded]    the same rows rounded to fp32 (the walk's rows)
     const double *ep;       // [2^A]               E_p(g(j))
     const float *epmin;     // [2^A / 32 + 2]      min over each body of ep rounded to fp32, + 2 padding
+    const float *epmin4;    // [2^A / 128 + 1]     min of epmin over each aligned group of 4 bodies, + 1 padding
     const double *Q;        // [n][n]              the caller's matrix (the definition's terms)
     PartialF64 *partials;   // [gridDim.x]: one per workgroup
     CtrlF64 *ctrl;
@@ -72,9 +73,11 @@ struct SearchArgsF64 {
 // of 32; the tables keep their full size).
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
                                    double *es, double *mint, float *mint32, double *ep,
-                                   float *epmin, uint64_t j_lo, uint64_t j_hi, hipStream_t stream);
+                                   float *epmin, float *epmin4, uint64_t j_lo, uint64_t j_hi,
+                                   hipStream_t stream);
 
-hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, hipStream_t stream);
+hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, float *epmin4_pad,
+                                hipStream_t stream);
 
 // lowest: the k-lowest search (each wave keeps its k lowest states in
 // args.lists) instead of the minimum, count and lowest minimiser.

@@ -283,10 +283,25 @@ __global__ __launch_bounds__(256) void build_prefix_f64_kernel(const double *__r
     }
 }
 
-__global__ void init_ctrl_f64_kernel(CtrlF64 *ctrl, double t0, float *epmin_pad)
+// The group gate's prefix bound: the minimum of the body minima over each
+// aligned group of four bodies.  Groups that straddle the slice's ends get
+// values that are never read.
+__global__ __launch_bounds__(256) void build_group_min_f64_kernel(const float *__restrict__ epmin,
+                                                                  float *__restrict__ epmin4,
+                                                                  uint64_t k_first, uint64_t k_end)
+{
+    const uint64_t k = k_first + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= k_end)
+        return;
+    const float *e = epmin + 4 * k;
+    epmin4[k] = fminf(fminf(e[0], e[1]), fminf(e[2], e[3]));
+}
+
+__global__ void init_ctrl_f64_kernel(CtrlF64 *ctrl, double t0, float *epmin_pad, float *epmin4_pad)
 {
     epmin_pad[0] = __int_as_float(0x7f800000);
     epmin_pad[1] = __int_as_float(0x7f800000);
+    epmin4_pad[0] = __int_as_float(0x7f800000);
     ctrl->counter = 0;
     ctrl->gbest = order_key(t0);
     ctrl->slow_total = 0;
@@ -568,8 +583,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         // 64-bit Gray step is formed only on the rare paths that need it.
         const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
         const uint32_t b0 = (uint32_t)(j_begin >> kU);
-        float epm_cur = epmin[b0];
-        float epm_next = epmin[b0 + 1];
+        // The group gate's prefix bound comes from the per-group table, read one
+        // group ahead (one padding entry past the last group); the body minima are
+        // read only where a pair or body gate needs them.
+        float q_next = A > kU + 1 ? a.epmin4[(b0 + 3) >> 2] : 0.f;
         uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
         float E[kR];
         uint64_t anchor_j = j_begin;  // E64 holds the suffix energies at prefix g(anchor_j)
@@ -577,7 +594,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
             uint32_t b = b0 + bi;
             bool last = bi + 1 == nbodies;
             const bool top_plus = (b & 1u) == 0;
-            float epm_after = epmin[b + 2];
             // The first body of an aligned group, and a unit's first body, start
             // from the binary64 anchor E64 (rounded to nearest); the others
             // continue the fp32 walk, so E64 moves once per group.
@@ -596,22 +612,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 const float emin = row_min8(E);
                 if ((in_group & 3u) == 0 && bi + 3 < nbodies && A > kU + 1) {
                     // four aligned bodies (never across an anchor group)
-                    const float epm_4 = epmin[b + 3];
+                    const float q = q_next;
+                    q_next = a.epmin4[(b >> 2) + 1];
                     const float bq = emin + (((b >> 2) & 1u) ? beta_q1 : beta_q0);
-                    const float ep4 = uniform_fmin(uniform_fmin(epm_cur, epm_next), uniform_fmin(epm_after, epm_4));
-                    if (__builtin_amdgcn_ballot_w64(bq + ep4 <= TD) == 0)
+                    if (__builtin_amdgcn_ballot_w64(bq + q <= TD) == 0)
                         covered = 3;
-                }
-                if (covered == 0 && top_plus && !last && A > kU) {
-                    const float bp = emin + (((b >> 1) & 1u) ? beta_p1 : beta_p0);
-                    if (__builtin_amdgcn_ballot_w64(bp + uniform_fmin(epm_cur, epm_next) <= TD) == 0)
-                        covered = 1;
                 }
                 if (covered != 0) {
                     check = false;
                 } else {
-                    const float bound = emin + (top_plus ? beta_s0 : beta_s1);
-                    check = __builtin_amdgcn_ballot_w64(bound + epm_cur <= TD) != 0;
+                    const float epm_cur = epmin[b];
+                    if (top_plus && !last && A > kU) {
+                        const float bp = emin + (((b >> 1) & 1u) ? beta_p1 : beta_p0);
+                        if (__builtin_amdgcn_ballot_w64(bp + uniform_fmin(epm_cur, epmin[b + 1]) <= TD) == 0)
+                            covered = 1;
+                    }
+                    if (covered != 0) {
+                        check = false;
+                    } else {
+                        const float bound = emin + (top_plus ? beta_s0 : beta_s1);
+                        check = __builtin_amdgcn_ballot_w64(bound + epm_cur <= TD) != 0;
+                    }
                 }
             }
             ++bodies;
@@ -650,9 +671,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 b += 3;
                 last = bi + 1 == nbodies;
                 in_group = b & (kAnchorGroup - 1);
-                epm_cur = epmin[b];
-                epm_next = epmin[b + 1];
-                epm_after = epmin[b + 2];
                 adds_body(E, Mr, false);
             } else if (!check && top_plus && covered != 0) {
                 // An even body whose odd partner a bound has cleared too: both run
@@ -674,9 +692,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 b = b1;
                 last = bi + 1 == nbodies;
                 in_group = b & (kAnchorGroup - 1);
-                epm_cur = epm_next;
-                epm_next = epm_after;
-                epm_after = epmin[b + 2];
                 adds_body(E, Mr, false);
             } else if (!check) {
                 adds_body(E, Mr, top_plus);
@@ -849,8 +864,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                     anchor_j = next;
                 }
             }
-            epm_cur = epm_next;
-            epm_next = epm_after;
         }
     }
 
@@ -987,7 +1000,8 @@ __global__ __launch_bounds__(256) void lowest_merge_f64_kernel(const LowEntryF64
 
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
                                    double *es, double *mint, float *mint32, double *ep,
-                                   float *epmin, uint64_t j_lo, uint64_t j_hi, hipStream_t stream)
+                                   float *epmin, float *epmin4, uint64_t j_lo, uint64_t j_hi,
+                                   hipStream_t stream)
 {
     const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
     hipLaunchKernelGGL(build_suffix_f64_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
@@ -1002,12 +1016,24 @@ hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64
     const uint64_t grid = blocks < (1ull << 14) ? blocks : (1ull << 14);
     hipLaunchKernelGGL(build_prefix_f64_kernel, dim3((unsigned)grid), dim3(256), 0, stream, U, ns,
                        A, j_first, j_hi, ep, epmin);
+    err = hipGetLastError();
+    if (err != hipSuccess || A < kU + 2)
+        return err;
+    // groups of four bodies holding the slice's bodies (inside the 256-step
+    // blocks the prefix builder just wrote)
+    const uint64_t k_first = j_lo >> (kU + 2), k_end = ((j_hi - 1) >> (kU + 2)) + 1;
+    const uint64_t g3 = (k_end - k_first + 255) / 256;
+    if (g3 > 0xffffffffull)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(build_group_min_f64_kernel, dim3((unsigned)g3), dim3(256), 0, stream, epmin, epmin4,
+                       k_first, k_end);
     return hipGetLastError();
 }
 
-hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, hipStream_t stream)
+hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, float *epmin4_pad,
+                                hipStream_t stream)
 {
-    hipLaunchKernelGGL(init_ctrl_f64_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0, epmin_pad);
+    hipLaunchKernelGGL(init_ctrl_f64_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0, epmin_pad, epmin4_pad);
     return hipGetLastError();
 }
 

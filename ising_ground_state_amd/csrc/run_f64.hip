@@ -97,7 +97,9 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     const uint64_t off_mint32 = al(off_mint + (uint64_t)A * cols_padded * 8);
     const uint64_t off_ep = al(off_mint32 + (uint64_t)A * cols_padded * 4);
     const uint64_t off_epmin = al(off_ep + (1ull << A) * 8);
-    const uint64_t off_part = al(off_epmin + ((1ull << (A - kRegBits)) + 2) * 4);
+    const uint64_t groups = A > kRegBits + 2 ? 1ull << (A - kRegBits - 2) : 1ull;
+    const uint64_t off_epmin4 = al(off_epmin + ((1ull << (A - kRegBits)) + 2) * 4);
+    const uint64_t off_part = al(off_epmin4 + (groups + 1) * 4);
     const uint64_t off_ctrl = al(off_part + (uint64_t)blocks * sizeof(PartialF64));  // one per workgroup
     // the k-lowest search: the per-wave lists, the merged list and its length
     const uint64_t list_entries = lowest ? (uint64_t)blocks * kWavesPerBlock * rq.lowest_k : 0;
@@ -118,6 +120,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     float *dmint32 = reinterpret_cast<float *>(base + off_mint32);
     double *dep = reinterpret_cast<double *>(base + off_ep);
     float *depmin = reinterpret_cast<float *>(base + off_epmin);
+    float *depmin4 = reinterpret_cast<float *>(base + off_epmin4);
     PartialF64 *dpart = reinterpret_cast<PartialF64 *>(base + off_part);
     CtrlF64 *dctrl = reinterpret_cast<CtrlF64 *>(base + off_ctrl);
     if (!call.create_events())
@@ -140,12 +143,13 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess ||
         hipMemcpyAsync(dU, U.data(), U.size() * 8, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
-    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, des, dmint, dmint32, dep, depmin, lo, hi,
+    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, des, dmint, dmint32, dep, depmin, depmin4, lo, hi,
                                 rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess ||
-        launch_init_ctrl_f64(dctrl, t0, depmin + (1ull << (A - kRegBits)), rq.stream) != hipSuccess)
+        launch_init_ctrl_f64(dctrl, t0, depmin + (1ull << (A - kRegBits)), depmin4 + groups, rq.stream) !=
+            hipSuccess)
         return QUBO_EDEVICE;
     SearchArgsF64 sa{};
     sa.es = des;
@@ -153,6 +157,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     sa.mint32 = dmint32;
     sa.ep = dep;
     sa.epmin = depmin;
+    sa.epmin4 = depmin4;
     sa.Q = rq.Q;
     sa.partials = dpart;
     sa.ctrl = dctrl;
