@@ -46,7 +46,7 @@ PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gray_search_gated_n48_counter
 # (split, segments, LDS rows) and the host run that sizes the grid, and the
 # compiler flags.
 KERNEL_INPUTS = [os.path.join(ROOT, "ising_ground_state_amd", "csrc", name)
-                 for name in ("kernels.hip", "kernels.h", "dpp.h", "plan.cpp", "plan.h", "run_int.hip")]
+                 for name in ("kernels.hip", "kernels.h", "walk.h", "dpp.h", "plan.cpp", "plan.h", "run_int.hip")]
 
 
 _C_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"', re.S)
@@ -396,9 +396,10 @@ def main():
         tf = q.last_timing()
         line["f64_C4f"] = {"value": states / (time.perf_counter() - t1) / 1e12, "unit": "1e12 states/s",
                            "workload": cf["desc"] + ", seed %d" % cf["seed"],
-                           "kernel": "gray_search_f64_kernel (fp32 walk, binary64 anchors and re-evaluation)",
+                           "kernel": "gray_search_f64_kernel (int32 walk over rounded scaled tables, "
+                                     "binary64 re-evaluation)",
                            "kernel_ms": tf["search_ms"],
-                           "frac_fp32_add_peak": states / (tf["search_ms"] / 1e3) / INT32_VALU_PEAK,
+                           "frac": OPS_PER_STATE * states / (tf["search_ms"] / 1e3) / INT32_VALU_PEAK,
                            "slow_bodies": tf["slow_bodies"], "candidates": tf["candidates"],
                            "coverage_ok": covers(tf, plan["prefix_bits"], plan["suffix_bits"]),
                            "result": [float.hex(rf.min_energy), rf.argmin, rf.count]}
@@ -410,8 +411,9 @@ def main():
         tl = q.last_timing()
         line["f64_spectrum_k64"] = {"value": states / (time.perf_counter() - t1) / 1e12, "unit": "1e12 states/s",
                                     "kernel": "gray_search_f64_kernel<lowest> (the 64 lowest binary64 states)",
-                                    "kernel_ms": tl["search_ms"], "slow_bodies": tl["slow_bodies"],
-                                    "candidates": tl["candidates"],
+                                    "kernel_ms": tl["search_ms"],
+                                    "frac": OPS_PER_STATE * states / (tl["search_ms"] / 1e3) / INT32_VALU_PEAK,
+                                    "slow_bodies": tl["slow_bodies"], "candidates": tl["candidates"],
                                     "first": [float.hex(lowf[0][0]), lowf[0][1]],
                                     "last": [float.hex(lowf[-1][0]), lowf[-1][1]],
                                     "head_is_min": (lowf[0][0], lowf[0][1]) == (rf.min_energy, rf.argmin)}

@@ -111,9 +111,9 @@ QUBO_API int qubo_abs_sum(const int32_t *Q_host, int n, int64_t *abs_sum);
 /* Host only; touches no device.  The guard of the binary64 searches
  * (qubo_search_f64 and its relatives) on a host copy of Q (n x n binary64,
  * row-major): every entry finite and S = sum |Q_ij| either 0 or in
- * [2^-100, 2^100].  Above, fp32 values of the walk could overflow; below, the
- * absolute error of fp32 arithmetic near its underflow threshold could exceed
- * the re-evaluation margin 2^-13 S.
+ * [2^-100, 2^100].  The range keeps the walk's scale factor 2^(17 - e)
+ * (S < 2^e) and every binary64 sum of the tables and the definition well
+ * inside binary64's normal range, with room to spare at both ends.
  * Returns QUBO_OK, QUBO_EINVAL (null Q, n outside [1, 63]) or QUBO_ERANGE. */
 QUBO_API int qubo_check_q_f64(const double *Q_host, int n);
 
@@ -260,17 +260,19 @@ typedef struct {
 } qubo_result_f64;
 /* Q: device pointer, n x n binary64, row-major; read only.  n: 1..58 (no
  * outer split).  prefix_bits, cache_bits, gray_lo, gray_hi, stream: as for
- * qubo_search_ex (cache_bits defaults to min(A, 10): binary64 rows in LDS).
- * flags: 0 or QUBO_FLAG_COLS8.  Every entry must be finite and sum |Q_ij|
+ * qubo_search_ex (the same planner and defaults).
+ * flags: 0 or QUBO_FLAG_COLS8.  Every entry must be finite and S = sum |Q_ij|
  * either 0 or in [2^-100, 2^100] (else QUBO_ERANGE; qubo_check_q_f64).
- * The walk is the integer kernel's, with a binary64 anchor per column advanced
- * once per 32 32-step bodies and every state one fp32 add; a
- * state whose fp32 energy comes within delta = 2^-13 sum |Q_ij| of the best
- * exact energy so far is re-evaluated from the definition on the GPU, so the
- * result is exactly the definition's.  Instances with many states within delta
- * of the minimum (e.g. Q = 0) are correct but slow: each such state costs an
- * O(n^2) evaluation.  Blocking; same ownership and error behaviour as
- * qubo_search_ex; qubo_last_timing reports the re-evaluated states. */
+ * The walk is the integer kernel's (one int32 add per state) over the tables
+ * of eq. 8 formed in binary64, scaled by s = 2^e (s S <= 2^17) and rounded to
+ * integers once each; a state's walked value then lies within A/2 + 2 of
+ * s E(x), and a state whose walked value comes within M = A/2 + 3 of s times
+ * the best exact energy so far (about 2^-13 S) is re-evaluated from the
+ * definition on the GPU, so the result is exactly the definition's.  Instances
+ * with many states that close to the minimum (e.g. Q = 0) are correct but
+ * slow: each such state costs an O(n^2) evaluation.  Blocking; same ownership
+ * and error behaviour as qubo_search_ex; qubo_last_timing reports the
+ * re-evaluated states. */
 QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_bits,
                              uint64_t gray_lo, uint64_t gray_hi, uint32_t flags, void *stream,
                              qubo_result_f64 *out);
@@ -280,8 +282,8 @@ QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_
  * qubo_search_lowest does for int32.  k: 1..QUBO_MAX_LOWEST.  Arguments, limits
  * and errors as for qubo_search_f64; out: host pointer to k entries, entries
  * 0..*found-1 receive the states in order; found: min(k, states searched).
- * Every state whose fp32 energy comes within delta of the lowest k-th exact
- * energy of any wave is re-evaluated from the definition, so the list is
+ * Every state whose walked value comes within the margin of the lowest k-th
+ * exact energy of any wave is re-evaluated from the definition, so the list is
  * exactly the definition's. */
 typedef struct {
     double energy;

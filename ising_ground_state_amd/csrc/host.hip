@@ -56,14 +56,11 @@ uint64_t fingerprint(const void *Qh, size_t bytes, int n)
 }
 
 // The binary64 guard: finite entries and S = sum |Q_ij| (rounded up) either 0
-// or in [2^-100, 2^100].  The upper end keeps every fp32 value of the walk in
-// range.  The lower end keeps the filter margin 2^-13 S above the absolute
-// error of fp32 arithmetic near underflow: each fp32 rounding errs by at most
-// 2^-24 of its result plus 2^-126 (the largest error of a value flushed to zero;
-// this build keeps subnormals, which err by at most 2^-150), and the fewer than
-// 1100 roundings between a binary64 anchor and a compare add at most 2^-115.8,
-// below the 988 * 2^-24 S >= 2^-114.1 of the margin left over by the relative
-// terms.  S = 0 means every entry is zero: every fp32 value is then exactly 0.
+// or in [2^-100, 2^100].  The walk of the binary64 search runs on its tables
+// scaled by s = 2^(17 - e) with S < 2^e and rounded to integers; the range
+// keeps s, s S and every binary64 sum of the tables and of the definition well
+// inside binary64's normal range (where each rounding errs by at most 2^-53 of
+// its result), with room at both ends.  S = 0 means every entry is zero.
 int guard_f64(const std::vector<double> &Qh, double *S_out)
 {
     double S = 0.0;

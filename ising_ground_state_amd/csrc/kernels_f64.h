@@ -8,14 +8,21 @@
 
 namespace qubo {
 
-// Suffix columns per lane of the binary64 search (four waves per SIMD).  Four columns fit six waves but ran 10 % slower: a body's fixed work
-// then covers half as many states.
+// Suffix columns per lane of the binary64 search (the integer search's default).
 constexpr int kColsPerLaneF64 = 8;
 
-// The lowest Gray bit whose binary64 row the search keeps in LDS: the anchor of
-// a column moves once per aligned group of 32 32-step bodies, by the rows of
-// Gray bit 9 and of one bit above it.
-constexpr int kLdsFirstBitF64 = 9;
+// The walk's tables are the binary64 tables scaled by s = 2^e and rounded to
+// integers, with e chosen so that s * sum |Q_ij| <= 2^kQuantBits.  The scaled
+// sums then keep about as many significant bits as the integer workloads of
+// that size; wider words switch more bits per add and the chip then runs at
+// a lower clock.
+constexpr int kQuantBits = 17;
+
+// Padding columns of the rounded suffix energies: above every threshold the
+// filter can take (at most 2^(kQuantBits + 2) + 19 + 2^kQuantBits + 33 after
+// subtracting a prefix energy), so they are never candidates, and the sums the
+// walk and its gates form from them stay far from int32 overflow.
+constexpr int32_t kPadQ = 1 << 30;
 
 // One workgroup's partial result (48 bytes).
 struct PartialF64 {
@@ -45,12 +52,11 @@ struct CtrlF64 {
 };
 
 struct SearchArgsF64 {
-    const double *es;       // [cols_padded]       E_s(c)
-    const double *mint;     // [A][cols_padded]    M_int rows by prefix variable
-    const float *mint32;    // [A][cols_padded]    the same rows rounded to fp32 (the walk's rows)
-    const double *ep;       // [2^A]               E_p(g(j))
-    const float *epmin;     // [2^A / 32 + 2]      min over each body of ep rounded to fp32, + 2 padding
-    const float *epmin4;    // [2^A / 128 + 1]     min of epmin over each aligned group of 4 bodies, + 1 padding
+    const int32_t *es;      // [cols_padded]       rint(s E_s(c)); kPadQ for padding columns
+    const int32_t *mint;    // [A][cols_padded]    rint(s M_int) rows by prefix variable
+    const int32_t *ep;      // [2^A]               rint(s E_p(g(j)))
+    const int32_t *epmin;   // [2^A / 32 + 2]      min of ep over each 32-step body, + 2 padding
+    const int32_t *epmin4;  // [2^A / 128 + 1]     min of epmin over each aligned group of 4 bodies, + 1 padding
     const double *Q;        // [n][n]              the caller's matrix (the definition's terms)
     PartialF64 *partials;   // [gridDim.x]: one per workgroup
     CtrlF64 *ctrl;
@@ -58,25 +64,31 @@ struct SearchArgsF64 {
     uint64_t cols_padded;
     uint64_t gray_lo, gray_hi;
     uint64_t seg_first, segs, seg_blocks, items;
+    double scale;           // s = 2^e
     int32_t A, B;
     int32_t n;              // variables of Q
     int32_t pad;            // padding variables appended below n (n < 5), the lowest index bits
     int32_t l_eff;          // Gray bits with rows on chip (registers + LDS)
     int32_t seg_bits;
-    float delta;            // filter margin: bounds every fp32 rounding of the walk and the gate
+    int32_t margin;         // M: |W(x) - s E(x)| < M - 1 for every state (rounding and binary64 error)
+    int32_t cap;            // filter threshold above every rounded energy (2^(kQuantBits + 2))
     int32_t k_low;          // k-lowest search: states kept per wave (1..64), else 0
+    int32_t pad1;
 };
 
-// E_s, M_int and E_p(g(j)) in binary64 from the folded matrix, M_int rounded to
-// fp32, and the per-body minima of E_p rounded to fp32.
-// Only the prefix energies of the Gray steps [j_lo, j_hi) are written (multiples
-// of 32; the tables keep their full size).
+// The rounded tables from the folded binary64 matrix U (ns x ns upper triangle):
+// E_s and M_int per column, E_p(g(j)) for the Gray steps [j_lo, j_hi)
+// (multiples of 32; the tables keep their full size), each sum formed in
+// binary64 and then scaled by `scale` and rounded to the nearest integer once;
+// the per-body and per-group minima of the rounded prefix energies.
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
-                                   double *es, double *mint, float *mint32, double *ep,
-                                   float *epmin, float *epmin4, uint64_t j_lo, uint64_t j_hi,
+                                   double scale, int32_t *es, int32_t *mint, int32_t *ep,
+                                   int32_t *epmin, int32_t *epmin4, uint64_t j_lo, uint64_t j_hi,
                                    hipStream_t stream);
 
-hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, float *epmin_pad, float *epmin4_pad,
+// Resets the work counter, seeds the shared bound with t0 and fills the
+// padding entries of the body and group minima.
+hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, int32_t *epmin_pad, int32_t *epmin4_pad,
                                 hipStream_t stream);
 
 // lowest: the k-lowest search (each wave keeps its k lowest states in

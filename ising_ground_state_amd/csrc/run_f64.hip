@@ -20,34 +20,21 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     if (!rq.Q || rq.n < 1 || rq.n > kMaxSingleVars || (lowest ? (!low || rq.lowest_k > kMaxLowest) : !out))
         return QUBO_EINVAL;
     const int n = rq.n;
-    // The binary64 rows of Gray bits 9 .. l-1 (the anchor's moves) sit in LDS
-    // (4 KiB each per workgroup): the default keeps 2 of them.
-    int cache_bits = rq.cache_bits;
-    if (cache_bits < 0 && n >= kMinSearchVars) {  // (tiny problems: the planner's fixed split)
-        qubo_plan probe;
-        const int rc0 = make_plan(n, rq.prefix_bits, -1, 256, kColsPerLaneF64, 0, &probe);
-        if (rc0 != QUBO_OK)
-            return rc0;
-        cache_bits = probe.prefix_bits < 11 ? probe.prefix_bits : 11;
-    }
     DeviceInfo dev;
     int rc = device_info(&dev);
     if (rc != QUBO_OK)
         return rc;
+    // The integer search's plan: the walk runs on int32 tables of the same shape.
     qubo_plan plan;
-    rc = make_plan(n, rq.prefix_bits, cache_bits, dev.num_cus, kColsPerLaneF64, 0, &plan);
+    rc = make_plan(n, rq.prefix_bits, rq.cache_bits, dev.num_cus, kColsPerLaneF64, 0, &plan);
     if (rc != QUBO_OK)
         return rc;
     const int ns = plan.n_search, A = plan.prefix_bits, B = plan.suffix_bits;
-    const int l_eff = plan.cache_bits;
     const int group = kWave * kColsPerLaneF64;
-    const int lds_bytes = (l_eff > kLdsFirstBitF64 ? l_eff - kLdsFirstBitF64 : 0) * group * 8;
-    if (lds_bytes > kMaxLdsBytes)
-        return QUBO_EPLAN;
+    const int lds_bytes = plan.lds_bytes;
 
     // Q to the host; the guard: finite entries and sum |Q_ij| either 0 or in
-    // [2^-100, 2^100], so that fp32 energies never overflow and the absolute
-    // error of fp32 near underflow stays inside the re-evaluation margin.
+    // [2^-100, 2^100].
     std::vector<double> Qh((size_t)n * n);
     if (hipMemcpyAsync(Qh.data(), rq.Q, Qh.size() * 8, hipMemcpyDeviceToHost, rq.stream) !=
             hipSuccess ||
@@ -58,15 +45,25 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     if (rc != QUBO_OK)
         return rc;
     // Fold to the upper triangle in binary64 (the walk's tables only; states
-    // are scored against Q itself) and pad small problems.
+    // are scored against Q itself) and pad small problems: a padding variable
+    // gets the positive diagonal S (1 for the zero matrix) and no couplings, so
+    // setting it raises a state's energy and keeps the tables on Q's scale.
     std::vector<double> U((size_t)ns * ns, 0.0);
     for (int i = 0; i < n; ++i) {
         U[(size_t)i * ns + i] = Qh[(size_t)i * n + i];
         for (int j = i + 1; j < n; ++j)
             U[(size_t)i * ns + j] = Qh[(size_t)i * n + j] + Qh[(size_t)j * n + i];
     }
+    const double pad_diag = S > 0.0 ? S : 1.0;
     for (int i = n; i < ns; ++i)
-        U[(size_t)i * ns + i] = 1.0;
+        U[(size_t)i * ns + i] = pad_diag;
+    // The scale s = 2^e with s * S_walk <= 2^kQuantBits, S_walk bounding the
+    // magnitude sum of the folded, padded matrix (and so of every table entry
+    // and every sub-sum the walk forms).
+    const double S_walk = S + (double)(ns - n) * pad_diag;
+    int ex = 0;
+    (void)std::frexp(S_walk, &ex);  // S_walk < 2^ex
+    const double scale = std::ldexp(1.0, kQuantBits - ex);
 
     uint64_t lo = 0, hi = 1ull << A;
     if (rq.ranged) {
@@ -93,10 +90,9 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     auto al = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
     const uint64_t off_u = 0;
     const uint64_t off_es = al(off_u + (uint64_t)ns * ns * 8);
-    const uint64_t off_mint = al(off_es + cols_padded * 8);
-    const uint64_t off_mint32 = al(off_mint + (uint64_t)A * cols_padded * 8);
-    const uint64_t off_ep = al(off_mint32 + (uint64_t)A * cols_padded * 4);
-    const uint64_t off_epmin = al(off_ep + (1ull << A) * 8);
+    const uint64_t off_mint = al(off_es + cols_padded * 4);
+    const uint64_t off_ep = al(off_mint + (uint64_t)A * cols_padded * 4);
+    const uint64_t off_epmin = al(off_ep + (1ull << A) * 4);
     const uint64_t groups = A > kRegBits + 2 ? 1ull << (A - kRegBits - 2) : 1ull;
     const uint64_t off_epmin4 = al(off_epmin + ((1ull << (A - kRegBits)) + 2) * 4);
     const uint64_t off_part = al(off_epmin4 + (groups + 1) * 4);
@@ -115,25 +111,23 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     }
     char *base = static_cast<char *>(call.ws);
     double *dU = reinterpret_cast<double *>(base + off_u);
-    double *des = reinterpret_cast<double *>(base + off_es);
-    double *dmint = reinterpret_cast<double *>(base + off_mint);
-    float *dmint32 = reinterpret_cast<float *>(base + off_mint32);
-    double *dep = reinterpret_cast<double *>(base + off_ep);
-    float *depmin = reinterpret_cast<float *>(base + off_epmin);
-    float *depmin4 = reinterpret_cast<float *>(base + off_epmin4);
+    int32_t *des = reinterpret_cast<int32_t *>(base + off_es);
+    int32_t *dmint = reinterpret_cast<int32_t *>(base + off_mint);
+    int32_t *dep = reinterpret_cast<int32_t *>(base + off_ep);
+    int32_t *depmin = reinterpret_cast<int32_t *>(base + off_epmin);
+    int32_t *depmin4 = reinterpret_cast<int32_t *>(base + off_epmin4);
     PartialF64 *dpart = reinterpret_cast<PartialF64 *>(base + off_part);
     CtrlF64 *dctrl = reinterpret_cast<CtrlF64 *>(base + off_ctrl);
     if (!call.create_events())
         return QUBO_EDEVICE;
 
-    // A state passes the filter when its fp32 energy is within delta of the
-    // best binary64 energy so far; delta = 2048 * 2^-24 S bounds every fp32
-    // rounding of the walk, the compare and the gates (at most 1060 * 2^-24 S)
-    // 1.93 times over.
-    const double delta = std::ldexp(S, -13);
-    float delta32 = (float)delta;
-    if ((double)delta32 < delta)
-        delta32 = std::nextafter(delta32, INFINITY);
+    // A state is re-evaluated when its rounded walk value W is at most
+    // floor(s T) + M for the bound T of the minimum: |W - s E| is at most
+    // (A + 2) / 2 for the rounded terms plus under 2^-20 of binary64 rounding,
+    // below M - 1 = A / 2 + 2.  The filter's cap 2^(kQuantBits + 2) lies above
+    // every W.
+    const int margin = A / 2 + 3;
+    const int filter_cap = 1 << (kQuantBits + 2);
     // The first threshold: E(0) = 0 when state 0 is searched, else above every energy.
     // (for the k-lowest search: always the bound, E(0) bounds only the minimum)
     double t0 = (lo == 0 && !lowest) ? 0.0 : 4.0 * S + 1.0;
@@ -143,7 +137,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess ||
         hipMemcpyAsync(dU, U.data(), U.size() * 8, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
-    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, des, dmint, dmint32, dep, depmin, depmin4, lo, hi,
+    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, scale, des, dmint, dep, depmin, depmin4, lo, hi,
                                 rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;
@@ -154,7 +148,6 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     SearchArgsF64 sa{};
     sa.es = des;
     sa.mint = dmint;
-    sa.mint32 = dmint32;
     sa.ep = dep;
     sa.epmin = depmin;
     sa.epmin4 = depmin4;
@@ -172,9 +165,11 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     sa.B = B;
     sa.n = n;
     sa.pad = ns - n;
-    sa.l_eff = l_eff;
+    sa.l_eff = plan.cache_bits < plan.seg_bits ? plan.cache_bits : plan.seg_bits;
     sa.seg_bits = plan.seg_bits;
-    sa.delta = delta32;
+    sa.scale = scale;
+    sa.margin = margin;
+    sa.cap = filter_cap;
     LowEntryF64 *dlists = reinterpret_cast<LowEntryF64 *>(base + off_lists);
     LowEntryF64 *dlow = reinterpret_cast<LowEntryF64 *>(base + off_low);
     int32_t *dlow_found = reinterpret_cast<int32_t *>(base + off_low_found);

@@ -1,0 +1,404 @@
+// The Gray walk of the QUBO search on CDNA4 (gfx950), shared by the integer
+// search and the search of a real-valued matrix (whose walk runs on rounded,
+// scaled integer tables): the helpers of one unrolled 32-step body and the loop
+// over work units with its bound gates (Maltsev, Remnev, Kapranov and
+// Krivtsova, "Terastate-per-second QUBO Brute-Force on a Single GPU", sec. III.B,
+// eq. 9 and Algorithm 2; sec. III.C for the units).  What happens to a body
+// whose bound reaches the threshold is up to the caller's mode.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+namespace qubo {
+
+constexpr int kU = 5;        // Gray bits with rows in VGPRs
+constexpr int kBody = 1 << kU;
+constexpr int kWaves = 4;    // waves per workgroup
+
+__device__ __forceinline__ uint64_t gray(uint64_t i) { return i ^ (i >> 1); }
+
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+
+// Marks a value that is equal in every lane as wave-uniform (kept in SGPRs).
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int R>
+__device__ __forceinline__ int row_min(const int (&E)[R]);
+
+// Min of 8 values: 3 x v_min3_i32 + 1 x v_min_i32.
+template <>
+__device__ __forceinline__ int row_min<8>(const int (&E)[8])
+{
+    const int a = imin(imin(E[0], E[1]), E[2]);
+    const int b = imin(imin(E[3], E[4]), E[5]);
+    const int c = imin(E[6], E[7]);
+    return imin(imin(a, b), c);
+}
+
+// Min of 16 values as a tree of 3-input mins (7 x v_min3_i32 + 1 x v_min_i32).
+template <>
+__device__ __forceinline__ int row_min<16>(const int (&E)[16])
+{
+    const int a = imin(imin(E[0], E[1]), E[2]);
+    const int b = imin(imin(E[3], E[4]), E[5]);
+    const int c = imin(imin(E[6], E[7]), E[8]);
+    const int d = imin(imin(E[9], E[10]), E[11]);
+    const int e = imin(imin(E[12], E[13]), E[14]);
+    const int f = imin(imin(a, b), c);
+    const int h = imin(imin(d, e), E[15]);
+    return imin(f, h);
+}
+
+template <int R>
+__device__ __forceinline__ void add_row(int (&E)[R], const int (&M)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        E[r] += M[r];
+}
+
+template <int R>
+__device__ __forceinline__ void sub_row(int (&E)[R], const int (&M)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        E[r] -= M[r];
+}
+
+// Keeps each column's energy of the current state in a VGPR: the compiler may
+// not fold a run of row updates into its net effect, so every state of the walk
+// is materialised by its own add (the O(1)-per-state evaluation of eq. 9).
+template <int R>
+__device__ __forceinline__ void materialise(int (&E)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        asm volatile("" : "+v"(E[r]));
+}
+
+// One unrolled body of 32 Gray steps with only the row updates (eq. 9): every
+// flip has a compile-time row and sign except the flip of bit 4, whose sign
+// alternates between bodies.
+template <int R>
+__device__ __forceinline__ void adds_body(int (&E)[R], const int (&Mr)[kU][R], bool top_plus)
+{
+#pragma unroll
+    for (int m = 0; m + 1 < kBody; ++m) {
+        const int t = __builtin_ctz((unsigned)(m + 1));
+        if (t < kU - 1) {
+            if ((((m + 1) >> (t + 1)) & 1) == 0)
+                add_row(E, Mr[t]);
+            else
+                sub_row(E, Mr[t]);
+        } else {
+            if (top_plus)
+                add_row(E, Mr[kU - 1]);
+            else
+                sub_row(E, Mr[kU - 1]);
+        }
+        materialise(E);
+    }
+}
+
+// The same body with the per-step test of Algorithm 2: after each state, the
+// lane's minimum over its 16 columns (a v_min3 tree) is compared with the
+// threshold T - E_p(g(j)).  Returns the OR over the body of the wave's hit masks.
+template <int R>
+__device__ __forceinline__ uint64_t checked_body(int (&E)[R], const int (&Mr)[kU][R],
+                                                 bool top_plus, int T,
+                                                 const int32_t *__restrict__ epb)
+{
+    uint64_t acc = 0;
+#pragma unroll
+    for (int m = 0; m < kBody; ++m) {
+        const int th = T - epb[m];
+        const int cm = row_min<R>(E);
+        acc |= __builtin_amdgcn_ballot_w64(cm <= th);
+        if (m + 1 < kBody) {
+            const int t = __builtin_ctz((unsigned)(m + 1));
+            if (t < kU - 1) {
+                if ((((m + 1) >> (t + 1)) & 1) == 0)
+                    add_row(E, Mr[t]);
+                else
+                    sub_row(E, Mr[t]);
+            } else {
+                if (top_plus)
+                    add_row(E, Mr[kU - 1]);
+                else
+                    sub_row(E, Mr[kU - 1]);
+            }
+        }
+    }
+    return acc;
+}
+
+
+// The loop over work units of one workgroup (a persistent grid: items come
+// from a global counter; an item is one column group and four consecutive
+// segments of the Gray walk, one per wave).  Per unit: E_sd at the segment's
+// first prefix (eq. 8), the rows of the five lowest Gray bits in registers,
+// the lane bounds of the gates, then the bodies of 32 Gray steps.
+//
+// Gated = true: before a body, a lower bound on every energy the body will
+// produce decides whether the per-step minimum is needed at all.  The body
+// visits all 32 patterns y of the 5 low Gray bits with the higher prefix bits
+// fixed; from the body's first state (low pattern s<<4, s = bit 5 of the step
+// index) a column's suffix-dependent energy can fall by at most
+//   beta0(c) - s M_4(c),   beta0(c) = sum_{t<5} min(0, M_t(c)),
+// and the prefix energy of any step is at least epmin[body].  A lane bounds all
+// its columns at once: min_c E(c) + min_c (beta0(c) - s M_4(c)), the second term
+// fixed per work unit for s = 0 and s = 1.  If no lane's bound reaches
+// T - epmin, no state of the body can reach the threshold T, and the body runs
+// the row updates only; otherwise it is walked exactly.  Every state still
+// costs its one add.  Gated = false (strict): every body runs the per-step test
+// of Algorithm 2 and is walked exactly where it hits.
+//
+// The mode provides
+//   int refresh(int T): T lowered to the threshold shared between waves;
+//   exact(E, Mr, base, top_plus, T, colbase, from_end): the exact walk of the
+//     body whose first Gray step is base (E holds its first state, or its last
+//     with from_end), leaving E at the body's last state and T lowered.
+// T only falls, so a body that a group or pair bound cleared stays cleared.
+// item_sh: one __shared__ word of the calling kernel; lds_rows: its dynamic LDS
+// ([l_eff - kU][64 R] rows of Gray bits kU .. l_eff - 1).
+template <int R, bool Gated, class Args, class Ctl, class Mode>
+__device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl,
+                                           const int32_t *__restrict__ es,
+                                           const int32_t *__restrict__ mint,
+                                           const int32_t *__restrict__ ep,
+                                           const int32_t *__restrict__ epmin, int32_t *lds_rows,
+                                           unsigned long long *item_sh, Mode &mode, int &T,
+                                           uint32_t &bodies, uint32_t &checked, uint32_t &slow_bodies)
+{
+    constexpr int kGroup = 64 * R;  // columns of a wave (and of a workgroup)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // This lane's column in the LDS rows, biased so that bit t's row is
+    // lds_lane + t * kGroup (one add per outer flip).
+    const int32_t *lds_lane = lds_rows - kU * kGroup + lane;
+    const int A = a.A;
+    const uint64_t cp = a.cols_padded;
+    long long cur_g = -1;
+
+    for (;;) {
+        if (threadIdx.x == 0)
+            *item_sh = atomicAdd(&ctrl->counter, 1ull);
+        __syncthreads();
+        const uint64_t item = uniform64(*item_sh);
+        __syncthreads();
+        if (item >= a.items)
+            break;
+        const uint64_t g = item / a.seg_blocks;
+        const uint64_t sb = item - g * a.seg_blocks;
+        if ((long long)g != cur_g) {
+            const int rows = a.l_eff - kU;
+            for (int k = threadIdx.x; k < rows * kGroup; k += blockDim.x) {
+                const int t = kU + k / kGroup;
+                const int col = k % kGroup;
+                lds_rows[k] = mint[(uint64_t)(A - 1 - t) * cp + g * kGroup + col];
+            }
+            __syncthreads();
+            cur_g = (long long)g;
+        }
+        const uint64_t seg = a.seg_first + sb * kWaves + (uint64_t)wave;
+        if (seg >= a.seg_first + a.segs)
+            continue;
+        uint64_t j_begin = seg << a.seg_bits;
+        uint64_t j_end = (seg + 1) << a.seg_bits;
+        j_begin = j_begin > a.gray_lo ? j_begin : a.gray_lo;
+        j_end = j_end < a.gray_hi ? j_end : a.gray_hi;
+        if (j_begin >= j_end)
+            continue;
+
+        const uint64_t col0 = g * kGroup + (uint64_t)lane;  // column of register r is col0 + 64 r
+
+        // E_sd at the first prefix of the segment: E_s + sum of the rows of its set bits (eq. 8).
+        int E[R];
+        {
+            const int32_t *src = es + col0;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                E[r] = src[r * 64];
+            uint64_t bits = gray(j_begin);
+            while (bits) {
+                const int t = __builtin_ctzll(bits);
+                bits &= bits - 1;
+                const int32_t *row = mint + (uint64_t)(A - 1 - t) * cp + col0;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    E[r] += row[r * 64];
+            }
+        }
+        int Mr[kU][R];
+#pragma unroll
+        for (int t = 0; t < kU; ++t) {
+            const int32_t *row = mint + (uint64_t)(A - 1 - t) * cp + col0;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                Mr[t][r] = row[r * 64];
+        }
+        // Lane bounds of the fall within a body, for s = 0 and s = 1; within an
+        // aligned pair of bodies (64 steps, Gray bits 0..5), for bit 5 = 0 and 1
+        // at the pair's start; and within an aligned group of four bodies (128
+        // steps, Gray bits 0..6: bits 0..5 start at 0), for bit 6 = 0 and 1 at
+        // the group's start.  The rows of bits 5 and 6 are read here only.
+        int beta_s0 = 0, beta_s1 = 0, beta_p0 = 0, beta_p1 = 0, beta_q0 = 0, beta_q1 = 0;
+        if (Gated) {
+            beta_s0 = INT_MAX;
+            beta_s1 = INT_MAX;
+            beta_p0 = INT_MAX;
+            beta_p1 = INT_MAX;
+            beta_q0 = INT_MAX;
+            beta_q1 = INT_MAX;
+            // (a bit that A does not have reads row 0, in bounds, and is ignored)
+            const int32_t *row5 = mint + (uint64_t)(A > kU ? A - 1 - kU : 0) * cp + col0;
+            const int32_t *row6 = mint + (uint64_t)(A > kU + 1 ? A - 2 - kU : 0) * cp + col0;
+            // Loaded either way (in bounds) and masked: no branch around the loads.
+            const int has5 = -(int)(A > kU), has6 = -(int)(A > kU + 1);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                int b = 0;
+#pragma unroll
+                for (int t = 0; t < kU; ++t)
+                    b += Mr[t][r] < 0 ? Mr[t][r] : 0;
+                beta_s0 = imin(beta_s0, b);
+                beta_s1 = imin(beta_s1, b - Mr[kU - 1][r]);
+                const int m5 = row5[r * 64] & has5;
+                beta_p0 = imin(beta_p0, b + (m5 < 0 ? m5 : 0));
+                beta_p1 = imin(beta_p1, b - (m5 > 0 ? m5 : 0));
+                const int m6 = row6[r * 64] & has6;
+                const int b5 = b + (m5 < 0 ? m5 : 0);
+                beta_q0 = imin(beta_q0, b5 + (m6 < 0 ? m6 : 0));
+                beta_q1 = imin(beta_q1, b5 - (m6 > 0 ? m6 : 0));
+                // One column at a time: with the sixteen row values loaded up
+                // front and the eight columns summed side by side, this set-up
+                // set the kernel's register count (a wave per SIMD less).
+                asm volatile(""
+                             : "+v"(beta_s0), "+v"(beta_s1), "+v"(beta_p0), "+v"(beta_p1), "+v"(beta_q0),
+                               "+v"(beta_q1)
+                             :
+                             : "memory");
+            }
+        }
+        T = mode.refresh(T);
+
+        // The body loop counts with 32-bit scalars (the SALU has no 64-bit
+        // less-than): a segment holds at most 2^13 bodies.
+        // Bodies are counted by their index b = j >> 5, a 32-bit value (A <= 32),
+        // so that the per-body bookkeeping is 32-bit scalar arithmetic; the
+        // 64-bit Gray step is formed only where a walk needs it.
+        const uint32_t nbodies = (uint32_t)((j_end - j_begin) >> kU);
+        const uint32_t b0 = (uint32_t)(j_begin >> kU);
+        // The group gate's prefix bound comes from the per-group table, read one
+        // group ahead (the table has one padding entry past the last group); the
+        // body minima are read only where a pair or body gate needs them.
+        int q_next = Gated && A > kU + 1 ? a.epmin4[(b0 + 3) >> 2] : 0;
+        uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
+        for (uint32_t bi = 0; bi < nbodies; ++bi) {
+            const uint32_t b = b0 + bi;
+            const bool last = bi + 1 == nbodies;
+            const bool top_plus = (b & 1u) == 0;
+            bool check = true;
+            if (Gated) {
+                // Padding columns hold INT_MAX with zero rows (beta 0), so a lane
+                // of padding columns only has the bound INT_MAX.
+                if (covered != 0) {
+                    // T has not risen since the bound that cleared this body was checked.
+                    check = false;
+                    --covered;
+                } else {
+                    const int emin = row_min<R>(E);
+                    if ((b & 3u) == 0 && bi + 3 < nbodies && A > kU + 1) {
+                        // The first of four aligned bodies: their 128 states of Gray
+                        // bits 0..6 fall by at most beta_q(bit 6 at the group's start).
+                        const int q = q_next;
+                        q_next = a.epmin4[(b >> 2) + 1];
+                        const int thq = T - q;
+                        const int bq = emin + (((b >> 2) & 1u) ? beta_q1 : beta_q0);
+                        if (__builtin_amdgcn_ballot_w64(bq <= thq) == 0)
+                            covered = 3;
+                    }
+                    if (covered != 0) {
+                        check = false;
+                    } else {
+                        const int epm_cur = epmin[b];
+                        if (top_plus && !last && A > kU) {
+                            // An even body and its partner: the 64 states of Gray bits
+                            // 0..5 fall by at most beta_p(bit 5 at the pair's start).
+                            const int thp = T - imin(epm_cur, epmin[b + 1]);
+                            const int bp = emin + (((b >> 1) & 1u) ? beta_p1 : beta_p0);
+                            if (__builtin_amdgcn_ballot_w64(bp <= thp) == 0)
+                                covered = 1;
+                        }
+                        if (covered != 0) {
+                            check = false;
+                        } else {
+                            const int thb = T - epm_cur;
+                            const int bound = emin + (top_plus ? beta_s0 : beta_s1);
+                            check = __builtin_amdgcn_ballot_w64(bound <= thb) != 0;
+                        }
+                    }
+                }
+            }
+            ++bodies;
+            if (!check) {
+                adds_body(E, Mr, top_plus);
+            } else {
+                ++checked;
+                // Strict mode walks exactly only after the per-step test hit; the
+                // gated kernel has already decided that the bound was reached.
+                const uint64_t base = (uint64_t)b << kU;
+                bool walk = Gated;
+                if (!Gated)
+                    walk = checked_body(E, Mr, top_plus, T, ep + base) != 0;
+                if (walk) {
+                    ++slow_bodies;
+                    mode.exact(E, Mr, base, top_plus, T, g * kGroup, !Gated);
+                }
+            }
+            if (!last) {
+                // Flip of Gray bit t = 5 + ctz(b + 1) into the next body (its sign is
+                // bit t + 1 of the next body's first step): its row comes from LDS or
+                // global memory.
+                const int t = kU + __builtin_ctz(b + 1);
+                const bool plus = (((b + 1) >> (t - kU + 1)) & 1u) == 0;
+                int row[R];
+                if (t < a.l_eff) {
+                    // Bit 5 (every other body) reads at constant offsets: the general
+                    // address costs a VALU instruction per body.  The asm marker keeps
+                    // the compiler from merging the branches into that address again.
+                    if (t == kU) {
+                        asm volatile("; exit flip of bit 5");
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            row[r] = lds_lane[kU * kGroup + r * 64];
+                    } else {
+                        const int32_t *src = lds_lane + t * kGroup;  // row of bit t, this lane
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            row[r] = src[r * 64];
+                    }
+                } else {
+                    const int32_t *src = mint + (uint64_t)(A - 1 - t) * cp + col0;
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        row[r] = src[r * 64];
+                }
+                if (plus)
+                    add_row(E, row);
+                else
+                    sub_row(E, row);
+            }
+        }
+    }
+}
+
+}  // namespace qubo

@@ -97,8 +97,8 @@ def test_check_q_guard():
 
 def test_check_q_f64_guard():
     """The binary64 guard: finite entries and S = sum |Q_ij| either 0 or in
-    [2^-100, 2^100].  The floor keeps the re-evaluation margin 2^-13 S above
-    the absolute error of fp32 arithmetic near its underflow threshold."""
+    [2^-100, 2^100].  The range keeps the walk's scale factor 2^(17 - e)
+    (S < 2^e) and the binary64 sums well inside binary64's normal range."""
     q.check_q_f64(np.zeros((4, 4)))
     q.check_q_f64(-np.zeros((4, 4)))  # negative zeros: S = 0
     for bad in (np.nan, np.inf, -np.inf):

@@ -100,12 +100,12 @@ def test_every_split_real(q, n):
 
 @pytest.mark.parametrize("case", ["normal", "subnormal"])
 def test_near_the_floor(q, case):
-    """S = sum |Q_ij| just above the guard's floor 2^-100.  'normal': every entry
-    in fp32's normal range (about 2^-107), so the re-evaluation margin 2^-13 S
-    is tight around the minimum.  'subnormal': every entry but one in fp32's
-    subnormal range (below 2^-126), where fp32 keeps only a few bits and errs by
-    an absolute amount; one diagonal entry lifts S above the floor.  The
-    minimum, its lowest index, the count and the 16 lowest states equal the
+    """S = sum |Q_ij| just above the guard's floor 2^-100, so the walk's scale
+    factor is 2^117.  'normal': entries of one magnitude (about 2^-107).
+    'subnormal': every entry but one 36 binary orders below S (2^-136, below
+    fp32's normal range), so the rounded tables hold them as 0 and only the
+    re-evaluation ranks the states; one diagonal entry lifts S above the floor.
+    The minimum, its lowest index, the count and the 16 lowest states equal the
     oracle's binary64 definition."""
     n = 14
     rng = np.random.default_rng(8701 if case == "normal" else 8702)
@@ -120,6 +120,42 @@ def test_near_the_floor(q, case):
     announce("f64 near the floor", case)
     assert q.search_f64(Qd).triple() == oracle.search_direct_f64(Q).triple()
     announce("f64 near the floor lowest", case)
+    assert q.lowest(Qd, 16) == oracle.lowest_f64(Q, 16)
+
+
+def test_ties_below_the_quantum(q):
+    """An integer-valued matrix (many exact ties) with diagonal perturbations
+    of about 2^-30: the states the perturbations separate are 2^21 times closer
+    than one unit of the rounded walk (S / 2^17), so the walk sees them as ties
+    and only the re-evaluation from the definition ranks them.  Minimum, lowest
+    minimiser, count and the 32 lowest states against the oracle."""
+    n = 16
+    Qi = np.array(qi.general_uniform(n, 8901, -3, 3), dtype=np.float64)
+    rng = np.random.default_rng(8902)
+    Q = Qi + np.diag(rng.uniform(-1.0, 1.0, size=n) * 2.0 ** -30)
+    Qd = dev_f(Q)
+    announce("f64 ties below the quantum")
+    assert q.search_f64(Qd).triple() == oracle.search_direct_f64(Q).triple()
+    announce("f64 ties below the quantum, lowest")
+    assert q.lowest(Qd, 32) == oracle.lowest_f64(Q, 32)
+    # integer-valued with exact ties: the count runs over the tied states
+    announce("f64 integer-valued ties, small entries")
+    assert q.search_f64(dev_f(Qi)).triple() == oracle.search_direct_f64(Qi).triple()
+
+
+def test_entries_below_the_quantum(q):
+    """One large diagonal entry and the rest about 10^12 times smaller: the
+    rounded tables hold the small entries as 0, so every state without the
+    large variable has the same walked value and is re-evaluated (2^11 of
+    them); the result still equals the definition's."""
+    n = 12
+    rng = np.random.default_rng(8903)
+    Q = rng.uniform(-1.0, 1.0, size=(n, n)) * 1e-9
+    Q[0, 0] = 1e3
+    Qd = dev_f(Q)
+    announce("f64 entries below the quantum")
+    assert q.search_f64(Qd).triple() == oracle.search_direct_f64(Q).triple()
+    announce("f64 entries below the quantum, lowest")
     assert q.lowest(Qd, 16) == oracle.lowest_f64(Q, 16)
 
 
@@ -152,9 +188,9 @@ RAGGED_F64 = [(32, 96), (64, 320), (96, 160), (32, 64), (96, 96 + 32 * 9), (160,
 @pytest.mark.parametrize("lo,hi", RAGGED_F64)
 def test_ragged_slices_real(q, lo, hi):
     """Slices that start on the second, third or fourth 32-step body of an
-    aligned group of four (the binary64 anchor then starts mid-group) or end
-    inside one, with the rows of the anchor's moves in LDS or in global memory;
-    the oracle evaluates every state of the slice from the binary64 definition.
+    aligned group of four (the group gate then waits for the next group) or end
+    inside one, with the exit flips' rows in LDS or in global memory; the
+    oracle evaluates every state of the slice from the binary64 definition.
     One real matrix (no ties) and one integer-valued (exact sums, many ties)."""
     n, A = 16, 11
     B = n - A

@@ -81,8 +81,8 @@ def test_every_split(q, n):
 
 @pytest.mark.parametrize("lo,hi", [(32, 96), (64, 320), (160, 1024 + 96), (0, 2048)])
 def test_ragged_slices(q, lo, hi):
-    """Slices that start mid-group of the binary64 anchor, against the sort of
-    the slice's definition energies."""
+    """Slices that start or end inside an aligned group of four 32-step bodies,
+    against the sort of the slice's definition energies."""
     n, A = 16, 11
     B = n - A
     js = np.arange(lo, hi, dtype=np.uint64)
