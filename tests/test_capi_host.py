@@ -116,7 +116,7 @@ def test_check_q_f64_guard():
     with pytest.raises(q.QuboError) as e:
         q.check_q_f64(Q)
     assert e.value.code == q.QUBO_ERANGE
-    # one entry deep in fp32's subnormal range next to one that lifts S above the floor
+    # entries 2^-40 below the floor next to one that lifts S above it
     Q = np.full((3, 3), 2.0 ** -140)
     Q[2, 2] = 2.0 ** -99
     q.check_q_f64(Q)

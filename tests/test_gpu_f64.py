@@ -72,8 +72,8 @@ def test_integer_valued_ties(q, n, seed, lo, hi):
 
 
 def test_mixed_magnitudes(q):
-    """Entries spanning 16 decades: fp32 alone cannot rank the states, the
-    re-evaluation against the definition must."""
+    """Entries spanning 16 decades: the rounded tables (17 significant bits of
+    S) cannot rank the states, the re-evaluation against the definition must."""
     rng = np.random.default_rng(8201)
     n = 13
     Q = rng.uniform(-1.0, 1.0, size=(n, n)) * 10.0 ** rng.integers(-8, 8, size=(n, n))
