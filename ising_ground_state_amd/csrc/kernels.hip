@@ -13,7 +13,8 @@
 //   * sec. IV.B.1-3: the rows of M_int and the suffix-dependent vector stay in
 //     registers, the prefix energies are read in Gray order.
 //
-// CDNA4 mapping of the search kernel:
+// CDNA4 mapping of the search kernel (its loop over work units and bodies is in
+// walk.h, shared with the binary64 search; this file holds the integer mode):
 //   * a lane owns R = 8 or 16 suffix columns: c = g*64R + r*64 + lane, so the
 //     lanes of a wave read consecutive dwords for each r (coalesced loads,
 //     conflict-free LDS reads);
