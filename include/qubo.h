@@ -268,9 +268,12 @@ typedef struct {
  * integers once each; a state's walked value then lies within A/2 + 2 of
  * s E(x), and a state whose walked value comes within M = A/2 + 3 of s times
  * the best exact energy so far (about 2^-13 S) is re-evaluated from the
- * definition on the GPU, so the result is exactly the definition's.  Instances
- * with many states that close to the minimum (e.g. Q = 0) are correct but
- * slow: each such state costs an O(n^2) evaluation.  Blocking; same ownership
+ * definition on the GPU, so the result is exactly the definition's.  A dyadic
+ * Q (every entry an integer multiple of 2^-f with sum |2^f Q_ij| <= 2^30 - 1,
+ * integer-valued matrices included), whose definition sums are all exact, is
+ * searched as the int32 matrix 2^f Q by the integer search instead.  Other
+ * instances with many states that close to the minimum are correct but slow:
+ * each such state costs an O(n^2) evaluation.  Blocking; same ownership
  * and error behaviour as qubo_search_ex; qubo_last_timing reports the
  * re-evaluated states. */
 QUBO_API int qubo_search_f64(const double *Q, int n, int prefix_bits, int cache_bits,

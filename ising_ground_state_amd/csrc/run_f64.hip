@@ -3,11 +3,49 @@
 #include "host.h"
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
+#include <cstdlib>
 
 namespace qubo_host {
 
 static_assert(sizeof(qubo::LowEntryF64) == sizeof(qubo_state_f64), "list entry layout");
+
+// A dyadic matrix: every entry an integer multiple of 2^-f with
+// sum |2^f Q_ij| <= 2^30 - 1.  Then every partial sum of the definition is a
+// multiple of 2^-f below 2^(30 - f) in magnitude, i.e. at most 30 significant
+// bits, so binary64 adds it exactly, in any order: E(x) = E_int(x) / 2^f with
+// E_int the energy of the int32 matrix 2^f Q, whose search is exact, ties and
+// counts included.  Writes that matrix and f; false when Q is not such a matrix.
+static bool dyadic_int32(const std::vector<double> &Qh, std::vector<int32_t> &Qi, int *f_out)
+{
+    // f = -(the lowest exponent of any entry's last set bit)
+    int f = INT_MIN;
+    for (double v : Qh) {
+        if (v == 0.0)
+            continue;
+        int ex = 0;
+        const double m = std::frexp(std::fabs(v), &ex);      // |v| = m 2^ex, m in [0.5, 1)
+        const uint64_t M = (uint64_t)std::ldexp(m, 53);       // 53-bit integer significand
+        const int lsb = ex - 53 + __builtin_ctzll(M);         // |v| = odd * 2^lsb
+        f = std::max(f, -lsb);
+    }
+    if (f == INT_MIN)
+        f = 0;  // the zero matrix
+    Qi.resize(Qh.size());
+    int64_t sum = 0;
+    for (size_t k = 0; k < Qh.size(); ++k) {
+        const double q = std::ldexp(Qh[k], f);  // exact: a power-of-two scale of an integer multiple
+        if (!(std::fabs(q) <= (double)qubo::kAbsSumLimit))
+            return false;
+        Qi[k] = (int32_t)q;
+        sum += std::llabs((long long)Qi[k]);
+        if (sum > qubo::kAbsSumLimit)
+            return false;
+    }
+    *f_out = f;
+    return true;
+}
 
 // have_cap: the search only has to find states with E <= cap (a real energy
 // found elsewhere); an empty result is then valid and *found says whether any
@@ -44,6 +82,59 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     rc = guard_f64(Qh, &S);
     if (rc != QUBO_OK)
         return rc;
+
+    // A dyadic matrix (integer-valued ones included) is searched as the int32
+    // matrix 2^f Q by the integer search, which is exact for it; energies come
+    // back divided by 2^f (exact: at least 2^-130 in magnitude when not 0).
+    {
+        std::vector<int32_t> Qi;
+        int f = 0;
+        if (dyadic_int32(Qh, Qi, &f)) {
+            std::vector<int32_t> Ui;
+            int64_t abs_sum = 0;
+            rc = fold_upper(Qi.data(), n, Ui, &abs_sum);
+            if (rc != QUBO_OK)
+                return rc;
+            Request irq;
+            irq.n = n;
+            irq.prefix_bits = rq.prefix_bits;
+            irq.cache_bits = rq.cache_bits;
+            irq.ranged = rq.ranged;
+            irq.gray_lo = rq.gray_lo;
+            irq.gray_hi = rq.gray_hi;
+            irq.stream = rq.stream;
+            irq.cols_per_lane = kColsPerLaneF64;
+            irq.lowest_k = rq.lowest_k;
+            // states with E <= cap are those with E_int <= floor(2^f cap)
+            int32_t icap = 0;
+            if (have_cap) {
+                const double c = std::floor(std::ldexp(cap, f));
+                icap = c > (double)abs_sum ? (int32_t)abs_sum : c < -(double)abs_sum ? (int32_t)-abs_sum - 1
+                                                                                       : (int32_t)c;
+            }
+            qubo_result ir{};
+            bool ifound = false;
+            qubo_timing t{};
+            std::vector<qubo_state> ilow;
+            rc = run_one(irq, dev, std::move(Ui), n, abs_sum, have_cap, icap, lowest ? nullptr : &ir, &ifound, &t,
+                         lowest ? &ilow : nullptr);
+            if (rc != QUBO_OK)
+                return rc;
+            last_timing() = t;
+            if (found)
+                *found = ifound;
+            if (lowest) {
+                low->clear();
+                for (const qubo_state &st : ilow)
+                    low->push_back(qubo_state_f64{std::ldexp((double)st.energy, -f), st.index});
+            } else if (ifound) {
+                out->min_energy = std::ldexp((double)ir.min_energy, -f);
+                out->argmin = ir.argmin;
+                out->count = ir.count;
+            }
+            return QUBO_OK;
+        }
+    }
     // Fold to the upper triangle in binary64 (the walk's tables only; states
     // are scored against Q itself) and pad small problems: a padding variable
     // gets the positive diagonal S (1 for the zero matrix) and no couplings, so

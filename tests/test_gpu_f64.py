@@ -159,6 +159,46 @@ def test_entries_below_the_quantum(q):
     assert q.lowest(Qd, 16) == oracle.lowest_f64(Q, 16)
 
 
+def test_dyadic_takes_the_integer_search(q):
+    """Entries in {-1/8, 0, 1/8} (exact ties, two minimisers): every partial sum
+    of the definition is exact, so the search runs as the integer search of 8 Q
+    (no state is re-evaluated) and gives the definition's minimum, count and
+    lowest states."""
+    n = 16
+    Q = np.array(qi.general_uniform(n, 8904, -1, 1), dtype=np.float64) / 8.0
+    Qd = dev_f(Q)
+    announce("f64 dyadic")
+    r = q.search_f64(Qd)
+    assert q.last_timing()["candidates"] == 0
+    assert r.triple() == oracle.search_direct_f64(Q).triple()
+    assert r.count > 1
+    announce("f64 dyadic lowest")
+    assert q.lowest(Qd, 32) == oracle.lowest_f64(Q, 32)
+    # the zero matrix: every one of the 2^36 states is a minimiser
+    announce("f64 zero n=36")
+    assert q.search_f64(dev_f(np.zeros((36, 36)))).triple() == (0.0, 0, 1 << 36)
+
+
+def test_exact_ties_on_the_rounded_walk(q):
+    """An integer-valued matrix with exact ties plus one variable whose
+    diagonal (1000 + pi) is not dyadic: the search takes the rounded walk, the
+    tied states pass the filter together, and the count of exact ties comes
+    from the re-evaluation."""
+    n = 15
+    Qi = np.array(qi.general_uniform(n, 8905, -1, 1), dtype=np.float64)
+    Q = np.zeros((n + 1, n + 1))
+    Q[1:, 1:] = Qi
+    Q[0, 0] = 1000.0 + np.pi
+    Qd = dev_f(Q)
+    announce("f64 exact ties, rounded walk")
+    r = q.search_f64(Qd)
+    assert q.last_timing()["candidates"] > 0
+    want = oracle.search_direct_f64(Q).triple()
+    assert r.triple() == want and want[2] > 1
+    announce("f64 exact ties, rounded walk, lowest")
+    assert q.lowest(Qd, 48) == oracle.lowest_f64(Q, 48)
+
+
 def test_zero_and_diagonal(q):
     announce("f64 zero")
     assert q.search_f64(dev_f(np.zeros((8, 8)))).triple() == (0.0, 0, 256)
