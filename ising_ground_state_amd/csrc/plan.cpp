@@ -6,12 +6,13 @@
 // the Gray walk over the prefix is cut into segments handed to waves (a split
 // over ranges of the prefix walk, in the spirit of III.C.1).  The paper tunes
 // A and B empirically for the register file of its GPU (sec. IV.B.1); here the
-// register budget is fixed by the kernel's compile-time shape (16 columns and 5
-// cached rows per lane) and the planner only sizes tables and work units.
+// register budget is fixed by the kernel's compile-time shape (8 or 16 columns
+// and 5 cached rows per lane) and the planner only sizes tables and work units.
 #include "plan.h"
 
 #include <algorithm>
 #include <cstdlib>
+#include <unordered_set>
 
 namespace qubo {
 
@@ -44,39 +45,68 @@ std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_searc
     return P;
 }
 
-int64_t descent_energy(const std::vector<int32_t> &U, int n)
+std::vector<int64_t> descent_energies(const std::vector<int32_t> &U, int n, int starts)
 {
     // F[v]: the change of E when variable v goes from 0 to 1 given the others
     // (U_vv plus the couplings to the set variables); flipping v moves E by F[v]
     // if x_v = 0 and by -F[v] if x_v = 1.
+    auto coupling = [&U, n](int a, int b) { return a < b ? U[(size_t)a * n + b] : U[(size_t)b * n + a]; };
+    std::unordered_set<uint64_t> seen;
+    std::vector<int64_t> es;
     std::vector<int64_t> F((size_t)n);
-    std::vector<int> x((size_t)n, 0);
-    for (int v = 0; v < n; ++v)
-        F[(size_t)v] = U[(size_t)v * n + v];
-    int64_t e = 0;
-    for (int step = 0; step < 4 * n + 4; ++step) {
-        int best = -1;
-        int64_t best_d = 0;
+    std::vector<int> x((size_t)n);
+    uint64_t sm = 0x51a7e5eedull;  // SplitMix64 state (Steele, Lea and Flood)
+    for (int st = 0; st < starts; ++st) {
+        uint64_t start = 0;
+        if (st > 0) {
+            uint64_t z = (sm += 0x9e3779b97f4a7c15ull);
+            z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+            z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+            start = z ^ (z >> 31);
+        }
+        int64_t e = 0;
+        for (int v = 0; v < n; ++v)
+            x[(size_t)v] = (int)((start >> v) & 1u);
         for (int v = 0; v < n; ++v) {
-            const int64_t d = x[(size_t)v] ? -F[(size_t)v] : F[(size_t)v];
-            if (d < best_d) {
-                best_d = d;
-                best = v;
+            int64_t f = U[(size_t)v * n + v];
+            for (int j = 0; j < n; ++j)
+                if (j != v && x[(size_t)j])
+                    f += coupling(v, j);
+            F[(size_t)v] = f;
+            if (x[(size_t)v])
+                for (int j = v; j < n; ++j)
+                    e += x[(size_t)j] ? U[(size_t)v * n + j] : 0;
+        }
+        for (int step = 0; step < 4 * n + 4; ++step) {
+            int best = -1;
+            int64_t best_d = 0;
+            for (int v = 0; v < n; ++v) {
+                const int64_t d = x[(size_t)v] ? -F[(size_t)v] : F[(size_t)v];
+                if (d < best_d) {
+                    best_d = d;
+                    best = v;
+                }
             }
+            if (best < 0)
+                break;  // a local minimum under single flips
+            const int64_t sg = x[(size_t)best] ? -1 : 1;
+            x[(size_t)best] ^= 1;
+            e += best_d;
+            for (int j = 0; j < n; ++j)
+                if (j != best)
+                    F[(size_t)j] += sg * coupling(j, best);
         }
-        if (best < 0)
-            break;  // a local minimum under single flips
-        const int64_t s = x[(size_t)best] ? -1 : 1;
-        x[(size_t)best] ^= 1;
-        e += best_d;
-        for (int j = 0; j < n; ++j) {
-            if (j == best)
-                continue;
-            const int32_t u = j < best ? U[(size_t)j * n + best] : U[(size_t)best * n + j];
-            F[(size_t)j] += s * u;
-        }
+        uint64_t key = 0;
+        for (int v = 0; v < n; ++v)
+            key |= (uint64_t)x[(size_t)v] << v;
+        if (seen.insert(key).second)
+            es.push_back(e);
+        for (int v = 0; v < n; ++v)  // the single-flip neighbours
+            if (seen.insert(key ^ (1ull << v)).second)
+                es.push_back(e + (x[(size_t)v] ? -F[(size_t)v] : F[(size_t)v]));
     }
-    return e;
+    std::sort(es.begin(), es.end());
+    return es;
 }
 
 static int ceil_log2(uint64_t v)

@@ -34,11 +34,16 @@ int fold_upper(const int32_t *Q, int n, std::vector<int32_t> &U, int64_t *abs_su
 // U_ii = +1 and no couplings, so they are 0 in every minimiser.
 std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_search);
 
-// Energy of the state that a steepest single-flip descent from state 0 reaches on
-// the folded matrix U (n x n upper triangle): a real state's energy, at most
-// E(0) = 0, used as the first threshold of a whole-space minimum search so that
-// the bound gates clear bodies from the start.  Exact in int64.
-int64_t descent_energy(const std::vector<int32_t> &U, int n);
+// Energies of distinct states of the folded matrix U (n x n upper triangle,
+// n <= 63), ascending: the states that steepest single-flip descents reach
+// from state 0 and from starts - 1 fixed pseudo-random states (SplitMix64, a
+// fixed seed), and their single-flip neighbours.  Exact in int64.  The first
+// is a real energy at most E(0) = 0 and the j-th bounds the j-th lowest energy
+// from above: first thresholds of a whole-space search, so that the bound gates
+// clear bodies from the start.  Only the thresholds depend on the starts,
+// never a search's result.
+std::vector<int64_t> descent_energies(const std::vector<int32_t> &U, int n, int starts);
+constexpr int kDescentStarts = 16;
 
 // Fills `out` for n variables on a device with `num_cus` compute units;
 // cols_per_lane is 8 or 16, or 0 for the default.  split_bits: -1 splits only

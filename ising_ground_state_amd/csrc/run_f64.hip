@@ -6,6 +6,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdlib>
+#include <unordered_set>
 
 namespace qubo_host {
 
@@ -45,6 +46,89 @@ static bool dyadic_int32(const std::vector<double> &Qh, std::vector<int32_t> &Qi
     }
     *f_out = f;
     return true;
+}
+
+// The definition's energy of one state (binary64, i ascending, j ascending over
+// the set variables; the same sums in the same order as the device).
+static double energy_def_host(const std::vector<double> &Qh, int n, const std::vector<char> &x)
+{
+    double e = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (!x[i])
+            continue;
+        for (int j = 0; j < n; ++j)
+            if (x[j])
+                e += Qh[(size_t)i * n + j];
+    }
+    return e;
+}
+
+// Energies of distinct real states, ascending: the states that steepest
+// single-flip descents reach (fields in binary64; at most 4n flips each) from
+// state 0 and from kDescentStarts - 1 fixed pseudo-random states (SplitMix64,
+// a fixed seed: only the first threshold depends on them, never the result),
+// and their single-flip neighbours, each scored by the definition.  The j-th
+// value bounds the j-th lowest energy of the whole space from above.
+static constexpr int kDescentStarts = 16;
+
+static std::vector<double> descent_energies(const std::vector<double> &Qh, int n)
+{
+    std::unordered_set<uint64_t> seen;
+    std::vector<double> es;
+    uint64_t sm = 0x51a7e5eedull;  // SplitMix64 state
+    auto next = [&sm]() {
+        uint64_t z = (sm += 0x9e3779b97f4a7c15ull);
+        z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+        z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+        return z ^ (z >> 31);
+    };
+    std::vector<char> x(n);
+    std::vector<double> F(n);  // F_v = Q_vv + sum_{j != v, x_j = 1} (Q_vj + Q_jv): the change of setting v
+    for (int s = 0; s < kDescentStarts; ++s) {
+        const uint64_t start = s == 0 ? 0 : next();
+        for (int v = 0; v < n; ++v)
+            x[v] = (char)((start >> v) & 1u);
+        for (int v = 0; v < n; ++v) {
+            double f = Qh[(size_t)v * n + v];
+            for (int j = 0; j < n; ++j)
+                if (j != v && x[j])
+                    f += Qh[(size_t)v * n + j] + Qh[(size_t)j * n + v];
+            F[v] = f;
+        }
+        for (int it = 0; it < 4 * n; ++it) {
+            int best = -1;
+            double gain = 0.0;
+            for (int v = 0; v < n; ++v) {
+                const double d = x[v] ? -F[v] : F[v];
+                if (d < gain) {
+                    gain = d;
+                    best = v;
+                }
+            }
+            if (best < 0)
+                break;
+            const double sgn = x[best] ? -1.0 : 1.0;
+            x[best] ^= 1;
+            for (int j = 0; j < n; ++j)
+                if (j != best)
+                    F[j] += sgn * (Qh[(size_t)j * n + best] + Qh[(size_t)best * n + j]);
+        }
+        uint64_t key = 0;
+        for (int v = 0; v < n; ++v)
+            key |= (uint64_t)x[v] << v;
+        for (int v = -1; v < n; ++v) {  // y, then its neighbours
+            const uint64_t k = v < 0 ? key : key ^ (1ull << v);
+            if (!seen.insert(k).second)
+                continue;
+            if (v >= 0)
+                x[v] ^= 1;
+            es.push_back(energy_def_host(Qh, n, x));
+            if (v >= 0)
+                x[v] ^= 1;
+        }
+    }
+    std::sort(es.begin(), es.end());
+    return es;
 }
 
 // have_cap: the search only has to find states with E <= cap (a real energy
@@ -219,9 +303,23 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     // every W.
     const int margin = A / 2 + 3;
     const int filter_cap = 1 << (kQuantBits + 2);
-    // The first threshold: E(0) = 0 when state 0 is searched, else above every energy.
-    // (for the k-lowest search: always the bound, E(0) bounds only the minimum)
+    // The first threshold: E(0) = 0 when state 0 is searched, else above every
+    // energy (for the k-lowest search: always that bound, E(0) bounds only the
+    // minimum).  A whole-space search starts from real energies instead: the
+    // lowest of the descents' states for the minimum, their k-th lowest for
+    // the k lowest (each wave's own list bounds the k-th lowest energy only
+    // loosely: it holds the lowest states of its share of the space), raised
+    // by 2^-40 S against any difference between the host's sums and the
+    // device's.
     double t0 = (lo == 0 && !lowest) ? 0.0 : 4.0 * S + 1.0;
+    if (!rq.ranged && n >= kMinSearchVars) {
+        const std::vector<double> es = descent_energies(Qh, n);
+        const size_t j = lowest ? (size_t)rq.lowest_k - 1 : 0;
+        if (j < es.size()) {
+            const double t = es[j] + std::ldexp(S, -40);
+            t0 = t < t0 ? t : t0;
+        }
+    }
     if (have_cap && cap < t0)
         t0 = cap;
 

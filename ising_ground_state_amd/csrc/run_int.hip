@@ -135,16 +135,20 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
 
     // The first threshold must be a real energy of the searched set or an upper
     // bound of all of them: E(0) = 0 when state 0 is searched, else sum |Q_ij|
-    // (always sum |Q_ij| for the spectrum, whose threshold bounds the k-th
-    // energy).  A whole-space minimum search starts from the energy of a
-    // single-flip descent from state 0 instead (a real state, at most 0), so
-    // that its gates clear bodies from the first one.  A caller's cap (an
-    // energy found elsewhere) may only lower it; it is never below -sum |U_ij|
-    // here, so every threshold stays within +-2 sum |U_ij|.
+    // (for the spectrum, whose threshold bounds the k-th energy, sum |Q_ij|).
+    // A whole-space search starts from the energies of single-flip descents
+    // instead (real states; the lowest for the minimum, the k-th lowest for
+    // the spectrum), so that its gates clear bodies from the first one.  With
+    // padding variables the spectrum keeps sum |Q_ij|: a neighbour that sets
+    // one is not a state of the problem.  A caller's cap (an energy found
+    // elsewhere) may only lower it; it is never below -sum |U_ij| here, so
+    // every threshold stays within +-2 sum |U_ij|.
     int32_t t0 = (lo == 0 && !lowest) ? 0 : (int32_t)abs_sum;
-    if (lo == 0 && hi == (1ull << A) && !lowest) {
-        const int64_t ed = descent_energy(U, ns);
-        t0 = ed < t0 ? (int32_t)ed : t0;
+    if (lo == 0 && hi == (1ull << A) && (!lowest || ns == n)) {
+        const std::vector<int64_t> es = descent_energies(U, ns, kDescentStarts);
+        const size_t j = lowest ? (size_t)k_low - 1 : 0;
+        if (j < es.size() && es[j] < t0)
+            t0 = (int32_t)es[j];
     }
     if (have_t0 && t0_cap < t0)
         t0 = t0_cap;
