@@ -117,6 +117,18 @@ QUBO_API int qubo_abs_sum(const int32_t *Q_host, int n, int64_t *abs_sum);
  * Returns QUBO_OK, QUBO_EINVAL (null Q, n outside [1, 63]) or QUBO_ERANGE. */
 QUBO_API int qubo_check_q_f64(const double *Q_host, int n);
 
+/* Host only; touches no device.  The exact int32 form of a dyadic binary64
+ * matrix, which the binary64 searches hand to the integer search (sec. VI.B:
+ * floating-point matrices).  Q_host: n x n binary64, row-major.  When every
+ * entry is an integer multiple of 2^-f and sum |2^f Q_ij| <= 2^30 - 1 (f the
+ * smallest such exponent, possibly negative; f = 0 for the zero matrix),
+ * writes the n x n int32 matrix 2^f Q to Q_int (host, n*n entries) and f to
+ * *f and returns QUBO_OK: every partial sum of the binary64 definition is then
+ * exact, so E(x) = E_int(x) / 2^f for every state.  Returns QUBO_ERANGE when Q
+ * has no such form (a non-finite entry included; Q_int and *f are then left
+ * unspecified), QUBO_EINVAL for null pointers or n outside [1, 63]. */
+QUBO_API int qubo_f64_as_int32(const double *Q_host, int n, int32_t *Q_int, int *f);
+
 /* Exhaustive search over all 2^n states (sec. III.B Algorithm 2 with the
  * splits of sec. III.C), on the HIP stream `stream` (a hipStream_t; NULL is the
  * null stream) of the current device.

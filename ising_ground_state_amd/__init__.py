@@ -126,7 +126,7 @@ class Result:
 
 _lib = None
 
-EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_abs_sum", "qubo_check_q_f64", "qubo_search", "qubo_search_noalloc", "qubo_search_range", "qubo_search_ex",
+EXPORTS = ("qubo_make_plan", "qubo_check_q", "qubo_abs_sum", "qubo_check_q_f64", "qubo_f64_as_int32", "qubo_search", "qubo_search_noalloc", "qubo_search_range", "qubo_search_ex",
            "qubo_build_tables", "qubo_last_timing", "qubo_search_lowest", "qubo_search_f64",
            "qubo_search_lowest_f64",
            "qubo_progress_init", "qubo_search_step", "qubo_progress_init_lowest", "qubo_search_step_lowest",
@@ -152,6 +152,7 @@ def load(path: str = LIB_PATH):
     lib.qubo_check_q.argtypes = [ctypes.c_void_p, ctypes.c_int]
     lib.qubo_abs_sum.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
     lib.qubo_check_q_f64.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.qubo_f64_as_int32.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
     lib.qubo_search.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                 ctypes.POINTER(_Result)]
     lib.qubo_search_noalloc.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -241,6 +242,24 @@ def check_q_f64(Q_host) -> None:
     rc = load().qubo_check_q_f64(q.ctypes.data_as(ctypes.c_void_p), q.shape[0])
     if rc != QUBO_OK:
         raise QuboError(rc, "qubo_check_q_f64")
+
+
+def f64_as_int32(Q_host):
+    """The exact int32 form of a dyadic binary64 host matrix: (Q_int, f) with
+    Q = Q_int / 2^f entry by entry and sum |Q_int| <= 2^30 - 1, the form the
+    binary64 searches hand to the integer search.  Raises QuboError(QUBO_ERANGE)
+    when Q has no such form."""
+    import numpy as np
+    q = np.ascontiguousarray(np.asarray(Q_host, dtype=np.float64))
+    if q.ndim != 2 or q.shape[0] != q.shape[1]:
+        raise ValueError("Q must be square")
+    out = np.zeros(q.shape, dtype=np.int32)
+    f = ctypes.c_int(0)
+    rc = load().qubo_f64_as_int32(q.ctypes.data_as(ctypes.c_void_p), q.shape[0],
+                                  out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(f))
+    if rc != QUBO_OK:
+        raise QuboError(rc, "qubo_f64_as_int32")
+    return out, f.value
 
 
 def _device_q(Q):

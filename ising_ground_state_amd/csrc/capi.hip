@@ -47,6 +47,20 @@ QUBO_API int qubo_check_q_f64(const double *Q_host, int n)
     return guard_f64(Qh, &S);
 }
 
+QUBO_API int qubo_f64_as_int32(const double *Q_host, int n, int32_t *Q_int, int *f)
+{
+    if (!Q_host || !Q_int || !f || n < 1 || n > QUBO_MAX_N)
+        return QUBO_EINVAL;
+    const std::vector<double> Qh(Q_host, Q_host + (size_t)n * n);
+    std::vector<int32_t> Qi;
+    int fe = 0;
+    if (!dyadic_int32(Qh, Qi, &fe))
+        return QUBO_ERANGE;
+    std::copy(Qi.begin(), Qi.end(), Q_int);
+    *f = fe;
+    return QUBO_OK;
+}
+
 QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bits, void *stream,
                 qubo_result *out)
 {

@@ -103,6 +103,11 @@ struct RequestF64 {
     int lowest_k = 0;  // > 0: the k-lowest search (its states go to *low)
 };
 
+// A dyadic binary64 matrix as int32: true, with Qi = 2^f Q exactly, when every
+// entry is an integer multiple of 2^-f and sum |2^f Q_ij| <= 2^30 - 1 (then
+// every partial sum of the binary64 definition is exact); false otherwise.
+bool dyadic_int32(const std::vector<double> &Qh, std::vector<int32_t> &Qi, int *f_out);
+
 // Keeps the k first states of `acc` merged with `add`, in (energy, index) order.
 void merge_lowest(std::vector<qubo_state> &acc, const std::vector<qubo_state> &add, int k);
 

@@ -12,42 +12,6 @@ namespace qubo_host {
 
 static_assert(sizeof(qubo::LowEntryF64) == sizeof(qubo_state_f64), "list entry layout");
 
-// A dyadic matrix: every entry an integer multiple of 2^-f with
-// sum |2^f Q_ij| <= 2^30 - 1.  Then every partial sum of the definition is a
-// multiple of 2^-f below 2^(30 - f) in magnitude, i.e. at most 30 significant
-// bits, so binary64 adds it exactly, in any order: E(x) = E_int(x) / 2^f with
-// E_int the energy of the int32 matrix 2^f Q, whose search is exact, ties and
-// counts included.  Writes that matrix and f; false when Q is not such a matrix.
-static bool dyadic_int32(const std::vector<double> &Qh, std::vector<int32_t> &Qi, int *f_out)
-{
-    // f = -(the lowest exponent of any entry's last set bit)
-    int f = INT_MIN;
-    for (double v : Qh) {
-        if (v == 0.0)
-            continue;
-        int ex = 0;
-        const double m = std::frexp(std::fabs(v), &ex);      // |v| = m 2^ex, m in [0.5, 1)
-        const uint64_t M = (uint64_t)std::ldexp(m, 53);       // 53-bit integer significand
-        const int lsb = ex - 53 + __builtin_ctzll(M);         // |v| = odd * 2^lsb
-        f = std::max(f, -lsb);
-    }
-    if (f == INT_MIN)
-        f = 0;  // the zero matrix
-    Qi.resize(Qh.size());
-    int64_t sum = 0;
-    for (size_t k = 0; k < Qh.size(); ++k) {
-        const double q = std::ldexp(Qh[k], f);  // exact: a power-of-two scale of an integer multiple
-        if (!(std::fabs(q) <= (double)qubo::kAbsSumLimit))
-            return false;
-        Qi[k] = (int32_t)q;
-        sum += std::llabs((long long)Qi[k]);
-        if (sum > qubo::kAbsSumLimit)
-            return false;
-    }
-    *f_out = f;
-    return true;
-}
-
 // The definition's energy of one state (binary64, i ascending, j ascending over
 // the set variables; the same sums in the same order as the device).
 static double energy_def_host(const std::vector<double> &Qh, int n, const std::vector<char> &x)

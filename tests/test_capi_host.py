@@ -134,6 +134,52 @@ def test_check_q_f64_guard():
     assert e.value.code == q.QUBO_ERANGE
 
 
+def test_f64_as_int32():
+    """The int32 form of a dyadic binary64 matrix (the binary64 searches' integer
+    path): the smallest exponent f, Q = Q_int / 2^f entry by entry, the limit
+    sum |Q_int| <= 2^30 - 1, and refusal of everything else."""
+    import oracle
+    import qubo_instances as qi
+    Qi = np.array(qi.general_uniform(10, 8951, -5, 5), dtype=np.int64)
+    assert (Qi % 2 != 0).any()
+    Qint, f = q.f64_as_int32(Qi.astype(np.float64))
+    assert f == 0 and (Qint == Qi).all()
+    Qint, f = q.f64_as_int32(Qi / 8.0)
+    assert f == 3 and (Qint == Qi).all()
+    Qint, f = q.f64_as_int32(Qi * 2.0 ** 40)  # multiples of 2^40: f < 0
+    assert f == -40 and (Qint == Qi).all()
+    Qint, f = q.f64_as_int32(np.zeros((3, 3)))
+    assert f == 0 and not Qint.any()
+    Qint, f = q.f64_as_int32(-np.zeros((3, 3)))
+    assert f == 0 and not Qint.any()
+    # the limit: sum |2^f Q| = 2^30 - 1 passes, 2^30 + 1 fails (f = 0: odd entries)
+    Q = np.zeros((2, 2))
+    Q[0, 0], Q[1, 1] = 2.0 ** 29, -(2.0 ** 29 - 1)
+    assert q.f64_as_int32(Q)[1] == 0
+    Q[1, 1] = -(2.0 ** 29 + 1)
+    with pytest.raises(q.QuboError) as e:
+        q.f64_as_int32(Q)
+    assert e.value.code == q.QUBO_ERANGE
+    Q[1, 1] = -(2.0 ** 29 - 1)
+    assert q.f64_as_int32(Q / 2.0 ** 10)[1] == 10  # the same limit after scaling
+    for bad in (0.1, np.pi, 2.0 ** -1074, np.nan, np.inf):
+        Q = np.ones((3, 3))
+        Q[0, 1] = bad
+        with pytest.raises(q.QuboError) as e:
+            q.f64_as_int32(Q)
+        assert e.value.code == q.QUBO_ERANGE, bad
+    Q = np.ones((3, 3))
+    Q[2, 2] = 2.0 ** -30  # dyadic, but 2^30 sum |Q| is above the limit
+    with pytest.raises(q.QuboError):
+        q.f64_as_int32(Q)
+    # the point of the form: the binary64 definition's energy of every state is
+    # E_int / 2^f exactly (oracle tier A in binary64 and in int64)
+    Q = Qi / 8.0
+    Qint, f = q.f64_as_int32(Q)
+    idx = np.arange(1 << 10, dtype=np.uint64)
+    assert (oracle.energies_f64(Q, idx) == oracle.energies(Qint, idx) / 2.0 ** f).all()
+
+
 def test_null_and_range_arguments_rejected_before_the_device():
     lib = q.load()
     r = q._Result()
