@@ -225,3 +225,42 @@ def test_largest_single_launch_n58(q):
             announce("n=58 slice lowest", k, top)
             low = q.lowest(Qd, 16, prefix_bits=A, gray_lo=lo, gray_hi=hi)
             assert low == [(int(e), int(i)) for e, i in cube["lowest16"]]
+
+
+def test_largest_single_launch_n58_f64(q):
+    """The binary64 search at n = 58 (A = 32, B = 26: its rounded walk at the
+    largest tables): C58 as binary64 with pi added to Q_00, so the matrix is not
+    dyadic and the search takes the rounded walk.  Every state of the stored
+    slices has x_0 = 0, where the sums never meet Q_00 and are exact integers,
+    so the slices' binary64 minima, indices, counts and 16 lowest states are
+    the stored integer oracle results."""
+    import torch
+    path = os.path.join(os.path.dirname(__file__), "golden", "C58sub.json")
+    if not os.path.exists(path):
+        pytest.skip("stored oracle result C58sub.json not written yet")
+    with open(path) as f:
+        g = json.load(f)
+    cfg = qi.make_config("C58")
+    assert qi.sha256_of(cfg["Q"]) == g["sha256_Q"]
+    Qf = np.asarray(cfg["Q"], dtype=np.float64)
+    Qf[0, 0] += np.pi
+    with pytest.raises(q.QuboError):
+        q.f64_as_int32(Qf)  # not dyadic: the rounded walk runs
+    A = q.make_plan(58)["prefix_bits"]
+    Qd = torch.as_tensor(Qf).to("cuda:0").contiguous()
+    for cube in g["cubes"]:
+        k, top = cube["k"], cube["top"]
+        assert top >> (k - 1) == 0  # variable 0 is 0 in the slice
+        m = inv_gray(top)
+        lo, hi = m << (A - k), (m + 1) << (A - k)
+        announce("n=58 binary64 slice", k, top)
+        r = q.search_f64(Qd, prefix_bits=A, gray_lo=lo, gray_hi=hi)
+        assert r.triple() == (float(cube["min_energy"]), cube["argmin"], cube["count"]), top
+        assert q.last_timing()["candidates"] > 0
+        check_coverage(q, 58, A, None, lo, hi)
+        if "lowest16" in cube:
+            announce("n=58 binary64 slice lowest", k, top)
+            low = q.lowest(Qd, 16, prefix_bits=A, gray_lo=lo, gray_hi=hi)
+            assert low == [(float(e), int(i)) for e, i in cube["lowest16"]]
+    del Qd
+    torch.cuda.synchronize()
