@@ -326,7 +326,7 @@ QUBO_API const char *qubo_strerror(int status)
 
 QUBO_API const char *qubo_version(void)
 {
-    return "qubo-mi355x 0.5 (gfx950; int32 minimum and k-lowest, 8 or 16 columns/lane; binary64; runs in steps)";
+    return "qubo-mi355x 0.6 (gfx950; int32 minimum and k-lowest, 8 or 16 columns/lane; binary64 on rounded int32 tables; runs in steps)";
 }
 
 }  // extern "C"
