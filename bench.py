@@ -265,6 +265,9 @@ def main():
                          "per point, then a summary line); every point must give the same result")
     ap.add_argument("--sweep-prefix", default="24,26,28,30,32", help="prefix_bits values of the sweep")
     ap.add_argument("--sweep-cache", default="8,10,12,13,14,16,18", help="cache_bits values of the sweep")
+    ap.add_argument("--sizes", default=None, metavar="LO-HI",
+                    help="instead of the benchmark: one whole-space search per size n in LO..HI (the "
+                         "analogue of P1's Table IV), one JSON line per size")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -282,6 +285,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     q.load()
+    if args.sizes:
+        lo, hi = (int(v) for v in args.sizes.split("-"))
+        size_scan(q, lo, hi)
+        return
     cfg = qi.make_config(args.config)
     n = cfg["n"]
     Qd = torch.tensor(cfg["Q"], dtype=torch.int32, device="cuda:0")
@@ -514,6 +521,75 @@ def split_sweep(q, Qd, cfg, prefixes, caches):
                       "best": best, "points": len(rows),
                       "all_same_result": all(r["same_result"] for r in rows),
                       "result": list(ref.triple())}), flush=True)
+
+
+STEPPED_ABOVE = 50  # larger searches run in steps of about 2^48 states, each printing its progress
+
+
+def size_scan(q, n_min, n_max):
+    """One whole-space search per size n: a symmetric int32 matrix with entries
+    uniform in [-100, 100] (seed 6000 + n; P1 times "a uniformly random
+    matrix", sec. V.C, with no range or seed given), timed from the call to its
+    result, tables and reduction included as in P1's Table IV.  Sizes up to 44
+    take the median of three calls after a warm-up, larger ones one call; above
+    STEPPED_ABOVE variables the search runs as a sequence of steps
+    (qubo_progress_init / qubo_search_step), whose device times are summed."""
+    import torch
+    import qubo_instances as qi
+    for n in range(n_min, n_max + 1):
+        Qd = torch.tensor(qi.symmetric_uniform(n, 6000 + n, -100, 100), dtype=torch.int32, device="cuda:0")
+        plan = q.make_plan(n)
+        A, B = plan["prefix_bits"], plan["suffix_bits"]
+        rec = {"n": n, "seed": 6000 + n, "prefix_bits": A, "suffix_bits": B, "states": 1 << n}
+        if n <= STEPPED_ABOVE:
+            reps = 3 if n <= 44 else 1
+            if n <= 44:
+                q.search(Qd)
+            walls, times = [], []
+            for _ in range(reps):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                r = q.search(Qd)
+                torch.cuda.synchronize()
+                walls.append(time.perf_counter() - t0)
+                times.append(q.last_timing())
+            i = sorted(range(reps), key=lambda k: walls[k])[reps // 2]
+            wall, t = walls[i], times[i]
+            rec.update({"calls": reps, "search_ms": t["search_ms"], "build_ms": t["build_ms"],
+                        "slow_bodies": t["slow_bodies"], "coverage_ok": covers(t, A, B)})
+            result = r.triple()
+        else:
+            p = q.progress_init(Qd)
+            search_ms = build_ms = 0.0
+            bodies = slow = steps = 0
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            done = False
+            while not done:
+                done = q.search_step(Qd, p)
+                t = q.last_timing()
+                search_ms += t["search_ms"]
+                build_ms += t["build_ms"]
+                bodies += t["bodies"]
+                slow += t["slow_bodies"]
+                steps += 1
+                print("[sizes] n=%d step %d of %d: %.1f s so far" % (n, steps, p.steps_total,
+                                                                   time.perf_counter() - t0),
+                      file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            group = 64 * t["cols_per_lane"]
+            cols_padded = -(-(1 << B) // group) * group
+            rec.update({"steps": steps, "search_ms": search_ms, "build_ms": build_ms, "slow_bodies": slow,
+                        "coverage_ok": bodies * 32 * group == (1 << A) * cols_padded})
+            result = p.result().triple()
+        rec.update({"wall_s": wall, "states_per_s_1e12": (1 << n) / wall / 1e12,
+                    "kernel_states_per_s_1e12": (1 << n) / (rec["search_ms"] / 1e3) / 1e12,
+                    "frac": (1 << n) / (rec["search_ms"] / 1e3) / INT32_VALU_PEAK,
+                    "result": list(result)})
+        print(json.dumps({"size_point": rec}), flush=True)
+        del Qd
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
