@@ -235,9 +235,10 @@ int make_plan(int n_total, int prefix_bits, int cache_bits, int num_cus, int col
     if (target_units > p.col_groups)
         split = ceil_log2((target_units + p.col_groups - 1) / p.col_groups);
     int c = A - split;
-    // but at least 2^10 steps (32 bodies) per unit where the walk is that long:
-    // a unit's start (its anchor rows and register rows from memory) must stay
-    // small against its walk, even when fewer units than resident waves result
+    // but at least 2^12 steps (128 bodies) per unit where the walk is that long:
+    // a unit's start (its rows from memory) must stay small against its walk,
+    // even when fewer units result (at n = 34..38, 2^10-step units ran 1.2 to
+    // 2.1 times slower than 2^12-step ones; larger sizes reach 2^12 anyway)
     c = std::max(c, std::min(A, kMinSegBits));
     c = std::max(c, kRegBits);
     c = std::min(c, kMaxSegBits);
