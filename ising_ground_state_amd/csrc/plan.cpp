@@ -238,8 +238,12 @@ int make_plan(int n_total, int prefix_bits, int cache_bits, int num_cus, int col
     // but at least 2^12 steps (128 bodies) per unit where the walk is that long:
     // a unit's start (its rows from memory) must stay small against its walk,
     // even when fewer units result (at n = 34..38, 2^10-step units ran 1.2 to
-    // 2.1 times slower than 2^12-step ones; larger sizes reach 2^12 anyway)
+    // 2.1 times slower than 2^12-step ones; larger sizes reach 2^12 anyway) --
+    // unless that leaves fewer units than resident waves: then down to 2^10
+    // steps until there are enough (n = 32 ran 30 % slower on 2,048 units)
     c = std::max(c, std::min(A, kMinSegBits));
+    while (c > kMinSegBitsIdle && p.col_groups * (1ull << (A - c)) < resident_waves)
+        --c;
     c = std::max(c, kRegBits);
     c = std::min(c, kMaxSegBits);
     c = std::min(c, A);

@@ -21,7 +21,8 @@ constexpr uint64_t kMaxMintBytes = 1ull << 33;  // 8 GiB
 constexpr int kMaxSingleVars = 58;       // largest n searched by a single launch
 constexpr int kMaxSplitBits = 32;        // at most 2^32 sub-problems
 constexpr int kMaxSegBits = 18;          // Gray steps per work unit at most 2^18 (a fine tail)
-constexpr int kMinSegBits = 12;          // and at least 2^12 where the prefix walk allows
+constexpr int kMinSegBits = 12;          // and at least 2^12 where the prefix walk allows,
+constexpr int kMinSegBitsIdle = 10;      // or 2^10 when longer units would leave waves idle
 
 constexpr int64_t kAbsSumLimit = (1ll << 30) - 1;
 
