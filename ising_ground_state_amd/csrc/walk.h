@@ -109,7 +109,7 @@ __device__ __forceinline__ void adds_body(int (&E)[R], const int (&Mr)[kU][R], b
 }
 
 // The same body with the per-step test of Algorithm 2: after each state, the
-// lane's minimum over its 16 columns (a v_min3 tree) is compared with the
+// lane's minimum over its R columns (a v_min3 tree) is compared with the
 // threshold T - E_p(g(j)).  Returns the OR over the body of the wave's hit masks.
 template <int R>
 __device__ __forceinline__ uint64_t checked_body(int (&E)[R], const int (&Mr)[kU][R],
@@ -139,7 +139,6 @@ __device__ __forceinline__ uint64_t checked_body(int (&E)[R], const int (&Mr)[kU
     }
     return acc;
 }
-
 
 // The loop over work units of one workgroup (a persistent grid: items come
 // from a global counter; an item is one column group and four consecutive
