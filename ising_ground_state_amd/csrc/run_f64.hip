@@ -95,6 +95,59 @@ static std::vector<double> descent_energies(const std::vector<double> &Qh, int n
     return es;
 }
 
+// A dyadic binary64 request (Qi = 2^f Q exactly; dyadic_int32) on the integer
+// search: states with E <= cap are those with E_int <= floor(2^f cap), and
+// energies come back divided by 2^f (exact: at least 2^-130 in magnitude when
+// not 0, since 2^f sum |Q_ij| <= 2^30 - 1 and sum |Q_ij| >= 2^-100).
+static int run_dyadic(const RequestF64 &rq, const DeviceInfo &dev, const std::vector<int32_t> &Qi, int f,
+                      qubo_result_f64 *out, bool have_cap, double cap, bool *found,
+                      std::vector<qubo_state_f64> *low)
+{
+    using namespace qubo;
+    const bool lowest = rq.lowest_k > 0;
+    std::vector<int32_t> Ui;
+    int64_t abs_sum = 0;
+    int rc = fold_upper(Qi.data(), rq.n, Ui, &abs_sum);
+    if (rc != QUBO_OK)
+        return rc;
+    Request irq;
+    irq.n = rq.n;
+    irq.prefix_bits = rq.prefix_bits;
+    irq.cache_bits = rq.cache_bits;
+    irq.ranged = rq.ranged;
+    irq.gray_lo = rq.gray_lo;
+    irq.gray_hi = rq.gray_hi;
+    irq.stream = rq.stream;
+    irq.cols_per_lane = kColsPerLaneF64;
+    irq.lowest_k = rq.lowest_k;
+    int32_t icap = 0;
+    if (have_cap) {
+        const double c = std::floor(std::ldexp(cap, f));
+        icap = c > (double)abs_sum ? (int32_t)abs_sum : c < -(double)abs_sum ? (int32_t)-abs_sum - 1 : (int32_t)c;
+    }
+    qubo_result ir{};
+    bool ifound = false;
+    qubo_timing t{};
+    std::vector<qubo_state> ilow;
+    rc = run_one(irq, dev, std::move(Ui), rq.n, abs_sum, have_cap, icap, lowest ? nullptr : &ir, &ifound, &t,
+                 lowest ? &ilow : nullptr);
+    if (rc != QUBO_OK)
+        return rc;
+    last_timing() = t;
+    if (found)
+        *found = ifound;
+    if (lowest) {
+        low->clear();
+        for (const qubo_state &st : ilow)
+            low->push_back(qubo_state_f64{std::ldexp((double)st.energy, -f), st.index});
+    } else if (ifound) {
+        out->min_energy = std::ldexp((double)ir.min_energy, -f);
+        out->argmin = ir.argmin;
+        out->count = ir.count;
+    }
+    return QUBO_OK;
+}
+
 // have_cap: the search only has to find states with E <= cap (a real energy
 // found elsewhere); an empty result is then valid and *found says whether any
 // state was recorded.
@@ -132,56 +185,12 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
         return rc;
 
     // A dyadic matrix (integer-valued ones included) is searched as the int32
-    // matrix 2^f Q by the integer search, which is exact for it; energies come
-    // back divided by 2^f (exact: at least 2^-130 in magnitude when not 0).
+    // matrix 2^f Q by the integer search, which is exact for it.
     {
         std::vector<int32_t> Qi;
         int f = 0;
-        if (dyadic_int32(Qh, Qi, &f)) {
-            std::vector<int32_t> Ui;
-            int64_t abs_sum = 0;
-            rc = fold_upper(Qi.data(), n, Ui, &abs_sum);
-            if (rc != QUBO_OK)
-                return rc;
-            Request irq;
-            irq.n = n;
-            irq.prefix_bits = rq.prefix_bits;
-            irq.cache_bits = rq.cache_bits;
-            irq.ranged = rq.ranged;
-            irq.gray_lo = rq.gray_lo;
-            irq.gray_hi = rq.gray_hi;
-            irq.stream = rq.stream;
-            irq.cols_per_lane = kColsPerLaneF64;
-            irq.lowest_k = rq.lowest_k;
-            // states with E <= cap are those with E_int <= floor(2^f cap)
-            int32_t icap = 0;
-            if (have_cap) {
-                const double c = std::floor(std::ldexp(cap, f));
-                icap = c > (double)abs_sum ? (int32_t)abs_sum : c < -(double)abs_sum ? (int32_t)-abs_sum - 1
-                                                                                       : (int32_t)c;
-            }
-            qubo_result ir{};
-            bool ifound = false;
-            qubo_timing t{};
-            std::vector<qubo_state> ilow;
-            rc = run_one(irq, dev, std::move(Ui), n, abs_sum, have_cap, icap, lowest ? nullptr : &ir, &ifound, &t,
-                         lowest ? &ilow : nullptr);
-            if (rc != QUBO_OK)
-                return rc;
-            last_timing() = t;
-            if (found)
-                *found = ifound;
-            if (lowest) {
-                low->clear();
-                for (const qubo_state &st : ilow)
-                    low->push_back(qubo_state_f64{std::ldexp((double)st.energy, -f), st.index});
-            } else if (ifound) {
-                out->min_energy = std::ldexp((double)ir.min_energy, -f);
-                out->argmin = ir.argmin;
-                out->count = ir.count;
-            }
-            return QUBO_OK;
-        }
+        if (dyadic_int32(Qh, Qi, &f))
+            return run_dyadic(rq, dev, Qi, f, out, have_cap, cap, found, low);
     }
     // Fold to the upper triangle in binary64 (the walk's tables only; states
     // are scored against Q itself) and pad small problems: a padding variable
