@@ -45,7 +45,8 @@ std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_searc
     return P;
 }
 
-std::vector<int64_t> descent_energies(const std::vector<int32_t> &U, int n, int starts)
+std::vector<int64_t> descent_energies(const std::vector<int32_t> &U, int n, int starts, int fixed,
+                                      uint64_t fixed_value)
 {
     // F[v]: the change of E when variable v goes from 0 to 1 given the others
     // (U_vv plus the couplings to the set variables); flipping v moves E by F[v]
@@ -66,7 +67,7 @@ std::vector<int64_t> descent_energies(const std::vector<int32_t> &U, int n, int 
         }
         int64_t e = 0;
         for (int v = 0; v < n; ++v)
-            x[(size_t)v] = (int)((start >> v) & 1u);
+            x[(size_t)v] = v < fixed ? (int)((fixed_value >> (fixed - 1 - v)) & 1u) : (int)((start >> v) & 1u);
         for (int v = 0; v < n; ++v) {
             int64_t f = U[(size_t)v * n + v];
             for (int j = 0; j < n; ++j)
@@ -80,7 +81,7 @@ std::vector<int64_t> descent_energies(const std::vector<int32_t> &U, int n, int 
         for (int step = 0; step < 4 * n + 4; ++step) {
             int best = -1;
             int64_t best_d = 0;
-            for (int v = 0; v < n; ++v) {
+            for (int v = fixed; v < n; ++v) {
                 const int64_t d = x[(size_t)v] ? -F[(size_t)v] : F[(size_t)v];
                 if (d < best_d) {
                     best_d = d;
@@ -101,12 +102,29 @@ std::vector<int64_t> descent_energies(const std::vector<int32_t> &U, int n, int 
             key |= (uint64_t)x[(size_t)v] << v;
         if (seen.insert(key).second)
             es.push_back(e);
-        for (int v = 0; v < n; ++v)  // the single-flip neighbours
+        for (int v = fixed; v < n; ++v)  // the single-flip neighbours
             if (seen.insert(key ^ (1ull << v)).second)
                 es.push_back(e + (x[(size_t)v] ? -F[(size_t)v] : F[(size_t)v]));
     }
     std::sort(es.begin(), es.end());
     return es;
+}
+
+void largest_subcube(uint64_t lo, uint64_t hi, int A, int *fixed, uint64_t *fixed_value)
+{
+    // the largest aligned block [m 2^s, (m + 1) 2^s) inside [lo, hi); its Gray
+    // codes share their top A - s bits, g(m) (g(j) >> s = g(j >> s))
+    for (int sb = A; sb >= 0; --sb) {
+        const uint64_t size = 1ull << sb;
+        const uint64_t m = (lo + size - 1) >> sb;
+        if ((m + 1) << sb <= hi && m < (1ull << (A - sb))) {
+            *fixed = A - sb;
+            *fixed_value = m ^ (m >> 1);
+            return;
+        }
+    }
+    *fixed = A;
+    *fixed_value = lo ^ (lo >> 1);
 }
 
 static int ceil_log2(uint64_t v)

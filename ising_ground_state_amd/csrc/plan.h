@@ -38,13 +38,22 @@ std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_searc
 // Energies of distinct states of the folded matrix U (n x n upper triangle,
 // n <= 63), ascending: the states that steepest single-flip descents reach
 // from state 0 and from starts - 1 fixed pseudo-random states (SplitMix64, a
-// fixed seed), and their single-flip neighbours.  Exact in int64.  The first
-// is a real energy at most E(0) = 0 and the j-th bounds the j-th lowest energy
-// from above: first thresholds of a whole-space search, so that the bound gates
-// clear bodies from the start.  Only the thresholds depend on the starts,
-// never a search's result.
-std::vector<int64_t> descent_energies(const std::vector<int32_t> &U, int n, int starts);
+// fixed seed), and their single-flip neighbours, with the first `fixed`
+// variables held at the bits of fixed_value (variable 0 its most significant
+// of `fixed` bits) throughout: states of that sub-cube only.  Exact in int64.
+// The first is a real energy and the j-th bounds the j-th lowest energy of the
+// sub-cube (and of any set holding it) from above: first thresholds of a
+// search, so that the bound gates clear bodies from the start.  Only the
+// thresholds depend on the starts, never a search's result.
+std::vector<int64_t> descent_energies(const std::vector<int32_t> &U, int n, int starts, int fixed = 0,
+                                      uint64_t fixed_value = 0);
 constexpr int kDescentStarts = 16;
+
+// The states of the Gray steps [lo, hi) of an A-bit prefix walk (lo < hi <=
+// 2^A) hold a sub-cube: the prefixes g(j) of the largest aligned block of steps
+// [m 2^s, (m + 1) 2^s) inside the range share their first A - s variables,
+// which spell g(m) (sec. III.C.1).  Writes A - s and g(m).
+void largest_subcube(uint64_t lo, uint64_t hi, int A, int *fixed, uint64_t *fixed_value);
 
 // Fills `out` for n variables on a device with `num_cus` compute units;
 // cols_per_lane is 8 or 16, or 0 for the default.  split_bits: -1 splits only

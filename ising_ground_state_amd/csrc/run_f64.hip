@@ -29,13 +29,15 @@ static double energy_def_host(const std::vector<double> &Qh, int n, const std::v
 
 // Energies of distinct real states, ascending: the states that steepest
 // single-flip descents reach (fields in binary64; at most 4n flips each) from
-// state 0 and from kDescentStarts - 1 fixed pseudo-random states (SplitMix64,
+// state 0 and from qubo::kDescentStarts - 1 fixed pseudo-random states (SplitMix64,
 // a fixed seed: only the first threshold depends on them, never the result),
-// and their single-flip neighbours, each scored by the definition.  The j-th
-// value bounds the j-th lowest energy of the whole space from above.
-static constexpr int kDescentStarts = 16;
-
-static std::vector<double> descent_energies(const std::vector<double> &Qh, int n)
+// and their single-flip neighbours, each scored by the definition, with the
+// first `fixed` variables held at the bits of fixed_value (variable 0 its most
+// significant of `fixed` bits): states of that sub-cube only.  The j-th value
+// bounds the j-th lowest energy of the sub-cube (and of any set holding it)
+// from above.
+static std::vector<double> descent_energies(const std::vector<double> &Qh, int n, int fixed,
+                                            uint64_t fixed_value)
 {
     std::unordered_set<uint64_t> seen;
     std::vector<double> es;
@@ -48,10 +50,10 @@ static std::vector<double> descent_energies(const std::vector<double> &Qh, int n
     };
     std::vector<char> x(n);
     std::vector<double> F(n);  // F_v = Q_vv + sum_{j != v, x_j = 1} (Q_vj + Q_jv): the change of setting v
-    for (int s = 0; s < kDescentStarts; ++s) {
+    for (int s = 0; s < qubo::kDescentStarts; ++s) {
         const uint64_t start = s == 0 ? 0 : next();
         for (int v = 0; v < n; ++v)
-            x[v] = (char)((start >> v) & 1u);
+            x[v] = v < fixed ? (char)((fixed_value >> (fixed - 1 - v)) & 1u) : (char)((start >> v) & 1u);
         for (int v = 0; v < n; ++v) {
             double f = Qh[(size_t)v * n + v];
             for (int j = 0; j < n; ++j)
@@ -62,7 +64,7 @@ static std::vector<double> descent_energies(const std::vector<double> &Qh, int n
         for (int it = 0; it < 4 * n; ++it) {
             int best = -1;
             double gain = 0.0;
-            for (int v = 0; v < n; ++v) {
+            for (int v = fixed; v < n; ++v) {
                 const double d = x[v] ? -F[v] : F[v];
                 if (d < gain) {
                     gain = d;
@@ -80,7 +82,9 @@ static std::vector<double> descent_energies(const std::vector<double> &Qh, int n
         uint64_t key = 0;
         for (int v = 0; v < n; ++v)
             key |= (uint64_t)x[v] << v;
-        for (int v = -1; v < n; ++v) {  // y, then its neighbours
+        for (int v = -1; v < n; ++v) {  // y, then its neighbours over the free variables
+            if (v >= 0 && v < fixed)
+                continue;
             const uint64_t k = v < 0 ? key : key ^ (1ull << v);
             if (!seen.insert(k).second)
                 continue;
@@ -285,8 +289,11 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     // by 2^-40 S against any difference between the host's sums and the
     // device's.
     double t0 = (lo == 0 && !lowest) ? 0.0 : 4.0 * S + 1.0;
-    if (!rq.ranged && n >= kMinSearchVars) {
-        const std::vector<double> es = descent_energies(Qh, n);
+    if (n >= kMinSearchVars) {
+        int fixed = 0;
+        uint64_t fixed_value = 0;
+        largest_subcube(lo, hi, A, &fixed, &fixed_value);  // the whole space: nothing fixed
+        const std::vector<double> es = descent_energies(Qh, n, fixed, fixed_value);
         const size_t j = lowest ? (size_t)rq.lowest_k - 1 : 0;
         if (j < es.size()) {
             const double t = es[j] + std::ldexp(S, -40);

@@ -136,16 +136,20 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     // The first threshold must be a real energy of the searched set or an upper
     // bound of all of them: E(0) = 0 when state 0 is searched, else sum |Q_ij|
     // (for the spectrum, whose threshold bounds the k-th energy, sum |Q_ij|).
-    // A whole-space search starts from the energies of single-flip descents
-    // instead (real states; the lowest for the minimum, the k-th lowest for
-    // the spectrum), so that its gates clear bodies from the first one.  With
-    // padding variables the spectrum keeps sum |Q_ij|: a neighbour that sets
-    // one is not a state of the problem.  A caller's cap (an energy found
+    // A search starts from the energies of single-flip descents inside the
+    // largest sub-cube its range holds instead (real states of the range; the
+    // lowest for the minimum, the k-th lowest for the spectrum), so that its
+    // gates clear bodies from the first one.  With padding variables (whole
+    // spaces only: slices need n >= 5) the spectrum keeps sum |Q_ij|: a
+    // neighbour that sets one is not a state of the problem.  A caller's cap (an energy found
     // elsewhere) may only lower it; it is never below -sum |U_ij| here, so
     // every threshold stays within +-2 sum |U_ij|.
     int32_t t0 = (lo == 0 && !lowest) ? 0 : (int32_t)abs_sum;
-    if (lo == 0 && hi == (1ull << A) && (!lowest || ns == n)) {
-        const std::vector<int64_t> es = descent_energies(U, ns, kDescentStarts);
+    if (!lowest || ns == n) {
+        int fixed = 0;
+        uint64_t fixed_value = 0;
+        largest_subcube(lo, hi, A, &fixed, &fixed_value);  // the whole space: nothing fixed
+        const std::vector<int64_t> es = descent_energies(U, ns, kDescentStarts, fixed, fixed_value);
         const size_t j = lowest ? (size_t)k_low - 1 : 0;
         if (j < es.size() && es[j] < t0)
             t0 = (int32_t)es[j];
