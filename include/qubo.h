@@ -6,7 +6,11 @@
  * QUBO Brute-Force on a Single GPU: A Matrix Prefix-Suffix Decomposition",
  * sec. I), with the prefix-suffix decomposition of sec. II (eq. 4 and eq. 8), the
  * Gray-code prefix walk of sec. III.B (eq. 9, Algorithm 2) and the parallel
- * splits of sec. III.C.  Every call is exact: integer arithmetic throughout.
+ * splits of sec. III.C.  Every call is exact: integer arithmetic throughout.  The
+ * qubo_*_f64 entry points search a binary64 Q (sec. VI.B, floating-point
+ * matrices): they return the exact answer of a fixed-order binary64 definition
+ * of E, from an integer walk over rounded tables and a re-evaluation of every
+ * state the rounding could not rank.
  *
  * Conventions shared by every entry point
  *   - Q is a dense n x n int32 matrix, row-major and contiguous.  It need not be
@@ -154,8 +158,9 @@ QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bit
  * uses one static device buffer of QUBO_NOALLOC_BYTES (128 MiB) that the
  * library holds on each GPU it runs on until the process ends.
  *   - Sizes: the plan's workspace (U, E_s, M_int, 4 x 2^prefix_bits bytes of
- *     prefix energies and their per-body minima, 32 bytes per wave, 256 bytes)
- *     must fit the buffer, else QUBO_ESCRATCH before any device work.  The
+ *     prefix energies with their body and group minima, 64 bytes per
+ *     workgroup, 256 bytes) must fit the buffer, else QUBO_ESCRATCH before any
+ *     device work.  The
  *     planner's default split fits up to n = 40 (73 MiB at n = 40); larger n
  *     fit with a smaller prefix_bits while M_int stays small (n = 42 at
  *     prefix_bits 24: 92 MiB); n = 48 does not fit.
