@@ -199,6 +199,43 @@ def test_exact_ties_on_the_rounded_walk(q):
     assert q.lowest(Qd, 48) == oracle.lowest_f64(Q, 48)
 
 
+def _real_family(kind, n, rng):
+    if kind == "uniform":
+        return rng.uniform(-1.0, 1.0, size=(n, n))
+    if kind == "log-uniform":  # magnitudes over twelve decades, random signs
+        return rng.choice([-1.0, 1.0], size=(n, n)) * 10.0 ** rng.uniform(-6, 6, size=(n, n))
+    if kind == "near-ties":  # small integers plus relative noise of 1e-12
+        Qi = rng.integers(-2, 3, size=(n, n)).astype(np.float64)
+        return Qi * (1.0 + 1e-12 * rng.standard_normal(size=(n, n)))
+    if kind == "sparse":  # nine entries in ten are zero
+        return rng.uniform(-5.0, 5.0, size=(n, n)) * (rng.random(size=(n, n)) < 0.1)
+    if kind == "low-rank":  # a rank-2 product: many near-degenerate states
+        u = rng.standard_normal(size=(n, 2))
+        return u @ u.T * np.pi
+    if kind == "heavy-tail":  # Cauchy entries: a few dominate S
+        return rng.standard_cauchy(size=(n, n))
+    raise KeyError(kind)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "log-uniform", "near-ties", "sparse", "low-rank", "heavy-tail"])
+def test_random_real_families(q, kind):
+    """Seeded families of real matrices that stress the rounded walk in
+    different ways (entries far below its 17-bit unit, ties broken below the
+    unit, zero rows, near-degenerate spectra, a few dominant entries), at
+    n = 8..16: minimum, lowest index, count and the 8 lowest states against
+    the oracle's binary64 definition."""
+    rng = np.random.default_rng(9900 + ["uniform", "log-uniform", "near-ties", "sparse", "low-rank",
+                                        "heavy-tail"].index(kind))
+    for n in (8, 11, 13, 16):
+        for rep in range(2):
+            Q = _real_family(kind, n, rng)
+            q.check_q_f64(Q)
+            Qd = dev_f(Q)
+            announce("f64 family", kind, n, rep)
+            assert q.search_f64(Qd).triple() == oracle.search_direct_f64(Q).triple(), (kind, n, rep)
+            assert q.lowest(Qd, 8) == oracle.lowest_f64(Q, 8), (kind, n, rep)
+
+
 def test_zero_and_diagonal(q):
     announce("f64 zero")
     assert q.search_f64(dev_f(np.zeros((8, 8)))).triple() == (0.0, 0, 256)
