@@ -281,8 +281,9 @@ typedef struct {
  * flags: 0 or QUBO_FLAG_COLS8.  Every entry must be finite and S = sum |Q_ij|
  * either 0 or in [2^-100, 2^100] (else QUBO_ERANGE; qubo_check_q_f64).
  * The walk is the integer kernel's (one int32 add per state) over the tables
- * of eq. 8 formed in binary64, scaled by s = 2^e (s S <= 2^17) and rounded to
- * integers once each; a state's walked value then lies within A/2 + 2 of
+ * of eq. 8 formed in binary64, scaled by s = 2^e (s S <= 2^17, or up to 2^28
+ * for a matrix whose entries spread over many orders of magnitude) and rounded
+ * to integers once each; a state's walked value then lies within A/2 + 2 of
  * s E(x), and a state whose walked value comes within M = A/2 + 3 of s times
  * the best exact energy so far (about 2^-13 S) is re-evaluated from the
  * definition on the GPU, so the result is exactly the definition's.  A dyadic

@@ -12,17 +12,20 @@ namespace qubo {
 constexpr int kColsPerLaneF64 = 8;
 
 // The walk's tables are the binary64 tables scaled by s = 2^e and rounded to
-// integers, with e chosen so that s * sum |Q_ij| <= 2^kQuantBits.  The scaled
-// sums then keep about as many significant bits as the integer workloads of
-// that size; wider words switch more bits per add and the chip then runs at
-// a lower clock.
+// integers, with e chosen so that s * sum |Q_ij| <= 2^q.  q = kQuantBits keeps
+// about as many significant bits as the integer workloads of that size (wider
+// words switch more bits per add and the chip then runs at a lower clock);
+// matrices whose entries spread over many orders of magnitude get up to
+// kQuantBitsMax, so that their small entries still rank states.
 constexpr int kQuantBits = 17;
+constexpr int kQuantBitsMax = 28;
 
 // Padding columns of the rounded suffix energies: above every threshold the
-// filter can take (at most 2^(kQuantBits + 2) + 19 + 2^kQuantBits + 33 after
+// filter can take (at most 2^(q + 2) + 19 + 2^q + 33 <= 2^30 + 2^28 + 52 after
 // subtracting a prefix energy), so they are never candidates, and the sums the
-// walk and its gates form from them stay far from int32 overflow.
-constexpr int32_t kPadQ = 1 << 30;
+// walk and its gates form from them (at most 3 * 2^29 + 2^28 + 33) stay below
+// 2^31.
+constexpr int32_t kPadQ = 3 << 29;
 
 // One workgroup's partial result (48 bytes).
 struct PartialF64 {
@@ -71,7 +74,7 @@ struct SearchArgsF64 {
     int32_t l_eff;          // Gray bits with rows on chip (registers + LDS)
     int32_t seg_bits;
     int32_t margin;         // M: |W(x) - s E(x)| < M - 1 for every state (rounding and binary64 error)
-    int32_t cap;            // filter threshold above every rounded energy (2^(kQuantBits + 2))
+    int32_t cap;            // filter threshold above every rounded energy (2^(q + 2))
     int32_t k_low;          // k-lowest search: states kept per wave (1..64), else 0
     int32_t pad1;
 };

@@ -17,7 +17,7 @@
 //   * W(x) differs from s E(x) by at most (A + 2) / 2 (one half per rounded
 //     term: E_s, E_p and at most A rows) plus s times the binary64 rounding of
 //     the tables and of the definition (under 2 n^2 2^-53 S with S = sum |Q_ij|,
-//     i.e. under 2^-20 once s S <= 2^17), so |W(x) - s E(x)| < M - 1 with
+//     i.e. under 2^-12 for s S <= 2^28), so |W(x) - s E(x)| < M - 1 with
 //     M = A / 2 + 3;
 //   * a state is re-evaluated from the definition, in binary64 and in the
 //     definition's order, whenever W(x) <= floor(s T) + M, where T bounds the

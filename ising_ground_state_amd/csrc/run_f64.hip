@@ -209,13 +209,31 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     const double pad_diag = S > 0.0 ? S : 1.0;
     for (int i = n; i < ns; ++i)
         U[(size_t)i * ns + i] = pad_diag;
-    // The scale s = 2^e with s * S_walk <= 2^kQuantBits, S_walk bounding the
-    // magnitude sum of the folded, padded matrix (and so of every table entry
-    // and every sub-sum the walk forms).
+    // The scale s = 2^e with s * S_walk <= 2^q, S_walk bounding the magnitude
+    // sum of the folded, padded matrix (and so of every table entry and every
+    // sub-sum the walk forms).  q = kQuantBits unless S_walk exceeds n^2 times
+    // the median nonzero |Q_ij| by more than 8: then by the excess, up to
+    // kQuantBitsMax (entries over many orders of magnitude would otherwise round
+    // to a few bits, leave many states with one walked value and send them all
+    // to re-evaluation).  Any q up to kQuantBitsMax keeps the proof below.
     const double S_walk = S + (double)(ns - n) * pad_diag;
+    int qbits = kQuantBits;
+    {
+        std::vector<double> mags;
+        mags.reserve(Qh.size());
+        for (double v : Qh)
+            if (v != 0.0)
+                mags.push_back(std::fabs(v));
+        if (!mags.empty()) {
+            std::nth_element(mags.begin(), mags.begin() + mags.size() / 2, mags.end());
+            const double spread = S_walk / ((double)n * n * mags[mags.size() / 2]);
+            const int extra = (int)std::floor(std::log2(spread)) - 3;
+            qbits = std::min(kQuantBitsMax, kQuantBits + std::max(0, extra));
+        }
+    }
     int ex = 0;
     (void)std::frexp(S_walk, &ex);  // S_walk < 2^ex
-    const double scale = std::ldexp(1.0, kQuantBits - ex);
+    const double scale = std::ldexp(1.0, qbits - ex);
 
     uint64_t lo = 0, hi = 1ull << A;
     if (rq.ranged) {
@@ -276,10 +294,10 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     // A state is re-evaluated when its rounded walk value W is at most
     // floor(s T) + M for the bound T of the minimum: |W - s E| is at most
     // (A + 2) / 2 for the rounded terms plus under 2^-20 of binary64 rounding,
-    // below M - 1 = A / 2 + 2.  The filter's cap 2^(kQuantBits + 2) lies above
-    // every W.
+    // below M - 1 = A / 2 + 2 (the binary64 part stays under 2^-12 at q = 28).
+    // The filter's cap 2^(q + 2) lies above every W.
     const int margin = A / 2 + 3;
-    const int filter_cap = 1 << (kQuantBits + 2);
+    const int filter_cap = 1 << (qbits + 2);
     // The first threshold: E(0) = 0 when state 0 is searched, else above every
     // energy (for the k-lowest search: always that bound, E(0) bounds only the
     // minimum).  A whole-space search starts from real energies instead: the

@@ -236,6 +236,24 @@ def test_random_real_families(q, kind):
             assert q.lowest(Qd, 8) == oracle.lowest_f64(Q, 8), (kind, n, rep)
 
 
+def test_one_dominant_entry(q):
+    """Entries uniform in [-1e-3, 1e-3] and one diagonal entry of 1e3: with the
+    walk's 17-bit tables the small entries would round to a quantum or two and
+    about 2^(n-1) states would share a walked value; the rounding widens to
+    the small entries' scale (up to 28 bits), the states stay ranked and only a
+    handful are re-evaluated.  Result against the oracle."""
+    n = 24
+    rng = np.random.default_rng(8906)
+    Q = rng.uniform(-1.0, 1.0, size=(n, n)) * 1e-3
+    Q[0, 0] = 1e3
+    Qd = dev_f(Q)
+    announce("f64 one dominant entry")
+    assert q.search_f64(Qd).triple() == oracle.search_direct_f64(Q).triple()
+    assert q.last_timing()["candidates"] < 1000
+    announce("f64 one dominant entry, lowest")
+    assert q.lowest(Qd, 16) == oracle.lowest_f64(Q, 16)
+
+
 def test_zero_and_diagonal(q):
     announce("f64 zero")
     assert q.search_f64(dev_f(np.zeros((8, 8)))).triple() == (0.0, 0, 256)
