@@ -336,16 +336,30 @@ def test_real_full_size_whole_space(q):
     """The whole n = 48 real-valued workload (C4f), checked by what holds at
     any size: the oracle's binary64 energy of the reported minimiser is the
     reported minimum, no single flip of it is lower, and every 32-step body was
-    walked once per column group."""
+    walked once per column group.  And by the oracle on the 2^26-state
+    sub-cube that holds the reported minimiser (its first 22 variables fixed):
+    the definition's minimum, lowest minimiser and count there are the
+    reported ones, and the library's slice search of that sub-cube (the
+    benchmark's split, A = 28) returns them too."""
     cfg = qi.make_config("C4f")
     Q = np.asarray(cfg["Q"], dtype=np.float64)
+    Qd = dev_f(Q)
     announce("f64 C4f whole space")
-    r = q.search_f64(dev_f(Q))
+    r = q.search_f64(Qd)
     check_coverage(q, 48)
     assert r.count >= 1
     assert oracle.energy_f64(Q, r.argmin) == r.min_energy
     flips = np.asarray([r.argmin ^ (1 << k) for k in range(48)], dtype=np.uint64)
     assert (oracle.energies_f64(Q, flips) >= r.min_energy).all()
+    k, free = 22, 26
+    top = r.argmin >> free
+    announce("f64 C4f oracle on the minimiser's sub-cube", top)
+    want = oracle.search_direct_f64(Q, top << free, (top + 1) << free).triple()
+    assert want[:2] == (r.min_energy, r.argmin)
+    A = q.make_plan(48)["prefix_bits"]
+    m = inv_gray(top)
+    sub = q.search_f64(Qd, prefix_bits=A, gray_lo=m << (A - k), gray_hi=(m + 1) << (A - k))
+    assert sub.triple() == want
 
 
 def test_integer_valued_full_size(q):
