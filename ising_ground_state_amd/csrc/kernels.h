@@ -69,9 +69,15 @@ struct SearchArgs {
 // written (j_lo, j_hi multiples of 32; the tables keep their full size).
 // The same launch writes epmin4[k] = min(epmin[4k .. 4k+3]) for the aligned
 // groups of four bodies that hold the slice's bodies (A >= 7).
+// Offsets (zero for eq. 8's own tables): E_s is raised by es_add and the prefix
+// energies lowered by it; the rows of the prefix variables v < offset_rows are
+// raised by K[v] = sum_j max(0, -U[v][A+j]), which U's prefix diagonal must
+// carry lowered by K[v] (the caller's copy of U), so that E_s + the rows of the
+// set prefix variables + E_p stays E(x) for every state.
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
-                               int32_t *es, int32_t *mint, int32_t *ep, int32_t *epmin,
-                               int32_t *epmin4, uint64_t j_lo, uint64_t j_hi, hipStream_t stream);
+                               int offset_rows, int32_t es_add, int32_t *es, int32_t *mint,
+                               int32_t *ep, int32_t *epmin, int32_t *epmin4, uint64_t j_lo,
+                               uint64_t j_hi, hipStream_t stream);
 
 // Resets the work counter, seeds the shared best with t0 (a real energy or an
 // upper bound) and fills the body-minimum table's two padding entries and the

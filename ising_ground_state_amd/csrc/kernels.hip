@@ -113,10 +113,14 @@ __device__ __forceinline__ void wave_combine(int &e, uint64_t &cnt, uint64_t &ar
 // One thread per suffix column c (suffix variable A+i is bit B-1-i of c):
 //   E_s[c]      = sum_{i <= j} U[A+i][A+j] xs_i xs_j            (eq. 8, E_s(U_B))
 //   M_int[v][c] = sum_j U[v][A+j] xs_j, v < A                   (M_int = Q_ps U_B^T)
+// plus the offsets: es_add on E_s, and on the rows of the prefix variables
+// v < offset_rows, K[v] = sum_j max(0, -U[v][A+j]), i.e. each of their terms
+// counts max(U, 0) when x_j = 1 and max(-U, 0) when x_j = 0.
 // Padding columns (c >= 2^B) get E_s = INT_MAX and zero rows, so they never
 // reach any threshold and stay constant under row updates.
 __global__ __launch_bounds__(256) void build_suffix_kernel(const int32_t *__restrict__ U, int ns,
                                                            int A, int B, uint64_t cols_padded,
+                                                           int offset_rows, int32_t es_add,
                                                            int32_t *__restrict__ es,
                                                            int32_t *__restrict__ mint)
 {
@@ -139,12 +143,14 @@ __global__ __launch_bounds__(256) void build_suffix_kernel(const int32_t *__rest
         }
         e += xi ? rowsum : 0;
     }
-    es[c] = e;
+    es[c] = e + es_add;
     for (int v = 0; v < A; ++v) {
+        const bool off = v < offset_rows;
         int m = 0;
         for (int j = 0; j < B; ++j) {
             const int xj = (int)((c >> (B - 1 - j)) & 1u);
-            m += xj ? U[v * ns + (A + j)] : 0;
+            const int u = U[v * ns + (A + j)];
+            m += xj ? (off && u < 0 ? 0 : u) : (off && u < 0 ? -u : 0);
         }
         mint[(uint64_t)v * cols_padded + c] = m;
     }
@@ -162,11 +168,13 @@ __global__ __launch_bounds__(256) void build_suffix_kernel(const int32_t *__rest
 // E_hi is summed in parallel, one high variable per thread, into one of two
 // LDS accumulators that alternate between blocks (each is cleared one block
 // ahead, so a block needs two barriers).  The A x A prefix part of U sits in
-// LDS for the whole launch (A <= 32).
+// LDS for the whole launch (A <= 32).  Every entry is raised by ep_add (the
+// offsets' constant; the rows' offsets reach the prefix energies through U's
+// prefix diagonal, which the caller lowers by K[v]).
 __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *__restrict__ U,
                                                                 int ns, int A, int L,
                                                                 uint64_t blk_first, uint64_t blk_end,
-                                                                int32_t *__restrict__ ep,
+                                                                int32_t ep_add, int32_t *__restrict__ ep,
                                                                 int32_t *__restrict__ epmin)
 {
     __shared__ int K[8];
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *_
         __syncthreads();
         const uint64_t j = (blk << L) | (uint64_t)tid;
         const uint32_t lo = (uint32_t)(gray(j) & ((1u << L) - 1));
-        int e = ehi_acc[it];
+        int e = ep_add + ehi_acc[it];
         for (int a = 0; a < L; ++a) {
             const int xa = (int)((lo >> (L - 1 - a)) & 1u);
             int row = K[a];
@@ -242,12 +250,13 @@ __global__ __launch_bounds__(256) void build_group_min_kernel(const int32_t *__r
 }
 
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
-                               int32_t *es, int32_t *mint, int32_t *ep, int32_t *epmin,
-                               int32_t *epmin4, uint64_t j_lo, uint64_t j_hi, hipStream_t stream)
+                               int offset_rows, int32_t es_add, int32_t *es, int32_t *mint,
+                               int32_t *ep, int32_t *epmin, int32_t *epmin4, uint64_t j_lo,
+                               uint64_t j_hi, hipStream_t stream)
 {
     const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
     hipLaunchKernelGGL(build_suffix_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
-                       cols_padded, es, mint);
+                       cols_padded, offset_rows, es_add, es, mint);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
@@ -262,7 +271,7 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
     if (A > 32)
         return hipErrorInvalidValue;  // (the builder stages at most 32 x 32 entries of U)
     hipLaunchKernelGGL(build_prefix_gray_kernel, dim3((unsigned)grid), dim3(1u << L), 0, stream,
-                       U, ns, A, L, blk_first, blk_end, ep, epmin);
+                       U, ns, A, L, blk_first, blk_end, -es_add, ep, epmin);
     err = hipGetLastError();
     if (err != hipSuccess || A < kU + 2)
         return err;

@@ -21,11 +21,24 @@ constexpr int kQuantBits = 17;
 constexpr int kQuantBitsMax = 28;
 
 // Padding columns of the rounded suffix energies: above every threshold the
-// filter can take (at most 2^(q + 2) + 19 + 2^q + 33 <= 2^30 + 2^28 + 52 after
-// subtracting a prefix energy), so they are never candidates, and the sums the
-// walk and its gates form from them (at most 3 * 2^29 + 2^28 + 33) stay below
-// 2^31.
+// filter can take (at most 2^(q + 2) + 19 + 2^q + 67 <= 2^30 + 2^28 + 86 after
+// subtracting a prefix energy, offsets included), so they are never
+// candidates, and the sums the walk and its gates form from them (at most
+// 3 * 2^29 + 2^28 + 67) stay below 2^31.
 constexpr int32_t kPadQ = 3 << 29;
+
+// Integer offsets of the rounded tables, added after rounding: E_s is raised
+// by es_add, the row of prefix variable v < rows by k[v], and every prefix
+// energy lowered by es_add and by k[v] of its set variables v < rows.  Each
+// state's walked value W(x) is unchanged; the offsets only keep the walked
+// suffix energies at or above zero (the integer search's table offsets, with
+// k[v] >= -min_c of the rounded row and es_add likewise for E_s plus the
+// other rows).  Every k[v] is at most 2^q + 2 and es_add at most 2^q + 16.
+struct TableOffsetsF64 {
+    int32_t rows;
+    int32_t es_add;
+    int32_t k[32];
+};
 
 // One workgroup's partial result (48 bytes).
 struct PartialF64 {
@@ -83,11 +96,12 @@ struct SearchArgsF64 {
 // E_s and M_int per column, E_p(g(j)) for the Gray steps [j_lo, j_hi)
 // (multiples of 32; the tables keep their full size), each sum formed in
 // binary64 and then scaled by `scale` and rounded to the nearest integer once;
-// the per-body and per-group minima of the rounded prefix energies.
+// the per-body and per-group minima of the rounded prefix energies; with the
+// integer offsets `off` added after rounding.
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
-                                   double scale, int32_t *es, int32_t *mint, int32_t *ep,
-                                   int32_t *epmin, int32_t *epmin4, uint64_t j_lo, uint64_t j_hi,
-                                   hipStream_t stream);
+                                   double scale, const TableOffsetsF64 &off, int32_t *es, int32_t *mint,
+                                   int32_t *ep, int32_t *epmin, int32_t *epmin4, uint64_t j_lo,
+                                   uint64_t j_hi, hipStream_t stream);
 
 // Resets the work counter, seeds the shared bound with t0 and fills the
 // padding entries of the body and group minima.

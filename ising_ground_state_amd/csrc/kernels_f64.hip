@@ -144,10 +144,12 @@ __device__ __forceinline__ int32_t round_scaled(double v, double scale)
 
 // One thread per suffix column c (suffix variable A+i is bit B-1-i of c):
 // E_s[c] and the rows M_int[v][c] (eq. 8), as in the integer build but summed
-// in binary64 and rounded.  Padding columns (c >= 2^B) get kPadQ and zero rows.
+// in binary64 and rounded, then offset (E_s by es_add, row v < rows by k[v]).
+// Padding columns (c >= 2^B) get kPadQ and zero rows.
 __global__ __launch_bounds__(256) void build_suffix_f64_kernel(const double *__restrict__ U, int ns,
                                                                int A, int B, uint64_t cols_padded,
-                                                               double scale, int32_t *__restrict__ es,
+                                                               double scale, TableOffsetsF64 off,
+                                                               int32_t *__restrict__ es,
                                                                int32_t *__restrict__ mint)
 {
     const uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -167,13 +169,13 @@ __global__ __launch_bounds__(256) void build_suffix_f64_kernel(const double *__r
             if ((c >> (B - 1 - j)) & 1u)
                 e += U[(A + i) * ns + (A + j)];
     }
-    es[c] = round_scaled(e, scale);
+    es[c] = round_scaled(e, scale) + off.es_add;
     for (int v = 0; v < A; ++v) {
         double m = 0.0;
         for (int j = 0; j < B; ++j)
             if ((c >> (B - 1 - j)) & 1u)
                 m += U[v * ns + (A + j)];
-        mint[(uint64_t)v * cols_padded + c] = round_scaled(m, scale);
+        mint[(uint64_t)v * cols_padded + c] = round_scaled(m, scale) + (v < off.rows ? off.k[v] : 0);
     }
 }
 
@@ -187,19 +189,24 @@ __global__ __launch_bounds__(256) void build_suffix_f64_kernel(const double *__r
 // a block computes K and one row of E_hi per high variable in parallel, and
 // every thread adds the rows in the same order (no floating-point atomics, so
 // the table does not depend on timing).  The order differs from the
-// definition's; the filter's margin covers any order.
+// definition's; the filter's margin covers any order.  The rounded energy is
+// then lowered by es_add and by k[v] of the set variables v < rows.
 __global__ __launch_bounds__(256) void build_prefix_f64_kernel(const double *__restrict__ U, int ns,
                                                                int A, uint64_t j_first, uint64_t j_end,
-                                                               double scale, int32_t *__restrict__ ep,
+                                                               double scale, TableOffsetsF64 off,
+                                                               int32_t *__restrict__ ep,
                                                                int32_t *__restrict__ epmin)
 {
     __shared__ double K[8];
     __shared__ double Upp[32][32];  // the A x A prefix part of U (A <= 32)
     __shared__ double ehi_row[32];  // H = A - 8 <= 24
+    __shared__ int koff[32];        // k[v] for v < rows, else 0
     const int L = A < 8 ? A : 8, H = A - L;
     const int tid = threadIdx.x;
     for (int k = tid; k < A * A; k += blockDim.x)
         Upp[k / A][k % A] = k % A >= k / A ? U[(k / A) * ns + (k % A)] : 0.0;
+    if (tid < 32)
+        koff[tid] = tid < off.rows ? off.k[tid] : 0;
     __syncthreads();
     for (uint64_t j0 = j_first + (uint64_t)blockIdx.x * blockDim.x; j0 < j_end;
          j0 += (uint64_t)gridDim.x * blockDim.x) {
@@ -236,7 +243,11 @@ __global__ __launch_bounds__(256) void build_prefix_f64_kernel(const double *__r
                         row += Upp[H + a][H + b];
                 e += row;
             }
-            m = round_scaled(e, scale);
+            const uint64_t gj = gray(j);  // prefix variable v is bit A-1-v
+            int koff_sum = off.es_add;
+            for (int v = 0; v < A; ++v)
+                koff_sum += (int)((gj >> (A - 1 - v)) & 1u) * koff[v];
+            m = round_scaled(e, scale) - koff_sum;
             ep[j] = m;
         }
 #pragma unroll
@@ -665,13 +676,15 @@ __global__ __launch_bounds__(256) void lowest_merge_f64_kernel(const LowEntryF64
 }  // namespace
 
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
-                                   double scale, int32_t *es, int32_t *mint, int32_t *ep,
-                                   int32_t *epmin, int32_t *epmin4, uint64_t j_lo, uint64_t j_hi,
-                                   hipStream_t stream)
+                                   double scale, const TableOffsetsF64 &off, int32_t *es, int32_t *mint,
+                                   int32_t *ep, int32_t *epmin, int32_t *epmin4, uint64_t j_lo,
+                                   uint64_t j_hi, hipStream_t stream)
 {
+    if (off.rows < 0 || off.rows > A || A > 32)
+        return hipErrorInvalidValue;
     const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
     hipLaunchKernelGGL(build_suffix_f64_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
-                       cols_padded, scale, es, mint);
+                       cols_padded, scale, off, es, mint);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
@@ -681,7 +694,7 @@ hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64
     const uint64_t blocks = (j_hi - j_first + 255) / 256;
     const uint64_t grid = blocks < (1ull << 14) ? blocks : (1ull << 14);
     hipLaunchKernelGGL(build_prefix_f64_kernel, dim3((unsigned)grid), dim3(256), 0, stream, U, ns,
-                       A, j_first, j_hi, scale, ep, epmin);
+                       A, j_first, j_hi, scale, off, ep, epmin);
     err = hipGetLastError();
     if (err != hipSuccess || A < kU + 2)
         return err;

@@ -45,6 +45,27 @@ std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_searc
     return P;
 }
 
+TableOffsets table_offsets(const std::vector<int32_t> &U, int ns, int A)
+{
+    TableOffsets t;
+    t.rows = A > kGateBits ? A - kGateBits : 0;
+    t.es_add = 0;
+    t.Uoff = U;
+    for (int v = 0; v < A; ++v) {
+        int64_t k = 0;
+        for (int j = A; j < ns; ++j)
+            k += std::max<int64_t>(0, -(int64_t)U[(size_t)v * ns + j]);
+        if (v < t.rows)
+            t.Uoff[(size_t)v * ns + v] = (int32_t)(U[(size_t)v * ns + v] - k);
+        else
+            t.es_add += k;
+    }
+    for (int i = A; i < ns; ++i)
+        for (int j = i; j < ns; ++j)
+            t.es_add += std::max<int64_t>(0, -(int64_t)U[(size_t)i * ns + j]);
+    return t;
+}
+
 std::vector<int64_t> descent_energies(const std::vector<int32_t> &U, int n, int starts, int fixed,
                                       uint64_t fixed_value)
 {

@@ -11,6 +11,7 @@ namespace qubo {
 
 // Compile-time shape of the search kernel.
 constexpr int kRegBits = 5;        // Gray bits whose M_int rows live in VGPRs
+constexpr int kGateBits = kRegBits + 2;  // and with the pair and group gates' bits: rows the gates read
 constexpr int kDefaultColsPerLane = 8;  // suffix columns per lane (R); 16 is the other build
 constexpr int kWave = 64;                // CDNA wavefront
 constexpr int kWavesPerBlock = 4;        // one wave per SIMD of a CU
@@ -70,6 +71,27 @@ int make_plan(int n, int prefix_bits, int cache_bits, int num_cus, int cols_per_
 // the fixed variables alone.  Writes sum |Usub_ij| to *sub_abs.
 void reduce_fixed(const std::vector<int32_t> &U, int n, int k, uint64_t f,
                   std::vector<int32_t> &Usub, int64_t *c, int64_t *sub_abs);
+
+// Offsets of the search's tables that keep the walked energies E_s(c) + sum of
+// the set prefix variables' rows at or above zero, so the walk's registers
+// never change sign (a sign change switches every high bit of the register; a
+// walk over values of one sign ran the chip at a higher clock).  Rows of the
+// prefix variables v < rows are raised by K[v] = sum_j max(0, -U[v][A+j])
+// (non-negative then), E_s by es_add = sum_{A <= i <= j} max(0, -U_ij) plus the
+// K[v] of the other rows (so E_s plus any of their signed rows stays >= 0),
+// and the prefix energies carry the same amounts lowered: -es_add, and U's
+// prefix diagonal lowered by K[v] for v < rows (Uoff, the builders' copy of U).
+// E(x) = E_s + rows + E_p holds unchanged for every state.  The offset rows are
+// those of the prefix variables outside the last kGateBits, whose rows the
+// bound gates read: moving K[v] between a gate's suffix side and its prefix
+// side inside one gate would loosen its bound; outside they are constant over
+// the gate's steps and cancel.  Every entry stays within sum |U_ij| of zero.
+struct TableOffsets {
+    int rows;
+    int64_t es_add;
+    std::vector<int32_t> Uoff;
+};
+TableOffsets table_offsets(const std::vector<int32_t> &U, int ns, int A);
 
 // Device workspace layout of a plan (byte offsets, all 256-aligned).
 struct Layout {

@@ -321,12 +321,41 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     if (have_cap && cap < t0)
         t0 = cap;
 
+    // Integer offsets that keep the walked suffix energies at or above zero
+    // (the integer search's table offsets, on the rounded tables): each row
+    // entry is rint(s m) with m a binary64 sub-sum of the row's terms, so
+    // rint(s m) >= -(s sum of the row's negative parts) - 1 > -k[v] with k[v] the
+    // ceiling of that scaled sum plus 1 (the sum's own rounding is far below
+    // 1/2); likewise for E_s.  Rows of the last kGateBits prefix variables keep
+    // their signs (the gates read them); their k[v] go to es_add.
+    TableOffsetsF64 off{};
+    off.rows = A > kGateBits ? A - kGateBits : 0;
+    {
+        auto neg_bound = [scale](double neg) { return (int64_t)std::ceil(neg * scale) + 1; };
+        int64_t es_add = 0;
+        double neg = 0.0;
+        for (int i = A; i < ns; ++i)
+            for (int j = i; j < ns; ++j)
+                neg += std::max(0.0, -U[(size_t)i * ns + j]);
+        es_add += neg_bound(neg);
+        for (int v = 0; v < A; ++v) {
+            double nv = 0.0;
+            for (int j = A; j < ns; ++j)
+                nv += std::max(0.0, -U[(size_t)v * ns + j]);
+            const int64_t k = neg_bound(nv);
+            if (v < off.rows)
+                off.k[v] = (int32_t)k;
+            else
+                es_add += k;
+        }
+        off.es_add = (int32_t)es_add;  // at most 8 bounds: s S_walk + 16 <= 2^q + 16
+    }
+
     if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess ||
         hipMemcpyAsync(dU, U.data(), U.size() * 8, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
-    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, scale, des, dmint, dep, depmin, depmin4, lo, hi,
-                                rq.stream) !=
-        hipSuccess)
+    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, scale, off, des, dmint, dep, depmin, depmin4, lo, hi,
+                                rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess ||
         launch_init_ctrl_f64(dctrl, t0, depmin + (1ull << (A - kRegBits)), depmin4 + groups, rq.stream) !=

@@ -111,10 +111,15 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     // Upload, build, search, reduce.
     if (!mark(0))
         return QUBO_EDEVICE;
-    if (hipMemcpyAsync(dU, U.data(), U.size() * 4, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
-        return QUBO_EDEVICE;
-    if (launch_build_tables(dU, ns, A, B, L.cols_padded, des, dmint, dep, depmin, depmin4, lo, hi, rq.stream) !=
+    // The search's tables are offset so that the walked energies keep one sign
+    // (table_offsets); the exported ones are eq. 8's own.
+    const bool offset = rq.mode != Mode::Build;
+    const TableOffsets off = offset ? table_offsets(U, ns, A) : TableOffsets{0, 0, U};
+    if (hipMemcpyAsync(dU, off.Uoff.data(), off.Uoff.size() * 4, hipMemcpyHostToDevice, rq.stream) !=
         hipSuccess)
+        return QUBO_EDEVICE;
+    if (launch_build_tables(dU, ns, A, B, L.cols_padded, off.rows, (int32_t)off.es_add, des, dmint, dep, depmin,
+                            depmin4, lo, hi, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     if (!mark(1))
         return QUBO_EDEVICE;
