@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "walk.h"
+
 namespace qubo {
 
 // One workgroup's partial result (40 bytes) with its coverage counters.
@@ -41,12 +43,18 @@ struct Ctrl {
     uint64_t checked_total;
 };
 
+// Row offsets of the Gray bits t < 7 whose rows the bound gates read (K of
+// prefix variable A-1-t; zero past A, and zero for tables without offsets).
+struct GateOffsets {
+    int32_t k[8];
+};
+
 struct SearchArgs {
     const int32_t *es;      // [cols_padded]       suffix energies E_s(c)
     const int32_t *mint;    // [A][cols_padded]    M_int rows by prefix variable
     const int32_t *ep;      // [2^A]               prefix energies in Gray order
     const int32_t *epmin;   // [2^A / 32 + 2]      min of ep over each 32-step body, + 2 padding
-    const int32_t *epmin4;  // [2^A / 128 + 1]     min of epmin over each aligned group of 4 bodies, + 1 padding
+    const int32_t *gates;   // [gate_lane_bounds_at(A) + 6 cols_padded / R]  the gates' table (walk.h)
     Partial *partials;      // [gridDim.x]: one per workgroup
     Ctrl *ctrl;
     LowEntry *lists;        // [gridDim.x * waves per block][k_low] (spectrum search only)
@@ -66,23 +74,47 @@ struct SearchArgs {
 // Cache builder (Maltsev et al., sec. III.A preprocessing, eq. 8): E_s, M_int
 // and the Gray-ordered prefix energies, from the folded upper-triangular U.
 // Only the prefix energies a search of the Gray steps [j_lo, j_hi) reads are
-// written (j_lo, j_hi multiples of 32; the tables keep their full size).
-// The same launch writes epmin4[k] = min(epmin[4k .. 4k+3]) for the aligned
-// groups of four bodies that hold the slice's bodies (A >= 7).
+// written (j_lo, j_hi multiples of 32; the tables keep their full size),
+// with the minimum of each 32-step body (epmin).
 // Offsets (zero for eq. 8's own tables): E_s is raised by es_add and the prefix
 // energies lowered by it; the rows of the prefix variables v < offset_rows are
 // raised by K[v] = sum_j max(0, -U[v][A+j]), which U's prefix diagonal must
 // carry lowered by K[v] (the caller's copy of U), so that E_s + the rows of the
-// set prefix variables + E_p stays E(x) for every state.
+// set prefix variables + E_p stays E(x) for every state.  kg: the offsets of
+// the rows of Gray bits 0..6 (K[A-1-t]); the body minima epmin are taken
+// relative to each body's first step (walk.h).
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
-                               int offset_rows, int32_t es_add, int32_t *es, int32_t *mint,
-                               int32_t *ep, int32_t *epmin, int32_t *epmin4, uint64_t j_lo,
-                               uint64_t j_hi, hipStream_t stream);
+                               int offset_rows, int32_t es_add, const GateOffsets &kg, int32_t *es,
+                               int32_t *mint, int32_t *ep, int32_t *epmin, uint64_t j_lo, uint64_t j_hi,
+                               hipStream_t stream);
+
+// The gates' table of a search (integer or over rounded tables; layout in
+// walk.h), from its rows and body minima (epmin, relative to each body's first
+// step) for the Gray steps [j_lo, j_hi):
+//   gates[4k]          the group bound of bodies 4k .. 4k+3, relative to the
+//                      group's first step (A >= 7);
+//   gates[4k + 1 + i]  the pair bound of bodies 4k+2i and 4k+2i+1, relative to
+//                      the pair's first step (A >= 6);
+//   then the lane bounds, six rows of 64 per column group (one entry per lane,
+//   R columns each): the bound on the fall of its suffix energies within a body
+//   (bit 4 clear or set at its start), a pair (bit 5) and a group (bit 6), over
+//   the rows less their offsets kg; padding columns count 0.
+// Pairs and groups that straddle the slice's ends get values that are never
+// read; the padding record's group bound is set by the control-block reset.
+hipError_t launch_gate_tables(const int32_t *mint, uint64_t cols_padded, int A, int B, int R,
+                              const GateOffsets &kg, const int32_t *epmin, int32_t *gates, uint64_t j_lo,
+                              uint64_t j_hi, hipStream_t stream);
+
+// Entries of the gates' table of a plan.
+inline uint64_t gate_table_len(int A, uint64_t cols_padded, int R)
+{
+    return gate_lane_bounds_at(A) + 6 * (cols_padded / (uint64_t)R);
+}
 
 // Resets the work counter, seeds the shared best with t0 (a real energy or an
 // upper bound) and fills the body-minimum table's two padding entries and the
-// group-minimum table's one.
-hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int32_t *epmin4_pad,
+// group bound of the gates' table's padding record.
+hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int32_t *gates_pad,
                             hipStream_t stream);
 
 // gated = true skips the per-step minimum of bodies whose lower bound cannot

@@ -170,11 +170,15 @@ __global__ __launch_bounds__(256) void build_suffix_kernel(const int32_t *__rest
 // ahead, so a block needs two barriers).  The A x A prefix part of U sits in
 // LDS for the whole launch (A <= 32).  Every entry is raised by ep_add (the
 // offsets' constant; the rows' offsets reach the prefix energies through U's
-// prefix diagonal, which the caller lowers by K[v]).
+// prefix diagonal, which the caller lowers by K[v]).  With row offsets kg[t] on
+// Gray bits t < 5, epmin[k] is taken relative to the body's first step: the
+// minimum over the body of ep[j] + sum_{t < 5 set in g(j)} kg[t], less that sum
+// at step 32k (only bit 4 can be set there: kg[4] for odd k).
 __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *__restrict__ U,
                                                                 int ns, int A, int L,
                                                                 uint64_t blk_first, uint64_t blk_end,
-                                                                int32_t ep_add, int32_t *__restrict__ ep,
+                                                                int32_t ep_add, GateOffsets kg,
+                                                                int32_t *__restrict__ ep,
                                                                 int32_t *__restrict__ epmin)
 {
     __shared__ int K[8];
@@ -225,34 +229,116 @@ __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *_
         // 32 consecutive j are 32 consecutive lanes of one wave (blocks have 2^L >= 32 threads).
         int m = e;
 #pragma unroll
+        for (int t = 0; t < kU; ++t)
+            m += (int)((lo >> t) & 1u) * kg.k[t];  // Gray bit t of g(j) (t < 5 <= L, or a zero kg past A)
+#pragma unroll
         for (int off = 16; off >= 1; off >>= 1) {
             const int o = __shfl_xor(m, off, 64);
             m = o < m ? o : m;
         }
         if ((tid & 31) == 0)
-            epmin[j >> 5] = m;
+            epmin[j >> 5] = m - (int)((j >> 5) & 1u) * kg.k[kU - 1];
         __syncthreads();  // K and this block's accumulator are rewritten two blocks on
     }
 }
 
-// Minimum of the body minima over each aligned group of four bodies (128 Gray
-// steps): the prefix-energy bound of the search's group gate, one scalar load per
-// group.  Groups that straddle the slice's ends get values that are never read.
+// The offsets of Gray bits 4, 5 and 6 set at the first step of body b:
+// g(32b) has bits 0..3 clear, bit 4 = b0, bit 5 = b0 ^ b1, bit 6 = b1 ^ b2.
+// Unsigned: the gate tables' entries past a slice's ends may be unset.
+__device__ __forceinline__ uint32_t body_start_offset(uint32_t b, const GateOffsets &kg)
+{
+    return (b & 1u) * (uint32_t)kg.k[kU - 1] + ((b ^ (b >> 1)) & 1u) * (uint32_t)kg.k[kU] +
+           (((b >> 1) ^ (b >> 2)) & 1u) * (uint32_t)kg.k[kU + 1];
+}
+
+// Pair bounds: min of the two body minima, each moved from its body's first
+// step to the pair's (+ the offsets set at the body's first step, - those at
+// the pair's: bits 0..4 clear there, bits 5 and 6 as at body 2p).
+__global__ __launch_bounds__(256) void build_pair_min_kernel(const int32_t *__restrict__ epmin,
+                                                             int32_t *__restrict__ gates,
+                                                             uint64_t p_first, uint64_t p_end,
+                                                             GateOffsets kg)
+{
+    const uint64_t p = p_first + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= p_end)
+        return;
+    const uint32_t b = (uint32_t)(2 * p);
+    const uint32_t at0 = body_start_offset(b, kg);
+    const int m0 = (int)((uint32_t)epmin[b] + at0);
+    const int m1 = (int)((uint32_t)epmin[b + 1] + body_start_offset(b + 1, kg));
+    gates[4 * (p >> 1) + 1 + (p & 1)] = (int)((uint32_t)imin(m0, m1) - at0);
+}
+
+// Group bounds: min of the four body minima, each moved to the group's first
+// step (g(128k): bits 0..5 clear, bit 6 = k0).
 __global__ __launch_bounds__(256) void build_group_min_kernel(const int32_t *__restrict__ epmin,
-                                                              int32_t *__restrict__ epmin4,
-                                                              uint64_t k_first, uint64_t k_end)
+                                                              int32_t *__restrict__ gates,
+                                                              uint64_t k_first, uint64_t k_end,
+                                                              GateOffsets kg)
 {
     const uint64_t k = k_first + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= k_end)
         return;
     const int32_t *e = epmin + 4 * k;
-    epmin4[k] = imin(imin(e[0], e[1]), imin(e[2], e[3]));
+    int m = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        m = imin(m, (int)((uint32_t)e[i] + body_start_offset((uint32_t)(4 * k + i), kg)));
+    gates[4 * k] = (int)((uint32_t)m - (uint32_t)(k & 1u) * (uint32_t)kg.k[kU + 1]);
+    gates[4 * k + 3] = 0;
+}
+
+// Lane bounds, one thread per column group g and lane (written as six rows of
+// 64 per column group: s0, s1, p0, p1, q0, q1): over the lane's R
+// columns c = g 64 R + 64 r + lane, with M_t(c) = row of Gray bit t less its
+// offset (0 for padding columns and for bits that A does not have),
+//   b(c) = sum_{t<5} min(0, M_t(c))          fall within a body from bits 0..4 clear,
+//   s0 = min_c b,  s1 = min_c (b - M_4)      bit 4 clear / set at the body's start,
+//   p0 = min_c (b + min(0, M_5)),  p1 = min_c (b - max(0, M_5))      pair, bit 5,
+//   q0, q1: as p0, p1 from b5 = b + min(0, M_5), with M_6              group, bit 6.
+template <int R>
+__global__ __launch_bounds__(256) void build_lane_bounds_kernel(const int32_t *__restrict__ mint,
+                                                                uint64_t cols_padded, int A, int B,
+                                                                GateOffsets kg,
+                                                                int32_t *__restrict__ out)
+{
+    const uint64_t nlb = cols_padded / R;
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nlb)
+        return;
+    const uint64_t g = i / 64, lane = i % 64;
+    const uint64_t col0 = g * 64 * R + lane;
+    int s0 = INT_MAX, s1 = INT_MAX, p0 = INT_MAX, p1 = INT_MAX, q0 = INT_MAX, q1 = INT_MAX;
+    for (int r = 0; r < R; ++r) {
+        const uint64_t c = col0 + 64 * (uint64_t)r;
+        const bool real = c < (1ull << B);
+        int m[kU + 2];
+        for (int t = 0; t < kU + 2; ++t)
+            m[t] = real && t < A ? mint[(uint64_t)(A - 1 - t) * cols_padded + c] - kg.k[t] : 0;
+        int b = 0;
+        for (int t = 0; t < kU; ++t)
+            b += m[t] < 0 ? m[t] : 0;
+        const int b5 = b + (m[kU] < 0 ? m[kU] : 0);
+        s0 = imin(s0, b);
+        s1 = imin(s1, b - m[kU - 1]);
+        p0 = imin(p0, b5);
+        p1 = imin(p1, b - (m[kU] > 0 ? m[kU] : 0));
+        q0 = imin(q0, b5 + (m[kU + 1] < 0 ? m[kU + 1] : 0));
+        q1 = imin(q1, b5 - (m[kU + 1] > 0 ? m[kU + 1] : 0));
+    }
+    int32_t *o = out + g * (6 * 64) + lane;  // column group g: six rows of 64
+    o[0] = s0;
+    o[64] = s1;
+    o[128] = p0;
+    o[192] = p1;
+    o[256] = q0;
+    o[320] = q1;
 }
 
 hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t cols_padded,
-                               int offset_rows, int32_t es_add, int32_t *es, int32_t *mint,
-                               int32_t *ep, int32_t *epmin, int32_t *epmin4, uint64_t j_lo,
-                               uint64_t j_hi, hipStream_t stream)
+                               int offset_rows, int32_t es_add, const GateOffsets &kg, int32_t *es,
+                               int32_t *mint, int32_t *ep, int32_t *epmin, uint64_t j_lo, uint64_t j_hi,
+                               hipStream_t stream)
 {
     const unsigned g1 = (unsigned)((cols_padded + 255) / 256);
     hipLaunchKernelGGL(build_suffix_kernel, dim3(g1), dim3(256), 0, stream, U, ns, A, B,
@@ -271,26 +357,53 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
     if (A > 32)
         return hipErrorInvalidValue;  // (the builder stages at most 32 x 32 entries of U)
     hipLaunchKernelGGL(build_prefix_gray_kernel, dim3((unsigned)grid), dim3(1u << L), 0, stream,
-                       U, ns, A, L, blk_first, blk_end, -es_add, ep, epmin);
+                       U, ns, A, L, blk_first, blk_end, -es_add, kg, ep, epmin);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_tables(const int32_t *mint, uint64_t cols_padded, int A, int B, int R,
+                              const GateOffsets &kg, const int32_t *epmin, int32_t *gates, uint64_t j_lo,
+                              uint64_t j_hi, hipStream_t stream)
+{
+    if ((R != 8 && R != 16) || cols_padded % (64ull * R) != 0 || j_lo >= j_hi || A < kU || A > 32)
+        return hipErrorInvalidValue;
+    const uint64_t nlb = cols_padded / R;
+    const uint64_t g0 = (nlb + 255) / 256;
+    if (g0 > 0xffffffffull)
+        return hipErrorInvalidValue;
+    if (R == 8)
+        hipLaunchKernelGGL(build_lane_bounds_kernel<8>, dim3((unsigned)g0), dim3(256), 0, stream, mint,
+                           cols_padded, A, B, kg, gates + gate_lane_bounds_at(A));
+    else
+        hipLaunchKernelGGL(build_lane_bounds_kernel<16>, dim3((unsigned)g0), dim3(256), 0, stream, mint,
+                           cols_padded, A, B, kg, gates + gate_lane_bounds_at(A));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || A < kU + 1)
+        return err;
+    // pairs and groups of bodies holding the slice's bodies
+    const uint64_t p_first = j_lo >> (kU + 1), p_end = ((j_hi - 1) >> (kU + 1)) + 1;
+    const uint64_t g2 = (p_end - p_first + 255) / 256;
+    if (g2 > 0xffffffffull)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(build_pair_min_kernel, dim3((unsigned)g2), dim3(256), 0, stream, epmin, gates,
+                       p_first, p_end, kg);
     err = hipGetLastError();
     if (err != hipSuccess || A < kU + 2)
         return err;
-    // groups of four bodies holding the slice's bodies (their epmin entries lie
-    // inside the prefix blocks just written: blocks span 2^L >= 128 steps)
     const uint64_t k_first = j_lo >> (kU + 2), k_end = ((j_hi - 1) >> (kU + 2)) + 1;
     const uint64_t g3 = (k_end - k_first + 255) / 256;
     if (g3 > 0xffffffffull)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(build_group_min_kernel, dim3((unsigned)g3), dim3(256), 0, stream, epmin, epmin4,
-                       k_first, k_end);
+    hipLaunchKernelGGL(build_group_min_kernel, dim3((unsigned)g3), dim3(256), 0, stream, epmin, gates,
+                       k_first, k_end, kg);
     return hipGetLastError();
 }
 
-__global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int32_t *epmin4_pad)
+__global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int32_t *gates_pad)
 {
     epmin_pad[0] = INT_MAX;  // read ahead by the last two bodies of the walk, never used
     epmin_pad[1] = INT_MAX;
-    epmin4_pad[0] = INT_MAX;  // read ahead by the walk's last group, never used
+    gates_pad[0] = INT_MAX;  // group bound read ahead by the walk's last group, never used
     ctrl->counter = 0;
     ctrl->gbest = t0;
     ctrl->slow_total = 0;
@@ -298,10 +411,10 @@ __global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int
     ctrl->checked_total = 0;
 }
 
-hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int32_t *epmin4_pad,
+hipError_t launch_init_ctrl(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int32_t *gates_pad,
                             hipStream_t stream)
 {
-    hipLaunchKernelGGL(init_ctrl_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0, epmin_pad, epmin4_pad);
+    hipLaunchKernelGGL(init_ctrl_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0, epmin_pad, gates_pad);
     return hipGetLastError();
 }
 

@@ -24,20 +24,24 @@ constexpr int kQuantBitsMax = 28;
 // filter can take (at most 2^(q + 2) + 19 + 2^q + 67 <= 2^30 + 2^28 + 86 after
 // subtracting a prefix energy, offsets included), so they are never
 // candidates, and the sums the walk and its gates form from them (at most
-// 3 * 2^29 + 2^28 + 67) stay below 2^31.
+// 3 * 2^29 + 2^28 + 67) stay below 2^31.  (A prefix energy with its offsets is
+// at least -(s S + 2 A + 3): the rounded energy and the at most A + 1 offset
+// bounds, each the ceiling of s times a part of S plus 1.)
 constexpr int32_t kPadQ = 3 << 29;
 
 // Integer offsets of the rounded tables, added after rounding: E_s is raised
 // by es_add, the row of prefix variable v < rows by k[v], and every prefix
 // energy lowered by es_add and by k[v] of its set variables v < rows.  Each
-// state's walked value W(x) is unchanged; the offsets only keep the walked
-// suffix energies at or above zero (the integer search's table offsets, with
-// k[v] >= -min_c of the rounded row and es_add likewise for E_s plus the
-// other rows).  Every k[v] is at most 2^q + 2 and es_add at most 2^q + 16.
+// state's walked value W(x) is unchanged; the offsets only keep the rows and
+// the walked suffix energies at or above zero (the integer search's table
+// offsets, with k[v] >= -min_c of the rounded row and es_add >= -min_c of the
+// rounded E_s).  Every k[v] and es_add is at most 2^q + 2.  kgate[t] = k[A-1-t]
+// for the Gray bits t < 7 (zero past A): the gates' share (walk.h).
 struct TableOffsetsF64 {
     int32_t rows;
     int32_t es_add;
     int32_t k[32];
+    int32_t kgate[8];
 };
 
 // One workgroup's partial result (48 bytes).
@@ -72,7 +76,7 @@ struct SearchArgsF64 {
     const int32_t *mint;    // [A][cols_padded]    rint(s M_int) rows by prefix variable
     const int32_t *ep;      // [2^A]               rint(s E_p(g(j)))
     const int32_t *epmin;   // [2^A / 32 + 2]      min of ep over each 32-step body, + 2 padding
-    const int32_t *epmin4;  // [2^A / 128 + 1]     min of epmin over each aligned group of 4 bodies, + 1 padding
+    const int32_t *gates;   // [gate_lane_bounds_at(A) + 6 cols_padded / 8]  the gates' table (walk.h)
     const double *Q;        // [n][n]              the caller's matrix (the definition's terms)
     PartialF64 *partials;   // [gridDim.x]: one per workgroup
     CtrlF64 *ctrl;
@@ -96,16 +100,17 @@ struct SearchArgsF64 {
 // E_s and M_int per column, E_p(g(j)) for the Gray steps [j_lo, j_hi)
 // (multiples of 32; the tables keep their full size), each sum formed in
 // binary64 and then scaled by `scale` and rounded to the nearest integer once;
-// the per-body and per-group minima of the rounded prefix energies; with the
-// integer offsets `off` added after rounding.
+// the per-body minima of the rounded prefix energies (relative to each body's
+// first step); with the integer offsets `off` added after rounding.  The
+// gates' other tables come from launch_gate_tables (kernels.h).
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
                                    double scale, const TableOffsetsF64 &off, int32_t *es, int32_t *mint,
-                                   int32_t *ep, int32_t *epmin, int32_t *epmin4, uint64_t j_lo,
-                                   uint64_t j_hi, hipStream_t stream);
+                                   int32_t *ep, int32_t *epmin, uint64_t j_lo, uint64_t j_hi,
+                                   hipStream_t stream);
 
 // Resets the work counter, seeds the shared bound with t0 and fills the
 // padding entries of the body and group minima.
-hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, int32_t *epmin_pad, int32_t *epmin4_pad,
+hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, int32_t *epmin_pad, int32_t *gates_pad,
                                 hipStream_t stream);
 
 // lowest: the k-lowest search (each wave keeps its k lowest states in

@@ -190,7 +190,10 @@ __global__ __launch_bounds__(256) void build_suffix_f64_kernel(const double *__r
 // every thread adds the rows in the same order (no floating-point atomics, so
 // the table does not depend on timing).  The order differs from the
 // definition's; the filter's margin covers any order.  The rounded energy is
-// then lowered by es_add and by k[v] of the set variables v < rows.
+// then lowered by es_add and by k[v] of the set variables v < rows; the body
+// minima are taken relative to the body's first step as in the integer build
+// (min over the body of ep + the gate offsets of its set Gray bits t < 5, less
+// those at step 32k: kgate[4] for odd k).
 __global__ __launch_bounds__(256) void build_prefix_f64_kernel(const double *__restrict__ U, int ns,
                                                                int A, uint64_t j_first, uint64_t j_end,
                                                                double scale, TableOffsetsF64 off,
@@ -249,35 +252,24 @@ __global__ __launch_bounds__(256) void build_prefix_f64_kernel(const double *__r
                 koff_sum += (int)((gj >> (A - 1 - v)) & 1u) * koff[v];
             m = round_scaled(e, scale) - koff_sum;
             ep[j] = m;
+#pragma unroll
+            for (int t = 0; t < kU; ++t)
+                m += (int)((gj >> t) & 1u) * off.kgate[t];
         }
 #pragma unroll
-        for (int off = 16; off >= 1; off >>= 1)
-            m = imin(m, __shfl_xor(m, off, 64));
+        for (int o = 16; o >= 1; o >>= 1)
+            m = imin(m, __shfl_xor(m, o, 64));
         if (j < j_end && (j & 31) == 0)
-            epmin[j >> 5] = m;
+            epmin[j >> 5] = m - (int)((j >> 5) & 1u) * off.kgate[kU - 1];
         __syncthreads();  // K and ehi_row are rewritten by the next block
     }
 }
 
-// The group gate's prefix bound: the minimum of the body minima over each
-// aligned group of four bodies.  Groups that straddle the slice's ends get
-// values that are never read.
-__global__ __launch_bounds__(256) void build_group_min_f64_kernel(const int32_t *__restrict__ epmin,
-                                                                  int32_t *__restrict__ epmin4,
-                                                                  uint64_t k_first, uint64_t k_end)
-{
-    const uint64_t k = k_first + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= k_end)
-        return;
-    const int32_t *e = epmin + 4 * k;
-    epmin4[k] = imin(imin(e[0], e[1]), imin(e[2], e[3]));
-}
-
-__global__ void init_ctrl_f64_kernel(CtrlF64 *ctrl, double t0, int32_t *epmin_pad, int32_t *epmin4_pad)
+__global__ void init_ctrl_f64_kernel(CtrlF64 *ctrl, double t0, int32_t *epmin_pad, int32_t *gates_pad)
 {
     epmin_pad[0] = INT_MAX;  // read ahead by the last two bodies of the walk, never used
     epmin_pad[1] = INT_MAX;
-    epmin4_pad[0] = INT_MAX;  // read ahead by the walk's last group, never used
+    gates_pad[0] = INT_MAX;  // group bound read ahead by the walk's last group, never used
     ctrl->counter = 0;
     ctrl->gbest = order_key(t0);
     ctrl->slow_total = 0;
@@ -677,8 +669,8 @@ __global__ __launch_bounds__(256) void lowest_merge_f64_kernel(const LowEntryF64
 
 hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64_t cols_padded,
                                    double scale, const TableOffsetsF64 &off, int32_t *es, int32_t *mint,
-                                   int32_t *ep, int32_t *epmin, int32_t *epmin4, uint64_t j_lo,
-                                   uint64_t j_hi, hipStream_t stream)
+                                   int32_t *ep, int32_t *epmin, uint64_t j_lo, uint64_t j_hi,
+                                   hipStream_t stream)
 {
     if (off.rows < 0 || off.rows > A || A > 32)
         return hipErrorInvalidValue;
@@ -695,24 +687,13 @@ hipError_t launch_build_tables_f64(const double *U, int ns, int A, int B, uint64
     const uint64_t grid = blocks < (1ull << 14) ? blocks : (1ull << 14);
     hipLaunchKernelGGL(build_prefix_f64_kernel, dim3((unsigned)grid), dim3(256), 0, stream, U, ns,
                        A, j_first, j_hi, scale, off, ep, epmin);
-    err = hipGetLastError();
-    if (err != hipSuccess || A < kU + 2)
-        return err;
-    // groups of four bodies holding the slice's bodies (inside the 256-step
-    // blocks the prefix builder just wrote)
-    const uint64_t k_first = j_lo >> (kU + 2), k_end = ((j_hi - 1) >> (kU + 2)) + 1;
-    const uint64_t g3 = (k_end - k_first + 255) / 256;
-    if (g3 > 0xffffffffull)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL(build_group_min_f64_kernel, dim3((unsigned)g3), dim3(256), 0, stream, epmin, epmin4,
-                       k_first, k_end);
     return hipGetLastError();
 }
 
-hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, int32_t *epmin_pad, int32_t *epmin4_pad,
+hipError_t launch_init_ctrl_f64(CtrlF64 *ctrl, double t0, int32_t *epmin_pad, int32_t *gates_pad,
                                 hipStream_t stream)
 {
-    hipLaunchKernelGGL(init_ctrl_f64_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0, epmin_pad, epmin4_pad);
+    hipLaunchKernelGGL(init_ctrl_f64_kernel, dim3(1), dim3(1), 0, stream, ctrl, t0, epmin_pad, gates_pad);
     return hipGetLastError();
 }
 

@@ -48,17 +48,19 @@ std::vector<int32_t> pad_upper(const std::vector<int32_t> &U, int n, int n_searc
 TableOffsets table_offsets(const std::vector<int32_t> &U, int ns, int A)
 {
     TableOffsets t;
-    t.rows = A > kGateBits ? A - kGateBits : 0;
+    t.rows = A;
     t.es_add = 0;
     t.Uoff = U;
+    for (int g = 0; g < 8; ++g)
+        t.kgate[g] = 0;
     for (int v = 0; v < A; ++v) {
         int64_t k = 0;
         for (int j = A; j < ns; ++j)
             k += std::max<int64_t>(0, -(int64_t)U[(size_t)v * ns + j]);
-        if (v < t.rows)
-            t.Uoff[(size_t)v * ns + v] = (int32_t)(U[(size_t)v * ns + v] - k);
-        else
-            t.es_add += k;
+        t.Uoff[(size_t)v * ns + v] = (int32_t)(U[(size_t)v * ns + v] - k);
+        const int bit = A - 1 - v;  // the Gray bit of variable v
+        if (bit < kGateBits)
+            t.kgate[bit] = (int32_t)k;
     }
     for (int i = A; i < ns; ++i)
         for (int j = i; j < ns; ++j)
@@ -324,8 +326,12 @@ Layout layout_of(const qubo_plan &p)
     off = align256(off + (1ull << p.prefix_bits) * 4);
     L.off_epmin = off;
     off = align256(off + ((1ull << (p.prefix_bits - kRegBits)) + 2) * 4);  // + 2 padding entries
-    L.off_epmin4 = off;  // per aligned group of four bodies, + 1 padding entry
-    off = align256(off + ((p.prefix_bits > kRegBits + 2 ? 1ull << (p.prefix_bits - kRegBits - 2) : 1ull) + 1) * 4);
+    // The gates' table: a record of four entries per aligned group of four
+    // bodies and a padding record, then six lane-bound tables of one entry per
+    // column group and lane.
+    L.off_gates = off;
+    const uint64_t groups = p.prefix_bits > kRegBits + 2 ? 1ull << (p.prefix_bits - kRegBits - 2) : 1ull;
+    off = align256(off + (4 * (groups + 1) + 6 * (L.cols_padded / p.cols_per_lane)) * 4);
     L.off_partials = off;
     off = align256(off + (uint64_t)p.blocks * 64);  // one partial (at most 64 bytes) per workgroup
     L.off_ctrl = off;

@@ -73,30 +73,29 @@ void reduce_fixed(const std::vector<int32_t> &U, int n, int k, uint64_t f,
                   std::vector<int32_t> &Usub, int64_t *c, int64_t *sub_abs);
 
 // Offsets of the search's tables that keep the walked energies E_s(c) + sum of
-// the set prefix variables' rows at or above zero, so the walk's registers
-// never change sign (a sign change switches every high bit of the register; a
-// walk over values of one sign ran the chip at a higher clock).  Rows of the
-// prefix variables v < rows are raised by K[v] = sum_j max(0, -U[v][A+j])
-// (non-negative then), E_s by es_add = sum_{A <= i <= j} max(0, -U_ij) plus the
-// K[v] of the other rows (so E_s plus any of their signed rows stays >= 0),
-// and the prefix energies carry the same amounts lowered: -es_add, and U's
-// prefix diagonal lowered by K[v] for v < rows (Uoff, the builders' copy of U).
-// E(x) = E_s + rows + E_p holds unchanged for every state.  The offset rows are
-// those of the prefix variables outside the last kGateBits, whose rows the
-// bound gates read: moving K[v] between a gate's suffix side and its prefix
-// side inside one gate would loosen its bound; outside they are constant over
-// the gate's steps and cancel.  Every entry stays within sum |U_ij| of zero.
+// the set prefix variables' rows, and every row, at or above zero, so that the
+// walk's registers and the rows it adds never change sign (a register that
+// crosses zero switches all of its high bits, and so does the operand path
+// between rows of either sign; a walk over values of one sign ran the chip at a
+// higher clock).  Each row v < A is raised by K[v] = sum_j max(0, -U[v][A+j]),
+// E_s by es_add = sum_{A <= i <= j} max(0, -U_ij), and the prefix energies carry
+// the same amounts lowered: -es_add, and U's prefix diagonal lowered by K[v]
+// (Uoff, the builders' copy of U).  E(x) = E_s + rows + E_p holds unchanged for
+// every state, and every entry stays within sum |U_ij| of zero.  kgate: K of the
+// rows of Gray bits 0..6 (variable A-1-t), which the bound gates take off their
+// rows and out of their prefix minima (walk.h).
 struct TableOffsets {
     int rows;
     int64_t es_add;
     std::vector<int32_t> Uoff;
+    int32_t kgate[8];
 };
 TableOffsets table_offsets(const std::vector<int32_t> &U, int ns, int A);
 
 // Device workspace layout of a plan (byte offsets, all 256-aligned).
 struct Layout {
     uint64_t cols_padded;  // 2^B rounded up to a multiple of the column-group size
-    uint64_t off_u, off_es, off_mint, off_ep, off_epmin, off_epmin4, off_partials, off_ctrl;
+    uint64_t off_u, off_es, off_mint, off_ep, off_epmin, off_gates, off_partials, off_ctrl;
     uint64_t total;
 };
 Layout layout_of(const qubo_plan &p);

@@ -264,8 +264,8 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     const uint64_t off_ep = al(off_mint + (uint64_t)A * cols_padded * 4);
     const uint64_t off_epmin = al(off_ep + (1ull << A) * 4);
     const uint64_t groups = A > kRegBits + 2 ? 1ull << (A - kRegBits - 2) : 1ull;
-    const uint64_t off_epmin4 = al(off_epmin + ((1ull << (A - kRegBits)) + 2) * 4);
-    const uint64_t off_part = al(off_epmin4 + (groups + 1) * 4);
+    const uint64_t off_gates = al(off_epmin + ((1ull << (A - kRegBits)) + 2) * 4);
+    const uint64_t off_part = al(off_gates + gate_table_len(A, cols_padded, kColsPerLaneF64) * 4);
     const uint64_t off_ctrl = al(off_part + (uint64_t)blocks * sizeof(PartialF64));  // one per workgroup
     // the k-lowest search: the per-wave lists, the merged list and its length
     const uint64_t list_entries = lowest ? (uint64_t)blocks * kWavesPerBlock * rq.lowest_k : 0;
@@ -285,7 +285,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     int32_t *dmint = reinterpret_cast<int32_t *>(base + off_mint);
     int32_t *dep = reinterpret_cast<int32_t *>(base + off_ep);
     int32_t *depmin = reinterpret_cast<int32_t *>(base + off_epmin);
-    int32_t *depmin4 = reinterpret_cast<int32_t *>(base + off_epmin4);
+    int32_t *dgates = reinterpret_cast<int32_t *>(base + off_gates);
     PartialF64 *dpart = reinterpret_cast<PartialF64 *>(base + off_part);
     CtrlF64 *dctrl = reinterpret_cast<CtrlF64 *>(base + off_ctrl);
     if (!call.create_events())
@@ -321,44 +321,43 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     if (have_cap && cap < t0)
         t0 = cap;
 
-    // Integer offsets that keep the walked suffix energies at or above zero
-    // (the integer search's table offsets, on the rounded tables): each row
-    // entry is rint(s m) with m a binary64 sub-sum of the row's terms, so
-    // rint(s m) >= -(s sum of the row's negative parts) - 1 > -k[v] with k[v] the
-    // ceiling of that scaled sum plus 1 (the sum's own rounding is far below
-    // 1/2); likewise for E_s.  Rows of the last kGateBits prefix variables keep
-    // their signs (the gates read them); their k[v] go to es_add.
+    // Integer offsets that keep the rows and the walked suffix energies at or
+    // above zero (the integer search's table offsets, on the rounded tables):
+    // each row entry is rint(s m) with m a binary64 sub-sum of the row's terms,
+    // so rint(s m) >= -(s sum of the row's negative parts) - 1 > -k[v] with k[v]
+    // the ceiling of that scaled sum plus 1 (the sum's own rounding is far below
+    // 1/2); likewise es_add for E_s.
     TableOffsetsF64 off{};
-    off.rows = A > kGateBits ? A - kGateBits : 0;
+    off.rows = A;
     {
-        auto neg_bound = [scale](double neg) { return (int64_t)std::ceil(neg * scale) + 1; };
-        int64_t es_add = 0;
+        auto neg_bound = [scale](double neg) { return (int32_t)std::ceil(neg * scale) + 1; };
         double neg = 0.0;
         for (int i = A; i < ns; ++i)
             for (int j = i; j < ns; ++j)
                 neg += std::max(0.0, -U[(size_t)i * ns + j]);
-        es_add += neg_bound(neg);
+        off.es_add = neg_bound(neg);
         for (int v = 0; v < A; ++v) {
             double nv = 0.0;
             for (int j = A; j < ns; ++j)
                 nv += std::max(0.0, -U[(size_t)v * ns + j]);
-            const int64_t k = neg_bound(nv);
-            if (v < off.rows)
-                off.k[v] = (int32_t)k;
-            else
-                es_add += k;
+            off.k[v] = neg_bound(nv);
+            if (A - 1 - v < kGateBits)
+                off.kgate[A - 1 - v] = off.k[v];
         }
-        off.es_add = (int32_t)es_add;  // at most 8 bounds: s S_walk + 16 <= 2^q + 16
     }
 
     if (hipEventRecord(call.ev[0], rq.stream) != hipSuccess ||
         hipMemcpyAsync(dU, U.data(), U.size() * 8, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
-    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, scale, off, des, dmint, dep, depmin, depmin4, lo, hi,
-                                rq.stream) != hipSuccess)
+    GateOffsets kg;
+    std::copy(off.kgate, off.kgate + 8, kg.k);
+    if (launch_build_tables_f64(dU, ns, A, B, cols_padded, scale, off, des, dmint, dep, depmin, lo, hi,
+                                rq.stream) != hipSuccess ||
+        launch_gate_tables(dmint, cols_padded, A, B, kColsPerLaneF64, kg, depmin, dgates, lo, hi, rq.stream) !=
+            hipSuccess)
         return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess ||
-        launch_init_ctrl_f64(dctrl, t0, depmin + (1ull << (A - kRegBits)), depmin4 + groups, rq.stream) !=
+        launch_init_ctrl_f64(dctrl, t0, depmin + (1ull << (A - kRegBits)), dgates + 4 * groups, rq.stream) !=
             hipSuccess)
         return QUBO_EDEVICE;
     SearchArgsF64 sa{};
@@ -366,7 +365,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
     sa.mint = dmint;
     sa.ep = dep;
     sa.epmin = depmin;
-    sa.epmin4 = depmin4;
+    sa.gates = dgates;
     sa.Q = rq.Q;
     sa.partials = dpart;
     sa.ctrl = dctrl;

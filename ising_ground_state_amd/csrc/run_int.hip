@@ -98,7 +98,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     int32_t *dmint = reinterpret_cast<int32_t *>(base + L.off_mint);
     int32_t *dep = reinterpret_cast<int32_t *>(base + L.off_ep);
     int32_t *depmin = reinterpret_cast<int32_t *>(base + L.off_epmin);
-    int32_t *depmin4 = reinterpret_cast<int32_t *>(base + L.off_epmin4);
+    int32_t *dgates = reinterpret_cast<int32_t *>(base + L.off_gates);
     Partial *dpart = reinterpret_cast<Partial *>(base + L.off_partials);
     Ctrl *dctrl = reinterpret_cast<Ctrl *>(base + L.off_ctrl);
 
@@ -114,12 +114,17 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     // The search's tables are offset so that the walked energies keep one sign
     // (table_offsets); the exported ones are eq. 8's own.
     const bool offset = rq.mode != Mode::Build;
-    const TableOffsets off = offset ? table_offsets(U, ns, A) : TableOffsets{0, 0, U};
+    const TableOffsets off = offset ? table_offsets(U, ns, A) : TableOffsets{0, 0, U, {}};
+    GateOffsets kg;
+    std::copy(off.kgate, off.kgate + 8, kg.k);
     if (hipMemcpyAsync(dU, off.Uoff.data(), off.Uoff.size() * 4, hipMemcpyHostToDevice, rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;
-    if (launch_build_tables(dU, ns, A, B, L.cols_padded, off.rows, (int32_t)off.es_add, des, dmint, dep, depmin,
-                            depmin4, lo, hi, rq.stream) != hipSuccess)
+    if (launch_build_tables(dU, ns, A, B, L.cols_padded, off.rows, (int32_t)off.es_add, kg, des, dmint, dep,
+                            depmin, lo, hi, rq.stream) != hipSuccess)
+        return QUBO_EDEVICE;
+    if (offset && launch_gate_tables(dmint, L.cols_padded, A, B, plan.cols_per_lane, kg, depmin, dgates, lo, hi,
+                                     rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     if (!mark(1))
         return QUBO_EDEVICE;
@@ -162,7 +167,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     if (have_t0 && t0_cap < t0)
         t0 = t0_cap;
     const uint64_t groups = A > kRegBits + 2 ? 1ull << (A - kRegBits - 2) : 1ull;
-    if (launch_init_ctrl(dctrl, t0, depmin + (1ull << (A - kRegBits)), depmin4 + groups, rq.stream) !=
+    if (launch_init_ctrl(dctrl, t0, depmin + (1ull << (A - kRegBits)), dgates + 4 * groups, rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;
 
@@ -171,7 +176,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     sa.mint = dmint;
     sa.ep = dep;
     sa.epmin = depmin;
-    sa.epmin4 = depmin4;
+    sa.gates = dgates;
     sa.partials = dpart;
     sa.ctrl = dctrl;
     sa.cols_padded = L.cols_padded;

@@ -20,6 +20,16 @@ constexpr int kWaves = 4;    // waves per workgroup
 
 __device__ __forceinline__ uint64_t gray(uint64_t i) { return i ^ (i >> 1); }
 
+// The gates' table of a search (launch_gate_tables): for each aligned group of
+// four bodies (at least one) a record of four entries {group bound, pair bound
+// of bodies 4k and 4k+1, pair bound of 4k+2 and 4k+3, unused}, one padding
+// record, then the lane bounds: per column group, six rows of 64 (one entry per
+// lane).  Entries before the lane bounds:
+__host__ __device__ constexpr uint64_t gate_lane_bounds_at(int A)
+{
+    return 4 * ((A > kU + 2 ? 1ull << (A - kU - 2) : 1ull) + 1);
+}
+
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 
 // Marks a value that is equal in every lane as wave-uniform (kept in SGPRs).
@@ -159,6 +169,17 @@ __device__ __forceinline__ uint64_t checked_body(int (&E)[R], const int (&Mr)[kU
 // the row updates only; otherwise it is walked exactly.  Every state still
 // costs its one add.  Gated = false (strict): every body runs the per-step test
 // of Algorithm 2 and is walked exactly where it hits.
+// The lane bounds depend only on the lane's columns, so the cache builders
+// compute them once per column group and lane (six tables in a.gates: body
+// s = 0 and 1, pair and group for bit 5 or 6 = 0 and 1), and the prefix bounds
+// of a body (epmin), an aligned pair and group (records of a.gates).
+//
+// The tables may carry offsets: the row of Gray bit t is M_t + K_t and the
+// prefix energies carry -K_t for each set bit t, so E and E_p each hold a share
+// of sum_{t set} K_t that cancels in their sum.  The lane bounds are then taken
+// over M_t = row - K_t, and the prefix bounds are, for each body (pair, group),
+// the minimum of E_p + sum_{t < 7 set} K_t over its steps less that sum at its
+// first step: the same bounds as without offsets, with no offset in this loop.
 //
 // The mode provides
 //   int refresh(int T): T lowered to the threshold shared between waves;
@@ -248,44 +269,22 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
         // aligned pair of bodies (64 steps, Gray bits 0..5), for bit 5 = 0 and 1
         // at the pair's start; and within an aligned group of four bodies (128
         // steps, Gray bits 0..6: bits 0..5 start at 0), for bit 6 = 0 and 1 at
-        // the group's start.  The rows of bits 5 and 6 are read here only.
+        // the group's start: per column group and lane, from the builders.
         int beta_s0 = 0, beta_s1 = 0, beta_p0 = 0, beta_p1 = 0, beta_q0 = 0, beta_q1 = 0;
         if (Gated) {
-            beta_s0 = INT_MAX;
-            beta_s1 = INT_MAX;
-            beta_p0 = INT_MAX;
-            beta_p1 = INT_MAX;
-            beta_q0 = INT_MAX;
-            beta_q1 = INT_MAX;
-            // (a bit that A does not have reads row 0, in bounds, and is ignored)
-            const int32_t *row5 = mint + (uint64_t)(A > kU ? A - 1 - kU : 0) * cp + col0;
-            const int32_t *row6 = mint + (uint64_t)(A > kU + 1 ? A - 2 - kU : 0) * cp + col0;
-            // Loaded either way (in bounds) and masked: no branch around the loads.
-            const int has5 = -(int)(A > kU), has6 = -(int)(A > kU + 1);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                int b = 0;
-#pragma unroll
-                for (int t = 0; t < kU; ++t)
-                    b += Mr[t][r] < 0 ? Mr[t][r] : 0;
-                beta_s0 = imin(beta_s0, b);
-                beta_s1 = imin(beta_s1, b - Mr[kU - 1][r]);
-                const int m5 = row5[r * 64] & has5;
-                beta_p0 = imin(beta_p0, b + (m5 < 0 ? m5 : 0));
-                beta_p1 = imin(beta_p1, b - (m5 > 0 ? m5 : 0));
-                const int m6 = row6[r * 64] & has6;
-                const int b5 = b + (m5 < 0 ? m5 : 0);
-                beta_q0 = imin(beta_q0, b5 + (m6 < 0 ? m6 : 0));
-                beta_q1 = imin(beta_q1, b5 - (m6 > 0 ? m6 : 0));
-                // One column at a time: with the sixteen row values loaded up
-                // front and the eight columns summed side by side, this set-up
-                // set the kernel's register count (a wave per SIMD less).
-                asm volatile(""
-                             : "+v"(beta_s0), "+v"(beta_s1), "+v"(beta_p0), "+v"(beta_p1), "+v"(beta_q0),
-                               "+v"(beta_q1)
-                             :
-                             : "memory");
-            }
+            // Column group g's lane bounds: 6 x 64 entries at gate_lane_bounds_at(A)
+            // + 384 g, addressed from col0 = g kGroup + lane (live here already; a
+            // separate lane offset, hoisted out of the unit loop, held two VGPRs
+            // through every body).  The barrier keeps the scalar part here too.
+            int64_t at = (int64_t)gate_lane_bounds_at(A) + (int64_t)g * (6 * 64) - (int64_t)(g * kGroup);
+            asm volatile("" : "+s"(at));
+            const int32_t *lb = a.gates + at + col0;
+            beta_s0 = lb[0];
+            beta_s1 = lb[64];
+            beta_p0 = lb[128];
+            beta_p1 = lb[192];
+            beta_q0 = lb[256];
+            beta_q1 = lb[320];
         }
         T = mode.refresh(T);
 
@@ -299,7 +298,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
         // The group gate's prefix bound comes from the per-group table, read one
         // group ahead (the table has one padding entry past the last group); the
         // body minima are read only where a pair or body gate needs them.
-        int q_next = Gated && A > kU + 1 ? a.epmin4[(b0 + 3) >> 2] : 0;
+        int q_next = Gated && A > kU + 1 ? a.gates[4 * ((b0 + 3) >> 2)] : 0;
         uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
             const uint32_t b = b0 + bi;
@@ -319,7 +318,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                         // The first of four aligned bodies: their 128 states of Gray
                         // bits 0..6 fall by at most beta_q(bit 6 at the group's start).
                         const int q = q_next;
-                        q_next = a.epmin4[(b >> 2) + 1];
+                        q_next = a.gates[4 * ((b >> 2) + 1)];
                         const int thq = T - q;
                         const int bq = emin + (((b >> 2) & 1u) ? beta_q1 : beta_q0);
                         if (__builtin_amdgcn_ballot_w64(bq <= thq) == 0)
@@ -328,11 +327,10 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                     if (covered != 0) {
                         check = false;
                     } else {
-                        const int epm_cur = epmin[b];
                         if (top_plus && !last && A > kU) {
                             // An even body and its partner: the 64 states of Gray bits
                             // 0..5 fall by at most beta_p(bit 5 at the pair's start).
-                            const int thp = T - imin(epm_cur, epmin[b + 1]);
+                            const int thp = T - a.gates[4 * (b >> 2) + 1 + ((b >> 1) & 1u)];
                             const int bp = emin + (((b >> 1) & 1u) ? beta_p1 : beta_p0);
                             if (__builtin_amdgcn_ballot_w64(bp <= thp) == 0)
                                 covered = 1;
@@ -340,7 +338,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                         if (covered != 0) {
                             check = false;
                         } else {
-                            const int thb = T - epm_cur;
+                            const int thb = T - epmin[b];
                             const int bound = emin + (top_plus ? beta_s0 : beta_s1);
                             check = __builtin_amdgcn_ballot_w64(bound <= thb) != 0;
                         }
