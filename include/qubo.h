@@ -21,8 +21,9 @@
  *     (sec. II.B, Fig. 2).  Variable i of the minimiser is (argmin >> (n-1-i)) & 1.
  *   - Overflow guard: the sum over all entries of |Q_ij| must not exceed
  *     2^30 - 1.  Every energy, partial energy and table entry the solver forms is
- *     a signed sub-sum of the folded matrix, and every comparison is between two
- *     such sums, so int32 is then exact everywhere.  (The paper instead bounds
+ *     a sum over distinct entries of the folded matrix, each taken with its sign
+ *     or as its positive or negative part, so at most that sum in magnitude, and
+ *     every comparison is between two such sums, so int32 is then exact everywhere.  (The paper instead bounds
  *     the spectrum with simulated annealing, sec. IV.B.5; this guard is exact.)
  *   - Status codes: 0 on success, a negative QUBO_E* code otherwise.  On error
  *     the output struct is left untouched.

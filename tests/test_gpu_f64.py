@@ -214,18 +214,25 @@ def _real_family(kind, n, rng):
         return u @ u.T * np.pi
     if kind == "heavy-tail":  # Cauchy entries: a few dominate S
         return rng.standard_cauchy(size=(n, n))
+    if kind == "negative":  # every entry <= 0: the tables' offsets are as large as S allows
+        return -rng.uniform(0.0, 1.0, size=(n, n))
+    if kind == "negative-log":  # and over twelve decades: offsets at the widest rounding (28 bits)
+        return -(10.0 ** rng.uniform(-6, 6, size=(n, n)))
     raise KeyError(kind)
 
 
-@pytest.mark.parametrize("kind", ["uniform", "log-uniform", "near-ties", "sparse", "low-rank", "heavy-tail"])
+FAMILIES = ["uniform", "log-uniform", "near-ties", "sparse", "low-rank", "heavy-tail", "negative",
+            "negative-log"]
+
+
+@pytest.mark.parametrize("kind", FAMILIES)
 def test_random_real_families(q, kind):
     """Seeded families of real matrices that stress the rounded walk in
     different ways (entries far below its 17-bit unit, ties broken below the
-    unit, zero rows, near-degenerate spectra, a few dominant entries), at
-    n = 8..16: minimum, lowest index, count and the 8 lowest states against
-    the oracle's binary64 definition."""
-    rng = np.random.default_rng(9900 + ["uniform", "log-uniform", "near-ties", "sparse", "low-rank",
-                                        "heavy-tail"].index(kind))
+    unit, zero rows, near-degenerate spectra, a few dominant entries, entries
+    of one sign), at n = 8..16: minimum, lowest index, count and the 8 lowest
+    states against the oracle's binary64 definition."""
+    rng = np.random.default_rng(9900 + FAMILIES.index(kind))
     for n in (8, 11, 13, 16):
         for rep in range(2):
             Q = _real_family(kind, n, rng)

@@ -159,6 +159,27 @@ def test_extreme_entries(q):
     assert q.search(dev_q(Q), prefix_bits=6, cache_bits=6).triple() == want
 
 
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_extreme_one_signed(q, sign):
+    """Near the overflow guard with every entry of one sign: the search's table
+    offsets (each row and the suffix energies raised by the sum of their
+    negative parts) are then as large as the entries allow (all negative) or
+    zero (all positive).  Padding columns (2^5 columns in a group of 512) and
+    the pair and group gates at several splits, with the strict per-step
+    minimum and 16 columns per lane; the minimum and the 8 lowest."""
+    n = 12
+    big = (2 ** 30 - 1) // (n * n)
+    Q = [[sign * abs(v) for v in row] for row in qi.general_uniform(n, 7202, -big, big)]
+    want = oracle.search_gray(Q).triple()
+    low = oracle.lowest(Q, 8)
+    Qd = dev_q(Q)
+    for A in (None, 6, 7, 9):
+        for strict, R in ((False, 8), (True, 8), (False, 16)):
+            announce("extreme one-signed", sign, A, strict, R)
+            assert q.search(Qd, prefix_bits=A, strict=strict, cols_per_lane=R).triple() == want, (A, strict, R)
+        assert q.lowest(Qd, 8, prefix_bits=A) == low, A
+
+
 # ---------------------------------------------------------------- configs
 
 @pytest.mark.parametrize("name,splits", [
