@@ -91,16 +91,17 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
 // The gates' table of a search (integer or over rounded tables; layout in
 // walk.h), from its rows and body minima (epmin, relative to each body's first
 // step) for the Gray steps [j_lo, j_hi):
-//   gates[4k]          the group bound of bodies 4k .. 4k+3, relative to the
+//   gates[k]           the group bound of bodies 4k .. 4k+3, relative to the
 //                      group's first step (A >= 7);
-//   gates[4k + 1 + i]  the pair bound of bodies 4k+2i and 4k+2i+1, relative to
-//                      the pair's first step (A >= 6);
+//   gates[gate_pairs_at(A) + p]  the pair bound of bodies 2p and 2p+1,
+//                      relative to the pair's first step (A >= 6);
 //   then the lane bounds, six rows of 64 per column group (one entry per lane,
 //   R columns each): the bound on the fall of its suffix energies within a body
 //   (bit 4 clear or set at its start), a pair (bit 5) and a group (bit 6), over
 //   the rows less their offsets kg; padding columns count 0.
 // Pairs and groups that straddle the slice's ends get values that are never
-// read; the padding record's group bound is set by the control-block reset.
+// read; the padding group bound (gates[gate_groups(A)]) is set by the
+// control-block reset.
 hipError_t launch_gate_tables(const int32_t *mint, uint64_t cols_padded, int A, int B, int R,
                               const GateOffsets &kg, const int32_t *epmin, int32_t *gates, uint64_t j_lo,
                               uint64_t j_hi, hipStream_t stream);

@@ -251,11 +251,12 @@ __device__ __forceinline__ uint32_t body_start_offset(uint32_t b, const GateOffs
            (((b >> 1) ^ (b >> 2)) & 1u) * (uint32_t)kg.k[kU + 1];
 }
 
-// Pair bounds: min of the two body minima, each moved from its body's first
-// step to the pair's (+ the offsets set at the body's first step, - those at
-// the pair's: bits 0..4 clear there, bits 5 and 6 as at body 2p).
+// Pair bounds (into the gates' pair table): min of the two body minima, each
+// moved from its body's first step to the pair's (+ the offsets set at the
+// body's first step, - those at the pair's: bits 0..4 clear there, bits 5 and 6
+// as at body 2p).
 __global__ __launch_bounds__(256) void build_pair_min_kernel(const int32_t *__restrict__ epmin,
-                                                             int32_t *__restrict__ gates,
+                                                             int32_t *__restrict__ pairs,
                                                              uint64_t p_first, uint64_t p_end,
                                                              GateOffsets kg)
 {
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(256) void build_pair_min_kernel(const int32_t *__re
     const uint32_t at0 = body_start_offset(b, kg);
     const int m0 = (int)((uint32_t)epmin[b] + at0);
     const int m1 = (int)((uint32_t)epmin[b + 1] + body_start_offset(b + 1, kg));
-    gates[4 * (p >> 1) + 1 + (p & 1)] = (int)((uint32_t)imin(m0, m1) - at0);
+    pairs[p] = (int)((uint32_t)imin(m0, m1) - at0);
 }
 
 // Group bounds: min of the four body minima, each moved to the group's first
@@ -284,8 +285,7 @@ __global__ __launch_bounds__(256) void build_group_min_kernel(const int32_t *__r
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         m = imin(m, (int)((uint32_t)e[i] + body_start_offset((uint32_t)(4 * k + i), kg)));
-    gates[4 * k] = (int)((uint32_t)m - (uint32_t)(k & 1u) * (uint32_t)kg.k[kU + 1]);
-    gates[4 * k + 3] = 0;
+    gates[k] = (int)((uint32_t)m - (uint32_t)(k & 1u) * (uint32_t)kg.k[kU + 1]);
 }
 
 // Lane bounds, one thread per column group g and lane (written as six rows of
@@ -385,8 +385,8 @@ hipError_t launch_gate_tables(const int32_t *mint, uint64_t cols_padded, int A, 
     const uint64_t g2 = (p_end - p_first + 255) / 256;
     if (g2 > 0xffffffffull)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(build_pair_min_kernel, dim3((unsigned)g2), dim3(256), 0, stream, epmin, gates,
-                       p_first, p_end, kg);
+    hipLaunchKernelGGL(build_pair_min_kernel, dim3((unsigned)g2), dim3(256), 0, stream, epmin,
+                       gates + gate_pairs_at(A), p_first, p_end, kg);
     err = hipGetLastError();
     if (err != hipSuccess || A < kU + 2)
         return err;

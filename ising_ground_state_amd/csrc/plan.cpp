@@ -326,12 +326,8 @@ Layout layout_of(const qubo_plan &p)
     off = align256(off + (1ull << p.prefix_bits) * 4);
     L.off_epmin = off;
     off = align256(off + ((1ull << (p.prefix_bits - kRegBits)) + 2) * 4);  // + 2 padding entries
-    // The gates' table: a record of four entries per aligned group of four
-    // bodies and a padding record, then six lane-bound tables of one entry per
-    // column group and lane.
-    L.off_gates = off;
-    const uint64_t groups = p.prefix_bits > kRegBits + 2 ? 1ull << (p.prefix_bits - kRegBits - 2) : 1ull;
-    off = align256(off + (4 * (groups + 1) + 6 * (L.cols_padded / p.cols_per_lane)) * 4);
+    L.off_gates = off;  // the gates' table (plan.h)
+    off = align256(off + (gate_lane_bounds_at(p.prefix_bits) + 6 * (L.cols_padded / p.cols_per_lane)) * 4);
     L.off_partials = off;
     off = align256(off + (uint64_t)p.blocks * 64);  // one partial (at most 64 bytes) per workgroup
     L.off_ctrl = off;

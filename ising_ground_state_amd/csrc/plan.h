@@ -27,6 +27,16 @@ constexpr int kMinSegBitsIdle = 10;      // or 2^10 when longer units would leav
 
 constexpr int64_t kAbsSumLimit = (1ll << 30) - 1;
 
+// The gates' table of a search (built by launch_gate_tables, read by the walk):
+// the group bound of each aligned group of four 32-step bodies (at least one)
+// and a padding entry; from gate_pairs_at(A) the pair bound of each aligned
+// pair of bodies; from gate_lane_bounds_at(A) the lane bounds, per column group
+// six rows of 64 (one entry per lane).  The group bounds, read once per group,
+// stay 4 bytes apart.
+constexpr uint64_t gate_groups(int A) { return A > kRegBits + 2 ? 1ull << (A - kRegBits - 2) : 1ull; }
+constexpr uint64_t gate_pairs_at(int A) { return gate_groups(A) + 1; }
+constexpr uint64_t gate_lane_bounds_at(int A) { return (gate_pairs_at(A) + 2 * gate_groups(A) + 63) & ~63ull; }
+
 // Folds a full n x n matrix into the upper triangle U (U_ii = Q_ii,
 // U_ij = Q_ij + Q_ji for i < j, 0 below), so x^T Q x = x^T U x, after checking
 // sum |Q_ij| <= 2^30 - 1.  Returns QUBO_OK or QUBO_ERANGE; writes the sum.

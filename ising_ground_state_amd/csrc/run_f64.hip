@@ -357,7 +357,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
             hipSuccess)
         return QUBO_EDEVICE;
     if (hipEventRecord(call.ev[1], rq.stream) != hipSuccess ||
-        launch_init_ctrl_f64(dctrl, t0, depmin + (1ull << (A - kRegBits)), dgates + 4 * groups, rq.stream) !=
+        launch_init_ctrl_f64(dctrl, t0, depmin + (1ull << (A - kRegBits)), dgates + gate_groups(A), rq.stream) !=
             hipSuccess)
         return QUBO_EDEVICE;
     SearchArgsF64 sa{};

@@ -167,7 +167,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     if (have_t0 && t0_cap < t0)
         t0 = t0_cap;
     const uint64_t groups = A > kRegBits + 2 ? 1ull << (A - kRegBits - 2) : 1ull;
-    if (launch_init_ctrl(dctrl, t0, depmin + (1ull << (A - kRegBits)), dgates + 4 * groups, rq.stream) !=
+    if (launch_init_ctrl(dctrl, t0, depmin + (1ull << (A - kRegBits)), dgates + gate_groups(A), rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;
 

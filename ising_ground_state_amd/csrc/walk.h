@@ -12,23 +12,15 @@
 #include <climits>
 #include <cstdint>
 
+#include "plan.h"  // kRegBits, the gates' table layout
+
 namespace qubo {
 
-constexpr int kU = 5;        // Gray bits with rows in VGPRs
+constexpr int kU = kRegBits;  // Gray bits with rows in VGPRs
 constexpr int kBody = 1 << kU;
 constexpr int kWaves = 4;    // waves per workgroup
 
 __device__ __forceinline__ uint64_t gray(uint64_t i) { return i ^ (i >> 1); }
-
-// The gates' table of a search (launch_gate_tables): for each aligned group of
-// four bodies (at least one) a record of four entries {group bound, pair bound
-// of bodies 4k and 4k+1, pair bound of 4k+2 and 4k+3, unused}, one padding
-// record, then the lane bounds: per column group, six rows of 64 (one entry per
-// lane).  Entries before the lane bounds:
-__host__ __device__ constexpr uint64_t gate_lane_bounds_at(int A)
-{
-    return 4 * ((A > kU + 2 ? 1ull << (A - kU - 2) : 1ull) + 1);
-}
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 
@@ -170,9 +162,9 @@ __device__ __forceinline__ uint64_t checked_body(int (&E)[R], const int (&Mr)[kU
 // costs its one add.  Gated = false (strict): every body runs the per-step test
 // of Algorithm 2 and is walked exactly where it hits.
 // The lane bounds depend only on the lane's columns, so the cache builders
-// compute them once per column group and lane (six tables in a.gates: body
+// compute them once per column group and lane (six rows in a.gates: body
 // s = 0 and 1, pair and group for bit 5 or 6 = 0 and 1), and the prefix bounds
-// of a body (epmin), an aligned pair and group (records of a.gates).
+// of a body (epmin), an aligned pair and group (a.gates).
 //
 // The tables may carry offsets: the row of Gray bit t is M_t + K_t and the
 // prefix energies carry -K_t for each set bit t, so E and E_p each hold a share
@@ -298,7 +290,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
         // The group gate's prefix bound comes from the per-group table, read one
         // group ahead (the table has one padding entry past the last group); the
         // body minima are read only where a pair or body gate needs them.
-        int q_next = Gated && A > kU + 1 ? a.gates[4 * ((b0 + 3) >> 2)] : 0;
+        int q_next = Gated && A > kU + 1 ? a.gates[(b0 + 3) >> 2] : 0;
         uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
             const uint32_t b = b0 + bi;
@@ -318,7 +310,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                         // The first of four aligned bodies: their 128 states of Gray
                         // bits 0..6 fall by at most beta_q(bit 6 at the group's start).
                         const int q = q_next;
-                        q_next = a.gates[4 * ((b >> 2) + 1)];
+                        q_next = a.gates[(b >> 2) + 1];
                         const int thq = T - q;
                         const int bq = emin + (((b >> 2) & 1u) ? beta_q1 : beta_q0);
                         if (__builtin_amdgcn_ballot_w64(bq <= thq) == 0)
@@ -330,7 +322,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                         if (top_plus && !last && A > kU) {
                             // An even body and its partner: the 64 states of Gray bits
                             // 0..5 fall by at most beta_p(bit 5 at the pair's start).
-                            const int thp = T - a.gates[4 * (b >> 2) + 1 + ((b >> 1) & 1u)];
+                            const int thp = T - a.gates[gate_pairs_at(A) + (b >> 1)];
                             const int bp = emin + (((b >> 1) & 1u) ? beta_p1 : beta_p0);
                             if (__builtin_amdgcn_ballot_w64(bp <= thp) == 0)
                                 covered = 1;
