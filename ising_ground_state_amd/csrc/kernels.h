@@ -33,15 +33,16 @@ struct LowEntry {
 constexpr int kMaxLowest = 64;  // one list entry per lane of a wave
 
 struct Ctrl {
-    unsigned long long counter;  // next work item
     int32_t gbest;               // best energy found by any wave so far (a real state's energy)
     int32_t pad0;
-    uint64_t pad1[6];
+    uint64_t pad1[7];
     Partial result;              // final reduction (offset 64)
     uint64_t slow_total;
     uint64_t bodies_total;
     uint64_t checked_total;
+    unsigned long long counter[kItemParts];  // next work item of each part
 };
+static_assert(sizeof(Ctrl) <= 256, "control block slot");
 
 // Row offsets of the Gray bits t < 7 whose rows the bound gates read (K of
 // prefix variable A-1-t; zero past A, and zero for tables without offsets).

@@ -404,7 +404,8 @@ __global__ void init_ctrl_kernel(Ctrl *ctrl, int32_t t0, int32_t *epmin_pad, int
     epmin_pad[0] = INT_MAX;  // read ahead by the last two bodies of the walk, never used
     epmin_pad[1] = INT_MAX;
     gates_pad[0] = INT_MAX;  // group bound read ahead by the walk's last group, never used
-    ctrl->counter = 0;
+    for (int p = 0; p < kItemParts; ++p)
+        ctrl->counter[p] = 0;
     ctrl->gbest = t0;
     ctrl->slow_total = 0;
     ctrl->bodies_total = 0;
@@ -669,7 +670,7 @@ struct IntMode {
 // exact walks of an integer mode (IntMode), then reduces its lanes' records into
 // one partial result per workgroup.
 template <int R, bool Gated, bool Lowest>
-__global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restrict__ es,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 8 && Gated ? 6 : 1))) void gray_search_kernel(const int32_t *__restrict__ es,
                                                           const int32_t *__restrict__ mint,
                                                           const int32_t *__restrict__ ep,
                                                           const int32_t *__restrict__ epmin,
@@ -678,7 +679,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
                                                           const SearchArgs a)
 {
     extern __shared__ int32_t lds_rows[];  // [l_eff - kU][64 R]
-    __shared__ unsigned long long item_sh;
+    __shared__ unsigned long long item_sh[2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -695,7 +696,7 @@ __global__ __launch_bounds__(256) void gray_search_kernel(const int32_t *__restr
     int T = read_gbest(ctrl);
 
     IntMode<Lowest> mode{rec, ep, ctrl, a.B, a.k_low, lane};
-    walk_units<R, Gated>(a, ctrl, es, mint, ep, epmin, lds_rows, &item_sh, mode, T, bodies, checked,
+    walk_units<R, Gated>(a, ctrl, es, mint, ep, epmin, lds_rows, item_sh, mode, T, bodies, checked,
                          slow_bodies);
 
     Sink sink;

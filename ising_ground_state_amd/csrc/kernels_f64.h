@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "plan.h"  // kItemParts
+
 namespace qubo {
 
 // Suffix columns per lane of the binary64 search (the integer search's default).
@@ -62,13 +64,13 @@ struct LowEntryF64 {
 };
 
 struct CtrlF64 {
-    unsigned long long counter;  // next work item
     long long gbest;             // upper bound of the minimum, as an order-preserving integer key
-    uint64_t pad[6];
+    uint64_t pad[7];
     PartialF64 result;           // final reduction (offset 64)
     uint64_t slow_total;
     uint64_t bodies_total;
     uint64_t candidates_total;
+    unsigned long long counter[kItemParts];  // next work item of each part
 };
 
 struct SearchArgsF64 {

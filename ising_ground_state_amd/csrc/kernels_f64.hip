@@ -270,7 +270,8 @@ __global__ void init_ctrl_f64_kernel(CtrlF64 *ctrl, double t0, int32_t *epmin_pa
     epmin_pad[0] = INT_MAX;  // read ahead by the last two bodies of the walk, never used
     epmin_pad[1] = INT_MAX;
     gates_pad[0] = INT_MAX;  // group bound read ahead by the walk's last group, never used
-    ctrl->counter = 0;
+    for (int p = 0; p < kItemParts; ++p)
+        ctrl->counter[p] = 0;
     ctrl->gbest = order_key(t0);
     ctrl->slow_total = 0;
     ctrl->bodies_total = 0;
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void g
                                                               const SearchArgsF64 a)
 {
     extern __shared__ int32_t lds_rows[];  // [l_eff - kU][64 kR]
-    __shared__ unsigned long long item_sh;
+    __shared__ unsigned long long item_sh[2];
     __shared__ double rec_e[64 * kWaves];
     __shared__ uint64_t rec_c[64 * kWaves], rec_a[64 * kWaves];
 
@@ -534,7 +535,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void g
                          a.k_low, lane, 0u};
     int T = mode.refresh(INT_MAX);
     uint32_t bodies = 0, checked = 0, slow = 0;
-    walk_units<kR, true>(a, ctrl, es, mint, ep, epmin, lds_rows, &item_sh, mode, T, bodies, checked, slow);
+    walk_units<kR, true>(a, ctrl, es, mint, ep, epmin, lds_rows, item_sh, mode, T, bodies, checked, slow);
 
     double e = rec_e[threadIdx.x];
     uint64_t cnt = rec_c[threadIdx.x], arg = rec_a[threadIdx.x];

@@ -24,6 +24,52 @@ constexpr int kMaxSplitBits = 32;        // at most 2^32 sub-problems
 constexpr int kMaxSegBits = 18;          // Gray steps per work unit at most 2^18 (a fine tail)
 constexpr int kMinSegBits = 12;          // and at least 2^12 where the prefix walk allows,
 constexpr int kMinSegBitsIdle = 10;      // or 2^10 when longer units would leave waves idle
+// Work items are handed out in kItemParts parts, one per XCD of an MI355X, in
+// tiles of 2^kTileGroupBits column groups by 2^kTileBlockBits segment blocks
+// (item_place, item_part; walk.h).
+constexpr int kItemParts = 8;
+constexpr int kTileGroupBits = 5;
+constexpr int kTileBlockBits = 5;
+
+// ceil(log2(v)) for v >= 1.
+constexpr int ceil_log2_u64(uint64_t v) { return v <= 1 ? 0 : 64 - __builtin_clzll(v - 1); }
+
+// The order of the work items of a search with G column groups and SB segment
+// blocks (an item: one column group, four consecutive segments).  The items
+// run over the 2^lg_g x 2^lg_s slots of the grid rounded up to powers of two
+// (lg_g = ceil_log2(G), lg_s = ceil_log2(SB)); slots outside G x SB are empty.
+// Slot i lies in a tile of up to 2^kTileGroupBits column groups by
+// 2^kTileBlockBits segment blocks; the tiles run in rows, row after row, and
+// inside a tile the column group runs fastest: the bits of i are, from the top,
+// the row, the tile in the row, the block in the tile and the group in the
+// tile.  A bijection of [0, 2^(lg_g + lg_s)) onto the (group, block) slots,
+// by shifts and masks.  constexpr: the device code and the host's checks call
+// the same function.
+struct ItemPlace {
+    uint64_t group, block;
+};
+constexpr ItemPlace item_place(uint64_t i, int lg_g, int lg_s)
+{
+    const int tg = lg_g < kTileGroupBits ? lg_g : kTileGroupBits;
+    const int ts = lg_s < kTileBlockBits ? lg_s : kTileBlockBits;
+    const uint64_t in_tile = i & ((1ull << (tg + ts)) - 1);
+    const uint64_t tile = (i >> (tg + ts)) & ((1ull << (lg_s - ts)) - 1);
+    const uint64_t row = i >> (tg + lg_s);
+    return ItemPlace{(row << tg) | (in_tile & ((1ull << tg) - 1)), (tile << ts) | (in_tile >> tg)};
+}
+
+// Part p of the slot order: kItemParts contiguous ranges [lo, lo + len) of
+// ceil(slots / kItemParts) slots (the last ones shorter or empty).
+struct ItemPart {
+    uint64_t lo, len;
+};
+constexpr ItemPart item_part(uint64_t slots, uint32_t p)
+{
+    const uint64_t part_len = (slots + kItemParts - 1) / kItemParts;
+    const uint64_t lo = (uint64_t)p * part_len;
+    const uint64_t len = lo >= slots ? 0 : (slots - lo < part_len ? slots - lo : part_len);
+    return ItemPart{lo, len};
+}
 
 constexpr int64_t kAbsSumLimit = (1ll << 30) - 1;
 

@@ -142,9 +142,37 @@ __device__ __forceinline__ uint64_t checked_body(int (&E)[R], const int (&Mr)[kU
     return acc;
 }
 
+// The next work item (slot) of a workgroup, by thread 0.  The slot order
+// (item_place in plan.h) is cut into kItemParts contiguous parts (item_part), each with a
+// counter.  Workgroup w draws from part w mod kItemParts first, which is the
+// XCD the dispatcher places it on (workgroups go to the XCDs in turn), then
+// from the parts after it once one is used up (a used-up part stays used up:
+// its counter only grows).  So the workgroups that share an L2 walk the rows of
+// a few column groups and the gate entries of a few segments at a time.  A
+// workgroup's next item lies about as many items on as its part has
+// workgroups (192 at six per CU), which keeps it in the same column group, and
+// its rows in LDS, while that count is a multiple of kTileGroups.
+// state: the parts this workgroup has found used up (thread 0's, kept in LDS).
+// Returns `slots` once every part is used up.
+template <class Ctl>
+__device__ __forceinline__ uint64_t next_item(Ctl *ctrl, uint64_t slots, unsigned long long &state)
+{
+    while (state < (unsigned long long)kItemParts) {
+        const uint32_t p = (blockIdx.x + (uint32_t)state) % kItemParts;
+        const ItemPart part = item_part(slots, p);
+        if (part.len != 0) {
+            const uint64_t k = atomicAdd(&ctrl->counter[p], 1ull);
+            if (k < part.len)
+                return part.lo + k;
+        }
+        ++state;
+    }
+    return slots;
+}
+
 // The loop over work units of one workgroup (a persistent grid: items come
-// from a global counter; an item is one column group and four consecutive
-// segments of the Gray walk, one per wave).  Per unit: E_sd at the segment's
+// from the counters of next_item; an item is one column group and four
+// consecutive segments of the Gray walk, one per wave).  Per unit: E_sd at the segment's
 // first prefix (eq. 8), the rows of the five lowest Gray bits in registers,
 // the lane bounds of the gates, then the bodies of 32 Gray steps.
 //
@@ -179,7 +207,7 @@ __device__ __forceinline__ uint64_t checked_body(int (&E)[R], const int (&Mr)[kU
 //     body whose first Gray step is base (E holds its first state, or its last
 //     with from_end), leaving E at the body's last state and T lowered.
 // T only falls, so a body that a group or pair bound cleared stays cleared.
-// item_sh: one __shared__ word of the calling kernel; lds_rows: its dynamic LDS
+// item_sh: two __shared__ words of the calling kernel; lds_rows: its dynamic LDS
 // ([l_eff - kU][64 R] rows of Gray bits kU .. l_eff - 1).
 template <int R, bool Gated, class Args, class Ctl, class Mode>
 __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl,
@@ -199,17 +227,25 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
     const int A = a.A;
     const uint64_t cp = a.cols_padded;
     long long cur_g = -1;
+    const uint64_t col_groups = cp / kGroup;
+    const int lg_g = ceil_log2_u64(col_groups), lg_s = ceil_log2_u64(a.seg_blocks);
+    const uint64_t slots = 1ull << (lg_g + lg_s);
+    if (threadIdx.x == 0)
+        item_sh[1] = 0;  // parts used up (thread 0's)
 
     for (;;) {
         if (threadIdx.x == 0)
-            *item_sh = atomicAdd(&ctrl->counter, 1ull);
+            item_sh[0] = next_item(ctrl, slots, item_sh[1]);
         __syncthreads();
-        const uint64_t item = uniform64(*item_sh);
+        const uint64_t item = uniform64(item_sh[0]);
         __syncthreads();
-        if (item >= a.items)
+        if (item >= slots)
             break;
-        const uint64_t g = item / a.seg_blocks;
-        const uint64_t sb = item - g * a.seg_blocks;
+        const ItemPlace place = item_place(item, lg_g, lg_s);
+        const uint64_t g = place.group;
+        const uint64_t sb = place.block;
+        if (g >= col_groups || sb >= a.seg_blocks)
+            continue;  // a slot outside the grid
         if ((long long)g != cur_g) {
             const int rows = a.l_eff - kU;
             for (int k = threadIdx.x; k < rows * kGroup; k += blockDim.x) {
