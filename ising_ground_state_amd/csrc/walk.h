@@ -207,7 +207,7 @@ __device__ __forceinline__ uint64_t next_item(Ctl *ctrl, uint64_t slots, unsigne
 //     body whose first Gray step is base (E holds its first state, or its last
 //     with from_end), leaving E at the body's last state and T lowered.
 // T only falls, so a body that a group or pair bound cleared stays cleared.
-// item_sh: two __shared__ words of the calling kernel; lds_rows: its dynamic LDS
+// item_sh: three __shared__ words of the calling kernel; lds_rows: its dynamic LDS
 // ([l_eff - kU][64 R] rows of Gray bits kU .. l_eff - 1).
 template <int R, bool Gated, class Args, class Ctl, class Mode>
 __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl,
@@ -227,25 +227,38 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
     const int A = a.A;
     const uint64_t cp = a.cols_padded;
     long long cur_g = -1;
-    const uint64_t col_groups = cp / kGroup;
-    const int lg_g = ceil_log2_u64(col_groups), lg_s = ceil_log2_u64(a.seg_blocks);
-    const uint64_t slots = 1ull << (lg_g + lg_s);
     if (threadIdx.x == 0)
-        item_sh[1] = 0;  // parts used up (thread 0's)
+        item_sh[2] = 0;  // parts used up (thread 0's)
 
     for (;;) {
-        if (threadIdx.x == 0)
-            item_sh[0] = next_item(ctrl, slots, item_sh[1]);
+        if (threadIdx.x == 0) {
+            // The grid of items and its slots, recomputed for each item so that
+            // none of it holds registers through the body loop.
+            uint64_t groups = cp / kGroup, blocks = a.seg_blocks;
+            asm volatile("" : "+s"(groups), "+s"(blocks));
+            const int lg_g = ceil_log2_u64(groups), lg_s = ceil_log2_u64(blocks);
+            const uint64_t slots = 1ull << (lg_g + lg_s);
+            uint64_t g = ~0ull, sb = 0;  // ~0: no item left
+            for (;;) {
+                const uint64_t slot = next_item(ctrl, slots, item_sh[2]);
+                if (slot >= slots)
+                    break;
+                const ItemPlace place = item_place(slot, lg_g, lg_s);
+                if (place.group < groups && place.block < blocks) {  // else a slot outside the grid
+                    g = place.group;
+                    sb = place.block;
+                    break;
+                }
+            }
+            item_sh[0] = g;
+            item_sh[1] = sb;
+        }
         __syncthreads();
-        const uint64_t item = uniform64(item_sh[0]);
+        const uint64_t g = uniform64(item_sh[0]);
+        const uint64_t sb = uniform64(item_sh[1]);
         __syncthreads();
-        if (item >= slots)
+        if (g == ~0ull)
             break;
-        const ItemPlace place = item_place(item, lg_g, lg_s);
-        const uint64_t g = place.group;
-        const uint64_t sb = place.block;
-        if (g >= col_groups || sb >= a.seg_blocks)
-            continue;  // a slot outside the grid
         if ((long long)g != cur_g) {
             const int rows = a.l_eff - kU;
             for (int k = threadIdx.x; k < rows * kGroup; k += blockDim.x) {

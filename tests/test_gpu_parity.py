@@ -255,6 +255,74 @@ def test_ragged_slices(q, lo, hi):
         [(int(E[i]), int(idx[i])) for i in order]
 
 
+def _aligned_blocks(lo, hi):
+    """[lo, hi) as maximal aligned blocks [m 2^s, (m + 1) 2^s): (m, s) pairs.
+    Each block of Gray steps is the sub-cube whose first A - s variables spell
+    g(m) (sec. III.C.1)."""
+    while lo < hi:
+        s = (lo & -lo).bit_length() - 1 if lo else (hi - lo).bit_length()
+        while (1 << s) > hi - lo:
+            s -= 1
+        yield lo >> s, s
+        lo += 1 << s
+
+
+def _combine(triples):
+    """min; count at the min; lowest index at the min (the final reduction's rule)."""
+    m = min(t[0] for t in triples)
+    return (m, min(t[1] for t in triples if t[0] == m), sum(t[2] for t in triples if t[0] == m))
+
+
+# Slices of about 40 segments of 2^10 Gray steps, so that the number of segment
+# blocks (four segments each) is not a power of two and the work-item order has
+# empty slots, over 2 (n = 26) and 8 (n = 30) column groups of 512 columns.
+TILE_SLICES = [(26, 16, 3 * 1024 + 96, 41 * 1024 + 160), (30, 18, 5 * 1024 + 32, 52 * 1024 + 64)]
+
+
+@pytest.mark.parametrize("n,A,lo,hi", TILE_SLICES)
+def test_slices_across_tiles(q, n, A, lo, hi):
+    """Minimum, lowest minimiser and count of a ragged slice against oracle tier
+    B on its aligned sub-cubes, gated and strict, 8 and 16 columns per lane; the
+    16 lowest states against the oracle's lists of the same sub-cubes."""
+    Q = qi.general_uniform(n, 7400 + n, -100, 100)
+    blocks = list(_aligned_blocks(lo, hi))
+    assert sum(1 << s for _, s in blocks) == hi - lo
+    want = _combine([oracle.search_gray(Q, k=A - s, top=gray(m)).triple() for m, s in blocks])
+    plan = q.make_plan(n, A)
+    assert plan["seg_bits"] == 10, plan  # segments of 2^10 steps: 39 and 48 segments
+    Qd = dev_q(Q)
+    for strict, R in ((False, 8), (True, 8), (False, 16), (True, 16)):
+        announce("slice across tiles", n, A, lo, hi, strict, R)
+        assert q.search_range(Qd, A, lo, hi, strict=strict, cols_per_lane=R).triple() == want
+        check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
+    lists = []
+    for m, s in blocks:
+        lists += oracle.lowest(Q, 16, fixed=A - s, top=gray(m))
+    announce("slice across tiles, 16 lowest", n, A, lo, hi)
+    assert q.lowest(Qd, 16, prefix_bits=A, gray_lo=lo, gray_hi=hi) == sorted(lists)[:16]
+
+
+def test_f64_slice_across_tiles(q):
+    """The binary64 search of a ragged slice over several segment blocks
+    (2^10-step segments, 39 of them) against the binary64 oracle on the index
+    ranges of its aligned sub-cubes."""
+    import torch
+    n, A, lo, hi = 22, 16, 3 * 1024 + 96, 41 * 1024 + 160
+    Q = qi.general_uniform_f64(n, 7450, -10.0, 10.0)
+    B = n - A
+    parts = []
+    for m, s in _aligned_blocks(lo, hi):
+        top = gray(m)  # the first A - s variables
+        base = top << (B + s)
+        r = oracle.search_direct_f64(Q, lo=base, hi=base + (1 << (B + s)))
+        parts.append(r.triple())
+    want = _combine(parts)
+    announce("f64 slice across tiles", n, A, lo, hi)
+    got = q.search_f64(torch.tensor(Q, dtype=torch.float64, device="cuda:0"), prefix_bits=A,
+                       gray_lo=lo, gray_hi=hi).triple()
+    assert got == want, (got, want)
+
+
 @pytest.mark.parametrize("name", ["C4sub", "C5sub", "C4sub36", "C5sub37"])
 def test_subcubes_at_full_size(q, name):
     """n = 48 and n = 50 at the benchmark's split (A = 28): seeded sub-cubes
