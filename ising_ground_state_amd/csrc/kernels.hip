@@ -679,7 +679,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 8 && G
                                                           const SearchArgs a)
 {
     extern __shared__ int32_t lds_rows[];  // [l_eff - kU][64 R]
-    __shared__ unsigned long long item_sh[3];
+    __shared__ unsigned long long item_sh[4];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

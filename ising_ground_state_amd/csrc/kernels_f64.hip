@@ -521,7 +521,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void g
                                                               const SearchArgsF64 a)
 {
     extern __shared__ int32_t lds_rows[];  // [l_eff - kU][64 kR]
-    __shared__ unsigned long long item_sh[3];
+    __shared__ unsigned long long item_sh[4];
     __shared__ double rec_e[64 * kWaves];
     __shared__ uint64_t rec_c[64 * kWaves], rec_a[64 * kWaves];
 

@@ -207,7 +207,7 @@ __device__ __forceinline__ uint64_t next_item(Ctl *ctrl, uint64_t slots, unsigne
 //     body whose first Gray step is base (E holds its first state, or its last
 //     with from_end), leaving E at the body's last state and T lowered.
 // T only falls, so a body that a group or pair bound cleared stays cleared.
-// item_sh: three __shared__ words of the calling kernel; lds_rows: its dynamic LDS
+// item_sh: four __shared__ words of the calling kernel; lds_rows: its dynamic LDS
 // ([l_eff - kU][64 R] rows of Gray bits kU .. l_eff - 1).
 template <int R, bool Gated, class Args, class Ctl, class Mode>
 __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl,
@@ -226,9 +226,12 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
     const int32_t *lds_lane = lds_rows - kU * kGroup + lane;
     const int A = a.A;
     const uint64_t cp = a.cols_padded;
-    long long cur_g = -1;
-    if (threadIdx.x == 0)
-        item_sh[2] = 0;  // parts used up (thread 0's)
+    // Thread 0's words: item_sh[2] the parts used up, item_sh[3] the column
+    // group whose rows are in LDS (none yet).
+    if (threadIdx.x == 0) {
+        item_sh[2] = 0;
+        item_sh[3] = ~0ull;
+    }
 
     for (;;) {
         if (threadIdx.x == 0) {
@@ -250,16 +253,20 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                     break;
                 }
             }
+            // The top bit of the block word asks for the group's rows in LDS.
+            const uint64_t reload = g != item_sh[3] ? 1ull << 63 : 0;
+            item_sh[3] = g;
             item_sh[0] = g;
-            item_sh[1] = sb;
+            item_sh[1] = sb | reload;
         }
         __syncthreads();
         const uint64_t g = uniform64(item_sh[0]);
-        const uint64_t sb = uniform64(item_sh[1]);
+        const uint64_t sbw = uniform64(item_sh[1]);
         __syncthreads();
         if (g == ~0ull)
             break;
-        if ((long long)g != cur_g) {
+        const uint64_t sb = sbw & ~(1ull << 63);
+        if (sbw >> 63) {
             const int rows = a.l_eff - kU;
             for (int k = threadIdx.x; k < rows * kGroup; k += blockDim.x) {
                 const int t = kU + k / kGroup;
@@ -267,7 +274,6 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                 lds_rows[k] = mint[(uint64_t)(A - 1 - t) * cp + g * kGroup + col];
             }
             __syncthreads();
-            cur_g = (long long)g;
         }
         const uint64_t seg = a.seg_first + sb * kWaves + (uint64_t)wave;
         if (seg >= a.seg_first + a.segs)
@@ -399,7 +405,10 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                     walk = checked_body(E, Mr, top_plus, T, ep + base) != 0;
                 if (walk) {
                     ++slow_bodies;
-                    mode.exact(E, Mr, base, top_plus, T, g * kGroup, !Gated);
+                    // The group's first column, from lane 0's: no register holds the
+                    // group through the body loop.
+                    const uint64_t colbase = uniform64(col0);
+                    mode.exact(E, Mr, base, top_plus, T, colbase, !Gated);
                 }
             }
             if (!last) {
