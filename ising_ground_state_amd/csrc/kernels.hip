@@ -674,6 +674,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 8 && G
                                                           const int32_t *__restrict__ mint,
                                                           const int32_t *__restrict__ ep,
                                                           const int32_t *__restrict__ epmin,
+                                                          const int32_t *__restrict__ gates,
                                                           Partial *__restrict__ partials,
                                                           Ctrl *__restrict__ ctrl,
                                                           const SearchArgs a)
@@ -696,7 +697,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 8 && G
     int T = read_gbest(ctrl);
 
     IntMode<Lowest> mode{rec, ep, ctrl, a.B, a.k_low, lane};
-    walk_units<R, Gated>(a, ctrl, es, mint, ep, epmin, lds_rows, item_sh, mode, T, bodies, checked,
+    walk_units<R, Gated>(a, ctrl, es, mint, ep, epmin, gates, lds_rows, item_sh, mode, T, bodies, checked,
                          slow_bodies);
 
     Sink sink;
@@ -751,7 +752,7 @@ template <int R, bool Gated, bool Lowest>
 static void launch_one(const SearchArgs &args, int blocks, int lds_bytes, hipStream_t stream)
 {
     hipLaunchKernelGGL((gray_search_kernel<R, Gated, Lowest>), dim3(blocks), dim3(64 * kWaves),
-                       lds_bytes, stream, args.es, args.mint, args.ep, args.epmin, args.partials,
+                       lds_bytes, stream, args.es, args.mint, args.ep, args.epmin, args.gates, args.partials,
                        args.ctrl, args);
 }
 

@@ -515,6 +515,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void g
                                                               const int32_t *__restrict__ mint,
                                                               const int32_t *__restrict__ ep,
                                                               const int32_t *__restrict__ epmin,
+                                                              const int32_t *__restrict__ gates,
                                                               const double *__restrict__ Q,
                                                               PartialF64 *__restrict__ partials,
                                                               CtrlF64 *__restrict__ ctrl,
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void g
                          a.k_low, lane, 0u};
     int T = mode.refresh(INT_MAX);
     uint32_t bodies = 0, checked = 0, slow = 0;
-    walk_units<kR, true>(a, ctrl, es, mint, ep, epmin, lds_rows, item_sh, mode, T, bodies, checked, slow);
+    walk_units<kR, true>(a, ctrl, es, mint, ep, epmin, gates, lds_rows, item_sh, mode, T, bodies, checked, slow);
 
     double e = rec_e[threadIdx.x];
     uint64_t cnt = rec_c[threadIdx.x], arg = rec_a[threadIdx.x];
@@ -705,11 +706,11 @@ hipError_t launch_search_f64(const SearchArgsF64 &args, bool lowest, int blocks,
         return hipErrorInvalidValue;
     if (lowest)
         hipLaunchKernelGGL(gray_search_f64_kernel<true>, dim3(blocks), dim3(64 * kWaves), lds_bytes,
-                           stream, args.es, args.mint, args.ep, args.epmin, args.Q, args.partials,
+                           stream, args.es, args.mint, args.ep, args.epmin, args.gates, args.Q, args.partials,
                            args.ctrl, args);
     else
         hipLaunchKernelGGL(gray_search_f64_kernel<false>, dim3(blocks), dim3(64 * kWaves), lds_bytes,
-                           stream, args.es, args.mint, args.ep, args.epmin, args.Q, args.partials,
+                           stream, args.es, args.mint, args.ep, args.epmin, args.gates, args.Q, args.partials,
                            args.ctrl, args);
     return hipGetLastError();
 }

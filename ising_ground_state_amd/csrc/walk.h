@@ -207,6 +207,9 @@ __device__ __forceinline__ uint64_t next_item(Ctl *ctrl, uint64_t slots, unsigne
 //     body whose first Gray step is base (E holds its first state, or its last
 //     with from_end), leaving E at the body's last state and T lowered.
 // T only falls, so a body that a group or pair bound cleared stays cleared.
+// gates: the gates' table, a __restrict__ kernel argument of the caller, so
+// that its wave-uniform reads are scalar loads (read through the argument
+// struct, they were vector loads into VGPRs, with a VALU address and copies);
 // item_sh: four __shared__ words of the calling kernel; lds_rows: its dynamic LDS
 // ([l_eff - kU][64 R] rows of Gray bits kU .. l_eff - 1).
 template <int R, bool Gated, class Args, class Ctl, class Mode>
@@ -214,7 +217,8 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                                            const int32_t *__restrict__ es,
                                            const int32_t *__restrict__ mint,
                                            const int32_t *__restrict__ ep,
-                                           const int32_t *__restrict__ epmin, int32_t *lds_rows,
+                                           const int32_t *__restrict__ epmin,
+                                           const int32_t *__restrict__ gates, int32_t *lds_rows,
                                            unsigned long long *item_sh, Mode &mode, int &T,
                                            uint32_t &bodies, uint32_t &checked, uint32_t &slow_bodies)
 {
@@ -325,7 +329,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
             // through every body).  The barrier keeps the scalar part here too.
             int64_t at = (int64_t)gate_lane_bounds_at(A) + (int64_t)g * (6 * 64) - (int64_t)(g * kGroup);
             asm volatile("" : "+s"(at));
-            const int32_t *lb = a.gates + at + col0;
+            const int32_t *lb = gates + at + col0;
             beta_s0 = lb[0];
             beta_s1 = lb[64];
             beta_p0 = lb[128];
@@ -345,7 +349,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
         // The group gate's prefix bound comes from the per-group table, read one
         // group ahead (the table has one padding entry past the last group); the
         // body minima are read only where a pair or body gate needs them.
-        int q_next = Gated && A > kU + 1 ? a.gates[(b0 + 3) >> 2] : 0;
+        int q_next = Gated && A > kU + 1 ? gates[(b0 + 3) >> 2] : 0;
         uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
             const uint32_t b = b0 + bi;
@@ -365,7 +369,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                         // The first of four aligned bodies: their 128 states of Gray
                         // bits 0..6 fall by at most beta_q(bit 6 at the group's start).
                         const int q = q_next;
-                        q_next = a.gates[(b >> 2) + 1];
+                        q_next = gates[(b >> 2) + 1];
                         const int thq = T - q;
                         const int bq = emin + (((b >> 2) & 1u) ? beta_q1 : beta_q0);
                         if (__builtin_amdgcn_ballot_w64(bq <= thq) == 0)
@@ -377,7 +381,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                         if (top_plus && !last && A > kU) {
                             // An even body and its partner: the 64 states of Gray bits
                             // 0..5 fall by at most beta_p(bit 5 at the pair's start).
-                            const int thp = T - a.gates[gate_pairs_at(A) + (b >> 1)];
+                            const int thp = T - gates[gate_pairs_at(A) + (b >> 1)];
                             const int bp = emin + (((b >> 1) & 1u) ? beta_p1 : beta_p0);
                             if (__builtin_amdgcn_ballot_w64(bp <= thp) == 0)
                                 covered = 1;
