@@ -423,14 +423,20 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                 const bool plus = (((b + 1) >> (t - kU + 1)) & 1u) == 0;
                 int row[R];
                 if (t < a.l_eff) {
-                    // Bit 5 (every other body) reads at constant offsets: the general
-                    // address costs a VALU instruction per body.  The asm marker keeps
-                    // the compiler from merging the branches into that address again.
+                    // Bits 5 and 6 (three bodies in four) read at constant offsets: the
+                    // general address costs a VALU instruction per body.  The asm
+                    // markers keep the compiler from merging the branches into that
+                    // address again.
                     if (t == kU) {
                         asm volatile("; exit flip of bit 5");
 #pragma unroll
                         for (int r = 0; r < R; ++r)
                             row[r] = lds_lane[kU * kGroup + r * 64];
+                    } else if (t == kU + 1) {
+                        asm volatile("; exit flip of bit 6");
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            row[r] = lds_lane[(kU + 1) * kGroup + r * 64];
                     } else {
                         const int32_t *src = lds_lane + t * kGroup;  // row of bit t, this lane
 #pragma unroll
