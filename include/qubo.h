@@ -161,10 +161,9 @@ QUBO_API int qubo_search(const int32_t *Q, int n, int prefix_bits, int cache_bit
  *   - Sizes: the plan's workspace (U, E_s, M_int, 4 x 2^prefix_bits bytes of
  *     prefix energies with their body and group minima, 64 bytes per
  *     workgroup, 256 bytes) must fit the buffer, else QUBO_ESCRATCH before any
- *     device work.  The
- *     planner's default split fits up to n = 40 (73 MiB at n = 40); larger n
- *     fit with a smaller prefix_bits while M_int stays small (n = 42 at
- *     prefix_bits 24: 92 MiB); n = 48 does not fit.
+ *     device work.  The planner's default split fits up to n = 40 (73 MiB at
+ *     n = 40); larger n fit with a smaller prefix_bits while M_int stays small
+ *     (n = 42 at prefix_bits 24: 92 MiB); n = 48 does not fit.
  *   - The buffer keeps the last call's contents; every call writes what it
  *     reads before reading it (its tables, partials and counters come from its
  *     own kernels, with no memset), so nothing carries over between calls.
