@@ -409,7 +409,8 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                     walk = checked_body(E, Mr, top_plus, T, ep + base) != 0;
                 if (walk) {
                     ++slow_bodies;
-                    // The group's first column, from lane 0's: no register holds the
+                    // The group's first column, from lane 0's (every lane is active
+                    // here: the walk decision is a ballot): no register holds the
                     // group through the body loop.
                     const uint64_t colbase = uniform64(col0);
                     mode.exact(E, Mr, base, top_plus, T, colbase, !Gated);
