@@ -602,26 +602,43 @@ __device__ __forceinline__ void exact_body(int (&E)[R], const int (&Mr)[kU][R], 
         else
             add_row(E, Mr[kU - 1]);
     }
+    // The body's 32 prefix energies in one coalesced load (lane i holds step
+    // i mod 32), read per step from a lane; a scalar load per step made every
+    // step wait for memory.
+    const int ep_lanes = ep[base + (uint64_t)(threadIdx.x & (kBody - 1))];
     const int neg_top = top_plus ? 0 : -1;
 #pragma unroll 1
-    for (int m = 0; m < kBody; ++m) {
-        const uint64_t j = base + (uint64_t)m;
-        const int epm = ep[j];
-        sink.step(E, epm, (gray(j) << B) | colbase, T);
-        // The row of the flipped bit t is chosen with selects, not branches:
-        // branches over t made the compiler keep copies of E at every merge.
-        // After the last step t = 5 and no row is chosen (d = 0).  The sign is
-        // an integer mask (0: add, -1: subtract, (d ^ neg) - neg), which stays
-        // in scalar registers; a boolean select here pulled T into VGPRs.
-        const int t = __builtin_ctz((unsigned)(m + 1));
-        const int neg = (t < kU - 1) ? -(((m + 1) >> (t + 1)) & 1) : neg_top;
+    for (int m = 0; m < kBody; m += 2) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            int d = 0;
+        for (int h = 0; h < 2; ++h) {
+            const int mm = m + h;
+            const int epm = __builtin_amdgcn_readlane(ep_lanes, mm);
+            // Only a step where some lane's minimum reaches T has states to
+            // record: the others cost the minimum and a compare.
+            if (__builtin_amdgcn_ballot_w64(row_min<R>(E) <= T - epm) != 0)
+                sink.step(E, epm, (gray(base + (uint64_t)mm) << B) | colbase, T);
+            if (h == 0) {
+                // Odd steps flip Gray bit 0; the sign is an integer mask (0: add,
+                // -1: subtract, (d ^ neg) - neg), which stays in scalar registers.
+                const int neg = -(((mm + 1) >> 1) & 1);
 #pragma unroll
-            for (int tt = 0; tt < kU; ++tt)
-                d = (tt == t) ? Mr[tt][r] : d;
-            E[r] += (d ^ neg) - neg;
+                for (int r = 0; r < R; ++r)
+                    E[r] += (Mr[0][r] ^ neg) - neg;
+            } else {
+                // Even steps flip bit t = ctz(m + 2) >= 1, chosen with selects
+                // (branches over t made the compiler keep copies of E at every
+                // merge).  After the last step t = 5 and no row is chosen.
+                const int t = __builtin_ctz((unsigned)(mm + 1));
+                const int neg = (t < kU - 1) ? -(((mm + 1) >> (t + 1)) & 1) : neg_top;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    int d = 0;
+#pragma unroll
+                    for (int tt = 1; tt < kU; ++tt)
+                        d = (tt == t) ? Mr[tt][r] : d;
+                    E[r] += (d ^ neg) - neg;
+                }
+            }
         }
     }
 }
@@ -653,14 +670,21 @@ struct IntMode {
             sink.k = k_low;
             sink.lane = lane;
         }
+        const int t_in = T;
         exact_body(E, Mr, base, top_plus, T, ep, B, colbase, sink, from_end);
         sink.store(rec, threadIdx.x);
-        // Every lane offers the same T to the shared best: a lane-0
-        // branch here (a divergent region inside the body loop) made
-        // the compiler keep T and the counters in VGPRs.
+        // Every lane offers the same T to the shared best (a lane-0 branch, a
+        // divergent region inside the body loop, made the compiler keep T and
+        // the counters in VGPRs), and only when the wave's bound is below the
+        // threshold the walk started from (a wave-uniform branch; the
+        // spectrum's walk lowers T as it inserts): every value T took before
+        // is already in the shared best, and most exact walks find nothing
+        // below it.  Offered after every exact walk, the waves queued on the
+        // one shared word (the planted n = 32 search ran 3.3 times slower).
         const int wm = sink.bound();
         T = wm < T ? wm : T;
-        atomicMin(&ctrl->gbest, T);
+        if (wm < t_in)
+            atomicMin(&ctrl->gbest, T);
         const int gb = read_gbest(ctrl);
         T = gb < T ? gb : T;
     }

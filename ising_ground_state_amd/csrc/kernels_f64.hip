@@ -398,6 +398,7 @@ struct F64Mode {
     {
         static_assert(R == kR, "one instantiation");
         const int neg_top = top_plus ? 0 : -1;
+
         if (!Lowest) {
             // First pass: the body's smallest W, plus 2 M, bounds the W of every
             // minimiser.  It leaves E at the body's last state, which differs
@@ -423,10 +424,14 @@ struct F64Mode {
             wl.lane = lane;
             wl.e = rec_e[threadIdx.x];
             wl.x = rec_a[threadIdx.x];
+            // The body's 32 prefix energies in one coalesced load (lane i holds
+            // step i mod 32), read per step from a lane: a scalar load per step
+            // made every step wait for memory (0.3 % of this search at n = 48).
+            const int ep_lanes = ep[base + (uint64_t)(threadIdx.x & (kBody - 1))];
 #pragma unroll 1
             for (int m = 0; m < kBody; ++m) {
                 const uint64_t j = base + (uint64_t)m;
-                const int th = T - ep[j];
+                const int th = T - __builtin_amdgcn_readlane(ep_lanes, m);
                 const uint64_t hi = (gray(j) << B) | colbase;
                 uint32_t hits = 0;
 #pragma unroll
@@ -455,9 +460,13 @@ struct F64Mode {
             }
             rec_e[threadIdx.x] = wl.e;
             rec_a[threadIdx.x] = wl.x;
+            // Offered only below the shared bound (a wave-uniform branch): the
+            // waves' unconditional offers after every exact walk queued on the
+            // one shared word.
             const double kt = wl.kth();
-            atomicMin(&ctrl->gbest, order_key(kt));
             const double gb = shared_bound();
+            if (kt < gb)
+                atomicMin(&ctrl->gbest, order_key(kt));
             T = imin(T, quant(gb < kt ? gb : kt));
         } else {
             // The record stays in LDS and is read and written per candidate
@@ -495,8 +504,9 @@ struct F64Mode {
                 flip_after(E, Mr, m, neg_top);
             }
             const double wm = wave_min_f64(rec_e[threadIdx.x]);
-            atomicMin(&ctrl->gbest, order_key(wm));
             const double gb = shared_bound();
+            if (wm < gb)
+                atomicMin(&ctrl->gbest, order_key(wm));
             T = imin(T, quant(gb < wm ? gb : wm));
         }
     }
