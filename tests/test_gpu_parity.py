@@ -218,10 +218,13 @@ def test_range_is_subcube(q, n, A, k):
             check_coverage(q, n, A, None, lo, hi, strict=strict, cols_per_lane=R)
 
 
-# (96, 288): bodies 3..8, one whole aligned group of four (4..7) between ragged
-# ends; (128, 224): bodies 4..6, a group start without its fourth body.
+# (96, 288): bodies 3..8, an aligned quarter of a group between ragged ends;
+# (128, 224): bodies 4..6.  The group gate covers aligned groups of eight bodies:
+# (256, 512) is bodies 8..15, one whole group; (224, 544) bodies 7..16, a whole
+# group between ragged ends; (256, 480) bodies 8..14, a group start without its
+# eighth body; (640, 1152) bodies 20..35, across the group boundaries at 24 and 32.
 RAGGED = [(32, 96), (96, 160), (0, 32), (32, 64), (64, 128 + 32), (1024 + 32, 2048 - 32), (0, 2048),
-          (96, 288), (128, 224)]
+          (96, 288), (128, 224), (256, 512), (224, 544), (256, 480), (640, 1152)]
 
 
 def _slice_states(n, A, lo, hi):
