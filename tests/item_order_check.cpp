@@ -1,6 +1,7 @@
-// Host check of the work-item order of the search (item_place and item_part in
-// plan.h, the functions the search kernels call): for grids of G column groups
-// by SB segment blocks, the slots [0, 2^(lg_g + lg_s)) map one-to-one onto the
+// Host checks of plan.h's layout functions that the search kernels use: the
+// gates' table layout, and the work-item order (item_place and item_part):
+// for grids of G column groups by SB segment blocks, the slots
+// [0, 2^(lg_g + lg_s)) map one-to-one onto the
 // (group, block) pairs of the grid rounded up to powers of two, every pair of
 // the grid G x SB is the image of exactly one slot, and the kItemParts parts
 // cover the slots once, in order.  Prints "ok" or the first failure.
@@ -63,8 +64,29 @@ static int check(uint64_t G, uint64_t SB)
     return 0;
 }
 
+// The gates' table layout (plan.h): group bounds (one per aligned group of
+// eight bodies) with a padding entry, then one pair bound per aligned pair,
+// then the lane bounds at a 64-entry boundary, with no overlap.
+static int check_gates_layout()
+{
+    for (int A = kRegBits; A <= kMaxPrefixBits; ++A) {
+        const uint64_t bodies = 1ull << (A - kRegBits);
+        const uint64_t groups = gate_groups(A), pairs = gate_pair_count(A);
+        const bool ok = groups >= 1 && (A < kRegBits + 3 || groups * 8 == bodies) &&
+                        (A < kRegBits + 1 || pairs * 2 == bodies) && gate_pairs_at(A) == groups + 1 &&
+                        gate_lane_bounds_at(A) >= gate_pairs_at(A) + pairs && gate_lane_bounds_at(A) % 64 == 0;
+        if (!ok) {
+            std::printf("gates layout A=%d\n", A);
+            return 1;
+        }
+    }
+    return 0;
+}
+
 int main()
 {
+    if (check_gates_layout())
+        return 1;
     const uint64_t sizes[] = {1, 2, 3, 5, 7, 8, 31, 32, 33, 63, 64, 65, 100, 256, 257, 1000, 2048};
     for (uint64_t G : sizes)
         for (uint64_t SB : sizes)

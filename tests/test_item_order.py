@@ -1,8 +1,10 @@
-"""The work-item order of the search kernels, checked on the host: the slot
-order (item_place) is a bijection onto the column-group x segment-block grid
-rounded up to powers of two, with the column group fastest inside a tile, and
-the parts (item_part) cover the slots once.  item_order_check.cpp calls the
-constexpr functions of plan.h that the kernels call."""
+"""Layout functions of the search kernels, checked on the host: the gates'
+table (group, pair and lane-bound regions in order, without overlap), and the
+work-item order: the slot order (item_place) is a bijection onto the
+column-group x segment-block grid rounded up to powers of two, with the column
+group fastest inside a tile, and the parts (item_part) cover the slots once.
+item_order_check.cpp calls the constexpr functions of plan.h that the kernels
+call."""
 import os
 import shutil
 import subprocess
