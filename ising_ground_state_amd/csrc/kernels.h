@@ -44,10 +44,10 @@ struct Ctrl {
 };
 static_assert(sizeof(Ctrl) <= 256, "control block slot");
 
-// Row offsets of the Gray bits t < 8 whose rows the bound gates read (K of
+// Row offsets of the Gray bits t < 9 whose rows the bound gates read (K of
 // prefix variable A-1-t; zero past A, and zero for tables without offsets).
 struct GateOffsets {
-    int32_t k[8];
+    int32_t k[16];
 };
 
 struct SearchArgs {
@@ -92,13 +92,13 @@ hipError_t launch_build_tables(const int32_t *U, int ns, int A, int B, uint64_t 
 // The gates' table of a search (integer or over rounded tables; layout in
 // walk.h), from its rows and body minima (epmin, relative to each body's first
 // step) for the Gray steps [j_lo, j_hi):
-//   gates[k]           the group bound of bodies 8k .. 8k+7, relative to the
-//                      group's first step (A >= 8);
+//   gates[k]           the group bound of bodies 16k .. 16k+15, relative to the
+//                      group's first step (A >= 9);
 //   gates[gate_pairs_at(A) + p]  the pair bound of bodies 2p and 2p+1,
 //                      relative to the pair's first step (A >= 6);
 //   then the lane bounds, six rows of 64 per column group (one entry per lane,
 //   R columns each): the bound on the fall of its suffix energies within a body
-//   (bit 4 clear or set at its start), a pair (bit 5) and a group (bit 7), over
+//   (bit 4 clear or set at its start), a pair (bit 5) and a group (bit 8), over
 //   the rows less their offsets kg; padding columns count 0.
 // Pairs and groups that straddle the slice's ends get values that are never
 // read; the padding group bound (gates[gate_groups(A)]) is set by the

@@ -32,7 +32,7 @@
 //     that records every state with E <= T (lowest index and exact counts),
 //     then lowers T.  This is the strict mode;
 //   * the default (gated) mode drops the per-step minimum: before an aligned
-//     group of eight bodies, then before an aligned pair, then before a single
+//     group of sixteen bodies, then before an aligned pair, then before a single
 //     body, one bound per lane (the smallest column energy at the start plus the
 //     largest possible fall over the free Gray bits, plus the smallest prefix
 //     energy of those bodies) is compared with T; only bodies some lane's bound
@@ -242,19 +242,21 @@ __global__ __launch_bounds__(256) void build_prefix_gray_kernel(const int32_t *_
     }
 }
 
-// The offsets of Gray bits 4 to 7 set at the first step of body b: g(32b) has
-// bits 0..3 clear, bit 4 = b0, bit 5 = b0 ^ b1, bit 6 = b1 ^ b2, bit 7 = b2 ^ b3.
+// The offsets of Gray bits 4 to 8 set at the first step of body b: g(32b) has
+// bits 0..3 clear, bit 4 = b0, bit 5 = b0 ^ b1, bit 6 = b1 ^ b2, bit 7 = b2 ^ b3,
+// bit 8 = b3 ^ b4.
 // Unsigned: the gate tables' entries past a slice's ends may be unset.
 __device__ __forceinline__ uint32_t body_start_offset(uint32_t b, const GateOffsets &kg)
 {
     return (b & 1u) * (uint32_t)kg.k[kU - 1] + ((b ^ (b >> 1)) & 1u) * (uint32_t)kg.k[kU] +
            (((b >> 1) ^ (b >> 2)) & 1u) * (uint32_t)kg.k[kU + 1] +
-           (((b >> 2) ^ (b >> 3)) & 1u) * (uint32_t)kg.k[kU + 2];
+           (((b >> 2) ^ (b >> 3)) & 1u) * (uint32_t)kg.k[kU + 2] +
+           (((b >> 3) ^ (b >> 4)) & 1u) * (uint32_t)kg.k[kU + 3];
 }
 
 // Pair bounds (into the gates' pair table): min of the two body minima, each
 // moved from its body's first step to the pair's (+ the offsets set at the
-// body's first step, - those at the pair's: bits 0..4 clear there, bits 5 to 7
+// body's first step, - those at the pair's: bits 0..4 clear there, bits 5 to 8
 // as at body 2p).
 __global__ __launch_bounds__(256) void build_pair_min_kernel(const int32_t *__restrict__ epmin,
                                                              int32_t *__restrict__ pairs,
@@ -271,8 +273,8 @@ __global__ __launch_bounds__(256) void build_pair_min_kernel(const int32_t *__re
     pairs[p] = (int)((uint32_t)imin(m0, m1) - at0);
 }
 
-// Group bounds: min of the eight body minima, each moved to the group's first
-// step (g(256k): bits 0..6 clear, bit 7 = k0).
+// Group bounds: min of the sixteen body minima, each moved to the group's first
+// step (g(512k): bits 0..7 clear, bit 8 = k0).
 __global__ __launch_bounds__(256) void build_group_min_kernel(const int32_t *__restrict__ epmin,
                                                               int32_t *__restrict__ gates,
                                                               uint64_t k_first, uint64_t k_end,
@@ -281,12 +283,12 @@ __global__ __launch_bounds__(256) void build_group_min_kernel(const int32_t *__r
     const uint64_t k = k_first + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= k_end)
         return;
-    const int32_t *e = epmin + 8 * k;
+    const int32_t *e = epmin + 16 * k;
     int m = INT_MAX;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        m = imin(m, (int)((uint32_t)e[i] + body_start_offset((uint32_t)(8 * k + i), kg)));
-    gates[k] = (int)((uint32_t)m - (uint32_t)(k & 1u) * (uint32_t)kg.k[kU + 2]);
+    for (int i = 0; i < 16; ++i)
+        m = imin(m, (int)((uint32_t)e[i] + body_start_offset((uint32_t)(16 * k + i), kg)));
+    gates[k] = (int)((uint32_t)m - (uint32_t)(k & 1u) * (uint32_t)kg.k[kU + 3]);
 }
 
 // Lane bounds, one thread per column group g and lane (written as six rows of
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(256) void build_group_min_kernel(const int32_t *__r
 //   b(c) = sum_{t<5} min(0, M_t(c))          fall within a body from bits 0..4 clear,
 //   s0 = min_c b,  s1 = min_c (b - M_4)      bit 4 clear / set at the body's start,
 //   p0 = min_c (b + min(0, M_5)),  p1 = min_c (b - max(0, M_5))      pair, bit 5,
-//   q0, q1: as p0, p1 from b6 = b + min(0, M_5) + min(0, M_6), with M_7   group, bit 7.
+//   q0, q1: as p0, p1 from b7 = b + sum_{5<=t<8} min(0, M_t), with M_8   group, bit 8.
 template <int R>
 __global__ __launch_bounds__(256) void build_lane_bounds_kernel(const int32_t *__restrict__ mint,
                                                                 uint64_t cols_padded, int A, int B,
@@ -313,8 +315,8 @@ __global__ __launch_bounds__(256) void build_lane_bounds_kernel(const int32_t *_
     for (int r = 0; r < R; ++r) {
         const uint64_t c = col0 + 64 * (uint64_t)r;
         const bool real = c < (1ull << B);
-        int m[kU + 3];
-        for (int t = 0; t < kU + 3; ++t)
+        int m[kU + 4];
+        for (int t = 0; t < kU + 4; ++t)
             m[t] = real && t < A ? mint[(uint64_t)(A - 1 - t) * cols_padded + c] - kg.k[t] : 0;
         int b = 0;
         for (int t = 0; t < kU; ++t)
@@ -324,9 +326,9 @@ __global__ __launch_bounds__(256) void build_lane_bounds_kernel(const int32_t *_
         s1 = imin(s1, b - m[kU - 1]);
         p0 = imin(p0, b5);
         p1 = imin(p1, b - (m[kU] > 0 ? m[kU] : 0));
-        const int b6 = b5 + (m[kU + 1] < 0 ? m[kU + 1] : 0);
-        q0 = imin(q0, b6 + (m[kU + 2] < 0 ? m[kU + 2] : 0));
-        q1 = imin(q1, b6 - (m[kU + 2] > 0 ? m[kU + 2] : 0));
+        const int b7 = b5 + (m[kU + 1] < 0 ? m[kU + 1] : 0) + (m[kU + 2] < 0 ? m[kU + 2] : 0);
+        q0 = imin(q0, b7 + (m[kU + 3] < 0 ? m[kU + 3] : 0));
+        q1 = imin(q1, b7 - (m[kU + 3] > 0 ? m[kU + 3] : 0));
     }
     int32_t *o = out + g * (6 * 64) + lane;  // column group g: six rows of 64
     o[0] = s0;
@@ -390,9 +392,9 @@ hipError_t launch_gate_tables(const int32_t *mint, uint64_t cols_padded, int A, 
     hipLaunchKernelGGL(build_pair_min_kernel, dim3((unsigned)g2), dim3(256), 0, stream, epmin,
                        gates + gate_pairs_at(A), p_first, p_end, kg);
     err = hipGetLastError();
-    if (err != hipSuccess || A < kU + 3)
+    if (err != hipSuccess || A < kU + 4)
         return err;
-    const uint64_t k_first = j_lo >> (kU + 3), k_end = ((j_hi - 1) >> (kU + 3)) + 1;
+    const uint64_t k_first = j_lo >> (kU + 4), k_end = ((j_hi - 1) >> (kU + 4)) + 1;
     const uint64_t g3 = (k_end - k_first + 255) / 256;
     if (g3 > 0xffffffffull)
         return hipErrorInvalidValue;

@@ -38,12 +38,12 @@ constexpr int32_t kPadQ = 3 << 29;
 // the walked suffix energies at or above zero (the integer search's table
 // offsets, with k[v] >= -min_c of the rounded row and es_add >= -min_c of the
 // rounded E_s).  Every k[v] and es_add is at most 2^q + 2.  kgate[t] = k[A-1-t]
-// for the Gray bits t < 8 (zero past A): the gates' share (walk.h).
+// for the Gray bits t < 9 (zero past A): the gates' share (walk.h).
 struct TableOffsetsF64 {
     int32_t rows;
     int32_t es_add;
     int32_t k[32];
-    int32_t kgate[8];
+    int32_t kgate[16];
 };
 
 // One workgroup's partial result (48 bytes).

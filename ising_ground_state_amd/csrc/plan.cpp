@@ -51,7 +51,7 @@ TableOffsets table_offsets(const std::vector<int32_t> &U, int ns, int A)
     t.rows = A;
     t.es_add = 0;
     t.Uoff = U;
-    for (int g = 0; g < 8; ++g)
+    for (int g = 0; g < 16; ++g)
         t.kgate[g] = 0;
     for (int v = 0; v < A; ++v) {
         int64_t k = 0;

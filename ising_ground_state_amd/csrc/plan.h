@@ -11,7 +11,7 @@ namespace qubo {
 
 // Compile-time shape of the search kernel.
 constexpr int kRegBits = 5;        // Gray bits whose M_int rows live in VGPRs
-constexpr int kGateBits = kRegBits + 3;  // and with the pair and group gates' bits: rows the gates read
+constexpr int kGateBits = kRegBits + 4;  // and with the pair and group gates' bits: rows the gates read
 constexpr int kDefaultColsPerLane = 8;  // suffix columns per lane (R); 16 is the other build
 constexpr int kWave = 64;                // CDNA wavefront
 constexpr int kWavesPerBlock = 4;        // one wave per SIMD of a CU
@@ -74,12 +74,12 @@ constexpr ItemPart item_part(uint64_t slots, uint32_t p)
 constexpr int64_t kAbsSumLimit = (1ll << 30) - 1;
 
 // The gates' table of a search (built by launch_gate_tables, read by the walk):
-// the group bound of each aligned group of eight 32-step bodies (at least one)
+// the group bound of each aligned group of sixteen 32-step bodies (at least one)
 // and a padding entry; from gate_pairs_at(A) the pair bound of each aligned
 // pair of bodies; from gate_lane_bounds_at(A) the lane bounds, per column group
 // six rows of 64 (one entry per lane).  The group bounds, read once per group,
 // stay 4 bytes apart.
-constexpr uint64_t gate_groups(int A) { return A > kRegBits + 3 ? 1ull << (A - kRegBits - 3) : 1ull; }
+constexpr uint64_t gate_groups(int A) { return A > kRegBits + 4 ? 1ull << (A - kRegBits - 4) : 1ull; }
 constexpr uint64_t gate_pair_count(int A) { return A > kRegBits + 1 ? 1ull << (A - kRegBits - 1) : 1ull; }
 constexpr uint64_t gate_pairs_at(int A) { return gate_groups(A) + 1; }
 constexpr uint64_t gate_lane_bounds_at(int A) { return (gate_pairs_at(A) + gate_pair_count(A) + 63) & ~63ull; }
@@ -139,13 +139,13 @@ void reduce_fixed(const std::vector<int32_t> &U, int n, int k, uint64_t f,
 // the same amounts lowered: -es_add, and U's prefix diagonal lowered by K[v]
 // (Uoff, the builders' copy of U).  E(x) = E_s + rows + E_p holds unchanged for
 // every state, and every entry stays within sum |U_ij| of zero.  kgate: K of the
-// rows of Gray bits 0..7 (variable A-1-t), which the bound gates take off their
+// rows of Gray bits 0..8 (variable A-1-t), which the bound gates take off their
 // rows and out of their prefix minima (walk.h).
 struct TableOffsets {
     int rows;
     int64_t es_add;
     std::vector<int32_t> Uoff;
-    int32_t kgate[8];
+    int32_t kgate[16];
 };
 TableOffsets table_offsets(const std::vector<int32_t> &U, int ns, int A);
 

@@ -350,7 +350,7 @@ int run_f64(const RequestF64 &rq, qubo_result_f64 *out, bool have_cap, double ca
         hipMemcpyAsync(dU, U.data(), U.size() * 8, hipMemcpyHostToDevice, rq.stream) != hipSuccess)
         return QUBO_EDEVICE;
     GateOffsets kg;
-    std::copy(off.kgate, off.kgate + 8, kg.k);
+    std::copy(off.kgate, off.kgate + 16, kg.k);
     if (launch_build_tables_f64(dU, ns, A, B, cols_padded, scale, off, des, dmint, dep, depmin, lo, hi,
                                 rq.stream) != hipSuccess ||
         launch_gate_tables(dmint, cols_padded, A, B, kColsPerLaneF64, kg, depmin, dgates, lo, hi, rq.stream) !=

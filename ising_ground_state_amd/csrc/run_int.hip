@@ -116,7 +116,7 @@ int run_one(const Request &rq, const DeviceInfo &dev, std::vector<int32_t> U, in
     const bool offset = rq.mode != Mode::Build;
     const TableOffsets off = offset ? table_offsets(U, ns, A) : TableOffsets{0, 0, U, {}};
     GateOffsets kg;
-    std::copy(off.kgate, off.kgate + 8, kg.k);
+    std::copy(off.kgate, off.kgate + 16, kg.k);
     if (hipMemcpyAsync(dU, off.Uoff.data(), off.Uoff.size() * 4, hipMemcpyHostToDevice, rq.stream) !=
         hipSuccess)
         return QUBO_EDEVICE;

@@ -191,15 +191,15 @@ __device__ __forceinline__ uint64_t next_item(Ctl *ctrl, uint64_t slots, unsigne
 // of Algorithm 2 and is walked exactly where it hits.
 // The lane bounds depend only on the lane's columns, so the cache builders
 // compute them once per column group and lane (six rows in the gates' table:
-// body s = 0 and 1, pair for bit 5 = 0 and 1, group of eight bodies for bit 7
-// = 0 and 1), and the prefix bounds of a body (epmin), an aligned pair and an
+// body s = 0 and 1, pair for bit 5 = 0 and 1, group of sixteen bodies for bit
+// 8 = 0 and 1), and the prefix bounds of a body (epmin), an aligned pair and an
 // aligned group (the gates' table).
 //
 // The tables may carry offsets: the row of Gray bit t is M_t + K_t and the
 // prefix energies carry -K_t for each set bit t, so E and E_p each hold a share
 // of sum_{t set} K_t that cancels in their sum.  The lane bounds are then taken
 // over M_t = row - K_t, and the prefix bounds are, for each body (pair, group),
-// the minimum of E_p + sum_{t < 8 set} K_t over its steps less that sum at its
+// the minimum of E_p + sum_{t < 9 set} K_t over its steps less that sum at its
 // first step: the same bounds as without offsets, with no offset in this loop.
 //
 // The mode provides
@@ -319,8 +319,8 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
         }
         // Lane bounds of the fall within a body, for s = 0 and s = 1; within an
         // aligned pair of bodies (64 steps, Gray bits 0..5), for bit 5 = 0 and 1
-        // at the pair's start; and within an aligned group of eight bodies (256
-        // steps, Gray bits 0..7: bits 0..6 start at 0), for bit 7 = 0 and 1 at
+        // at the pair's start; and within an aligned group of sixteen bodies (512
+        // steps, Gray bits 0..8: bits 0..7 start at 0), for bit 8 = 0 and 1 at
         // the group's start: per column group and lane, from the builders.
         int beta_s0 = 0, beta_s1 = 0, beta_p0 = 0, beta_p1 = 0, beta_q0 = 0, beta_q1 = 0;
         if (Gated) {
@@ -350,7 +350,7 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
         // The group gate's prefix bound comes from the per-group table, read one
         // group ahead (the table has one padding entry past the last group); the
         // body minima are read only where a pair or body gate needs them.
-        int q_next = Gated && A > kU + 2 ? gates[(b0 + 7) >> 3] : 0;
+        int q_next = Gated && A > kU + 3 ? gates[(b0 + 15) >> 4] : 0;
         uint32_t covered = 0;  // bodies ahead that a pair or group bound has cleared
         for (uint32_t bi = 0; bi < nbodies; ++bi) {
             const uint32_t b = b0 + bi;
@@ -366,15 +366,15 @@ __device__ __forceinline__ void walk_units(const Args &a, Ctl *__restrict__ ctrl
                     --covered;
                 } else {
                     const int emin = row_min<R>(E);
-                    if ((b & 7u) == 0 && bi + 7 < nbodies && A > kU + 2) {
-                        // The first of eight aligned bodies: their 256 states of Gray
-                        // bits 0..7 fall by at most beta_q(bit 7 at the group's start).
+                    if ((b & 15u) == 0 && bi + 15 < nbodies && A > kU + 3) {
+                        // The first of sixteen aligned bodies: their 512 states of Gray
+                        // bits 0..8 fall by at most beta_q(bit 8 at the group's start).
                         const int q = q_next;
-                        q_next = gates[(b >> 3) + 1];
+                        q_next = gates[(b >> 4) + 1];
                         const int thq = T - q;
-                        const int bq = emin + (((b >> 3) & 1u) ? beta_q1 : beta_q0);
+                        const int bq = emin + (((b >> 4) & 1u) ? beta_q1 : beta_q0);
                         if (__builtin_amdgcn_ballot_w64(bq <= thq) == 0)
-                            covered = 7;
+                            covered = 15;
                     }
                     if (covered != 0) {
                         check = false;

@@ -65,14 +65,14 @@ static int check(uint64_t G, uint64_t SB)
 }
 
 // The gates' table layout (plan.h): group bounds (one per aligned group of
-// eight bodies) with a padding entry, then one pair bound per aligned pair,
+// sixteen bodies) with a padding entry, then one pair bound per aligned pair,
 // then the lane bounds at a 64-entry boundary, with no overlap.
 static int check_gates_layout()
 {
     for (int A = kRegBits; A <= kMaxPrefixBits; ++A) {
         const uint64_t bodies = 1ull << (A - kRegBits);
         const uint64_t groups = gate_groups(A), pairs = gate_pair_count(A);
-        const bool ok = groups >= 1 && (A < kRegBits + 3 || groups * 8 == bodies) &&
+        const bool ok = groups >= 1 && (A < kRegBits + 4 || groups * 16 == bodies) &&
                         (A < kRegBits + 1 || pairs * 2 == bodies) && gate_pairs_at(A) == groups + 1 &&
                         gate_lane_bounds_at(A) >= gate_pairs_at(A) + pairs && gate_lane_bounds_at(A) % 64 == 0;
         if (!ok) {

@@ -284,12 +284,12 @@ def test_range_is_subcube_real(q, n, A, k):
 
 
 RAGGED_F64 = [(32, 96), (64, 320), (96, 160), (32, 64), (96, 96 + 32 * 9), (160, 1024 + 96),
-              (1024 + 32, 2048 - 32), (0, 2048), (224, 544), (256, 480)]
+              (1024 + 32, 2048 - 32), (0, 2048), (224, 544), (256, 480), (480, 1056), (512, 992)]
 
 
 @pytest.mark.parametrize("lo,hi", RAGGED_F64)
 def test_ragged_slices_real(q, lo, hi):
-    """Slices that start inside an aligned group of eight 32-step bodies (the
+    """Slices that start inside an aligned group of sixteen 32-step bodies (the
     group gate then waits for the next group) or end inside one, or hold one
     whole group between ragged ends, with the exit flips' rows in LDS or in
     global memory; the

@@ -79,9 +79,9 @@ def test_every_split(q, n):
             check_coverage(q, n, A, l)
 
 
-@pytest.mark.parametrize("lo,hi", [(32, 96), (64, 320), (160, 1024 + 96), (0, 2048), (224, 544)])
+@pytest.mark.parametrize("lo,hi", [(32, 96), (64, 320), (160, 1024 + 96), (0, 2048), (224, 544), (480, 1056)])
 def test_ragged_slices(q, lo, hi):
-    """Slices that start or end inside an aligned group of eight 32-step bodies,
+    """Slices that start or end inside an aligned group of sixteen 32-step bodies,
     against the sort of the slice's definition energies."""
     n, A = 16, 11
     B = n - A

@@ -219,12 +219,14 @@ def test_range_is_subcube(q, n, A, k):
 
 
 # (96, 288): bodies 3..8, an aligned quarter of a group between ragged ends;
-# (128, 224): bodies 4..6.  The group gate covers aligned groups of eight bodies:
-# (256, 512) is bodies 8..15, one whole group; (224, 544) bodies 7..16, a whole
-# group between ragged ends; (256, 480) bodies 8..14, a group start without its
-# eighth body; (640, 1152) bodies 20..35, across the group boundaries at 24 and 32.
+# (128, 224): bodies 4..6; (256, 512) bodies 8..15; (224, 544) bodies 7..16;
+# (256, 480) bodies 8..14; (640, 1152) bodies 20..35.  The group gate covers
+# aligned groups of sixteen bodies: (512, 1024) is bodies 16..31, one whole
+# group; (480, 1056) bodies 15..32, a whole group between ragged ends;
+# (512, 992) bodies 16..30, a group start without its sixteenth body.
 RAGGED = [(32, 96), (96, 160), (0, 32), (32, 64), (64, 128 + 32), (1024 + 32, 2048 - 32), (0, 2048),
-          (96, 288), (128, 224), (256, 512), (224, 544), (256, 480), (640, 1152)]
+          (96, 288), (128, 224), (256, 512), (224, 544), (256, 480), (640, 1152), (512, 1024), (480, 1056),
+          (512, 992)]
 
 
 def _slice_states(n, A, lo, hi):
